@@ -1,0 +1,391 @@
+/*
+ * Oracle for maximal clique enumeration: TEST INFRASTRUCTURE ONLY.
+ *
+ * A plain, slow, single-threaded CPU reference that the GPU engine is checked
+ * against. Only the tests, the smoke check and the bench's CPU-baseline leg may
+ * load it; the product path never does. It shares no code, header or table with
+ * the GPU library.
+ *
+ * What it computes follows "Parallelizing Maximal Clique Enumeration on GPUs"
+ * (arxiv 2212.01473v2):
+ *   - section 2.1: G is simple and undirected; a maximal clique is a clique not
+ *     contained in a larger clique; the answer is the set of all of them;
+ *   - section 2.3, Algorithm 2: Bron-Kerbosch with pivoting, with Tomita's rule
+ *     (pivot = vertex of P u X with the most neighbours in P);
+ *   - section 2.4, Algorithm 3: one independent first-level subtree per vertex
+ *     v_i, P = later neighbours, X = earlier neighbours, under a degeneracy order;
+ *   - section 2.4 "Induced Subgraphs": each subtree only needs the edges between
+ *     P u X and P, so sets are bitsets over the root's neighbourhood.
+ *
+ * Readings where the pages are silent (each also listed in the design notes):
+ *   - ordering: round-synchronous k-core peel. At level k every alive vertex of
+ *     current degree <= k is removed in one round; k rises to the smallest alive
+ *     degree when a round finds none. Vertex v is "earlier" than u iff
+ *     (round(v), v) < (round(u), u). Any degeneracy order gives the same cliques.
+ *   - pivot ties: smallest vertex id. Branch order: ascending vertex id.
+ *   - result: count, histogram by clique size, and the order-free set hash
+ *       h(c)        = mix64(c + G)
+ *       hash(C)     = mix64(sum_{c in C} h(c) + |C| * G)        (mod 2^64)
+ *       set hash    = sum over maximal cliques C of hash(C)     (mod 2^64)
+ *     with G = 0x9E3779B97F4A7C15 and mix64 the SplitMix64 finaliser
+ *     (Steele, Lea and Flood, OOPSLA 2014).
+ */
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define GOLDEN 0x9E3779B97F4A7C15ULL
+
+/* error classes reported by oracle_validate */
+#define OV_ROWPTR 1   /* row_ptr[0] != 0, row_ptr[n] != nnz, or a row that runs backwards */
+#define OV_RANGE 2    /* a column id outside [0, n) */
+#define OV_LOOP 4     /* an edge (v, v) */
+#define OV_ORDER 8    /* a row that is not strictly ascending (unsorted or duplicate) */
+#define OV_ASYM 16    /* u in N(v) but v not in N(u) */
+
+uint64_t oracle_mix64(uint64_t z) {
+  z ^= z >> 30;
+  z *= 0xBF58476D1CE4E5B9ULL;
+  z ^= z >> 27;
+  z *= 0x94D049BB133111EBULL;
+  z ^= z >> 31;
+  return z;
+}
+
+/* hash of one clique given as a list of vertex ids (any order) */
+uint64_t oracle_clique_hash(int k, const int32_t *ids) {
+  uint64_t s = 0;
+  for (int i = 0; i < k; i++) s += oracle_mix64((uint64_t)(int64_t)ids[i] + GOLDEN);
+  return oracle_mix64(s + (uint64_t)k * GOLDEN);
+}
+
+/* does the sorted row ci[lo..hi) contain key? plain binary search */
+static int row_has(const int32_t *ci, int64_t lo, int64_t hi, int32_t key) {
+  while (lo < hi) {
+    int64_t mid = lo + (hi - lo) / 2;
+    if (ci[mid] == key) return 1;
+    if (ci[mid] < key) lo = mid + 1;
+    else hi = mid;
+  }
+  return 0;
+}
+
+static int adjacent(const int32_t *rp, const int32_t *ci, int32_t u, int32_t v) {
+  return row_has(ci, rp[u], rp[u + 1], v);
+}
+
+/* Checks that (rp, ci) is a simple undirected graph in CSR form. Returns 0 or a
+   bitmask of the OV_* classes found. */
+int oracle_validate(int32_t n, int64_t nnz, const int32_t *rp, const int32_t *ci) {
+  int err = 0;
+  if (n < 0 || nnz < 0) return OV_ROWPTR;
+  if (rp[0] != 0 || (int64_t)rp[n] != nnz) err |= OV_ROWPTR;
+  for (int32_t v = 0; v < n; v++)
+    if (rp[v] > rp[v + 1] || rp[v] < 0 || (int64_t)rp[v + 1] > nnz) err |= OV_ROWPTR;
+  if (err) return err;
+  for (int32_t v = 0; v < n; v++) {
+    for (int64_t e = rp[v]; e < rp[v + 1]; e++) {
+      int32_t u = ci[e];
+      if (u < 0 || u >= n) { err |= OV_RANGE; continue; }
+      if (u == v) err |= OV_LOOP;
+      if (e + 1 < rp[v + 1] && ci[e + 1] <= u) err |= OV_ORDER;
+    }
+  }
+  if (err & (OV_RANGE | OV_ORDER)) return err;   /* binary search needs sorted, in-range rows */
+  for (int32_t v = 0; v < n; v++)
+    for (int64_t e = rp[v]; e < rp[v + 1]; e++)
+      if (!adjacent(rp, ci, ci[e], v)) err |= OV_ASYM;
+  return err;
+}
+
+/* Round-synchronous k-core peel (the ordering reading above).
+   core[v] = k at v's removal (the core number), rnd[v] = round index.
+   Returns d = max core number (0 for n == 0), or -1 on allocation failure. */
+int32_t oracle_peel(int32_t n, const int32_t *rp, const int32_t *ci, int32_t *core, int32_t *rnd) {
+  if (n == 0) return 0;
+  int32_t *deg = (int32_t *)malloc(sizeof(int32_t) * (size_t)n);
+  int32_t *alive = (int32_t *)malloc(sizeof(int32_t) * (size_t)n);
+  int32_t *front = (int32_t *)malloc(sizeof(int32_t) * (size_t)n);
+  char *gone = (char *)calloc((size_t)n, 1);
+  if (!deg || !alive || !front || !gone) { free(deg); free(alive); free(front); free(gone); return -1; }
+  int32_t na = n, k = 0, round = 0, d = 0;
+  for (int32_t v = 0; v < n; v++) { deg[v] = rp[v + 1] - rp[v]; alive[v] = v; }
+  while (na > 0) {
+    int32_t nf = 0;
+    for (int32_t i = 0; i < na; i++)
+      if (deg[alive[i]] <= k) front[nf++] = alive[i];
+    if (nf == 0) {             /* nothing at this level: raise k to the smallest alive degree */
+      int32_t mn = deg[alive[0]];
+      for (int32_t i = 1; i < na; i++) if (deg[alive[i]] < mn) mn = deg[alive[i]];
+      k = mn;
+      continue;
+    }
+    for (int32_t i = 0; i < nf; i++) {
+      int32_t v = front[i];
+      gone[v] = 1; core[v] = k; rnd[v] = round;
+    }
+    if (k > d) d = k;
+    for (int32_t i = 0; i < nf; i++) {
+      int32_t v = front[i];
+      for (int64_t e = rp[v]; e < rp[v + 1]; e++)
+        if (!gone[ci[e]]) deg[ci[e]]--;
+    }
+    round++;
+    int32_t w = 0;
+    for (int32_t i = 0; i < na; i++) if (!gone[alive[i]]) alive[w++] = alive[i];
+    na = w;
+  }
+  free(deg); free(alive); free(front); free(gone);
+  return d;
+}
+
+/* ------------------------------------------------------------------ search */
+typedef struct {
+  /* graph */
+  const int32_t *rp, *ci;
+  const int32_t *rnd;
+  /* current root: L = P_root (ascending id) followed by X_root (ascending id) */
+  int32_t root, p, nl;
+  int32_t *L;
+  int wp, wl;          /* words in a P-bitset and in an L-bitset */
+  uint64_t *adjP;      /* nl rows of wp words: bit b of row a iff L[a] ~ L[b], b < p */
+  uint64_t *colL;      /* p rows of wl words:  bit a of row b iff L[a] ~ L[b] */
+  uint64_t *arena;     /* per-level P and X copies */
+  int32_t *R;          /* clique under construction (global ids, R[0] = root) */
+  int32_t *tmp;
+  /* output */
+  uint64_t count, hash;
+  uint64_t *hist;
+  int32_t hist_cap, hist_len;
+  int64_t nodes, budget;
+  int over_budget, hist_overflow;
+} search;
+
+static int later(const int32_t *rnd, int32_t u, int32_t v) {  /* is u after v in the order? */
+  return rnd[u] > rnd[v] || (rnd[u] == rnd[v] && u > v);
+}
+
+static int popc(uint64_t x) { return __builtin_popcountll(x); }
+
+static void report(search *s, int k) {
+  s->count++;
+  s->hash += oracle_clique_hash(k, s->R);
+  if (k < s->hist_cap) s->hist[k]++;
+  else s->hist_overflow = 1;
+  if (k + 1 > s->hist_len) s->hist_len = k + 1;
+}
+
+/* Algorithm 2 with Tomita's pivot. P is a p-bit set of P_root members; X is an
+   nl-bit set over L (its low p bits are X members from P_root, the rest from
+   X_root). depth = |R| - 1. Level `depth` owns arena record depth: P, X, cand. */
+static void bkt(search *s, int depth) {
+  if (s->over_budget) return;
+  s->nodes++;
+  if (s->budget > 0 && s->nodes > s->budget) { s->over_budget = 1; return; }
+  int wp = s->wp, wl = s->wl;
+  uint64_t *P = s->arena + (size_t)depth * (2 * wp + wl);
+  uint64_t *X = P + wp;
+  uint64_t *cand = X + wl;
+  int pe = 1, xe = 1;
+  for (int w = 0; w < wp; w++) if (P[w]) { pe = 0; break; }
+  for (int w = 0; w < wl; w++) if (X[w]) { xe = 0; break; }
+  if (pe) {
+    if (xe) report(s, depth + 1);     /* Algorithm 2, lines 2-3 */
+    return;                           /* P empty: no branch can follow */
+  }
+  /* pivot: u in P u X maximising |P n N(u)|, ties to the smallest vertex id */
+  int32_t best = -1, bestc = -1;
+  for (int w = 0; w < wl; w++) {
+    uint64_t bits = X[w] | (w < wp ? P[w] : 0);
+    while (bits) {
+      int32_t u = w * 64 + __builtin_ctzll(bits);
+      bits &= bits - 1;
+      const uint64_t *row = s->adjP + (size_t)u * wp;
+      int c = 0;
+      for (int i = 0; i < wp; i++) c += popc(P[i] & row[i]);
+      if (c > bestc || (c == bestc && s->L[u] < s->L[best])) { best = u; bestc = c; }
+    }
+  }
+  /* branches: v in P - N(pivot), ascending id */
+  const uint64_t *prow = s->adjP + (size_t)best * wp;
+  for (int w = 0; w < wp; w++) cand[w] = P[w] & ~prow[w];
+  uint64_t *Pn = s->arena + (size_t)(depth + 1) * (2 * wp + wl);
+  uint64_t *Xn = Pn + wp;
+  for (int w = 0; w < wp; w++) {
+    while (cand[w]) {
+      int b = __builtin_ctzll(cand[w]);
+      cand[w] &= cand[w] - 1;
+      int32_t v = w * 64 + b;
+      const uint64_t *vrow = s->adjP + (size_t)v * wp;
+      const uint64_t *vcol = s->colL + (size_t)v * wl;
+      for (int i = 0; i < wp; i++) Pn[i] = P[i] & vrow[i];      /* P n N(v) */
+      for (int i = 0; i < wl; i++) Xn[i] = X[i] & vcol[i];      /* X n N(v) */
+      s->R[depth + 1] = s->L[v];
+      bkt(s, depth + 1);
+      P[w] &= ~(1ULL << b);          /* P = P - {v} */
+      X[w] |= (1ULL << b);           /* X = X u {v} */
+      if (s->over_budget) return;
+    }
+  }
+}
+
+/* Builds the root's neighbourhood bitsets and runs Algorithm 2 from ({root}, P, X). */
+static int run_root(search *s, int32_t root, int32_t *loc) {
+  const int32_t *rp = s->rp, *ci = s->ci;
+  int64_t lo = rp[root], hi = rp[root + 1];
+  int32_t deg = (int32_t)(hi - lo);
+  int32_t p = 0;
+  for (int64_t e = lo; e < hi; e++) if (later(s->rnd, ci[e], root)) s->L[p++] = ci[e];
+  int32_t nx = p;
+  for (int64_t e = lo; e < hi; e++) if (!later(s->rnd, ci[e], root)) s->L[nx++] = ci[e];
+  s->root = root; s->p = p; s->nl = deg;
+  int wp = (p + 63) / 64; if (wp == 0) wp = 1;
+  int wl = (deg + 63) / 64; if (wl == 0) wl = 1;
+  s->wp = wp; s->wl = wl;
+  s->adjP = (uint64_t *)calloc((size_t)(deg > 0 ? deg : 1) * wp, sizeof(uint64_t));
+  s->colL = (uint64_t *)calloc((size_t)(p > 0 ? p : 1) * wl, sizeof(uint64_t));
+  s->arena = (uint64_t *)calloc((size_t)(p + 2) * (2 * wp + wl), sizeof(uint64_t));
+  if (!s->adjP || !s->colL || !s->arena) { free(s->adjP); free(s->colL); free(s->arena); return -1; }
+  for (int32_t a = 0; a < deg; a++) loc[s->L[a]] = a;
+  /* adjP[a] bit b  <=>  L[b] in N(L[a]) with b < p */
+  for (int32_t a = 0; a < deg; a++) {
+    int32_t x = s->L[a];
+    for (int64_t e = rp[x]; e < rp[x + 1]; e++) {
+      int32_t b = loc[ci[e]];
+      if (b >= 0 && b < p) s->adjP[(size_t)a * wp + (b >> 6)] |= 1ULL << (b & 63);
+    }
+  }
+  for (int32_t a = 0; a < deg; a++)
+    for (int32_t b = 0; b < p; b++)
+      if ((s->adjP[(size_t)a * wp + (b >> 6)] >> (b & 63)) & 1)
+        s->colL[(size_t)b * wl + (a >> 6)] |= 1ULL << (a & 63);
+  for (int32_t a = 0; a < deg; a++) loc[s->L[a]] = -1;
+  uint64_t *P = s->arena, *X = s->arena + wp;
+  for (int32_t b = 0; b < p; b++) P[b >> 6] |= 1ULL << (b & 63);
+  for (int32_t a = p; a < deg; a++) X[a >> 6] |= 1ULL << (a & 63);
+  s->R[0] = root;
+  bkt(s, 0);
+  free(s->adjP); free(s->colL); free(s->arena);
+  s->adjP = s->colL = s->arena = NULL;
+  return 0;
+}
+
+/* Enumerates the maximal cliques whose earliest vertex (in the peel order) is in
+   roots[0..nroots) (roots == NULL: every vertex, i.e. the whole graph).
+   node_budget > 0 stops after that many search-tree nodes and returns 1.
+   hist must hold hist_cap entries; hist_len receives max clique size + 1 (0 if none).
+   Returns 0 on success, 1 over budget, 2 hist_cap too small, -1 on allocation failure,
+   -2 for a root id out of range. */
+int oracle_mce(int32_t n, const int32_t *rp, const int32_t *ci, const int32_t *rnd,
+               const int32_t *roots, int32_t nroots, int64_t node_budget,
+               uint64_t *count, uint64_t *hash, uint64_t *hist, int32_t hist_cap,
+               int32_t *hist_len, int64_t *nodes) {
+  search s;
+  memset(&s, 0, sizeof(s));
+  s.rp = rp; s.ci = ci; s.rnd = rnd;
+  s.hist = hist; s.hist_cap = hist_cap; s.budget = node_budget;
+  for (int32_t i = 0; i < hist_cap; i++) hist[i] = 0;
+  int32_t maxdeg = 0;
+  for (int32_t v = 0; v < n; v++) if (rp[v + 1] - rp[v] > maxdeg) maxdeg = rp[v + 1] - rp[v];
+  s.L = (int32_t *)malloc(sizeof(int32_t) * (size_t)(maxdeg + 1));
+  s.R = (int32_t *)malloc(sizeof(int32_t) * (size_t)(maxdeg + 2));
+  int32_t *loc = (int32_t *)malloc(sizeof(int32_t) * (size_t)(n > 0 ? n : 1));
+  if (!s.L || !s.R || !loc) { free(s.L); free(s.R); free(loc); return -1; }
+  for (int32_t v = 0; v < n; v++) loc[v] = -1;
+  int rc = 0;
+  int32_t cnt = roots ? nroots : n;
+  for (int32_t i = 0; i < cnt && !s.over_budget; i++) {
+    int32_t r = roots ? roots[i] : i;
+    if (r < 0 || r >= n) { rc = -2; break; }
+    if (run_root(&s, r, loc) != 0) { rc = -1; break; }
+  }
+  free(s.L); free(s.R); free(loc);
+  *count = s.count; *hash = s.hash; *hist_len = s.hist_len;
+  if (nodes) *nodes = s.nodes;
+  if (rc) return rc;
+  if (s.over_budget) return 1;
+  if (s.hist_overflow) return 2;
+  return 0;
+}
+
+/* Small graphs only: like oracle_mce over every root, but writes each maximal
+   clique (its ids, sorted ascending) into out, cliques separated by -1.
+   Returns the number of int32 written, or -1 if out_cap is too small. */
+typedef struct { int32_t *out; int64_t cap, len; int overflow; } lister;
+static lister *g_list;
+
+static void list_clique(const int32_t *R, int k) {
+  if (!g_list || g_list->overflow) return;
+  if (g_list->len + k + 1 > g_list->cap) { g_list->overflow = 1; return; }
+  int32_t *dst = g_list->out + g_list->len;
+  for (int i = 0; i < k; i++) dst[i] = R[i];
+  for (int i = 1; i < k; i++) {          /* insertion sort */
+    int32_t x = dst[i]; int j = i - 1;
+    while (j >= 0 && dst[j] > x) { dst[j + 1] = dst[j]; j--; }
+    dst[j + 1] = x;
+  }
+  dst[k] = -1;
+  g_list->len += k + 1;
+}
+
+/* plain Bron-Kerbosch with Tomita pivot over explicit sorted vertex lists (no
+   bitsets), used only to list cliques of small graphs */
+static void bk_list(const int32_t *rp, const int32_t *ci, int32_t *R, int k,
+                    const int32_t *P, int np, const int32_t *X, int nx) {
+  if (np == 0) {
+    if (nx == 0) list_clique(R, k);
+    return;
+  }
+  int32_t best = -1; int bestc = -1;
+  for (int i = 0; i < np + nx; i++) {
+    int32_t u = i < np ? P[i] : X[i - np];
+    int c = 0;
+    for (int j = 0; j < np; j++) c += adjacent(rp, ci, u, P[j]);
+    if (c > bestc || (c == bestc && u < best)) { best = u; bestc = c; }
+  }
+  int32_t *Pc = (int32_t *)malloc(sizeof(int32_t) * (np + 1));
+  int32_t *Xc = (int32_t *)malloc(sizeof(int32_t) * (np + nx + 1));
+  int32_t *Pn = (int32_t *)malloc(sizeof(int32_t) * (np + 1));
+  int32_t *Xn = (int32_t *)malloc(sizeof(int32_t) * (np + nx + 1));
+  int32_t *br = (int32_t *)malloc(sizeof(int32_t) * (np + 1));
+  int ncp = np, ncx = nx, nb = 0;
+  memcpy(Pc, P, sizeof(int32_t) * np);
+  memcpy(Xc, X, sizeof(int32_t) * nx);
+  for (int j = 0; j < np; j++) if (!adjacent(rp, ci, best, P[j])) br[nb++] = P[j];
+  for (int t = 0; t < nb; t++) {
+    int32_t v = br[t];
+    int a = 0, b = 0;
+    for (int j = 0; j < ncp; j++) if (adjacent(rp, ci, v, Pc[j])) Pn[a++] = Pc[j];
+    for (int j = 0; j < ncx; j++) if (adjacent(rp, ci, v, Xc[j])) Xn[b++] = Xc[j];
+    R[k] = v;
+    bk_list(rp, ci, R, k + 1, Pn, a, Xn, b);
+    int w = 0;
+    for (int j = 0; j < ncp; j++) if (Pc[j] != v) Pc[w++] = Pc[j];
+    ncp = w;
+    Xc[ncx++] = v;
+  }
+  free(Pc); free(Xc); free(Pn); free(Xn); free(br);
+}
+
+int64_t oracle_list(int32_t n, const int32_t *rp, const int32_t *ci, const int32_t *rnd,
+                    int32_t *out, int64_t out_cap) {
+  lister l = {out, out_cap, 0, 0};
+  g_list = &l;
+  int32_t maxdeg = 0;
+  for (int32_t v = 0; v < n; v++) if (rp[v + 1] - rp[v] > maxdeg) maxdeg = rp[v + 1] - rp[v];
+  int32_t *P = (int32_t *)malloc(sizeof(int32_t) * (maxdeg + 1));
+  int32_t *X = (int32_t *)malloc(sizeof(int32_t) * (maxdeg + 1));
+  int32_t *R = (int32_t *)malloc(sizeof(int32_t) * (maxdeg + 2));
+  for (int32_t v = 0; v < n; v++) {
+    int np = 0, nx = 0;
+    for (int64_t e = rp[v]; e < rp[v + 1]; e++) {
+      if (later(rnd, ci[e], v)) P[np++] = ci[e];
+      else X[nx++] = ci[e];
+    }
+    R[0] = v;
+    bk_list(rp, ci, R, 1, P, np, X, nx);
+  }
+  free(P); free(X); free(R);
+  g_list = NULL;
+  return l.overflow ? -1 : l.len;
+}
