@@ -1,0 +1,179 @@
+/*
+ * mce.h -- C ABI of the MI355X (gfx950) maximal clique enumeration engine.
+ *
+ * The engine computes every maximal clique of a simple undirected graph exactly
+ * ("Parallelizing Maximal Clique Enumeration on GPUs", arxiv 2212.01473v2,
+ * section 2.1: a maximal clique is a clique that is not contained in a larger
+ * one; section 4.1: the timed work is the clique count plus the degeneracy
+ * ordering). It returns three results instead of listing cliques:
+ *   - count: the number of maximal cliques (64-bit; section 4, Table 1 has graphs
+ *     with more than 2^32 of them);
+ *   - hist[k]: the number of maximal cliques with k vertices;
+ *   - hash: an order-free 64-bit digest of the clique set,
+ *         h(c)     = mix64(c + G)
+ *         hash(C)  = mix64(sum_{c in C} h(c) + |C| * G)       (mod 2^64)
+ *         hash     = sum over maximal cliques C of hash(C)    (mod 2^64)
+ *     where c is an input vertex id, G = 0x9E3779B97F4A7C15 and mix64 is the
+ *     SplitMix64 finaliser (Steele, Lea and Flood, OOPSLA 2014). The pages only
+ *     count cliques; the digest exists so that two engines can be compared on
+ *     the set itself.
+ *
+ * Method (all on the GPU): a k-core peel gives a degeneracy order (section 2.4);
+ * every vertex roots an independent first-level subtree (section 2.4, Algorithm
+ * 3) searched depth-first by one wavefront with Bron-Kerbosch pivoting (section
+ * 2.3, Algorithm 2) over a bit-encoded partial induced subgraph (section 3.4) and
+ * a compact excluded set (section 3.5); idle wavefronts receive branches from
+ * busy ones through a worker list (section 3.3).
+ *
+ * Threading: an engine belongs to one host thread at a time. Engines are
+ * independent of each other. Every call returns an mce_status; no call throws.
+ */
+#ifndef MCE_H
+#define MCE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct mce_engine mce_engine;
+
+typedef enum {
+  MCE_OK = 0,
+  MCE_ERR_ARG = -1,      /* bad argument: null pointer, negative size, buffer too small */
+  MCE_ERR_GRAPH = -2,    /* input is not a simple undirected graph in CSR form */
+  MCE_ERR_NOMEM = -3,    /* device or host allocation failed */
+  MCE_ERR_DEVICE = -4,   /* a HIP runtime call failed */
+  MCE_ERR_STATE = -5,    /* call out of order, e.g. mce_result before any run */
+  MCE_ERR_TIMEOUT = -6,  /* the search ran past mce_config.timeout_ms and was abandoned */
+  MCE_ERR_LIMIT = -7     /* the graph exceeds a limit of this build (degeneracy > 2048) */
+} mce_status;
+
+/* Classes of malformed input, reported in mce_graph_info.graph_errors when
+   mce_run returns MCE_ERR_GRAPH (section 2.1: G is simple and undirected). */
+#define MCE_GRAPH_ROWPTR 1u  /* row_ptr[0] != 0, row_ptr[n] != nnz, or a row that runs backwards */
+#define MCE_GRAPH_RANGE 2u   /* a column id outside [0, n) */
+#define MCE_GRAPH_LOOP 4u    /* a self-loop (v, v) */
+#define MCE_GRAPH_ORDER 8u   /* a row not strictly ascending: unsorted or a duplicate edge */
+#define MCE_GRAPH_ASYM 16u   /* u in N(v) but v not in N(u) */
+
+/* mce_config.flags */
+#define MCE_FLAG_HBM_STAGING 1u  /* keep induced-subgraph rows and DFS stacks in HBM even
+                                    when they fit in LDS (section 3.4 data in device memory) */
+#define MCE_FLAG_PHASE_TIMES 2u  /* record per-phase GPU times in mce_run_stats */
+
+typedef struct {
+  uint32_t struct_size;   /* sizeof(mce_config); 0 is taken as the current size */
+  int32_t device;         /* HIP device ordinal; -1: the device current at mce_create */
+  int32_t worker_list;    /* 1: idle wavefronts receive donated branches (section 3.3); 0: off */
+  int32_t donate_min_p;   /* donate a branch only if its P has at least this many vertices
+                             (section 3.3 uses 10); must be >= 1 */
+  int32_t validate;       /* 1: check the CSR before searching (MCE_ERR_GRAPH on failure) */
+  int32_t max_workers;    /* 0: as many wavefronts as are resident; else at most this many */
+  int64_t timeout_ms;     /* wall-clock limit of one search launch; 0: 120000 */
+  uint32_t flags;         /* MCE_FLAG_* */
+} mce_config;
+
+/* Facts about the last graph run. */
+typedef struct {
+  int32_t n;
+  int64_t nnz;            /* directed entries = 2 |E| */
+  int32_t max_degree;     /* Delta */
+  int32_t degeneracy;     /* d = largest core number */
+  int32_t rounds;         /* peel rounds (the order is (round, id), see mce_ordering) */
+  int32_t max_p;          /* largest |P| at a first-level subtree root (<= d) */
+  int32_t max_x;          /* largest |X| at a first-level subtree root (<= Delta) */
+  int64_t isolated;       /* roots with degree 0, each a maximal clique of size 1 */
+  int64_t roots;          /* first-level subtrees searched (n for mce_run) */
+  uint32_t graph_errors;  /* MCE_GRAPH_* bits when the last run returned MCE_ERR_GRAPH */
+} mce_graph_facts;
+
+/* Counters of the last run, summed over wavefronts. */
+typedef struct {
+  uint32_t struct_size;      /* sizeof(mce_run_stats) */
+  int32_t workers;           /* wavefronts in the largest search launch */
+  int32_t launches;          /* search launches (one per bitset width class) */
+  int32_t pad_;
+  uint64_t nodes;            /* search-tree nodes whose pivot was evaluated */
+  uint64_t leaves;           /* maximal cliques reported (== count minus isolated) */
+  uint64_t donations;        /* branches handed to idle wavefronts (section 3.3, Table 2) */
+  uint64_t pivot_rows;       /* sum over nodes of |P u X_P| rows scanned for the pivot */
+  uint64_t pivot_words;      /* pivot_rows times the bitset width in 64-bit words */
+  uint64_t xx_tests;         /* membership tests of the X_X array against CSR rows */
+  uint64_t ip_rows;          /* induced-subgraph rows built (sum of |P| over roots) */
+  uint64_t busy_ticks;       /* sum over wavefronts of wall-clock ticks spent searching */
+  uint64_t max_busy_ticks;   /* largest per-wavefront busy time */
+  uint64_t max_nodes;        /* largest per-wavefront node count (section 4.3 load) */
+  uint64_t kernel_ticks;     /* wall-clock ticks of the longest search launch */
+  double tick_hz;            /* rate of the tick counters */
+  double ms_total;           /* mce_run wall time on the host, end to end */
+  double ms_validate, ms_peel, ms_orient;   /* GPU phase times, with MCE_FLAG_PHASE_TIMES */
+  double ms_search;          /* search kernels alone (events around each launch), same flag */
+} mce_run_stats;
+
+/* Fills cfg with the defaults: device -1, worker_list 1, donate_min_p 10,
+   validate 1, max_workers 0, timeout_ms 120000, flags 0. */
+mce_status mce_config_init(mce_config* cfg);
+
+/* Creates an engine on cfg->device (cfg may be NULL for the defaults). The engine
+   owns all device scratch memory; it grows on demand and is freed by mce_destroy.
+   On success *out receives the engine. */
+mce_status mce_create(const mce_config* cfg, mce_engine** out);
+
+/* Enumerates all maximal cliques of the graph (n vertices, nnz = row_ptr[n]
+   directed entries) given as CSR in DEVICE memory: row_ptr int32[n+1],
+   col_idx int32[nnz], every row sorted strictly ascending, both directions of
+   each edge present. The caller owns both arrays; they must stay valid and
+   unchanged until the call returns. Work is queued on `stream` (a hipStream_t;
+   NULL = the null stream) and the call returns after it completes. n == 0 is
+   valid (count 0). nnz must be < 2^31. Results are read with mce_result. */
+mce_status mce_run(mce_engine* e, int32_t n, int64_t nnz, const int32_t* row_ptr,
+                   const int32_t* col_idx, void* stream);
+
+/* Like mce_run, but only searches the first-level subtrees of the given roots
+   (section 2.4, Algorithm 3): the result covers exactly the maximal cliques
+   whose earliest vertex in the degeneracy order (see mce_ordering) is one of
+   roots[0..nroots). roots is an int32 array in DEVICE memory; ids must be
+   distinct and in [0, n) (duplicates are counted twice). */
+mce_status mce_run_roots(mce_engine* e, int32_t n, int64_t nnz, const int32_t* row_ptr,
+                         const int32_t* col_idx, const int32_t* roots, int32_t nroots,
+                         void* stream);
+
+/* Results of the last successful run, on the host. hist (nullable) receives
+   hist[0..hist_len); hist_len = largest clique size + 1, or 0 if count == 0.
+   If hist is non-NULL and hist_cap < hist_len the call returns MCE_ERR_ARG and
+   still sets *hist_len. count, hash and hist_len may be NULL. */
+mce_status mce_result(const mce_engine* e, uint64_t* count, uint64_t* hash, uint64_t* hist,
+                      int32_t hist_cap, int32_t* hist_len);
+
+/* Graph facts of the last run (also filled when it returned MCE_ERR_GRAPH). */
+mce_status mce_graph_info(const mce_engine* e, mce_graph_facts* info);
+
+/* Copies the degeneracy order of the last run into caller DEVICE buffers of n
+   int32 each: core[v] = core number of v, round[v] = the peel round that removed
+   v. At level k the peel removes, in one round, every remaining vertex with at
+   most k remaining neighbours; k rises to the smallest remaining degree when a
+   round finds none (section 2.4 asks only for some degeneracy order; this is the
+   one the engine uses). u comes after v iff (round[u], u) > (round[v], v).
+   Either pointer may be NULL. Synchronous on `stream`. */
+mce_status mce_ordering(const mce_engine* e, int32_t* core, int32_t* round, void* stream);
+
+/* Counters of the last run. stats->struct_size must be set by the caller. */
+mce_status mce_stats(const mce_engine* e, mce_run_stats* stats);
+
+/* Text of the last error of this engine ("" if none). Valid until the next call. */
+const char* mce_last_error(const mce_engine* e);
+
+/* Name of a status code. */
+const char* mce_status_string(mce_status s);
+
+/* Frees the engine and all its device memory. NULL is ignored. */
+void mce_destroy(mce_engine* e);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MCE_H */

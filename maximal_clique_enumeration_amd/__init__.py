@@ -1,0 +1,279 @@
+"""Python binding of the MI355X maximal clique enumeration engine (libmce.so).
+
+The functions named ``mce_*`` mirror the C ABI in ``include/mce.h`` one to one and
+only marshal arguments; every step of the computation runs in the HIP library.
+``Engine`` is a thin convenience wrapper that takes torch tensors (device memory
+and streams come from PyTorch; nothing else does).
+
+If the library has not been built, importing still works but every call raises
+``MceLibraryMissing``: there is no CPU fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass, field
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmce.so")
+
+MCE_OK, MCE_ERR_ARG, MCE_ERR_GRAPH, MCE_ERR_NOMEM = 0, -1, -2, -3
+MCE_ERR_DEVICE, MCE_ERR_STATE, MCE_ERR_TIMEOUT, MCE_ERR_LIMIT = -4, -5, -6, -7
+MCE_GRAPH_ROWPTR, MCE_GRAPH_RANGE, MCE_GRAPH_LOOP, MCE_GRAPH_ORDER, MCE_GRAPH_ASYM = 1, 2, 4, 8, 16
+MCE_FLAG_HBM_STAGING, MCE_FLAG_PHASE_TIMES = 1, 2
+
+# every function the C header declares
+EXPORTS = ("mce_config_init", "mce_create", "mce_run", "mce_run_roots", "mce_result",
+           "mce_graph_info", "mce_ordering", "mce_stats", "mce_last_error",
+           "mce_status_string", "mce_destroy")
+
+
+class MceLibraryMissing(RuntimeError):
+    pass
+
+
+class MceError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{status_name(status)}: {message}")
+        self.status = status
+        self.message = message
+
+
+class mce_config(ctypes.Structure):
+    _fields_ = [("struct_size", ctypes.c_uint32), ("device", ctypes.c_int32),
+                ("worker_list", ctypes.c_int32), ("donate_min_p", ctypes.c_int32),
+                ("validate", ctypes.c_int32), ("max_workers", ctypes.c_int32),
+                ("timeout_ms", ctypes.c_int64), ("flags", ctypes.c_uint32)]
+
+
+class mce_graph_facts(ctypes.Structure):
+    _fields_ = [("n", ctypes.c_int32), ("nnz", ctypes.c_int64), ("max_degree", ctypes.c_int32),
+                ("degeneracy", ctypes.c_int32), ("rounds", ctypes.c_int32),
+                ("max_p", ctypes.c_int32), ("max_x", ctypes.c_int32),
+                ("isolated", ctypes.c_int64), ("roots", ctypes.c_int64),
+                ("graph_errors", ctypes.c_uint32)]
+
+
+class mce_run_stats(ctypes.Structure):
+    _fields_ = [("struct_size", ctypes.c_uint32), ("workers", ctypes.c_int32),
+                ("launches", ctypes.c_int32), ("pad_", ctypes.c_int32),
+                ("nodes", ctypes.c_uint64), ("leaves", ctypes.c_uint64),
+                ("donations", ctypes.c_uint64), ("pivot_rows", ctypes.c_uint64),
+                ("pivot_words", ctypes.c_uint64), ("xx_tests", ctypes.c_uint64),
+                ("ip_rows", ctypes.c_uint64), ("busy_ticks", ctypes.c_uint64),
+                ("max_busy_ticks", ctypes.c_uint64), ("max_nodes", ctypes.c_uint64),
+                ("kernel_ticks", ctypes.c_uint64), ("tick_hz", ctypes.c_double),
+                ("ms_total", ctypes.c_double), ("ms_validate", ctypes.c_double),
+                ("ms_peel", ctypes.c_double), ("ms_orient", ctypes.c_double),
+                ("ms_search", ctypes.c_double)]
+
+
+_lib = None
+
+
+def lib_built() -> bool:
+    return os.path.exists(LIB_PATH)
+
+
+def load_library():
+    """Load libmce.so; raises MceLibraryMissing if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise MceLibraryMissing(f"{LIB_PATH} is not built; run __graft_entry__.build() or "
+                                "python -m maximal_clique_enumeration_amd.build")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i32, i64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
+    P = ctypes.POINTER
+    lib.mce_config_init.argtypes = [P(mce_config)]
+    lib.mce_create.argtypes = [P(mce_config), P(vp)]
+    lib.mce_run.argtypes = [vp, i32, i64, vp, vp, vp]
+    lib.mce_run_roots.argtypes = [vp, i32, i64, vp, vp, vp, i32, vp]
+    lib.mce_result.argtypes = [vp, P(ctypes.c_uint64), P(ctypes.c_uint64), P(ctypes.c_uint64), i32, P(i32)]
+    lib.mce_graph_info.argtypes = [vp, P(mce_graph_facts)]
+    lib.mce_ordering.argtypes = [vp, vp, vp, vp]
+    lib.mce_stats.argtypes = [vp, P(mce_run_stats)]
+    lib.mce_last_error.argtypes = [vp]
+    lib.mce_last_error.restype = ctypes.c_char_p
+    lib.mce_status_string.argtypes = [ctypes.c_int]
+    lib.mce_status_string.restype = ctypes.c_char_p
+    lib.mce_destroy.argtypes = [vp]
+    lib.mce_destroy.restype = None
+    for name in ("mce_config_init", "mce_create", "mce_run", "mce_run_roots", "mce_result",
+                 "mce_graph_info", "mce_ordering", "mce_stats"):
+        getattr(lib, name).restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+# ---------------------------------------------------------------- C ABI mirrors
+def mce_config_init(cfg: mce_config) -> int:
+    return load_library().mce_config_init(ctypes.byref(cfg))
+
+
+def mce_create(cfg: mce_config | None, out: ctypes.c_void_p) -> int:
+    return load_library().mce_create(ctypes.byref(cfg) if cfg is not None else None, ctypes.byref(out))
+
+
+def mce_run(engine, n, nnz, row_ptr, col_idx, stream) -> int:
+    return load_library().mce_run(engine, n, nnz, row_ptr, col_idx, stream)
+
+
+def mce_run_roots(engine, n, nnz, row_ptr, col_idx, roots, nroots, stream) -> int:
+    return load_library().mce_run_roots(engine, n, nnz, row_ptr, col_idx, roots, nroots, stream)
+
+
+def mce_result(engine, count, hash_, hist, hist_cap, hist_len) -> int:
+    return load_library().mce_result(engine, count, hash_, hist, hist_cap, hist_len)
+
+
+def mce_graph_info(engine, info: mce_graph_facts) -> int:
+    return load_library().mce_graph_info(engine, ctypes.byref(info))
+
+
+def mce_ordering(engine, core, round_, stream) -> int:
+    return load_library().mce_ordering(engine, core, round_, stream)
+
+
+def mce_stats(engine, stats: mce_run_stats) -> int:
+    return load_library().mce_stats(engine, ctypes.byref(stats))
+
+
+def mce_last_error(engine) -> str:
+    return load_library().mce_last_error(engine).decode()
+
+
+def mce_status_string(status: int) -> str:
+    return load_library().mce_status_string(status).decode()
+
+
+def mce_destroy(engine) -> None:
+    load_library().mce_destroy(engine)
+
+
+def status_name(status: int) -> str:
+    names = {0: "MCE_OK", -1: "MCE_ERR_ARG", -2: "MCE_ERR_GRAPH", -3: "MCE_ERR_NOMEM",
+             -4: "MCE_ERR_DEVICE", -5: "MCE_ERR_STATE", -6: "MCE_ERR_TIMEOUT", -7: "MCE_ERR_LIMIT"}
+    return names.get(status, f"status {status}")
+
+
+# ---------------------------------------------------------------- torch wrapper
+@dataclass
+class Result:
+    count: int
+    hash: int
+    hist: list = field(default_factory=list)
+
+    def key(self):
+        return (self.count, self.hash, tuple(self.hist))
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None and t.numel() else ctypes.c_void_p(0)
+
+
+class Engine:
+    """One engine on one GPU. Inputs are int32 CUDA tensors (CSR)."""
+
+    def __init__(self, device: int | None = None, worker_list: bool = True, donate_min_p: int = 10,
+                 validate: bool = True, max_workers: int = 0, timeout_ms: int = 120000,
+                 hbm_staging: bool = False, phase_times: bool = False):
+        import torch
+        if device is None:
+            device = torch.cuda.current_device()
+        self.device = device
+        cfg = mce_config()
+        self._check(mce_config_init(cfg), "mce_config_init", None)
+        cfg.device = device
+        cfg.worker_list = 1 if worker_list else 0
+        cfg.donate_min_p = donate_min_p
+        cfg.validate = 1 if validate else 0
+        cfg.max_workers = max_workers
+        cfg.timeout_ms = timeout_ms
+        cfg.flags = (MCE_FLAG_HBM_STAGING if hbm_staging else 0) | (MCE_FLAG_PHASE_TIMES if phase_times else 0)
+        h = ctypes.c_void_p()
+        with torch.cuda.device(device):
+            self._check(mce_create(cfg, h), "mce_create", None)
+        self._h = h
+
+    def _check(self, status, what, handle):
+        if status != MCE_OK:
+            msg = mce_last_error(handle) if handle else what
+            raise MceError(status, msg)
+
+    def close(self):
+        if getattr(self, "_h", None) is not None and self._h.value:
+            mce_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *a):
+        self.close()
+
+    @staticmethod
+    def _check_csr(row_ptr, col_idx):
+        import torch
+        for name, t in (("row_ptr", row_ptr), ("col_idx", col_idx)):
+            if t.dtype != torch.int32 or not t.is_cuda or not t.is_contiguous():
+                raise ValueError(f"{name} must be a contiguous int32 CUDA tensor")
+
+    def run(self, row_ptr, col_idx, roots=None, stream=None) -> Result:
+        """Enumerate all maximal cliques (or those of the first-level subtrees of
+        `roots`). Returns (count, hash, hist)."""
+        import torch
+        self._check_csr(row_ptr, col_idx)
+        n = row_ptr.numel() - 1
+        nnz = col_idx.numel()
+        if stream is None:
+            stream = torch.cuda.current_stream(row_ptr.device)
+        sp = ctypes.c_void_p(stream.cuda_stream)
+        if roots is None:
+            st = mce_run(self._h, n, nnz, _ptr(row_ptr), _ptr(col_idx), sp)
+        else:
+            if roots.dtype != torch.int32 or not roots.is_cuda or not roots.is_contiguous():
+                raise ValueError("roots must be a contiguous int32 CUDA tensor")
+            st = mce_run_roots(self._h, n, nnz, _ptr(row_ptr), _ptr(col_idx), _ptr(roots), roots.numel(), sp)
+        self._check(st, "mce_run", self._h)
+        return self.result()
+
+    def result(self) -> Result:
+        cnt = ctypes.c_uint64()
+        hsh = ctypes.c_uint64()
+        hl = ctypes.c_int32()
+        self._check(mce_result(self._h, ctypes.byref(cnt), ctypes.byref(hsh), None, 0, ctypes.byref(hl)),
+                    "mce_result", self._h)
+        cap = max(hl.value, 1)
+        buf = (ctypes.c_uint64 * cap)()
+        self._check(mce_result(self._h, None, None, buf, cap, ctypes.byref(hl)), "mce_result", self._h)
+        return Result(int(cnt.value), int(hsh.value), [int(buf[i]) for i in range(hl.value)])
+
+    def graph_info(self) -> dict:
+        info = mce_graph_facts()
+        self._check(mce_graph_info(self._h, info), "mce_graph_info", self._h)
+        return {name: getattr(info, name) for name, _ in mce_graph_facts._fields_}
+
+    def ordering(self, n: int, device=None):
+        """(core, round) of the last run as int32 CUDA tensors."""
+        import torch
+        dev = torch.device("cuda", self.device if device is None else device)
+        core = torch.empty(n, dtype=torch.int32, device=dev)
+        rnd = torch.empty(n, dtype=torch.int32, device=dev)
+        stream = torch.cuda.current_stream(dev)
+        self._check(mce_ordering(self._h, _ptr(core), _ptr(rnd), ctypes.c_void_p(stream.cuda_stream)),
+                    "mce_ordering", self._h)
+        return core, rnd
+
+    def stats(self) -> dict:
+        st = mce_run_stats()
+        st.struct_size = ctypes.sizeof(mce_run_stats)
+        self._check(mce_stats(self._h, st), "mce_stats", self._h)
+        return {name: getattr(st, name) for name, _ in mce_run_stats._fields_ if name != "pad_"}

@@ -1,0 +1,480 @@
+// Host side of the engine: the C ABI declared in include/mce.h.
+//
+// One mce_run queues, on the caller's stream: CSR validation, the k-core peel
+// (degeneracy order, "Parallelizing Maximal Clique Enumeration on GPUs" section
+// 2.4), the per-root P/X split, then one persistent search launch per bitset
+// width class (sections 3.1-3.5), and reads back count, histogram and hash.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <chrono>
+#include <cstdio>
+#include <cstring>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "../../include/mce.h"
+#include "mce_internal.h"
+
+namespace {
+
+struct DevBuf {
+  void* p = nullptr;
+  size_t bytes = 0;
+};
+
+struct HostPinned {
+  void* p = nullptr;
+  size_t bytes = 0;
+};
+
+}  // namespace
+
+struct mce_engine {
+  mce_config cfg;
+  int device = 0;
+  int num_cu = 0;
+  double tick_hz = 100e6;
+  int peel_blocks_max = 1;
+  std::string err;
+
+  DevBuf ctl, deg, rnd, core, alive0, alive1, front0, front1, pcount, lists, results, wl, slots, stats;
+  HostPinned host;    // staging for device -> host copies
+  hipEvent_t ev[6] = {};
+  bool have_events = false;
+
+  // last run
+  bool have_result = false;
+  bool have_order = false;
+  int32_t last_n = 0;
+  uint64_t count = 0, hash = 0;
+  std::vector<uint64_t> hist;
+  mce_graph_facts info{};
+  mce_run_stats stats_out{};
+};
+
+namespace {
+
+mce_status fail(mce_engine* e, mce_status s, const std::string& msg) {
+  if (e) e->err = msg;
+  return s;
+}
+
+mce_status hip_fail(mce_engine* e, hipError_t h, const char* what) {
+  std::string m = std::string(what) + ": " + hipGetErrorString(h);
+  return fail(e, h == hipErrorOutOfMemory ? MCE_ERR_NOMEM : MCE_ERR_DEVICE, m);
+}
+
+hipError_t ensure(DevBuf& b, size_t bytes) {
+  if (bytes == 0) bytes = 1;
+  if (b.bytes >= bytes) return hipSuccess;
+  if (b.p) (void)hipFree(b.p);
+  b.p = nullptr;
+  b.bytes = 0;
+  hipError_t h = hipMalloc(&b.p, bytes);
+  if (h == hipSuccess) b.bytes = bytes;
+  return h;
+}
+
+hipError_t ensure_host(HostPinned& b, size_t bytes) {
+  if (b.bytes >= bytes) return hipSuccess;
+  if (b.p) (void)hipHostFree(b.p);
+  b.p = nullptr;
+  b.bytes = 0;
+  hipError_t h = hipHostMalloc(&b.p, bytes, hipHostMallocDefault);
+  if (h == hipSuccess) b.bytes = bytes;
+  return h;
+}
+
+void release(DevBuf& b) {
+  if (b.p) (void)hipFree(b.p);
+  b.p = nullptr;
+  b.bytes = 0;
+}
+
+template <class T>
+T* dp(DevBuf& b) {
+  return static_cast<T*>(b.p);
+}
+
+double ms_since(std::chrono::steady_clock::time_point t0) {
+  return std::chrono::duration<double, std::milli>(std::chrono::steady_clock::now() - t0).count();
+}
+
+constexpr size_t kHistWords = MCE_MAX_P + 2;   // global histogram entries
+
+mce_status run_impl(mce_engine* e, int32_t n, int64_t nnz, const int32_t* row_ptr, const int32_t* col_idx,
+                    const int32_t* roots, int32_t nroots, bool subset, void* stream) {
+  const auto t0 = std::chrono::steady_clock::now();
+  if (!e) return MCE_ERR_ARG;
+  e->err.clear();
+  e->have_result = false;
+  e->have_order = false;
+  if (n < 0 || nnz < 0) return fail(e, MCE_ERR_ARG, "n and nnz must be >= 0");
+  if (nnz >= 0x7FFFFFFFLL) return fail(e, MCE_ERR_ARG, "nnz must be < 2^31");
+  if (n > 0 && !row_ptr) return fail(e, MCE_ERR_ARG, "row_ptr is NULL");
+  if (nnz > 0 && !col_idx) return fail(e, MCE_ERR_ARG, "col_idx is NULL");
+  if (subset && (nroots < 0 || (nroots > 0 && !roots))) return fail(e, MCE_ERR_ARG, "bad roots");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t h = hipSetDevice(e->device);
+  if (h != hipSuccess) return hip_fail(e, h, "hipSetDevice");
+
+  e->info = mce_graph_facts{};
+  e->info.n = n;
+  e->info.nnz = nnz;
+  std::memset(&e->stats_out, 0, sizeof(e->stats_out));
+  e->stats_out.struct_size = sizeof(mce_run_stats);
+  e->stats_out.tick_hz = e->tick_hz;
+  e->hist.clear();
+  e->count = e->hash = 0;
+  e->last_n = n;
+  const int cnt = subset ? nroots : n;
+  e->info.roots = cnt;
+  if (n == 0) {
+    if (subset && nroots > 0) return fail(e, MCE_ERR_ARG, "roots given for an empty graph");
+    e->have_result = true;
+    e->stats_out.ms_total = ms_since(t0);
+    return MCE_OK;
+  }
+  const bool timing = (e->cfg.flags & MCE_FLAG_PHASE_TIMES) && e->have_events;
+  const bool hbm = (e->cfg.flags & MCE_FLAG_HBM_STAGING) != 0;
+  const u64 budget = (u64)((double)e->cfg.timeout_ms * 1e-3 * e->tick_hz);
+
+  size_t nb = (size_t)n * sizeof(int);
+  if ((h = ensure(e->ctl, sizeof(MceCtl))) != hipSuccess || (h = ensure(e->deg, nb)) != hipSuccess ||
+      (h = ensure(e->rnd, nb)) != hipSuccess || (h = ensure(e->core, nb)) != hipSuccess ||
+      (h = ensure(e->alive0, nb)) != hipSuccess || (h = ensure(e->alive1, nb)) != hipSuccess ||
+      (h = ensure(e->front0, nb)) != hipSuccess || (h = ensure(e->front1, nb)) != hipSuccess ||
+      (h = ensure(e->pcount, (size_t)std::max(cnt, 1) * sizeof(int))) != hipSuccess ||
+      (h = ensure(e->lists, (size_t)std::max(cnt, 1) * sizeof(int))) != hipSuccess ||
+      (h = ensure(e->results, (1 + kHistWords) * sizeof(u64))) != hipSuccess ||
+      (h = ensure(e->wl, sizeof(MceWl))) != hipSuccess ||
+      (h = ensure_host(e->host, sizeof(MceCtl) + (1 + kHistWords) * sizeof(u64))) != hipSuccess)
+    return hip_fail(e, h, "allocation");
+
+  MceCtl* ctl = dp<MceCtl>(e->ctl);
+  u64* results = dp<u64>(e->results);
+  if ((h = hipMemsetAsync(ctl, 0, sizeof(MceCtl), s)) != hipSuccess) return hip_fail(e, h, "memset");
+  if ((h = hipMemsetAsync(results, 0, (1 + kHistWords) * sizeof(u64), s)) != hipSuccess)
+    return hip_fail(e, h, "memset");
+
+  const int grid = std::max(1, e->num_cu * 8);
+  if (timing) (void)hipEventRecord(e->ev[0], s);
+  if (e->cfg.validate) {
+    if ((h = mce_launch_validate(n, nnz, row_ptr, col_idx, ctl, grid, s)) != hipSuccess)
+      return hip_fail(e, h, "validate launch");
+  }
+  if (timing) (void)hipEventRecord(e->ev[1], s);
+  // the peel: one block for small graphs (no grid barrier traffic), else a full grid
+  int pblocks = n <= 16384 ? 1 : std::min(e->peel_blocks_max, (n + 255) / 256);
+  if ((h = mce_launch_peel(n, row_ptr, col_idx, dp<int>(e->deg), dp<int>(e->rnd), dp<int>(e->core),
+                           dp<int>(e->alive0), dp<int>(e->alive1), dp<int>(e->front0), dp<int>(e->front1),
+                           ctl, budget, pblocks, s)) != hipSuccess)
+    return hip_fail(e, h, "peel launch");
+  if (timing) (void)hipEventRecord(e->ev[2], s);
+  if ((h = mce_launch_orient(n, row_ptr, col_idx, dp<int>(e->rnd), subset ? roots : nullptr, cnt,
+                             dp<int>(e->pcount), ctl, grid, s)) != hipSuccess)
+    return hip_fail(e, h, "orient launch");
+  MceCtl* hctl = static_cast<MceCtl*>(e->host.p);
+  if ((h = hipMemcpyAsync(hctl, ctl, sizeof(MceCtl), hipMemcpyDeviceToHost, s)) != hipSuccess)
+    return hip_fail(e, h, "readback");
+  if ((h = hipStreamSynchronize(s)) != hipSuccess) return hip_fail(e, h, "synchronize after orient");
+
+  const u32 gbits = hctl->status & 0x1Fu;
+  e->info.max_degree = hctl->max_degree;
+  if (gbits) {
+    e->info.graph_errors = gbits;
+    return fail(e, MCE_ERR_GRAPH, "input is not a simple undirected graph in CSR form");
+  }
+  if (hctl->status & MCE_E_TIMEOUT) return fail(e, MCE_ERR_TIMEOUT, "k-core peel ran past the time limit");
+  if (hctl->status & MCE_E_ROOTS) return fail(e, MCE_ERR_ARG, "a root id is outside [0, n)");
+  e->info.degeneracy = hctl->degeneracy;
+  e->info.rounds = hctl->rounds;
+  e->info.max_p = hctl->max_p;
+  e->info.max_x = hctl->max_x;
+  e->info.isolated = (int64_t)hctl->isolated;
+  e->have_order = true;
+  if (hctl->status & MCE_E_LIMIT)
+    return fail(e, MCE_ERR_LIMIT, "a first-level subtree has more than 2048 later neighbours");
+
+  // roots per class, heaviest class first
+  ClassOffsets off{};
+  int counts[MCE_NCLASS];
+  int total = 0;
+  for (int c = 0; c < MCE_NCLASS; c++) {
+    counts[c] = hctl->class_count[c];
+    off.off[c] = total;
+    total += counts[c];
+  }
+  const u64 iso = hctl->isolated, iso_hash = hctl->isolated_hash;
+  if (total > 0) {
+    if ((h = mce_launch_bucket(n, subset ? roots : nullptr, cnt, dp<int>(e->pcount), off, dp<int>(e->lists), ctl,
+                               grid, s)) != hipSuccess)
+      return hip_fail(e, h, "bucket launch");
+  }
+  if (timing) (void)hipEventRecord(e->ev[3], s);
+
+  std::vector<u64> stat_sum(MCE_NSTAT, 0);
+  double ms_search = 0;   // search kernels only, from events around each launch
+  u64 max_busy = 0, max_nodes = 0, max_ticks = 0;
+  int max_workers_used = 0, launches = 0;
+  for (int c = MCE_NCLASS - 1; c >= 0; c--) {
+    if (counts[c] == 0) continue;
+    int nw = mce_search_max_workers(c, hbm, e->num_cu);
+    if (nw <= 0) return fail(e, MCE_ERR_DEVICE, "search kernel occupancy query failed");
+    if (e->cfg.max_workers > 0) nw = std::min(nw, (int)e->cfg.max_workers);
+    if (!e->cfg.worker_list) nw = std::min(nw, counts[c]);
+    SlotLayout L = mce_slot_layout(c, std::max(hctl->max_x, 1));
+    if ((h = ensure(e->slots, L.bytes * (size_t)nw)) != hipSuccess) return hip_fail(e, h, "worker slots");
+    if ((h = ensure(e->stats, (size_t)nw * MCE_NSTAT * sizeof(u64))) != hipSuccess)
+      return hip_fail(e, h, "stats buffer");
+    if ((h = mce_launch_wl_init(dp<MceWl>(e->wl), nw, s)) != hipSuccess) return hip_fail(e, h, "wl init");
+    SearchParams prm{};
+    prm.rp = row_ptr;
+    prm.ci = col_idx;
+    prm.rnd = dp<int>(e->rnd);
+    prm.roots = dp<int>(e->lists) + off.off[c];
+    prm.nroots = counts[c];
+    prm.nworkers = nw;
+    prm.g_hist = results + 1;
+    prm.g_hash = results;
+    prm.wl = dp<MceWl>(e->wl);
+    prm.slots = dp<char>(e->slots);
+    prm.slot_bytes = L.bytes;
+    prm.off_rows = L.off_rows;
+    prm.off_hv = L.off_hv;
+    prm.off_pid = L.off_pid;
+    prm.off_stack = L.off_stack;
+    prm.off_xx = L.off_xx;
+    prm.off_mail = L.off_mail;
+    prm.donate_min_p = std::max(1, (int)e->cfg.donate_min_p);
+    prm.worker_list = e->cfg.worker_list ? 1 : 0;
+    prm.budget = budget;
+    prm.status = &ctl->status;
+    prm.stats = dp<u64>(e->stats);
+    if (timing) (void)hipEventRecord(e->ev[4], s);
+    if ((h = mce_launch_search(c, hbm, prm, s)) != hipSuccess) return hip_fail(e, h, "search launch");
+    if (timing) (void)hipEventRecord(e->ev[5], s);
+    launches++;
+    max_workers_used = std::max(max_workers_used, nw);
+    // per-wavefront counters of this launch
+    std::vector<u64> st((size_t)nw * MCE_NSTAT);
+    if ((h = hipMemcpyAsync(st.data(), e->stats.p, st.size() * sizeof(u64), hipMemcpyDeviceToHost, s)) !=
+        hipSuccess)
+      return hip_fail(e, h, "stats readback");
+    if ((h = hipStreamSynchronize(s)) != hipSuccess) return hip_fail(e, h, "synchronize after search");
+    if (timing) {
+      float ms = 0;
+      (void)hipEventElapsedTime(&ms, e->ev[4], e->ev[5]);
+      ms_search += ms;
+    }
+    for (int w = 0; w < nw; w++) {
+      const u64* r = &st[(size_t)w * MCE_NSTAT];
+      for (int i = 0; i < MCE_NSTAT; i++) stat_sum[i] += r[i];
+      max_busy = std::max(max_busy, r[ST_BUSY_TICKS]);
+      max_nodes = std::max(max_nodes, r[ST_NODES]);
+      max_ticks = std::max(max_ticks, r[ST_TOTAL_TICKS]);
+    }
+  }
+
+  u64* hres = reinterpret_cast<u64*>(static_cast<char*>(e->host.p) + sizeof(MceCtl));
+  if ((h = hipMemcpyAsync(hres, results, (1 + kHistWords) * sizeof(u64), hipMemcpyDeviceToHost, s)) != hipSuccess ||
+      (h = hipMemcpyAsync(hctl, ctl, sizeof(MceCtl), hipMemcpyDeviceToHost, s)) != hipSuccess)
+    return hip_fail(e, h, "result readback");
+  if ((h = hipStreamSynchronize(s)) != hipSuccess) return hip_fail(e, h, "synchronize at end");
+  if (hctl->status & MCE_E_TIMEOUT) return fail(e, MCE_ERR_TIMEOUT, "search ran past the time limit");
+  if (hctl->status & MCE_E_PROTO) return fail(e, MCE_ERR_DEVICE, "worker-list bookkeeping error");
+  if (hctl->status & MCE_E_LIMIT) return fail(e, MCE_ERR_LIMIT, "subtree larger than its width class");
+
+  std::vector<uint64_t> hist(kHistWords, 0);
+  for (size_t k = 0; k < kHistWords; k++) hist[k] = hres[1 + k];
+  hist[1] += iso;
+  u64 count = 0;
+  size_t len = 0;
+  for (size_t k = 0; k < kHistWords; k++) {
+    count += hist[k];
+    if (hist[k]) len = k + 1;
+  }
+  hist.resize(len);
+  e->hist = hist;
+  e->count = count;
+  e->hash = hres[0] + iso_hash;
+  e->have_result = true;
+
+  mce_run_stats& so = e->stats_out;
+  so.workers = max_workers_used;
+  so.launches = launches;
+  so.nodes = stat_sum[ST_NODES];
+  so.leaves = stat_sum[ST_LEAVES];
+  so.donations = stat_sum[ST_DONATIONS];
+  so.pivot_rows = stat_sum[ST_PIVOT_ROWS];
+  so.pivot_words = stat_sum[ST_PIVOT_WORDS];
+  so.xx_tests = stat_sum[ST_XX_TESTS];
+  so.ip_rows = stat_sum[ST_IP_ROWS];
+  so.busy_ticks = stat_sum[ST_BUSY_TICKS];
+  so.max_busy_ticks = max_busy;
+  so.max_nodes = max_nodes;
+  so.kernel_ticks = max_ticks;
+  if (timing) {
+    float a = 0, b = 0, c = 0;
+    (void)hipEventElapsedTime(&a, e->ev[0], e->ev[1]);
+    (void)hipEventElapsedTime(&b, e->ev[1], e->ev[2]);
+    (void)hipEventElapsedTime(&c, e->ev[2], e->ev[3]);
+    so.ms_validate = a;
+    so.ms_peel = b;
+    so.ms_orient = c;   // orientation, host readback and root bucketing
+    so.ms_search = ms_search;
+  }
+  so.ms_total = ms_since(t0);
+  return MCE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+mce_status mce_config_init(mce_config* cfg) {
+  if (!cfg) return MCE_ERR_ARG;
+  std::memset(cfg, 0, sizeof(*cfg));
+  cfg->struct_size = sizeof(mce_config);
+  cfg->device = -1;
+  cfg->worker_list = 1;
+  cfg->donate_min_p = 10;
+  cfg->validate = 1;
+  cfg->max_workers = 0;
+  cfg->timeout_ms = 120000;
+  cfg->flags = 0;
+  return MCE_OK;
+}
+
+mce_status mce_create(const mce_config* cfg, mce_engine** out) {
+  if (!out) return MCE_ERR_ARG;
+  *out = nullptr;
+  mce_config c;
+  mce_config_init(&c);
+  if (cfg) {
+    size_t sz = cfg->struct_size ? std::min<size_t>(cfg->struct_size, sizeof(mce_config)) : sizeof(mce_config);
+    std::memcpy(&c, cfg, sz);
+    c.struct_size = sizeof(mce_config);
+  }
+  if (c.donate_min_p < 1 || c.max_workers < 0 || c.timeout_ms < 0) return MCE_ERR_ARG;
+  if (c.timeout_ms == 0) c.timeout_ms = 120000;
+  mce_engine* e = new (std::nothrow) mce_engine();
+  if (!e) return MCE_ERR_NOMEM;
+  e->cfg = c;
+  int dev = c.device;
+  if (dev < 0) {
+    if (hipGetDevice(&dev) != hipSuccess) {
+      delete e;
+      return MCE_ERR_DEVICE;
+    }
+  }
+  e->device = dev;
+  if (hipSetDevice(dev) != hipSuccess) {
+    delete e;
+    return MCE_ERR_DEVICE;
+  }
+  int cus = 0, khz = 0, coop = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      hipDeviceGetAttribute(&coop, hipDeviceAttributeCooperativeLaunch, dev) != hipSuccess) {
+    delete e;
+    return MCE_ERR_DEVICE;
+  }
+  if (!coop) {
+    delete e;
+    return MCE_ERR_DEVICE;
+  }
+  if (hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, dev) == hipSuccess && khz > 0)
+    e->tick_hz = (double)khz * 1e3;
+  e->num_cu = cus;
+  e->peel_blocks_max = mce_peel_max_blocks(cus);
+  e->have_events = true;
+  for (auto& ev : e->ev)
+    if (hipEventCreate(&ev) != hipSuccess) e->have_events = false;
+  *out = e;
+  return MCE_OK;
+}
+
+mce_status mce_run(mce_engine* e, int32_t n, int64_t nnz, const int32_t* row_ptr, const int32_t* col_idx,
+                   void* stream) {
+  return run_impl(e, n, nnz, row_ptr, col_idx, nullptr, 0, false, stream);
+}
+
+mce_status mce_run_roots(mce_engine* e, int32_t n, int64_t nnz, const int32_t* row_ptr, const int32_t* col_idx,
+                         const int32_t* roots, int32_t nroots, void* stream) {
+  return run_impl(e, n, nnz, row_ptr, col_idx, roots, nroots, true, stream);
+}
+
+mce_status mce_result(const mce_engine* e, uint64_t* count, uint64_t* hash, uint64_t* hist, int32_t hist_cap,
+                      int32_t* hist_len) {
+  if (!e) return MCE_ERR_ARG;
+  if (!e->have_result) return MCE_ERR_STATE;
+  int32_t len = (int32_t)e->hist.size();
+  if (hist_len) *hist_len = len;
+  if (count) *count = e->count;
+  if (hash) *hash = e->hash;
+  if (hist) {
+    if (hist_cap < len) return MCE_ERR_ARG;
+    for (int32_t i = 0; i < len; i++) hist[i] = e->hist[i];
+  }
+  return MCE_OK;
+}
+
+mce_status mce_graph_info(const mce_engine* e, mce_graph_facts* info) {
+  if (!e || !info) return MCE_ERR_ARG;
+  *info = e->info;
+  return MCE_OK;
+}
+
+mce_status mce_ordering(const mce_engine* e, int32_t* core, int32_t* round, void* stream) {
+  if (!e) return MCE_ERR_ARG;
+  if (!e->have_order) return MCE_ERR_STATE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  size_t nb = (size_t)e->last_n * sizeof(int32_t);
+  if (nb == 0) return MCE_OK;
+  if (hipSetDevice(e->device) != hipSuccess) return MCE_ERR_DEVICE;
+  if (core && hipMemcpyAsync(core, e->core.p, nb, hipMemcpyDeviceToDevice, s) != hipSuccess) return MCE_ERR_DEVICE;
+  if (round && hipMemcpyAsync(round, e->rnd.p, nb, hipMemcpyDeviceToDevice, s) != hipSuccess) return MCE_ERR_DEVICE;
+  if (hipStreamSynchronize(s) != hipSuccess) return MCE_ERR_DEVICE;
+  return MCE_OK;
+}
+
+mce_status mce_stats(const mce_engine* e, mce_run_stats* stats) {
+  if (!e || !stats) return MCE_ERR_ARG;
+  uint32_t want = stats->struct_size ? stats->struct_size : (uint32_t)sizeof(mce_run_stats);
+  size_t n = std::min<size_t>(want, sizeof(mce_run_stats));
+  std::memcpy(stats, &e->stats_out, n);
+  stats->struct_size = (uint32_t)n;
+  return MCE_OK;
+}
+
+const char* mce_last_error(const mce_engine* e) { return e ? e->err.c_str() : "null engine"; }
+
+const char* mce_status_string(mce_status s) {
+  switch (s) {
+    case MCE_OK: return "MCE_OK";
+    case MCE_ERR_ARG: return "MCE_ERR_ARG";
+    case MCE_ERR_GRAPH: return "MCE_ERR_GRAPH";
+    case MCE_ERR_NOMEM: return "MCE_ERR_NOMEM";
+    case MCE_ERR_DEVICE: return "MCE_ERR_DEVICE";
+    case MCE_ERR_STATE: return "MCE_ERR_STATE";
+    case MCE_ERR_TIMEOUT: return "MCE_ERR_TIMEOUT";
+    case MCE_ERR_LIMIT: return "MCE_ERR_LIMIT";
+  }
+  return "MCE_ERR_UNKNOWN";
+}
+
+void mce_destroy(mce_engine* e) {
+  if (!e) return;
+  (void)hipSetDevice(e->device);
+  DevBuf* bufs[] = {&e->ctl, &e->deg, &e->rnd, &e->core, &e->alive0, &e->alive1, &e->front0,
+                    &e->front1, &e->pcount, &e->lists, &e->results, &e->wl, &e->slots, &e->stats};
+  for (DevBuf* b : bufs) release(*b);
+  if (e->host.p) (void)hipHostFree(e->host.p);
+  for (auto& ev : e->ev)
+    if (ev) (void)hipEventDestroy(ev);
+  delete e;
+}
+
+}  // extern "C"

@@ -1,0 +1,178 @@
+// Device-side building blocks shared by the engine's kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+typedef unsigned long long u64;
+typedef unsigned int u32;
+
+#define MCE_WAVE 64
+#define MCE_GOLDEN 0x9E3779B97F4A7C15ULL
+
+// engine error bits, above the MCE_GRAPH_* input classes (bits 0..4)
+#define MCE_E_TIMEOUT (1u << 16)   // a bounded wait or the search ran past its deadline
+#define MCE_E_LIMIT (1u << 17)     // a root's P does not fit the launch's bitset width
+#define MCE_E_PROTO (1u << 18)     // worker-list bookkeeping went wrong
+#define MCE_E_ROOTS (1u << 19)     // a root id outside [0, n)
+
+// Number of bitset-width classes: widths 1, 2, 4, 8, 16, 32 words (P up to 2048).
+#define MCE_NCLASS 6
+#define MCE_MAX_P 2048
+#define MCE_MAX_WORKERS 8192
+
+__host__ __device__ inline int mce_class_of(int p) {   // smallest class whose 64*W >= p
+  int c = 0;
+  while (c < MCE_NCLASS - 1 && (64 << c) < p) c++;
+  return c;
+}
+
+// Control block: one per run, zeroed by the host before the first kernel.
+struct MceCtl {
+  u32 status;            // MCE_GRAPH_* | MCE_E_*
+  int max_degree;
+  int degeneracy;
+  int rounds;
+  int max_p;
+  int max_x;
+  int min_deg;           // peel: smallest alive degree at a level start
+  int pad0;
+  u64 isolated;          // roots of degree 0
+  u64 isolated_hash;     // sum of their clique hashes
+  int class_count[MCE_NCLASS];
+  int class_cursor[MCE_NCLASS];
+  int asize[2];          // peel: alive-list sizes (ping-pong)
+  int fsize[2];          // peel: frontier sizes (ping-pong)
+  u32 bar_count;         // grid barrier
+  u32 bar_gen;
+};
+
+// Worker-list state of one search launch (section 3.3 of the pages): a bitmap
+// of idle wavefront ids plus one wake flag per wavefront.
+struct MceWl {
+  u32 root_ctr;          // next first-level subtree to hand out (phase 1)
+  int n_busy;            // wavefronts that are searching or about to receive work
+  int n_waiting;         // wavefronts published in idle_bits (a hint for donors)
+  u32 done;              // 1: every wavefront is idle, or the launch is abandoned
+  u64 idle_bits[MCE_MAX_WORKERS / 64];
+  u32 flag[MCE_MAX_WORKERS];   // 1: a donor filled this wavefront's mailbox
+};
+
+// ---------------------------------------------------------------- hashing
+__device__ __forceinline__ u64 mce_mix64(u64 z) {
+  z ^= z >> 30;
+  z *= 0xBF58476D1CE4E5B9ULL;
+  z ^= z >> 27;
+  z *= 0x94D049BB133111EBULL;
+  z ^= z >> 31;
+  return z;
+}
+__device__ __forceinline__ u64 mce_vertex_term(int v) { return mce_mix64((u64)(long long)v + MCE_GOLDEN); }
+__device__ __forceinline__ u64 mce_clique_term(u64 sum, int k) { return mce_mix64(sum + (u64)k * MCE_GOLDEN); }
+
+// ---------------------------------------------------------------- lanes
+__device__ __forceinline__ int lane_id() { return __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u)); }
+__device__ __forceinline__ u64 ballot(bool p) { return __builtin_amdgcn_ballot_w64(p); }
+__device__ __forceinline__ int mbcnt(u64 m) {   // set bits of m below this lane
+  return __builtin_amdgcn_mbcnt_hi((u32)(m >> 32), __builtin_amdgcn_mbcnt_lo((u32)m, 0u));
+}
+__device__ __forceinline__ int uni(int x) { return __builtin_amdgcn_readfirstlane(x); }
+__device__ __forceinline__ u32 uni(u32 x) { return (u32)__builtin_amdgcn_readfirstlane((int)x); }
+__device__ __forceinline__ u64 uni(u64 x) {
+  u32 lo = (u32)__builtin_amdgcn_readfirstlane((int)(u32)x);
+  u32 hi = (u32)__builtin_amdgcn_readfirstlane((int)(u32)(x >> 32));
+  return ((u64)hi << 32) | lo;
+}
+__device__ __forceinline__ u64 read_lane(u64 x, int l) {
+  u32 lo = (u32)__builtin_amdgcn_readlane((int)(u32)x, l);
+  u32 hi = (u32)__builtin_amdgcn_readlane((int)(u32)(x >> 32), l);
+  return ((u64)hi << 32) | lo;
+}
+__device__ __forceinline__ int read_lane(int x, int l) { return __builtin_amdgcn_readlane(x, l); }
+
+// Whole-wave reductions with DPP row operations, result in every lane.
+// Must be called with all 64 lanes active.
+template <int CTRL, int ROWS>
+__device__ __forceinline__ u32 dpp_u32(u32 v) {
+  return (u32)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, ROWS, 0xF, false);
+}
+#define MCE_DPP_REDUCE(NAME, OP)                                   \
+  __device__ __forceinline__ u32 NAME(u32 x) {                     \
+    x = OP(x, dpp_u32<0xB1, 0xF>(x));   /* quad_perm 1,0,3,2 */    \
+    x = OP(x, dpp_u32<0x4E, 0xF>(x));   /* quad_perm 2,3,0,1 */    \
+    x = OP(x, dpp_u32<0x141, 0xF>(x));  /* row_half_mirror  */     \
+    x = OP(x, dpp_u32<0x140, 0xF>(x));  /* row_mirror       */     \
+    x = OP(x, dpp_u32<0x142, 0xA>(x));  /* row_bcast15 -> rows 1,3 */ \
+    x = OP(x, dpp_u32<0x143, 0xC>(x));  /* row_bcast31 -> rows 2,3 */ \
+    return (u32)__builtin_amdgcn_readlane((int)x, 63);            \
+  }
+__device__ __forceinline__ u32 op_max(u32 a, u32 b) { return a > b ? a : b; }
+__device__ __forceinline__ u32 op_add(u32 a, u32 b) { return a + b; }
+__device__ __forceinline__ u32 op_or(u32 a, u32 b) { return a | b; }
+MCE_DPP_REDUCE(wave_max_u32, op_max)
+MCE_DPP_REDUCE(wave_sum_u32, op_add)
+MCE_DPP_REDUCE(wave_or_u32, op_or)
+__device__ __forceinline__ u64 wave_sum_u64(u64 x) {   // via two 32-bit halves with carries
+  u32 lo = (u32)x, hi = (u32)(x >> 32);
+  // sum of lo halves can overflow 32 bits: split lo into 16-bit pieces
+  u32 l0 = wave_sum_u32(lo & 0xFFFFu);
+  u32 l1 = wave_sum_u32(lo >> 16);
+  u32 h = wave_sum_u32(hi);
+  return ((u64)h << 32) + ((u64)l1 << 16) + (u64)l0;
+}
+__device__ __forceinline__ int wave_min_i32_nonneg(int x) {   // x >= 0 in every lane
+  return (int)(0x7FFFFFFFu - wave_max_u32(0x7FFFFFFFu - (u32)x));
+}
+
+// ---------------------------------------------------------------- scoped atomics
+__device__ __forceinline__ u32 ld_relaxed(const u32* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ int ld_relaxed(const int* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ u64 ld_relaxed(const u64* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_relaxed(u32* p, u32 v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_release(u32* p, u32 v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void fence_release_agent() { __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent"); }
+__device__ __forceinline__ void fence_acquire_agent() { __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent"); }
+__device__ __forceinline__ void fence_acq_rel_agent() { __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "agent"); }
+
+// ---------------------------------------------------------------- CSR lookups
+// Is key in the sorted range ci[lo, hi)?
+__device__ __forceinline__ bool csr_range_has(const int* __restrict__ ci, int lo, int hi, int key) {
+  int len = hi - lo;
+  while (len > 0) {
+    int half = len >> 1;
+    int mid = lo + half;
+    if (ci[mid] < key) {
+      lo = mid + 1;
+      len -= half + 1;
+    } else {
+      len = half;
+    }
+  }
+  return lo < hi && ci[lo] == key;
+}
+
+// Are x and y adjacent? Searches the shorter of the two rows.
+__device__ __forceinline__ bool csr_adjacent(const int* __restrict__ rp, const int* __restrict__ ci,
+                                             int x, int y) {
+  int xa = rp[x], xb = rp[x + 1];
+  int ya = rp[y], yb = rp[y + 1];
+  if (xb - xa <= yb - ya) return csr_range_has(ci, xa, xb, y);
+  return csr_range_has(ci, ya, yb, x);
+}
+
+// "u comes after v" in the degeneracy order (round, id).
+__device__ __forceinline__ bool order_after(int ru, int u, int rv, int v) {
+  return ru > rv || (ru == rv && u > v);
+}
+
+__device__ __forceinline__ bool past_deadline(u64 deadline) { return wall_clock64() > deadline; }

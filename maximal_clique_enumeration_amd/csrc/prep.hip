@@ -1,0 +1,354 @@
+// Preprocessing before the search: input checks, the degeneracy order and the
+// split of every vertex's neighbourhood into later (P) and earlier (X) parts.
+//
+// "Parallelizing Maximal Clique Enumeration on GPUs" (arxiv 2212.01473v2):
+//  - section 2.1: the input is a simple undirected graph;
+//  - section 2.4 (degeneracy ordering): order the vertices so that each has at
+//    most d later neighbours; section 4.1 counts this preprocessing as timed work;
+//  - section 2.4, Algorithm 3: root v_i gets P = later neighbours, X = earlier.
+#include "mce_device.h"
+#include "mce_internal.h"
+
+#include <algorithm>
+
+// ------------------------------------------------------------------ validation
+// Pass 1: row_ptr is monotone and inside [0, nnz]; degrees; Delta.
+__global__ __launch_bounds__(256) void k_validate_rowptr(int n, long long nnz, const int* __restrict__ rp,
+                                                          MceCtl* ctl) {
+  u32 bad = 0;
+  int dmax = 0;
+  for (int v = blockIdx.x * blockDim.x + threadIdx.x; v < n; v += gridDim.x * blockDim.x) {
+    int a = rp[v], b = rp[v + 1];
+    if (a > b || a < 0 || (long long)b > nnz) bad |= 1u;   // MCE_GRAPH_ROWPTR
+    else dmax = max(dmax, b - a);
+  }
+  if (blockIdx.x == 0 && threadIdx.x == 0) {
+    if (rp[0] != 0 || (long long)rp[n] != nnz) bad |= 1u;
+  }
+  u32 b = wave_or_u32(bad);
+  u32 m = wave_max_u32((u32)dmax);
+  if (lane_id() == 0) {
+    if (b) atomicOr(&ctl->status, b);
+    if (m) atomicMax(&ctl->max_degree, (int)m);
+  }
+}
+
+// Pass 2 (only if pass 1 found nothing): ids in range, no loops, rows strictly
+// ascending, and every edge present in both directions. One wavefront per row.
+__global__ __launch_bounds__(256) void k_validate_cols(int n, const int* __restrict__ rp,
+                                                        const int* __restrict__ ci, MceCtl* ctl) {
+  if (ld_relaxed(&ctl->status) != 0) return;
+  const int lane = lane_id();
+  const int wave = (blockIdx.x * blockDim.x + threadIdx.x) / MCE_WAVE;
+  const int nwaves = gridDim.x * blockDim.x / MCE_WAVE;
+  u32 bad = 0;
+  for (int v = wave; v < n; v += nwaves) {
+    int a = rp[v], b = rp[v + 1];
+    for (int e = a + lane; e < b; e += MCE_WAVE) {
+      int u = ci[e];
+      if (u < 0 || u >= n) {
+        bad |= 2u;                                 // MCE_GRAPH_RANGE
+        continue;
+      }
+      if (u == v) bad |= 4u;                       // MCE_GRAPH_LOOP
+      if (e + 1 < b && ci[e + 1] <= u) bad |= 8u;  // MCE_GRAPH_ORDER
+      if (!csr_range_has(ci, rp[u], rp[u + 1], v)) bad |= 16u;  // MCE_GRAPH_ASYM
+    }
+  }
+  u32 bb = wave_or_u32(bad);
+  if (lane == 0 && bb) atomicOr(&ctl->status, bb);
+}
+
+// ------------------------------------------------------------------ k-core peel
+// Grid-wide barrier for a cooperative launch. Every wave passes an agent-scope
+// release before arriving and an acquire after leaving, because the 8 XCDs keep
+// separate L2 caches. Bounded: past the deadline it flags MCE_E_TIMEOUT and lets
+// the block go, and the caller checks the flag after every barrier.
+__device__ void grid_barrier(MceCtl* ctl, u64 deadline) {
+  fence_release_agent();
+  __syncthreads();
+  if (gridDim.x > 1) {
+    if (threadIdx.x == 0) {
+      u32 gen = __hip_atomic_load(&ctl->bar_gen, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT);
+      u32 arrived = __hip_atomic_fetch_add(&ctl->bar_count, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT) + 1;
+      if (arrived == gridDim.x) {
+        __hip_atomic_store(&ctl->bar_count, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(&ctl->bar_gen, gen + 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+      } else {
+        u32 spins = 0;
+        while (__hip_atomic_load(&ctl->bar_gen, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) == gen) {
+          __builtin_amdgcn_s_sleep(2);
+          if ((++spins & 1023u) == 0 && past_deadline(deadline)) {
+            atomicOr(&ctl->status, MCE_E_TIMEOUT);
+            break;
+          }
+        }
+      }
+    }
+    __syncthreads();
+  }
+  fence_acquire_agent();
+}
+
+// Round-synchronous peel. Level k: every alive vertex with current degree <= k
+// leaves in one round (rnd = round, core = k); its alive neighbours lose one
+// degree each, and a neighbour whose degree falls from k+1 to k joins the next
+// round of the same level. When a round removes nothing, k becomes the smallest
+// alive degree. Launched cooperatively; gridDim 1 for small graphs.
+__global__ __launch_bounds__(256) void k_peel(int n, const int* __restrict__ rp, const int* __restrict__ ci,
+                                               int* deg, int* rnd, int* core, int* alive0, int* alive1,
+                                               int* front0, int* front1, MceCtl* ctl, u64 budget) {
+  if (ld_relaxed(&ctl->status) != 0) return;   // rejected input: nothing to order
+  const u64 deadline = wall_clock64() + budget;
+  const int gtid = blockIdx.x * blockDim.x + threadIdx.x;
+  const int gsize = gridDim.x * blockDim.x;
+  const int lane = lane_id();
+  const int wave = gtid / MCE_WAVE;
+  const int nwaves = gsize / MCE_WAVE;
+  int* alive[2] = {alive0, alive1};
+  int* front[2] = {front0, front1};
+
+  for (int v = gtid; v < n; v += gsize) {
+    deg[v] = rp[v + 1] - rp[v];
+    rnd[v] = -1;
+    alive0[v] = v;
+  }
+  if (gtid == 0) {
+    ctl->asize[0] = n;
+    ctl->asize[1] = 0;
+    ctl->fsize[0] = 0;
+    ctl->fsize[1] = 0;
+    ctl->min_deg = 0x7FFFFFFF;
+  }
+  grid_barrier(ctl, deadline);
+
+  int cur = 0, fb = 0, nf = 0, k = 0, round = 0;
+  int na = n;
+  for (;;) {
+    if (ld_relaxed(&ctl->status) & MCE_E_TIMEOUT) return;
+    if (nf == 0) {
+      // new level: compact the alive list and find the smallest alive degree
+      const int* src = alive[cur];
+      int* dst = alive[cur ^ 1];
+      int mn = 0x7FFFFFFF;
+      for (int base = wave * MCE_WAVE; base < na; base += nwaves * MCE_WAVE) {
+        int i = base + lane;
+        bool keep = false;
+        int v = 0;
+        if (i < na) {
+          v = src[i];
+          keep = rnd[v] < 0;
+          if (keep) mn = min(mn, deg[v]);
+        }
+        u64 m = ballot(keep);
+        int pos = 0;
+        if (lane == 0 && m) pos = atomicAdd(&ctl->asize[cur ^ 1], __popcll(m));
+        pos = read_lane(pos, 0);
+        if (keep) dst[pos + mbcnt(m)] = v;
+      }
+      int wmn = wave_min_i32_nonneg(mn);
+      if (lane == 0 && wmn != 0x7FFFFFFF) atomicMin(&ctl->min_deg, wmn);
+      grid_barrier(ctl, deadline);
+      if (ld_relaxed(&ctl->status) & MCE_E_TIMEOUT) return;
+      cur ^= 1;
+      na = ld_relaxed(&ctl->asize[cur]);
+      if (na == 0) break;
+      k = ld_relaxed(&ctl->min_deg);
+      // the frontier of the level's first round
+      const int* al = alive[cur];
+      int* fr = front[fb];
+      for (int base = wave * MCE_WAVE; base < na; base += nwaves * MCE_WAVE) {
+        int i = base + lane;
+        bool in = false;
+        int v = 0;
+        if (i < na) {
+          v = al[i];
+          in = deg[v] <= k;
+        }
+        u64 m = ballot(in);
+        int pos = 0;
+        if (lane == 0 && m) pos = atomicAdd(&ctl->fsize[fb], __popcll(m));
+        pos = read_lane(pos, 0);
+        if (in) fr[pos + mbcnt(m)] = v;
+      }
+      if (gtid == 0) ctl->asize[cur ^ 1] = 0;   // read by nobody until the next level
+      grid_barrier(ctl, deadline);
+      if (ld_relaxed(&ctl->status) & MCE_E_TIMEOUT) return;
+      nf = ld_relaxed(&ctl->fsize[fb]);
+    }
+    // the round: mark the frontier removed
+    const int* fr = front[fb];
+    for (int i = gtid; i < nf; i += gsize) {
+      int v = fr[i];
+      rnd[v] = round;
+      core[v] = k;
+    }
+    if (gtid == 0) {
+      ctl->fsize[fb ^ 1] = 0;
+      ctl->min_deg = 0x7FFFFFFF;
+    }
+    grid_barrier(ctl, deadline);
+    if (ld_relaxed(&ctl->status) & MCE_E_TIMEOUT) return;
+    // ... and take one degree from each alive neighbour
+    int* nx = front[fb ^ 1];
+    for (int i = wave; i < nf; i += nwaves) {
+      int v = fr[i];
+      int a = rp[v], b = rp[v + 1];
+      for (int base = a; base < b; base += MCE_WAVE) {
+        int e = base + lane;
+        bool joins = false;
+        int u = 0;
+        if (e < b) {
+          u = ci[e];
+          if (__hip_atomic_load(&rnd[u], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < 0) {
+            int old = atomicSub(&deg[u], 1);
+            joins = old == k + 1;
+          }
+        }
+        u64 m = ballot(joins);
+        int pos = 0;
+        if (lane == 0 && m) pos = atomicAdd(&ctl->fsize[fb ^ 1], __popcll(m));
+        pos = read_lane(pos, 0);
+        if (joins) nx[pos + mbcnt(m)] = u;
+      }
+    }
+    grid_barrier(ctl, deadline);
+    if (ld_relaxed(&ctl->status) & MCE_E_TIMEOUT) return;
+    fb ^= 1;
+    nf = ld_relaxed(&ctl->fsize[fb]);
+    round++;
+  }
+  if (gtid == 0) {
+    ctl->rounds = round;
+    ctl->degeneracy = k;
+  }
+}
+
+// ------------------------------------------------------------------ orientation
+// Per root: |P| = later neighbours, |X| = earlier ones. Degree-0 roots are
+// maximal cliques of size 1 and are counted here. Roots with |P| >= 1 are
+// counted per bitset-width class.
+__global__ __launch_bounds__(256) void k_orient(int n, const int* __restrict__ rp, const int* __restrict__ ci,
+                                                 const int* __restrict__ rnd, const int* __restrict__ roots,
+                                                 int nroots, int* pcount, MceCtl* ctl) {
+  if (ld_relaxed(&ctl->status) != 0) return;
+  const int lane = lane_id();
+  const int gsize = gridDim.x * blockDim.x;
+  int cnt = roots ? nroots : n;
+  u64 iso = 0, iso_hash = 0;
+  int pmax = 0, xmax = 0;
+  u32 lim = 0;
+  int ccount[MCE_NCLASS];
+  for (int c = 0; c < MCE_NCLASS; c++) ccount[c] = 0;
+  for (int base = blockIdx.x * blockDim.x; base < cnt; base += gsize) {
+    int i = base + threadIdx.x;
+    int p = 0;
+    int v = i < cnt ? (roots ? roots[i] : i) : 0;
+    if (i < cnt && (v < 0 || v >= n)) {   // caller-supplied root out of range: flag it, touch nothing
+      lim |= 2u;
+      pcount[i] = 0;
+    } else if (i < cnt) {
+      int a = rp[v], b = rp[v + 1];
+      int rv = rnd[v];
+      for (int e = a; e < b; e++) {
+        int u = ci[e];
+        p += order_after(rnd[u], u, rv, v) ? 1 : 0;
+      }
+      pcount[i] = p;
+      if (b == a) {
+        iso++;
+        iso_hash += mce_clique_term(mce_vertex_term(v), 1);
+      }
+      pmax = max(pmax, p);
+      xmax = max(xmax, (b - a) - p);
+      if (p > MCE_MAX_P) lim |= 1u;
+    }
+    for (int c = 0; c < MCE_NCLASS; c++) {
+      u64 m = ballot(i < cnt && p > 0 && p <= MCE_MAX_P && mce_class_of(p) == c);
+      ccount[c] += __popcll(m);
+    }
+  }
+  u64 wiso = wave_sum_u64(iso);
+  u64 whash = wave_sum_u64(iso_hash);
+  u32 wpm = wave_max_u32((u32)pmax);
+  u32 wxm = wave_max_u32((u32)xmax);
+  u32 wl = wave_or_u32(lim);
+  if (lane == 0) {
+    if (wiso) {
+      atomicAdd(&ctl->isolated, wiso);
+      atomicAdd(&ctl->isolated_hash, whash);
+    }
+    atomicMax(&ctl->max_p, (int)wpm);
+    atomicMax(&ctl->max_x, (int)wxm);
+    if (wl & 1u) atomicOr(&ctl->status, MCE_E_LIMIT);
+    if (wl & 2u) atomicOr(&ctl->status, MCE_E_ROOTS);
+    for (int c = 0; c < MCE_NCLASS; c++)
+      if (ccount[c]) atomicAdd(&ctl->class_count[c], ccount[c]);
+  }
+}
+
+// Scatter the roots with |P| >= 1 into one list per class, starting at off[c].
+__global__ __launch_bounds__(256) void k_bucket(int n, const int* __restrict__ roots, int nroots,
+                                                 const int* __restrict__ pcount, ClassOffsets off,
+                                                 int* lists, MceCtl* ctl) {
+  if (ld_relaxed(&ctl->status) != 0) return;
+  const int lane = lane_id();
+  const int gsize = gridDim.x * blockDim.x;
+  int cnt = roots ? nroots : n;
+  for (int base = blockIdx.x * blockDim.x; base < cnt; base += gsize) {
+    int i = base + threadIdx.x;
+    int p = i < cnt ? pcount[i] : 0;
+    int c = (p > 0 && p <= MCE_MAX_P) ? mce_class_of(p) : -1;
+    for (int cc = 0; cc < MCE_NCLASS; cc++) {
+      u64 m = ballot(c == cc);
+      if (!m) continue;
+      int pos = 0;
+      if (lane == 0) pos = atomicAdd(&ctl->class_cursor[cc], __popcll(m));
+      pos = read_lane(pos, 0);
+      if (c == cc) lists[off.off[cc] + pos + mbcnt(m)] = roots ? roots[i] : i;
+    }
+  }
+}
+
+// ------------------------------------------------------------------ launchers
+hipError_t mce_launch_validate(int n, long long nnz, const int* rp, const int* ci, MceCtl* ctl,
+                               int blocks, hipStream_t s) {
+  int nb = max(1, min(blocks, (n + 255) / 256));
+  hipLaunchKernelGGL(k_validate_rowptr, dim3(nb), dim3(256), 0, s, n, nnz, rp, ctl);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  int nbw = (int)std::max(1LL, std::min((long long)blocks, ((long long)n + 3) / 4));
+  hipLaunchKernelGGL(k_validate_cols, dim3(nbw), dim3(256), 0, s, n, rp, ci, ctl);
+  return hipGetLastError();
+}
+
+hipError_t mce_launch_peel(int n, const int* rp, const int* ci, int* deg, int* rnd, int* core, int* alive0,
+                           int* alive1, int* front0, int* front1, MceCtl* ctl, u64 budget, int blocks,
+                           hipStream_t s) {
+  void* args[] = {&n, (void*)&rp, (void*)&ci, &deg, &rnd, &core, &alive0, &alive1,
+                  &front0, &front1, &ctl, &budget};
+  return hipLaunchCooperativeKernel((const void*)k_peel, dim3(blocks), dim3(256), args, 0, s);
+}
+
+int mce_peel_max_blocks(int num_cu) {
+  int per_cu = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, (const void*)k_peel, 256, 0) != hipSuccess)
+    return 1;
+  return max(1, per_cu * num_cu);
+}
+
+hipError_t mce_launch_orient(int n, const int* rp, const int* ci, const int* rnd, const int* roots, int nroots,
+                             int* pcount, MceCtl* ctl, int blocks, hipStream_t s) {
+  int cnt = roots ? nroots : n;
+  int nb = max(1, min(blocks, (cnt + 255) / 256));
+  hipLaunchKernelGGL(k_orient, dim3(nb), dim3(256), 0, s, n, rp, ci, rnd, roots, nroots, pcount, ctl);
+  return hipGetLastError();
+}
+
+hipError_t mce_launch_bucket(int n, const int* roots, int nroots, const int* pcount, ClassOffsets off, int* lists,
+                             MceCtl* ctl, int blocks, hipStream_t s) {
+  int cnt = roots ? nroots : n;
+  int nb = max(1, min(blocks, (cnt + 255) / 256));
+  hipLaunchKernelGGL(k_bucket, dim3(nb), dim3(256), 0, s, n, roots, nroots, pcount, off, lists, ctl);
+  return hipGetLastError();
+}

@@ -1,0 +1,216 @@
+"""GPU parity: the HIP engine, called through the C ABI, against the oracle.
+
+Every case compares count, histogram and hash element by element (integer work:
+the bar is bit-exact). Inputs are seeded synthetic graphs from mce_inputs.
+"""
+import numpy as np
+import pytest
+
+import mce_inputs as mi
+import oracle
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+if not torch.cuda.is_available():   # pragma: no cover - CPU-only runs deselect these
+    pytest.skip("needs a GPU", allow_module_level=True)
+
+import maximal_clique_enumeration_amd as mce  # noqa: E402
+
+DEV = torch.device("cuda", 0)
+
+
+@pytest.fixture(scope="module")
+def eng():
+    if not mce.lib_built():
+        from maximal_clique_enumeration_amd import build
+        build.build()
+    e = mce.Engine(device=0, timeout_ms=60000)
+    yield e
+    e.close()
+
+
+def on_gpu(g):
+    return torch.from_numpy(g.row_ptr).to(DEV), torch.from_numpy(g.col_idx).to(DEV)
+
+
+def check(eng, g, roots=None):
+    rp, ci = on_gpu(g)
+    r = None if roots is None else torch.from_numpy(np.asarray(roots, np.int32)).to(DEV)
+    got = eng.run(rp, ci, roots=r)
+    want = oracle.mce(g.n, g.row_ptr, g.col_idx, roots=roots)
+    assert want.complete
+    assert got.count == want.count, (g.name, got, want)
+    assert got.hist == want.hist, (g.name, got.hist, want.hist)
+    assert got.hash == want.hash, (g.name, hex(got.hash), hex(want.hash))
+    return got
+
+
+# ------------------------------------------------------------------ small worked cases
+def test_fig1a(eng):
+    got = check(eng, mi.fig1a())
+    assert got.count == 2 and got.hist == [0, 0, 0, 1, 1]
+
+
+@pytest.mark.parametrize("n", [1, 2, 3, 17, 64, 65, 66, 129, 130, 200])
+def test_complete(eng, n):
+    got = check(eng, mi.complete(n))
+    assert got.count == 1 and len(got.hist) == n + 1
+
+
+@pytest.mark.parametrize("n", [1, 5, 1000])
+def test_empty(eng, n):
+    got = check(eng, mi.empty(n))
+    assert got.count == n
+
+
+@pytest.mark.parametrize("n", [4, 7, 100, 5000])
+def test_cycle(eng, n):
+    got = check(eng, mi.cycle(n))
+    assert got.count == n
+
+
+@pytest.mark.parametrize("k", [1, 2, 5, 9, 12])
+def test_moon_moser(eng, k):
+    got = check(eng, mi.moon_moser(3 * k))
+    assert got.count == 3 ** k
+
+
+def test_moon_moser_45_full(eng):
+    """The bench workload, whole graph: 3^15 maximal cliques of size 15."""
+    got = check(eng, mi.config_graph(1))
+    assert got.count == 14_348_907 and got.hist[15] == 14_348_907
+
+
+@pytest.mark.parametrize("seed", range(40))
+def test_random_small(eng, seed):
+    rng = np.random.default_rng(seed)
+    n = int(rng.integers(1, 90))
+    p = float(rng.choice([0.05, 0.2, 0.4, 0.6, 0.8, 0.95]))
+    check(eng, mi.random_small(n, p, 500 + seed))
+
+
+@pytest.mark.parametrize("n,p,seed", [(300, 0.3, 1), (200, 0.5, 2), (160, 0.7, 3), (400, 0.4, 4),
+                                      (300, 0.5, 4)])
+def test_random_dense(eng, n, p, seed):
+    """Roots with |P| above 64 and 128 (bitset widths 2 and 4 words), deep trees."""
+    check(eng, mi.random_small(n, p, seed))
+
+
+@pytest.mark.parametrize("sizes", [[2, 3, 4, 5], [1] * 70, [3, 1, 4, 1, 5, 9, 2, 6],
+                                   [3] * 5 + [1] * 300, [2] * 10 + [1] * 600, [2] * 3 + [1] * 1200])
+def test_multipartite(eng, sizes):
+    """Complete multipartite graphs: prod(sizes) cliques of size len(sizes); the
+    large ones put |P| near 300, 600 and 1200 (widths 8, 16 and 32 words)."""
+    got = check(eng, mi.complete_multipartite(sizes))
+    assert got.count == int(np.prod(sizes))
+
+
+def test_er_2000(eng):
+    """The small configuration: G(2000, 0.01), seed 1."""
+    check(eng, mi.config_graph(0))
+
+
+def test_chung_lu_with_planted_cliques(eng):
+    """A power-law graph with overlapping planted cliques: long X_X arrays."""
+    check(eng, mi.chung_lu(20000, 12.0, 2.3, None, 3, planted=40, planted_min=10, planted_max=30))
+
+
+def test_disjoint_union_and_isolated(eng):
+    g = mi.disjoint_union(mi.moon_moser(15), mi.empty(7), mi.cycle(9), mi.complete(70))
+    check(eng, g)
+
+
+# ------------------------------------------------------------------ ordering
+@pytest.mark.parametrize("make", [lambda: mi.config_graph(0), lambda: mi.moon_moser(45),
+                                  lambda: mi.chung_lu(30000, 15.0, 2.2, None, 9, planted=10),
+                                  lambda: mi.path(40), lambda: mi.random_small(500, 0.3, 4)])
+def test_ordering_matches_oracle(eng, make):
+    g = make()
+    rp, ci = on_gpu(g)
+    eng.run(rp, ci)
+    core, rnd = eng.ordering(g.n)
+    ocore, ornd, d = oracle.peel(g.n, g.row_ptr, g.col_idx)
+    assert np.array_equal(core.cpu().numpy(), ocore)
+    assert np.array_equal(rnd.cpu().numpy(), ornd)
+    info = eng.graph_info()
+    assert info["degeneracy"] == d and info["rounds"] == int(ornd.max()) + 1
+    assert info["max_degree"] == int(g.degrees().max())
+
+
+# ------------------------------------------------------------------ root subsets
+def test_root_subsets(eng):
+    g = mi.chung_lu(20000, 12.0, 2.3, None, 5, planted=20, planted_min=8, planted_max=25)
+    rng = np.random.default_rng(3)
+    roots = rng.choice(g.n, size=3000, replace=False).astype(np.int32)
+    check(eng, g, roots=roots)
+    check(eng, g, roots=roots[:1])
+    check(eng, g, roots=np.zeros(0, np.int32))
+
+
+# ------------------------------------------------------------------ stress matrix
+@pytest.mark.parametrize("worker_list", [False, True])
+@pytest.mark.parametrize("donate_min_p", [1, 10, 1000])
+@pytest.mark.parametrize("max_workers", [1, 2, 7, 0])
+def test_stress_matrix(worker_list, donate_min_p, max_workers):
+    graphs = [mi.moon_moser(30), mi.random_small(120, 0.5, 8),
+              mi.chung_lu(5000, 10.0, 2.3, None, 2, planted=10, planted_min=8, planted_max=20)]
+    with mce.Engine(device=0, worker_list=worker_list, donate_min_p=donate_min_p,
+                    max_workers=max_workers, timeout_ms=60000) as e:
+        for g in graphs:
+            got = check(e, g)
+        st = e.stats()
+        if worker_list and donate_min_p == 1 and max_workers in (2, 7, 0):
+            assert st["donations"] > 0
+
+
+def test_hbm_staging_and_repeats():
+    g = mi.moon_moser(36)
+    want = oracle.mce(g.n, g.row_ptr, g.col_idx)
+    rp, ci = on_gpu(g)
+    for hbm in (False, True):
+        with mce.Engine(device=0, hbm_staging=hbm, timeout_ms=60000) as e:
+            for _ in range(5):
+                assert e.run(rp, ci).key() == want.key()
+
+
+# ------------------------------------------------------------------ input checks
+def _bad(eng, n, rp, ci):
+    trp = torch.from_numpy(np.asarray(rp, np.int32)).to(DEV)
+    tci = torch.from_numpy(np.asarray(ci, np.int32)).to(DEV)
+    with pytest.raises(mce.MceError) as ex:
+        eng.run(trp, tci)
+    assert ex.value.status == mce.MCE_ERR_GRAPH
+    return eng.graph_info()["graph_errors"]
+
+
+def test_rejects_malformed(eng):
+    g = mi.random_small(12, 0.5, 5)
+    rp, ci = g.row_ptr.copy(), g.col_idx.copy()
+    bad = ci.copy(); bad[0] = g.n
+    assert _bad(eng, g.n, rp, bad) & mce.MCE_GRAPH_RANGE
+    bad = ci.copy(); bad[rp[0]] = 0
+    assert _bad(eng, g.n, rp, bad) & (mce.MCE_GRAPH_LOOP | mce.MCE_GRAPH_ASYM)
+    r0 = int(np.argmax(np.diff(rp) >= 2))
+    bad = ci.copy(); bad[rp[r0]], bad[rp[r0] + 1] = bad[rp[r0] + 1], bad[rp[r0]]
+    assert _bad(eng, g.n, rp, bad) & mce.MCE_GRAPH_ORDER
+    badrp = rp.copy(); badrp[3] = badrp[4] + 1
+    assert _bad(eng, g.n, badrp, ci) & mce.MCE_GRAPH_ROWPTR
+    u, w = map(int, g.edge_list()[0])
+    keep = np.ones(ci.size, bool)
+    keep[rp[u] + int(np.nonzero(ci[rp[u]:rp[u + 1]] == w)[0][0])] = False
+    rp2 = rp.copy(); rp2[u + 1:] -= 1
+    assert _bad(eng, g.n, rp2, ci[keep]) == mce.MCE_GRAPH_ASYM
+    # the engine still works afterwards
+    check(eng, g)
+
+
+def test_bad_roots_and_empty_graph(eng):
+    g = mi.cycle(10)
+    rp, ci = on_gpu(g)
+    with pytest.raises(mce.MceError) as ex:
+        eng.run(rp, ci, roots=torch.tensor([3, 10], dtype=torch.int32, device=DEV))
+    assert ex.value.status == mce.MCE_ERR_ARG
+    e0 = mi.empty(0)
+    got = eng.run(*on_gpu(e0))
+    assert got.count == 0 and got.hist == [] and got.hash == 0
