@@ -229,7 +229,7 @@ mce_status run_impl(mce_engine* e, int32_t n, int64_t nnz, const int32_t* row_pt
     if ((h = ensure(e->slots, L.bytes * (size_t)nw)) != hipSuccess) return hip_fail(e, h, "worker slots");
     if ((h = ensure(e->stats, (size_t)nw * MCE_NSTAT * sizeof(u64))) != hipSuccess)
       return hip_fail(e, h, "stats buffer");
-    if ((h = mce_launch_wl_init(dp<MceWl>(e->wl), nw, s)) != hipSuccess) return hip_fail(e, h, "wl init");
+    if ((h = mce_launch_wl_init(dp<MceWl>(e->wl), s)) != hipSuccess) return hip_fail(e, h, "wl init");
     SearchParams prm{};
     prm.rp = row_ptr;
     prm.ci = col_idx;

@@ -48,12 +48,15 @@ struct MceCtl {
 };
 
 // Worker-list state of one search launch (section 3.3 of the pages): a bitmap
-// of idle wavefront ids plus one wake flag per wavefront.
+// of idle wavefront ids plus one wake flag per wavefront. All zero at launch.
+// Termination does not assume that every wavefront of the grid is resident: a
+// wavefront counts in n_active only while it holds a task or is about to take a
+// first-level subtree, so waves that start late find the roots gone and leave.
 struct MceWl {
   u32 root_ctr;          // next first-level subtree to hand out (phase 1)
-  int n_busy;            // wavefronts that are searching or about to receive work
+  int n_active;          // wavefronts holding (or about to take) a task
   int n_waiting;         // wavefronts published in idle_bits (a hint for donors)
-  u32 done;              // 1: every wavefront is idle, or the launch is abandoned
+  u32 done;              // 1: roots exhausted and no task held anywhere, or abandoned
   u64 idle_bits[MCE_MAX_WORKERS / 64];
   u32 flag[MCE_MAX_WORKERS];   // 1: a donor filled this wavefront's mailbox
 };

@@ -67,8 +67,8 @@ hipError_t mce_launch_orient(int n, const int* rp, const int* ci, const int* rnd
 hipError_t mce_launch_bucket(int n, const int* roots, int nroots, const int* pcount, ClassOffsets off, int* lists,
                              MceCtl* ctl, int blocks, hipStream_t s);
 
-// Largest cooperative grid for the search kernel of a class (0 on error).
+// Resident wavefronts of the search kernel of a class over the whole chip (0 on error).
 int mce_search_max_workers(int wclass, bool hbm_staging, int num_cu);
 hipError_t mce_launch_search(int wclass, bool hbm_staging, const SearchParams& prm, hipStream_t s);
 
-hipError_t mce_launch_wl_init(MceWl* wl, int nworkers, hipStream_t s);
+hipError_t mce_launch_wl_init(MceWl* wl, hipStream_t s);

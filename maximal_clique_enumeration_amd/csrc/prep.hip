@@ -234,7 +234,7 @@ __global__ __launch_bounds__(256) void k_orient(int n, const int* __restrict__ r
   if (ld_relaxed(&ctl->status) != 0) return;
   const int lane = lane_id();
   const int gsize = gridDim.x * blockDim.x;
-  int cnt = roots ? nroots : n;
+  int cnt = nroots;   // roots == NULL: the identity list 0..nroots-1
   u64 iso = 0, iso_hash = 0;
   int pmax = 0, xmax = 0;
   u32 lim = 0;
@@ -294,7 +294,7 @@ __global__ __launch_bounds__(256) void k_bucket(int n, const int* __restrict__ r
   if (ld_relaxed(&ctl->status) != 0) return;
   const int lane = lane_id();
   const int gsize = gridDim.x * blockDim.x;
-  int cnt = roots ? nroots : n;
+  int cnt = nroots;   // roots == NULL: the identity list 0..nroots-1
   for (int base = blockIdx.x * blockDim.x; base < cnt; base += gsize) {
     int i = base + threadIdx.x;
     int p = i < cnt ? pcount[i] : 0;
@@ -330,16 +330,19 @@ hipError_t mce_launch_peel(int n, const int* rp, const int* ci, int* deg, int* r
   return hipLaunchCooperativeKernel((const void*)k_peel, dim3(blocks), dim3(256), args, 0, s);
 }
 
+// The peel's grid barrier needs every block resident: stay well inside the
+// occupancy limit (two 256-thread blocks per CU keep the streaming passes at
+// full bandwidth).
 int mce_peel_max_blocks(int num_cu) {
   int per_cu = 0;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, (const void*)k_peel, 256, 0) != hipSuccess)
     return 1;
-  return max(1, per_cu * num_cu);
+  return max(1, min(per_cu, 2) * num_cu);
 }
 
 hipError_t mce_launch_orient(int n, const int* rp, const int* ci, const int* rnd, const int* roots, int nroots,
                              int* pcount, MceCtl* ctl, int blocks, hipStream_t s) {
-  int cnt = roots ? nroots : n;
+  int cnt = nroots;   // roots == NULL: the identity list 0..nroots-1
   int nb = max(1, min(blocks, (cnt + 255) / 256));
   hipLaunchKernelGGL(k_orient, dim3(nb), dim3(256), 0, s, n, rp, ci, rnd, roots, nroots, pcount, ctl);
   return hipGetLastError();
@@ -347,7 +350,7 @@ hipError_t mce_launch_orient(int n, const int* rp, const int* ci, const int* rnd
 
 hipError_t mce_launch_bucket(int n, const int* roots, int nroots, const int* pcount, ClassOffsets off, int* lists,
                              MceCtl* ctl, int blocks, hipStream_t s) {
-  int cnt = roots ? nroots : n;
+  int cnt = nroots;   // roots == NULL: the identity list 0..nroots-1
   int nb = max(1, min(blocks, (cnt + 255) / 256));
   hipLaunchKernelGGL(k_bucket, dim3(nb), dim3(256), 0, s, n, roots, nroots, pcount, off, lists, ctl);
   return hipGetLastError();

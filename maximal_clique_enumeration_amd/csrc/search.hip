@@ -1,6 +1,6 @@
 // The search: Bron-Kerbosch with pivoting over independent first-level subtrees,
-// one wavefront per subtree, as a single persistent cooperative launch per
-// bitset-width class.
+// one wavefront per subtree, as a single persistent launch per bitset-width
+// class.
 //
 // "Parallelizing Maximal Clique Enumeration on GPUs" (arxiv 2212.01473v2):
 //  - section 2.3, Algorithm 2: branch on P - N(pivot); after a branch on v,
@@ -37,13 +37,16 @@ struct Dims {
 };
 
 // ------------------------------------------------------------------ worker list
-// Receiver side (section 3.3): give up the busy count; if this was the last busy
-// wavefront, end the launch; else publish this id and spin on the wake flag with
-// exponential back-off. Returns 1 with a task in the mailbox, 0 to exit.
+// Receiver side (section 3.3): give up this wave's share of n_active. The wave
+// that brings it to zero after the roots ran out ends the launch (no task is
+// held anywhere and none can appear, since only active waves donate). Any other
+// wave publishes its id and spins on its wake flag with exponential back-off.
+// Returns 1 with a task in the mailbox (the donor re-counted this wave as
+// active), 0 to exit.
 __device__ int wl_wait(MceWl* wl, int wid, u64 deadline, u32* status) {
   int res = 0;
   if (lane_id() == 0) {
-    int left = __hip_atomic_fetch_add(&wl->n_busy, -1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT) - 1;
+    int left = __hip_atomic_fetch_add(&wl->n_active, -1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT) - 1;
     if (left <= 0) {
       if (left < 0) atomicOr(status, MCE_E_PROTO);
       st_release(&wl->done, 1u);
@@ -75,7 +78,9 @@ __device__ int wl_wait(MceWl* wl, int wid, u64 deadline, u32* status) {
   return res;
 }
 
-// Donor side: take one idle wavefront out of the bitmap, or -1.
+// Donor side: take one idle wavefront out of the bitmap, or -1. The claimed
+// wave is counted active before the donor can ever give up its own share, so
+// n_active cannot reach zero while the donated branch is in flight.
 __device__ int wl_claim(MceWl* wl, int wid, int nworkers) {
   int r = -1;
   if (lane_id() == 0) {
@@ -99,7 +104,7 @@ __device__ int wl_claim(MceWl* wl, int wid, int nworkers) {
       }
       if (r >= 0) {
         __hip_atomic_fetch_add(&wl->n_waiting, -1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __hip_atomic_fetch_add(&wl->n_busy, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_fetch_add(&wl->n_active, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
     }
   }
@@ -215,6 +220,9 @@ __global__ __launch_bounds__(64) void k_search(SearchParams prm) {
   const u64 t_start = wall_clock64();
   bool phase2 = false;
   bool abort = false;
+  // this wave is active until phase 1 finds the roots exhausted (wl_wait gives
+  // the share back)
+  if (lane == 0) __hip_atomic_fetch_add(&wl->n_active, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 
   for (;;) {
     // ---------------------------------------------------------- get a task
@@ -513,17 +521,16 @@ __global__ __launch_bounds__(64) void k_search(SearchParams prm) {
   }
 }
 
-// Worker-list reset before a launch: everything zero, every wavefront busy.
-__global__ void k_wl_init(MceWl* wl, int nworkers) {
+// Worker-list reset before a launch: every word zero.
+__global__ void k_wl_init(MceWl* wl) {
   u32* w = (u32*)wl;
   const int nw = (int)(sizeof(MceWl) / 4);
   for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < nw; i += gridDim.x * blockDim.x) w[i] = 0;
-  if (blockIdx.x == 0 && threadIdx.x == 0) wl->n_busy = nworkers;
 }
 
 // ------------------------------------------------------------------ host side
-hipError_t mce_launch_wl_init(MceWl* wl, int nworkers, hipStream_t s) {
-  hipLaunchKernelGGL(k_wl_init, dim3(1), dim3(1024), 0, s, wl, nworkers);
+hipError_t mce_launch_wl_init(MceWl* wl, hipStream_t s) {
+  hipLaunchKernelGGL(k_wl_init, dim3(1), dim3(1024), 0, s, wl);
   return hipGetLastError();
 }
 
@@ -605,5 +612,6 @@ hipError_t mce_launch_search(int wclass, bool hbm, const SearchParams& prm, hipS
   size_t lds = search_lds(wclass, hbm);
   SearchParams p = prm;
   void* args[] = {&p};
-  return hipLaunchCooperativeKernel(fn, dim3(prm.nworkers), dim3(64), args, (unsigned)lds, s);
+  // an ordinary launch: the worker list does not need every wave resident
+  return hipLaunchKernel(fn, dim3(prm.nworkers), dim3(64), args, (unsigned)lds, s);
 }
