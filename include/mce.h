@@ -21,9 +21,10 @@
  * Method (all on the GPU): a k-core peel gives a degeneracy order (section 2.4);
  * every vertex roots an independent first-level subtree (section 2.4, Algorithm
  * 3) searched depth-first by one wavefront with Bron-Kerbosch pivoting (section
- * 2.3, Algorithm 2) over a bit-encoded partial induced subgraph (section 3.4) and
- * a compact excluded set (section 3.5); idle wavefronts receive branches from
- * busy ones through a worker list (section 3.3).
+ * 2.3, Algorithm 2) over a bit-encoded partial or full induced subgraph (section
+ * 3.4, built per root into device memory before the search) and a compact
+ * excluded set (section 3.5); idle wavefronts receive branches from busy ones
+ * through a worker list (section 3.3).
  *
  * Threading: an engine belongs to one host thread at a time. Engines are
  * independent of each other. Every call returns an mce_status; no call throws.
@@ -64,6 +65,15 @@ typedef enum {
                                     when they fit in LDS (section 3.4 data in device memory) */
 #define MCE_FLAG_PHASE_TIMES 2u  /* record per-phase GPU times in mce_run_stats */
 
+/* mce_config.subgraph: how each subtree's induced subgraph is encoded (section
+   3.4). Partial: bit rows for P x P only, edges between P and X looked up in the
+   CSR, pivot drawn from P u X_P (section 3.5, last paragraph). Full: bit rows for
+   (P u X) x P, pivot drawn from all of P u X. Auto follows section 4.5: partial
+   when Delta / d > 200, else full. */
+#define MCE_SUBGRAPH_AUTO 0
+#define MCE_SUBGRAPH_PARTIAL 1
+#define MCE_SUBGRAPH_FULL 2
+
 typedef struct {
   uint32_t struct_size;   /* sizeof(mce_config); 0 is taken as the current size */
   int32_t device;         /* HIP device ordinal; -1: the device current at mce_create */
@@ -74,6 +84,7 @@ typedef struct {
   int32_t max_workers;    /* 0: as many wavefronts as are resident; else at most this many */
   int64_t timeout_ms;     /* wall-clock limit of one search launch; 0: 120000 */
   uint32_t flags;         /* MCE_FLAG_* */
+  int32_t subgraph;       /* MCE_SUBGRAPH_* (0 = auto) */
 } mce_config;
 
 /* Facts about the last graph run. */
@@ -88,13 +99,14 @@ typedef struct {
   int64_t isolated;       /* roots with degree 0, each a maximal clique of size 1 */
   int64_t roots;          /* first-level subtrees searched (n for mce_run) */
   uint32_t graph_errors;  /* MCE_GRAPH_* bits when the last run returned MCE_ERR_GRAPH */
+  int32_t subgraph;       /* MCE_SUBGRAPH_PARTIAL or _FULL: the encoding used; 0 before the search */
 } mce_graph_facts;
 
 /* Counters of the last run, summed over wavefronts. */
 typedef struct {
   uint32_t struct_size;      /* sizeof(mce_run_stats) */
   int32_t workers;           /* wavefronts in the largest search launch */
-  int32_t launches;          /* search launches (one per bitset width class) */
+  int32_t launches;          /* search launches (one per bitset width and staging sub-class) */
   int32_t pad_;
   uint64_t nodes;            /* search-tree nodes whose pivot was evaluated */
   uint64_t leaves;           /* maximal cliques reported (== count minus isolated) */
@@ -102,7 +114,7 @@ typedef struct {
   uint64_t pivot_rows;       /* sum over nodes of |P u X_P| rows scanned for the pivot */
   uint64_t pivot_words;      /* pivot_rows times the bitset width in 64-bit words */
   uint64_t xx_tests;         /* membership tests of the X_X array against CSR rows */
-  uint64_t ip_rows;          /* induced-subgraph rows built (sum of |P| over roots) */
+  uint64_t table_words;      /* 64-bit words of induced-subgraph tables built */
   uint64_t busy_ticks;       /* sum over wavefronts of wall-clock ticks spent searching */
   uint64_t max_busy_ticks;   /* largest per-wavefront busy time */
   uint64_t max_nodes;        /* largest per-wavefront node count (section 4.3 load) */
@@ -111,10 +123,11 @@ typedef struct {
   double ms_total;           /* mce_run wall time on the host, end to end */
   double ms_validate, ms_peel, ms_orient;   /* GPU phase times, with MCE_FLAG_PHASE_TIMES */
   double ms_search;          /* search kernels alone (events around each launch), same flag */
+  double ms_build;           /* induced-subgraph build kernels, same flag */
 } mce_run_stats;
 
 /* Fills cfg with the defaults: device -1, worker_list 1, donate_min_p 10,
-   validate 1, max_workers 0, timeout_ms 120000, flags 0. */
+   validate 1, max_workers 0, timeout_ms 120000, flags 0, subgraph auto. */
 mce_status mce_config_init(mce_config* cfg);
 
 /* Creates an engine on cfg->device (cfg may be NULL for the defaults). The engine

@@ -21,6 +21,7 @@ MCE_OK, MCE_ERR_ARG, MCE_ERR_GRAPH, MCE_ERR_NOMEM = 0, -1, -2, -3
 MCE_ERR_DEVICE, MCE_ERR_STATE, MCE_ERR_TIMEOUT, MCE_ERR_LIMIT = -4, -5, -6, -7
 MCE_GRAPH_ROWPTR, MCE_GRAPH_RANGE, MCE_GRAPH_LOOP, MCE_GRAPH_ORDER, MCE_GRAPH_ASYM = 1, 2, 4, 8, 16
 MCE_FLAG_HBM_STAGING, MCE_FLAG_PHASE_TIMES = 1, 2
+MCE_SUBGRAPH_AUTO, MCE_SUBGRAPH_PARTIAL, MCE_SUBGRAPH_FULL = 0, 1, 2
 
 # every function the C header declares
 EXPORTS = ("mce_config_init", "mce_create", "mce_run", "mce_run_roots", "mce_result",
@@ -43,7 +44,8 @@ class mce_config(ctypes.Structure):
     _fields_ = [("struct_size", ctypes.c_uint32), ("device", ctypes.c_int32),
                 ("worker_list", ctypes.c_int32), ("donate_min_p", ctypes.c_int32),
                 ("validate", ctypes.c_int32), ("max_workers", ctypes.c_int32),
-                ("timeout_ms", ctypes.c_int64), ("flags", ctypes.c_uint32)]
+                ("timeout_ms", ctypes.c_int64), ("flags", ctypes.c_uint32),
+                ("subgraph", ctypes.c_int32)]
 
 
 class mce_graph_facts(ctypes.Structure):
@@ -51,7 +53,7 @@ class mce_graph_facts(ctypes.Structure):
                 ("degeneracy", ctypes.c_int32), ("rounds", ctypes.c_int32),
                 ("max_p", ctypes.c_int32), ("max_x", ctypes.c_int32),
                 ("isolated", ctypes.c_int64), ("roots", ctypes.c_int64),
-                ("graph_errors", ctypes.c_uint32)]
+                ("graph_errors", ctypes.c_uint32), ("subgraph", ctypes.c_int32)]
 
 
 class mce_run_stats(ctypes.Structure):
@@ -60,12 +62,12 @@ class mce_run_stats(ctypes.Structure):
                 ("nodes", ctypes.c_uint64), ("leaves", ctypes.c_uint64),
                 ("donations", ctypes.c_uint64), ("pivot_rows", ctypes.c_uint64),
                 ("pivot_words", ctypes.c_uint64), ("xx_tests", ctypes.c_uint64),
-                ("ip_rows", ctypes.c_uint64), ("busy_ticks", ctypes.c_uint64),
+                ("table_words", ctypes.c_uint64), ("busy_ticks", ctypes.c_uint64),
                 ("max_busy_ticks", ctypes.c_uint64), ("max_nodes", ctypes.c_uint64),
                 ("kernel_ticks", ctypes.c_uint64), ("tick_hz", ctypes.c_double),
                 ("ms_total", ctypes.c_double), ("ms_validate", ctypes.c_double),
                 ("ms_peel", ctypes.c_double), ("ms_orient", ctypes.c_double),
-                ("ms_search", ctypes.c_double)]
+                ("ms_search", ctypes.c_double), ("ms_build", ctypes.c_double)]
 
 
 _lib = None
@@ -178,7 +180,7 @@ class Engine:
 
     def __init__(self, device: int | None = None, worker_list: bool = True, donate_min_p: int = 10,
                  validate: bool = True, max_workers: int = 0, timeout_ms: int = 120000,
-                 hbm_staging: bool = False, phase_times: bool = False):
+                 hbm_staging: bool = False, phase_times: bool = False, subgraph: str = "auto"):
         import torch
         if device is None:
             device = torch.cuda.current_device()
@@ -192,6 +194,10 @@ class Engine:
         cfg.max_workers = max_workers
         cfg.timeout_ms = timeout_ms
         cfg.flags = (MCE_FLAG_HBM_STAGING if hbm_staging else 0) | (MCE_FLAG_PHASE_TIMES if phase_times else 0)
+        modes = {"auto": MCE_SUBGRAPH_AUTO, "partial": MCE_SUBGRAPH_PARTIAL, "full": MCE_SUBGRAPH_FULL}
+        if subgraph not in modes:
+            raise ValueError(f"subgraph must be one of {sorted(modes)}")
+        cfg.subgraph = modes[subgraph]
         h = ctypes.c_void_p()
         with torch.cuda.device(device):
             self._check(mce_create(cfg, h), "mce_create", None)

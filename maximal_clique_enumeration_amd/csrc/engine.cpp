@@ -39,9 +39,10 @@ struct mce_engine {
   int peel_blocks_max = 1;
   std::string err;
 
-  DevBuf ctl, deg, rnd, core, alive0, alive1, front0, front1, pcount, lists, results, wl, slots, stats;
+  DevBuf ctl, deg, rnd, core, alive0, alive1, front0, front1, pcount, xcount, lists, taboff, heap, results, wl,
+      slots, stats;
   HostPinned host;    // staging for device -> host copies
-  hipEvent_t ev[6] = {};
+  hipEvent_t ev[4 + 4 * MCE_NSUB] = {};
   bool have_events = false;
 
   // last run
@@ -147,6 +148,7 @@ mce_status run_impl(mce_engine* e, int32_t n, int64_t nnz, const int32_t* row_pt
       (h = ensure(e->alive0, nb)) != hipSuccess || (h = ensure(e->alive1, nb)) != hipSuccess ||
       (h = ensure(e->front0, nb)) != hipSuccess || (h = ensure(e->front1, nb)) != hipSuccess ||
       (h = ensure(e->pcount, (size_t)std::max(cnt, 1) * sizeof(int))) != hipSuccess ||
+      (h = ensure(e->xcount, (size_t)std::max(cnt, 1) * sizeof(int))) != hipSuccess ||
       (h = ensure(e->lists, (size_t)std::max(cnt, 1) * sizeof(int))) != hipSuccess ||
       (h = ensure(e->results, (1 + kHistWords) * sizeof(u64))) != hipSuccess ||
       (h = ensure(e->wl, sizeof(MceWl))) != hipSuccess ||
@@ -174,7 +176,7 @@ mce_status run_impl(mce_engine* e, int32_t n, int64_t nnz, const int32_t* row_pt
     return hip_fail(e, h, "peel launch");
   if (timing) (void)hipEventRecord(e->ev[2], s);
   if ((h = mce_launch_orient(n, row_ptr, col_idx, dp<int>(e->rnd), subset ? roots : nullptr, cnt,
-                             dp<int>(e->pcount), ctl, grid, s)) != hipSuccess)
+                             dp<int>(e->pcount), dp<int>(e->xcount), ctl, grid, s)) != hipSuccess)
     return hip_fail(e, h, "orient launch");
   MceCtl* hctl = static_cast<MceCtl*>(e->host.p);
   if ((h = hipMemcpyAsync(hctl, ctl, sizeof(MceCtl), hipMemcpyDeviceToHost, s)) != hipSuccess)
@@ -198,85 +200,133 @@ mce_status run_impl(mce_engine* e, int32_t n, int64_t nnz, const int32_t* row_pt
   if (hctl->status & MCE_E_LIMIT)
     return fail(e, MCE_ERR_LIMIT, "a first-level subtree has more than 2048 later neighbours");
 
-  // roots per class, heaviest class first
-  ClassOffsets off{};
-  int counts[MCE_NCLASS];
+  // Induced-subgraph mode (section 3.4; section 4.5 picks partial when
+  // Delta / d > 200, else full). Local row indices of the full subgraph must
+  // stay below 2^20 for the pivot keys.
+  int mode;
+  const int dd = std::max(1, hctl->degeneracy);
+  const bool full_fits = (long long)hctl->max_p + hctl->max_x < (long long)MCE_MAX_LOCAL;
+  if (e->cfg.subgraph == MCE_SUBGRAPH_PARTIAL) {
+    mode = MCE_MODE_IP;
+  } else if (e->cfg.subgraph == MCE_SUBGRAPH_FULL) {
+    if (!full_fits) return fail(e, MCE_ERR_LIMIT, "full induced subgraph: |P| + |X| of a root exceeds 2^20");
+    mode = MCE_MODE_IPX;
+  } else {
+    mode = (hctl->max_degree > 200LL * dd || !full_fits) ? MCE_MODE_IP : MCE_MODE_IPX;
+  }
+  e->info.subgraph = mode == MCE_MODE_IPX ? MCE_SUBGRAPH_FULL : MCE_SUBGRAPH_PARTIAL;
+
+  // roots per sub-class of that mode
+  SubOffsets off{};
+  int counts[MCE_NSUB];
   int total = 0;
-  for (int c = 0; c < MCE_NCLASS; c++) {
-    counts[c] = hctl->class_count[c];
+  size_t heap_words = 0;
+  for (int c = 0; c < MCE_NSUB; c++) {
+    counts[c] = hctl->sub_count[mode][c];
     off.off[c] = total;
     total += counts[c];
+    heap_words = std::max(heap_words, (size_t)hctl->sub_words[mode][c]);
   }
   const u64 iso = hctl->isolated, iso_hash = hctl->isolated_hash;
+
+  // launch plan, heaviest width first; every buffer sized before any launch
+  struct Plan {
+    int sub, nw;
+    SearchLayout L;
+  };
+  std::vector<Plan> plan;
+  size_t slot_bytes = 0;
+  int stat_rows = 0;
+  for (int c = MCE_NSUB - 1; c >= 0; c--) {
+    if (counts[c] == 0) continue;
+    Plan pl;
+    pl.sub = c;
+    pl.L = mce_search_layout(c, mode, hctl->sub_maxp[mode][c], hctl->sub_maxx[mode][c], hctl->sub_maxr[mode][c],
+                             hbm);
+    int nw = mce_search_max_workers(pl.L, e->num_cu);
+    if (nw <= 0) return fail(e, MCE_ERR_DEVICE, "search kernel occupancy query failed");
+    if (e->cfg.max_workers > 0) nw = std::min(nw, (int)e->cfg.max_workers);
+    if (!e->cfg.worker_list) nw = std::min(nw, counts[c]);
+    pl.nw = nw;
+    slot_bytes = std::max(slot_bytes, pl.L.slot_bytes * (size_t)nw);
+    stat_rows += nw;
+    plan.push_back(pl);
+  }
   if (total > 0) {
-    if ((h = mce_launch_bucket(n, subset ? roots : nullptr, cnt, dp<int>(e->pcount), off, dp<int>(e->lists), ctl,
-                               grid, s)) != hipSuccess)
+    if ((h = ensure(e->taboff, (size_t)total * sizeof(u64))) != hipSuccess ||
+        (h = ensure(e->heap, heap_words * sizeof(u64))) != hipSuccess ||
+        (h = ensure(e->slots, slot_bytes)) != hipSuccess ||
+        (h = ensure(e->stats, (size_t)stat_rows * MCE_NSTAT * sizeof(u64))) != hipSuccess)
+      return hip_fail(e, h, "search buffers");
+    if ((h = hipMemsetAsync(e->stats.p, 0, (size_t)stat_rows * MCE_NSTAT * sizeof(u64), s)) != hipSuccess)
+      return hip_fail(e, h, "memset");
+    if ((h = mce_launch_bucket(subset ? roots : nullptr, cnt, dp<int>(e->pcount), dp<int>(e->xcount), mode, off,
+                               dp<int>(e->lists), ctl, grid, s)) != hipSuccess)
       return hip_fail(e, h, "bucket launch");
   }
   if (timing) (void)hipEventRecord(e->ev[3], s);
 
-  std::vector<u64> stat_sum(MCE_NSTAT, 0);
-  double ms_search = 0;   // search kernels only, from events around each launch
-  u64 max_busy = 0, max_nodes = 0, max_ticks = 0;
-  int max_workers_used = 0, launches = 0;
-  for (int c = MCE_NCLASS - 1; c >= 0; c--) {
-    if (counts[c] == 0) continue;
-    int nw = mce_search_max_workers(c, hbm, e->num_cu);
-    if (nw <= 0) return fail(e, MCE_ERR_DEVICE, "search kernel occupancy query failed");
-    if (e->cfg.max_workers > 0) nw = std::min(nw, (int)e->cfg.max_workers);
-    if (!e->cfg.worker_list) nw = std::min(nw, counts[c]);
-    SlotLayout L = mce_slot_layout(c, std::max(hctl->max_x, 1));
-    if ((h = ensure(e->slots, L.bytes * (size_t)nw)) != hipSuccess) return hip_fail(e, h, "worker slots");
-    if ((h = ensure(e->stats, (size_t)nw * MCE_NSTAT * sizeof(u64))) != hipSuccess)
-      return hip_fail(e, h, "stats buffer");
-    if ((h = mce_launch_wl_init(dp<MceWl>(e->wl), s)) != hipSuccess) return hip_fail(e, h, "wl init");
+  int launches = 0, max_workers_used = 0, stat_off = 0;
+  int evi = 4;
+  for (const Plan& pl : plan) {
+    const int c = pl.sub;
+    const SearchLayout& L = pl.L;
+    BuildParams bp{};
+    bp.rp = row_ptr;
+    bp.ci = col_idx;
+    bp.rnd = dp<int>(e->rnd);
+    bp.roots = dp<int>(e->lists) + off.off[c];
+    bp.nroots = counts[c];
+    bp.W = 1 << L.wclass;
+    bp.mode = mode;
+    bp.heap = dp<u64>(e->heap);
+    bp.heap_words = heap_words;
+    bp.heap_top = &ctl->heap_top[c];
+    bp.tab_off = dp<u64>(e->taboff) + off.off[c];
+    bp.status = &ctl->status;
+    if (timing) (void)hipEventRecord(e->ev[evi], s);
+    if ((h = mce_launch_build(bp, e->num_cu * 16, s)) != hipSuccess) return hip_fail(e, h, "build launch");
+    if (timing) (void)hipEventRecord(e->ev[evi + 1], s);
+    if ((h = mce_launch_wl_init(dp<MceWl>(e->wl), pl.nw, s)) != hipSuccess) return hip_fail(e, h, "wl init");
     SearchParams prm{};
     prm.rp = row_ptr;
     prm.ci = col_idx;
-    prm.rnd = dp<int>(e->rnd);
-    prm.roots = dp<int>(e->lists) + off.off[c];
+    prm.heap = dp<u64>(e->heap);
+    prm.tab_off = dp<u64>(e->taboff) + off.off[c];
     prm.nroots = counts[c];
-    prm.nworkers = nw;
+    prm.nworkers = pl.nw;
+    prm.hcap = L.hcap;
+    prm.l_hist = L.l_hist;
+    prm.l_hv = L.l_hv;
+    prm.l_pid = L.l_pid;
+    prm.l_stack = L.l_stack;
+    prm.l_rows = L.l_rows;
+    prm.l_xx = L.l_xx;
+    prm.slot_bytes = L.slot_bytes;
+    prm.s_stack = L.s_stack;
+    prm.s_xx = L.s_xx;
+    prm.s_mail = L.s_mail;
     prm.g_hist = results + 1;
     prm.g_hash = results;
     prm.wl = dp<MceWl>(e->wl);
     prm.slots = dp<char>(e->slots);
-    prm.slot_bytes = L.bytes;
-    prm.off_rows = L.off_rows;
-    prm.off_hv = L.off_hv;
-    prm.off_pid = L.off_pid;
-    prm.off_stack = L.off_stack;
-    prm.off_xx = L.off_xx;
-    prm.off_mail = L.off_mail;
     prm.donate_min_p = std::max(1, (int)e->cfg.donate_min_p);
     prm.worker_list = e->cfg.worker_list ? 1 : 0;
     prm.budget = budget;
     prm.status = &ctl->status;
-    prm.stats = dp<u64>(e->stats);
-    if (timing) (void)hipEventRecord(e->ev[4], s);
-    if ((h = mce_launch_search(c, hbm, prm, s)) != hipSuccess) return hip_fail(e, h, "search launch");
-    if (timing) (void)hipEventRecord(e->ev[5], s);
+    prm.stats = dp<u64>(e->stats) + (size_t)stat_off * MCE_NSTAT;
+    if (timing) (void)hipEventRecord(e->ev[evi + 2], s);
+    if ((h = mce_launch_search(L, prm, s)) != hipSuccess) return hip_fail(e, h, "search launch");
+    if (timing) (void)hipEventRecord(e->ev[evi + 3], s);
+    evi += 4;
+    stat_off += pl.nw;
     launches++;
-    max_workers_used = std::max(max_workers_used, nw);
-    // per-wavefront counters of this launch
-    std::vector<u64> st((size_t)nw * MCE_NSTAT);
-    if ((h = hipMemcpyAsync(st.data(), e->stats.p, st.size() * sizeof(u64), hipMemcpyDeviceToHost, s)) !=
-        hipSuccess)
-      return hip_fail(e, h, "stats readback");
-    if ((h = hipStreamSynchronize(s)) != hipSuccess) return hip_fail(e, h, "synchronize after search");
-    if (timing) {
-      float ms = 0;
-      (void)hipEventElapsedTime(&ms, e->ev[4], e->ev[5]);
-      ms_search += ms;
-    }
-    for (int w = 0; w < nw; w++) {
-      const u64* r = &st[(size_t)w * MCE_NSTAT];
-      for (int i = 0; i < MCE_NSTAT; i++) stat_sum[i] += r[i];
-      max_busy = std::max(max_busy, r[ST_BUSY_TICKS]);
-      max_nodes = std::max(max_nodes, r[ST_NODES]);
-      max_ticks = std::max(max_ticks, r[ST_TOTAL_TICKS]);
-    }
+    max_workers_used = std::max(max_workers_used, pl.nw);
   }
+  std::vector<u64> st((size_t)stat_rows * MCE_NSTAT);
+  if (stat_rows > 0 &&
+      (h = hipMemcpyAsync(st.data(), e->stats.p, st.size() * sizeof(u64), hipMemcpyDeviceToHost, s)) != hipSuccess)
+    return hip_fail(e, h, "stats readback");
 
   u64* hres = reinterpret_cast<u64*>(static_cast<char*>(e->host.p) + sizeof(MceCtl));
   if ((h = hipMemcpyAsync(hres, results, (1 + kHistWords) * sizeof(u64), hipMemcpyDeviceToHost, s)) != hipSuccess ||
@@ -286,6 +336,16 @@ mce_status run_impl(mce_engine* e, int32_t n, int64_t nnz, const int32_t* row_pt
   if (hctl->status & MCE_E_TIMEOUT) return fail(e, MCE_ERR_TIMEOUT, "search ran past the time limit");
   if (hctl->status & MCE_E_PROTO) return fail(e, MCE_ERR_DEVICE, "worker-list bookkeeping error");
   if (hctl->status & MCE_E_LIMIT) return fail(e, MCE_ERR_LIMIT, "subtree larger than its width class");
+  if (hctl->status & MCE_E_HEAP) return fail(e, MCE_ERR_DEVICE, "induced-subgraph heap overflow");
+  std::vector<u64> stat_sum(MCE_NSTAT, 0);
+  u64 max_busy = 0, max_nodes = 0, max_ticks = 0;
+  for (int w = 0; w < stat_rows; w++) {
+    const u64* r = &st[(size_t)w * MCE_NSTAT];
+    for (int i = 0; i < MCE_NSTAT; i++) stat_sum[i] += r[i];
+    max_busy = std::max(max_busy, r[ST_BUSY_TICKS]);
+    max_nodes = std::max(max_nodes, r[ST_NODES]);
+    max_ticks = std::max(max_ticks, r[ST_TOTAL_TICKS]);
+  }
 
   std::vector<uint64_t> hist(kHistWords, 0);
   for (size_t k = 0; k < kHistWords; k++) hist[k] = hres[1 + k];
@@ -311,7 +371,9 @@ mce_status run_impl(mce_engine* e, int32_t n, int64_t nnz, const int32_t* row_pt
   so.pivot_rows = stat_sum[ST_PIVOT_ROWS];
   so.pivot_words = stat_sum[ST_PIVOT_WORDS];
   so.xx_tests = stat_sum[ST_XX_TESTS];
-  so.ip_rows = stat_sum[ST_IP_ROWS];
+  u64 words_built = 0;
+  for (const Plan& pl : plan) words_built += hctl->sub_words[mode][pl.sub];
+  so.table_words = words_built;
   so.busy_ticks = stat_sum[ST_BUSY_TICKS];
   so.max_busy_ticks = max_busy;
   so.max_nodes = max_nodes;
@@ -323,8 +385,17 @@ mce_status run_impl(mce_engine* e, int32_t n, int64_t nnz, const int32_t* row_pt
     (void)hipEventElapsedTime(&c, e->ev[2], e->ev[3]);
     so.ms_validate = a;
     so.ms_peel = b;
-    so.ms_orient = c;   // orientation, host readback and root bucketing
-    so.ms_search = ms_search;
+    so.ms_orient = c;   // orientation, host read-back and root bucketing
+    double mb = 0, ms = 0;
+    for (int i = 0; i < launches; i++) {
+      float x = 0, y = 0;
+      (void)hipEventElapsedTime(&x, e->ev[4 + 4 * i], e->ev[5 + 4 * i]);
+      (void)hipEventElapsedTime(&y, e->ev[6 + 4 * i], e->ev[7 + 4 * i]);
+      mb += x;
+      ms += y;
+    }
+    so.ms_build = mb;
+    so.ms_search = ms;
   }
   so.ms_total = ms_since(t0);
   return MCE_OK;
@@ -345,6 +416,7 @@ mce_status mce_config_init(mce_config* cfg) {
   cfg->max_workers = 0;
   cfg->timeout_ms = 120000;
   cfg->flags = 0;
+  cfg->subgraph = MCE_SUBGRAPH_AUTO;
   return MCE_OK;
 }
 
@@ -358,7 +430,9 @@ mce_status mce_create(const mce_config* cfg, mce_engine** out) {
     std::memcpy(&c, cfg, sz);
     c.struct_size = sizeof(mce_config);
   }
-  if (c.donate_min_p < 1 || c.max_workers < 0 || c.timeout_ms < 0) return MCE_ERR_ARG;
+  if (c.donate_min_p < 1 || c.max_workers < 0 || c.timeout_ms < 0 || c.subgraph < MCE_SUBGRAPH_AUTO ||
+      c.subgraph > MCE_SUBGRAPH_FULL)
+    return MCE_ERR_ARG;
   if (c.timeout_ms == 0) c.timeout_ms = 120000;
   mce_engine* e = new (std::nothrow) mce_engine();
   if (!e) return MCE_ERR_NOMEM;
@@ -468,8 +542,9 @@ const char* mce_status_string(mce_status s) {
 void mce_destroy(mce_engine* e) {
   if (!e) return;
   (void)hipSetDevice(e->device);
-  DevBuf* bufs[] = {&e->ctl, &e->deg, &e->rnd, &e->core, &e->alive0, &e->alive1, &e->front0,
-                    &e->front1, &e->pcount, &e->lists, &e->results, &e->wl, &e->slots, &e->stats};
+  DevBuf* bufs[] = {&e->ctl,    &e->deg,   &e->rnd,    &e->core,    &e->alive0, &e->alive1,
+                    &e->front0, &e->front1, &e->pcount, &e->xcount, &e->lists,  &e->taboff,
+                    &e->heap,   &e->results, &e->wl,    &e->slots,  &e->stats};
   for (DevBuf* b : bufs) release(*b);
   if (e->host.p) (void)hipHostFree(e->host.p);
   for (auto& ev : e->ev)

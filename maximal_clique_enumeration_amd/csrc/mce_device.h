@@ -15,16 +15,53 @@ typedef unsigned int u32;
 #define MCE_E_LIMIT (1u << 17)     // a root's P does not fit the launch's bitset width
 #define MCE_E_PROTO (1u << 18)     // worker-list bookkeeping went wrong
 #define MCE_E_ROOTS (1u << 19)     // a root id outside [0, n)
+#define MCE_E_HEAP (1u << 20)      // the induced-subgraph heap was too small
 
-// Number of bitset-width classes: widths 1, 2, 4, 8, 16, 32 words (P up to 2048).
+// Bitset-width classes: widths 1, 2, 4, 8, 16, 32 words of 64 bits (P up to 2048).
 #define MCE_NCLASS 6
 #define MCE_MAX_P 2048
 #define MCE_MAX_WORKERS 8192
+// Sub-classes: a width class split by whether a root's induced subgraph (rows
+// and X_X array) is staged in LDS ("light") or read from HBM ("heavy").
+#define MCE_NSUB (2 * MCE_NCLASS)
+#define MCE_LIGHT_BYTES 4096
+// pivot keys pack (count << 20 | ~local index): local indices stay below 2^20
+#define MCE_MAX_LOCAL ((1 << 20) - 1)
+
+// Induced-subgraph modes (section 3.4 of the pages): partial (P x P rows, P-X
+// edges looked up in the CSR) or full (P x (P u X) rows).
+#define MCE_MODE_IP 0
+#define MCE_MODE_IPX 1
 
 __host__ __device__ inline int mce_class_of(int p) {   // smallest class whose 64*W >= p
   int c = 0;
   while (c < MCE_NCLASS - 1 && (64 << c) < p) c++;
   return c;
+}
+
+// Rows of a root's induced subgraph: P rows only (IP) or P and X rows (IPX).
+__host__ __device__ inline long long mce_table_rows(int p, int x, int mode) {
+  return mode == MCE_MODE_IPX ? (long long)p + x : (long long)p;
+}
+
+// Words (u64) of a root's table in the heap:
+//   [0] p | x << 32    [1] root id    [2] hash term of the root
+//   [3 .. 3 + rows*W)  bit rows over the root's P (local index order = id order)
+//   then p hash terms of the P members, then p + x int32 ids (P ids, X ids).
+__host__ __device__ inline unsigned long long mce_table_words(int p, int x, int W, int mode) {
+  return 3ull + (unsigned long long)mce_table_rows(p, x, mode) * (unsigned long long)W + (unsigned long long)p +
+         ((unsigned long long)p + (unsigned long long)x + 1ull) / 2ull;
+}
+
+// LDS bytes that staging a root's rows and X_X array takes.
+__host__ __device__ inline unsigned long long mce_stage_bytes(int p, int x, int W, int mode) {
+  return (unsigned long long)mce_table_rows(p, x, mode) * (unsigned long long)W * 8ull +
+         (unsigned long long)x * 4ull;
+}
+
+__host__ __device__ inline int mce_sub_of(int p, int x, int mode) {
+  const int c = mce_class_of(p);
+  return 2 * c + (mce_stage_bytes(p, x, 1 << c, mode) > MCE_LIGHT_BYTES ? 1 : 0);
 }
 
 // Control block: one per run, zeroed by the host before the first kernel.
@@ -39,26 +76,50 @@ struct MceCtl {
   int pad0;
   u64 isolated;          // roots of degree 0
   u64 isolated_hash;     // sum of their clique hashes
-  int class_count[MCE_NCLASS];
-  int class_cursor[MCE_NCLASS];
+  // per induced-subgraph mode and sub-class: roots, largest |P|, largest |X|,
+  // largest row count, heap words of their tables
+  int sub_count[2][MCE_NSUB];
+  int sub_maxp[2][MCE_NSUB];
+  int sub_maxx[2][MCE_NSUB];
+  int sub_maxr[2][MCE_NSUB];   // largest row count of a table
+  u64 sub_words[2][MCE_NSUB];
+  int sub_cursor[MCE_NSUB];
+  u64 heap_top[MCE_NSUB];   // build: bump allocator of each sub-class's heap
   int asize[2];          // peel: alive-list sizes (ping-pong)
   int fsize[2];          // peel: frontier sizes (ping-pong)
   u32 bar_count;         // grid barrier
   u32 bar_gen;
 };
 
-// Worker-list state of one search launch (section 3.3 of the pages): a bitmap
-// of idle wavefront ids plus one wake flag per wavefront. All zero at launch.
+// Worker-list state of one search launch (section 3.3 of the pages), zeroed
+// before the launch. Idle wavefronts enqueue their ids in a multi-producer
+// multi-consumer ring (capacity = wavefronts of the launch, so it cannot
+// overflow) and sleep on a wake flag of their own. Every hot counter sits on
+// its own 128-byte line.
+//
 // Termination does not assume that every wavefront of the grid is resident: a
 // wavefront counts in n_active only while it holds a task or is about to take a
-// first-level subtree, so waves that start late find the roots gone and leave.
+// first-level subtree. The wavefront whose release brings n_active to zero
+// after the roots ran out writes MCE_FLAG_EXIT into every wake flag; a wave
+// that starts later finds the roots gone and leaves the same way.
+#define MCE_LINE_WORDS 32     // u32 words per 128-byte line
+#define MCE_FLAG_TASK 1u
+#define MCE_FLAG_EXIT 2u
 struct MceWl {
   u32 root_ctr;          // next first-level subtree to hand out (phase 1)
+  u32 pad0[MCE_LINE_WORDS - 1];
   int n_active;          // wavefronts holding (or about to take) a task
-  int n_waiting;         // wavefronts published in idle_bits (a hint for donors)
-  u32 done;              // 1: roots exhausted and no task held anywhere, or abandoned
-  u64 idle_bits[MCE_MAX_WORKERS / 64];
-  u32 flag[MCE_MAX_WORKERS];   // 1: a donor filled this wavefront's mailbox
+  u32 pad1[MCE_LINE_WORDS - 1];
+  int avail;             // ring entries not yet claimed by a donor
+  u32 pad2[MCE_LINE_WORDS - 1];
+  u32 head;              // next ring slot a donor claims
+  u32 pad3[MCE_LINE_WORDS - 1];
+  u32 tail;              // next ring slot an idle wave fills
+  u32 pad4[MCE_LINE_WORDS - 1];
+  u32 done;              // set on abort (time limit); donors poll it
+  u32 pad5[MCE_LINE_WORDS - 1];
+  u64 ring[MCE_MAX_WORKERS];                    // sequence << 32 | (wave id + 1)
+  u32 flag[MCE_MAX_WORKERS * MCE_LINE_WORDS];   // wake flag of wave w at w * MCE_LINE_WORDS
 };
 
 // ---------------------------------------------------------------- hashing
@@ -115,9 +176,8 @@ __device__ __forceinline__ u32 op_or(u32 a, u32 b) { return a | b; }
 MCE_DPP_REDUCE(wave_max_u32, op_max)
 MCE_DPP_REDUCE(wave_sum_u32, op_add)
 MCE_DPP_REDUCE(wave_or_u32, op_or)
-__device__ __forceinline__ u64 wave_sum_u64(u64 x) {   // via two 32-bit halves with carries
+__device__ __forceinline__ u64 wave_sum_u64(u64 x) {   // via 16/16/32-bit pieces, carries kept
   u32 lo = (u32)x, hi = (u32)(x >> 32);
-  // sum of lo halves can overflow 32 bits: split lo into 16-bit pieces
   u32 l0 = wave_sum_u32(lo & 0xFFFFu);
   u32 l1 = wave_sum_u32(lo >> 16);
   u32 h = wave_sum_u32(hi);
@@ -136,6 +196,9 @@ __device__ __forceinline__ int ld_relaxed(const int* p) {
 }
 __device__ __forceinline__ u64 ld_relaxed(const u64* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ u32 ld_acquire(const u32* p) {
+  return __hip_atomic_load(p, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT);
 }
 __device__ __forceinline__ void st_relaxed(u32* p, u32 v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);

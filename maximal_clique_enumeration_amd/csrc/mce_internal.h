@@ -5,10 +5,12 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <algorithm>
+
 #include "mce_device.h"
 
-struct ClassOffsets {
-  int off[MCE_NCLASS];
+struct SubOffsets {
+  int off[MCE_NSUB];
 };
 
 // Per-wavefront statistics written by the search kernel (u64 each).
@@ -27,19 +29,32 @@ enum {
   MCE_NSTAT
 };
 
+// Where one search launch keeps its per-wave state: LDS word offsets (dynamic
+// shared memory) and byte offsets inside the wave's HBM slot.
+struct SearchLayout {
+  int sub, wclass, mode;
+  int pcap, xcap, rcap;   // largest |P|, |X|, row count over the launch's roots
+  int levels, hcap;       // stack records, histogram entries
+  bool srows, sstack;     // rows + X_X staged in LDS; level stack in LDS
+  int l_hist, l_hv, l_pid, l_stack, l_rows, l_xx;
+  size_t lds_bytes;
+  size_t s_stack, s_xx, s_mail, slot_bytes;
+};
+
 struct SearchParams {
   const int* rp;
   const int* ci;
-  const int* rnd;
-  const int* roots;      // this launch's first-level subtree roots
+  const u64* heap;       // induced-subgraph tables of this launch's roots
+  const u64* tab_off;    // word offset of each root's table (by list index)
   int nroots;
   int nworkers;
+  int hcap;
+  int l_hist, l_hv, l_pid, l_stack, l_rows, l_xx;
+  size_t slot_bytes, s_stack, s_xx, s_mail;
   u64* g_hist;           // global histogram (MCE_MAX_P + 2 entries)
   u64* g_hash;
   MceWl* wl;
   char* slots;           // one HBM slot per wavefront
-  size_t slot_bytes;
-  size_t off_rows, off_hv, off_pid, off_stack, off_xx, off_mail;
   int donate_min_p;
   int worker_list;
   u64 budget;            // wall-clock ticks after which the launch is abandoned
@@ -47,14 +62,20 @@ struct SearchParams {
   u64* stats;            // nworkers * MCE_NSTAT
 };
 
-// Slot layout for a width class: byte offsets and total size per wavefront.
-struct SlotLayout {
-  size_t off_rows, off_hv, off_pid, off_stack, off_xx, off_mail, bytes;
+struct BuildParams {
+  const int* rp;
+  const int* ci;
+  const int* rnd;
+  const int* roots;      // the sub-class's roots
+  int nroots;
+  int W;                 // bitset words of the sub-class
+  int mode;              // MCE_MODE_IP / MCE_MODE_IPX
+  u64* heap;
+  u64 heap_words;
+  u64* heap_top;         // bump allocator (zeroed before the launch)
+  u64* tab_off;          // out: word offset of each root's table
+  u32* status;
 };
-SlotLayout mce_slot_layout(int wclass, int max_x);
-size_t mce_search_lds_bytes(int wclass, bool lds_rows, bool lds_stack);
-bool mce_search_lds_rows(int wclass);
-bool mce_search_lds_stack(int wclass);
 
 hipError_t mce_launch_validate(int n, long long nnz, const int* rp, const int* ci, MceCtl* ctl, int blocks,
                                hipStream_t s);
@@ -62,13 +83,16 @@ hipError_t mce_launch_peel(int n, const int* rp, const int* ci, int* deg, int* r
                            int* alive1, int* front0, int* front1, MceCtl* ctl, u64 budget, int blocks,
                            hipStream_t s);
 int mce_peel_max_blocks(int num_cu);
+// roots == NULL: the roots are 0 .. nroots-1
 hipError_t mce_launch_orient(int n, const int* rp, const int* ci, const int* rnd, const int* roots, int nroots,
-                             int* pcount, MceCtl* ctl, int blocks, hipStream_t s);
-hipError_t mce_launch_bucket(int n, const int* roots, int nroots, const int* pcount, ClassOffsets off, int* lists,
-                             MceCtl* ctl, int blocks, hipStream_t s);
+                             int* pcount, int* xcount, MceCtl* ctl, int blocks, hipStream_t s);
+hipError_t mce_launch_bucket(const int* roots, int nroots, const int* pcount, const int* xcount, int mode,
+                             SubOffsets off, int* lists, MceCtl* ctl, int blocks, hipStream_t s);
 
-// Resident wavefronts of the search kernel of a class over the whole chip (0 on error).
-int mce_search_max_workers(int wclass, bool hbm_staging, int num_cu);
-hipError_t mce_launch_search(int wclass, bool hbm_staging, const SearchParams& prm, hipStream_t s);
+hipError_t mce_launch_build(const BuildParams& prm, int blocks, hipStream_t s);
 
-hipError_t mce_launch_wl_init(MceWl* wl, hipStream_t s);
+SearchLayout mce_search_layout(int sub, int mode, int pcap, int xcap, int rcap, bool force_hbm);
+// Resident wavefronts of a search layout over the whole chip (0 on error).
+int mce_search_max_workers(const SearchLayout& L, int num_cu);
+hipError_t mce_launch_search(const SearchLayout& L, const SearchParams& prm, hipStream_t s);
+hipError_t mce_launch_wl_init(MceWl* wl, int nworkers, hipStream_t s);

@@ -226,53 +226,77 @@ __global__ __launch_bounds__(256) void k_peel(int n, const int* __restrict__ rp,
 
 // ------------------------------------------------------------------ orientation
 // Per root: |P| = later neighbours, |X| = earlier ones. Degree-0 roots are
-// maximal cliques of size 1 and are counted here. Roots with |P| >= 1 are
-// counted per bitset-width class.
+// maximal cliques of size 1 and are counted here. Roots with 1 <= |P| <= MCE_MAX_P
+// are tallied per sub-class under both induced-subgraph modes (count, largest
+// |P|, |X| and row count, heap words), so that the host can pick the mode and
+// size every launch from one read-back.
 __global__ __launch_bounds__(256) void k_orient(int n, const int* __restrict__ rp, const int* __restrict__ ci,
                                                  const int* __restrict__ rnd, const int* __restrict__ roots,
-                                                 int nroots, int* pcount, MceCtl* ctl) {
+                                                 int nroots, int* pcount, int* xcount, MceCtl* ctl) {
   if (ld_relaxed(&ctl->status) != 0) return;
   const int lane = lane_id();
   const int gsize = gridDim.x * blockDim.x;
-  int cnt = nroots;   // roots == NULL: the identity list 0..nroots-1
+  const int cnt = nroots;   // roots == NULL: the identity list 0..nroots-1
   u64 iso = 0, iso_hash = 0;
-  int pmax = 0, xmax = 0;
+  int pmax = 0, xmax = 0, dmax = 0;
   u32 lim = 0;
-  int ccount[MCE_NCLASS];
-  for (int c = 0; c < MCE_NCLASS; c++) ccount[c] = 0;
   for (int base = blockIdx.x * blockDim.x; base < cnt; base += gsize) {
-    int i = base + threadIdx.x;
-    int p = 0;
-    int v = i < cnt ? (roots ? roots[i] : i) : 0;
+    const int i = base + threadIdx.x;
+    int p = 0, x = 0;
+    bool valid = false;
+    const int v = i < cnt ? (roots ? roots[i] : i) : 0;
     if (i < cnt && (v < 0 || v >= n)) {   // caller-supplied root out of range: flag it, touch nothing
       lim |= 2u;
       pcount[i] = 0;
+      xcount[i] = 0;
     } else if (i < cnt) {
-      int a = rp[v], b = rp[v + 1];
-      int rv = rnd[v];
+      const int a = rp[v], b = rp[v + 1];
+      const int rv = rnd[v];
       for (int e = a; e < b; e++) {
-        int u = ci[e];
+        const int u = ci[e];
         p += order_after(rnd[u], u, rv, v) ? 1 : 0;
       }
+      x = (b - a) - p;
       pcount[i] = p;
+      xcount[i] = x;
       if (b == a) {
         iso++;
         iso_hash += mce_clique_term(mce_vertex_term(v), 1);
       }
       pmax = max(pmax, p);
-      xmax = max(xmax, (b - a) - p);
+      xmax = max(xmax, x);
+      dmax = max(dmax, b - a);
       if (p > MCE_MAX_P) lim |= 1u;
+      valid = p > 0 && p <= MCE_MAX_P;
     }
-    for (int c = 0; c < MCE_NCLASS; c++) {
-      u64 m = ballot(i < cnt && p > 0 && p <= MCE_MAX_P && mce_class_of(p) == c);
-      ccount[c] += __popcll(m);
+    for (int mode = 0; mode < 2; mode++) {
+      const int sub = valid ? mce_sub_of(p, x, mode) : -1;
+      u64 pending = ballot(valid);
+      while (pending) {
+        const int s = read_lane(sub, __builtin_ctzll(pending));
+        const bool mine = sub == s;
+        const u64 m = ballot(mine);
+        pending &= ~m;
+        const u32 mp = wave_max_u32(mine ? (u32)p : 0u);
+        const u32 mx = wave_max_u32(mine ? (u32)x : 0u);
+        const u32 mr = wave_max_u32(mine ? (u32)mce_table_rows(p, x, mode) : 0u);
+        const u64 words = wave_sum_u64(mine ? mce_table_words(p, x, 1 << (s >> 1), mode) : 0ull);
+        if (lane == 0) {
+          atomicAdd(&ctl->sub_count[mode][s], __popcll(m));
+          atomicMax(&ctl->sub_maxp[mode][s], (int)mp);
+          atomicMax(&ctl->sub_maxx[mode][s], (int)mx);
+          atomicMax(&ctl->sub_maxr[mode][s], (int)mr);
+          atomicAdd(&ctl->sub_words[mode][s], words);
+        }
+      }
     }
   }
-  u64 wiso = wave_sum_u64(iso);
-  u64 whash = wave_sum_u64(iso_hash);
-  u32 wpm = wave_max_u32((u32)pmax);
-  u32 wxm = wave_max_u32((u32)xmax);
-  u32 wl = wave_or_u32(lim);
+  const u64 wiso = wave_sum_u64(iso);
+  const u64 whash = wave_sum_u64(iso_hash);
+  const u32 wpm = wave_max_u32((u32)pmax);
+  const u32 wxm = wave_max_u32((u32)xmax);
+  const u32 wdm = wave_max_u32((u32)dmax);
+  const u32 wl = wave_or_u32(lim);
   if (lane == 0) {
     if (wiso) {
       atomicAdd(&ctl->isolated, wiso);
@@ -280,32 +304,36 @@ __global__ __launch_bounds__(256) void k_orient(int n, const int* __restrict__ r
     }
     atomicMax(&ctl->max_p, (int)wpm);
     atomicMax(&ctl->max_x, (int)wxm);
+    atomicMax(&ctl->max_degree, (int)wdm);
     if (wl & 1u) atomicOr(&ctl->status, MCE_E_LIMIT);
     if (wl & 2u) atomicOr(&ctl->status, MCE_E_ROOTS);
-    for (int c = 0; c < MCE_NCLASS; c++)
-      if (ccount[c]) atomicAdd(&ctl->class_count[c], ccount[c]);
   }
 }
 
-// Scatter the roots with |P| >= 1 into one list per class, starting at off[c].
-__global__ __launch_bounds__(256) void k_bucket(int n, const int* __restrict__ roots, int nroots,
-                                                 const int* __restrict__ pcount, ClassOffsets off,
-                                                 int* lists, MceCtl* ctl) {
+// Scatter the roots with 1 <= |P| <= MCE_MAX_P into one list per sub-class of
+// the chosen mode, starting at off[sub].
+__global__ __launch_bounds__(256) void k_bucket(const int* __restrict__ roots, int nroots,
+                                                 const int* __restrict__ pcount, const int* __restrict__ xcount,
+                                                 int mode, SubOffsets off, int* lists, MceCtl* ctl) {
   if (ld_relaxed(&ctl->status) != 0) return;
   const int lane = lane_id();
   const int gsize = gridDim.x * blockDim.x;
-  int cnt = nroots;   // roots == NULL: the identity list 0..nroots-1
-  for (int base = blockIdx.x * blockDim.x; base < cnt; base += gsize) {
-    int i = base + threadIdx.x;
-    int p = i < cnt ? pcount[i] : 0;
-    int c = (p > 0 && p <= MCE_MAX_P) ? mce_class_of(p) : -1;
-    for (int cc = 0; cc < MCE_NCLASS; cc++) {
-      u64 m = ballot(c == cc);
-      if (!m) continue;
+  for (int base = blockIdx.x * blockDim.x; base < nroots; base += gsize) {
+    const int i = base + threadIdx.x;
+    const int p = i < nroots ? pcount[i] : 0;
+    const int x = i < nroots ? xcount[i] : 0;
+    const bool valid = p > 0 && p <= MCE_MAX_P;
+    const int sub = valid ? mce_sub_of(p, x, mode) : -1;
+    u64 pending = ballot(valid);
+    while (pending) {
+      const int s = read_lane(sub, __builtin_ctzll(pending));
+      const bool mine = sub == s;
+      const u64 m = ballot(mine);
+      pending &= ~m;
       int pos = 0;
-      if (lane == 0) pos = atomicAdd(&ctl->class_cursor[cc], __popcll(m));
+      if (lane == 0) pos = atomicAdd(&ctl->sub_cursor[s], __popcll(m));
       pos = read_lane(pos, 0);
-      if (c == cc) lists[off.off[cc] + pos + mbcnt(m)] = roots ? roots[i] : i;
+      if (mine) lists[off.off[s] + pos + mbcnt(m)] = roots ? roots[i] : i;
     }
   }
 }
@@ -341,17 +369,15 @@ int mce_peel_max_blocks(int num_cu) {
 }
 
 hipError_t mce_launch_orient(int n, const int* rp, const int* ci, const int* rnd, const int* roots, int nroots,
-                             int* pcount, MceCtl* ctl, int blocks, hipStream_t s) {
-  int cnt = nroots;   // roots == NULL: the identity list 0..nroots-1
-  int nb = max(1, min(blocks, (cnt + 255) / 256));
-  hipLaunchKernelGGL(k_orient, dim3(nb), dim3(256), 0, s, n, rp, ci, rnd, roots, nroots, pcount, ctl);
+                             int* pcount, int* xcount, MceCtl* ctl, int blocks, hipStream_t s) {
+  const int nb = max(1, min(blocks, (nroots + 255) / 256));
+  hipLaunchKernelGGL(k_orient, dim3(nb), dim3(256), 0, s, n, rp, ci, rnd, roots, nroots, pcount, xcount, ctl);
   return hipGetLastError();
 }
 
-hipError_t mce_launch_bucket(int n, const int* roots, int nroots, const int* pcount, ClassOffsets off, int* lists,
-                             MceCtl* ctl, int blocks, hipStream_t s) {
-  int cnt = nroots;   // roots == NULL: the identity list 0..nroots-1
-  int nb = max(1, min(blocks, (cnt + 255) / 256));
-  hipLaunchKernelGGL(k_bucket, dim3(nb), dim3(256), 0, s, n, roots, nroots, pcount, off, lists, ctl);
+hipError_t mce_launch_bucket(const int* roots, int nroots, const int* pcount, const int* xcount, int mode,
+                             SubOffsets off, int* lists, MceCtl* ctl, int blocks, hipStream_t s) {
+  const int nb = max(1, min(blocks, (nroots + 255) / 256));
+  hipLaunchKernelGGL(k_bucket, dim3(nb), dim3(256), 0, s, roots, nroots, pcount, xcount, mode, off, lists, ctl);
   return hipGetLastError();
 }

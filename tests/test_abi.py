@@ -44,6 +44,7 @@ def test_status_strings_without_device(lib):
     cfg = mce.mce_config()
     assert mce.mce_config_init(cfg) == 0
     assert (cfg.worker_list, cfg.donate_min_p, cfg.validate, cfg.timeout_ms) == (1, 10, 1, 120000)
+    assert cfg.subgraph == mce.MCE_SUBGRAPH_AUTO
     assert cfg.struct_size == ctypes.sizeof(mce.mce_config)
 
 

@@ -20,12 +20,14 @@ import maximal_clique_enumeration_amd as mce  # noqa: E402
 DEV = torch.device("cuda", 0)
 
 
-@pytest.fixture(scope="module")
-def eng():
+@pytest.fixture(scope="module", params=["partial", "full"])
+def eng(request):
+    """One engine per induced-subgraph encoding (section 3.4): every case that
+    takes this fixture runs under both."""
     if not mce.lib_built():
         from maximal_clique_enumeration_amd import build
         build.build()
-    e = mce.Engine(device=0, timeout_ms=20000)
+    e = mce.Engine(device=0, timeout_ms=20000, subgraph=request.param)
     yield e
     e.close()
 
@@ -37,6 +39,7 @@ def on_gpu(g):
 def check(eng, g, roots=None):
     rp, ci = on_gpu(g)
     r = None if roots is None else torch.from_numpy(np.asarray(roots, np.int32)).to(DEV)
+    print(f"case {g.name} n={g.n} m={g.m}", flush=True)
     got = eng.run(rp, ci, roots=r)
     want = oracle.mce(g.n, g.row_ptr, g.col_idx, roots=roots)
     assert want.complete
