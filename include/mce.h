@@ -64,6 +64,8 @@ typedef enum {
 #define MCE_FLAG_HBM_STAGING 1u  /* keep induced-subgraph rows and DFS stacks in HBM even
                                     when they fit in LDS (section 3.4 data in device memory) */
 #define MCE_FLAG_PHASE_TIMES 2u  /* record per-phase GPU times in mce_run_stats */
+#define MCE_FLAG_COUNTERS 4u     /* count pivot rows and X_X tests (mce_run_stats.pivot_rows,
+                                    xx_tests); the narrowest search kernel skips them otherwise */
 
 /* mce_config.subgraph: how each subtree's induced subgraph is encoded (section
    3.4). Partial: bit rows for P x P only, edges between P and X looked up in the
@@ -111,9 +113,9 @@ typedef struct {
   uint64_t nodes;            /* search-tree nodes whose pivot was evaluated */
   uint64_t leaves;           /* maximal cliques reported (== count minus isolated) */
   uint64_t donations;        /* branches handed to idle wavefronts (section 3.3, Table 2) */
-  uint64_t pivot_rows;       /* sum over nodes of |P u X_P| rows scanned for the pivot */
+  uint64_t pivot_rows;       /* rows scored for the pivot (P u X_P, and X_X with the full subgraph) */
   uint64_t pivot_words;      /* pivot_rows times the bitset width in 64-bit words */
-  uint64_t xx_tests;         /* membership tests of the X_X array against CSR rows */
+  uint64_t xx_tests;         /* X_X entries tested for adjacency to a branch vertex */
   uint64_t table_words;      /* 64-bit words of induced-subgraph tables built */
   uint64_t busy_ticks;       /* sum over wavefronts of wall-clock ticks spent searching */
   uint64_t max_busy_ticks;   /* largest per-wavefront busy time */
@@ -124,6 +126,12 @@ typedef struct {
   double ms_validate, ms_peel, ms_orient;   /* GPU phase times, with MCE_FLAG_PHASE_TIMES */
   double ms_search;          /* search kernels alone (events around each launch), same flag */
   double ms_build;           /* induced-subgraph build kernels, same flag */
+  uint64_t donate_ticks;     /* sum over wavefronts of ticks spent handing branches over */
+  uint64_t setup_ticks;      /* sum over wavefronts of ticks from a wake-up to the search start */
+  uint64_t first_ticks;      /* sum over wavefronts of ticks from kernel start to their first task */
+  uint64_t start_spread_ticks; /* largest gap between the first and last wavefront start of a launch */
+  uint64_t claim_checks;     /* worker-list claim attempts by donors */
+  uint64_t donate_ok_ticks;  /* ticks of the successful donations alone */
 } mce_run_stats;
 
 /* Fills cfg with the defaults: device -1, worker_list 1, donate_min_p 10,

@@ -20,7 +20,7 @@ LIB_PATH = os.path.join(_HERE, "libmce.so")
 MCE_OK, MCE_ERR_ARG, MCE_ERR_GRAPH, MCE_ERR_NOMEM = 0, -1, -2, -3
 MCE_ERR_DEVICE, MCE_ERR_STATE, MCE_ERR_TIMEOUT, MCE_ERR_LIMIT = -4, -5, -6, -7
 MCE_GRAPH_ROWPTR, MCE_GRAPH_RANGE, MCE_GRAPH_LOOP, MCE_GRAPH_ORDER, MCE_GRAPH_ASYM = 1, 2, 4, 8, 16
-MCE_FLAG_HBM_STAGING, MCE_FLAG_PHASE_TIMES = 1, 2
+MCE_FLAG_HBM_STAGING, MCE_FLAG_PHASE_TIMES, MCE_FLAG_COUNTERS = 1, 2, 4
 MCE_SUBGRAPH_AUTO, MCE_SUBGRAPH_PARTIAL, MCE_SUBGRAPH_FULL = 0, 1, 2
 
 # every function the C header declares
@@ -67,7 +67,10 @@ class mce_run_stats(ctypes.Structure):
                 ("kernel_ticks", ctypes.c_uint64), ("tick_hz", ctypes.c_double),
                 ("ms_total", ctypes.c_double), ("ms_validate", ctypes.c_double),
                 ("ms_peel", ctypes.c_double), ("ms_orient", ctypes.c_double),
-                ("ms_search", ctypes.c_double), ("ms_build", ctypes.c_double)]
+                ("ms_search", ctypes.c_double), ("ms_build", ctypes.c_double),
+                ("donate_ticks", ctypes.c_uint64), ("setup_ticks", ctypes.c_uint64),
+                ("first_ticks", ctypes.c_uint64), ("start_spread_ticks", ctypes.c_uint64),
+                ("claim_checks", ctypes.c_uint64), ("donate_ok_ticks", ctypes.c_uint64)]
 
 
 _lib = None
@@ -180,7 +183,8 @@ class Engine:
 
     def __init__(self, device: int | None = None, worker_list: bool = True, donate_min_p: int = 10,
                  validate: bool = True, max_workers: int = 0, timeout_ms: int = 120000,
-                 hbm_staging: bool = False, phase_times: bool = False, subgraph: str = "auto"):
+                 hbm_staging: bool = False, phase_times: bool = False, subgraph: str = "auto",
+                 counters: bool = False):
         import torch
         if device is None:
             device = torch.cuda.current_device()
@@ -193,7 +197,8 @@ class Engine:
         cfg.validate = 1 if validate else 0
         cfg.max_workers = max_workers
         cfg.timeout_ms = timeout_ms
-        cfg.flags = (MCE_FLAG_HBM_STAGING if hbm_staging else 0) | (MCE_FLAG_PHASE_TIMES if phase_times else 0)
+        cfg.flags = ((MCE_FLAG_HBM_STAGING if hbm_staging else 0) | (MCE_FLAG_PHASE_TIMES if phase_times else 0)
+                     | (MCE_FLAG_COUNTERS if counters else 0))
         modes = {"auto": MCE_SUBGRAPH_AUTO, "partial": MCE_SUBGRAPH_PARTIAL, "full": MCE_SUBGRAPH_FULL}
         if subgraph not in modes:
             raise ValueError(f"subgraph must be one of {sorted(modes)}")

@@ -242,7 +242,7 @@ mce_status run_impl(mce_engine* e, int32_t n, int64_t nnz, const int32_t* row_pt
     Plan pl;
     pl.sub = c;
     pl.L = mce_search_layout(c, mode, hctl->sub_maxp[mode][c], hctl->sub_maxx[mode][c], hctl->sub_maxr[mode][c],
-                             hbm);
+                             hbm, (e->cfg.flags & MCE_FLAG_COUNTERS) != 0);
     int nw = mce_search_max_workers(pl.L, e->num_cu);
     if (nw <= 0) return fail(e, MCE_ERR_DEVICE, "search kernel occupancy query failed");
     if (e->cfg.max_workers > 0) nw = std::min(nw, (int)e->cfg.max_workers);
@@ -287,7 +287,7 @@ mce_status run_impl(mce_engine* e, int32_t n, int64_t nnz, const int32_t* row_pt
     if (timing) (void)hipEventRecord(e->ev[evi], s);
     if ((h = mce_launch_build(bp, e->num_cu * 16, s)) != hipSuccess) return hip_fail(e, h, "build launch");
     if (timing) (void)hipEventRecord(e->ev[evi + 1], s);
-    if ((h = mce_launch_wl_init(dp<MceWl>(e->wl), pl.nw, s)) != hipSuccess) return hip_fail(e, h, "wl init");
+    if ((h = mce_launch_wl_init(dp<MceWl>(e->wl), pl.nw, counts[c], s)) != hipSuccess) return hip_fail(e, h, "wl init");
     SearchParams prm{};
     prm.rp = row_ptr;
     prm.ci = col_idx;
@@ -296,6 +296,7 @@ mce_status run_impl(mce_engine* e, int32_t n, int64_t nnz, const int32_t* row_pt
     prm.nroots = counts[c];
     prm.nworkers = pl.nw;
     prm.hcap = L.hcap;
+    prm.l_misc = L.l_misc;
     prm.l_hist = L.l_hist;
     prm.l_hv = L.l_hv;
     prm.l_pid = L.l_pid;
@@ -338,13 +339,24 @@ mce_status run_impl(mce_engine* e, int32_t n, int64_t nnz, const int32_t* row_pt
   if (hctl->status & MCE_E_LIMIT) return fail(e, MCE_ERR_LIMIT, "subtree larger than its width class");
   if (hctl->status & MCE_E_HEAP) return fail(e, MCE_ERR_DEVICE, "induced-subgraph heap overflow");
   std::vector<u64> stat_sum(MCE_NSTAT, 0);
-  u64 max_busy = 0, max_nodes = 0, max_ticks = 0;
-  for (int w = 0; w < stat_rows; w++) {
-    const u64* r = &st[(size_t)w * MCE_NSTAT];
-    for (int i = 0; i < MCE_NSTAT; i++) stat_sum[i] += r[i];
-    max_busy = std::max(max_busy, r[ST_BUSY_TICKS]);
-    max_nodes = std::max(max_nodes, r[ST_NODES]);
-    max_ticks = std::max(max_ticks, r[ST_TOTAL_TICKS]);
+  u64 max_busy = 0, max_nodes = 0, max_ticks = 0, start_spread = 0;
+  {
+    int row = 0;
+    for (const Plan& pl : plan) {
+      u64 smin = ~0ull, smax = 0;
+      for (int w = 0; w < pl.nw; w++, row++) {
+        const u64* r = &st[(size_t)row * MCE_NSTAT];
+        for (int i = 0; i < MCE_NSTAT; i++) stat_sum[i] += r[i];
+        max_busy = std::max(max_busy, r[ST_BUSY_TICKS]);
+        max_nodes = std::max(max_nodes, r[ST_NODES]);
+        max_ticks = std::max(max_ticks, r[ST_TOTAL_TICKS]);
+        if (r[ST_START_ABS]) {
+          smin = std::min(smin, r[ST_START_ABS]);
+          smax = std::max(smax, r[ST_START_ABS]);
+        }
+      }
+      if (smax >= smin && smin != ~0ull) start_spread = std::max(start_spread, smax - smin);
+    }
   }
 
   std::vector<uint64_t> hist(kHistWords, 0);
@@ -378,6 +390,12 @@ mce_status run_impl(mce_engine* e, int32_t n, int64_t nnz, const int32_t* row_pt
   so.max_busy_ticks = max_busy;
   so.max_nodes = max_nodes;
   so.kernel_ticks = max_ticks;
+  so.donate_ticks = stat_sum[ST_DONATE_TICKS];
+  so.setup_ticks = stat_sum[ST_SETUP_TICKS];
+  so.first_ticks = stat_sum[ST_FIRST_TICKS];
+  so.start_spread_ticks = start_spread;
+  so.claim_checks = stat_sum[ST_CHECKS];
+  so.donate_ok_ticks = stat_sum[ST_DONATE_OK_TICKS];
   if (timing) {
     float a = 0, b = 0, c = 0;
     (void)hipEventElapsedTime(&a, e->ev[0], e->ev[1]);

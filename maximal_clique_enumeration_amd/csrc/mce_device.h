@@ -206,6 +206,27 @@ __device__ __forceinline__ void st_relaxed(u32* p, u32 v) {
 __device__ __forceinline__ void st_release(u32* p, u32 v) {
   __hip_atomic_store(p, v, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
 }
+__device__ __forceinline__ u64 ld_relaxed64(const u64* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_relaxed64(u64* p, u64 v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_relaxed_i(int* p, int v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// Wait until every memory operation this wave issued has completed. Agent-scope
+// relaxed atomic stores (sc1) are performed at the device coherence point, so
+// once this wait returns they are visible to agent-scope atomic loads of any
+// wave. Publishing data as "atomic stores, wait, flag store" replaces an
+// agent-scope release fence, whose L2 write-back serialises across the chip
+// when thousands of waves issue it. The signal fences keep the compiler from
+// moving memory operations across the wait.
+__device__ __forceinline__ void wait_stores_complete() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0);
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
 __device__ __forceinline__ void fence_release_agent() { __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent"); }
 __device__ __forceinline__ void fence_acquire_agent() { __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent"); }
 __device__ __forceinline__ void fence_acq_rel_agent() { __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "agent"); }

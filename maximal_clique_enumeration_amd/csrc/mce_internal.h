@@ -26,6 +26,12 @@ enum {
   ST_ROOTS,
   ST_RECEIVED,
   ST_TOTAL_TICKS,
+  ST_DONATE_TICKS,   // handing branches over (claim + mailbox + wake)
+  ST_SETUP_TICKS,    // receiving: mailbox and induced subgraph read until the search starts
+  ST_FIRST_TICKS,    // kernel start until the first task (root or received) starts
+  ST_START_ABS,      // wall-clock tick at which the wave started
+  ST_CHECKS,         // worker-list claim attempts
+  ST_DONATE_OK_TICKS,  // ticks of the successful donations alone
   MCE_NSTAT
 };
 
@@ -36,7 +42,8 @@ struct SearchLayout {
   int pcap, xcap, rcap;   // largest |P|, |X|, row count over the launch's roots
   int levels, hcap;       // stack records, histogram entries
   bool srows, sstack;     // rows + X_X staged in LDS; level stack in LDS
-  int l_hist, l_hv, l_pid, l_stack, l_rows, l_xx;
+  bool counters;          // count pivot rows and X_X tests (width 1 keeps them out of the timed kernel)
+  int l_misc, l_hist, l_hv, l_pid, l_stack, l_rows, l_xx;
   size_t lds_bytes;
   size_t s_stack, s_xx, s_mail, slot_bytes;
 };
@@ -49,7 +56,7 @@ struct SearchParams {
   int nroots;
   int nworkers;
   int hcap;
-  int l_hist, l_hv, l_pid, l_stack, l_rows, l_xx;
+  int l_misc, l_hist, l_hv, l_pid, l_stack, l_rows, l_xx;
   size_t slot_bytes, s_stack, s_xx, s_mail;
   u64* g_hist;           // global histogram (MCE_MAX_P + 2 entries)
   u64* g_hash;
@@ -91,8 +98,8 @@ hipError_t mce_launch_bucket(const int* roots, int nroots, const int* pcount, co
 
 hipError_t mce_launch_build(const BuildParams& prm, int blocks, hipStream_t s);
 
-SearchLayout mce_search_layout(int sub, int mode, int pcap, int xcap, int rcap, bool force_hbm);
+SearchLayout mce_search_layout(int sub, int mode, int pcap, int xcap, int rcap, bool force_hbm, bool counters);
 // Resident wavefronts of a search layout over the whole chip (0 on error).
 int mce_search_max_workers(const SearchLayout& L, int num_cu);
 hipError_t mce_launch_search(const SearchLayout& L, const SearchParams& prm, hipStream_t s);
-hipError_t mce_launch_wl_init(MceWl* wl, int nworkers, hipStream_t s);
+hipError_t mce_launch_wl_init(MceWl* wl, int nworkers, int nroots, hipStream_t s);

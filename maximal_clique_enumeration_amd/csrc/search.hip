@@ -33,36 +33,37 @@
 #include "mce_internal.h"
 
 #define REC_WORDS(W) (3 * (W) + 2)   // per level: P[W], X_P[W], C[W], s, (lpX | open << 32)
-#define MAIL_HDR 3                   // mailbox: (root list index | k << 32), lpX, s; then P, X_P, X_X
+// mailbox (agent-scope atomic words): table offset, (k | lpX << 32), s; then
+// P[W], X_P[W], then the X_X entries as int32
+#define MAIL_HDR 3
 
 // ------------------------------------------------------------------ worker list
+// Every word two waves exchange is an agent-scope relaxed atomic; there is no
+// agent-scope fence anywhere (each would write back or invalidate an L2, which
+// serialises across the chip). Data is published as "atomic stores, wait for
+// completion, flag store" and read after the flag with atomic loads.
+//
 // 64-bit ring slot: sequence number (high half) and wave id + 1 (low half).
-// Producer of ring index t waits for sequence t (the previous lap's consumer is
-// done with the slot) and publishes sequence t + 1; the consumer of index h
-// waits for sequence h + 1 and hands the slot to lap h + nworkers.
-__device__ __forceinline__ u64 ld_acquire64(const u64* p) {
-  return __hip_atomic_load(p, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ void st_release64(u64* p, u64 v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
-}
-
+// The producer of ring index t waits for sequence t (the previous lap's
+// consumer is done with the slot) and publishes sequence t + 1; the consumer of
+// index h waits for sequence h + 1 and hands the slot to lap h + nworkers.
 #define WL_SPIN_LIMIT (1u << 22)
 
 // Receiver side (section 3.3). Gives up this wave's share of n_active; the wave
 // that brings it to zero (no task held anywhere; only active waves donate, so
 // none can appear) writes MCE_FLAG_EXIT into every wake flag. Any other wave
-// enqueues its id and spins on its flag with exponential back-off. Returns 1
+// enqueues its id and sleeps on its flag with exponential back-off. Returns 1
 // with a task in the mailbox (the donor counted this wave active again), 0 to
-// exit. The flag is cleared before the share is given up, so the exit broadcast
-// (ordered after every share release) cannot be overwritten.
+// exit. The flag is cleared, and the clear completed, before the share is given
+// up, so the exit broadcast (issued after every share release) is never lost.
 __device__ int wl_wait(MceWl* wl, int wid, int nworkers, u64 deadline, u32* status) {
   int res = 0, bcast = 0;
   if (lane_id() == 0) {
     u32* my = &wl->flag[(size_t)wid * MCE_LINE_WORDS];
     st_relaxed(my, 0u);
+    wait_stores_complete();
     const int left =
-        __hip_atomic_fetch_add(&wl->n_active, -1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT) - 1;
+        __hip_atomic_fetch_add(&wl->n_active, -1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) - 1;
     if (left <= 0) {
       if (left < 0) atomicOr(status, MCE_E_PROTO);
       bcast = 1;
@@ -70,16 +71,19 @@ __device__ int wl_wait(MceWl* wl, int wid, int nworkers, u64 deadline, u32* stat
       const u32 t = __hip_atomic_fetch_add(&wl->tail, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       u64* slot = &wl->ring[t % (u32)nworkers];
       u32 spins = 0;
-      while ((u32)(ld_acquire64(slot) >> 32) != t) {
+      while ((u32)(ld_relaxed64(slot) >> 32) != t) {
         if (++spins > WL_SPIN_LIMIT) {
           atomicOr(status, MCE_E_PROTO);
           break;
         }
         __builtin_amdgcn_s_sleep(1);
       }
-      st_release64(slot, ((u64)(t + 1u) << 32) | (u64)(u32)(wid + 1));
-      __hip_atomic_fetch_add(&wl->avail, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
-      int backoff = 1;
+      st_relaxed64(slot, ((u64)(t + 1u) << 32) | (u64)(u32)(wid + 1));
+      wait_stores_complete();
+      __hip_atomic_fetch_add(&wl->avail, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      // exponential back-off in a few long sleeps: a sleeping wave issues a
+      // handful of scalar instructions per several microseconds, so idle waves
+      // do not starve the compute unit's scalar unit that busy waves need
       u32 it = 0;
       for (;;) {
         const u32 f = ld_relaxed(my);
@@ -89,11 +93,13 @@ __device__ int wl_wait(MceWl* wl, int wid, int nworkers, u64 deadline, u32* stat
         }
         if ((++it & 7u) == 0 && past_deadline(deadline)) {
           atomicOr(status, MCE_E_TIMEOUT);
-          st_release(&wl->done, 1u);
+          st_relaxed(&wl->done, 1u);
           break;
         }
-        for (int i = 0; i < backoff; i++) __builtin_amdgcn_s_sleep(2);
-        if (backoff < 32) backoff <<= 1;
+        if (it < 4) __builtin_amdgcn_s_sleep(4);
+        else if (it < 8) __builtin_amdgcn_s_sleep(16);
+        else if (it < 12) __builtin_amdgcn_s_sleep(64);
+        else __builtin_amdgcn_s_sleep(127);
       }
     }
   }
@@ -102,34 +108,34 @@ __device__ int wl_wait(MceWl* wl, int wid, int nworkers, u64 deadline, u32* stat
     for (int i = lane_id(); i < nworkers; i += MCE_WAVE)
       st_relaxed(&wl->flag[(size_t)i * MCE_LINE_WORDS], MCE_FLAG_EXIT);
   }
-  fence_acquire_agent();
   return res;
 }
 
 // Donor side: take one idle wave out of the ring, or -1. The claimed wave is
-// counted active before the donor can ever give up its own share, so n_active
-// cannot reach zero while the donated branch is in flight.
+// counted active before the donor can ever give up its own share (same-address
+// atomics of one wave stay in order), so n_active cannot reach zero while the
+// donated branch is in flight.
 __device__ int wl_claim(MceWl* wl, int nworkers, u32* status) {
   int r = -1;
   if (lane_id() == 0) {
     if (ld_relaxed(&wl->avail) > 0) {
-      const int old = __hip_atomic_fetch_add(&wl->avail, -1, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT);
+      const int old = __hip_atomic_fetch_add(&wl->avail, -1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       if (old > 0) {
         const u32 h = __hip_atomic_fetch_add(&wl->head, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         u64* slot = &wl->ring[h % (u32)nworkers];
         u64 val = 0;
         u32 spins = 0;
-        while ((u32)((val = ld_acquire64(slot)) >> 32) != h + 1u) {
+        while ((u32)((val = ld_relaxed64(slot)) >> 32) != h + 1u) {
           if (++spins > WL_SPIN_LIMIT) {
             atomicOr(status, MCE_E_PROTO);
-            st_release(&wl->done, 1u);
+            st_relaxed(&wl->done, 1u);
             break;
           }
           __builtin_amdgcn_s_sleep(1);
         }
         if ((u32)(val >> 32) == h + 1u) {
           r = (int)(u32)val - 1;
-          st_release64(slot, (u64)(h + (u32)nworkers) << 32);
+          st_relaxed64(slot, (u64)(h + (u32)nworkers) << 32);
           __hip_atomic_fetch_add(&wl->n_active, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
       } else {
@@ -138,6 +144,32 @@ __device__ int wl_claim(MceWl* wl, int nworkers, u32* status) {
     }
   }
   return read_lane(r, 0);
+}
+
+// Wake a claimed receiver after its mailbox has been written with atomic stores.
+__device__ __forceinline__ void wl_wake(MceWl* wl, int rcv) {
+  wait_stores_complete();
+  if (lane_id() == 0) st_relaxed(&wl->flag[(size_t)rcv * MCE_LINE_WORDS], MCE_FLAG_TASK);
+}
+
+// Phase 1 (section 3.3): the next first-level subtree from the shared counter,
+// or nroots when none is left. Every subtree goes through the counter: a wave
+// that has not started yet must never hold a subtree that other waves count as
+// taken, or they could finish and leave while it still needs the worker list.
+__device__ __forceinline__ u32 next_root(MceWl* wl, u32 nroots) {
+  u32 idx = nroots;
+  if (lane_id() == 0) {
+    if (ld_relaxed(&wl->root_ctr) < nroots) idx = atomicAdd(&wl->root_ctr, 1u);
+  }
+  return (u32)read_lane((int)idx, 0);
+}
+
+// Count this wave active, and wait until the increment is performed: it must
+// precede the wave's first root-counter increment, or another wave could see
+// the roots gone and the count at zero while this wave holds a subtree.
+__device__ __forceinline__ void wl_join(MceWl* wl) {
+  if (lane_id() == 0) __hip_atomic_fetch_add(&wl->n_active, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  wait_stores_complete();
 }
 
 // ------------------------------------------------------------------ X_X membership
@@ -217,6 +249,23 @@ __device__ bool xx_any(const int* xx, int L, const T& test) {
   return false;
 }
 
+// Copy the entries of xx[0, L) adjacent to v to a mailbox, in order, with
+// atomic stores; returns how many.
+template <class T>
+__device__ int xx_filter_copy(const int* xx, int L, const T& test, int* dst) {
+  const int lane = lane_id();
+  int n = 0;
+  for (int c = 0; c < L; c += MCE_WAVE) {
+    const int i = c + lane;
+    const int a = i < L ? xx[i] : 0;
+    const bool keep = i < L && test.adj(a);
+    const u64 m = ballot(keep);
+    if (keep) st_relaxed_i(&dst[n + mbcnt(m)], a);
+    n += __popcll(m);
+  }
+  return n;
+}
+
 // ------------------------------------------------------------------ the kernel
 template <int W, bool IPX, bool SROWS, bool SSTACK>
 __global__ __launch_bounds__(64) void k_search(SearchParams prm) {
@@ -246,7 +295,7 @@ __global__ __launch_bounds__(64) void k_search(SearchParams prm) {
   __syncthreads();
   // this wave is active until phase 1 finds the roots exhausted (wl_wait gives
   // the share back)
-  if (lane == 0) __hip_atomic_fetch_add(&wl->n_active, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  wl_join(wl);
 
   u64 hacc = 0;
   u64 st_nodes = 0, st_leaves = 0, st_don = 0, st_prow = 0, st_xx = 0, st_roots = 0, st_recv = 0;
@@ -257,36 +306,34 @@ __global__ __launch_bounds__(64) void k_search(SearchParams prm) {
 
   for (;;) {
     // ---------------------------------------------------------- get a task
-    int tidx = 0, k0 = 1, lpx = 0;
-    u64 s = 0, pj = 0, xj = 0;
+    int k0 = 1, lpx = 0;
+    u64 toff = 0, s = 0, pj = 0, xj = 0;
     if (!phase2) {
-      u32 idx = 0;
-      if (lane == 0) idx = atomicAdd(&wl->root_ctr, 1u);
-      idx = (u32)read_lane((int)idx, 0);
+      const u32 idx = next_root(wl, (u32)prm.nroots);
       if (idx >= (u32)prm.nroots) {
         phase2 = true;
         continue;
       }
-      tidx = (int)idx;
+      toff = uni(prm.tab_off[idx]);
     } else {
       if (!prm.worker_list) break;
       const u64 t0 = wall_clock64();
       const int got = wl_wait(wl, wid, prm.nworkers, deadline, prm.status);
       idle_ticks += wall_clock64() - t0;
       if (!got) break;
-      const u64 h0 = mail[0];
-      tidx = (int)(u32)h0;
-      k0 = (int)(h0 >> 32);
-      lpx = (int)(u32)mail[1];
-      s = mail[2];
+      toff = uni(ld_relaxed64(&mail[0]));
+      const u64 m1 = uni(ld_relaxed64(&mail[1]));
+      k0 = (int)(u32)m1;
+      lpx = (int)(m1 >> 32);
+      s = uni(ld_relaxed64(&mail[2]));
       if (lane < W) {
-        pj = mail[MAIL_HDR + lane];
-        xj = mail[MAIL_HDR + W + lane];
+        pj = ld_relaxed64(&mail[MAIL_HDR + lane]);
+        xj = ld_relaxed64(&mail[MAIL_HDR + W + lane]);
       }
     }
 
     // ---------------------------------------------------------- the root's induced subgraph
-    const u64* T = prm.heap + prm.tab_off[tidx];
+    const u64* T = prm.heap + toff;
     const u64 hdr = T[0];
     const int p = (int)(u32)hdr;
     const int x = (int)(hdr >> 32);
@@ -316,8 +363,8 @@ __global__ __launch_bounds__(64) void k_search(SearchParams prm) {
       for (int i = lane; i < x; i += MCE_WAVE) xx[i] = IPX ? p + i : gids[p + i];
       st_roots++;
     } else {
-      const int* mx = (const int*)(mail + MAIL_HDR + 2 * W);
-      for (int i = lane; i < lpx; i += MCE_WAVE) xx[i] = mx[i];
+      const u32* mx = (const u32*)(mail + MAIL_HDR + 2 * W);
+      for (int i = lane; i < lpx; i += MCE_WAVE) xx[i] = (int)ld_relaxed(&mx[i]);
       st_recv++;
     }
     __syncthreads();
@@ -344,7 +391,7 @@ __global__ __launch_bounds__(64) void k_search(SearchParams prm) {
               stop = 1;
             } else if (past_deadline(deadline)) {
               atomicOr(prm.status, MCE_E_TIMEOUT);
-              st_release(&wl->done, 1u);
+              st_relaxed(&wl->done, 1u);
               stop = 1;
             }
           }
@@ -484,17 +531,16 @@ __global__ __launch_bounds__(64) void k_search(SearchParams prm) {
               u64* dm = (u64*)(dslot + prm.s_mail);
               int* dx = (int*)(dm + MAIL_HDR + 2 * W);
               if (lane < W) {
-                dm[MAIL_HDR + lane] = pn;
-                dm[MAIL_HDR + W + lane] = xn;
+                st_relaxed64(&dm[MAIL_HDR + lane], pn);
+                st_relaxed64(&dm[MAIL_HDR + W + lane], xn);
               }
-              for (int i = lane; i < lpx_child; i += MCE_WAVE) dx[i] = xx[i];
+              for (int i = lane; i < lpx_child; i += MCE_WAVE) st_relaxed_i(&dx[i], xx[i]);
               if (lane == 0) {
-                dm[0] = (u64)(u32)tidx | ((u64)(u32)k_child << 32);
-                dm[1] = (u64)(u32)lpx_child;
-                dm[2] = s_child;
+                st_relaxed64(&dm[0], toff);
+                st_relaxed64(&dm[1], (u64)(u32)k_child | ((u64)(u32)lpx_child << 32));
+                st_relaxed64(&dm[2], s_child);
               }
-              fence_release_agent();
-              if (lane == 0) st_release(&wl->flag[(size_t)rcv * MCE_LINE_WORDS], MCE_FLAG_TASK);
+              wl_wake(wl, rcv);
               st_don++;
               wl_gap = 1;
               continue;
@@ -553,14 +599,397 @@ __global__ __launch_bounds__(64) void k_search(SearchParams prm) {
   }
 }
 
+// ------------------------------------------------------------------ width 1 (|P_root| <= 64)
+// The hot case: every set over P fits one 64-bit word, so the current level's
+// P, X_P, C, hash sum, lpX and open count are wave-uniform scalars (SALU work,
+// scalar branches), and lane i holds row i of P, the hash term and the id of P
+// member i, read by v_readlane. The level stack lives in VGPRs, level l in lane
+// l (depth <= |P_root| - 2 < 64), and clique sizes below 64 are counted in
+// lane k of a per-lane histogram. Few values stay live in scalar registers:
+// timing and rare counters sit in LDS; CNT adds the work counters (pivot rows
+// scored, X_X entries tested) for measurement runs.
+template <bool IPX, bool SROWS, bool CNT>
+__global__ __launch_bounds__(64) void k_search_w1(SearchParams prm) {
+  extern __shared__ u64 lds[];
+
+  const int lane = lane_id();
+  const int wid = blockIdx.x;
+  MceWl* wl = prm.wl;
+
+  char* slot = prm.slots + (size_t)wid * prm.slot_bytes;
+  u64* mail = (u64*)(slot + prm.s_mail);
+  u64* s_hist = lds + prm.l_hist;   // clique sizes >= 64
+  // [0] start tick, [1] deadline, [2] idle ticks, [3] nodes, [4] donate ticks,
+  // [5] setup ticks, [6] first-task tick, [7] ticks of successful donations
+  u64* s_misc = lds + prm.l_misc;
+  int* xx = SROWS ? (int*)(lds + prm.l_xx) : (int*)(slot + prm.s_xx);
+  u64* lrows = lds + prm.l_rows;
+
+  if (ld_relaxed(prm.status) & (MCE_E_HEAP | MCE_E_LIMIT)) return;
+  for (int i = lane; i < prm.hcap; i += MCE_WAVE) s_hist[i] = 0;
+  if (lane == 0) {
+    const u64 t0 = wall_clock64();
+    s_misc[0] = t0;
+    s_misc[1] = t0 + prm.budget;
+    s_misc[2] = 0;
+    s_misc[3] = 0;
+    s_misc[4] = 0;
+    s_misc[5] = 0;
+    s_misc[6] = 0;
+    s_misc[7] = 0;
+  }
+  wl_join(wl);
+  __syncthreads();
+
+  u64 hist_lane = 0;   // lane k: maximal cliques of size k (k < 64)
+  u64 hacc = 0;
+  u32 nodes = 0;       // since the last fold into s_misc[3]
+  u32 st_don = 0, st_roots = 0, st_recv = 0, st_checks = 0;
+  u64 st_prow = 0, st_xx = 0;   // CNT only
+  bool phase2 = false;
+  bool abort = false;
+  int wl_countdown = 1, wl_gap = 1;
+
+  for (;;) {
+    // ---------------------------------------------------------- get a task
+    int k0 = 1, lpx = 0;
+    u64 toff = 0, s = 0, P = 0, XP = 0;
+    if (!phase2) {
+      const u32 idx = next_root(wl, (u32)prm.nroots);
+      if (idx >= (u32)prm.nroots) {
+        phase2 = true;
+        continue;
+      }
+      toff = uni(prm.tab_off[idx]);
+    } else {
+      if (!prm.worker_list) break;
+      const u64 t0 = wall_clock64();
+      const int got = wl_wait(wl, wid, prm.nworkers, uni(s_misc[1]), prm.status);
+      if (lane == 0) {
+        const u64 t1 = wall_clock64();
+        s_misc[2] += t1 - t0;
+        s_misc[5] -= t1;   // plus the search start below
+      }
+      if (!got) {
+        if (lane == 0) s_misc[5] += wall_clock64();
+        break;
+      }
+      toff = uni(ld_relaxed64(&mail[0]));
+      const u64 m1 = uni(ld_relaxed64(&mail[1]));
+      k0 = (int)(u32)m1;
+      lpx = (int)(m1 >> 32);
+      s = uni(ld_relaxed64(&mail[2]));
+      P = uni(ld_relaxed64(&mail[MAIL_HDR]));
+      XP = uni(ld_relaxed64(&mail[MAIL_HDR + 1]));
+    }
+
+    // ---------------------------------------------------------- the root's induced subgraph
+    const u64* T = prm.heap + toff;
+    const u64 hdr = uni(T[0]);
+    const int p = (int)(u32)hdr;
+    const int x = (int)(hdr >> 32);
+    const int nrows = IPX ? p + x : p;
+    const u64* grow = T + 3;
+    const u64* ghv = grow + nrows;
+    const int* gids = (const int*)(ghv + p);
+    const u64* rows;
+    if constexpr (SROWS) {
+      if (IPX) {
+        for (int i = p + lane; i < nrows; i += MCE_WAVE) lrows[i] = grow[i];   // X rows
+      }
+      rows = lrows;
+    } else {
+      rows = grow;
+    }
+    const u64 myrow = lane < p ? grow[lane] : 0ull;
+    const u64 myhv = lane < p ? ghv[lane] : 0ull;
+    const int mypid = (!IPX && lane < p) ? gids[lane] : 0;
+    if (!phase2) {
+      s = uni(T[2]);
+      lpx = x;
+      P = p >= 64 ? ~0ull : ((1ull << p) - 1);
+      for (int i = lane; i < x; i += MCE_WAVE) xx[i] = IPX ? p + i : gids[p + i];
+      st_roots++;
+    } else {
+      const u32* mx = (const u32*)(mail + MAIL_HDR + 2);
+      for (int i = lane; i < lpx; i += MCE_WAVE) xx[i] = (int)ld_relaxed(&mx[i]);
+      st_recv++;
+    }
+    __syncthreads();
+    if (lane == 0) {
+      const u64 t1 = wall_clock64();
+      if (phase2) s_misc[5] += t1;
+      if (s_misc[6] == 0) s_misc[6] = t1;
+    }
+
+    // ---------------------------------------------------------- depth-first search
+    u64 stP = 0, stX = 0, stC = 0, stS = 0, stL = 0;   // level stack, level l in lane l
+    u64 C = 0;
+    int l = 0;
+    bool need_pivot = true;
+    for (;;) {
+      if (need_pivot) {
+        need_pivot = false;
+        if ((++nodes & 1023u) == 0) {
+          int stop = 0;
+          if (lane == 0) {
+            s_misc[3] += nodes;
+            nodes = 0;
+            if (ld_relaxed(&wl->done)) {
+              stop = 1;
+            } else if (past_deadline(s_misc[1])) {
+              atomicOr(prm.status, MCE_E_TIMEOUT);
+              st_relaxed(&wl->done, 1u);
+              stop = 1;
+            }
+          }
+          nodes = (u32)read_lane((int)nodes, 0);
+          if (read_lane(stop, 0)) {
+            abort = true;
+            break;
+          }
+        }
+        // Tomita pivot over P u X_P (lane i scores P member i), then X_X with the
+        // full subgraph; ties to the smallest local index
+        const u64 cand = P | XP;
+        if constexpr (CNT) st_prow += (u64)__popcll(cand);
+        u32 best = 0;
+        if ((cand >> lane) & 1ull) best = ((u32)__popcll(P & myrow) << 20) | (u32)(MCE_MAX_LOCAL - lane);
+        if constexpr (IPX) {
+          if (lpx > 0) {
+            const u32 pc = (u32)__popcll(P);
+            if constexpr (CNT) st_prow += (u64)lpx;
+            for (int c0 = 0; c0 < lpx; c0 += MCE_WAVE) {
+              const int i = c0 + lane;
+              if (i < lpx) {
+                const int a = xx[i];
+                const u32 key = ((u32)__popcll(P & rows[a]) << 20) | (u32)(MCE_MAX_LOCAL - a);
+                best = best > key ? best : key;
+              }
+              if (c0 + MCE_WAVE < lpx && (wave_max_u32(best) >> 20) == pc) break;
+            }
+          }
+        }
+        best = wave_max_u32(best);
+        const int u = MCE_MAX_LOCAL - (int)(best & (u32)MCE_MAX_LOCAL);
+        const u64 ru = u < p ? read_lane(myrow, u) : uni(rows[u]);
+        C = P & ~ru;
+
+        // Donation (section 3.3), checked at node entry with a back-off while
+        // nobody is idle. The branch handed over is the first unexplored one of
+        // the shallowest level that has any (the largest piece of work this wave
+        // holds); the current level qualifies only with another branch left.
+        // Taking a sibling out of order is sound: the receiver's X holds every
+        // sibling taken before it, and the donor's later siblings see it in X.
+        if (prm.worker_list && --wl_countdown <= 0) {
+          wl_countdown = wl_gap;
+          const u64 sm = ballot(lane < l && stC != 0);
+          int dl = -1;
+          if (sm) dl = __builtin_ctzll(sm);
+          else if (__popcll(C) >= 2) dl = l;
+          if (dl >= 0) {
+            u64 dP = P, dX = XP, dC = C, ds = s;
+            int dlpx = lpx;
+            if (dl < l) {
+              dP = read_lane(stP, dl);
+              dX = read_lane(stX, dl);
+              dC = read_lane(stC, dl);
+              ds = read_lane(stS, dl);
+              dlpx = (int)(u32)read_lane(stL, dl);
+            }
+            const int v = __builtin_ctzll(dC);
+            const u64 vbit = 1ull << v;
+            const u64 rv = read_lane(myrow, v);
+            const u64 pn = dP & rv;
+            const u64 xn = dX & rv;
+            if (__popcll(pn) >= prm.donate_min_p) {
+              const u64 td = wall_clock64();
+              const int rcv = wl_claim(wl, prm.nworkers, prm.status);
+              st_checks++;
+              if (rcv >= 0) {
+                char* dslot = prm.slots + (size_t)rcv * prm.slot_bytes;
+                u64* dm = (u64*)(dslot + prm.s_mail);
+                int* dx = (int*)(dm + MAIL_HDR + 2);
+                int lpxc = 0;
+                if (dlpx > 0) {
+                  XxTest<1, IPX> test;
+                  test.rows = rows;
+                  test.rp = prm.rp;
+                  test.ci = prm.ci;
+                  test.v = v;
+                  if constexpr (!IPX) {
+                    test.vg = read_lane(mypid, v);
+                    test.va = prm.rp[test.vg];
+                    test.vb = prm.rp[test.vg + 1];
+                  }
+                  lpxc = xx_filter_copy(xx, dlpx, test, dx);
+                }
+                const u64 s_don = ds + read_lane(myhv, v);
+                if (lane == 0) {
+                  st_relaxed64(&dm[0], toff);
+                  st_relaxed64(&dm[1], (u64)(u32)(k0 + dl + 1) | ((u64)(u32)lpxc << 32));
+                  st_relaxed64(&dm[2], s_don);
+                  st_relaxed64(&dm[MAIL_HDR], pn);
+                  st_relaxed64(&dm[MAIL_HDR + 1], xn);
+                }
+                wl_wake(wl, rcv);
+                // the donor's level dl moves on past v: C -= {v}, P -= {v}, X_P += {v}
+                if (dl < l) {
+                  if (lane == dl) {
+                    stC = dC ^ vbit;
+                    stP = dP ^ vbit;
+                    stX = dX | vbit;
+                  }
+                } else {
+                  C ^= vbit;
+                  P ^= vbit;
+                  XP |= vbit;
+                }
+                st_don++;
+                wl_gap = 1;
+                wl_countdown = 1;
+                if (lane == 0) {
+                  const u64 dt = wall_clock64() - td;
+                  s_misc[4] += dt;
+                  s_misc[7] += dt;
+                }
+              } else {
+                if (lane == 0) s_misc[4] += wall_clock64() - td;
+                wl_gap = wl_gap < 32 ? 2 * wl_gap : 32;
+                wl_countdown = wl_gap;
+              }
+            }
+          }
+        }
+      }
+
+      // next branch of this level: the lowest vertex of C = P - N(pivot)
+      if (C == 0) {
+        if (l == 0) break;
+        l--;
+        P = read_lane(stP, l);
+        XP = read_lane(stX, l);
+        C = read_lane(stC, l);
+        s = read_lane(stS, l);
+        lpx = (int)(u32)read_lane(stL, l);
+        continue;
+      }
+      const int v = __builtin_ctzll(C);
+      const u64 vbit = 1ull << v;
+      C ^= vbit;   // C -= {v}; P -= {v}; X_P += {v} (Algorithm 2)
+      P ^= vbit;
+      XP |= vbit;
+      const u64 rv = read_lane(myrow, v);
+      const u64 pn = P & rv;   // P n N(v)
+      const u64 xn = XP & rv;  // X_P n N(v)
+      if (pn == 0) {
+        // P n N(v) is empty: R u {v} is maximal iff X n N(v) is empty too
+        if (xn == 0) {
+          bool maximal = true;
+          if (lpx > 0) {
+            if constexpr (CNT) st_xx += (u64)lpx;
+            XxTest<1, IPX> test;
+            test.rows = rows;
+            test.rp = prm.rp;
+            test.ci = prm.ci;
+            test.v = v;
+            if constexpr (!IPX) {
+              test.vg = read_lane(mypid, v);
+              test.va = prm.rp[test.vg];
+              test.vb = prm.rp[test.vg + 1];
+            }
+            maximal = !xx_any(xx, lpx, test);
+          }
+          if (maximal) {
+            const int k = k0 + l + 1;
+            hacc += mce_clique_term(s + read_lane(myhv, v), k);
+            if (k < 64) {
+              hist_lane += lane == k ? 1ull : 0ull;
+            } else if (lane == 0) {
+              s_hist[k] += 1;
+            }
+          }
+        }
+        continue;
+      }
+      // X_X n N(v): stable partition, the child's part is xx[0, lpx_child)
+      int lpx_child = 0;
+      if (lpx > 0) {
+        if constexpr (CNT) st_xx += (u64)lpx;
+        XxTest<1, IPX> test;
+        test.rows = rows;
+        test.rp = prm.rp;
+        test.ci = prm.ci;
+        test.v = v;
+        if constexpr (!IPX) {
+          test.vg = read_lane(mypid, v);
+          test.va = prm.rp[test.vg];
+          test.vb = prm.rp[test.vg + 1];
+        }
+        lpx_child = xx_partition(xx, lpx, test);
+      }
+      // descend: save this level in lane l, the child becomes the current level
+      if (lane == l) {
+        stP = P;
+        stX = XP;
+        stC = C;
+        stS = s;
+        stL = (u64)(u32)lpx;
+      }
+      l++;
+      s += read_lane(myhv, v);
+      P = pn;
+      XP = xn;
+      lpx = lpx_child;
+      need_pivot = true;
+    }
+    if (abort) break;
+  }
+
+  // ---------------------------------------------------------- flush
+  const u64 t_end = wall_clock64();
+  u64 leaves = wave_sum_u64(hist_lane);
+  if (!abort) {
+    __syncthreads();
+    if (hist_lane) atomicAdd(&prm.g_hist[lane], hist_lane);
+    for (int i = 64 + lane; i < prm.hcap; i += MCE_WAVE) {
+      const u64 h = s_hist[i];
+      if (h) atomicAdd(&prm.g_hist[i], h);
+    }
+    if (lane == 0 && hacc) atomicAdd(prm.g_hash, hacc);
+  }
+  for (int i = 64; i < prm.hcap; i++) leaves += s_hist[i];
+  if (lane == 0) {
+    u64* st = prm.stats + (size_t)wid * MCE_NSTAT;
+    const u64 total = t_end - s_misc[0];
+    st[ST_NODES] = s_misc[3] + nodes;
+    st[ST_LEAVES] = leaves;
+    st[ST_DONATIONS] = st_don;
+    st[ST_PIVOT_ROWS] = st_prow;
+    st[ST_PIVOT_WORDS] = st_prow;
+    st[ST_XX_TESTS] = st_xx;
+    st[ST_IP_ROWS] = 0;
+    st[ST_BUSY_TICKS] = total - s_misc[2];
+    st[ST_ROOTS] = st_roots;
+    st[ST_RECEIVED] = st_recv;
+    st[ST_TOTAL_TICKS] = total;
+    st[ST_DONATE_TICKS] = s_misc[4];
+    st[ST_SETUP_TICKS] = s_misc[5];
+    st[ST_FIRST_TICKS] = s_misc[6] ? s_misc[6] - s_misc[0] : total;
+    st[ST_START_ABS] = s_misc[0];
+    st[ST_CHECKS] = st_checks;
+    st[ST_DONATE_OK_TICKS] = s_misc[7];
+  }
+}
+
 // Worker-list reset before a launch: counters zero, ring slot i at sequence i,
 // wake flags of the launch's waves zero.
-__global__ void k_wl_init(MceWl* wl, int nworkers) {
+__global__ void k_wl_init(MceWl* wl, int nworkers, int nroots) {
   const int tid = blockIdx.x * blockDim.x + threadIdx.x;
   const int nt = gridDim.x * blockDim.x;
   u32* head = (u32*)wl;
   const int nhead = (int)(offsetof(MceWl, ring) / 4);
-  for (int i = tid; i < nhead; i += nt) head[i] = 0;
+  for (int i = tid; i < nhead; i += nt) head[i] = 0u;
   for (int i = tid; i < nworkers; i += nt) {
     wl->ring[i] = (u64)(u32)i << 32;
     wl->flag[(size_t)i * MCE_LINE_WORDS] = 0;
@@ -568,9 +997,9 @@ __global__ void k_wl_init(MceWl* wl, int nworkers) {
 }
 
 // ------------------------------------------------------------------ host side
-hipError_t mce_launch_wl_init(MceWl* wl, int nworkers, hipStream_t s) {
+hipError_t mce_launch_wl_init(MceWl* wl, int nworkers, int nroots, hipStream_t s) {
   hipLaunchKernelGGL(k_wl_init, dim3(std::max(1, std::min(64, (nworkers + 255) / 256))), dim3(256), 0, s, wl,
-                     nworkers);
+                     nworkers, nroots);
   return hipGetLastError();
 }
 
@@ -579,14 +1008,12 @@ static const void* fn() {
   return (const void*)k_search<W, IPX, SR, SS>;
 }
 
-// Variants: widths 1, 2, 4 stage rows (light sub-classes) and stack in LDS as
-// the layout allows; wider classes keep both in HBM.
+// Variants (width 1 has its own kernel): widths 2 and 4 stage rows (light
+// sub-classes) and the stack in LDS as the layout allows; wider classes keep
+// both in HBM.
 template <bool IPX>
 static const void* pick(int wclass, bool srows, bool sstack) {
   switch (wclass) {
-    case 0:
-      return srows ? (sstack ? fn<1, IPX, true, true>() : fn<1, IPX, true, false>())
-                   : (sstack ? fn<1, IPX, false, true>() : fn<1, IPX, false, false>());
     case 1:
       return srows ? (sstack ? fn<2, IPX, true, true>() : fn<2, IPX, true, false>())
                    : (sstack ? fn<2, IPX, false, true>() : fn<2, IPX, false, false>());
@@ -601,6 +1028,15 @@ static const void* pick(int wclass, bool srows, bool sstack) {
 }
 
 static const void* search_kernel(const SearchLayout& L) {
+  if (L.wclass == 0) {
+    const bool ipx = L.mode == MCE_MODE_IPX;
+    if (L.counters)
+      return ipx ? (L.srows ? (const void*)k_search_w1<true, true, true> : (const void*)k_search_w1<true, false, true>)
+                 : (L.srows ? (const void*)k_search_w1<false, true, true>
+                            : (const void*)k_search_w1<false, false, true>);
+    return ipx ? (L.srows ? (const void*)k_search_w1<true, true, false> : (const void*)k_search_w1<true, false, false>)
+               : (L.srows ? (const void*)k_search_w1<false, true, false> : (const void*)k_search_w1<false, false, false>);
+  }
   if (L.wclass >= 3 && (L.srows || L.sstack)) return nullptr;
   return L.mode == MCE_MODE_IPX ? pick<true>(L.wclass, L.srows, L.sstack) : pick<false>(L.wclass, L.srows, L.sstack);
 }
@@ -609,8 +1045,9 @@ static size_t a256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 // LDS words: histogram, hash terms, P ids (partial only), then the stack and the
 // staged rows and X_X array when they are placed in LDS.
-SearchLayout mce_search_layout(int sub, int mode, int pcap, int xcap, int rcap, bool force_hbm) {
+SearchLayout mce_search_layout(int sub, int mode, int pcap, int xcap, int rcap, bool force_hbm, bool counters) {
   SearchLayout L{};
+  L.counters = counters;
   L.sub = sub;
   L.wclass = sub >> 1;
   L.mode = mode;
@@ -624,14 +1061,17 @@ SearchLayout mce_search_layout(int sub, int mode, int pcap, int xcap, int rcap, 
   const size_t rec = (size_t)REC_WORDS(W);
   L.srows = !force_hbm && light && L.wclass <= 2;
   const size_t stack_words = (size_t)L.levels * rec;
-  L.sstack = !force_hbm && L.wclass <= 2 && stack_words * 8 <= 12288;
+  // width 1 keeps its level stack in VGPRs
+  L.sstack = L.wclass > 0 && !force_hbm && L.wclass <= 2 && stack_words * 8 <= 12288;
   size_t o = 0;
+  L.l_misc = (int)o;
+  o += 8;   // width-1 kernel: timing and rare counters
   L.l_hist = (int)o;
   o += (size_t)L.hcap;
   L.l_hv = (int)o;
-  o += (size_t)L.pcap;
+  if (L.wclass > 0) o += (size_t)L.pcap;   // width 1 keeps hash terms and ids in VGPRs
   L.l_pid = (int)o;
-  if (mode == MCE_MODE_IP) o += ((size_t)L.pcap + 1) / 2;
+  if (L.wclass > 0 && mode == MCE_MODE_IP) o += ((size_t)L.pcap + 1) / 2;
   L.l_stack = (int)o;
   if (L.sstack) o += stack_words;
   L.l_rows = (int)o;
