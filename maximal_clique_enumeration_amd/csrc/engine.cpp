@@ -287,7 +287,7 @@ mce_status run_impl(mce_engine* e, int32_t n, int64_t nnz, const int32_t* row_pt
     if (timing) (void)hipEventRecord(e->ev[evi], s);
     if ((h = mce_launch_build(bp, e->num_cu * 16, s)) != hipSuccess) return hip_fail(e, h, "build launch");
     if (timing) (void)hipEventRecord(e->ev[evi + 1], s);
-    if ((h = mce_launch_wl_init(dp<MceWl>(e->wl), pl.nw, counts[c], s)) != hipSuccess) return hip_fail(e, h, "wl init");
+    if ((h = mce_launch_wl_init(dp<MceWl>(e->wl), pl.nw, s)) != hipSuccess) return hip_fail(e, h, "wl init");
     SearchParams prm{};
     prm.rp = row_ptr;
     prm.ci = col_idx;

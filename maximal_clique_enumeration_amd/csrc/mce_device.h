@@ -91,35 +91,36 @@ struct MceCtl {
   u32 bar_gen;
 };
 
-// Worker-list state of one search launch (section 3.3 of the pages), zeroed
-// before the launch. Idle wavefronts enqueue their ids in a multi-producer
-// multi-consumer ring (capacity = wavefronts of the launch, so it cannot
-// overflow) and sleep on a wake flag of their own. Every hot counter sits on
-// its own 128-byte line.
+// Worker-list state of one search launch (section 3.3 of the pages). Each
+// wavefront owns one 128-byte line: word 0 is its wake flag, word 16 its
+// request word. A wave that runs out of work closes its request word, gives up
+// its share of n_active and asks busy waves for branches: it picks a wave at
+// random and, if that wave's request word is open (0), writes its own id + 1
+// there with a compare-and-swap, then sleeps on its wake flag. A busy wave
+// reads only its own request word (once per search-tree node) and answers with
+// a branch (MCE_FLAG_TASK, after counting the receiver active) or with
+// MCE_FLAG_RETRY. Every hot word is private to one wave, so no atomic is
+// contended by thousands of waves.
 //
 // Termination does not assume that every wavefront of the grid is resident: a
 // wavefront counts in n_active only while it holds a task or is about to take a
-// first-level subtree. The wavefront whose release brings n_active to zero
-// after the roots ran out writes MCE_FLAG_EXIT into every wake flag; a wave
-// that starts later finds the roots gone and leaves the same way.
+// first-level subtree, and request words start closed. The wavefront whose
+// release brings n_active to zero writes MCE_FLAG_EXIT into every wake flag; a
+// wave that starts later finds the roots gone and leaves the same way.
 #define MCE_LINE_WORDS 32     // u32 words per 128-byte line
+#define MCE_REQ_WORD 16       // request word inside a wave's line
 #define MCE_FLAG_TASK 1u
 #define MCE_FLAG_EXIT 2u
+#define MCE_FLAG_RETRY 3u
+#define MCE_REQ_CLOSED 0xFFFFFFFFu
 struct MceWl {
   u32 root_ctr;          // next first-level subtree to hand out (phase 1)
   u32 pad0[MCE_LINE_WORDS - 1];
   int n_active;          // wavefronts holding (or about to take) a task
   u32 pad1[MCE_LINE_WORDS - 1];
-  int avail;             // ring entries not yet claimed by a donor
+  u32 done;              // set on abort (time limit or protocol error)
   u32 pad2[MCE_LINE_WORDS - 1];
-  u32 head;              // next ring slot a donor claims
-  u32 pad3[MCE_LINE_WORDS - 1];
-  u32 tail;              // next ring slot an idle wave fills
-  u32 pad4[MCE_LINE_WORDS - 1];
-  u32 done;              // set on abort (time limit); donors poll it
-  u32 pad5[MCE_LINE_WORDS - 1];
-  u64 ring[MCE_MAX_WORKERS];                    // sequence << 32 | (wave id + 1)
-  u32 flag[MCE_MAX_WORKERS * MCE_LINE_WORDS];   // wake flag of wave w at w * MCE_LINE_WORDS
+  u32 line[MCE_MAX_WORKERS * MCE_LINE_WORDS];   // wave w: flag at [w*32], request at [w*32 + 16]
 };
 
 // ---------------------------------------------------------------- hashing

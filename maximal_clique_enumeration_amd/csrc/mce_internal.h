@@ -102,4 +102,4 @@ SearchLayout mce_search_layout(int sub, int mode, int pcap, int xcap, int rcap, 
 // Resident wavefronts of a search layout over the whole chip (0 on error).
 int mce_search_max_workers(const SearchLayout& L, int num_cu);
 hipError_t mce_launch_search(const SearchLayout& L, const SearchParams& prm, hipStream_t s);
-hipError_t mce_launch_wl_init(MceWl* wl, int nworkers, int nroots, hipStream_t s);
+hipError_t mce_launch_wl_init(MceWl* wl, int nworkers, hipStream_t s);

@@ -32,7 +32,7 @@
 #include "mce_device.h"
 #include "mce_internal.h"
 
-#define REC_WORDS(W) (3 * (W) + 2)   // per level: P[W], X_P[W], C[W], s, (lpX | open << 32)
+#define REC_WORDS(W) (3 * (W) + 2)   // per level: P[W], X_P[W], C[W], s, lpX
 // mailbox (agent-scope atomic words): table offset, (k | lpX << 32), s; then
 // P[W], X_P[W], then the X_X entries as int32
 #define MAIL_HDR 3
@@ -42,24 +42,64 @@
 // agent-scope fence anywhere (each would write back or invalidate an L2, which
 // serialises across the chip). Data is published as "atomic stores, wait for
 // completion, flag store" and read after the flag with atomic loads.
-//
-// 64-bit ring slot: sequence number (high half) and wave id + 1 (low half).
-// The producer of ring index t waits for sequence t (the previous lap's
-// consumer is done with the slot) and publishes sequence t + 1; the consumer of
-// index h waits for sequence h + 1 and hands the slot to lap h + nworkers.
 #define WL_SPIN_LIMIT (1u << 22)
 
-// Receiver side (section 3.3). Gives up this wave's share of n_active; the wave
-// that brings it to zero (no task held anywhere; only active waves donate, so
-// none can appear) writes MCE_FLAG_EXIT into every wake flag. Any other wave
-// enqueues its id and sleeps on its flag with exponential back-off. Returns 1
-// with a task in the mailbox (the donor counted this wave active again), 0 to
-// exit. The flag is cleared, and the clear completed, before the share is given
-// up, so the exit broadcast (issued after every share release) is never lost.
-__device__ int wl_wait(MceWl* wl, int wid, int nworkers, u64 deadline, u32* status) {
+__device__ __forceinline__ u32* wl_flag(MceWl* wl, int w) { return &wl->line[(size_t)w * MCE_LINE_WORDS]; }
+__device__ __forceinline__ u32* wl_req(MceWl* wl, int w) {
+  return &wl->line[(size_t)w * MCE_LINE_WORDS + MCE_REQ_WORD];
+}
+__device__ __forceinline__ u32 xorshift32(u32& x) {
+  x ^= x << 13;
+  x ^= x >> 17;
+  x ^= x << 5;
+  return x;
+}
+
+// A wave that starts a task accepts branch requests again.
+__device__ __forceinline__ void wl_open(MceWl* wl, int wid) {
+  if (lane_id() == 0) st_relaxed(wl_req(wl, wid), 0u);
+}
+
+// The request word of this wave, read by every lane (uniform).
+__device__ __forceinline__ u32 wl_poll(MceWl* wl, int wid) { return uni(ld_relaxed(wl_req(wl, wid))); }
+
+// Answer a request without a branch; reopen the request word.
+__device__ __forceinline__ void wl_refuse(MceWl* wl, int wid, int rcv) {
+  if (lane_id() == 0) {
+    st_relaxed(wl_flag(wl, rcv), MCE_FLAG_RETRY);
+    st_relaxed(wl_req(wl, wid), 0u);
+  }
+}
+
+// Hand a branch to rcv after its mailbox was written with atomic stores: count
+// it active (before this wave can ever give up its own share: same-address
+// atomics of one wave stay in order, and the wait below completes the
+// increment before the receiver can run), wake it, reopen the request word.
+__device__ __forceinline__ void wl_give(MceWl* wl, int wid, int rcv) {
+  if (lane_id() == 0) __hip_atomic_fetch_add(&wl->n_active, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  wait_stores_complete();
+  if (lane_id() == 0) {
+    st_relaxed(wl_flag(wl, rcv), MCE_FLAG_TASK);
+    st_relaxed(wl_req(wl, wid), 0u);
+  }
+}
+
+// Receiver side (section 3.3). Closes this wave's request word (refusing a
+// request that raced in), gives up its share of n_active, and asks random busy
+// waves for a branch until one arrives. The wave that brings n_active to zero
+// (no task held anywhere; only active waves hand out branches, so none can
+// appear) writes MCE_FLAG_EXIT into every wake flag. Returns 1 with a task in
+// the mailbox (the donor counted this wave active again), 0 to exit.
+// Ordering: the refusal and the flag reset complete before the share is given
+// up, and an answer flag is only consumed with a compare-and-swap, so the exit
+// broadcast (issued after every share release) cannot be overwritten.
+__device__ int wl_idle(MceWl* wl, int wid, int nworkers, u64 deadline, u32* status, u32& rng) {
   int res = 0, bcast = 0;
   if (lane_id() == 0) {
-    u32* my = &wl->flag[(size_t)wid * MCE_LINE_WORDS];
+    u32* my = wl_flag(wl, wid);
+    const u32 old = __hip_atomic_exchange(wl_req(wl, wid), MCE_REQ_CLOSED, __ATOMIC_RELAXED,
+                                          __HIP_MEMORY_SCOPE_AGENT);
+    if (old != 0u && old != MCE_REQ_CLOSED) st_relaxed(wl_flag(wl, (int)old - 1), MCE_FLAG_RETRY);
     st_relaxed(my, 0u);
     wait_stores_complete();
     const int left =
@@ -67,89 +107,66 @@ __device__ int wl_wait(MceWl* wl, int wid, int nworkers, u64 deadline, u32* stat
     if (left <= 0) {
       if (left < 0) atomicOr(status, MCE_E_PROTO);
       bcast = 1;
-    } else {
-      const u32 t = __hip_atomic_fetch_add(&wl->tail, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      u64* slot = &wl->ring[t % (u32)nworkers];
-      u32 spins = 0;
-      while ((u32)(ld_relaxed64(slot) >> 32) != t) {
-        if (++spins > WL_SPIN_LIMIT) {
-          atomicOr(status, MCE_E_PROTO);
-          break;
-        }
-        __builtin_amdgcn_s_sleep(1);
-      }
-      st_relaxed64(slot, ((u64)(t + 1u) << 32) | (u64)(u32)(wid + 1));
-      wait_stores_complete();
-      __hip_atomic_fetch_add(&wl->avail, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      // exponential back-off in a few long sleeps: a sleeping wave issues a
-      // handful of scalar instructions per several microseconds, so idle waves
-      // do not starve the compute unit's scalar unit that busy waves need
-      u32 it = 0;
-      for (;;) {
+    } else if (nworkers > 1) {
+      u32 fails = 0, it = 0;
+      bool stop = false;
+      while (!stop) {
         const u32 f = ld_relaxed(my);
-        if (f) {
-          res = f == MCE_FLAG_TASK;
-          break;
-        }
-        if ((++it & 7u) == 0 && past_deadline(deadline)) {
+        if (f == MCE_FLAG_EXIT) break;
+        if ((++it & 15u) == 0 && past_deadline(deadline)) {
           atomicOr(status, MCE_E_TIMEOUT);
           st_relaxed(&wl->done, 1u);
           break;
         }
-        if (it < 4) __builtin_amdgcn_s_sleep(4);
-        else if (it < 8) __builtin_amdgcn_s_sleep(16);
-        else if (it < 12) __builtin_amdgcn_s_sleep(64);
-        else __builtin_amdgcn_s_sleep(127);
+        const int v = (int)(xorshift32(rng) % (u32)nworkers);
+        u32 expected = 0u;
+        if (v != wid && ld_relaxed(wl_req(wl, v)) == 0u &&
+            __hip_atomic_compare_exchange_strong(wl_req(wl, v), &expected, (u32)wid + 1u, __ATOMIC_RELAXED,
+                                                 __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) {
+          // wait for the answer: the asked wave reads its request word once per node
+          u32 spins = 0;
+          for (;;) {
+            const u32 a = ld_relaxed(my);
+            if (a == MCE_FLAG_TASK) {
+              res = 1;
+              stop = true;
+              break;
+            }
+            if (a == MCE_FLAG_EXIT) {
+              stop = true;
+              break;
+            }
+            if (a == MCE_FLAG_RETRY) {
+              u32 e = MCE_FLAG_RETRY;
+              if (!__hip_atomic_compare_exchange_strong(my, &e, 0u, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                                        __HIP_MEMORY_SCOPE_AGENT))
+                stop = true;   // the exit broadcast replaced the refusal
+              break;
+            }
+            if ((++spins & 255u) == 0 && past_deadline(deadline)) {
+              atomicOr(status, MCE_E_TIMEOUT);
+              st_relaxed(&wl->done, 1u);
+              stop = true;
+              break;
+            }
+            __builtin_amdgcn_s_sleep(2);
+          }
+          fails = 0;
+        } else {
+          // the wave asked is idle or busy with another request: back off
+          ++fails;
+          if (fails < 16) __builtin_amdgcn_s_sleep(2);
+          else if (fails < 64) __builtin_amdgcn_s_sleep(16);
+          else __builtin_amdgcn_s_sleep(64);
+        }
       }
     }
   }
   res = read_lane(res, 0);
   if (read_lane(bcast, 0)) {
-    for (int i = lane_id(); i < nworkers; i += MCE_WAVE)
-      st_relaxed(&wl->flag[(size_t)i * MCE_LINE_WORDS], MCE_FLAG_EXIT);
+    for (int i = lane_id(); i < nworkers; i += MCE_WAVE) st_relaxed(wl_flag(wl, i), MCE_FLAG_EXIT);
   }
   return res;
-}
-
-// Donor side: take one idle wave out of the ring, or -1. The claimed wave is
-// counted active before the donor can ever give up its own share (same-address
-// atomics of one wave stay in order), so n_active cannot reach zero while the
-// donated branch is in flight.
-__device__ int wl_claim(MceWl* wl, int nworkers, u32* status) {
-  int r = -1;
-  if (lane_id() == 0) {
-    if (ld_relaxed(&wl->avail) > 0) {
-      const int old = __hip_atomic_fetch_add(&wl->avail, -1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      if (old > 0) {
-        const u32 h = __hip_atomic_fetch_add(&wl->head, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        u64* slot = &wl->ring[h % (u32)nworkers];
-        u64 val = 0;
-        u32 spins = 0;
-        while ((u32)((val = ld_relaxed64(slot)) >> 32) != h + 1u) {
-          if (++spins > WL_SPIN_LIMIT) {
-            atomicOr(status, MCE_E_PROTO);
-            st_relaxed(&wl->done, 1u);
-            break;
-          }
-          __builtin_amdgcn_s_sleep(1);
-        }
-        if ((u32)(val >> 32) == h + 1u) {
-          r = (int)(u32)val - 1;
-          st_relaxed64(slot, (u64)(h + (u32)nworkers) << 32);
-          __hip_atomic_fetch_add(&wl->n_active, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        }
-      } else {
-        __hip_atomic_fetch_add(&wl->avail, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      }
-    }
-  }
-  return read_lane(r, 0);
-}
-
-// Wake a claimed receiver after its mailbox has been written with atomic stores.
-__device__ __forceinline__ void wl_wake(MceWl* wl, int rcv) {
-  wait_stores_complete();
-  if (lane_id() == 0) st_relaxed(&wl->flag[(size_t)rcv * MCE_LINE_WORDS], MCE_FLAG_TASK);
 }
 
 // Phase 1 (section 3.3): the next first-level subtree from the shared counter,
@@ -293,7 +310,7 @@ __global__ __launch_bounds__(64) void k_search(SearchParams prm) {
   if (ld_relaxed(prm.status) & (MCE_E_HEAP | MCE_E_LIMIT)) return;
   for (int i = lane; i < prm.hcap; i += MCE_WAVE) s_hist[i] = 0;
   __syncthreads();
-  // this wave is active until phase 1 finds the roots exhausted (wl_wait gives
+  // this wave is active until phase 1 finds the roots exhausted (wl_idle gives
   // the share back)
   wl_join(wl);
 
@@ -302,7 +319,8 @@ __global__ __launch_bounds__(64) void k_search(SearchParams prm) {
   u64 idle_ticks = 0;
   bool phase2 = false;
   bool abort = false;
-  int wl_countdown = 0, wl_gap = 1;
+  u32 rng = 0x9E3779B9u ^ ((u32)wid * 0x85EBCA6Bu) ^ (u32)prm.nroots;
+  if (rng == 0) rng = 1;
 
   for (;;) {
     // ---------------------------------------------------------- get a task
@@ -318,7 +336,7 @@ __global__ __launch_bounds__(64) void k_search(SearchParams prm) {
     } else {
       if (!prm.worker_list) break;
       const u64 t0 = wall_clock64();
-      const int got = wl_wait(wl, wid, prm.nworkers, deadline, prm.status);
+      const int got = wl_idle(wl, wid, prm.nworkers, deadline, prm.status, rng);
       idle_ticks += wall_clock64() - t0;
       if (!got) break;
       toff = uni(ld_relaxed64(&mail[0]));
@@ -372,12 +390,13 @@ __global__ __launch_bounds__(64) void k_search(SearchParams prm) {
     if constexpr (W == 1) {
       if (lane < p) myrow = rows[lane];
     }
+    if (prm.worker_list) wl_open(wl, wid);
+    u32 rq_next = 0;   // request word, read at one node and acted on at the next
 
     // ---------------------------------------------------------- depth-first search
     // Current level in registers: P, X_P, C (lane w < W holds word w), s = sum of
-    // the hash terms of R, lpX, open = shallower levels with branches left.
+    // the hash terms of R, lpX.
     u64 cj = 0;
-    int open = 0;
     int l = 0;
     bool need_pivot = true;
     for (;;) {
@@ -457,6 +476,87 @@ __global__ __launch_bounds__(64) void k_search(SearchParams prm) {
         } else {
           if (lane < W) cj = pj & ~rows[(size_t)u * W + lane];
         }
+
+        // Branch requests (section 3.3; the idle wave asks, see wl_idle): the
+        // request word read at the previous node is acted on now. The branch
+        // handed over is the first unexplored one of the shallowest level that
+        // has any; the current level qualifies only with another branch left.
+        if (prm.worker_list) {
+          const u32 rq = rq_next;
+          if (rq != 0u && rq != MCE_REQ_CLOSED) {
+            const int rcv = (int)rq - 1;
+            bool given = false;
+            int dl = -1;
+            for (int q = 0; q < l && dl < 0; q++) {
+              const u64 cq = lane < W ? stk[(size_t)q * REC + 2 * W + lane] : 0ull;
+              if (ballot(cq != 0)) dl = q;
+            }
+            if (dl < 0 && wave_sum_u32(lane < W ? (u32)__popcll(cj) : 0u) >= 2u) dl = l;
+            if (dl >= 0) {
+              u64* Rd = stk + (size_t)dl * REC;
+              u64 dP = pj, dX = xj, dC = cj, ds = s;
+              int dlpx = lpx;
+              if (dl < l) {
+                dP = lane < W ? Rd[lane] : 0ull;
+                dX = lane < W ? Rd[W + lane] : 0ull;
+                dC = lane < W ? Rd[2 * W + lane] : 0ull;
+                u64 sv = 0, mv = 0;
+                if (lane == 0) {   // written by lane 0, read back by lane 0
+                  sv = Rd[3 * W];
+                  mv = Rd[3 * W + 1];
+                }
+                ds = read_lane(sv, 0);
+                dlpx = (int)(u32)read_lane(mv, 0);
+              }
+              const u64 dnz = ballot(lane < W && dC != 0);
+              const int j0 = __builtin_ctzll(dnz);
+              const u64 cw = read_lane(dC, j0);
+              const int v = j0 * 64 + __builtin_ctzll(cw);
+              const u64 vbit = cw & (~cw + 1);
+              const u64 rv = lane < W ? rows[(size_t)v * W + lane] : 0ull;
+              const u64 pn = dP & rv;
+              const u64 xn = dX & rv;
+              if ((int)wave_sum_u32(lane < W ? (u32)__popcll(pn) : 0u) >= prm.donate_min_p) {
+                char* dslot = prm.slots + (size_t)rcv * prm.slot_bytes;
+                u64* dm = (u64*)(dslot + prm.s_mail);
+                int* dx = (int*)(dm + MAIL_HDR + 2 * W);
+                int lpxc = 0;
+                if (dlpx > 0) {
+                  XxTest<W, IPX> dtest;
+                  dtest.init(rows, rp, ci, v, pid, true);
+                  lpxc = xx_filter_copy(xx, dlpx, dtest, dx);
+                }
+                if (lane < W) {
+                  st_relaxed64(&dm[MAIL_HDR + lane], pn);
+                  st_relaxed64(&dm[MAIL_HDR + W + lane], xn);
+                }
+                const u64 s_don = ds + hv[v];
+                if (lane == 0) {
+                  st_relaxed64(&dm[0], toff);
+                  st_relaxed64(&dm[1], (u64)(u32)(k0 + dl + 1) | ((u64)(u32)lpxc << 32));
+                  st_relaxed64(&dm[2], s_don);
+                }
+                wl_give(wl, wid, rcv);
+                // the donor's level dl moves on past v: C -= {v}, P -= {v}, X_P += {v}
+                if (lane == j0) {
+                  if (dl < l) {
+                    Rd[2 * W + j0] = dC & ~vbit;
+                    Rd[j0] = dP & ~vbit;
+                    Rd[W + j0] = dX | vbit;
+                  } else {
+                    cj &= ~vbit;
+                    pj &= ~vbit;
+                    xj |= vbit;
+                  }
+                }
+                st_don++;
+                given = true;
+              }
+            }
+            if (!given) wl_refuse(wl, wid, rcv);
+          }
+          rq_next = wl_poll(wl, wid);
+        }
       }
 
       // next branch of this level: the lowest vertex of C = P - N(pivot)
@@ -478,14 +578,12 @@ __global__ __launch_bounds__(64) void k_search(SearchParams prm) {
         s = read_lane(sv, 0);
         mv = read_lane(mv, 0);
         lpx = (int)(u32)mv;
-        open = (int)(mv >> 32);
         continue;
       }
       const int j0 = __builtin_ctzll(nz);
       const u64 cw = read_lane(cj, j0);
       const int v = j0 * 64 + __builtin_ctzll(cw);
       const u64 vbit = cw & (~cw + 1);
-      const bool more_here = (nz & ~(1ull << j0)) != 0 || (cw & (cw - 1)) != 0;
       u64 rv;
       if constexpr (W == 1) rv = read_lane(myrow, v);
       else rv = lane < W ? rows[(size_t)v * W + lane] : 0;
@@ -516,41 +614,6 @@ __global__ __launch_bounds__(64) void k_search(SearchParams prm) {
       st_xx += (u64)lpx;
       const int lpx_child = lpx > 0 ? xx_partition(xx, lpx, test) : 0;
 
-      // donate this branch to an idle wave? (section 3.3 conditions)
-      if (prm.worker_list && more_here && open > 0) {
-        if (wl_countdown > 0) {
-          wl_countdown--;
-        } else {
-          u32 pc;
-          if constexpr (W == 1) pc = (u32)__popcll(read_lane(pn, 0));
-          else pc = wave_sum_u32(lane < W ? (u32)__popcll(pn) : 0u);
-          if ((int)pc >= prm.donate_min_p) {
-            const int rcv = wl_claim(wl, prm.nworkers, prm.status);
-            if (rcv >= 0) {
-              char* dslot = prm.slots + (size_t)rcv * prm.slot_bytes;
-              u64* dm = (u64*)(dslot + prm.s_mail);
-              int* dx = (int*)(dm + MAIL_HDR + 2 * W);
-              if (lane < W) {
-                st_relaxed64(&dm[MAIL_HDR + lane], pn);
-                st_relaxed64(&dm[MAIL_HDR + W + lane], xn);
-              }
-              for (int i = lane; i < lpx_child; i += MCE_WAVE) st_relaxed_i(&dx[i], xx[i]);
-              if (lane == 0) {
-                st_relaxed64(&dm[0], toff);
-                st_relaxed64(&dm[1], (u64)(u32)k_child | ((u64)(u32)lpx_child << 32));
-                st_relaxed64(&dm[2], s_child);
-              }
-              wl_wake(wl, rcv);
-              st_don++;
-              wl_gap = 1;
-              continue;
-            }
-            // nobody idle: look again after a growing number of branches
-            wl_countdown = wl_gap;
-            wl_gap = wl_gap < 64 ? 2 * wl_gap : 64;
-          }
-        }
-      }
       // descend: save this level, the child becomes the current level
       u64* R = stk + (size_t)l * REC;
       if (lane < W) {
@@ -560,9 +623,8 @@ __global__ __launch_bounds__(64) void k_search(SearchParams prm) {
       }
       if (lane == 0) {
         R[3 * W] = s;
-        R[3 * W + 1] = (u64)(u32)lpx | ((u64)(u32)open << 32);
+        R[3 * W + 1] = (u64)(u32)lpx;
       }
-      open += more_here ? 1 : 0;
       l++;
       pj = pn;
       xj = xn;
@@ -601,7 +663,7 @@ __global__ __launch_bounds__(64) void k_search(SearchParams prm) {
 
 // ------------------------------------------------------------------ width 1 (|P_root| <= 64)
 // The hot case: every set over P fits one 64-bit word, so the current level's
-// P, X_P, C, hash sum, lpX and open count are wave-uniform scalars (SALU work,
+// P, X_P, C, hash sum and lpX are wave-uniform scalars (SALU work,
 // scalar branches), and lane i holds row i of P, the hash term and the id of P
 // member i, read by v_readlane. The level stack lives in VGPRs, level l in lane
 // l (depth <= |P_root| - 2 < 64), and clique sizes below 64 are counted in
@@ -648,7 +710,8 @@ __global__ __launch_bounds__(64) void k_search_w1(SearchParams prm) {
   u64 st_prow = 0, st_xx = 0;   // CNT only
   bool phase2 = false;
   bool abort = false;
-  int wl_countdown = 1, wl_gap = 1;
+  u32 rng = 0x9E3779B9u ^ ((u32)wid * 0x85EBCA6Bu) ^ (u32)prm.nroots;
+  if (rng == 0) rng = 1;
 
   for (;;) {
     // ---------------------------------------------------------- get a task
@@ -664,7 +727,7 @@ __global__ __launch_bounds__(64) void k_search_w1(SearchParams prm) {
     } else {
       if (!prm.worker_list) break;
       const u64 t0 = wall_clock64();
-      const int got = wl_wait(wl, wid, prm.nworkers, uni(s_misc[1]), prm.status);
+      const int got = wl_idle(wl, wid, prm.nworkers, uni(s_misc[1]), prm.status, rng);
       if (lane == 0) {
         const u64 t1 = wall_clock64();
         s_misc[2] += t1 - t0;
@@ -721,6 +784,8 @@ __global__ __launch_bounds__(64) void k_search_w1(SearchParams prm) {
       if (phase2) s_misc[5] += t1;
       if (s_misc[6] == 0) s_misc[6] = t1;
     }
+    if (prm.worker_list) wl_open(wl, wid);
+    u32 rq_next = 0;   // request word, read at one node and acted on at the next
 
     // ---------------------------------------------------------- depth-first search
     u64 stP = 0, stX = 0, stC = 0, stS = 0, stL = 0;   // level stack, level l in lane l
@@ -775,38 +840,41 @@ __global__ __launch_bounds__(64) void k_search_w1(SearchParams prm) {
         const u64 ru = u < p ? read_lane(myrow, u) : uni(rows[u]);
         C = P & ~ru;
 
-        // Donation (section 3.3), checked at node entry with a back-off while
-        // nobody is idle. The branch handed over is the first unexplored one of
-        // the shallowest level that has any (the largest piece of work this wave
-        // holds); the current level qualifies only with another branch left.
-        // Taking a sibling out of order is sound: the receiver's X holds every
-        // sibling taken before it, and the donor's later siblings see it in X.
-        if (prm.worker_list && --wl_countdown <= 0) {
-          wl_countdown = wl_gap;
-          const u64 sm = ballot(lane < l && stC != 0);
-          int dl = -1;
-          if (sm) dl = __builtin_ctzll(sm);
-          else if (__popcll(C) >= 2) dl = l;
-          if (dl >= 0) {
-            u64 dP = P, dX = XP, dC = C, ds = s;
-            int dlpx = lpx;
-            if (dl < l) {
-              dP = read_lane(stP, dl);
-              dX = read_lane(stX, dl);
-              dC = read_lane(stC, dl);
-              ds = read_lane(stS, dl);
-              dlpx = (int)(u32)read_lane(stL, dl);
-            }
-            const int v = __builtin_ctzll(dC);
-            const u64 vbit = 1ull << v;
-            const u64 rv = read_lane(myrow, v);
-            const u64 pn = dP & rv;
-            const u64 xn = dX & rv;
-            if (__popcll(pn) >= prm.donate_min_p) {
-              const u64 td = wall_clock64();
-              const int rcv = wl_claim(wl, prm.nworkers, prm.status);
-              st_checks++;
-              if (rcv >= 0) {
+        // Branch requests (section 3.3; here the idle wave asks, see wl_idle):
+        // the request word read at the previous node is acted on now, and read
+        // again for the next one, so its latency hides behind this node. The
+        // branch handed over is the first unexplored one of the shallowest
+        // level that has any (the largest piece of work this wave holds); the
+        // current level qualifies only with another branch left. Taking a
+        // sibling out of order is sound: the receiver's X holds every sibling
+        // taken before it, and the donor's later siblings see it in X.
+        if (prm.worker_list) {
+          const u32 rq = rq_next;
+          if (rq != 0u && rq != MCE_REQ_CLOSED) {
+            const int rcv = (int)rq - 1;
+            const u64 td = wall_clock64();
+            st_checks++;
+            bool given = false;
+            const u64 sm = ballot(lane < l && stC != 0);
+            int dl = -1;
+            if (sm) dl = __builtin_ctzll(sm);
+            else if (__popcll(C) >= 2) dl = l;
+            if (dl >= 0) {
+              u64 dP = P, dX = XP, dC = C, ds = s;
+              int dlpx = lpx;
+              if (dl < l) {
+                dP = read_lane(stP, dl);
+                dX = read_lane(stX, dl);
+                dC = read_lane(stC, dl);
+                ds = read_lane(stS, dl);
+                dlpx = (int)(u32)read_lane(stL, dl);
+              }
+              const int v = __builtin_ctzll(dC);
+              const u64 vbit = 1ull << v;
+              const u64 rv = read_lane(myrow, v);
+              const u64 pn = dP & rv;
+              const u64 xn = dX & rv;
+              if (__popcll(pn) >= prm.donate_min_p) {
                 char* dslot = prm.slots + (size_t)rcv * prm.slot_bytes;
                 u64* dm = (u64*)(dslot + prm.s_mail);
                 int* dx = (int*)(dm + MAIL_HDR + 2);
@@ -832,7 +900,7 @@ __global__ __launch_bounds__(64) void k_search_w1(SearchParams prm) {
                   st_relaxed64(&dm[MAIL_HDR], pn);
                   st_relaxed64(&dm[MAIL_HDR + 1], xn);
                 }
-                wl_wake(wl, rcv);
+                wl_give(wl, wid, rcv);
                 // the donor's level dl moves on past v: C -= {v}, P -= {v}, X_P += {v}
                 if (dl < l) {
                   if (lane == dl) {
@@ -846,20 +914,14 @@ __global__ __launch_bounds__(64) void k_search_w1(SearchParams prm) {
                   XP |= vbit;
                 }
                 st_don++;
-                wl_gap = 1;
-                wl_countdown = 1;
-                if (lane == 0) {
-                  const u64 dt = wall_clock64() - td;
-                  s_misc[4] += dt;
-                  s_misc[7] += dt;
-                }
-              } else {
-                if (lane == 0) s_misc[4] += wall_clock64() - td;
-                wl_gap = wl_gap < 32 ? 2 * wl_gap : 32;
-                wl_countdown = wl_gap;
+                given = true;
+                if (lane == 0) s_misc[7] += wall_clock64() - td;
               }
             }
+            if (!given) wl_refuse(wl, wid, rcv);
+            if (lane == 0) s_misc[4] += wall_clock64() - td;
           }
+          rq_next = wl_poll(wl, wid);
         }
       }
 
@@ -982,24 +1044,24 @@ __global__ __launch_bounds__(64) void k_search_w1(SearchParams prm) {
   }
 }
 
-// Worker-list reset before a launch: counters zero, ring slot i at sequence i,
-// wake flags of the launch's waves zero.
-__global__ void k_wl_init(MceWl* wl, int nworkers, int nroots) {
+// Worker-list reset before a launch: counters zero, wake flags zero, request
+// words closed (a wave opens its own when it starts a task).
+__global__ void k_wl_init(MceWl* wl, int nworkers) {
   const int tid = blockIdx.x * blockDim.x + threadIdx.x;
   const int nt = gridDim.x * blockDim.x;
   u32* head = (u32*)wl;
-  const int nhead = (int)(offsetof(MceWl, ring) / 4);
+  const int nhead = (int)(offsetof(MceWl, line) / 4);
   for (int i = tid; i < nhead; i += nt) head[i] = 0u;
   for (int i = tid; i < nworkers; i += nt) {
-    wl->ring[i] = (u64)(u32)i << 32;
-    wl->flag[(size_t)i * MCE_LINE_WORDS] = 0;
+    wl->line[(size_t)i * MCE_LINE_WORDS] = 0u;
+    wl->line[(size_t)i * MCE_LINE_WORDS + MCE_REQ_WORD] = MCE_REQ_CLOSED;
   }
 }
 
 // ------------------------------------------------------------------ host side
-hipError_t mce_launch_wl_init(MceWl* wl, int nworkers, int nroots, hipStream_t s) {
+hipError_t mce_launch_wl_init(MceWl* wl, int nworkers, hipStream_t s) {
   hipLaunchKernelGGL(k_wl_init, dim3(std::max(1, std::min(64, (nworkers + 255) / 256))), dim3(256), 0, s, wl,
-                     nworkers, nroots);
+                     nworkers);
   return hipGetLastError();
 }
 
