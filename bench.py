@@ -1,18 +1,20 @@
 """Benchmark: maximal cliques per second and end-to-end MCE time on one MI355X.
 
 One step = one full mce_run over a device-resident CSR graph: validation, k-core
-peel, orientation, and every search launch, ending with the count, histogram
-and hash on the host (the timed scope of "Parallelizing Maximal Clique
-Enumeration on GPUs", section 4.1: counting plus degeneracy preprocessing,
-graph already loaded). The default workload is the Moon-Moser graph on 45
-vertices (3^15 maximal cliques of size 15).
+peel, orientation, the induced-subgraph builds and every search launch, ending
+with the count, histogram and hash on the host (the timed scope of
+"Parallelizing Maximal Clique Enumeration on GPUs", section 4.1: counting plus
+degeneracy preprocessing, graph already loaded). The default workload is the
+Moon-Moser graph on 45 vertices (3^15 maximal cliques of size 15).
 
-Prints one JSON line. Also reports:
-  roofline      the search kernel's algorithmic integer/bitwise work per launch
-                divided by its average launch time (HIP events around each launch
-                on the engine's stream), against the chip's int32 VALU peak;
-  cpu_baseline  the oracle (single-threaded CPU Bron-Kerbosch-Tomita) timed on a
-                bounded sample of the same workload on this host.
+Prints one JSON line. Besides the metric it reports:
+  roofline      the search kernel's algorithmic integer/bitwise lane-ops per
+                launch divided by its average launch time (HIP events around each
+                search launch, recorded on the engine's stream), against the int32
+                vector peak. The search tree does not depend on scheduling, so one
+                counting run gives the exact work of every timed run.
+  cpu_baseline  the oracle (single-threaded CPU Bron-Kerbosch-Tomita) timed on the
+                same graph on this host.
 """
 from __future__ import annotations
 
@@ -26,12 +28,13 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
-# MI355X: 256 CUs x 4 SIMD x 16 lanes x 2.4 GHz int32 VALU lane-ops per second
-VALU_INT32_PEAK = 256 * 64 * 2.4e9
-# algorithmic int32 operations per counted unit (roofline)
-OPS_PER_PIVOT_WORD = 4      # 64-bit AND (2) + 64-bit popcount (2 x v_bcnt)
-OPS_PER_LEAF = 24           # one mix64 of the clique sum in 32-bit pieces
-OPS_PER_XX_TEST = 16        # binary search step count ~ log2(degree), one compare each
+# MI355X int32 vector peak: 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz lane-ops/s
+VALU_INT32_PEAK = 256 * 4 * 16 * 2.4e9
+# algorithmic int32 lane-ops per counted unit
+OPS_PER_PIVOT_WORD = 4      # 64-bit AND (2) + 64-bit popcount (2)
+OPS_PER_BRANCH_WORD = 10    # P n N(v), X_P n N(v) (2 x 2) and the C, P, X_P updates (3 x 2)
+OPS_PER_XX_TEST = 2         # one bit test (full subgraph)
+OPS_PER_LEAF = 20           # one mix64 of the clique's hash sum
 
 
 def parse():
@@ -43,15 +46,25 @@ def parse():
     ap.add_argument("--seed", type=int, default=1)
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calib-copy-mb", type=int, default=0,
+                    help="also run one device copy of this many MiB (counter calibration runs)")
     ap.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "search_traffic.json"))
     return ap.parse_args()
+
+
+def algorithmic_ops(st):
+    w = st["pivot_words"] / st["pivot_rows"] if st["pivot_rows"] else 1.0
+    # a donated branch is taken by no wave: add the donations back
+    branches = st["branches"] + st["donations"]
+    return (st["pivot_words"] * OPS_PER_PIVOT_WORD + branches * w * OPS_PER_BRANCH_WORD
+            + st["xx_tests"] * OPS_PER_XX_TEST + st["leaves"] * OPS_PER_LEAF)
 
 
 def cpu_baseline(g, budget_s):
     """The oracle on the same graph, repeated until the budget is used (one
     thread). Reports cliques per second over the whole sample."""
     import oracle
-    reps, cliques, t_used = 0, 0, 0.0
+    reps, cliques = 0, 0
     t0 = time.perf_counter()
     while True:
         r = oracle.mce(g.n, g.row_ptr, g.col_idx)
@@ -75,18 +88,30 @@ def main():
     import maximal_clique_enumeration_amd as mce
     import mce_inputs
 
-    if not mce.lib_built():
-        from maximal_clique_enumeration_amd import build
-        build.build()
+    mce.load_library()   # raises if the HIP library is not built: no fallback
     g = mce_inputs.config_graph(args.config, seed=args.seed)
     dev = torch.device("cuda", 0)
     rp = torch.from_numpy(g.row_ptr).to(dev)
     ci = torch.from_numpy(g.col_idx).to(dev)
+    if args.calib_copy_mb:
+        src = torch.empty(args.calib_copy_mb << 18, dtype=torch.int32, device=dev)
+        src.fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
     torch.cuda.synchronize()
+
+    # counting run: exact algorithmic work of the search (deterministic tree)
+    with mce.Engine(device=0, counters=True, timeout_ms=100000) as ecnt:
+        ref = ecnt.run(rp, ci)
+        cst = ecnt.stats()
+    ops = algorithmic_ops(cst)
+
     eng = mce.Engine(device=0, phase_times=True, timeout_ms=100000)
-    ref = None
     for _ in range(args.warmup):
-        ref = eng.run(rp, ci)
+        r = eng.run(rp, ci)
+        if r.key() != ref.key():
+            raise SystemExit("results differ between runs")
     torch.cuda.synchronize()
     times, search_ms, stats = [], [], []
     t_start = time.perf_counter()
@@ -97,17 +122,15 @@ def main():
         st = eng.stats()
         search_ms.append(st["ms_search"])
         stats.append(st)
-        if ref is not None and r.key() != ref.key():
+        if r.key() != ref.key():
             raise SystemExit("results differ between steps")
-        ref = r
     torch.cuda.synchronize()
     total = time.perf_counter() - t_start
     count = ref.count
     value = count * args.steps / total
     st = stats[-1]
     avg_search_s = sum(search_ms) / len(search_ms) / 1e3
-    ops = (st["pivot_words"] * OPS_PER_PIVOT_WORD + st["leaves"] * OPS_PER_LEAF
-           + st["xx_tests"] * OPS_PER_XX_TEST)
+    launches = max(1, st["launches"])
     achieved = ops / avg_search_s if avg_search_s > 0 else 0.0
     traffic = None
     if os.path.exists(args.traffic_json):
@@ -119,10 +142,13 @@ def main():
         except (OSError, ValueError):
             traffic = None
     roofline = {"bound": "alu", "achieved": achieved / 1e12, "peak": VALU_INT32_PEAK / 1e12,
-                "unit": "Tops/s (int32 VALU lane-ops)", "frac": achieved / VALU_INT32_PEAK,
-                "traffic": traffic, "kernel": "k_search (search launch)",
-                "search_ms": avg_search_s * 1e3, "ops_per_launch": ops}
+                "unit": "Tops/s (int32 vector lane-ops)", "frac": achieved / VALU_INT32_PEAK,
+                "traffic": traffic, "kernel": "k_search_w1 (search launches)",
+                "search_ms_per_step": avg_search_s * 1e3, "launches_per_step": launches,
+                "ops_per_step": ops}
     info = eng.graph_info()
+    busy = (st["busy_ticks"] / (st["workers"] * st["kernel_ticks"])
+            if st["workers"] and st["kernel_ticks"] else None)
     out = {
         "metric": "maximal cliques/sec and end-to-end MCE time per graph on 1 MI355X",
         "value": value,
@@ -138,17 +164,19 @@ def main():
         "data": "synthetic",
         "config": {"workload": g.name, "n": g.n, "edges": g.m, "degeneracy": info["degeneracy"],
                    "max_degree": info["max_degree"], "maximal_cliques": count,
-                   "parallelism": "single GPU, one wavefront per subtree + worker list",
+                   "subgraph": "full" if info["subgraph"] == mce.MCE_SUBGRAPH_FULL else "partial",
+                   "parallelism": "single GPU, one wavefront per subtree + branch requests",
                    "seed": args.seed},
         "roofline": roofline,
         "detail": {"e2e_ms_min": min(times) * 1e3, "e2e_ms_median": sorted(times)[len(times) // 2] * 1e3,
                    "nodes": st["nodes"], "donations": st["donations"], "workers": st["workers"],
-                   "busy_frac": (st["busy_ticks"] / (st["workers"] * st["kernel_ticks"])
-                                 if st["workers"] and st["kernel_ticks"] else None),
+                   "busy_frac": busy,
                    "max_over_avg_nodes": (st["max_nodes"] / (st["nodes"] / st["workers"])
                                           if st["nodes"] and st["workers"] else None),
                    "ms_validate": st["ms_validate"], "ms_peel": st["ms_peel"],
-                   "ms_orient": st["ms_orient"], "hash": hex(ref.hash)},
+                   "ms_orient": st["ms_orient"], "ms_build": st["ms_build"],
+                   "pivot_rows": cst["pivot_rows"], "branches": cst["branches"],
+                   "xx_tests": cst["xx_tests"], "leaves": cst["leaves"], "hash": hex(ref.hash)},
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(g, args.cpu_seconds)

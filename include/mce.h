@@ -64,8 +64,8 @@ typedef enum {
 #define MCE_FLAG_HBM_STAGING 1u  /* keep induced-subgraph rows and DFS stacks in HBM even
                                     when they fit in LDS (section 3.4 data in device memory) */
 #define MCE_FLAG_PHASE_TIMES 2u  /* record per-phase GPU times in mce_run_stats */
-#define MCE_FLAG_COUNTERS 4u     /* count pivot rows and X_X tests (mce_run_stats.pivot_rows,
-                                    xx_tests); the narrowest search kernel skips them otherwise */
+#define MCE_FLAG_COUNTERS 4u     /* count pivot rows, X_X tests and branches (mce_run_stats.pivot_rows,
+                                    xx_tests, branches); the width-1 search kernel skips them otherwise */
 
 /* mce_config.subgraph: how each subtree's induced subgraph is encoded (section
    3.4). Partial: bit rows for P x P only, edges between P and X looked up in the
@@ -132,6 +132,8 @@ typedef struct {
   uint64_t start_spread_ticks; /* largest gap between the first and last wavefront start of a launch */
   uint64_t claim_checks;     /* worker-list claim attempts by donors */
   uint64_t donate_ok_ticks;  /* ticks of the successful donations alone */
+  uint64_t branches;         /* branches taken (child nodes and leaf tests); with MCE_FLAG_COUNTERS
+                                for the width-1 kernel */
 } mce_run_stats;
 
 /* Fills cfg with the defaults: device -1, worker_list 1, donate_min_p 10,

@@ -70,7 +70,8 @@ class mce_run_stats(ctypes.Structure):
                 ("ms_search", ctypes.c_double), ("ms_build", ctypes.c_double),
                 ("donate_ticks", ctypes.c_uint64), ("setup_ticks", ctypes.c_uint64),
                 ("first_ticks", ctypes.c_uint64), ("start_spread_ticks", ctypes.c_uint64),
-                ("claim_checks", ctypes.c_uint64), ("donate_ok_ticks", ctypes.c_uint64)]
+                ("claim_checks", ctypes.c_uint64), ("donate_ok_ticks", ctypes.c_uint64),
+                ("branches", ctypes.c_uint64)]
 
 
 _lib = None

@@ -386,6 +386,7 @@ mce_status run_impl(mce_engine* e, int32_t n, int64_t nnz, const int32_t* row_pt
   u64 words_built = 0;
   for (const Plan& pl : plan) words_built += hctl->sub_words[mode][pl.sub];
   so.table_words = words_built;
+  so.branches = stat_sum[ST_BRANCHES];
   so.busy_ticks = stat_sum[ST_BUSY_TICKS];
   so.max_busy_ticks = max_busy;
   so.max_nodes = max_nodes;

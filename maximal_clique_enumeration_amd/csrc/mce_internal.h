@@ -21,7 +21,7 @@ enum {
   ST_PIVOT_ROWS,
   ST_PIVOT_WORDS,
   ST_XX_TESTS,
-  ST_IP_ROWS,
+  ST_BRANCHES,       // branches taken (child nodes and leaf tests)
   ST_BUSY_TICKS,
   ST_ROOTS,
   ST_RECEIVED,

@@ -315,7 +315,7 @@ __global__ __launch_bounds__(64) void k_search(SearchParams prm) {
   wl_join(wl);
 
   u64 hacc = 0;
-  u64 st_nodes = 0, st_leaves = 0, st_don = 0, st_prow = 0, st_xx = 0, st_roots = 0, st_recv = 0;
+  u64 st_nodes = 0, st_leaves = 0, st_don = 0, st_prow = 0, st_xx = 0, st_roots = 0, st_recv = 0, st_br = 0;
   u64 idle_ticks = 0;
   bool phase2 = false;
   bool abort = false;
@@ -584,6 +584,7 @@ __global__ __launch_bounds__(64) void k_search(SearchParams prm) {
       const u64 cw = read_lane(cj, j0);
       const int v = j0 * 64 + __builtin_ctzll(cw);
       const u64 vbit = cw & (~cw + 1);
+      st_br++;
       u64 rv;
       if constexpr (W == 1) rv = read_lane(myrow, v);
       else rv = lane < W ? rows[(size_t)v * W + lane] : 0;
@@ -653,7 +654,7 @@ __global__ __launch_bounds__(64) void k_search(SearchParams prm) {
     st[ST_PIVOT_ROWS] = st_prow;
     st[ST_PIVOT_WORDS] = st_prow * (u64)W;
     st[ST_XX_TESTS] = st_xx;
-    st[ST_IP_ROWS] = 0;
+    st[ST_BRANCHES] = st_br;
     st[ST_BUSY_TICKS] = (t_end - t_start) - idle_ticks;
     st[ST_ROOTS] = st_roots;
     st[ST_RECEIVED] = st_recv;
@@ -707,7 +708,7 @@ __global__ __launch_bounds__(64) void k_search_w1(SearchParams prm) {
   u64 hacc = 0;
   u32 nodes = 0;       // since the last fold into s_misc[3]
   u32 st_don = 0, st_roots = 0, st_recv = 0, st_checks = 0;
-  u64 st_prow = 0, st_xx = 0;   // CNT only
+  u64 st_prow = 0, st_xx = 0, st_br = 0;   // CNT only
   bool phase2 = false;
   bool abort = false;
   u32 rng = 0x9E3779B9u ^ ((u32)wid * 0x85EBCA6Bu) ^ (u32)prm.nroots;
@@ -938,6 +939,7 @@ __global__ __launch_bounds__(64) void k_search_w1(SearchParams prm) {
       }
       const int v = __builtin_ctzll(C);
       const u64 vbit = 1ull << v;
+      if constexpr (CNT) st_br++;
       C ^= vbit;   // C -= {v}; P -= {v}; X_P += {v} (Algorithm 2)
       P ^= vbit;
       XP |= vbit;
@@ -1030,7 +1032,7 @@ __global__ __launch_bounds__(64) void k_search_w1(SearchParams prm) {
     st[ST_PIVOT_ROWS] = st_prow;
     st[ST_PIVOT_WORDS] = st_prow;
     st[ST_XX_TESTS] = st_xx;
-    st[ST_IP_ROWS] = 0;
+    st[ST_BRANCHES] = st_br;
     st[ST_BUSY_TICKS] = total - s_misc[2];
     st[ST_ROOTS] = st_roots;
     st[ST_RECEIVED] = st_recv;
