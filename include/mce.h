@@ -48,7 +48,7 @@ typedef enum {
   MCE_ERR_NOMEM = -3,    /* device or host allocation failed */
   MCE_ERR_DEVICE = -4,   /* a HIP runtime call failed */
   MCE_ERR_STATE = -5,    /* call out of order, e.g. mce_result before any run */
-  MCE_ERR_TIMEOUT = -6,  /* the search ran past mce_config.timeout_ms and was abandoned */
+  MCE_ERR_TIMEOUT = -6,  /* the run passed mce_config.timeout_ms and was abandoned */
   MCE_ERR_LIMIT = -7     /* the graph exceeds a limit of this build (degeneracy > 2048) */
 } mce_status;
 
@@ -84,7 +84,7 @@ typedef struct {
                              (section 3.3 uses 10); must be >= 1 */
   int32_t validate;       /* 1: check the CSR before searching (MCE_ERR_GRAPH on failure) */
   int32_t max_workers;    /* 0: as many wavefronts as are resident; else at most this many */
-  int64_t timeout_ms;     /* wall-clock limit of one search launch; 0: 120000 */
+  int64_t timeout_ms;     /* wall-clock limit of one run, counted from the start of the peel; 0: 120000 */
   uint32_t flags;         /* MCE_FLAG_* */
   int32_t subgraph;       /* MCE_SUBGRAPH_* (0 = auto) */
 } mce_config;

@@ -314,6 +314,7 @@ mce_status run_impl(mce_engine* e, int32_t n, int64_t nnz, const int32_t* row_pt
     prm.donate_min_p = std::max(1, (int)e->cfg.donate_min_p);
     prm.worker_list = e->cfg.worker_list ? 1 : 0;
     prm.budget = budget;
+    prm.t_run = &ctl->t_run;
     prm.status = &ctl->status;
     prm.stats = dp<u64>(e->stats) + (size_t)stat_off * MCE_NSTAT;
     if (timing) (void)hipEventRecord(e->ev[evi + 2], s);

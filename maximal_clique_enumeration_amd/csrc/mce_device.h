@@ -86,9 +86,10 @@ struct MceCtl {
   int sub_cursor[MCE_NSUB];
   u64 heap_top[MCE_NSUB];   // build: bump allocator of each sub-class's heap
   int asize[2];          // peel: alive-list sizes (ping-pong)
-  int fsize[2];          // peel: frontier sizes (ping-pong)
+  int fsize[3];          // peel: frontier sizes (rotating: read, filled, being reset)
   u32 bar_count;         // grid barrier
   u32 bar_gen;
+  u64 t_run;             // wall-clock tick at the start of the peel: the run's time limit counts from it
 };
 
 // Worker-list state of one search launch (section 3.3 of the pages). Each

@@ -64,7 +64,8 @@ struct SearchParams {
   char* slots;           // one HBM slot per wavefront
   int donate_min_p;
   int worker_list;
-  u64 budget;            // wall-clock ticks after which the launch is abandoned
+  u64 budget;            // wall-clock ticks after the run start (t_run) at which the search is abandoned
+  const u64* t_run;      // run start tick, written by the peel
   u32* status;
   u64* stats;            // nworkers * MCE_NSTAT
 };

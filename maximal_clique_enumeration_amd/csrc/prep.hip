@@ -60,24 +60,30 @@ __global__ __launch_bounds__(256) void k_validate_cols(int n, const int* __restr
 }
 
 // ------------------------------------------------------------------ k-core peel
-// Grid-wide barrier for a cooperative launch. Every wave passes an agent-scope
-// release before arriving and an acquire after leaving, because the 8 XCDs keep
-// separate L2 caches. Bounded: past the deadline it flags MCE_E_TIMEOUT and lets
-// the block go, and the caller checks the flag after every barrier.
-__device__ void grid_barrier(MceCtl* ctl, u64 deadline) {
-  fence_release_agent();
+// Grid-wide barrier for a cooperative launch, without agent-scope fences (their
+// L2 write-back / invalidate serialises when hundreds of blocks issue them).
+// Everything the peel passes between blocks is read and written with
+// agent-scope relaxed atomics, which are performed at the device coherence
+// point; the barrier only has to order them: each block waits until its own
+// memory operations completed, then arrives, and the last arrival opens the next
+// generation. Bounded: past the deadline it flags MCE_E_TIMEOUT and lets the
+// block go; the caller checks the flag after every barrier.
+__device__ void grid_sync(MceCtl* ctl, u64 deadline) {
+  wait_stores_complete();
   __syncthreads();
   if (gridDim.x > 1) {
     if (threadIdx.x == 0) {
-      u32 gen = __hip_atomic_load(&ctl->bar_gen, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT);
-      u32 arrived = __hip_atomic_fetch_add(&ctl->bar_count, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT) + 1;
+      const u32 gen = ld_relaxed(&ctl->bar_gen);
+      wait_stores_complete();   // the generation is read before this block arrives
+      const u32 arrived = __hip_atomic_fetch_add(&ctl->bar_count, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1;
       if (arrived == gridDim.x) {
-        __hip_atomic_store(&ctl->bar_count, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __hip_atomic_store(&ctl->bar_gen, gen + 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+        st_relaxed(&ctl->bar_count, 0u);
+        wait_stores_complete();
+        st_relaxed(&ctl->bar_gen, gen + 1);
       } else {
         u32 spins = 0;
-        while (__hip_atomic_load(&ctl->bar_gen, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) == gen) {
-          __builtin_amdgcn_s_sleep(2);
+        while (ld_relaxed(&ctl->bar_gen) == gen) {
+          __builtin_amdgcn_s_sleep(1);
           if ((++spins & 1023u) == 0 && past_deadline(deadline)) {
             atomicOr(&ctl->status, MCE_E_TIMEOUT);
             break;
@@ -87,19 +93,27 @@ __device__ void grid_barrier(MceCtl* ctl, u64 deadline) {
     }
     __syncthreads();
   }
-  fence_acquire_agent();
 }
 
-// Round-synchronous peel. Level k: every alive vertex with current degree <= k
-// leaves in one round (rnd = round, core = k); its alive neighbours lose one
-// degree each, and a neighbour whose degree falls from k+1 to k joins the next
-// round of the same level. When a round removes nothing, k becomes the smallest
-// alive degree. Launched cooperatively; gridDim 1 for small graphs.
+__device__ __forceinline__ int ldi(const int* p) { return ld_relaxed(p); }
+__device__ __forceinline__ void sti(int* p, int v) { st_relaxed_i(p, v); }
+
+// Round-synchronous peel (section 2.4 asks for a degeneracy order; this is the
+// one the engine uses). Level k: every remaining vertex of current degree <= k
+// leaves in one round (rnd = round, core = k). The removed vertices' remaining
+// neighbours lose one degree each, and a neighbour whose degree falls from k+1
+// to k joins the next round of the same level; when a round removes nothing, k
+// becomes the smallest remaining degree. Marking the round's vertices and
+// decrementing their neighbours happen in the same phase: a vertex of the
+// current round already has degree <= k, so a decrement can never make it join
+// again (that needs a fall from k+1). One grid barrier per round. Launched
+// cooperatively; one block for small graphs.
 __global__ __launch_bounds__(256) void k_peel(int n, const int* __restrict__ rp, const int* __restrict__ ci,
                                                int* deg, int* rnd, int* core, int* alive0, int* alive1,
                                                int* front0, int* front1, MceCtl* ctl, u64 budget) {
   if (ld_relaxed(&ctl->status) != 0) return;   // rejected input: nothing to order
-  const u64 deadline = wall_clock64() + budget;
+  const u64 t0 = wall_clock64();
+  const u64 deadline = t0 + budget;
   const int gtid = blockIdx.x * blockDim.x + threadIdx.x;
   const int gsize = gridDim.x * blockDim.x;
   const int lane = lane_id();
@@ -109,117 +123,114 @@ __global__ __launch_bounds__(256) void k_peel(int n, const int* __restrict__ rp,
   int* front[2] = {front0, front1};
 
   for (int v = gtid; v < n; v += gsize) {
-    deg[v] = rp[v + 1] - rp[v];
-    rnd[v] = -1;
-    alive0[v] = v;
+    sti(&deg[v], rp[v + 1] - rp[v]);
+    sti(&rnd[v], -1);
+    sti(&alive0[v], v);
   }
   if (gtid == 0) {
-    ctl->asize[0] = n;
-    ctl->asize[1] = 0;
-    ctl->fsize[0] = 0;
-    ctl->fsize[1] = 0;
-    ctl->min_deg = 0x7FFFFFFF;
+    st_relaxed64(&ctl->t_run, t0);
+    sti(&ctl->asize[0], n);
+    sti(&ctl->asize[1], 0);
+    sti(&ctl->fsize[0], 0);
+    sti(&ctl->fsize[1], 0);
+    sti(&ctl->fsize[2], 0);
+    sti(&ctl->min_deg, 0x7FFFFFFF);
   }
-  grid_barrier(ctl, deadline);
+  grid_sync(ctl, deadline);
 
-  int cur = 0, fb = 0, nf = 0, k = 0, round = 0;
+  int cur = 0, nf = 0, k = 0, r = 0;
   int na = n;
   for (;;) {
     if (ld_relaxed(&ctl->status) & MCE_E_TIMEOUT) return;
     if (nf == 0) {
-      // new level: compact the alive list and find the smallest alive degree
+      // new level: compact the remaining list and find the smallest remaining degree
       const int* src = alive[cur];
       int* dst = alive[cur ^ 1];
       int mn = 0x7FFFFFFF;
       for (int base = wave * MCE_WAVE; base < na; base += nwaves * MCE_WAVE) {
-        int i = base + lane;
+        const int i = base + lane;
         bool keep = false;
         int v = 0;
         if (i < na) {
-          v = src[i];
-          keep = rnd[v] < 0;
-          if (keep) mn = min(mn, deg[v]);
+          v = ldi(&src[i]);
+          keep = ldi(&rnd[v]) < 0;
+          if (keep) mn = min(mn, ldi(&deg[v]));
         }
-        u64 m = ballot(keep);
+        const u64 m = ballot(keep);
         int pos = 0;
         if (lane == 0 && m) pos = atomicAdd(&ctl->asize[cur ^ 1], __popcll(m));
         pos = read_lane(pos, 0);
-        if (keep) dst[pos + mbcnt(m)] = v;
+        if (keep) sti(&dst[pos + mbcnt(m)], v);
       }
-      int wmn = wave_min_i32_nonneg(mn);
+      const int wmn = wave_min_i32_nonneg(mn);
       if (lane == 0 && wmn != 0x7FFFFFFF) atomicMin(&ctl->min_deg, wmn);
-      grid_barrier(ctl, deadline);
+      grid_sync(ctl, deadline);
       if (ld_relaxed(&ctl->status) & MCE_E_TIMEOUT) return;
       cur ^= 1;
-      na = ld_relaxed(&ctl->asize[cur]);
+      na = ldi(&ctl->asize[cur]);
       if (na == 0) break;
-      k = ld_relaxed(&ctl->min_deg);
-      // the frontier of the level's first round
+      k = ldi(&ctl->min_deg);
+      // the level's first round: every remaining vertex of degree <= k
       const int* al = alive[cur];
-      int* fr = front[fb];
+      int* fr = front[r & 1];
       for (int base = wave * MCE_WAVE; base < na; base += nwaves * MCE_WAVE) {
-        int i = base + lane;
+        const int i = base + lane;
         bool in = false;
         int v = 0;
         if (i < na) {
-          v = al[i];
-          in = deg[v] <= k;
+          v = ldi(&al[i]);
+          in = ldi(&deg[v]) <= k;
         }
-        u64 m = ballot(in);
+        const u64 m = ballot(in);
         int pos = 0;
-        if (lane == 0 && m) pos = atomicAdd(&ctl->fsize[fb], __popcll(m));
+        if (lane == 0 && m) pos = atomicAdd(&ctl->fsize[r % 3], __popcll(m));
         pos = read_lane(pos, 0);
-        if (in) fr[pos + mbcnt(m)] = v;
+        if (in) sti(&fr[pos + mbcnt(m)], v);
       }
-      if (gtid == 0) ctl->asize[cur ^ 1] = 0;   // read by nobody until the next level
-      grid_barrier(ctl, deadline);
+      grid_sync(ctl, deadline);
       if (ld_relaxed(&ctl->status) & MCE_E_TIMEOUT) return;
-      nf = ld_relaxed(&ctl->fsize[fb]);
+      nf = ldi(&ctl->fsize[r % 3]);
     }
-    // the round: mark the frontier removed
-    const int* fr = front[fb];
-    for (int i = gtid; i < nf; i += gsize) {
-      int v = fr[i];
-      rnd[v] = round;
-      core[v] = k;
-    }
+    // round r: remove the frontier, take one degree from each remaining neighbour
     if (gtid == 0) {
-      ctl->fsize[fb ^ 1] = 0;
-      ctl->min_deg = 0x7FFFFFFF;
+      // counters nobody reads any more: the frontier size read two rounds ago,
+      // the old remaining-list size and the level's minimum
+      sti(&ctl->fsize[(r + 2) % 3], 0);
+      sti(&ctl->asize[cur ^ 1], 0);
+      sti(&ctl->min_deg, 0x7FFFFFFF);
     }
-    grid_barrier(ctl, deadline);
-    if (ld_relaxed(&ctl->status) & MCE_E_TIMEOUT) return;
-    // ... and take one degree from each alive neighbour
-    int* nx = front[fb ^ 1];
+    const int* fr = front[r & 1];
+    int* nx = front[(r + 1) & 1];
+    int* nxs = &ctl->fsize[(r + 1) % 3];
     for (int i = wave; i < nf; i += nwaves) {
-      int v = fr[i];
-      int a = rp[v], b = rp[v + 1];
+      const int v = ldi(&fr[i]);
+      if (lane == 0) {
+        sti(&rnd[v], r);
+        core[v] = k;
+      }
+      const int a = rp[v], b = rp[v + 1];
       for (int base = a; base < b; base += MCE_WAVE) {
-        int e = base + lane;
+        const int e = base + lane;
         bool joins = false;
         int u = 0;
         if (e < b) {
           u = ci[e];
-          if (__hip_atomic_load(&rnd[u], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < 0) {
-            int old = atomicSub(&deg[u], 1);
-            joins = old == k + 1;
-          }
+          if (ldi(&rnd[u]) < 0) joins = atomicSub(&deg[u], 1) == k + 1;
         }
-        u64 m = ballot(joins);
+        const u64 m = ballot(joins);
         int pos = 0;
-        if (lane == 0 && m) pos = atomicAdd(&ctl->fsize[fb ^ 1], __popcll(m));
+        if (lane == 0 && m) pos = atomicAdd(nxs, __popcll(m));
         pos = read_lane(pos, 0);
-        if (joins) nx[pos + mbcnt(m)] = u;
+        if (joins) sti(&nx[pos + mbcnt(m)], u);
       }
     }
-    grid_barrier(ctl, deadline);
+    grid_sync(ctl, deadline);
     if (ld_relaxed(&ctl->status) & MCE_E_TIMEOUT) return;
-    fb ^= 1;
-    nf = ld_relaxed(&ctl->fsize[fb]);
-    round++;
+    nf = ldi(nxs);
+    r++;
   }
   if (gtid == 0) {
-    ctl->rounds = round;
+    ctl->rounds = r;
     ctl->degeneracy = k;
   }
 }

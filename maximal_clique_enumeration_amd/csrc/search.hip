@@ -295,7 +295,7 @@ __global__ __launch_bounds__(64) void k_search(SearchParams prm) {
   const int* __restrict__ ci = prm.ci;
   MceWl* wl = prm.wl;
   const u64 t_start = wall_clock64();
-  const u64 deadline = t_start + prm.budget;
+  const u64 deadline = ld_relaxed64(prm.t_run) + prm.budget;
 
   char* slot = prm.slots + (size_t)wid * prm.slot_bytes;
   u64* mail = (u64*)(slot + prm.s_mail);
@@ -693,7 +693,7 @@ __global__ __launch_bounds__(64) void k_search_w1(SearchParams prm) {
   if (lane == 0) {
     const u64 t0 = wall_clock64();
     s_misc[0] = t0;
-    s_misc[1] = t0 + prm.budget;
+    s_misc[1] = ld_relaxed64(prm.t_run) + prm.budget;
     s_misc[2] = 0;
     s_misc[3] = 0;
     s_misc[4] = 0;
