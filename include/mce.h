@@ -66,6 +66,9 @@ typedef enum {
 #define MCE_FLAG_PHASE_TIMES 2u  /* record per-phase GPU times in mce_run_stats */
 #define MCE_FLAG_COUNTERS 4u     /* count pivot rows, X_X tests and branches (mce_run_stats.pivot_rows,
                                     xx_tests, branches); the width-1 search kernel skips them otherwise */
+#define MCE_FLAG_NO_MICRO 8u     /* subtrees with |P| <= 64 and |X| <= 64 go to the width-1 wavefront
+                                    kernel like the rest; by default the micro kernel searches them, one
+                                    search-tree node per lane (section 3.1's finer work split) */
 
 /* mce_config.subgraph: how each subtree's induced subgraph is encoded (section
    3.4). Partial: bit rows for P x P only, edges between P and X looked up in the
@@ -81,7 +84,8 @@ typedef struct {
   int32_t device;         /* HIP device ordinal; -1: the device current at mce_create */
   int32_t worker_list;    /* 1: idle wavefronts receive donated branches (section 3.3); 0: off */
   int32_t donate_min_p;   /* donate a branch only if its P has at least this many vertices
-                             (section 3.3 uses 10); must be >= 1 */
+                             (section 3.3 uses 10); the micro kernel hands over a batch of
+                             frames, and the bound applies to their |P| summed; must be >= 1 */
   int32_t validate;       /* 1: check the CSR before searching (MCE_ERR_GRAPH on failure) */
   int32_t max_workers;    /* 0: as many wavefronts as are resident; else at most this many */
   int64_t timeout_ms;     /* wall-clock limit of one run, counted from the start of the peel; 0: 120000 */
@@ -134,6 +138,12 @@ typedef struct {
   uint64_t donate_ok_ticks;  /* ticks of the successful donations alone */
   uint64_t branches;         /* branches taken (child nodes and leaf tests); with MCE_FLAG_COUNTERS
                                 for the width-1 kernel */
+  uint64_t max_stack_frames; /* micro kernel: most frames one wavefront's stack held */
+  int32_t micro_roots;       /* first-level subtrees searched by the micro kernel */
+  int32_t pad2_;
+  uint64_t steps;            /* micro kernel: wavefront steps (each lane holding a frame takes one
+                                node or branch) */
+  uint64_t lane_steps;       /* micro kernel: lanes holding a frame, summed over steps */
 } mce_run_stats;
 
 /* Fills cfg with the defaults: device -1, worker_list 1, donate_min_p 10,

@@ -20,7 +20,7 @@ LIB_PATH = os.path.join(_HERE, "libmce.so")
 MCE_OK, MCE_ERR_ARG, MCE_ERR_GRAPH, MCE_ERR_NOMEM = 0, -1, -2, -3
 MCE_ERR_DEVICE, MCE_ERR_STATE, MCE_ERR_TIMEOUT, MCE_ERR_LIMIT = -4, -5, -6, -7
 MCE_GRAPH_ROWPTR, MCE_GRAPH_RANGE, MCE_GRAPH_LOOP, MCE_GRAPH_ORDER, MCE_GRAPH_ASYM = 1, 2, 4, 8, 16
-MCE_FLAG_HBM_STAGING, MCE_FLAG_PHASE_TIMES, MCE_FLAG_COUNTERS = 1, 2, 4
+MCE_FLAG_HBM_STAGING, MCE_FLAG_PHASE_TIMES, MCE_FLAG_COUNTERS, MCE_FLAG_NO_MICRO = 1, 2, 4, 8
 MCE_SUBGRAPH_AUTO, MCE_SUBGRAPH_PARTIAL, MCE_SUBGRAPH_FULL = 0, 1, 2
 
 # every function the C header declares
@@ -71,7 +71,12 @@ class mce_run_stats(ctypes.Structure):
                 ("donate_ticks", ctypes.c_uint64), ("setup_ticks", ctypes.c_uint64),
                 ("first_ticks", ctypes.c_uint64), ("start_spread_ticks", ctypes.c_uint64),
                 ("claim_checks", ctypes.c_uint64), ("donate_ok_ticks", ctypes.c_uint64),
-                ("branches", ctypes.c_uint64)]
+                ("branches", ctypes.c_uint64),
+                ("max_stack_frames", ctypes.c_uint64),
+                ("micro_roots", ctypes.c_int32),
+                ("pad2_", ctypes.c_int32),
+                ("steps", ctypes.c_uint64),
+                ("lane_steps", ctypes.c_uint64)]
 
 
 _lib = None
@@ -185,7 +190,7 @@ class Engine:
     def __init__(self, device: int | None = None, worker_list: bool = True, donate_min_p: int = 10,
                  validate: bool = True, max_workers: int = 0, timeout_ms: int = 120000,
                  hbm_staging: bool = False, phase_times: bool = False, subgraph: str = "auto",
-                 counters: bool = False):
+                 counters: bool = False, micro: bool = True):
         import torch
         if device is None:
             device = torch.cuda.current_device()
@@ -199,7 +204,7 @@ class Engine:
         cfg.max_workers = max_workers
         cfg.timeout_ms = timeout_ms
         cfg.flags = ((MCE_FLAG_HBM_STAGING if hbm_staging else 0) | (MCE_FLAG_PHASE_TIMES if phase_times else 0)
-                     | (MCE_FLAG_COUNTERS if counters else 0))
+                     | (MCE_FLAG_COUNTERS if counters else 0) | (0 if micro else MCE_FLAG_NO_MICRO))
         modes = {"auto": MCE_SUBGRAPH_AUTO, "partial": MCE_SUBGRAPH_PARTIAL, "full": MCE_SUBGRAPH_FULL}
         if subgraph not in modes:
             raise ValueError(f"subgraph must be one of {sorted(modes)}")
@@ -288,4 +293,4 @@ class Engine:
         st = mce_run_stats()
         st.struct_size = ctypes.sizeof(mce_run_stats)
         self._check(mce_stats(self._h, st), "mce_stats", self._h)
-        return {name: getattr(st, name) for name, _ in mce_run_stats._fields_ if name != "pad_"}
+        return {name: getattr(st, name) for name, _ in mce_run_stats._fields_ if name not in ("pad_", "pad2_")}

@@ -10,7 +10,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libmce.so")
-SOURCES = ["prep.hip", "subgraph.hip", "search.hip", "engine.cpp"]
+SOURCES = ["prep.hip", "subgraph.hip", "search.hip", "micro.hip", "engine.cpp"]
 
 HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")
 ARCH = os.environ.get("MCE_OFFLOAD_ARCH", "gfx950")

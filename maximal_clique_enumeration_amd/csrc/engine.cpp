@@ -40,7 +40,7 @@ struct mce_engine {
   std::string err;
 
   DevBuf ctl, deg, rnd, core, alive0, alive1, front0, front1, pcount, xcount, lists, taboff, heap, results, wl,
-      slots, stats;
+      slots, stats, mstack, mail;
   HostPinned host;    // staging for device -> host copies
   hipEvent_t ev[4 + 4 * MCE_NSUB] = {};
   bool have_events = false;
@@ -104,6 +104,7 @@ double ms_since(std::chrono::steady_clock::time_point t0) {
 }
 
 constexpr size_t kHistWords = MCE_MAX_P + 2;   // global histogram entries
+constexpr int kMicroStack = 4096;              // frames per wavefront stack of the micro search
 
 mce_status run_impl(mce_engine* e, int32_t n, int64_t nnz, const int32_t* row_ptr, const int32_t* col_idx,
                     const int32_t* roots, int32_t nroots, bool subset, void* stream) {
@@ -216,16 +217,18 @@ mce_status run_impl(mce_engine* e, int32_t n, int64_t nnz, const int32_t* row_pt
   }
   e->info.subgraph = mode == MCE_MODE_IPX ? MCE_SUBGRAPH_FULL : MCE_SUBGRAPH_PARTIAL;
 
-  // roots per sub-class of that mode
+  // roots per sub-class of that mode (and with the micro sub-class on or off)
+  const bool micro_on = (e->cfg.flags & MCE_FLAG_NO_MICRO) == 0;
+  const int var = mode | (micro_on ? 0 : 2);
   SubOffsets off{};
   int counts[MCE_NSUB];
   int total = 0;
   size_t heap_words = 0;
   for (int c = 0; c < MCE_NSUB; c++) {
-    counts[c] = hctl->sub_count[mode][c];
+    counts[c] = hctl->sub_count[var][c];
     off.off[c] = total;
     total += counts[c];
-    heap_words = std::max(heap_words, (size_t)hctl->sub_words[mode][c]);
+    heap_words = std::max(heap_words, (size_t)hctl->sub_words[var][c]);
   }
   const u64 iso = hctl->isolated, iso_hash = hctl->isolated_hash;
 
@@ -235,20 +238,28 @@ mce_status run_impl(mce_engine* e, int32_t n, int64_t nnz, const int32_t* row_pt
     SearchLayout L;
   };
   std::vector<Plan> plan;
-  size_t slot_bytes = 0;
+  size_t slot_bytes = 0, mstack_bytes = 0, mail_bytes = 0;
   int stat_rows = 0;
+  const bool counters = (e->cfg.flags & MCE_FLAG_COUNTERS) != 0;
   for (int c = MCE_NSUB - 1; c >= 0; c--) {
     if (counts[c] == 0) continue;
-    Plan pl;
+    Plan pl{};
     pl.sub = c;
-    pl.L = mce_search_layout(c, mode, hctl->sub_maxp[mode][c], hctl->sub_maxx[mode][c], hctl->sub_maxr[mode][c],
-                             hbm, (e->cfg.flags & MCE_FLAG_COUNTERS) != 0);
-    int nw = mce_search_max_workers(pl.L, e->num_cu);
+    int nw;
+    if (c == MCE_SUB_MICRO) {
+      nw = mce_micro_max_workers(counters, e->num_cu);
+      mstack_bytes = (size_t)std::max(nw, 1) * 6 * kMicroStack * sizeof(u64);
+      mail_bytes = (size_t)std::max(nw, 1) * mce_micro_mail_words() * sizeof(u64);
+    } else {
+      pl.L = mce_search_layout(c, mode, hctl->sub_maxp[var][c], hctl->sub_maxx[var][c], hctl->sub_maxr[var][c],
+                               hbm, counters);
+      nw = mce_search_max_workers(pl.L, e->num_cu);
+    }
     if (nw <= 0) return fail(e, MCE_ERR_DEVICE, "search kernel occupancy query failed");
     if (e->cfg.max_workers > 0) nw = std::min(nw, (int)e->cfg.max_workers);
     if (!e->cfg.worker_list) nw = std::min(nw, counts[c]);
     pl.nw = nw;
-    slot_bytes = std::max(slot_bytes, pl.L.slot_bytes * (size_t)nw);
+    if (c != MCE_SUB_MICRO) slot_bytes = std::max(slot_bytes, pl.L.slot_bytes * (size_t)nw);
     stat_rows += nw;
     plan.push_back(pl);
   }
@@ -256,12 +267,14 @@ mce_status run_impl(mce_engine* e, int32_t n, int64_t nnz, const int32_t* row_pt
     if ((h = ensure(e->taboff, (size_t)total * sizeof(u64))) != hipSuccess ||
         (h = ensure(e->heap, heap_words * sizeof(u64))) != hipSuccess ||
         (h = ensure(e->slots, slot_bytes)) != hipSuccess ||
-        (h = ensure(e->stats, (size_t)stat_rows * MCE_NSTAT * sizeof(u64))) != hipSuccess)
+        (h = ensure(e->stats, (size_t)stat_rows * MCE_NSTAT * sizeof(u64))) != hipSuccess ||
+        (mstack_bytes && (h = ensure(e->mstack, mstack_bytes)) != hipSuccess) ||
+        (mail_bytes && (h = ensure(e->mail, mail_bytes)) != hipSuccess))
       return hip_fail(e, h, "search buffers");
     if ((h = hipMemsetAsync(e->stats.p, 0, (size_t)stat_rows * MCE_NSTAT * sizeof(u64), s)) != hipSuccess)
       return hip_fail(e, h, "memset");
-    if ((h = mce_launch_bucket(subset ? roots : nullptr, cnt, dp<int>(e->pcount), dp<int>(e->xcount), mode, off,
-                               dp<int>(e->lists), ctl, grid, s)) != hipSuccess)
+    if ((h = mce_launch_bucket(subset ? roots : nullptr, cnt, dp<int>(e->pcount), dp<int>(e->xcount), mode,
+                               micro_on ? 1 : 0, off, dp<int>(e->lists), ctl, grid, s)) != hipSuccess)
       return hip_fail(e, h, "bucket launch");
   }
   if (timing) (void)hipEventRecord(e->ev[3], s);
@@ -277,8 +290,10 @@ mce_status run_impl(mce_engine* e, int32_t n, int64_t nnz, const int32_t* row_pt
     bp.rnd = dp<int>(e->rnd);
     bp.roots = dp<int>(e->lists) + off.off[c];
     bp.nroots = counts[c];
-    bp.W = 1 << L.wclass;
-    bp.mode = mode;
+    const bool micro = c == MCE_SUB_MICRO;
+    bp.W = micro ? 1 : 1 << L.wclass;
+    bp.mode = micro ? MCE_MODE_IPX : mode;
+    bp.micro = micro ? 1 : 0;
     bp.heap = dp<u64>(e->heap);
     bp.heap_words = heap_words;
     bp.heap_top = &ctl->heap_top[c];
@@ -288,6 +303,34 @@ mce_status run_impl(mce_engine* e, int32_t n, int64_t nnz, const int32_t* row_pt
     if ((h = mce_launch_build(bp, e->num_cu * 16, s)) != hipSuccess) return hip_fail(e, h, "build launch");
     if (timing) (void)hipEventRecord(e->ev[evi + 1], s);
     if ((h = mce_launch_wl_init(dp<MceWl>(e->wl), pl.nw, s)) != hipSuccess) return hip_fail(e, h, "wl init");
+    if (micro) {
+      MicroParams mp{};
+      mp.heap = dp<u64>(e->heap);
+      mp.tab_off = dp<u64>(e->taboff) + off.off[c];
+      mp.nroots = counts[c];
+      mp.nworkers = pl.nw;
+      mp.stacks = dp<u64>(e->mstack);
+      mp.stack_cap = kMicroStack;
+      mp.mail_words = mce_micro_mail_words();
+      mp.mail = dp<u64>(e->mail);
+      mp.g_hist = results + 1;
+      mp.g_hash = results;
+      mp.wl = dp<MceWl>(e->wl);
+      mp.donate_min_p = std::max(1, (int)e->cfg.donate_min_p);
+      mp.worker_list = e->cfg.worker_list ? 1 : 0;
+      mp.budget = budget;
+      mp.t_run = &ctl->t_run;
+      mp.status = &ctl->status;
+      mp.stats = dp<u64>(e->stats) + (size_t)stat_off * MCE_NSTAT;
+      if (timing) (void)hipEventRecord(e->ev[evi + 2], s);
+      if ((h = mce_launch_micro(counters, mp, s)) != hipSuccess) return hip_fail(e, h, "micro search launch");
+      if (timing) (void)hipEventRecord(e->ev[evi + 3], s);
+      evi += 4;
+      stat_off += pl.nw;
+      launches++;
+      max_workers_used = std::max(max_workers_used, pl.nw);
+      continue;
+    }
     SearchParams prm{};
     prm.rp = row_ptr;
     prm.ci = col_idx;
@@ -340,7 +383,7 @@ mce_status run_impl(mce_engine* e, int32_t n, int64_t nnz, const int32_t* row_pt
   if (hctl->status & MCE_E_LIMIT) return fail(e, MCE_ERR_LIMIT, "subtree larger than its width class");
   if (hctl->status & MCE_E_HEAP) return fail(e, MCE_ERR_DEVICE, "induced-subgraph heap overflow");
   std::vector<u64> stat_sum(MCE_NSTAT, 0);
-  u64 max_busy = 0, max_nodes = 0, max_ticks = 0, start_spread = 0;
+  u64 max_busy = 0, max_nodes = 0, max_ticks = 0, start_spread = 0, max_stack = 0;
   {
     int row = 0;
     for (const Plan& pl : plan) {
@@ -351,6 +394,7 @@ mce_status run_impl(mce_engine* e, int32_t n, int64_t nnz, const int32_t* row_pt
         max_busy = std::max(max_busy, r[ST_BUSY_TICKS]);
         max_nodes = std::max(max_nodes, r[ST_NODES]);
         max_ticks = std::max(max_ticks, r[ST_TOTAL_TICKS]);
+        max_stack = std::max(max_stack, r[ST_STACK_MAX]);
         if (r[ST_START_ABS]) {
           smin = std::min(smin, r[ST_START_ABS]);
           smax = std::max(smax, r[ST_START_ABS]);
@@ -385,7 +429,7 @@ mce_status run_impl(mce_engine* e, int32_t n, int64_t nnz, const int32_t* row_pt
   so.pivot_words = stat_sum[ST_PIVOT_WORDS];
   so.xx_tests = stat_sum[ST_XX_TESTS];
   u64 words_built = 0;
-  for (const Plan& pl : plan) words_built += hctl->sub_words[mode][pl.sub];
+  for (const Plan& pl : plan) words_built += hctl->sub_words[var][pl.sub];
   so.table_words = words_built;
   so.branches = stat_sum[ST_BRANCHES];
   so.busy_ticks = stat_sum[ST_BUSY_TICKS];
@@ -398,6 +442,10 @@ mce_status run_impl(mce_engine* e, int32_t n, int64_t nnz, const int32_t* row_pt
   so.start_spread_ticks = start_spread;
   so.claim_checks = stat_sum[ST_CHECKS];
   so.donate_ok_ticks = stat_sum[ST_DONATE_OK_TICKS];
+  so.max_stack_frames = max_stack;
+  so.steps = stat_sum[ST_STEPS];
+  so.lane_steps = stat_sum[ST_LANE_STEPS];
+  so.micro_roots = counts[MCE_SUB_MICRO];
   if (timing) {
     float a = 0, b = 0, c = 0;
     (void)hipEventElapsedTime(&a, e->ev[0], e->ev[1]);
@@ -564,7 +612,7 @@ void mce_destroy(mce_engine* e) {
   (void)hipSetDevice(e->device);
   DevBuf* bufs[] = {&e->ctl,    &e->deg,   &e->rnd,    &e->core,    &e->alive0, &e->alive1,
                     &e->front0, &e->front1, &e->pcount, &e->xcount, &e->lists,  &e->taboff,
-                    &e->heap,   &e->results, &e->wl,    &e->slots,  &e->stats};
+                    &e->heap,   &e->results, &e->wl,    &e->slots,  &e->stats,  &e->mstack, &e->mail};
   for (DevBuf* b : bufs) release(*b);
   if (e->host.p) (void)hipHostFree(e->host.p);
   for (auto& ev : e->ev)

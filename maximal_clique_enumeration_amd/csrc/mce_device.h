@@ -22,9 +22,14 @@ typedef unsigned int u32;
 #define MCE_MAX_P 2048
 #define MCE_MAX_WORKERS 8192
 // Sub-classes: a width class split by whether a root's induced subgraph (rows
-// and X_X array) is staged in LDS ("light") or read from HBM ("heavy").
-#define MCE_NSUB (2 * MCE_NCLASS)
+// and X_X array) is staged in LDS ("light") or read from HBM ("heavy"), plus the
+// micro sub-class: |P| <= 64 and |X| <= 64, searched one frame per lane.
+#define MCE_SUB_MICRO (2 * MCE_NCLASS)
+#define MCE_NSUB (2 * MCE_NCLASS + 1)
+#define MCE_MICRO_MAX 64
 #define MCE_LIGHT_BYTES 4096
+// classification variants tallied by the orientation: mode | (micro off << 1)
+#define MCE_NVAR 4
 // pivot keys pack (count << 20 | ~local index): local indices stay below 2^20
 #define MCE_MAX_LOCAL ((1 << 20) - 1)
 
@@ -59,9 +64,23 @@ __host__ __device__ inline unsigned long long mce_stage_bytes(int p, int x, int 
          (unsigned long long)x * 4ull;
 }
 
-__host__ __device__ inline int mce_sub_of(int p, int x, int mode) {
+__host__ __device__ inline bool mce_is_micro(int p, int x) { return p <= MCE_MICRO_MAX && x <= MCE_MICRO_MAX; }
+
+// Micro table: the full table's header and P u X rows, then for each P member
+// the bitset of the X members adjacent to it, the P hash terms and the ids.
+__host__ __device__ inline unsigned long long mce_micro_table_words(int p, int x) {
+  return 3ull + (unsigned long long)(p + x) + 2ull * (unsigned long long)p + ((unsigned long long)(p + x) + 1ull) / 2ull;
+}
+
+__host__ __device__ inline int mce_sub_of(int p, int x, int mode, bool micro) {
+  if (micro && mce_is_micro(p, x)) return MCE_SUB_MICRO;
   const int c = mce_class_of(p);
   return 2 * c + (mce_stage_bytes(p, x, 1 << c, mode) > MCE_LIGHT_BYTES ? 1 : 0);
+}
+
+__host__ __device__ inline unsigned long long mce_sub_table_words(int p, int x, int sub, int mode) {
+  if (sub == MCE_SUB_MICRO) return mce_micro_table_words(p, x);
+  return mce_table_words(p, x, 1 << (sub >> 1), mode);
 }
 
 // Control block: one per run, zeroed by the host before the first kernel.
@@ -76,13 +95,13 @@ struct MceCtl {
   int pad0;
   u64 isolated;          // roots of degree 0
   u64 isolated_hash;     // sum of their clique hashes
-  // per induced-subgraph mode and sub-class: roots, largest |P|, largest |X|,
-  // largest row count, heap words of their tables
-  int sub_count[2][MCE_NSUB];
-  int sub_maxp[2][MCE_NSUB];
-  int sub_maxx[2][MCE_NSUB];
-  int sub_maxr[2][MCE_NSUB];   // largest row count of a table
-  u64 sub_words[2][MCE_NSUB];
+  // per classification variant (subgraph mode, micro sub-class on/off) and
+  // sub-class: roots, largest |P|, largest |X|, largest row count, heap words
+  int sub_count[MCE_NVAR][MCE_NSUB];
+  int sub_maxp[MCE_NVAR][MCE_NSUB];
+  int sub_maxx[MCE_NVAR][MCE_NSUB];
+  int sub_maxr[MCE_NVAR][MCE_NSUB];   // largest row count of a table
+  u64 sub_words[MCE_NVAR][MCE_NSUB];
   int sub_cursor[MCE_NSUB];
   u64 heap_top[MCE_NSUB];   // build: bump allocator of each sub-class's heap
   int asize[2];          // peel: alive-list sizes (ping-pong)
@@ -101,7 +120,9 @@ struct MceCtl {
 // reads only its own request word (once per search-tree node) and answers with
 // a branch (MCE_FLAG_TASK, after counting the receiver active) or with
 // MCE_FLAG_RETRY. Every hot word is private to one wave, so no atomic is
-// contended by thousands of waves.
+// contended by thousands of waves. A bitmap of the open request words lets an
+// idle wave pick a busy wave in one read instead of probing idle ones; it is
+// only a hint (the compare-and-swap on the request word decides).
 //
 // Termination does not assume that every wavefront of the grid is resident: a
 // wavefront counts in n_active only while it holds a task or is about to take a
@@ -121,6 +142,9 @@ struct MceWl {
   u32 pad1[MCE_LINE_WORDS - 1];
   u32 done;              // set on abort (time limit or protocol error)
   u32 pad2[MCE_LINE_WORDS - 1];
+  // bit w of word w / 64 (one word per 128-byte line): wave w's request word is
+  // open, a hint for askers
+  u64 open_mask[MCE_MAX_WORKERS / 64 * 16];
   u32 line[MCE_MAX_WORKERS * MCE_LINE_WORDS];   // wave w: flag at [w*32], request at [w*32 + 16]
 };
 

@@ -32,6 +32,9 @@ enum {
   ST_START_ABS,      // wall-clock tick at which the wave started
   ST_CHECKS,         // worker-list claim attempts
   ST_DONATE_OK_TICKS,  // ticks of the successful donations alone
+  ST_STACK_MAX,      // micro kernel: most frames the wave's stack held
+  ST_STEPS,          // micro kernel: steps (every lane advances its frame by one node or branch)
+  ST_LANE_STEPS,     // micro kernel: lanes holding a frame, summed over steps
   MCE_NSTAT
 };
 
@@ -70,6 +73,28 @@ struct SearchParams {
   u64* stats;            // nworkers * MCE_NSTAT
 };
 
+// The micro search (|P| <= 64, |X| <= 64): one frame per lane, a frame stack
+// per wavefront in HBM (structure of arrays: word j of slot i at j * cap + i).
+struct MicroParams {
+  const u64* heap;
+  const u64* tab_off;
+  int nroots;
+  int nworkers;
+  u64* stacks;           // nworkers * 6 * stack_cap words
+  int stack_cap;         // frames per wave, a power of two
+  int mail_words;        // u64 words of one mailbox
+  u64* mail;             // nworkers mailboxes
+  u64* g_hist;
+  u64* g_hash;
+  MceWl* wl;
+  int donate_min_p;
+  int worker_list;
+  u64 budget;
+  const u64* t_run;
+  u32* status;
+  u64* stats;            // nworkers * MCE_NSTAT
+};
+
 struct BuildParams {
   const int* rp;
   const int* ci;
@@ -78,6 +103,7 @@ struct BuildParams {
   int nroots;
   int W;                 // bitset words of the sub-class
   int mode;              // MCE_MODE_IP / MCE_MODE_IPX
+  int micro;             // micro table: full rows plus the X column of every P member
   u64* heap;
   u64 heap_words;
   u64* heap_top;         // bump allocator (zeroed before the launch)
@@ -95,7 +121,7 @@ int mce_peel_max_blocks(int num_cu);
 hipError_t mce_launch_orient(int n, const int* rp, const int* ci, const int* rnd, const int* roots, int nroots,
                              int* pcount, int* xcount, MceCtl* ctl, int blocks, hipStream_t s);
 hipError_t mce_launch_bucket(const int* roots, int nroots, const int* pcount, const int* xcount, int mode,
-                             SubOffsets off, int* lists, MceCtl* ctl, int blocks, hipStream_t s);
+                             int micro, SubOffsets off, int* lists, MceCtl* ctl, int blocks, hipStream_t s);
 
 hipError_t mce_launch_build(const BuildParams& prm, int blocks, hipStream_t s);
 
@@ -104,3 +130,7 @@ SearchLayout mce_search_layout(int sub, int mode, int pcap, int xcap, int rcap, 
 int mce_search_max_workers(const SearchLayout& L, int num_cu);
 hipError_t mce_launch_search(const SearchLayout& L, const SearchParams& prm, hipStream_t s);
 hipError_t mce_launch_wl_init(MceWl* wl, int nworkers, hipStream_t s);
+
+int mce_micro_mail_words();
+int mce_micro_max_workers(bool counters, int num_cu);
+hipError_t mce_launch_micro(bool counters, const MicroParams& prm, hipStream_t s);

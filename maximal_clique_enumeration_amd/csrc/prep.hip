@@ -238,9 +238,10 @@ __global__ __launch_bounds__(256) void k_peel(int n, const int* __restrict__ rp,
 // ------------------------------------------------------------------ orientation
 // Per root: |P| = later neighbours, |X| = earlier ones. Degree-0 roots are
 // maximal cliques of size 1 and are counted here. Roots with 1 <= |P| <= MCE_MAX_P
-// are tallied per sub-class under both induced-subgraph modes (count, largest
-// |P|, |X| and row count, heap words), so that the host can pick the mode and
-// size every launch from one read-back.
+// are tallied per sub-class under every classification variant (subgraph mode,
+// micro sub-class on or off): count, largest |P|, |X| and row count, heap
+// words, so that the host can pick the variant and size every launch from one
+// read-back.
 __global__ __launch_bounds__(256) void k_orient(int n, const int* __restrict__ rp, const int* __restrict__ ci,
                                                  const int* __restrict__ rnd, const int* __restrict__ roots,
                                                  int nroots, int* pcount, int* xcount, MceCtl* ctl) {
@@ -280,8 +281,9 @@ __global__ __launch_bounds__(256) void k_orient(int n, const int* __restrict__ r
       if (p > MCE_MAX_P) lim |= 1u;
       valid = p > 0 && p <= MCE_MAX_P;
     }
-    for (int mode = 0; mode < 2; mode++) {
-      const int sub = valid ? mce_sub_of(p, x, mode) : -1;
+    for (int var = 0; var < MCE_NVAR; var++) {
+      const int mode = var & 1;
+      const int sub = valid ? mce_sub_of(p, x, mode, (var >> 1) == 0) : -1;
       u64 pending = ballot(valid);
       while (pending) {
         const int s = read_lane(sub, __builtin_ctzll(pending));
@@ -290,14 +292,14 @@ __global__ __launch_bounds__(256) void k_orient(int n, const int* __restrict__ r
         pending &= ~m;
         const u32 mp = wave_max_u32(mine ? (u32)p : 0u);
         const u32 mx = wave_max_u32(mine ? (u32)x : 0u);
-        const u32 mr = wave_max_u32(mine ? (u32)mce_table_rows(p, x, mode) : 0u);
-        const u64 words = wave_sum_u64(mine ? mce_table_words(p, x, 1 << (s >> 1), mode) : 0ull);
+        const u32 mr = wave_max_u32(mine ? (u32)mce_table_rows(p, x, s == MCE_SUB_MICRO ? MCE_MODE_IPX : mode) : 0u);
+        const u64 words = wave_sum_u64(mine ? mce_sub_table_words(p, x, s, mode) : 0ull);
         if (lane == 0) {
-          atomicAdd(&ctl->sub_count[mode][s], __popcll(m));
-          atomicMax(&ctl->sub_maxp[mode][s], (int)mp);
-          atomicMax(&ctl->sub_maxx[mode][s], (int)mx);
-          atomicMax(&ctl->sub_maxr[mode][s], (int)mr);
-          atomicAdd(&ctl->sub_words[mode][s], words);
+          atomicAdd(&ctl->sub_count[var][s], __popcll(m));
+          atomicMax(&ctl->sub_maxp[var][s], (int)mp);
+          atomicMax(&ctl->sub_maxx[var][s], (int)mx);
+          atomicMax(&ctl->sub_maxr[var][s], (int)mr);
+          atomicAdd(&ctl->sub_words[var][s], words);
         }
       }
     }
@@ -325,7 +327,7 @@ __global__ __launch_bounds__(256) void k_orient(int n, const int* __restrict__ r
 // the chosen mode, starting at off[sub].
 __global__ __launch_bounds__(256) void k_bucket(const int* __restrict__ roots, int nroots,
                                                  const int* __restrict__ pcount, const int* __restrict__ xcount,
-                                                 int mode, SubOffsets off, int* lists, MceCtl* ctl) {
+                                                 int mode, int micro, SubOffsets off, int* lists, MceCtl* ctl) {
   if (ld_relaxed(&ctl->status) != 0) return;
   const int lane = lane_id();
   const int gsize = gridDim.x * blockDim.x;
@@ -334,7 +336,7 @@ __global__ __launch_bounds__(256) void k_bucket(const int* __restrict__ roots, i
     const int p = i < nroots ? pcount[i] : 0;
     const int x = i < nroots ? xcount[i] : 0;
     const bool valid = p > 0 && p <= MCE_MAX_P;
-    const int sub = valid ? mce_sub_of(p, x, mode) : -1;
+    const int sub = valid ? mce_sub_of(p, x, mode, micro != 0) : -1;
     u64 pending = ballot(valid);
     while (pending) {
       const int s = read_lane(sub, __builtin_ctzll(pending));
@@ -387,8 +389,9 @@ hipError_t mce_launch_orient(int n, const int* rp, const int* ci, const int* rnd
 }
 
 hipError_t mce_launch_bucket(const int* roots, int nroots, const int* pcount, const int* xcount, int mode,
-                             SubOffsets off, int* lists, MceCtl* ctl, int blocks, hipStream_t s) {
+                             int micro, SubOffsets off, int* lists, MceCtl* ctl, int blocks, hipStream_t s) {
   const int nb = max(1, min(blocks, (nroots + 255) / 256));
-  hipLaunchKernelGGL(k_bucket, dim3(nb), dim3(256), 0, s, roots, nroots, pcount, xcount, mode, off, lists, ctl);
+  hipLaunchKernelGGL(k_bucket, dim3(nb), dim3(256), 0, s, roots, nroots, pcount, xcount, mode, micro, off, lists,
+                     ctl);
   return hipGetLastError();
 }

@@ -37,157 +37,7 @@
 // P[W], X_P[W], then the X_X entries as int32
 #define MAIL_HDR 3
 
-// ------------------------------------------------------------------ worker list
-// Every word two waves exchange is an agent-scope relaxed atomic; there is no
-// agent-scope fence anywhere (each would write back or invalidate an L2, which
-// serialises across the chip). Data is published as "atomic stores, wait for
-// completion, flag store" and read after the flag with atomic loads.
-#define WL_SPIN_LIMIT (1u << 22)
-
-__device__ __forceinline__ u32* wl_flag(MceWl* wl, int w) { return &wl->line[(size_t)w * MCE_LINE_WORDS]; }
-__device__ __forceinline__ u32* wl_req(MceWl* wl, int w) {
-  return &wl->line[(size_t)w * MCE_LINE_WORDS + MCE_REQ_WORD];
-}
-__device__ __forceinline__ u32 xorshift32(u32& x) {
-  x ^= x << 13;
-  x ^= x >> 17;
-  x ^= x << 5;
-  return x;
-}
-
-// A wave that starts a task accepts branch requests again.
-__device__ __forceinline__ void wl_open(MceWl* wl, int wid) {
-  if (lane_id() == 0) st_relaxed(wl_req(wl, wid), 0u);
-}
-
-// The request word of this wave, read by every lane (uniform).
-__device__ __forceinline__ u32 wl_poll(MceWl* wl, int wid) { return uni(ld_relaxed(wl_req(wl, wid))); }
-
-// Answer a request without a branch; reopen the request word.
-__device__ __forceinline__ void wl_refuse(MceWl* wl, int wid, int rcv) {
-  if (lane_id() == 0) {
-    st_relaxed(wl_flag(wl, rcv), MCE_FLAG_RETRY);
-    st_relaxed(wl_req(wl, wid), 0u);
-  }
-}
-
-// Hand a branch to rcv after its mailbox was written with atomic stores: count
-// it active (before this wave can ever give up its own share: same-address
-// atomics of one wave stay in order, and the wait below completes the
-// increment before the receiver can run), wake it, reopen the request word.
-__device__ __forceinline__ void wl_give(MceWl* wl, int wid, int rcv) {
-  if (lane_id() == 0) __hip_atomic_fetch_add(&wl->n_active, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  wait_stores_complete();
-  if (lane_id() == 0) {
-    st_relaxed(wl_flag(wl, rcv), MCE_FLAG_TASK);
-    st_relaxed(wl_req(wl, wid), 0u);
-  }
-}
-
-// Receiver side (section 3.3). Closes this wave's request word (refusing a
-// request that raced in), gives up its share of n_active, and asks random busy
-// waves for a branch until one arrives. The wave that brings n_active to zero
-// (no task held anywhere; only active waves hand out branches, so none can
-// appear) writes MCE_FLAG_EXIT into every wake flag. Returns 1 with a task in
-// the mailbox (the donor counted this wave active again), 0 to exit.
-// Ordering: the refusal and the flag reset complete before the share is given
-// up, and an answer flag is only consumed with a compare-and-swap, so the exit
-// broadcast (issued after every share release) cannot be overwritten.
-__device__ int wl_idle(MceWl* wl, int wid, int nworkers, u64 deadline, u32* status, u32& rng) {
-  int res = 0, bcast = 0;
-  if (lane_id() == 0) {
-    u32* my = wl_flag(wl, wid);
-    const u32 old = __hip_atomic_exchange(wl_req(wl, wid), MCE_REQ_CLOSED, __ATOMIC_RELAXED,
-                                          __HIP_MEMORY_SCOPE_AGENT);
-    if (old != 0u && old != MCE_REQ_CLOSED) st_relaxed(wl_flag(wl, (int)old - 1), MCE_FLAG_RETRY);
-    st_relaxed(my, 0u);
-    wait_stores_complete();
-    const int left =
-        __hip_atomic_fetch_add(&wl->n_active, -1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) - 1;
-    if (left <= 0) {
-      if (left < 0) atomicOr(status, MCE_E_PROTO);
-      bcast = 1;
-    } else if (nworkers > 1) {
-      u32 fails = 0, it = 0;
-      bool stop = false;
-      while (!stop) {
-        const u32 f = ld_relaxed(my);
-        if (f == MCE_FLAG_EXIT) break;
-        if ((++it & 15u) == 0 && past_deadline(deadline)) {
-          atomicOr(status, MCE_E_TIMEOUT);
-          st_relaxed(&wl->done, 1u);
-          break;
-        }
-        const int v = (int)(xorshift32(rng) % (u32)nworkers);
-        u32 expected = 0u;
-        if (v != wid && ld_relaxed(wl_req(wl, v)) == 0u &&
-            __hip_atomic_compare_exchange_strong(wl_req(wl, v), &expected, (u32)wid + 1u, __ATOMIC_RELAXED,
-                                                 __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) {
-          // wait for the answer: the asked wave reads its request word once per node
-          u32 spins = 0;
-          for (;;) {
-            const u32 a = ld_relaxed(my);
-            if (a == MCE_FLAG_TASK) {
-              res = 1;
-              stop = true;
-              break;
-            }
-            if (a == MCE_FLAG_EXIT) {
-              stop = true;
-              break;
-            }
-            if (a == MCE_FLAG_RETRY) {
-              u32 e = MCE_FLAG_RETRY;
-              if (!__hip_atomic_compare_exchange_strong(my, &e, 0u, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
-                                                        __HIP_MEMORY_SCOPE_AGENT))
-                stop = true;   // the exit broadcast replaced the refusal
-              break;
-            }
-            if ((++spins & 255u) == 0 && past_deadline(deadline)) {
-              atomicOr(status, MCE_E_TIMEOUT);
-              st_relaxed(&wl->done, 1u);
-              stop = true;
-              break;
-            }
-            __builtin_amdgcn_s_sleep(2);
-          }
-          fails = 0;
-        } else {
-          // the wave asked is idle or busy with another request: back off
-          ++fails;
-          if (fails < 16) __builtin_amdgcn_s_sleep(2);
-          else if (fails < 64) __builtin_amdgcn_s_sleep(16);
-          else __builtin_amdgcn_s_sleep(64);
-        }
-      }
-    }
-  }
-  res = read_lane(res, 0);
-  if (read_lane(bcast, 0)) {
-    for (int i = lane_id(); i < nworkers; i += MCE_WAVE) st_relaxed(wl_flag(wl, i), MCE_FLAG_EXIT);
-  }
-  return res;
-}
-
-// Phase 1 (section 3.3): the next first-level subtree from the shared counter,
-// or nroots when none is left. Every subtree goes through the counter: a wave
-// that has not started yet must never hold a subtree that other waves count as
-// taken, or they could finish and leave while it still needs the worker list.
-__device__ __forceinline__ u32 next_root(MceWl* wl, u32 nroots) {
-  u32 idx = nroots;
-  if (lane_id() == 0) {
-    if (ld_relaxed(&wl->root_ctr) < nroots) idx = atomicAdd(&wl->root_ctr, 1u);
-  }
-  return (u32)read_lane((int)idx, 0);
-}
-
-// Count this wave active, and wait until the increment is performed: it must
-// precede the wave's first root-counter increment, or another wave could see
-// the roots gone and the count at zero while this wave holds a subtree.
-__device__ __forceinline__ void wl_join(MceWl* wl) {
-  if (lane_id() == 0) __hip_atomic_fetch_add(&wl->n_active, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  wait_stores_complete();
-}
+#include "worklist.h"
 
 // ------------------------------------------------------------------ X_X membership
 // Is entry a of X_X adjacent to the branch vertex v (P-local index)?
@@ -318,6 +168,7 @@ __global__ __launch_bounds__(64) void k_search(SearchParams prm) {
   u64 st_nodes = 0, st_leaves = 0, st_don = 0, st_prow = 0, st_xx = 0, st_roots = 0, st_recv = 0, st_br = 0;
   u64 idle_ticks = 0;
   bool phase2 = false;
+  bool req_closed = true;   // the request word starts closed and is closed again by wl_idle
   bool abort = false;
   u32 rng = 0x9E3779B9u ^ ((u32)wid * 0x85EBCA6Bu) ^ (u32)prm.nroots;
   if (rng == 0) rng = 1;
@@ -337,6 +188,7 @@ __global__ __launch_bounds__(64) void k_search(SearchParams prm) {
       if (!prm.worker_list) break;
       const u64 t0 = wall_clock64();
       const int got = wl_idle(wl, wid, prm.nworkers, deadline, prm.status, rng);
+      req_closed = true;
       idle_ticks += wall_clock64() - t0;
       if (!got) break;
       toff = uni(ld_relaxed64(&mail[0]));
@@ -390,7 +242,10 @@ __global__ __launch_bounds__(64) void k_search(SearchParams prm) {
     if constexpr (W == 1) {
       if (lane < p) myrow = rows[lane];
     }
-    if (prm.worker_list) wl_open(wl, wid);
+    if (prm.worker_list && req_closed) {
+      wl_open(wl, wid);
+      req_closed = false;
+    }
     u32 rq_next = 0;   // request word, read at one node and acted on at the next
 
     // ---------------------------------------------------------- depth-first search
@@ -710,6 +565,7 @@ __global__ __launch_bounds__(64) void k_search_w1(SearchParams prm) {
   u32 st_don = 0, st_roots = 0, st_recv = 0, st_checks = 0;
   u64 st_prow = 0, st_xx = 0, st_br = 0;   // CNT only
   bool phase2 = false;
+  bool req_closed = true;   // the request word starts closed and is closed again by wl_idle
   bool abort = false;
   u32 rng = 0x9E3779B9u ^ ((u32)wid * 0x85EBCA6Bu) ^ (u32)prm.nroots;
   if (rng == 0) rng = 1;
@@ -729,6 +585,7 @@ __global__ __launch_bounds__(64) void k_search_w1(SearchParams prm) {
       if (!prm.worker_list) break;
       const u64 t0 = wall_clock64();
       const int got = wl_idle(wl, wid, prm.nworkers, uni(s_misc[1]), prm.status, rng);
+      req_closed = true;
       if (lane == 0) {
         const u64 t1 = wall_clock64();
         s_misc[2] += t1 - t0;
@@ -785,7 +642,10 @@ __global__ __launch_bounds__(64) void k_search_w1(SearchParams prm) {
       if (phase2) s_misc[5] += t1;
       if (s_misc[6] == 0) s_misc[6] = t1;
     }
-    if (prm.worker_list) wl_open(wl, wid);
+    if (prm.worker_list && req_closed) {
+      wl_open(wl, wid);
+      req_closed = false;
+    }
     u32 rq_next = 0;   // request word, read at one node and acted on at the next
 
     // ---------------------------------------------------------- depth-first search

@@ -8,7 +8,8 @@
 //    vertex of P u X over P, the partial one rows for P over P only (P-X edges
 //    are then looked up in the CSR during the search).
 //
-// Table layout (u64 words, see mce_table_words): header (p | x << 32), root id,
+// Table layout (u64 words, see mce_table_words; micro tables add the X column of
+// every P member after the rows, see mce_micro_table_words): header (p | x << 32), root id,
 // root hash term, rows (row a = bit b set iff L[a] ~ P[b], local order = id
 // order, P first), p hash terms of the P members, p + x int32 ids.
 //
@@ -53,8 +54,8 @@ __global__ __launch_bounds__(64) void k_build(BuildParams prm) {
       }
       continue;
     }
-    const long long nrows = mce_table_rows(np, nx, prm.mode);
-    const u64 words = mce_table_words(np, nx, W, prm.mode);
+    const long long nrows = mce_table_rows(np, nx, prm.micro ? MCE_MODE_IPX : prm.mode);
+    const u64 words = prm.micro ? mce_micro_table_words(np, nx) : mce_table_words(np, nx, W, prm.mode);
     u64 off = 0;
     if (lane == 0) off = atomicAdd(prm.heap_top, words);
     off = read_lane(off, 0);
@@ -68,7 +69,8 @@ __global__ __launch_bounds__(64) void k_build(BuildParams prm) {
     if (lane == 0) prm.tab_off[i] = off;
     u64* T = prm.heap + off;
     u64* rows = T + 3;
-    u64* hvs = rows + (size_t)nrows * W;
+    u64* xcol = rows + (size_t)nrows * W;   // micro tables only
+    u64* hvs = prm.micro ? xcol + np : xcol;
     int* ids = (int*)(hvs + np);
     if (lane == 0) {
       T[0] = (u64)(u32)np | ((u64)(u32)nx << 32);
@@ -128,6 +130,15 @@ __global__ __launch_bounds__(64) void k_build(BuildParams prm) {
           const u64 word = ballot(bit);
           if (lane == 0) rows[(size_t)ra * W + w] = word;
         }
+      }
+    }
+    if (prm.micro) {
+      // micro table: X column of every P member (the transpose of the X rows)
+      __syncthreads();   // the X rows are in the table
+      u64 col = 0;
+      if (lane < np) {
+        for (int j = 0; j < nx; j++) col |= ((rows[np + j] >> lane) & 1ull) << j;
+        xcol[lane] = col;
       }
     }
     __syncthreads();

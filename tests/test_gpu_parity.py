@@ -20,14 +20,16 @@ import maximal_clique_enumeration_amd as mce  # noqa: E402
 DEV = torch.device("cuda", 0)
 
 
-@pytest.fixture(scope="module", params=["partial", "full"])
+@pytest.fixture(scope="module", params=["partial", "full", "partial-nomicro", "full-nomicro"])
 def eng(request):
-    """One engine per induced-subgraph encoding (section 3.4): every case that
-    takes this fixture runs under both."""
+    """One engine per induced-subgraph encoding (section 3.4), with the micro
+    kernel (one search-tree node per lane for subtrees with |P|, |X| <= 64) on
+    and off: every case that takes this fixture runs under all four."""
     if not mce.lib_built():
         from maximal_clique_enumeration_amd import build
         build.build()
-    e = mce.Engine(device=0, timeout_ms=20000, subgraph=request.param)
+    sub, _, nomicro = request.param.partition("-")
+    e = mce.Engine(device=0, timeout_ms=20000, subgraph=sub, micro=not nomicro)
     yield e
     e.close()
 
@@ -152,33 +154,54 @@ def test_root_subsets(eng):
 
 
 # ------------------------------------------------------------------ stress matrix
+@pytest.mark.parametrize("micro", [True, False])
 @pytest.mark.parametrize("worker_list", [False, True])
-@pytest.mark.parametrize("donate_min_p", [1, 10, 1000])
+@pytest.mark.parametrize("donate_min_p", [1, 10, 1 << 20])
 @pytest.mark.parametrize("max_workers", [1, 2, 7, 0])
-def test_stress_matrix(worker_list, donate_min_p, max_workers):
+def test_stress_matrix(worker_list, donate_min_p, max_workers, micro):
     graphs = [mi.moon_moser(30), mi.random_small(120, 0.5, 8),
               mi.chung_lu(5000, 10.0, 2.3, None, 2, planted=10, planted_min=8, planted_max=20)]
     donations = 0
     with mce.Engine(device=0, worker_list=worker_list, donate_min_p=donate_min_p,
-                    max_workers=max_workers, timeout_ms=20000) as e:
+                    max_workers=max_workers, timeout_ms=20000, micro=micro) as e:
         for g in graphs:
             check(e, g)
             donations += e.stats()["donations"]
-    if not worker_list or donate_min_p == 1000 or max_workers == 1:
+    if not worker_list or donate_min_p == 1 << 20 or max_workers == 1:
         assert donations == 0
 
 
+@pytest.mark.parametrize("micro", [True, False])
 @pytest.mark.parametrize("max_workers", [2, 7, 64, 0])
-def test_single_root_is_shared(max_workers):
+def test_single_root_is_shared(max_workers, micro):
     """One first-level subtree (root 0 of the Moon-Moser graph on 45 vertices,
     3^14 maximal cliques) and idle wavefronts: the worker list must hand branches
     over, and the result must not change."""
     g = mi.moon_moser(45)
-    with mce.Engine(device=0, donate_min_p=1, max_workers=max_workers, timeout_ms=20000) as e:
+    with mce.Engine(device=0, donate_min_p=1, max_workers=max_workers, timeout_ms=20000, micro=micro) as e:
         got = check(e, g, roots=np.array([0], np.int32))
         assert got.count == 3 ** 14
         st = e.stats()
         assert st["donations"] > 0 and st["leaves"] == 3 ** 14
+        assert st["micro_roots"] == (1 if micro else 0)
+
+
+def test_micro_routing():
+    """Subtrees with |P| <= 64 and |X| <= 64 go to the micro kernel unless it is
+    switched off; larger ones never do. The frame stack stays far below its
+    4096-frame capacity (an overflow is reported as MCE_ERR_LIMIT)."""
+    g = mi.chung_lu(20000, 12.0, 2.3, None, 5, planted=20, planted_min=8, planted_max=25)
+    deg = g.degrees()
+    with mce.Engine(device=0, timeout_ms=20000) as e:
+        check(e, g)
+        st = e.stats()
+        info = e.graph_info()
+        assert 0 < st["micro_roots"] <= int((deg > 0).sum())
+        assert info["max_x"] > 64 and st["launches"] >= 2   # the hubs go to the wavefront kernels
+        assert 0 < st["max_stack_frames"] < 4096
+    with mce.Engine(device=0, timeout_ms=20000, micro=False) as e:
+        check(e, g)
+        assert e.stats()["micro_roots"] == 0 and e.stats()["max_stack_frames"] == 0
 
 
 def test_hbm_staging_and_repeats():
