@@ -196,6 +196,26 @@ mce_status mce_ordering(const mce_engine* e, int32_t* core, int32_t* round, void
 /* Counters of the last run. stats->struct_size must be set by the caller. */
 mce_status mce_stats(const mce_engine* e, mce_run_stats* stats);
 
+/* One wavefront of a search launch in the last run (load-balance trace, section
+   4.3 measures the same imbalance as nodes per SM). Ticks are the device wall
+   clock (mce_run_stats.tick_hz). */
+typedef struct {
+  int32_t launch;           /* search launch index within the run */
+  int32_t worker;           /* wavefront index within the launch */
+  uint64_t start_tick;      /* the wavefront started */
+  uint64_t first_tick;      /* its first task (a subtree or received branches) started; 0: none */
+  uint64_t last_tick;       /* its last task ended */
+  uint64_t end_tick;        /* it left the launch */
+  uint64_t busy_ticks;      /* ticks holding a task */
+  uint64_t nodes;           /* search-tree nodes it expanded */
+  uint64_t donations;       /* branch batches it handed over */
+  uint64_t received;        /* branch batches it received */
+} mce_worker_record;
+
+/* Copies up to cap records of the last run's wavefronts into out (host memory)
+   and stores the number available in *count. out may be NULL to query the count. */
+mce_status mce_worker_trace(const mce_engine* e, mce_worker_record* out, int32_t cap, int32_t* count);
+
 /* Text of the last error of this engine ("" if none). Valid until the next call. */
 const char* mce_last_error(const mce_engine* e);
 

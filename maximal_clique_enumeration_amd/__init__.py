@@ -25,7 +25,7 @@ MCE_SUBGRAPH_AUTO, MCE_SUBGRAPH_PARTIAL, MCE_SUBGRAPH_FULL = 0, 1, 2
 
 # every function the C header declares
 EXPORTS = ("mce_config_init", "mce_create", "mce_run", "mce_run_roots", "mce_result",
-           "mce_graph_info", "mce_ordering", "mce_stats", "mce_last_error",
+           "mce_graph_info", "mce_ordering", "mce_stats", "mce_worker_trace", "mce_last_error",
            "mce_status_string", "mce_destroy")
 
 
@@ -54,6 +54,14 @@ class mce_graph_facts(ctypes.Structure):
                 ("max_p", ctypes.c_int32), ("max_x", ctypes.c_int32),
                 ("isolated", ctypes.c_int64), ("roots", ctypes.c_int64),
                 ("graph_errors", ctypes.c_uint32), ("subgraph", ctypes.c_int32)]
+
+
+class mce_worker_record(ctypes.Structure):
+    _fields_ = [("launch", ctypes.c_int32), ("worker", ctypes.c_int32),
+                ("start_tick", ctypes.c_uint64), ("first_tick", ctypes.c_uint64),
+                ("last_tick", ctypes.c_uint64), ("end_tick", ctypes.c_uint64),
+                ("busy_ticks", ctypes.c_uint64), ("nodes", ctypes.c_uint64),
+                ("donations", ctypes.c_uint64), ("received", ctypes.c_uint64)]
 
 
 class mce_run_stats(ctypes.Structure):
@@ -105,6 +113,7 @@ def load_library():
     lib.mce_graph_info.argtypes = [vp, P(mce_graph_facts)]
     lib.mce_ordering.argtypes = [vp, vp, vp, vp]
     lib.mce_stats.argtypes = [vp, P(mce_run_stats)]
+    lib.mce_worker_trace.argtypes = [vp, P(mce_worker_record), i32, P(i32)]
     lib.mce_last_error.argtypes = [vp]
     lib.mce_last_error.restype = ctypes.c_char_p
     lib.mce_status_string.argtypes = [ctypes.c_int]
@@ -149,6 +158,10 @@ def mce_ordering(engine, core, round_, stream) -> int:
 
 def mce_stats(engine, stats: mce_run_stats) -> int:
     return load_library().mce_stats(engine, ctypes.byref(stats))
+
+
+def mce_worker_trace(engine, out, cap: int, count) -> int:
+    return load_library().mce_worker_trace(engine, out, cap, count)
 
 
 def mce_last_error(engine) -> str:
@@ -288,6 +301,14 @@ class Engine:
         self._check(mce_ordering(self._h, _ptr(core), _ptr(rnd), ctypes.c_void_p(stream.cuda_stream)),
                     "mce_ordering", self._h)
         return core, rnd
+
+    def worker_trace(self) -> list[dict]:
+        """One record per wavefront of the last run's search launches."""
+        n = ctypes.c_int32()
+        self._check(mce_worker_trace(self._h, None, 0, ctypes.byref(n)), "mce_worker_trace", self._h)
+        recs = (mce_worker_record * max(1, n.value))()
+        self._check(mce_worker_trace(self._h, recs, n.value, ctypes.byref(n)), "mce_worker_trace", self._h)
+        return [{name: getattr(r, name) for name, _ in mce_worker_record._fields_} for r in recs[:n.value]]
 
     def stats(self) -> dict:
         st = mce_run_stats()

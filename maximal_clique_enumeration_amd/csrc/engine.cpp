@@ -53,6 +53,7 @@ struct mce_engine {
   std::vector<uint64_t> hist;
   mce_graph_facts info{};
   mce_run_stats stats_out{};
+  std::vector<mce_worker_record> trace;
 };
 
 namespace {
@@ -247,7 +248,8 @@ mce_status run_impl(mce_engine* e, int32_t n, int64_t nnz, const int32_t* row_pt
     pl.sub = c;
     int nw;
     if (c == MCE_SUB_MICRO) {
-      nw = mce_micro_max_workers(counters, e->num_cu);
+      // 8 wavefronts per CU: more add start-up spread and little throughput
+      nw = std::min(mce_micro_max_workers(counters, e->num_cu), 8 * e->num_cu);
       mstack_bytes = (size_t)std::max(nw, 1) * 6 * kMicroStack * sizeof(u64);
       mail_bytes = (size_t)std::max(nw, 1) * mce_micro_mail_words() * sizeof(u64);
     } else {
@@ -383,6 +385,7 @@ mce_status run_impl(mce_engine* e, int32_t n, int64_t nnz, const int32_t* row_pt
   if (hctl->status & MCE_E_LIMIT) return fail(e, MCE_ERR_LIMIT, "subtree larger than its width class");
   if (hctl->status & MCE_E_HEAP) return fail(e, MCE_ERR_DEVICE, "induced-subgraph heap overflow");
   std::vector<u64> stat_sum(MCE_NSTAT, 0);
+  e->trace.clear();
   u64 max_busy = 0, max_nodes = 0, max_ticks = 0, start_spread = 0, max_stack = 0;
   {
     int row = 0;
@@ -390,6 +393,18 @@ mce_status run_impl(mce_engine* e, int32_t n, int64_t nnz, const int32_t* row_pt
       u64 smin = ~0ull, smax = 0;
       for (int w = 0; w < pl.nw; w++, row++) {
         const u64* r = &st[(size_t)row * MCE_NSTAT];
+        mce_worker_record rec{};
+        rec.launch = (int32_t)(&pl - plan.data());
+        rec.worker = w;
+        rec.start_tick = r[ST_START_ABS];
+        rec.first_tick = r[ST_FIRST_ABS];
+        rec.last_tick = r[ST_LAST_ABS];
+        rec.end_tick = r[ST_START_ABS] + r[ST_TOTAL_TICKS];
+        rec.busy_ticks = r[ST_BUSY_TICKS];
+        rec.nodes = r[ST_NODES];
+        rec.donations = r[ST_DONATIONS];
+        rec.received = r[ST_RECEIVED];
+        e->trace.push_back(rec);
         for (int i = 0; i < MCE_NSTAT; i++) stat_sum[i] += r[i];
         max_busy = std::max(max_busy, r[ST_BUSY_TICKS]);
         max_nodes = std::max(max_nodes, r[ST_NODES]);
@@ -588,6 +603,17 @@ mce_status mce_stats(const mce_engine* e, mce_run_stats* stats) {
   size_t n = std::min<size_t>(want, sizeof(mce_run_stats));
   std::memcpy(stats, &e->stats_out, n);
   stats->struct_size = (uint32_t)n;
+  return MCE_OK;
+}
+
+mce_status mce_worker_trace(const mce_engine* e, mce_worker_record* out, int32_t cap, int32_t* count) {
+  if (!e || cap < 0) return MCE_ERR_ARG;
+  if (!e->have_result) return MCE_ERR_STATE;
+  const int32_t n = (int32_t)e->trace.size();
+  if (count) *count = n;
+  if (out) {
+    for (int32_t i = 0; i < std::min(n, cap); i++) out[i] = e->trace[i];
+  }
   return MCE_OK;
 }
 

@@ -35,6 +35,8 @@ enum {
   ST_STACK_MAX,      // micro kernel: most frames the wave's stack held
   ST_STEPS,          // micro kernel: steps (every lane advances its frame by one node or branch)
   ST_LANE_STEPS,     // micro kernel: lanes holding a frame, summed over steps
+  ST_FIRST_ABS,      // wall-clock tick at which the first task started (0: none)
+  ST_LAST_ABS,       // wall-clock tick at which the last task ended
   MCE_NSTAT
 };
 

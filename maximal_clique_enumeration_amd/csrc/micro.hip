@@ -13,13 +13,18 @@
 //
 // MI355X mapping. One 64-lane wavefront works on one root's table (staged in
 // LDS). A search-tree node is a self-contained frame of six words: P, X_P, X_X,
-// C (branches left, once the pivot is known), the hash sum of R, and |R| with a
-// started flag. The wave's lanes share one LIFO frame stack in HBM (structure of
-// arrays, so a step's pops and pushes are coalesced). Each step:
-//   1. lanes without a frame pop one from the top;
-//   2. fresh frames compute their pivot (lane-private loop over the candidates);
-//   3. every started frame takes one branch: a leaf is counted at once; a lane
-//      that descends pushes its parent when the parent has branches left;
+// C (branches left, once the pivot is known), the hash sum of R, and |R|. The
+// wave's lanes share one LIFO stack of started frames (pivot known, branches
+// left): its top MICRO_L frames live in LDS, older ones spill to a per-wave HBM
+// area (structure of arrays, so spills and refills are coalesced). Each step:
+//   1. lanes without a frame pop the newest ones;
+//   2. lanes whose frame has no pivot yet score up to MICRO_K pivot candidates
+//      (Tomita: the vertex of P u X with the most neighbours in P); a frame with
+//      more candidates carries its partial maximum into the next step, so one
+//      shallow frame does not hold 63 lanes for a whole scan;
+//   3. lanes with a started frame take branches: up to MICRO_B leaf branches
+//      (R u {v} with P n N(v) empty) in a row, or one branch that descends, after
+//      which the parent goes on the stack if it has branches left;
 //   4. a pending branch request from an idle wave is answered with frames from
 //      the bottom of the stack (the shallowest, largest ones).
 // Every frame is a whole node of Algorithm 2, so any lane of any wave can carry
@@ -29,8 +34,20 @@
 #include "mce_internal.h"
 #include "worklist.h"
 
-#define MF 6            // words per frame
-#define MICRO_DON 32    // frames per donation at most
+#ifndef MICRO_K
+#define MICRO_K 8      // pivot candidates scored per lane and step
+#endif
+#ifndef MICRO_B
+#define MICRO_B 4      // leaf branches per lane and step
+#endif
+#ifndef MICRO_L
+#define MICRO_L 256    // stack frames kept in LDS (power of two, >= 128)
+#endif
+#define MF 6           // words per frame
+#define MICRO_QCAP (MCE_WAVE * (MICRO_B + 1))
+#define MICRO_DON 32   // frames per donation at most
+
+static_assert((MICRO_L & (MICRO_L - 1)) == 0 && MICRO_L >= 128, "LDS stack size");
 
 template <bool CNT>
 __global__ __launch_bounds__(64) void k_search_micro(MicroParams prm) {
@@ -38,6 +55,10 @@ __global__ __launch_bounds__(64) void k_search_micro(MicroParams prm) {
   __shared__ u64 s_xcol[MCE_MICRO_MAX];
   __shared__ u64 s_hv[MCE_MICRO_MAX];
   __shared__ u64 s_hist[MCE_MICRO_MAX + 4];
+  __shared__ u64 s_stk[MF][MICRO_L];
+  // found cliques waiting for their hash mix (sum of member terms + |C| G),
+  // mixed 64 at a time so that every lane of the mix is busy
+  __shared__ u64 s_q[MICRO_QCAP];
 
   const int lane = lane_id();
   const int wid = blockIdx.x;
@@ -49,18 +70,21 @@ __global__ __launch_bounds__(64) void k_search_micro(MicroParams prm) {
   wl_join(wl);
   __syncthreads();
 
-  const u32 cap = (u32)prm.stack_cap;   // power of two
-  const u32 cmask = cap - 1;
-  u64* stk = prm.stacks + (size_t)wid * MF * cap;   // word j of slot i at stk[j * cap + i]
+  const u32 cap = (u32)prm.stack_cap;   // HBM frames per wave, a power of two
+  const u32 cmask = cap - 1u;
+  const u32 lmask = MICRO_L - 1u;
+  u64* hstk = prm.stacks + (size_t)wid * MF * cap;   // word j of slot i at hstk[j * cap + i]
   u64* mail = prm.mail + (size_t)wid * prm.mail_words;
 
-  u64 hacc = 0;   // per lane: sum of the clique hashes this lane reported
+  u64 hacc = 0;   // per lane: sum of the clique hashes this lane mixed
+  u32 qn = 0;     // cliques in s_q (uniform)
   u64 st_nodes = 0, st_br = 0, st_don = 0, st_roots = 0, st_recv = 0, st_prow = 0;
-  u64 idle_ticks = 0;
-  u32 max_depth_stack = 0;
   u64 st_steps = 0, st_lanes = 0;
+  u64 idle_ticks = 0;
+  u32 max_stack = 0;
   u32 rng = 0x9E3779B9u ^ ((u32)wid * 0x85EBCA6Bu) ^ (u32)prm.nroots;
   if (rng == 0) rng = 1;
+  u64 t_first = 0, t_last = 0;
   bool phase2 = false;
   bool req_closed = true;   // the request word starts closed and is closed again by wl_idle
   bool abort = false;
@@ -91,15 +115,20 @@ __global__ __launch_bounds__(64) void k_search_micro(MicroParams prm) {
     const u64 hdr = uni(T[0]);
     const int p = (int)(u32)hdr;
     const int x = (int)(hdr >> 32);
-    for (int i = lane; i < p + x; i += MCE_WAVE) s_rows[i] = T[3 + i];
+    // rows: P member j at j, X_X member a at MCE_MICRO_MAX + a
+    if (lane < p) s_rows[lane] = T[3 + lane];
+    if (lane < x) s_rows[MCE_MICRO_MAX + lane] = T[3 + p + lane];
     if (lane < p) {
       s_xcol[lane] = T[3 + p + x + lane];
       s_hv[lane] = T[3 + p + x + p + lane];
     }
-    // lane frame
+    // the lane's frame, and its pivot scan while the frame is not started
     u64 fP = 0, fX = 0, fXX = 0, fC = 0, fS = 0;
     int fK = 0;
     bool fst = false, has = false;
+    u64 pcm = 0, pcx = 0;   // candidates left to score: P u X_P rows, X_X rows
+    u32 pbc = 0;            // best score so far: neighbours in P plus one (0: none yet)
+    u64 pbr = 0;            // its row
     if (!phase2) {
       if (lane == 0) {
         fP = p >= 64 ? ~0ull : ((1ull << p) - 1);
@@ -107,19 +136,20 @@ __global__ __launch_bounds__(64) void k_search_micro(MicroParams prm) {
         fS = T[2];
         fK = 1;
         has = true;
+        pcm = fP;
+        pcx = fXX;
       }
       st_roots++;
     } else {
-      if (lane < nfr) {
+      if (lane < nfr) {   // donated frames are started
         const u64* mf = mail + 2;
         fP = ld_relaxed64(&mf[0 * MICRO_DON + lane]);
         fX = ld_relaxed64(&mf[1 * MICRO_DON + lane]);
         fXX = ld_relaxed64(&mf[2 * MICRO_DON + lane]);
         fC = ld_relaxed64(&mf[3 * MICRO_DON + lane]);
         fS = ld_relaxed64(&mf[4 * MICRO_DON + lane]);
-        const u64 m = ld_relaxed64(&mf[5 * MICRO_DON + lane]);
-        fK = (int)(u32)m;
-        fst = (m >> 32) != 0;
+        fK = (int)ld_relaxed64(&mf[5 * MICRO_DON + lane]);
+        fst = true;
         has = true;
       }
       st_recv++;
@@ -129,30 +159,41 @@ __global__ __launch_bounds__(64) void k_search_micro(MicroParams prm) {
       wl_open(wl, wid);
       req_closed = false;
     }
-    u32 bot = 0, top = 0;   // the wave's stack holds slots [bot, top) (mod cap)
+    if (t_first == 0) t_first = wall_clock64();
+    // the stack holds virtual slots [bot, top): [bot, mid) in HBM (slot & cmask),
+    // [mid, top) in LDS (slot & lmask)
+    u32 bot = 0, mid = 0, top = 0;
 
     // ---------------------------------------------------------- steps
     for (;;) {
       // this wave's request word, read now and acted on at the end of the step
-      // (the load completes while the step works)
       u32 rq_raw = 0u;
       if (prm.worker_list) rq_raw = ld_relaxed(wl_req(wl, wid));
+
       // 1. lanes without a frame pop the newest ones
       const u64 idle = ballot(!has);
-      const u32 avail = top - bot;
-      if (idle && avail) {
-        const u32 take = min((u32)__popcll(idle), avail);
+      if (idle && top != bot) {
+        if (top == mid) {
+          // LDS part empty: bring the newest HBM frames back
+          const u32 f = min(mid - bot, (u32)MCE_WAVE);
+          if ((u32)lane < f) {
+            const u32 v = mid - f + (u32)lane;
+            for (int j = 0; j < MF; j++) s_stk[j][v & lmask] = hstk[(size_t)j * cap + (v & cmask)];
+          }
+          mid -= f;
+          __syncthreads();
+        }
+        const u32 take = min((u32)__popcll(idle), top - mid);
         const u32 rank = (u32)mbcnt(idle);
         if (!has && rank < take) {
-          const u32 slot = (top - 1u - rank) & cmask;
-          fP = stk[0 * (size_t)cap + slot];
-          fX = stk[1 * (size_t)cap + slot];
-          fXX = stk[2 * (size_t)cap + slot];
-          fC = stk[3 * (size_t)cap + slot];
-          fS = stk[4 * (size_t)cap + slot];
-          const u64 m = stk[5 * (size_t)cap + slot];
-          fK = (int)(u32)m;
-          fst = (m >> 32) != 0;
+          const u32 sl = (top - 1u - rank) & lmask;
+          fP = s_stk[0][sl];
+          fX = s_stk[1][sl];
+          fXX = s_stk[2][sl];
+          fC = s_stk[3][sl];
+          fS = s_stk[4][sl];
+          fK = (int)s_stk[5][sl];
+          fst = true;
           has = true;
         }
         top -= take;
@@ -178,120 +219,180 @@ __global__ __launch_bounds__(64) void k_search_micro(MicroParams prm) {
         }
       }
 
-      // 2. pivot of the fresh frames: the candidate of P u X_P u X_X with the
-      //    most neighbours in P (Tomita); an X vertex adjacent to all of P ends
-      //    the node at once
-      const bool fresh = has && !fst;
-      st_nodes += (u64)__popcll(ballot(fresh));
-      if (fresh) {
-        const u32 pc = (u32)__popcll(fP);
-        u64 cm = fP | fX;
-        u32 bc = 0;
-        u64 brow = 0;
-        bool found = false;
-        while (cm) {
-          const int u = __builtin_ctzll(cm);
-          cm &= cm - 1;
-          const u64 r = s_rows[u];
-          const u32 c = (u32)__popcll(fP & r);
-          if (!found || c > bc) {
-            bc = c;
-            brow = r;
-            found = true;
+      // 2. pivot scan (Tomita): score the next MICRO_K candidates of P u X_P
+      //    (rows 0..p-1) and X_X (rows from MCE_MICRO_MAX) by |P n N(u)|; the
+      //    candidates are picked first so that their row reads overlap. An X
+      //    vertex adjacent to all of P ends the node (no maximal clique below it).
+      const bool pv = has && !fst;
+      if (ballot(pv)) {
+        const u32 pc1 = (u32)__popcll(fP) + 1u;   // a score of pc1 means |P n N(u)| = |P|
+        if (pv) {
+          int cu[MICRO_K];
+          bool cv[MICRO_K];
+#pragma unroll
+          for (int i = 0; i < MICRO_K; i++) {
+            cv[i] = (pcm | pcx) != 0ull;
+            if (pcm) {
+              cu[i] = __builtin_ctzll(pcm);
+              pcm &= pcm - 1ull;
+            } else if (pcx) {
+              cu[i] = MCE_MICRO_MAX + __builtin_ctzll(pcx);
+              pcx &= pcx - 1ull;
+            } else {
+              cu[i] = 0;
+            }
           }
-          if constexpr (CNT) st_prow++;
-        }
-        u64 cx = fXX;
-        while (cx && bc < pc) {
-          const int a = __builtin_ctzll(cx);
-          cx &= cx - 1;
-          const u64 r = s_rows[p + a];
-          const u32 c = (u32)__popcll(fP & r);
-          if (c > bc) {
-            bc = c;
-            brow = r;
+          u64 cr[MICRO_K];
+#pragma unroll
+          for (int i = 0; i < MICRO_K; i++) cr[i] = s_rows[cu[i]];
+#pragma unroll
+          for (int i = 0; i < MICRO_K; i++) {
+            const u32 c = cv[i] ? (u32)__popcll(fP & cr[i]) + 1u : 0u;
+            if (c > pbc) {
+              pbc = c;
+              pbr = cr[i];
+            }
+            if constexpr (CNT) st_prow += cv[i] ? 1u : 0u;
           }
-          if constexpr (CNT) st_prow++;
         }
-        fC = fP & ~brow;
-        fst = true;
-        if (fC == 0) has = false;
+        const bool done = pv && ((pcm | pcx) == 0ull || pbc >= pc1);
+        st_nodes += (u64)__popcll(ballot(done));
+        if (done) {
+          fC = pbc >= pc1 ? 0ull : fP & ~pbr;
+          fst = true;
+          if (fC == 0) has = false;
+        }
       }
 
-      // 3. one branch per started frame (Algorithm 2: child (P n N(v), X n N(v)),
-      //    then P -= {v}, X += {v})
-      const bool br = has && fst;
-      st_br += (u64)__popcll(ballot(br));
-      bool push = false, emit = false;
+      // 3. branches (Algorithm 2: child (P n N(v), X n N(v)), then P -= {v},
+      //    X += {v}) in ascending order of v; the next MICRO_B branch vertices are
+      //    known up front, so their reads overlap. Leaf branches are taken in a
+      //    row; a descending one ends the lane's step.
+      bool push = false;
+      u32 nemit = 0;
       int kemit = 0;
       u64 pP = 0, pX = 0, pXX = 0, pC = 0, pS = 0;
       int pK = 0;
-      if (br) {
-        const int v = __builtin_ctzll(fC);
-        const u64 vbit = 1ull << v;
-        fC ^= vbit;
-        fP ^= vbit;
-        const u64 r = s_rows[v];
-        const u64 pn = fP & r;
-        const u64 xn = fX & r;
-        const u64 xxn = fXX & s_xcol[v];
-        fX |= vbit;
-        const u64 sc = fS + s_hv[v];
-        const int kc = fK + 1;
-        if (pn == 0) {
-          // a leaf: R u {v} is maximal iff X n N(v) is empty
-          if ((xn | xxn) == 0) {
-            emit = true;
-            kemit = kc;
-            hacc += mce_clique_term(sc, kc);
+      // (the loop runs in every lane so that found cliques can be queued with
+      // wave-wide ballots; lanes without a started frame take no branch)
+      {
+        const bool brl = has && fst;
+        int bv[MICRO_B];
+        bool bval[MICRO_B];
+        u64 cm = brl ? fC : 0ull;
+#pragma unroll
+        for (int i = 0; i < MICRO_B; i++) {
+          bval[i] = cm != 0ull;
+          bv[i] = bval[i] ? __builtin_ctzll(cm) : 0;
+          cm &= cm - 1ull;
+        }
+        u64 br_row[MICRO_B], br_xc[MICRO_B], br_hv[MICRO_B];
+#pragma unroll
+        for (int i = 0; i < MICRO_B; i++) {
+          br_row[i] = s_rows[bv[i]];
+          br_xc[i] = s_xcol[bv[i]];
+          br_hv[i] = s_hv[bv[i]];
+        }
+        bool go = brl;
+#pragma unroll
+        for (int i = 0; i < MICRO_B; i++) {
+          bool emit = false;
+          u64 z = 0;
+          if (go && bval[i]) {
+            const u64 vbit = 1ull << bv[i];
+            fC ^= vbit;
+            fP ^= vbit;
+            const u64 r = br_row[i];
+            const u64 pn = fP & r;
+            const u64 xn = fX & r;
+            const u64 xxn = fXX & br_xc[i];
+            fX |= vbit;
+            const u64 sc = fS + br_hv[i];
+            const int kc = fK + 1;
+            if constexpr (CNT) st_br++;
+            if (pn == 0) {
+              // a leaf: R u {v} is maximal iff X n N(v) is empty
+              if ((xn | xxn) == 0) {
+                nemit++;
+                kemit = kc;
+                emit = true;
+                z = sc + (u64)kc * MCE_GOLDEN;
+              }
+              if (fC == 0) {
+                has = false;
+                go = false;
+              }
+            } else {
+              push = fC != 0;
+              pP = fP;
+              pX = fX;
+              pXX = fXX;
+              pC = fC;
+              pS = fS;
+              pK = fK;
+              fP = pn;
+              fX = xn;
+              fXX = xxn;
+              fS = sc;
+              fK = kc;
+              fst = false;
+              pcm = pn | xn;
+              pcx = xxn;
+              pbc = 0;
+              go = false;
+            }
           }
-          if (fC == 0) has = false;
-        } else {
-          push = fC != 0;
-          pP = fP;
-          pX = fX;
-          pXX = fXX;
-          pC = fC;
-          pS = fS;
-          pK = fK;
-          fP = pn;
-          fX = xn;
-          fXX = xxn;
-          fS = sc;
-          fK = kc;
-          fst = false;
+          const u64 qm = ballot(emit);
+          if (qm) {
+            if (emit) s_q[qn + (u32)mbcnt(qm)] = z;
+            qn += (u32)__popcll(qm);
+          }
         }
       }
-      const u64 em = ballot(emit);
+      // a full round of queued cliques: mix one per lane
+      while (qn >= (u32)MCE_WAVE) {
+        qn -= (u32)MCE_WAVE;
+        hacc += mce_mix64(s_q[qn + (u32)lane]);
+      }
+      // clique sizes: one shared counter update for the most common size
+      const u64 em = ballot(nemit != 0);
       if (em) {
         const int kf = read_lane(kemit, __builtin_ctzll(em));
-        const u64 same = ballot(emit && kemit == kf);
-        if (lane == 0) atomicAdd(&s_hist[kf], (u64)__popcll(same));
-        if (emit && kemit != kf) atomicAdd(&s_hist[kemit], 1ull);
+        const bool same = nemit != 0 && kemit == kf;
+        const u32 tot = wave_sum_u32(same ? nemit : 0u);
+        if (lane == 0) atomicAdd(&s_hist[kf], (u64)tot);
+        if (nemit != 0 && !same) atomicAdd(&s_hist[kemit], (u64)nemit);
       }
-      // parents with branches left go on the stack
+      // parents with branches left go on the stack (LDS; its oldest frames spill to HBM)
       const u64 pm = ballot(push);
       if (pm) {
         const u32 np = (u32)__popcll(pm);
-        if (top - bot + np > cap) {   // the stack is sized far beyond any depth x lanes
-          if (lane == 0) {
-            atomicOr(prm.status, MCE_E_LIMIT);
-            st_relaxed(&wl->done, 1u);
+        if (top - mid + np > (u32)MICRO_L) {
+          // move the oldest MCE_WAVE LDS frames to HBM (top - mid > MICRO_L - 64 here)
+          if (mid - bot + (u32)MCE_WAVE > cap) {
+            if (lane == 0) {
+              atomicOr(prm.status, MCE_E_LIMIT);
+              st_relaxed(&wl->done, 1u);
+            }
+            abort = true;
+            break;
           }
-          abort = true;
-          break;
+          const u32 v = mid + (u32)lane;
+          for (int j = 0; j < MF; j++) hstk[(size_t)j * cap + (v & cmask)] = s_stk[j][v & lmask];
+          mid += (u32)MCE_WAVE;
+          __syncthreads();
         }
         if (push) {
-          const u32 slot = (top + (u32)mbcnt(pm)) & cmask;
-          stk[0 * (size_t)cap + slot] = pP;
-          stk[1 * (size_t)cap + slot] = pX;
-          stk[2 * (size_t)cap + slot] = pXX;
-          stk[3 * (size_t)cap + slot] = pC;
-          stk[4 * (size_t)cap + slot] = pS;
-          stk[5 * (size_t)cap + slot] = (u64)(u32)pK | (1ull << 32);
+          const u32 sl = (top + (u32)mbcnt(pm)) & lmask;
+          s_stk[0][sl] = pP;
+          s_stk[1][sl] = pX;
+          s_stk[2][sl] = pXX;
+          s_stk[3][sl] = pC;
+          s_stk[4][sl] = pS;
+          s_stk[5][sl] = (u64)(u32)pK;
         }
         top += np;
-        max_depth_stack = max(max_depth_stack, top - bot);
+        max_stack = max(max_stack, top - bot);
       }
 
       // 4. branch requests: frames from the bottom of the stack
@@ -302,20 +403,29 @@ __global__ __launch_bounds__(64) void k_search_micro(MicroParams prm) {
           // half the stack (rounded up, at most MICRO_DON frames) if the frames
           // hold at least donate_min_p candidate vertices together
           u32 give = min((top - bot + 1u) / 2u, (u32)MICRO_DON);
-          const u64 gp = (u32)lane < give ? stk[0 * (size_t)cap + ((bot + (u32)lane) & cmask)] : 0ull;
-          if (give && wave_sum_u32((u32)__popcll(gp)) < (u32)prm.donate_min_p) give = 0;
+          const u32 inh = mid - bot;   // frames in HBM
+          const u32 v = bot + (u32)lane;
+          u64 g[MF] = {0, 0, 0, 0, 0, 0};
+          if ((u32)lane < give) {
+            if ((u32)lane < inh) {
+              for (int j = 0; j < MF; j++) g[j] = hstk[(size_t)j * cap + (v & cmask)];
+            } else {
+              for (int j = 0; j < MF; j++) g[j] = s_stk[j][v & lmask];
+            }
+          }
+          if (give && wave_sum_u32((u32)__popcll(g[0])) < (u32)prm.donate_min_p) give = 0;
           if (give) {
             u64* dm = prm.mail + (size_t)rcv * prm.mail_words;
             u64* df = dm + 2;
             if ((u32)lane < give) {
-              const u32 slot = (bot + (u32)lane) & cmask;
-              for (int j = 0; j < MF; j++) st_relaxed64(&df[j * MICRO_DON + lane], stk[(size_t)j * cap + slot]);
+              for (int j = 0; j < MF; j++) st_relaxed64(&df[j * MICRO_DON + lane], g[j]);
             }
             if (lane == 0) {
               st_relaxed64(&dm[0], toff);
               st_relaxed64(&dm[1], (u64)give);
             }
             bot += give;
+            if (give > inh) mid = bot;
             wl_give(wl, wid, rcv);
             st_don++;
           } else {
@@ -324,14 +434,16 @@ __global__ __launch_bounds__(64) void k_search_micro(MicroParams prm) {
         }
       }
       // Stack slots pass between lanes of this wave from step to step: the
-      // vector memory operations of one wave are coherent with each other, and
-      // this keeps the compiler from moving them across steps.
+      // vector memory and LDS operations of one wave are performed in order,
+      // and this keeps the compiler from moving them across steps.
       __atomic_signal_fence(__ATOMIC_SEQ_CST);
     }
+    t_last = wall_clock64();
     if (abort) break;
   }
 
   // ---------------------------------------------------------- flush
+  if ((u32)lane < qn) hacc += mce_mix64(s_q[lane]);
   const u64 t_end = wall_clock64();
   const u64 hsum = wave_sum_u64(hacc);
   __syncthreads();
@@ -344,6 +456,7 @@ __global__ __launch_bounds__(64) void k_search_micro(MicroParams prm) {
   const u64 leaves = wave_sum_u64(mine);
   if (!abort && lane == 0 && hsum) atomicAdd(prm.g_hash, hsum);
   const u64 prow = CNT ? wave_sum_u64(st_prow) : 0ull;
+  const u64 nbr = CNT ? wave_sum_u64(st_br) : 0ull;
   if (lane == 0) {
     u64* st = prm.stats + (size_t)wid * MCE_NSTAT;
     const u64 total = t_end - t_start;
@@ -353,15 +466,17 @@ __global__ __launch_bounds__(64) void k_search_micro(MicroParams prm) {
     st[ST_PIVOT_ROWS] = prow;
     st[ST_PIVOT_WORDS] = prow;
     st[ST_XX_TESTS] = 0;
-    st[ST_BRANCHES] = st_br;
+    st[ST_BRANCHES] = nbr;
     st[ST_BUSY_TICKS] = total - idle_ticks;
     st[ST_ROOTS] = st_roots;
     st[ST_RECEIVED] = st_recv;
     st[ST_TOTAL_TICKS] = total;
     st[ST_START_ABS] = t_start;
-    st[ST_STACK_MAX] = max_depth_stack;
+    st[ST_STACK_MAX] = max_stack;
     st[ST_STEPS] = st_steps;
     st[ST_LANE_STEPS] = st_lanes;
+    st[ST_FIRST_ABS] = t_first;
+    st[ST_LAST_ABS] = t_last;
   }
 }
 

@@ -167,6 +167,7 @@ __global__ __launch_bounds__(64) void k_search(SearchParams prm) {
   u64 hacc = 0;
   u64 st_nodes = 0, st_leaves = 0, st_don = 0, st_prow = 0, st_xx = 0, st_roots = 0, st_recv = 0, st_br = 0;
   u64 idle_ticks = 0;
+  u64 t_first = 0, t_last = 0;
   bool phase2 = false;
   bool req_closed = true;   // the request word starts closed and is closed again by wl_idle
   bool abort = false;
@@ -246,6 +247,7 @@ __global__ __launch_bounds__(64) void k_search(SearchParams prm) {
       wl_open(wl, wid);
       req_closed = false;
     }
+    if (t_first == 0) t_first = wall_clock64();
     u32 rq_next = 0;   // request word, read at one node and acted on at the next
 
     // ---------------------------------------------------------- depth-first search
@@ -488,6 +490,7 @@ __global__ __launch_bounds__(64) void k_search(SearchParams prm) {
       lpx = lpx_child;
       need_pivot = true;
     }
+    t_last = wall_clock64();
     if (abort) break;
   }
 
@@ -514,6 +517,9 @@ __global__ __launch_bounds__(64) void k_search(SearchParams prm) {
     st[ST_ROOTS] = st_roots;
     st[ST_RECEIVED] = st_recv;
     st[ST_TOTAL_TICKS] = t_end - t_start;
+    st[ST_START_ABS] = t_start;
+    st[ST_FIRST_ABS] = t_first;
+    st[ST_LAST_ABS] = t_last;
   }
 }
 
@@ -564,6 +570,7 @@ __global__ __launch_bounds__(64) void k_search_w1(SearchParams prm) {
   u32 nodes = 0;       // since the last fold into s_misc[3]
   u32 st_don = 0, st_roots = 0, st_recv = 0, st_checks = 0;
   u64 st_prow = 0, st_xx = 0, st_br = 0;   // CNT only
+  u64 t_last = 0;
   bool phase2 = false;
   bool req_closed = true;   // the request word starts closed and is closed again by wl_idle
   bool abort = false;
@@ -867,6 +874,7 @@ __global__ __launch_bounds__(64) void k_search_w1(SearchParams prm) {
       lpx = lpx_child;
       need_pivot = true;
     }
+    t_last = wall_clock64();
     if (abort) break;
   }
 
@@ -901,6 +909,8 @@ __global__ __launch_bounds__(64) void k_search_w1(SearchParams prm) {
     st[ST_SETUP_TICKS] = s_misc[5];
     st[ST_FIRST_TICKS] = s_misc[6] ? s_misc[6] - s_misc[0] : total;
     st[ST_START_ABS] = s_misc[0];
+    st[ST_FIRST_ABS] = s_misc[6];
+    st[ST_LAST_ABS] = t_last;
     st[ST_CHECKS] = st_checks;
     st[ST_DONATE_OK_TICKS] = s_misc[7];
   }

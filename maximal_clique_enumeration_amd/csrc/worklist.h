@@ -172,8 +172,8 @@ __device__ int wl_idle(MceWl* wl, int wid, int nworkers, u64 deadline, u32* stat
         // nobody open, or the wave asked is busy with another request: back off
         ++fails;
         if (fails < 16) __builtin_amdgcn_s_sleep(2);
-        else if (fails < 64) __builtin_amdgcn_s_sleep(16);
-        else __builtin_amdgcn_s_sleep(64);
+        else if (fails < 64) __builtin_amdgcn_s_sleep(8);
+        else __builtin_amdgcn_s_sleep(16);
       }
     }
   }
