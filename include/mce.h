@@ -144,6 +144,8 @@ typedef struct {
   uint64_t steps;            /* micro kernel: wavefront steps (each lane holding a frame takes one
                                 node or branch) */
   uint64_t lane_steps;       /* micro kernel: lanes holding a frame, summed over steps */
+  uint64_t peel_ticks[4];    /* k-core peel, as seen by its first block: barrier waits, level
+                                passes, round work, total */
 } mce_run_stats;
 
 /* Fills cfg with the defaults: device -1, worker_list 1, donate_min_p 10,

@@ -84,7 +84,8 @@ class mce_run_stats(ctypes.Structure):
                 ("micro_roots", ctypes.c_int32),
                 ("pad2_", ctypes.c_int32),
                 ("steps", ctypes.c_uint64),
-                ("lane_steps", ctypes.c_uint64)]
+                ("lane_steps", ctypes.c_uint64),
+                ("peel_ticks", ctypes.c_uint64 * 4)]
 
 
 _lib = None
@@ -314,4 +315,6 @@ class Engine:
         st = mce_run_stats()
         st.struct_size = ctypes.sizeof(mce_run_stats)
         self._check(mce_stats(self._h, st), "mce_stats", self._h)
-        return {name: getattr(st, name) for name, _ in mce_run_stats._fields_ if name not in ("pad_", "pad2_")}
+        out = {name: getattr(st, name) for name, _ in mce_run_stats._fields_ if name not in ("pad_", "pad2_")}
+        out["peel_ticks"] = list(out["peel_ticks"])
+        return out

@@ -39,7 +39,7 @@ struct mce_engine {
   int peel_blocks_max = 1;
   std::string err;
 
-  DevBuf ctl, deg, rnd, core, alive0, alive1, front0, front1, pcount, xcount, lists, taboff, heap, results, wl,
+  DevBuf ctl, deg, rnd, core, alive0, alive1, front0, front1, bfront0, bfront1, pcount, xcount, lists, taboff, heap, results, wl,
       slots, stats, mstack, mail;
   HostPinned host;    // staging for device -> host copies
   hipEvent_t ev[4 + 4 * MCE_NSUB] = {};
@@ -149,6 +149,7 @@ mce_status run_impl(mce_engine* e, int32_t n, int64_t nnz, const int32_t* row_pt
       (h = ensure(e->rnd, nb)) != hipSuccess || (h = ensure(e->core, nb)) != hipSuccess ||
       (h = ensure(e->alive0, nb)) != hipSuccess || (h = ensure(e->alive1, nb)) != hipSuccess ||
       (h = ensure(e->front0, nb)) != hipSuccess || (h = ensure(e->front1, nb)) != hipSuccess ||
+      (h = ensure(e->bfront0, nb)) != hipSuccess || (h = ensure(e->bfront1, nb)) != hipSuccess ||
       (h = ensure(e->pcount, (size_t)std::max(cnt, 1) * sizeof(int))) != hipSuccess ||
       (h = ensure(e->xcount, (size_t)std::max(cnt, 1) * sizeof(int))) != hipSuccess ||
       (h = ensure(e->lists, (size_t)std::max(cnt, 1) * sizeof(int))) != hipSuccess ||
@@ -171,10 +172,10 @@ mce_status run_impl(mce_engine* e, int32_t n, int64_t nnz, const int32_t* row_pt
   }
   if (timing) (void)hipEventRecord(e->ev[1], s);
   // the peel: one block for small graphs (no grid barrier traffic), else a full grid
-  int pblocks = n <= 16384 ? 1 : std::min(e->peel_blocks_max, (n + 255) / 256);
+  int pblocks = n <= 16384 ? 1 : std::min(e->peel_blocks_max, (n + 1023) / 1024);
   if ((h = mce_launch_peel(n, row_ptr, col_idx, dp<int>(e->deg), dp<int>(e->rnd), dp<int>(e->core),
                            dp<int>(e->alive0), dp<int>(e->alive1), dp<int>(e->front0), dp<int>(e->front1),
-                           ctl, budget, pblocks, s)) != hipSuccess)
+                           dp<int>(e->bfront0), dp<int>(e->bfront1), ctl, budget, pblocks, s)) != hipSuccess)
     return hip_fail(e, h, "peel launch");
   if (timing) (void)hipEventRecord(e->ev[2], s);
   if ((h = mce_launch_orient(n, row_ptr, col_idx, dp<int>(e->rnd), subset ? roots : nullptr, cnt,
@@ -458,6 +459,7 @@ mce_status run_impl(mce_engine* e, int32_t n, int64_t nnz, const int32_t* row_pt
   so.claim_checks = stat_sum[ST_CHECKS];
   so.donate_ok_ticks = stat_sum[ST_DONATE_OK_TICKS];
   so.max_stack_frames = max_stack;
+  for (int i = 0; i < 4; i++) so.peel_ticks[i] = hctl->peel_ticks[i];
   so.steps = stat_sum[ST_STEPS];
   so.lane_steps = stat_sum[ST_LANE_STEPS];
   so.micro_roots = counts[MCE_SUB_MICRO];
@@ -637,7 +639,7 @@ void mce_destroy(mce_engine* e) {
   if (!e) return;
   (void)hipSetDevice(e->device);
   DevBuf* bufs[] = {&e->ctl,    &e->deg,   &e->rnd,    &e->core,    &e->alive0, &e->alive1,
-                    &e->front0, &e->front1, &e->pcount, &e->xcount, &e->lists,  &e->taboff,
+                    &e->front0, &e->front1, &e->bfront0, &e->bfront1, &e->pcount, &e->xcount, &e->lists,  &e->taboff,
                     &e->heap,   &e->results, &e->wl,    &e->slots,  &e->stats,  &e->mstack, &e->mail};
   for (DevBuf* b : bufs) release(*b);
   if (e->host.p) (void)hipHostFree(e->host.p);

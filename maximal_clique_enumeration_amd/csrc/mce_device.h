@@ -106,9 +106,10 @@ struct MceCtl {
   u64 heap_top[MCE_NSUB];   // build: bump allocator of each sub-class's heap
   int asize[2];          // peel: alive-list sizes (ping-pong)
   int fsize[3];          // peel: frontier sizes (rotating: read, filled, being reset)
-  u32 bar_count;         // grid barrier
-  u32 bar_gen;
+  int bsize[3];          // peel: big-vertex frontier sizes (same rotation)
+  u32 bar_count;         // grid barrier: arrivals so far in the launch
   u64 t_run;             // wall-clock tick at the start of the peel: the run's time limit counts from it
+  u64 peel_ticks[4];     // block 0 of the peel: barrier waits, level passes, round work, total
 };
 
 // Worker-list state of one search launch (section 3.3 of the pages). Each

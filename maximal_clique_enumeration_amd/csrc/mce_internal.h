@@ -116,8 +116,8 @@ struct BuildParams {
 hipError_t mce_launch_validate(int n, long long nnz, const int* rp, const int* ci, MceCtl* ctl, int blocks,
                                hipStream_t s);
 hipError_t mce_launch_peel(int n, const int* rp, const int* ci, int* deg, int* rnd, int* core, int* alive0,
-                           int* alive1, int* front0, int* front1, MceCtl* ctl, u64 budget, int blocks,
-                           hipStream_t s);
+                           int* alive1, int* front0, int* front1, int* bfront0, int* bfront1, MceCtl* ctl,
+                           u64 budget, int blocks, hipStream_t s);
 int mce_peel_max_blocks(int num_cu);
 // roots == NULL: the roots are 0 .. nroots-1
 hipError_t mce_launch_orient(int n, const int* rp, const int* ci, const int* rnd, const int* roots, int nroots,

@@ -65,29 +65,26 @@ __global__ __launch_bounds__(256) void k_validate_cols(int n, const int* __restr
 // Everything the peel passes between blocks is read and written with
 // agent-scope relaxed atomics, which are performed at the device coherence
 // point; the barrier only has to order them: each block waits until its own
-// memory operations completed, then arrives, and the last arrival opens the next
-// generation. Bounded: past the deadline it flags MCE_E_TIMEOUT and lets the
-// block go; the caller checks the flag after every barrier.
-__device__ void grid_sync(MceCtl* ctl, u64 deadline) {
+// memory operations completed, then arrives. The arrival counter only grows
+// (it is zeroed with the control block before the launch): barrier number e of
+// the launch is complete once it reaches e * gridDim.x, so no block has to
+// reset it or open a generation, and a block needs one atomic add and its
+// polls. Bounded: past the deadline it flags MCE_E_TIMEOUT and lets the block
+// go; the caller checks the flag after every barrier.
+__device__ void grid_sync(MceCtl* ctl, u64 deadline, u32& epoch, bool solo = false) {
   wait_stores_complete();
   __syncthreads();
-  if (gridDim.x > 1) {
+  if (gridDim.x > 1 && !solo) {
     if (threadIdx.x == 0) {
-      const u32 gen = ld_relaxed(&ctl->bar_gen);
-      wait_stores_complete();   // the generation is read before this block arrives
-      const u32 arrived = __hip_atomic_fetch_add(&ctl->bar_count, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1;
-      if (arrived == gridDim.x) {
-        st_relaxed(&ctl->bar_count, 0u);
-        wait_stores_complete();
-        st_relaxed(&ctl->bar_gen, gen + 1);
-      } else {
-        u32 spins = 0;
-        while (ld_relaxed(&ctl->bar_gen) == gen) {
-          __builtin_amdgcn_s_sleep(1);
-          if ((++spins & 1023u) == 0 && past_deadline(deadline)) {
-            atomicOr(&ctl->status, MCE_E_TIMEOUT);
-            break;
-          }
+      epoch++;
+      const u32 target = epoch * gridDim.x;
+      __hip_atomic_fetch_add(&ctl->bar_count, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      u32 spins = 0;
+      while (ld_relaxed(&ctl->bar_count) < target) {
+        __builtin_amdgcn_s_sleep(1);
+        if ((++spins & 1023u) == 0 && past_deadline(deadline)) {
+          atomicOr(&ctl->status, MCE_E_TIMEOUT);
+          break;
         }
       }
     }
@@ -95,145 +92,316 @@ __device__ void grid_sync(MceCtl* ctl, u64 deadline) {
   }
 }
 
-__device__ __forceinline__ int ldi(const int* p) { return ld_relaxed(p); }
-__device__ __forceinline__ void sti(int* p, int v) { st_relaxed_i(p, v); }
+// Peel memory operations at a chosen scope: agent scope while the whole grid
+// works (the blocks sit on different XCDs, whose L2s are not coherent with each
+// other), workgroup scope once block 0 works alone (its XCD's L2 is then the
+// only cache that matters, and an operation is an L2 round trip instead of one
+// to the device coherence point).
+#define SA __HIP_MEMORY_SCOPE_AGENT
+#define SW __HIP_MEMORY_SCOPE_WORKGROUP
+template <int S>
+__device__ __forceinline__ int pld(const int* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, S);
+}
+template <int S>
+__device__ __forceinline__ void pst(int* p, int v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, S);
+}
+template <int S>
+__device__ __forceinline__ int padd(int* p, int v) {
+  return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, S);
+}
+template <int S>
+__device__ __forceinline__ void pmin(int* p, int v) {
+  __hip_atomic_fetch_min(p, v, __ATOMIC_RELAXED, S);
+}
+
+// Vertices whose CSR row is longer than PEEL_BIG join the big frontier, whose
+// rows are split into PEEL_SPAN-edge spans shared by all waves of the round.
+#ifndef PEEL_BIG
+#define PEEL_BIG 512
+#endif
+#define PEEL_SPAN (4 * MCE_WAVE)
+#ifndef PEEL_SOLO
+#define PEEL_SOLO 4096
+#endif
+#define PEEL_THREADS 1024
+
+// Appends the lanes with `in` set to the next frontier: the regular list, or
+// the big list for vertices of degree > PEEL_BIG. Whole wave.
+template <int S>
+__device__ __forceinline__ void peel_append(bool in, int v, const int* __restrict__ rp, int* fr, int* fsize,
+                                            int* bfr, int* bsize) {
+  const int lane = lane_id();
+  const bool big = in && rp[v + 1] - rp[v] > PEEL_BIG;
+  const u64 mr = ballot(in && !big);
+  const u64 mb = ballot(big);
+  int pr = 0, pb = 0;
+  if (lane == 0 && mr) pr = padd<S>(fsize, __popcll(mr));
+  if (lane == 0 && mb) pb = padd<S>(bsize, __popcll(mb));
+  pr = read_lane(pr, 0);
+  pb = read_lane(pb, 0);
+  if (in && !big) pst<S>(&fr[pr + mbcnt(mr)], v);
+  if (big) pst<S>(&bfr[pb + mbcnt(mb)], v);
+}
+
+// One span of a removed vertex's row [base, min(base + PEEL_SPAN, b)): take one
+// degree from each neighbour (all four 64-edge pieces in flight together). A
+// neighbour that falls from k + 1 to k joins the next round. The decrement is
+// unconditional: a vertex already removed has degree <= k at its removal and
+// only loses more, so it never falls from k + 1 again; its degree is not read.
+template <int S>
+__device__ __forceinline__ void peel_span(int base, int b, int k, const int* __restrict__ rp,
+                                          const int* __restrict__ ci, int* deg, int* nx, int* nxs, int* bnx,
+                                          int* bnxs) {
+  const int lane = lane_id();
+  int u[4];
+  bool ok[4];
+#pragma unroll
+  for (int q = 0; q < 4; q++) {
+    const int e = base + q * MCE_WAVE + lane;
+    ok[q] = e < b;
+    u[q] = ok[q] ? ci[e] : 0;
+  }
+  bool joins[4];
+#pragma unroll
+  for (int q = 0; q < 4; q++) joins[q] = ok[q] && padd<S>(&deg[u[q]], -1) == k + 1;
+#pragma unroll
+  for (int q = 0; q < 4; q++) {
+    if (ballot(joins[q])) peel_append<S>(joins[q], u[q], rp, nx, nxs, bnx, bnxs);
+  }
+}
+
+struct PeelArgs {
+  int n;
+  const int* rp;
+  const int* ci;
+  int* deg;
+  int* rnd;
+  int* core;
+  int* alive0;
+  int* alive1;
+  int* front0;
+  int* front1;
+  int* bfront0;
+  int* bfront1;
+  MceCtl* ctl;
+  u64 deadline;
+  // ping-pong buffers by parity (selects, not indexed arrays: no scratch memory)
+  __device__ int* alive(int i) const { return (i & 1) ? alive1 : alive0; }
+  __device__ int* front(int i) const { return (i & 1) ? front1 : front0; }
+  __device__ int* bfront(int i) const { return (i & 1) ? bfront1 : bfront0; }
+};
+
+struct PeelState {
+  int cur, nf, nb, k, r, na;
+  bool level_known;     // the level's remaining list and k are known, its first round is not built
+  u32 epoch;            // grid barriers passed (thread 0 of each block)
+  u64 tb, tl, tr, tm;   // first block's thread 0: barrier, level, round ticks; last mark
+};
+
+#define PEEL_MARK(acc)                \
+  if (timer) {                        \
+    const u64 t = wall_clock64();     \
+    st.acc += t - st.tm;              \
+    st.tm = t;                        \
+  }
+
+// Rounds of the peel at scope S (see k_peel). `wave`/`nwaves` index the waves
+// taking part. Returns 0 when every vertex is ordered, 1 when the remaining
+// list has shrunk to PEEL_SOLO vertices or fewer (grid phase only), -1 on a
+// time-out.
+template <int S, bool SOLO>
+__device__ int peel_rounds(const PeelArgs& A, PeelState& st, int wave, int nwaves, bool timer) {
+  const int lane = lane_id();
+  const bool lead = SOLO ? threadIdx.x == 0 : (blockIdx.x == 0 && threadIdx.x == 0);
+  MceCtl* ctl = A.ctl;
+  const int* rp = A.rp;
+  for (;;) {
+    if (st.nf == 0 && st.nb == 0) {
+      if (!st.level_known) {
+      // new level: compact the remaining list and find the smallest remaining degree
+      const int* src = A.alive(st.cur);
+      int* dst = A.alive(st.cur ^ 1);
+      int mn = 0x7FFFFFFF;
+      for (int base = wave * MCE_WAVE; base < st.na; base += nwaves * MCE_WAVE) {
+        const int i = base + lane;
+        bool keep = false;
+        int v = 0;
+        if (i < st.na) {
+          v = pld<S>(&src[i]);
+          keep = pld<S>(&A.rnd[v]) < 0;
+          if (keep) mn = min(mn, pld<S>(&A.deg[v]));
+        }
+        const u64 m = ballot(keep);
+        int pos = 0;
+        if (lane == 0 && m) pos = padd<S>(&ctl->asize[st.cur ^ 1], __popcll(m));
+        pos = read_lane(pos, 0);
+        if (keep) pst<S>(&dst[pos + mbcnt(m)], v);
+      }
+      const int wmn = wave_min_i32_nonneg(mn);
+      if (lane == 0 && wmn != 0x7FFFFFFF) pmin<S>(&ctl->min_deg, wmn);
+      PEEL_MARK(tl);
+      grid_sync(ctl, A.deadline, st.epoch, SOLO);
+      PEEL_MARK(tb);
+      st.cur ^= 1;
+      const u32 status = ld_relaxed(&ctl->status);
+      st.na = pld<S>(&ctl->asize[st.cur]);
+      const int kmin = pld<S>(&ctl->min_deg);   // no remaining vertex: k stays the degeneracy
+      if (status & MCE_E_TIMEOUT) return -1;
+      if (st.na == 0) return 0;
+      st.k = kmin;
+      if (!SOLO && gridDim.x > 1 && st.na <= PEEL_SOLO) {
+        st.level_known = true;
+        return 1;
+      }
+      }
+      st.level_known = false;
+      // the level's first round: every remaining vertex of degree <= k
+      const int* al = A.alive(st.cur);
+      for (int base = wave * MCE_WAVE; base < st.na; base += nwaves * MCE_WAVE) {
+        const int i = base + lane;
+        bool in = false;
+        int v = 0;
+        if (i < st.na) {
+          v = pld<S>(&al[i]);
+          in = pld<S>(&A.deg[v]) <= st.k;
+        }
+        peel_append<S>(in, v, rp, A.front(st.r), &ctl->fsize[st.r % 3], A.bfront(st.r),
+                       &ctl->bsize[st.r % 3]);
+      }
+      PEEL_MARK(tl);
+      grid_sync(ctl, A.deadline, st.epoch, SOLO);
+      PEEL_MARK(tb);
+      const u32 status2 = ld_relaxed(&ctl->status);
+      st.nf = pld<S>(&ctl->fsize[st.r % 3]);
+      st.nb = pld<S>(&ctl->bsize[st.r % 3]);
+      if (status2 & MCE_E_TIMEOUT) return -1;
+    }
+    // round r: remove the frontier, take one degree from each neighbour
+    const int r = st.r, k = st.k;
+    if (lead) {
+      // counters nobody reads any more: the frontier sizes read two rounds ago,
+      // the old remaining-list size and the level's minimum
+      pst<S>(&ctl->fsize[(r + 2) % 3], 0);
+      pst<S>(&ctl->bsize[(r + 2) % 3], 0);
+      pst<S>(&ctl->asize[st.cur ^ 1], 0);
+      pst<S>(&ctl->min_deg, 0x7FFFFFFF);
+    }
+    const int* fr = A.front(r);
+    const int* bfr = A.bfront(r);
+    int* nx = A.front(r + 1);
+    int* nxs = &ctl->fsize[(r + 1) % 3];
+    int* bnx = A.bfront(r + 1);
+    int* bnxs = &ctl->bsize[(r + 1) % 3];
+    // vertices of small degree: one wave each
+    for (int i = wave; i < st.nf; i += nwaves) {
+      const int v = pld<S>(&fr[i]);
+      if (lane == 0) {
+        pst<S>(&A.rnd[v], r);
+        A.core[v] = k;
+      }
+      const int a = rp[v], b = rp[v + 1];
+      for (int base = a; base < b; base += PEEL_SPAN) peel_span<S>(base, b, k, rp, A.ci, A.deg, nx, nxs, bnx, bnxs);
+    }
+    // vertices of large degree: their spans are dealt round-robin to all waves
+    for (int j0 = 0; j0 < st.nb; j0 += MCE_WAVE) {
+      const int jl = j0 + lane;
+      const int vl = jl < st.nb ? pld<S>(&bfr[jl]) : 0;
+      const int al = jl < st.nb ? rp[vl] : 0;
+      const int bl = jl < st.nb ? rp[vl + 1] : 0;
+      const int cnt = min(MCE_WAVE, st.nb - j0);
+      for (int t = 0; t < cnt; t++) {
+        const int j = j0 + t;
+        const int v = read_lane(vl, t);
+        const int a = read_lane(al, t);
+        const int b = read_lane(bl, t);
+        if (j % nwaves == wave && lane == 0) {
+          pst<S>(&A.rnd[v], r);
+          A.core[v] = k;
+        }
+        const int nsp = (b - a + PEEL_SPAN - 1) / PEEL_SPAN;
+        for (int c = (wave - j % nwaves + nwaves) % nwaves; c < nsp; c += nwaves)
+          peel_span<S>(a + c * PEEL_SPAN, b, k, rp, A.ci, A.deg, nx, nxs, bnx, bnxs);
+      }
+    }
+    PEEL_MARK(tr);
+    grid_sync(ctl, A.deadline, st.epoch, SOLO);
+    PEEL_MARK(tb);
+    const u32 status = ld_relaxed(&ctl->status);
+    st.nf = pld<S>(nxs);
+    st.nb = pld<S>(bnxs);
+    st.r++;
+    if (status & MCE_E_TIMEOUT) return -1;
+  }
+}
 
 // Round-synchronous peel (section 2.4 asks for a degeneracy order; this is the
 // one the engine uses). Level k: every remaining vertex of current degree <= k
-// leaves in one round (rnd = round, core = k). The removed vertices' remaining
+// leaves in one round (rnd = round, core = k). The removed vertices'
 // neighbours lose one degree each, and a neighbour whose degree falls from k+1
 // to k joins the next round of the same level; when a round removes nothing, k
 // becomes the smallest remaining degree. Marking the round's vertices and
 // decrementing their neighbours happen in the same phase: a vertex of the
 // current round already has degree <= k, so a decrement can never make it join
 // again (that needs a fall from k+1). One grid barrier per round. Launched
-// cooperatively; one block for small graphs.
-__global__ __launch_bounds__(256) void k_peel(int n, const int* __restrict__ rp, const int* __restrict__ ci,
-                                               int* deg, int* rnd, int* core, int* alive0, int* alive1,
-                                               int* front0, int* front1, MceCtl* ctl, u64 budget) {
+// cooperatively; one block for small graphs. Late rounds are small (the
+// remaining graph is the dense core), so once at most PEEL_SOLO vertices remain
+// block 0 finishes alone at workgroup scope and the other blocks leave.
+__global__ __launch_bounds__(PEEL_THREADS) void k_peel(int n, const int* __restrict__ rp,
+                                                        const int* __restrict__ ci, int* deg, int* rnd, int* core,
+                                                        int* alive0, int* alive1, int* front0, int* front1,
+                                                        int* bfront0, int* bfront1, MceCtl* ctl, u64 budget) {
   if (ld_relaxed(&ctl->status) != 0) return;   // rejected input: nothing to order
   const u64 t0 = wall_clock64();
-  const u64 deadline = t0 + budget;
+  PeelArgs A{n, rp, ci, deg, rnd, core, alive0, alive1, front0, front1, bfront0, bfront1, ctl, t0 + budget};
   const int gtid = blockIdx.x * blockDim.x + threadIdx.x;
   const int gsize = gridDim.x * blockDim.x;
-  const int lane = lane_id();
-  const int wave = gtid / MCE_WAVE;
-  const int nwaves = gsize / MCE_WAVE;
-  int* alive[2] = {alive0, alive1};
-  int* front[2] = {front0, front1};
+  const bool timer = blockIdx.x == 0 && threadIdx.x == 0;
+  PeelState st{0, 0, 0, 0, 0, n, false, 0u, 0, 0, 0, t0};
 
   for (int v = gtid; v < n; v += gsize) {
-    sti(&deg[v], rp[v + 1] - rp[v]);
-    sti(&rnd[v], -1);
-    sti(&alive0[v], v);
+    pst<SA>(&deg[v], rp[v + 1] - rp[v]);
+    pst<SA>(&rnd[v], -1);
+    pst<SA>(&alive0[v], v);
   }
   if (gtid == 0) {
     st_relaxed64(&ctl->t_run, t0);
-    sti(&ctl->asize[0], n);
-    sti(&ctl->asize[1], 0);
-    sti(&ctl->fsize[0], 0);
-    sti(&ctl->fsize[1], 0);
-    sti(&ctl->fsize[2], 0);
-    sti(&ctl->min_deg, 0x7FFFFFFF);
+    pst<SA>(&ctl->asize[0], n);
+    pst<SA>(&ctl->asize[1], 0);
+    for (int i = 0; i < 3; i++) {
+      pst<SA>(&ctl->fsize[i], 0);
+      pst<SA>(&ctl->bsize[i], 0);
+    }
+    pst<SA>(&ctl->min_deg, 0x7FFFFFFF);
   }
-  grid_sync(ctl, deadline);
+  grid_sync(ctl, A.deadline, st.epoch);
 
-  int cur = 0, nf = 0, k = 0, r = 0;
-  int na = n;
-  for (;;) {
-    if (ld_relaxed(&ctl->status) & MCE_E_TIMEOUT) return;
-    if (nf == 0) {
-      // new level: compact the remaining list and find the smallest remaining degree
-      const int* src = alive[cur];
-      int* dst = alive[cur ^ 1];
-      int mn = 0x7FFFFFFF;
-      for (int base = wave * MCE_WAVE; base < na; base += nwaves * MCE_WAVE) {
-        const int i = base + lane;
-        bool keep = false;
-        int v = 0;
-        if (i < na) {
-          v = ldi(&src[i]);
-          keep = ldi(&rnd[v]) < 0;
-          if (keep) mn = min(mn, ldi(&deg[v]));
-        }
-        const u64 m = ballot(keep);
-        int pos = 0;
-        if (lane == 0 && m) pos = atomicAdd(&ctl->asize[cur ^ 1], __popcll(m));
-        pos = read_lane(pos, 0);
-        if (keep) sti(&dst[pos + mbcnt(m)], v);
-      }
-      const int wmn = wave_min_i32_nonneg(mn);
-      if (lane == 0 && wmn != 0x7FFFFFFF) atomicMin(&ctl->min_deg, wmn);
-      grid_sync(ctl, deadline);
-      if (ld_relaxed(&ctl->status) & MCE_E_TIMEOUT) return;
-      cur ^= 1;
-      na = ldi(&ctl->asize[cur]);
-      if (na == 0) break;
-      k = ldi(&ctl->min_deg);
-      // the level's first round: every remaining vertex of degree <= k
-      const int* al = alive[cur];
-      int* fr = front[r & 1];
-      for (int base = wave * MCE_WAVE; base < na; base += nwaves * MCE_WAVE) {
-        const int i = base + lane;
-        bool in = false;
-        int v = 0;
-        if (i < na) {
-          v = ldi(&al[i]);
-          in = ldi(&deg[v]) <= k;
-        }
-        const u64 m = ballot(in);
-        int pos = 0;
-        if (lane == 0 && m) pos = atomicAdd(&ctl->fsize[r % 3], __popcll(m));
-        pos = read_lane(pos, 0);
-        if (in) sti(&fr[pos + mbcnt(m)], v);
-      }
-      grid_sync(ctl, deadline);
-      if (ld_relaxed(&ctl->status) & MCE_E_TIMEOUT) return;
-      nf = ldi(&ctl->fsize[r % 3]);
+  int res;
+  if (gridDim.x > 1) {
+    res = peel_rounds<SA, false>(A, st, gtid / MCE_WAVE, gsize / MCE_WAVE, timer);
+    if (res == 1) {
+      if (blockIdx.x != 0) return;
+      // block 0 goes on alone: drop any stale copy its XCD's caches may hold
+      // of what the other blocks wrote
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+      res = peel_rounds<SW, true>(A, st, threadIdx.x / MCE_WAVE, blockDim.x / MCE_WAVE, timer);
     }
-    // round r: remove the frontier, take one degree from each remaining neighbour
-    if (gtid == 0) {
-      // counters nobody reads any more: the frontier size read two rounds ago,
-      // the old remaining-list size and the level's minimum
-      sti(&ctl->fsize[(r + 2) % 3], 0);
-      sti(&ctl->asize[cur ^ 1], 0);
-      sti(&ctl->min_deg, 0x7FFFFFFF);
-    }
-    const int* fr = front[r & 1];
-    int* nx = front[(r + 1) & 1];
-    int* nxs = &ctl->fsize[(r + 1) % 3];
-    for (int i = wave; i < nf; i += nwaves) {
-      const int v = ldi(&fr[i]);
-      if (lane == 0) {
-        sti(&rnd[v], r);
-        core[v] = k;
-      }
-      const int a = rp[v], b = rp[v + 1];
-      for (int base = a; base < b; base += MCE_WAVE) {
-        const int e = base + lane;
-        bool joins = false;
-        int u = 0;
-        if (e < b) {
-          u = ci[e];
-          if (ldi(&rnd[u]) < 0) joins = atomicSub(&deg[u], 1) == k + 1;
-        }
-        const u64 m = ballot(joins);
-        int pos = 0;
-        if (lane == 0 && m) pos = atomicAdd(nxs, __popcll(m));
-        pos = read_lane(pos, 0);
-        if (joins) sti(&nx[pos + mbcnt(m)], u);
-      }
-    }
-    grid_sync(ctl, deadline);
-    if (ld_relaxed(&ctl->status) & MCE_E_TIMEOUT) return;
-    nf = ldi(nxs);
-    r++;
+  } else {
+    res = peel_rounds<SW, true>(A, st, threadIdx.x / MCE_WAVE, blockDim.x / MCE_WAVE, timer);
   }
-  if (gtid == 0) {
-    ctl->rounds = r;
-    ctl->degeneracy = k;
+  if (res < 0) return;
+  if (threadIdx.x == 0 && blockIdx.x == 0) {
+    ctl->rounds = st.r;
+    ctl->degeneracy = st.k;
+    ctl->peel_ticks[0] = st.tb;
+    ctl->peel_ticks[1] = st.tl;
+    ctl->peel_ticks[2] = st.tr;
+    ctl->peel_ticks[3] = wall_clock64() - t0;
   }
 }
+#undef PEEL_MARK
+
 
 // ------------------------------------------------------------------ orientation
 // Per root: |P| = later neighbours, |X| = earlier ones. Degree-0 roots are
@@ -364,21 +532,21 @@ hipError_t mce_launch_validate(int n, long long nnz, const int* rp, const int* c
 }
 
 hipError_t mce_launch_peel(int n, const int* rp, const int* ci, int* deg, int* rnd, int* core, int* alive0,
-                           int* alive1, int* front0, int* front1, MceCtl* ctl, u64 budget, int blocks,
-                           hipStream_t s) {
+                           int* alive1, int* front0, int* front1, int* bfront0, int* bfront1, MceCtl* ctl,
+                           u64 budget, int blocks, hipStream_t s) {
   void* args[] = {&n, (void*)&rp, (void*)&ci, &deg, &rnd, &core, &alive0, &alive1,
-                  &front0, &front1, &ctl, &budget};
-  return hipLaunchCooperativeKernel((const void*)k_peel, dim3(blocks), dim3(256), args, 0, s);
+                  &front0, &front1, &bfront0, &bfront1, &ctl, &budget};
+  return hipLaunchCooperativeKernel((const void*)k_peel, dim3(blocks), dim3(PEEL_THREADS), args, 0, s);
 }
 
-// The peel's grid barrier needs every block resident: stay well inside the
-// occupancy limit (two 256-thread blocks per CU keep the streaming passes at
-// full bandwidth).
+// The peel's grid barrier needs every block resident: one block per CU, well
+// inside the occupancy limit.
 int mce_peel_max_blocks(int num_cu) {
   int per_cu = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, (const void*)k_peel, 256, 0) != hipSuccess)
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, (const void*)k_peel, PEEL_THREADS, 0) != hipSuccess ||
+      per_cu < 1)
     return 1;
-  return max(1, min(per_cu, 2) * num_cu);
+  return num_cu;
 }
 
 hipError_t mce_launch_orient(int n, const int* rp, const int* ci, const int* rnd, const int* roots, int nroots,

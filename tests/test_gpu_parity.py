@@ -129,6 +129,7 @@ def test_disjoint_union_and_isolated(eng):
 # ------------------------------------------------------------------ ordering
 @pytest.mark.parametrize("make", [lambda: mi.config_graph(0), lambda: mi.moon_moser(45),
                                   lambda: mi.chung_lu(30000, 15.0, 2.2, None, 9, planted=10),
+                                  lambda: mi.chung_lu(200000, 20.0, 2.3, None, 11, planted=50),
                                   lambda: mi.path(40), lambda: mi.random_small(500, 0.3, 4)])
 def test_ordering_matches_oracle(eng, make):
     g = make()
