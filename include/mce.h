@@ -146,6 +146,11 @@ typedef struct {
   uint64_t lane_steps;       /* micro kernel: lanes holding a frame, summed over steps */
   uint64_t peel_ticks[4];    /* k-core peel, as seen by its first block: barrier waits, level
                                 passes, round work, total */
+  int32_t launch_sub[16];    /* per search launch (up to `launches`): its sub-class (bitset width
+                                class * 2 + HBM staging, or 12 for the micro kernel) */
+  int32_t launch_roots[16];  /* first-level subtrees of the launch */
+  float launch_build_ms[16]; /* its induced-subgraph build, with MCE_FLAG_PHASE_TIMES */
+  float launch_search_ms[16];/* its search, same flag */
 } mce_run_stats;
 
 /* Fills cfg with the defaults: device -1, worker_list 1, donate_min_p 10,

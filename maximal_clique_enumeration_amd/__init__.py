@@ -85,7 +85,11 @@ class mce_run_stats(ctypes.Structure):
                 ("pad2_", ctypes.c_int32),
                 ("steps", ctypes.c_uint64),
                 ("lane_steps", ctypes.c_uint64),
-                ("peel_ticks", ctypes.c_uint64 * 4)]
+                ("peel_ticks", ctypes.c_uint64 * 4),
+                ("launch_sub", ctypes.c_int32 * 16),
+                ("launch_roots", ctypes.c_int32 * 16),
+                ("launch_build_ms", ctypes.c_float * 16),
+                ("launch_search_ms", ctypes.c_float * 16)]
 
 
 _lib = None
@@ -316,5 +320,6 @@ class Engine:
         st.struct_size = ctypes.sizeof(mce_run_stats)
         self._check(mce_stats(self._h, st), "mce_stats", self._h)
         out = {name: getattr(st, name) for name, _ in mce_run_stats._fields_ if name not in ("pad_", "pad2_")}
-        out["peel_ticks"] = list(out["peel_ticks"])
+        for key in ("peel_ticks", "launch_sub", "launch_roots", "launch_build_ms", "launch_search_ms"):
+            out[key] = list(out[key])[: (4 if key == "peel_ticks" else out["launches"])]
         return out

@@ -39,7 +39,7 @@ struct mce_engine {
   int peel_blocks_max = 1;
   std::string err;
 
-  DevBuf ctl, deg, rnd, core, alive0, alive1, front0, front1, bfront0, bfront1, pcount, xcount, lists, taboff, heap, results, wl,
+  DevBuf ctl, deg, rnd, core, alive0, alive1, front0, front1, bfront0, bfront1, pcount, xcount, lists, taboff, scan, heap, results, wl,
       slots, stats, mstack, mail;
   HostPinned host;    // staging for device -> host copies
   hipEvent_t ev[4 + 4 * MCE_NSUB] = {};
@@ -268,6 +268,7 @@ mce_status run_impl(mce_engine* e, int32_t n, int64_t nnz, const int32_t* row_pt
   }
   if (total > 0) {
     if ((h = ensure(e->taboff, (size_t)total * sizeof(u64))) != hipSuccess ||
+        (h = ensure(e->scan, (size_t)mce_scan_temp_words(total) * sizeof(u64))) != hipSuccess ||
         (h = ensure(e->heap, heap_words * sizeof(u64))) != hipSuccess ||
         (h = ensure(e->slots, slot_bytes)) != hipSuccess ||
         (h = ensure(e->stats, (size_t)stat_rows * MCE_NSTAT * sizeof(u64))) != hipSuccess ||
@@ -277,8 +278,12 @@ mce_status run_impl(mce_engine* e, int32_t n, int64_t nnz, const int32_t* row_pt
     if ((h = hipMemsetAsync(e->stats.p, 0, (size_t)stat_rows * MCE_NSTAT * sizeof(u64), s)) != hipSuccess)
       return hip_fail(e, h, "memset");
     if ((h = mce_launch_bucket(subset ? roots : nullptr, cnt, dp<int>(e->pcount), dp<int>(e->xcount), mode,
-                               micro_on ? 1 : 0, off, dp<int>(e->lists), ctl, grid, s)) != hipSuccess)
+                               micro_on ? 1 : 0, off, dp<int>(e->lists), dp<u64>(e->taboff), ctl, grid, s)) !=
+        hipSuccess)
       return hip_fail(e, h, "bucket launch");
+    // table sizes -> heap offsets (every sub-class's launch reuses the heap from its first root's offset)
+    if ((h = mce_launch_scan(dp<u64>(e->taboff), total, dp<u64>(e->scan), s)) != hipSuccess)
+      return hip_fail(e, h, "table offset scan");
   }
   if (timing) (void)hipEventRecord(e->ev[3], s);
 
@@ -299,11 +304,10 @@ mce_status run_impl(mce_engine* e, int32_t n, int64_t nnz, const int32_t* row_pt
     bp.micro = micro ? 1 : 0;
     bp.heap = dp<u64>(e->heap);
     bp.heap_words = heap_words;
-    bp.heap_top = &ctl->heap_top[c];
     bp.tab_off = dp<u64>(e->taboff) + off.off[c];
     bp.status = &ctl->status;
     if (timing) (void)hipEventRecord(e->ev[evi], s);
-    if ((h = mce_launch_build(bp, e->num_cu * 16, s)) != hipSuccess) return hip_fail(e, h, "build launch");
+    if ((h = mce_launch_build(bp, e->num_cu * 32, s)) != hipSuccess) return hip_fail(e, h, "build launch");
     if (timing) (void)hipEventRecord(e->ev[evi + 1], s);
     if ((h = mce_launch_wl_init(dp<MceWl>(e->wl), pl.nw, s)) != hipSuccess) return hip_fail(e, h, "wl init");
     if (micro) {
@@ -459,6 +463,10 @@ mce_status run_impl(mce_engine* e, int32_t n, int64_t nnz, const int32_t* row_pt
   so.claim_checks = stat_sum[ST_CHECKS];
   so.donate_ok_ticks = stat_sum[ST_DONATE_OK_TICKS];
   so.max_stack_frames = max_stack;
+  for (size_t i = 0; i < plan.size() && i < 16; i++) {
+    so.launch_sub[i] = plan[i].sub;
+    so.launch_roots[i] = counts[plan[i].sub];
+  }
   for (int i = 0; i < 4; i++) so.peel_ticks[i] = hctl->peel_ticks[i];
   so.steps = stat_sum[ST_STEPS];
   so.lane_steps = stat_sum[ST_LANE_STEPS];
@@ -478,6 +486,10 @@ mce_status run_impl(mce_engine* e, int32_t n, int64_t nnz, const int32_t* row_pt
       (void)hipEventElapsedTime(&y, e->ev[6 + 4 * i], e->ev[7 + 4 * i]);
       mb += x;
       ms += y;
+      if (i < 16) {
+        so.launch_build_ms[i] = x;
+        so.launch_search_ms[i] = y;
+      }
     }
     so.ms_build = mb;
     so.ms_search = ms;
@@ -639,7 +651,7 @@ void mce_destroy(mce_engine* e) {
   if (!e) return;
   (void)hipSetDevice(e->device);
   DevBuf* bufs[] = {&e->ctl,    &e->deg,   &e->rnd,    &e->core,    &e->alive0, &e->alive1,
-                    &e->front0, &e->front1, &e->bfront0, &e->bfront1, &e->pcount, &e->xcount, &e->lists,  &e->taboff,
+                    &e->front0, &e->front1, &e->bfront0, &e->bfront1, &e->pcount, &e->xcount, &e->lists,  &e->taboff, &e->scan,
                     &e->heap,   &e->results, &e->wl,    &e->slots,  &e->stats,  &e->mstack, &e->mail};
   for (DevBuf* b : bufs) release(*b);
   if (e->host.p) (void)hipHostFree(e->host.p);

@@ -103,7 +103,6 @@ struct MceCtl {
   int sub_maxr[MCE_NVAR][MCE_NSUB];   // largest row count of a table
   u64 sub_words[MCE_NVAR][MCE_NSUB];
   int sub_cursor[MCE_NSUB];
-  u64 heap_top[MCE_NSUB];   // build: bump allocator of each sub-class's heap
   int asize[2];          // peel: alive-list sizes (ping-pong)
   int fsize[3];          // peel: frontier sizes (rotating: read, filled, being reset)
   int bsize[3];          // peel: big-vertex frontier sizes (same rotation)

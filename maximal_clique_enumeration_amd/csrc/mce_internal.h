@@ -57,7 +57,7 @@ struct SearchParams {
   const int* rp;
   const int* ci;
   const u64* heap;       // induced-subgraph tables of this launch's roots
-  const u64* tab_off;    // word offset of each root's table (by list index)
+  const u64* tab_off;    // table offset of each root (by list index), relative to tab_off[0]
   int nroots;
   int nworkers;
   int hcap;
@@ -79,7 +79,7 @@ struct SearchParams {
 // per wavefront in HBM (structure of arrays: word j of slot i at j * cap + i).
 struct MicroParams {
   const u64* heap;
-  const u64* tab_off;
+  const u64* tab_off;    // relative to tab_off[0], as in SearchParams
   int nroots;
   int nworkers;
   u64* stacks;           // nworkers * 6 * stack_cap words
@@ -108,8 +108,8 @@ struct BuildParams {
   int micro;             // micro table: full rows plus the X column of every P member
   u64* heap;
   u64 heap_words;
-  u64* heap_top;         // bump allocator (zeroed before the launch)
-  u64* tab_off;          // out: word offset of each root's table
+  const u64* tab_off;    // each root's table offset, as an exclusive prefix sum of table sizes that
+                         // runs over all sub-classes: offsets relative to tab_off[0]
   u32* status;
 };
 
@@ -122,8 +122,14 @@ int mce_peel_max_blocks(int num_cu);
 // roots == NULL: the roots are 0 .. nroots-1
 hipError_t mce_launch_orient(int n, const int* rp, const int* ci, const int* rnd, const int* roots, int nroots,
                              int* pcount, int* xcount, MceCtl* ctl, int blocks, hipStream_t s);
+// Groups the roots by sub-class into `lists` and writes each one's table size
+// (u64 words) at the same position of `words`.
 hipError_t mce_launch_bucket(const int* roots, int nroots, const int* pcount, const int* xcount, int mode,
-                             int micro, SubOffsets off, int* lists, MceCtl* ctl, int blocks, hipStream_t s);
+                             int micro, SubOffsets off, int* lists, u64* words, MceCtl* ctl, int blocks,
+                             hipStream_t s);
+// In-place exclusive prefix sum of n u64 values; tsum holds mce_scan_temp_words(n) words.
+int mce_scan_temp_words(int n);
+hipError_t mce_launch_scan(u64* a, int n, u64* tsum, hipStream_t s);
 
 hipError_t mce_launch_build(const BuildParams& prm, int blocks, hipStream_t s);
 

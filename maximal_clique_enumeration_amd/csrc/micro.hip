@@ -100,7 +100,7 @@ __global__ __launch_bounds__(64) void k_search_micro(MicroParams prm) {
         phase2 = true;
         continue;
       }
-      toff = uni(prm.tab_off[idx]);
+      toff = uni(prm.tab_off[idx]) - uni(prm.tab_off[0]);
     } else {
       if (!prm.worker_list) break;
       const u64 t0 = wall_clock64();

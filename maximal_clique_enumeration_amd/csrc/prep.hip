@@ -495,7 +495,8 @@ __global__ __launch_bounds__(256) void k_orient(int n, const int* __restrict__ r
 // the chosen mode, starting at off[sub].
 __global__ __launch_bounds__(256) void k_bucket(const int* __restrict__ roots, int nroots,
                                                  const int* __restrict__ pcount, const int* __restrict__ xcount,
-                                                 int mode, int micro, SubOffsets off, int* lists, MceCtl* ctl) {
+                                                 int mode, int micro, SubOffsets off, int* lists, u64* words,
+                                                 MceCtl* ctl) {
   if (ld_relaxed(&ctl->status) != 0) return;
   const int lane = lane_id();
   const int gsize = gridDim.x * blockDim.x;
@@ -514,7 +515,10 @@ __global__ __launch_bounds__(256) void k_bucket(const int* __restrict__ roots, i
       int pos = 0;
       if (lane == 0) pos = atomicAdd(&ctl->sub_cursor[s], __popcll(m));
       pos = read_lane(pos, 0);
-      if (mine) lists[off.off[s] + pos + mbcnt(m)] = roots ? roots[i] : i;
+      if (mine) {
+        lists[off.off[s] + pos + mbcnt(m)] = roots ? roots[i] : i;
+        words[off.off[s] + pos + mbcnt(m)] = mce_sub_table_words(p, x, s, mode);
+      }
     }
   }
 }
@@ -557,9 +561,100 @@ hipError_t mce_launch_orient(int n, const int* rp, const int* ci, const int* rnd
 }
 
 hipError_t mce_launch_bucket(const int* roots, int nroots, const int* pcount, const int* xcount, int mode,
-                             int micro, SubOffsets off, int* lists, MceCtl* ctl, int blocks, hipStream_t s) {
+                             int micro, SubOffsets off, int* lists, u64* words, MceCtl* ctl, int blocks,
+                             hipStream_t s) {
   const int nb = max(1, min(blocks, (nroots + 255) / 256));
   hipLaunchKernelGGL(k_bucket, dim3(nb), dim3(256), 0, s, roots, nroots, pcount, xcount, mode, micro, off, lists,
-                     ctl);
+                     words, ctl);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------------ table offsets
+// In-place exclusive prefix sum of the table sizes (u64), so that every root's
+// table has a fixed heap offset before the build runs; a shared bump counter
+// would take one contended atomic per root. Three passes: tiles of
+// SCAN_TILE words (four per thread) scanned within a block, the tile totals
+// scanned by one block, the tile prefixes added.
+#define SCAN_THREADS 1024
+#define SCAN_TILE (4 * SCAN_THREADS)
+
+__device__ __forceinline__ u64 wave_incl_scan_u64(u64 v) {
+  const int lane = lane_id();
+#pragma unroll
+  for (int d = 1; d < MCE_WAVE; d <<= 1) {
+    const u64 t = __shfl_up(v, d, MCE_WAVE);
+    if (lane >= d) v += t;
+  }
+  return v;
+}
+
+// Exclusive scan of one value per thread over the block.
+__device__ void block_excl_scan_u64(u64 v, u64& excl) {
+  __shared__ u64 s_w[SCAN_THREADS / MCE_WAVE];
+  const int lane = lane_id(), w = threadIdx.x / MCE_WAVE;
+  const u64 inc = wave_incl_scan_u64(v);
+  if (lane == MCE_WAVE - 1) s_w[w] = inc;
+  __syncthreads();
+  if (w == 0) {
+    const u64 t = lane < SCAN_THREADS / MCE_WAVE ? s_w[lane] : 0ull;
+    const u64 ti = wave_incl_scan_u64(t);
+    if (lane < SCAN_THREADS / MCE_WAVE) s_w[lane] = ti - t;
+  }
+  __syncthreads();
+  excl = s_w[w] + inc - v;
+  __syncthreads();
+}
+
+__global__ __launch_bounds__(SCAN_THREADS) void k_scan_tiles(u64* a, int n, u64* tsum) {
+  const int base = blockIdx.x * SCAN_TILE + threadIdx.x * 4;
+  u64 v[4], sum = 0;
+#pragma unroll
+  for (int q = 0; q < 4; q++) {
+    v[q] = base + q < n ? a[base + q] : 0ull;
+    sum += v[q];
+  }
+  u64 excl;
+  block_excl_scan_u64(sum, excl);
+#pragma unroll
+  for (int q = 0; q < 4; q++) {
+    if (base + q < n) a[base + q] = excl;
+    excl += v[q];
+  }
+  if (threadIdx.x == SCAN_THREADS - 1) tsum[blockIdx.x] = excl;   // the tile's total
+}
+
+__global__ __launch_bounds__(SCAN_THREADS) void k_scan_totals(u64* tsum, int nt) {
+  u64 carry = 0;
+  for (int b0 = 0; b0 < nt; b0 += SCAN_THREADS) {
+    const int i = b0 + threadIdx.x;
+    const u64 v = i < nt ? tsum[i] : 0ull;
+    u64 excl;
+    block_excl_scan_u64(v, excl);
+    if (i < nt) tsum[i] = carry + excl;
+    // block total = last thread's exclusive + its value
+    __shared__ u64 s_last;
+    if (threadIdx.x == SCAN_THREADS - 1) s_last = excl + v;
+    __syncthreads();
+    carry += s_last;
+    __syncthreads();
+  }
+}
+
+__global__ __launch_bounds__(SCAN_THREADS) void k_scan_add(u64* a, int n, const u64* tsum) {
+  const int base = blockIdx.x * SCAN_TILE + threadIdx.x * 4;
+  const u64 add = tsum[blockIdx.x];
+#pragma unroll
+  for (int q = 0; q < 4; q++)
+    if (base + q < n) a[base + q] += add;
+}
+
+int mce_scan_temp_words(int n) { return (n + SCAN_TILE - 1) / SCAN_TILE + 1; }
+
+hipError_t mce_launch_scan(u64* a, int n, u64* tsum, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  const int nt = (n + SCAN_TILE - 1) / SCAN_TILE;
+  hipLaunchKernelGGL(k_scan_tiles, dim3(nt), dim3(SCAN_THREADS), 0, s, a, n, tsum);
+  hipLaunchKernelGGL(k_scan_totals, dim3(1), dim3(SCAN_THREADS), 0, s, tsum, nt);
+  hipLaunchKernelGGL(k_scan_add, dim3(nt), dim3(SCAN_THREADS), 0, s, a, n, (const u64*)tsum);
   return hipGetLastError();
 }
