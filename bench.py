@@ -49,13 +49,43 @@ def parse():
     ap.add_argument("--calib-copy-mb", type=int, default=0,
                     help="also run one device copy of this many MiB (counter calibration runs)")
     ap.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "search_traffic.json"))
+    ap.add_argument("--counters-json", default=os.path.join(ROOT, "profiles", "search_counters.json"))
     return ap.parse_args()
+
+
+KERNEL_SOURCES = {"k_search_micro": "micro.hip", "k_search_w1": "search.hip", "k_search": "search.hip"}
+
+
+def kernel_source_hash(kernel):
+    """SHA-256 prefix of the source file that defines `kernel` (profiles taken on
+    another version of the kernel are not used)."""
+    import hashlib
+    path = os.path.join(ROOT, "maximal_clique_enumeration_amd", "csrc", KERNEL_SOURCES[kernel])
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def load_profile(path, config, kernel):
+    """A committed counter summary for this workload and the current kernel source, or None."""
+    if not os.path.exists(path):
+        return None
+    try:
+        with open(path) as f:
+            tj = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if tj.get("config") != config or tj.get("kernel_family") != kernel:
+        return None
+    if tj.get("source_sha256_16") != kernel_source_hash(kernel):
+        return None
+    return tj
 
 
 def algorithmic_ops(st):
     w = st["pivot_words"] / st["pivot_rows"] if st["pivot_rows"] else 1.0
-    # a donated branch is taken by no wave: add the donations back
-    branches = st["branches"] + st["donations"]
+    # the wavefront kernels hand a donated branch over untaken: add those back;
+    # the micro kernel hands over frames whose branches are counted where taken
+    branches = st["branches"] + (st["donations"] if st["steps"] == 0 else 0)
     return (st["pivot_words"] * OPS_PER_PIVOT_WORD + branches * w * OPS_PER_BRANCH_WORD
             + st["xx_tests"] * OPS_PER_XX_TEST + st["leaves"] * OPS_PER_LEAF)
 
@@ -132,20 +162,20 @@ def main():
     avg_search_s = sum(search_ms) / len(search_ms) / 1e3
     launches = max(1, st["launches"])
     achieved = ops / avg_search_s if avg_search_s > 0 else 0.0
-    traffic = None
-    if os.path.exists(args.traffic_json):
-        try:
-            with open(args.traffic_json) as f:
-                tj = json.load(f)
-            if tj.get("config") == args.config:
-                traffic = tj.get("bytes_per_launch")
-        except (OSError, ValueError):
-            traffic = None
+    kernel = "k_search_micro" if st["steps"] > 0 and launches == 1 else "k_search_w1"
+    tj = load_profile(args.traffic_json, args.config, kernel)
+    traffic = tj.get("bytes_per_launch") if tj else None
     roofline = {"bound": "alu", "achieved": achieved / 1e12, "peak": VALU_INT32_PEAK / 1e12,
                 "unit": "Tops/s (int32 vector lane-ops)", "frac": achieved / VALU_INT32_PEAK,
-                "traffic": traffic, "kernel": "k_search_w1 (search launches)",
+                "traffic": traffic, "kernel": kernel,
                 "search_ms_per_step": avg_search_s * 1e3, "launches_per_step": launches,
                 "ops_per_step": ops}
+    cj = load_profile(args.counters_json, args.config, kernel)
+    if cj and avg_search_s > 0:
+        # VALU issue: each wave64 VALU instruction occupies a 16-lane SIMD for 4 cycles
+        simd_cycles = 256 * 4 * 2.4e9 * avg_search_s
+        roofline["valu_issue_frac"] = cj["sq_insts_valu_per_launch"] * 4 / simd_cycles
+        roofline["salu_issue_frac"] = cj["sq_insts_salu_per_launch"] / (256 * 2.4e9 * avg_search_s)
     info = eng.graph_info()
     busy = (st["busy_ticks"] / (st["workers"] * st["kernel_ticks"])
             if st["workers"] and st["kernel_ticks"] else None)
@@ -165,11 +195,13 @@ def main():
         "config": {"workload": g.name, "n": g.n, "edges": g.m, "degeneracy": info["degeneracy"],
                    "max_degree": info["max_degree"], "maximal_cliques": count,
                    "subgraph": "full" if info["subgraph"] == mce.MCE_SUBGRAPH_FULL else "partial",
-                   "parallelism": "single GPU, one wavefront per subtree + branch requests",
+                   "parallelism": "single GPU: one search-tree node per lane (micro kernel), frame stacks "
+                                  "per wavefront, branch requests between wavefronts",
                    "seed": args.seed},
         "roofline": roofline,
         "detail": {"e2e_ms_min": min(times) * 1e3, "e2e_ms_median": sorted(times)[len(times) // 2] * 1e3,
                    "nodes": st["nodes"], "donations": st["donations"], "workers": st["workers"],
+                   "steps": st["steps"], "lane_util": (st["lane_steps"] / (64 * st["steps"]) if st["steps"] else None),
                    "busy_frac": busy,
                    "max_over_avg_nodes": (st["max_nodes"] / (st["nodes"] / st["workers"])
                                           if st["nodes"] and st["workers"] else None),

@@ -9,9 +9,10 @@ a failing check, not as a silent mismatch) and:
   - otherwise the results on seeded root samples (the maximal cliques whose
     earliest vertex in the peel order is a sampled root, "Parallelizing Maximal
     Clique Enumeration on GPUs", section 2.4, Algorithm 3): uniformly drawn
-    roots, and the roots with the largest later-neighbour sets among those the
-    oracle finishes within a node budget. The whole R-MAT and large Chung-Lu
-    graphs have too many maximal cliques to enumerate in a test.
+    roots, and the roots with the largest later-neighbour sets, each kept only if
+    the oracle finishes its subtree within a node budget (the test compares
+    exactly the kept roots). The whole R-MAT and large Chung-Lu graphs have too
+    many maximal cliques to enumerate in a test.
 
 Run from the repository root:  python tests/golden/make_configs.py
 """
@@ -34,9 +35,10 @@ import oracle  # noqa: E402
 WHOLE = (0, 1, 3)
 SAMPLED = (2, 4)
 N_UNIFORM = 3000          # uniformly drawn roots per sampled configuration
-N_HEAVY_TRY = 400         # candidates with the largest |P| tried one by one
+UNIFORM_BUDGET = 200_000  # oracle search-tree nodes allowed per uniform root
+N_HEAVY_TRY = 150         # candidates with the largest |P| tried one by one
 N_HEAVY_KEEP = 60         # heavy roots kept
-HEAVY_BUDGET = 2_000_000  # oracle search-tree nodes allowed per heavy root
+HEAVY_BUDGET = 1_000_000  # oracle search-tree nodes allowed per heavy root
 
 
 def later_counts(g, rnd):
@@ -69,10 +71,15 @@ def main():
             rec["whole"] = entry(r)
         else:
             rng = np.random.default_rng(1000 + idx)
-            uni = np.sort(rng.choice(g.n, size=N_UNIFORM, replace=False)).astype(np.int32)
+            draw = np.sort(rng.choice(g.n, size=N_UNIFORM, replace=False)).astype(np.int32)
+            kept = [int(v) for v in draw
+                    if oracle.mce(g.n, g.row_ptr, g.col_idx, roots=np.array([v], np.int32),
+                                  node_budget=UNIFORM_BUDGET, rnd=rnd).complete]
+            uni = np.array(kept, np.int32)
             r = oracle.mce(g.n, g.row_ptr, g.col_idx, roots=uni, rnd=rnd)
             assert r.complete
-            rec["uniform"] = {"roots": uni.tolist(), **entry(r)}
+            rec["uniform"] = {"roots": uni.tolist(), "drawn": int(draw.size), **entry(r)}
+            print(idx, "uniform", uni.size, "of", draw.size, round(time.time() - t0, 1), flush=True)
             p = later_counts(g, rnd)
             cand = np.argsort(-p, kind="stable")[:N_HEAVY_TRY]
             keep = []
