@@ -10,6 +10,7 @@
 #include <chrono>
 #include <cstdio>
 #include <cstring>
+#include <map>
 #include <new>
 #include <string>
 #include <vector>
@@ -39,7 +40,7 @@ struct mce_engine {
   int peel_blocks_max = 1;
   std::string err;
 
-  DevBuf ctl, deg, rnd, core, alive0, alive1, front0, front1, bfront0, bfront1, pcount, xcount, lists, taboff, scan, heap, results, wl,
+  DevBuf ctl, deg, rnd, core, alive0, alive1, front0, front1, bfront0, bfront1, pcount, xcount, lists, taboff, scan, heap, wl,
       slots, stats, mstack, mail;
   HostPinned host;    // staging for device -> host copies
   hipEvent_t ev[4 + 4 * MCE_NSUB] = {};
@@ -54,6 +55,18 @@ struct mce_engine {
   mce_graph_facts info{};
   mce_run_stats stats_out{};
   std::vector<mce_worker_record> trace;
+
+  // per-wave counters of the last run stay on the device until mce_stats or
+  // mce_worker_trace asks for them (they are diagnostics, not results)
+  struct LaunchInfo {
+    int sub, nw, roots;
+  };
+  std::vector<LaunchInfo> last_plan;
+  int last_stat_rows = 0;
+  bool stats_pending = false;
+  bool last_timing = false;
+  // resident-wave counts per kernel variant (occupancy queries cost ~0.1 ms each)
+  std::map<std::pair<int, long long>, int> occupancy;
 };
 
 namespace {
@@ -105,6 +118,9 @@ double ms_since(std::chrono::steady_clock::time_point t0) {
 }
 
 constexpr size_t kHistWords = MCE_MAX_P + 2;   // global histogram entries
+// control block, then the result words (hash, histogram): one clear, one read-back
+constexpr size_t kIoBytes = sizeof(MceCtl) + (1 + kHistWords) * sizeof(u64);
+static_assert(sizeof(MceCtl) % sizeof(u64) == 0, "results follow the control block");
 constexpr int kMicroStack = 4096;              // frames per wavefront stack of the micro search
 
 mce_status run_impl(mce_engine* e, int32_t n, int64_t nnz, const int32_t* row_ptr, const int32_t* col_idx,
@@ -123,6 +139,7 @@ mce_status run_impl(mce_engine* e, int32_t n, int64_t nnz, const int32_t* row_pt
   hipError_t h = hipSetDevice(e->device);
   if (h != hipSuccess) return hip_fail(e, h, "hipSetDevice");
 
+  e->stats_pending = false;
   e->info = mce_graph_facts{};
   e->info.n = n;
   e->info.nnz = nnz;
@@ -145,7 +162,7 @@ mce_status run_impl(mce_engine* e, int32_t n, int64_t nnz, const int32_t* row_pt
   const u64 budget = (u64)((double)e->cfg.timeout_ms * 1e-3 * e->tick_hz);
 
   size_t nb = (size_t)n * sizeof(int);
-  if ((h = ensure(e->ctl, sizeof(MceCtl))) != hipSuccess || (h = ensure(e->deg, nb)) != hipSuccess ||
+  if ((h = ensure(e->ctl, kIoBytes)) != hipSuccess || (h = ensure(e->deg, nb)) != hipSuccess ||
       (h = ensure(e->rnd, nb)) != hipSuccess || (h = ensure(e->core, nb)) != hipSuccess ||
       (h = ensure(e->alive0, nb)) != hipSuccess || (h = ensure(e->alive1, nb)) != hipSuccess ||
       (h = ensure(e->front0, nb)) != hipSuccess || (h = ensure(e->front1, nb)) != hipSuccess ||
@@ -153,16 +170,13 @@ mce_status run_impl(mce_engine* e, int32_t n, int64_t nnz, const int32_t* row_pt
       (h = ensure(e->pcount, (size_t)std::max(cnt, 1) * sizeof(int))) != hipSuccess ||
       (h = ensure(e->xcount, (size_t)std::max(cnt, 1) * sizeof(int))) != hipSuccess ||
       (h = ensure(e->lists, (size_t)std::max(cnt, 1) * sizeof(int))) != hipSuccess ||
-      (h = ensure(e->results, (1 + kHistWords) * sizeof(u64))) != hipSuccess ||
       (h = ensure(e->wl, sizeof(MceWl))) != hipSuccess ||
-      (h = ensure_host(e->host, sizeof(MceCtl) + (1 + kHistWords) * sizeof(u64))) != hipSuccess)
+      (h = ensure_host(e->host, kIoBytes)) != hipSuccess)
     return hip_fail(e, h, "allocation");
 
   MceCtl* ctl = dp<MceCtl>(e->ctl);
-  u64* results = dp<u64>(e->results);
-  if ((h = hipMemsetAsync(ctl, 0, sizeof(MceCtl), s)) != hipSuccess) return hip_fail(e, h, "memset");
-  if ((h = hipMemsetAsync(results, 0, (1 + kHistWords) * sizeof(u64), s)) != hipSuccess)
-    return hip_fail(e, h, "memset");
+  u64* results = reinterpret_cast<u64*>(dp<char>(e->ctl) + sizeof(MceCtl));   // hash, then the histogram
+  if ((h = hipMemsetAsync(ctl, 0, kIoBytes, s)) != hipSuccess) return hip_fail(e, h, "memset");
 
   const int grid = std::max(1, e->num_cu * 8);
   if (timing) (void)hipEventRecord(e->ev[0], s);
@@ -250,13 +264,20 @@ mce_status run_impl(mce_engine* e, int32_t n, int64_t nnz, const int32_t* row_pt
     int nw;
     if (c == MCE_SUB_MICRO) {
       // 8 wavefronts per CU: more add start-up spread and little throughput
-      nw = std::min(mce_micro_max_workers(counters, e->num_cu), 8 * e->num_cu);
+      const auto key = std::make_pair(-1 - (counters ? 1 : 0), 0LL);
+      auto it = e->occupancy.find(key);
+      if (it == e->occupancy.end()) it = e->occupancy.emplace(key, mce_micro_max_workers(counters, e->num_cu)).first;
+      nw = std::min(it->second, 8 * e->num_cu);
       mstack_bytes = (size_t)std::max(nw, 1) * 6 * kMicroStack * sizeof(u64);
       mail_bytes = (size_t)std::max(nw, 1) * mce_micro_mail_words() * sizeof(u64);
     } else {
       pl.L = mce_search_layout(c, mode, hctl->sub_maxp[var][c], hctl->sub_maxx[var][c], hctl->sub_maxr[var][c],
                                hbm, counters);
-      nw = mce_search_max_workers(pl.L, e->num_cu);
+      const auto key = std::make_pair(((c * 2 + mode) * 2 + (counters ? 1 : 0)) * 2 + (pl.L.srows ? 1 : 0),
+                                      (long long)pl.L.lds_bytes * 2 + (pl.L.sstack ? 1 : 0));
+      auto it = e->occupancy.find(key);
+      if (it == e->occupancy.end()) it = e->occupancy.emplace(key, mce_search_max_workers(pl.L, e->num_cu)).first;
+      nw = it->second;
     }
     if (nw <= 0) return fail(e, MCE_ERR_DEVICE, "search kernel occupancy query failed");
     if (e->cfg.max_workers > 0) nw = std::min(nw, (int)e->cfg.max_workers);
@@ -275,8 +296,6 @@ mce_status run_impl(mce_engine* e, int32_t n, int64_t nnz, const int32_t* row_pt
         (mstack_bytes && (h = ensure(e->mstack, mstack_bytes)) != hipSuccess) ||
         (mail_bytes && (h = ensure(e->mail, mail_bytes)) != hipSuccess))
       return hip_fail(e, h, "search buffers");
-    if ((h = hipMemsetAsync(e->stats.p, 0, (size_t)stat_rows * MCE_NSTAT * sizeof(u64), s)) != hipSuccess)
-      return hip_fail(e, h, "memset");
     if ((h = mce_launch_bucket(subset ? roots : nullptr, cnt, dp<int>(e->pcount), dp<int>(e->xcount), mode,
                                micro_on ? 1 : 0, off, dp<int>(e->lists), dp<u64>(e->taboff), ctl, grid, s)) !=
         hipSuccess)
@@ -309,7 +328,9 @@ mce_status run_impl(mce_engine* e, int32_t n, int64_t nnz, const int32_t* row_pt
     if (timing) (void)hipEventRecord(e->ev[evi], s);
     if ((h = mce_launch_build(bp, e->num_cu * 32, s)) != hipSuccess) return hip_fail(e, h, "build launch");
     if (timing) (void)hipEventRecord(e->ev[evi + 1], s);
-    if ((h = mce_launch_wl_init(dp<MceWl>(e->wl), pl.nw, s)) != hipSuccess) return hip_fail(e, h, "wl init");
+    if ((h = mce_launch_wl_init(dp<MceWl>(e->wl), pl.nw, dp<u64>(e->stats) + (size_t)stat_off * MCE_NSTAT, s)) !=
+        hipSuccess)
+      return hip_fail(e, h, "wl init");
     if (micro) {
       MicroParams mp{};
       mp.heap = dp<u64>(e->heap);
@@ -375,54 +396,15 @@ mce_status run_impl(mce_engine* e, int32_t n, int64_t nnz, const int32_t* row_pt
     launches++;
     max_workers_used = std::max(max_workers_used, pl.nw);
   }
-  std::vector<u64> st((size_t)stat_rows * MCE_NSTAT);
-  if (stat_rows > 0 &&
-      (h = hipMemcpyAsync(st.data(), e->stats.p, st.size() * sizeof(u64), hipMemcpyDeviceToHost, s)) != hipSuccess)
-    return hip_fail(e, h, "stats readback");
-
-  u64* hres = reinterpret_cast<u64*>(static_cast<char*>(e->host.p) + sizeof(MceCtl));
-  if ((h = hipMemcpyAsync(hres, results, (1 + kHistWords) * sizeof(u64), hipMemcpyDeviceToHost, s)) != hipSuccess ||
-      (h = hipMemcpyAsync(hctl, ctl, sizeof(MceCtl), hipMemcpyDeviceToHost, s)) != hipSuccess)
+  // results: one read-back of the control block and the result words
+  if ((h = hipMemcpyAsync(e->host.p, ctl, kIoBytes, hipMemcpyDeviceToHost, s)) != hipSuccess)
     return hip_fail(e, h, "result readback");
   if ((h = hipStreamSynchronize(s)) != hipSuccess) return hip_fail(e, h, "synchronize at end");
+  const u64* hres = reinterpret_cast<const u64*>(static_cast<const char*>(e->host.p) + sizeof(MceCtl));
   if (hctl->status & MCE_E_TIMEOUT) return fail(e, MCE_ERR_TIMEOUT, "search ran past the time limit");
   if (hctl->status & MCE_E_PROTO) return fail(e, MCE_ERR_DEVICE, "worker-list bookkeeping error");
   if (hctl->status & MCE_E_LIMIT) return fail(e, MCE_ERR_LIMIT, "subtree larger than its width class");
   if (hctl->status & MCE_E_HEAP) return fail(e, MCE_ERR_DEVICE, "induced-subgraph heap overflow");
-  std::vector<u64> stat_sum(MCE_NSTAT, 0);
-  e->trace.clear();
-  u64 max_busy = 0, max_nodes = 0, max_ticks = 0, start_spread = 0, max_stack = 0;
-  {
-    int row = 0;
-    for (const Plan& pl : plan) {
-      u64 smin = ~0ull, smax = 0;
-      for (int w = 0; w < pl.nw; w++, row++) {
-        const u64* r = &st[(size_t)row * MCE_NSTAT];
-        mce_worker_record rec{};
-        rec.launch = (int32_t)(&pl - plan.data());
-        rec.worker = w;
-        rec.start_tick = r[ST_START_ABS];
-        rec.first_tick = r[ST_FIRST_ABS];
-        rec.last_tick = r[ST_LAST_ABS];
-        rec.end_tick = r[ST_START_ABS] + r[ST_TOTAL_TICKS];
-        rec.busy_ticks = r[ST_BUSY_TICKS];
-        rec.nodes = r[ST_NODES];
-        rec.donations = r[ST_DONATIONS];
-        rec.received = r[ST_RECEIVED];
-        e->trace.push_back(rec);
-        for (int i = 0; i < MCE_NSTAT; i++) stat_sum[i] += r[i];
-        max_busy = std::max(max_busy, r[ST_BUSY_TICKS]);
-        max_nodes = std::max(max_nodes, r[ST_NODES]);
-        max_ticks = std::max(max_ticks, r[ST_TOTAL_TICKS]);
-        max_stack = std::max(max_stack, r[ST_STACK_MAX]);
-        if (r[ST_START_ABS]) {
-          smin = std::min(smin, r[ST_START_ABS]);
-          smax = std::max(smax, r[ST_START_ABS]);
-        }
-      }
-      if (smax >= smin && smin != ~0ull) start_spread = std::max(start_spread, smax - smin);
-    }
-  }
 
   std::vector<uint64_t> hist(kHistWords, 0);
   for (size_t k = 0; k < kHistWords; k++) hist[k] = hres[1 + k];
@@ -442,15 +424,75 @@ mce_status run_impl(mce_engine* e, int32_t n, int64_t nnz, const int32_t* row_pt
   mce_run_stats& so = e->stats_out;
   so.workers = max_workers_used;
   so.launches = launches;
+  u64 words_built = 0;
+  for (const Plan& pl : plan) words_built += hctl->sub_words[var][pl.sub];
+  so.table_words = words_built;
+  e->last_plan.clear();
+  for (size_t i = 0; i < plan.size(); i++) {
+    e->last_plan.push_back({plan[i].sub, plan[i].nw, counts[plan[i].sub]});
+    if (i < 16) {
+      so.launch_sub[i] = plan[i].sub;
+      so.launch_roots[i] = counts[plan[i].sub];
+    }
+  }
+  for (int i = 0; i < 4; i++) so.peel_ticks[i] = hctl->peel_ticks[i];
+  so.micro_roots = counts[MCE_SUB_MICRO];
+  e->last_stat_rows = stat_rows;
+  e->last_timing = timing;
+  e->stats_pending = true;
+  so.ms_total = ms_since(t0);
+  return MCE_OK;
+}
+
+// Per-wave counters and phase times of the last run, read on demand.
+mce_status collect_stats(mce_engine* e) {
+  if (!e->stats_pending) return MCE_OK;
+  hipError_t h = hipSetDevice(e->device);
+  if (h != hipSuccess) return hip_fail(e, h, "hipSetDevice");
+  std::vector<u64> st((size_t)e->last_stat_rows * MCE_NSTAT);
+  if (!st.empty() && (h = hipMemcpy(st.data(), e->stats.p, st.size() * sizeof(u64), hipMemcpyDeviceToHost)) !=
+                         hipSuccess)
+    return hip_fail(e, h, "stats readback");
+  mce_run_stats& so = e->stats_out;
+  std::vector<u64> stat_sum(MCE_NSTAT, 0);
+  e->trace.clear();
+  u64 max_busy = 0, max_nodes = 0, max_ticks = 0, start_spread = 0, max_stack = 0;
+  int row = 0;
+  for (size_t li = 0; li < e->last_plan.size(); li++) {
+    const auto& pl = e->last_plan[li];
+    u64 smin = ~0ull, smax = 0;
+    for (int w = 0; w < pl.nw; w++, row++) {
+      const u64* r = &st[(size_t)row * MCE_NSTAT];
+      mce_worker_record rec{};
+      rec.launch = (int32_t)li;
+      rec.worker = w;
+      rec.start_tick = r[ST_START_ABS];
+      rec.first_tick = r[ST_FIRST_ABS];
+      rec.last_tick = r[ST_LAST_ABS];
+      rec.end_tick = r[ST_START_ABS] + r[ST_TOTAL_TICKS];
+      rec.busy_ticks = r[ST_BUSY_TICKS];
+      rec.nodes = r[ST_NODES];
+      rec.donations = r[ST_DONATIONS];
+      rec.received = r[ST_RECEIVED];
+      e->trace.push_back(rec);
+      for (int i = 0; i < MCE_NSTAT; i++) stat_sum[i] += r[i];
+      max_busy = std::max(max_busy, r[ST_BUSY_TICKS]);
+      max_nodes = std::max(max_nodes, r[ST_NODES]);
+      max_ticks = std::max(max_ticks, r[ST_TOTAL_TICKS]);
+      max_stack = std::max(max_stack, r[ST_STACK_MAX]);
+      if (r[ST_START_ABS]) {
+        smin = std::min(smin, r[ST_START_ABS]);
+        smax = std::max(smax, r[ST_START_ABS]);
+      }
+    }
+    if (smax >= smin && smin != ~0ull) start_spread = std::max(start_spread, smax - smin);
+  }
   so.nodes = stat_sum[ST_NODES];
   so.leaves = stat_sum[ST_LEAVES];
   so.donations = stat_sum[ST_DONATIONS];
   so.pivot_rows = stat_sum[ST_PIVOT_ROWS];
   so.pivot_words = stat_sum[ST_PIVOT_WORDS];
   so.xx_tests = stat_sum[ST_XX_TESTS];
-  u64 words_built = 0;
-  for (const Plan& pl : plan) words_built += hctl->sub_words[var][pl.sub];
-  so.table_words = words_built;
   so.branches = stat_sum[ST_BRANCHES];
   so.busy_ticks = stat_sum[ST_BUSY_TICKS];
   so.max_busy_ticks = max_busy;
@@ -463,15 +505,9 @@ mce_status run_impl(mce_engine* e, int32_t n, int64_t nnz, const int32_t* row_pt
   so.claim_checks = stat_sum[ST_CHECKS];
   so.donate_ok_ticks = stat_sum[ST_DONATE_OK_TICKS];
   so.max_stack_frames = max_stack;
-  for (size_t i = 0; i < plan.size() && i < 16; i++) {
-    so.launch_sub[i] = plan[i].sub;
-    so.launch_roots[i] = counts[plan[i].sub];
-  }
-  for (int i = 0; i < 4; i++) so.peel_ticks[i] = hctl->peel_ticks[i];
   so.steps = stat_sum[ST_STEPS];
   so.lane_steps = stat_sum[ST_LANE_STEPS];
-  so.micro_roots = counts[MCE_SUB_MICRO];
-  if (timing) {
+  if (e->last_timing) {
     float a = 0, b = 0, c = 0;
     (void)hipEventElapsedTime(&a, e->ev[0], e->ev[1]);
     (void)hipEventElapsedTime(&b, e->ev[1], e->ev[2]);
@@ -480,7 +516,7 @@ mce_status run_impl(mce_engine* e, int32_t n, int64_t nnz, const int32_t* row_pt
     so.ms_peel = b;
     so.ms_orient = c;   // orientation, host read-back and root bucketing
     double mb = 0, ms = 0;
-    for (int i = 0; i < launches; i++) {
+    for (int i = 0; i < (int)e->last_plan.size(); i++) {
       float x = 0, y = 0;
       (void)hipEventElapsedTime(&x, e->ev[4 + 4 * i], e->ev[5 + 4 * i]);
       (void)hipEventElapsedTime(&y, e->ev[6 + 4 * i], e->ev[7 + 4 * i]);
@@ -494,7 +530,7 @@ mce_status run_impl(mce_engine* e, int32_t n, int64_t nnz, const int32_t* row_pt
     so.ms_build = mb;
     so.ms_search = ms;
   }
-  so.ms_total = ms_since(t0);
+  e->stats_pending = false;
   return MCE_OK;
 }
 
@@ -613,6 +649,8 @@ mce_status mce_ordering(const mce_engine* e, int32_t* core, int32_t* round, void
 
 mce_status mce_stats(const mce_engine* e, mce_run_stats* stats) {
   if (!e || !stats) return MCE_ERR_ARG;
+  const mce_status cs = collect_stats(const_cast<mce_engine*>(e));
+  if (cs != MCE_OK) return cs;
   uint32_t want = stats->struct_size ? stats->struct_size : (uint32_t)sizeof(mce_run_stats);
   size_t n = std::min<size_t>(want, sizeof(mce_run_stats));
   std::memcpy(stats, &e->stats_out, n);
@@ -623,6 +661,8 @@ mce_status mce_stats(const mce_engine* e, mce_run_stats* stats) {
 mce_status mce_worker_trace(const mce_engine* e, mce_worker_record* out, int32_t cap, int32_t* count) {
   if (!e || cap < 0) return MCE_ERR_ARG;
   if (!e->have_result) return MCE_ERR_STATE;
+  const mce_status cs = collect_stats(const_cast<mce_engine*>(e));
+  if (cs != MCE_OK) return cs;
   const int32_t n = (int32_t)e->trace.size();
   if (count) *count = n;
   if (out) {
@@ -652,7 +692,7 @@ void mce_destroy(mce_engine* e) {
   (void)hipSetDevice(e->device);
   DevBuf* bufs[] = {&e->ctl,    &e->deg,   &e->rnd,    &e->core,    &e->alive0, &e->alive1,
                     &e->front0, &e->front1, &e->bfront0, &e->bfront1, &e->pcount, &e->xcount, &e->lists,  &e->taboff, &e->scan,
-                    &e->heap,   &e->results, &e->wl,    &e->slots,  &e->stats,  &e->mstack, &e->mail};
+                    &e->heap,   &e->wl,    &e->slots,  &e->stats,  &e->mstack, &e->mail};
   for (DevBuf* b : bufs) release(*b);
   if (e->host.p) (void)hipHostFree(e->host.p);
   for (auto& ev : e->ev)

@@ -137,7 +137,8 @@ SearchLayout mce_search_layout(int sub, int mode, int pcap, int xcap, int rcap, 
 // Resident wavefronts of a search layout over the whole chip (0 on error).
 int mce_search_max_workers(const SearchLayout& L, int num_cu);
 hipError_t mce_launch_search(const SearchLayout& L, const SearchParams& prm, hipStream_t s);
-hipError_t mce_launch_wl_init(MceWl* wl, int nworkers, hipStream_t s);
+// Clears the worker list for nworkers waves and their counter rows (nworkers * MCE_NSTAT u64).
+hipError_t mce_launch_wl_init(MceWl* wl, int nworkers, u64* stats, hipStream_t s);
 
 int mce_micro_mail_words();
 int mce_micro_max_workers(bool counters, int num_cu);

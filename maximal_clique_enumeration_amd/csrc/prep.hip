@@ -540,6 +540,8 @@ hipError_t mce_launch_peel(int n, const int* rp, const int* ci, int* deg, int* r
                            u64 budget, int blocks, hipStream_t s) {
   void* args[] = {&n, (void*)&rp, (void*)&ci, &deg, &rnd, &core, &alive0, &alive1,
                   &front0, &front1, &bfront0, &bfront1, &ctl, &budget};
+  // one block needs no grid barrier, hence no cooperative launch
+  if (blocks == 1) return hipLaunchKernel((const void*)k_peel, dim3(1), dim3(PEEL_THREADS), args, 0, s);
   return hipLaunchCooperativeKernel((const void*)k_peel, dim3(blocks), dim3(PEEL_THREADS), args, 0, s);
 }
 
@@ -654,7 +656,9 @@ hipError_t mce_launch_scan(u64* a, int n, u64* tsum, hipStream_t s) {
   if (n <= 0) return hipSuccess;
   const int nt = (n + SCAN_TILE - 1) / SCAN_TILE;
   hipLaunchKernelGGL(k_scan_tiles, dim3(nt), dim3(SCAN_THREADS), 0, s, a, n, tsum);
-  hipLaunchKernelGGL(k_scan_totals, dim3(1), dim3(SCAN_THREADS), 0, s, tsum, nt);
-  hipLaunchKernelGGL(k_scan_add, dim3(nt), dim3(SCAN_THREADS), 0, s, a, n, (const u64*)tsum);
+  if (nt > 1) {   // one tile is already scanned
+    hipLaunchKernelGGL(k_scan_totals, dim3(1), dim3(SCAN_THREADS), 0, s, tsum, nt);
+    hipLaunchKernelGGL(k_scan_add, dim3(nt), dim3(SCAN_THREADS), 0, s, a, n, (const u64*)tsum);
+  }
   return hipGetLastError();
 }

@@ -918,7 +918,9 @@ __global__ __launch_bounds__(64) void k_search_w1(SearchParams prm) {
 
 // Worker-list reset before a launch: counters zero, wake flags zero, request
 // words closed (a wave opens its own when it starts a task).
-__global__ void k_wl_init(MceWl* wl, int nworkers) {
+// Worker-list words and the launch's per-wave counter rows start at zero
+// (request words closed).
+__global__ void k_wl_init(MceWl* wl, int nworkers, u64* stats) {
   const int tid = blockIdx.x * blockDim.x + threadIdx.x;
   const int nt = gridDim.x * blockDim.x;
   u32* head = (u32*)wl;
@@ -928,12 +930,13 @@ __global__ void k_wl_init(MceWl* wl, int nworkers) {
     wl->line[(size_t)i * MCE_LINE_WORDS] = 0u;
     wl->line[(size_t)i * MCE_LINE_WORDS + MCE_REQ_WORD] = MCE_REQ_CLOSED;
   }
+  for (long long i = tid; i < (long long)nworkers * MCE_NSTAT; i += nt) stats[i] = 0ull;
 }
 
 // ------------------------------------------------------------------ host side
-hipError_t mce_launch_wl_init(MceWl* wl, int nworkers, hipStream_t s) {
+hipError_t mce_launch_wl_init(MceWl* wl, int nworkers, u64* stats, hipStream_t s) {
   hipLaunchKernelGGL(k_wl_init, dim3(std::max(1, std::min(64, (nworkers + 255) / 256))), dim3(256), 0, s, wl,
-                     nworkers);
+                     nworkers, stats);
   return hipGetLastError();
 }
 
