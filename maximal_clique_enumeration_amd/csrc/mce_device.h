@@ -130,7 +130,8 @@ struct MceCtl {
 // release brings n_active to zero writes MCE_FLAG_EXIT into every wake flag; a
 // wave that starts later finds the roots gone and leaves the same way.
 #define MCE_LINE_WORDS 32     // u32 words per 128-byte line
-#define MCE_REQ_WORD 16       // request word inside a wave's line
+#define MCE_REQ_WORD 16       // first request slot inside a wave's line
+#define MCE_REQ_SLOTS 4       // request slots per wave (the micro kernel answers up to four per step)
 #define MCE_FLAG_TASK 1u
 #define MCE_FLAG_EXIT 2u
 #define MCE_FLAG_RETRY 3u

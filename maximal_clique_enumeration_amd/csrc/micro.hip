@@ -104,7 +104,7 @@ __global__ __launch_bounds__(64) void k_search_micro(MicroParams prm) {
     } else {
       if (!prm.worker_list) break;
       const u64 t0 = wall_clock64();
-      const int got = wl_idle(wl, wid, prm.nworkers, deadline, prm.status, rng);
+      const int got = wl_idle(wl, wid, prm.nworkers, deadline, prm.status, rng, MCE_REQ_SLOTS);
       req_closed = true;
       idle_ticks += wall_clock64() - t0;
       if (!got) break;
@@ -156,7 +156,7 @@ __global__ __launch_bounds__(64) void k_search_micro(MicroParams prm) {
     }
     __syncthreads();
     if (prm.worker_list && req_closed) {
-      wl_open(wl, wid);
+      wl_open(wl, wid, MCE_REQ_SLOTS);
       req_closed = false;
     }
     if (t_first == 0) t_first = wall_clock64();
@@ -168,7 +168,7 @@ __global__ __launch_bounds__(64) void k_search_micro(MicroParams prm) {
     for (;;) {
       // this wave's request word, read now and acted on at the end of the step
       u32 rq_raw = 0u;
-      if (prm.worker_list) rq_raw = ld_relaxed(wl_req(wl, wid));
+      if (prm.worker_list && lane < MCE_REQ_SLOTS) rq_raw = ld_relaxed(wl_req(wl, wid, lane));
 
       // 1. lanes without a frame pop the newest ones
       const u64 idle = ballot(!has);
@@ -224,35 +224,48 @@ __global__ __launch_bounds__(64) void k_search_micro(MicroParams prm) {
       //    candidates are picked first so that their row reads overlap. An X
       //    vertex adjacent to all of P ends the node (no maximal clique below it).
       const bool pv = has && !fst;
-      if (ballot(pv)) {
+      const u64 pvm = ballot(pv);
+      if (pvm) {
         const u32 pc1 = (u32)__popcll(fP) + 1u;   // a score of pc1 means |P n N(u)| = |P|
+        const bool xx = ballot(pv && pcx != 0ull) != 0ull;
         if (pv) {
-          int cu[MICRO_K];
-          bool cv[MICRO_K];
+          {
+            int cu[MICRO_K];
+            bool cv[MICRO_K];
+            if (xx) {
 #pragma unroll
-          for (int i = 0; i < MICRO_K; i++) {
-            cv[i] = (pcm | pcx) != 0ull;
-            if (pcm) {
-              cu[i] = __builtin_ctzll(pcm);
-              pcm &= pcm - 1ull;
-            } else if (pcx) {
-              cu[i] = MCE_MICRO_MAX + __builtin_ctzll(pcx);
-              pcx &= pcx - 1ull;
-            } else {
-              cu[i] = 0;
+              for (int i = 0; i < MICRO_K; i++) {
+                cv[i] = (pcm | pcx) != 0ull;
+                if (pcm) {
+                  cu[i] = __builtin_ctzll(pcm);
+                  pcm &= pcm - 1ull;
+                } else if (pcx) {
+                  cu[i] = MCE_MICRO_MAX + __builtin_ctzll(pcx);
+                  pcx &= pcx - 1ull;
+                } else {
+                  cu[i] = 0;
+                }
+              }
+            } else {   // no X_X candidate in any lane
+#pragma unroll
+              for (int i = 0; i < MICRO_K; i++) {
+                cv[i] = pcm != 0ull;
+                cu[i] = cv[i] ? __builtin_ctzll(pcm) : 0;
+                pcm &= pcm - 1ull;
+              }
             }
-          }
-          u64 cr[MICRO_K];
+            u64 cr[MICRO_K];
 #pragma unroll
-          for (int i = 0; i < MICRO_K; i++) cr[i] = s_rows[cu[i]];
+            for (int i = 0; i < MICRO_K; i++) cr[i] = s_rows[cu[i]];
 #pragma unroll
-          for (int i = 0; i < MICRO_K; i++) {
-            const u32 c = cv[i] ? (u32)__popcll(fP & cr[i]) + 1u : 0u;
-            if (c > pbc) {
-              pbc = c;
-              pbr = cr[i];
+            for (int i = 0; i < MICRO_K; i++) {
+              const u32 c = cv[i] ? (u32)__popcll(fP & cr[i]) + 1u : 0u;
+              if (c > pbc) {
+                pbc = c;
+                pbr = cr[i];
+              }
+              if constexpr (CNT) st_prow += cv[i] ? 1u : 0u;
             }
-            if constexpr (CNT) st_prow += cv[i] ? 1u : 0u;
           }
         }
         const bool done = pv && ((pcm | pcx) == 0ull || pbc >= pc1);
@@ -395,26 +408,34 @@ __global__ __launch_bounds__(64) void k_search_micro(MicroParams prm) {
         max_stack = max(max_stack, top - bot);
       }
 
-      // 4. branch requests: frames from the bottom of the stack
+      // 4. branch requests (up to MCE_REQ_SLOTS per step; slot k was read by
+      //    lane k): each receiver gets an equal share of the stack's bottom
+      //    frames (the shallowest), at most MICRO_DON, leaving this wave as much
+      //    as one receiver, if the frames hold at least donate_min_p candidate
+      //    vertices together. All mailboxes are published with one wait.
       if (prm.worker_list) {
-        const u32 rq = uni(rq_raw);
-        if (rq != 0u && rq != MCE_REQ_CLOSED) {
-          const int rcv = (int)rq - 1;
-          // half the stack (rounded up, at most MICRO_DON frames) if the frames
-          // hold at least donate_min_p candidate vertices together
-          u32 give = min((top - bot + 1u) / 2u, (u32)MICRO_DON);
-          const u32 inh = mid - bot;   // frames in HBM
-          const u32 v = bot + (u32)lane;
-          u64 g[MF] = {0, 0, 0, 0, 0, 0};
-          if ((u32)lane < give) {
-            if ((u32)lane < inh) {
-              for (int j = 0; j < MF; j++) g[j] = hstk[(size_t)j * cap + (v & cmask)];
-            } else {
-              for (int j = 0; j < MF; j++) g[j] = s_stk[j][v & lmask];
+        const bool pend = lane < MCE_REQ_SLOTS && rq_raw != 0u && rq_raw != MCE_REQ_CLOSED;
+        const u64 pm = ballot(pend);
+        if (pm) {
+          const u32 nreq = (u32)__popcll(pm);
+          const u32 share = min((u32)MICRO_DON, max(1u, (top - bot) / (nreq + 1u)));
+          u64 given = 0;
+          for (u64 rest = pm; rest; rest &= rest - 1ull) {
+            const int k = __builtin_ctzll(rest);
+            const int rcv = (int)read_lane((int)rq_raw, k) - 1;
+            u32 give = min(share, top - bot);
+            const u32 inh = mid - bot;   // frames in HBM
+            const u32 v = bot + (u32)lane;
+            u64 g[MF] = {0, 0, 0, 0, 0, 0};
+            if ((u32)lane < give) {
+              if ((u32)lane < inh) {
+                for (int j = 0; j < MF; j++) g[j] = hstk[(size_t)j * cap + (v & cmask)];
+              } else {
+                for (int j = 0; j < MF; j++) g[j] = s_stk[j][v & lmask];
+              }
             }
-          }
-          if (give && wave_sum_u32((u32)__popcll(g[0])) < (u32)prm.donate_min_p) give = 0;
-          if (give) {
+            if (give && wave_sum_u32((u32)__popcll(g[0])) < (u32)prm.donate_min_p) give = 0;
+            if (!give) continue;
             u64* dm = prm.mail + (size_t)rcv * prm.mail_words;
             u64* df = dm + 2;
             if ((u32)lane < give) {
@@ -426,10 +447,18 @@ __global__ __launch_bounds__(64) void k_search_micro(MicroParams prm) {
             }
             bot += give;
             if (give > inh) mid = bot;
-            wl_give(wl, wid, rcv);
-            st_don++;
-          } else {
-            wl_refuse(wl, wid, rcv);
+            given |= 1ull << k;
+          }
+          // count the receivers active before they can run (see wl_give), then wake them
+          if (given) {
+            if (lane == 0)
+              __hip_atomic_fetch_add(&wl->n_active, __popcll(given), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            wait_stores_complete();
+            st_don += (u64)__popcll(given);
+          }
+          if (pend) {
+            st_relaxed(wl_flag(wl, (int)rq_raw - 1), ((given >> lane) & 1ull) ? MCE_FLAG_TASK : MCE_FLAG_RETRY);
+            st_relaxed(wl_req(wl, wid, lane), 0u);
           }
         }
       }

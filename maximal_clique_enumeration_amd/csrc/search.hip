@@ -928,7 +928,7 @@ __global__ void k_wl_init(MceWl* wl, int nworkers, u64* stats) {
   for (int i = tid; i < nhead; i += nt) head[i] = 0u;
   for (int i = tid; i < nworkers; i += nt) {
     wl->line[(size_t)i * MCE_LINE_WORDS] = 0u;
-    wl->line[(size_t)i * MCE_LINE_WORDS + MCE_REQ_WORD] = MCE_REQ_CLOSED;
+    for (int k = 0; k < MCE_REQ_SLOTS; k++) wl->line[(size_t)i * MCE_LINE_WORDS + MCE_REQ_WORD + k] = MCE_REQ_CLOSED;
   }
   for (long long i = tid; i < (long long)nworkers * MCE_NSTAT; i += nt) stats[i] = 0ull;
 }

@@ -13,8 +13,10 @@
 #define WL_SPIN_LIMIT (1u << 22)
 
 __device__ __forceinline__ u32* wl_flag(MceWl* wl, int w) { return &wl->line[(size_t)w * MCE_LINE_WORDS]; }
-__device__ __forceinline__ u32* wl_req(MceWl* wl, int w) {
-  return &wl->line[(size_t)w * MCE_LINE_WORDS + MCE_REQ_WORD];
+// Request slot k of wave w (the wavefront kernels use slot 0 only; the micro
+// kernel takes up to MCE_REQ_SLOTS requests per step).
+__device__ __forceinline__ u32* wl_req(MceWl* wl, int w, int k = 0) {
+  return &wl->line[(size_t)w * MCE_LINE_WORDS + MCE_REQ_WORD + k];
 }
 __device__ __forceinline__ u64* wl_mask_word(MceWl* wl, int w) { return &wl->open_mask[(size_t)(w >> 6) * 16]; }
 __device__ __forceinline__ u32 xorshift32(u32& x) {
@@ -28,11 +30,11 @@ __device__ __forceinline__ u32 xorshift32(u32& x) {
 // request word (before the first task, and after wl_idle): between two
 // first-level subtrees the word is open and may already hold a request, which a
 // plain store would erase, leaving the requester waiting for an answer.
-__device__ __forceinline__ void wl_open(MceWl* wl, int wid) {
-  if (lane_id() == 0) {
-    st_relaxed(wl_req(wl, wid), 0u);
+__device__ __forceinline__ void wl_open(MceWl* wl, int wid, int nslots = 1) {
+  const int lane = lane_id();
+  if (lane < nslots) st_relaxed(wl_req(wl, wid, lane), 0u);
+  if (lane == 0)
     __hip_atomic_fetch_or(wl_mask_word(wl, wid), 1ull << (wid & 63), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  }
 }
 
 // A wave whose request word the open-mask shows open, drawn from one mask word
@@ -53,11 +55,11 @@ __device__ __forceinline__ int wl_pick_open(MceWl* wl, int wid, int nworkers, u3
 // The request word of this wave, read by every lane (uniform).
 __device__ __forceinline__ u32 wl_poll(MceWl* wl, int wid) { return uni(ld_relaxed(wl_req(wl, wid))); }
 
-// Answer a request without a branch; reopen the request word.
-__device__ __forceinline__ void wl_refuse(MceWl* wl, int wid, int rcv) {
+// Answer a request without a branch; reopen the request slot.
+__device__ __forceinline__ void wl_refuse(MceWl* wl, int wid, int rcv, int slot = 0) {
   if (lane_id() == 0) {
     st_relaxed(wl_flag(wl, rcv), MCE_FLAG_RETRY);
-    st_relaxed(wl_req(wl, wid), 0u);
+    st_relaxed(wl_req(wl, wid, slot), 0u);
   }
 }
 
@@ -84,14 +86,16 @@ __device__ __forceinline__ void wl_give(MceWl* wl, int wid, int rcv) {
 // Ordering: the refusal and the flag reset complete before the share is given
 // up, and an answer flag is only consumed with a compare-and-swap, so the exit
 // broadcast (issued after every share release) cannot be overwritten.
-__device__ int wl_idle(MceWl* wl, int wid, int nworkers, u64 deadline, u32* status, u32& rng) {
+__device__ int wl_idle(MceWl* wl, int wid, int nworkers, u64 deadline, u32* status, u32& rng, int nslots = 1) {
   const int lane = lane_id();
   u32* my = wl_flag(wl, wid);
   int left = 0;
-  if (lane == 0) {
-    const u32 old = __hip_atomic_exchange(wl_req(wl, wid), MCE_REQ_CLOSED, __ATOMIC_RELAXED,
+  if (lane < nslots) {   // close every slot, refusing a request that raced in
+    const u32 old = __hip_atomic_exchange(wl_req(wl, wid, lane), MCE_REQ_CLOSED, __ATOMIC_RELAXED,
                                           __HIP_MEMORY_SCOPE_AGENT);
     if (old != 0u && old != MCE_REQ_CLOSED) st_relaxed(wl_flag(wl, (int)old - 1), MCE_FLAG_RETRY);
+  }
+  if (lane == 0) {
     __hip_atomic_fetch_and(wl_mask_word(wl, wid), ~(1ull << (wid & 63)), __ATOMIC_RELAXED,
                            __HIP_MEMORY_SCOPE_AGENT);
     st_relaxed(my, 0u);
@@ -124,9 +128,10 @@ __device__ int wl_idle(MceWl* wl, int wid, int nworkers, u64 deadline, u32* stat
       int asked = 0;
       if (lane == 0) {
         const int v = wl_pick_open(wl, wid, nworkers, rng);
+        const int k = nslots > 1 ? (int)(xorshift32(rng) % (u32)nslots) : 0;
         u32 expected = 0u;
-        if (v >= 0 && ld_relaxed(wl_req(wl, v)) == 0u &&
-            __hip_atomic_compare_exchange_strong(wl_req(wl, v), &expected, (u32)wid + 1u, __ATOMIC_RELAXED,
+        if (v >= 0 && ld_relaxed(wl_req(wl, v, k)) == 0u &&
+            __hip_atomic_compare_exchange_strong(wl_req(wl, v, k), &expected, (u32)wid + 1u, __ATOMIC_RELAXED,
                                                  __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) {
           asked = 1;
           // wait for the answer: the asked wave reads its request word once per node
