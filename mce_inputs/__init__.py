@@ -74,23 +74,37 @@ def from_edges(n: int, u, v, name: str = "") -> Graph:
         raise ValueError("n must fit int32")
     keep = u != v
     u, v = u[keep], v[keep]
-    lo = np.minimum(u, v)
-    hi = np.maximum(u, v)
-    key = np.unique(lo * n + hi)            # undirected, deduplicated
-    lo = key // n if n else key
-    hi = key % n if n else key
-    src = np.concatenate([lo, hi])
-    dst = np.concatenate([hi, lo])
-    key2 = src * n + dst
-    key2.sort()
-    src = key2 // n if n else key2
-    dst = key2 % n if n else key2
-    if dst.size >= 2 ** 31:
+    if n == 0 or u.size == 0:
+        return Graph(n, np.zeros(n + 1, np.int32), np.zeros(0, np.int32), name)
+    # undirected, deduplicated, sorted by (lo, hi)
+    key = np.minimum(u, v) * n + np.maximum(u, v)
+    del u, v
+    key.sort()
+    if key.size > 1:
+        key = key[np.concatenate(([True], key[1:] != key[:-1]))]
+    lo, hi = np.divmod(key, n)
+    del key
+    m = lo.size
+    if 2 * m >= 2 ** 31:
         raise ValueError("nnz must fit int32")
-    counts = np.bincount(src, minlength=n) if n else np.zeros(0, np.int64)
+    # row v = its smaller neighbours (ascending), then its larger ones (ascending)
+    cnt_up = np.bincount(lo, minlength=n)
+    cnt_dn = np.bincount(hi, minlength=n)
     row_ptr = np.zeros(n + 1, dtype=np.int64)
-    np.cumsum(counts, out=row_ptr[1:])
-    return Graph(n, row_ptr.astype(np.int32), dst.astype(np.int32), name)
+    np.cumsum(cnt_up + cnt_dn, out=row_ptr[1:])
+    dst = np.empty(2 * m, dtype=np.int32)
+    # larger neighbours: the (lo, hi) order already groups them by lo, ascending
+    up_start = np.cumsum(cnt_up) - cnt_up
+    dst[row_ptr[:-1][lo] + cnt_dn[lo] + (np.arange(m, dtype=np.int64) - up_start[lo])] = hi
+    # smaller neighbours: group by hi, ascending lo
+    rkey = hi * n + lo
+    del lo
+    rkey.sort()
+    rhi, rlo = np.divmod(rkey, n)
+    del rkey
+    dn_start = np.cumsum(cnt_dn) - cnt_dn
+    dst[row_ptr[:-1][rhi] + (np.arange(m, dtype=np.int64) - dn_start[rhi])] = rlo
+    return Graph(n, row_ptr.astype(np.int32), dst, name)
 
 
 # ---------------------------------------------------------------- small families
@@ -212,14 +226,27 @@ def rmat(scale: int, edge_factor: int, a: float, b: float, c: float, d: float, s
     rng = np.random.Generator(np.random.PCG64(seed))
     n = 1 << scale
     m = edge_factor * n
-    u = np.zeros(m, dtype=np.int64)
-    v = np.zeros(m, dtype=np.int64)
-    cuts = np.array([a, a + b, a + b + c])
+    idt = np.int32 if scale < 31 else np.int64
+    u = np.zeros(m, dtype=idt)
+    v = np.zeros(m, dtype=idt)
+    # buffers reused across levels (fresh large temporaries cost page faults)
+    r = np.empty(m, dtype=np.float64)
+    q = np.empty(m, dtype=np.int8)
+    t = np.empty(m, dtype=np.bool_)
+    c0, c1, c2 = a, a + b, a + b + c
     for _ in range(scale):
-        r = rng.random(m)
-        q = np.searchsorted(cuts, r, side="right")   # 0:(0,0) 1:(0,1) 2:(1,0) 3:(1,1)
-        u = (u << 1) | (q >> 1)
-        v = (v << 1) | (q & 1)
+        rng.random(out=r)
+        # quadrant 0:(0,0) 1:(0,1) 2:(1,0) 3:(1,1) = the number of cut points <= r
+        np.greater_equal(r, c0, out=t)
+        q[:] = t
+        np.greater_equal(r, c1, out=t)
+        q += t
+        np.greater_equal(r, c2, out=t)
+        q += t
+        u <<= 1
+        u |= q >> 1
+        v <<= 1
+        v |= q & 1
     return from_edges(n, u, v, f"rmat{scale}_{edge_factor}_{seed}")
 
 
@@ -235,10 +262,10 @@ def _chung_lu_weights(n: int, mean: float, gamma: float, w_max: float) -> np.nda
     lo, hi = 1e-9, 1e12
     for _ in range(200):
         mid = math.sqrt(lo * hi)
-        if mean_of(mid) < mean:
-            lo = mid
-        else:
-            hi = mid
+        nlo, nhi = (mid, hi) if mean_of(mid) < mean else (lo, mid)
+        if (nlo, nhi) == (lo, hi):
+            break   # a fixed point: every further step would leave (lo, hi) as they are
+        lo, hi = nlo, nhi
     i0 = math.sqrt(lo * hi)
     return w_max * i0 ** alpha * (i + i0) ** (-alpha)
 

@@ -36,7 +36,8 @@ WHOLE = (0, 1, 3)
 SAMPLED = (2, 4)
 N_UNIFORM = 3000          # uniformly drawn roots per sampled configuration
 UNIFORM_BUDGET = 200_000  # oracle search-tree nodes allowed per uniform root
-N_HEAVY_TRY = 150         # candidates with the largest |P| tried one by one
+HEAVY_POOL = 20_000       # the roots of largest |P| ...
+N_HEAVY_TRY = 150         # ... of which this many, evenly spaced from the largest down, are tried
 N_HEAVY_KEEP = 60         # heavy roots kept
 HEAVY_BUDGET = 1_000_000  # oracle search-tree nodes allowed per heavy root
 
@@ -81,7 +82,10 @@ def main():
             rec["uniform"] = {"roots": uni.tolist(), "drawn": int(draw.size), **entry(r)}
             print(idx, "uniform", uni.size, "of", draw.size, round(time.time() - t0, 1), flush=True)
             p = later_counts(g, rnd)
-            cand = np.argsort(-p, kind="stable")[:N_HEAVY_TRY]
+            # the very largest |P| sit in the dense core, whose subtrees exceed any
+            # test budget: spread the candidates over the largest HEAVY_POOL
+            pool = np.argsort(-p, kind="stable")[:HEAVY_POOL]
+            cand = pool[np.linspace(0, pool.size - 1, min(N_HEAVY_TRY, pool.size)).astype(np.int64)]
             keep = []
             for v in cand:
                 rv = oracle.mce(g.n, g.row_ptr, g.col_idx, roots=np.array([v], np.int32),

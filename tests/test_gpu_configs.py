@@ -63,6 +63,7 @@ def test_whole_graph(idx, subgraph):
         assert e.graph_info()["degeneracy"] == GOLD[str(idx)]["degeneracy"]
 
 
+@pytest.mark.timeout(900)   # generating the 4M-vertex graph takes about 1.5 minutes on the host
 @pytest.mark.parametrize("kind", ["uniform", "heavy"])
 @pytest.mark.parametrize("idx", [2, 4])
 def test_root_sample(idx, kind):
@@ -70,6 +71,7 @@ def test_root_sample(idx, kind):
     want = GOLD[str(idx)][kind]
     roots = np.asarray(want["roots"], np.int32)
     print(f"case cfg{idx} {kind} roots ({roots.size})", flush=True)
+    assert roots.size > 0, "the sample holds no root"
     with mce.Engine(device=0, timeout_ms=60000) as e:
         got = e.run(rp, ci, roots=torch.from_numpy(roots).to(DEV))
         same(got, want)
