@@ -45,7 +45,7 @@ class mce_config(ctypes.Structure):
                 ("worker_list", ctypes.c_int32), ("donate_min_p", ctypes.c_int32),
                 ("validate", ctypes.c_int32), ("max_workers", ctypes.c_int32),
                 ("timeout_ms", ctypes.c_int64), ("flags", ctypes.c_uint32),
-                ("subgraph", ctypes.c_int32)]
+                ("subgraph", ctypes.c_int32), ("micro_donate_min_p", ctypes.c_int32)]
 
 
 class mce_graph_facts(ctypes.Structure):
@@ -205,10 +205,10 @@ def _ptr(t):
 class Engine:
     """One engine on one GPU. Inputs are int32 CUDA tensors (CSR)."""
 
-    def __init__(self, device: int | None = None, worker_list: bool = True, donate_min_p: int = 10,
+    def __init__(self, device: int | None = None, worker_list: bool = True, donate_min_p: int = 1,
                  validate: bool = True, max_workers: int = 0, timeout_ms: int = 120000,
                  hbm_staging: bool = False, phase_times: bool = False, subgraph: str = "auto",
-                 counters: bool = False, micro: bool = True):
+                 counters: bool = False, micro: bool = True, micro_donate_min_p: int = 10):
         import torch
         if device is None:
             device = torch.cuda.current_device()
@@ -218,6 +218,7 @@ class Engine:
         cfg.device = device
         cfg.worker_list = 1 if worker_list else 0
         cfg.donate_min_p = donate_min_p
+        cfg.micro_donate_min_p = micro_donate_min_p
         cfg.validate = 1 if validate else 0
         cfg.max_workers = max_workers
         cfg.timeout_ms = timeout_ms

@@ -344,7 +344,7 @@ mce_status run_impl(mce_engine* e, int32_t n, int64_t nnz, const int32_t* row_pt
       mp.g_hist = results + 1;
       mp.g_hash = results;
       mp.wl = dp<MceWl>(e->wl);
-      mp.donate_min_p = std::max(1, (int)e->cfg.donate_min_p);
+      mp.donate_min_p = e->cfg.micro_donate_min_p > 0 ? (int)e->cfg.micro_donate_min_p : 10;
       mp.worker_list = e->cfg.worker_list ? 1 : 0;
       mp.budget = budget;
       mp.t_run = &ctl->t_run;
@@ -544,7 +544,8 @@ mce_status mce_config_init(mce_config* cfg) {
   cfg->struct_size = sizeof(mce_config);
   cfg->device = -1;
   cfg->worker_list = 1;
-  cfg->donate_min_p = 10;
+  cfg->donate_min_p = 1;
+  cfg->micro_donate_min_p = 10;
   cfg->validate = 1;
   cfg->max_workers = 0;
   cfg->timeout_ms = 120000;
@@ -563,7 +564,8 @@ mce_status mce_create(const mce_config* cfg, mce_engine** out) {
     std::memcpy(&c, cfg, sz);
     c.struct_size = sizeof(mce_config);
   }
-  if (c.donate_min_p < 1 || c.max_workers < 0 || c.timeout_ms < 0 || c.subgraph < MCE_SUBGRAPH_AUTO ||
+  if (c.donate_min_p < 1 || c.micro_donate_min_p < 0 || c.max_workers < 0 || c.timeout_ms < 0 ||
+      c.subgraph < MCE_SUBGRAPH_AUTO ||
       c.subgraph > MCE_SUBGRAPH_FULL)
     return MCE_ERR_ARG;
   if (c.timeout_ms == 0) c.timeout_ms = 120000;

@@ -43,7 +43,8 @@ def test_status_strings_without_device(lib):
     assert lib.mce_status_string(-2) == b"MCE_ERR_GRAPH"
     cfg = mce.mce_config()
     assert mce.mce_config_init(cfg) == 0
-    assert (cfg.worker_list, cfg.donate_min_p, cfg.validate, cfg.timeout_ms) == (1, 10, 1, 120000)
+    assert (cfg.worker_list, cfg.donate_min_p, cfg.validate, cfg.timeout_ms) == (1, 1, 1, 120000)
+    assert cfg.micro_donate_min_p == 10
     assert cfg.subgraph == mce.MCE_SUBGRAPH_AUTO
     assert cfg.struct_size == ctypes.sizeof(mce.mce_config)
 

@@ -164,7 +164,8 @@ def test_stress_matrix(worker_list, donate_min_p, max_workers, micro):
               mi.chung_lu(5000, 10.0, 2.3, None, 2, planted=10, planted_min=8, planted_max=20)]
     donations = 0
     with mce.Engine(device=0, worker_list=worker_list, donate_min_p=donate_min_p,
-                    max_workers=max_workers, timeout_ms=20000, micro=micro) as e:
+                    micro_donate_min_p=donate_min_p, max_workers=max_workers, timeout_ms=20000,
+                    micro=micro) as e:
         for g in graphs:
             check(e, g)
             donations += e.stats()["donations"]
