@@ -122,6 +122,9 @@ constexpr size_t kHistWords = MCE_MAX_P + 2;   // global histogram entries
 constexpr size_t kIoBytes = sizeof(MceCtl) + (1 + kHistWords) * sizeof(u64);
 static_assert(sizeof(MceCtl) % sizeof(u64) == 0, "results follow the control block");
 constexpr int kMicroStack = 4096;              // frames per wavefront stack of the micro search
+// Tables other than micro ones are built by the split build: a root's rows are
+// dealt over several blocks, about this many (root, part) blocks per CU.
+constexpr int kSplitBlocksPerCu = 16;
 
 mce_status run_impl(mce_engine* e, int32_t n, int64_t nnz, const int32_t* row_ptr, const int32_t* col_idx,
                     const int32_t* roots, int32_t nroots, bool subset, void* stream) {
@@ -325,6 +328,12 @@ mce_status run_impl(mce_engine* e, int32_t n, int64_t nnz, const int32_t* row_pt
     bp.heap_words = heap_words;
     bp.tab_off = dp<u64>(e->taboff) + off.off[c];
     bp.status = &ctl->status;
+    if (!micro) {
+      // enough (root, part) blocks to fill the chip, at most one part per 64-row slab
+      const int nslab = std::max(1, (hctl->sub_maxr[var][c] + 63) / 64);
+      const int want = (kSplitBlocksPerCu * e->num_cu + counts[c] - 1) / counts[c];
+      bp.parts = std::max(1, std::min(want, nslab));
+    }
     if (timing) (void)hipEventRecord(e->ev[evi], s);
     if ((h = mce_launch_build(bp, e->num_cu * 32, s)) != hipSuccess) return hip_fail(e, h, "build launch");
     if (timing) (void)hipEventRecord(e->ev[evi + 1], s);

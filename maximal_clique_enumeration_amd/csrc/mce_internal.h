@@ -106,6 +106,7 @@ struct BuildParams {
   int W;                 // bitset words of the sub-class
   int mode;              // MCE_MODE_IP / MCE_MODE_IPX
   int micro;             // micro table: full rows plus the X column of every P member
+  int parts;             // > 0: split build, each root's 64-row slabs dealt over this many blocks
   u64* heap;
   u64 heap_words;
   const u64* tab_off;    // each root's table offset, as an exclusive prefix sum of table sizes that
@@ -131,6 +132,8 @@ hipError_t mce_launch_bucket(const int* roots, int nroots, const int* pcount, co
 int mce_scan_temp_words(int n);
 hipError_t mce_launch_scan(u64* a, int n, u64* tsum, hipStream_t s);
 
+// One wavefront per root (prm.parts == 0), or the split build: a head kernel for
+// the ids and hash terms, then a rows kernel over nroots * parts blocks.
 hipError_t mce_launch_build(const BuildParams& prm, int blocks, hipStream_t s);
 
 SearchLayout mce_search_layout(int sub, int mode, int pcap, int xcap, int rcap, bool force_hbm, bool counters);

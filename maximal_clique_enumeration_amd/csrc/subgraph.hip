@@ -13,139 +13,21 @@
 // root hash term, rows (row a = bit b set iff L[a] ~ P[b], local order = id
 // order, P first), p hash terms of the P members, p + x int32 ids.
 //
-// One 64-lane wavefront per root. A row is filled either by streaming the
-// member's CSR row and looking every neighbour up in P (sorted, in LDS), or, for
-// members of high degree, by probing each P member in that CSR row.
+// Two builds:
+//  - micro tables (|P|, |X| <= 64): one 64-lane wavefront per root, one lane per
+//    row;
+//  - every other table, the split build: a head kernel writes each root's
+//    header, ids and hash terms, then every root's rows, in slabs of 64, are
+//    dealt over several blocks, so that one root with tens of thousands of rows
+//    (X members of a hub in the full subgraph) is built by the whole chip.
+// A row is filled either by walking the member's CSR row and looking every
+// neighbour up in an LDS hash of P, or, for members of high degree, by probing
+// each P member in that CSR row.
 #include "mce_device.h"
 #include "mce_internal.h"
 
-__global__ __launch_bounds__(64) void k_build(BuildParams prm) {
-  __shared__ int s_pid[MCE_MAX_P];
-  __shared__ u64 s_row[MCE_MAX_P / 64];
-  const int lane = lane_id();
-  const int W = prm.W;
-  const int* __restrict__ rp = prm.rp;
-  const int* __restrict__ ci = prm.ci;
-  const int* __restrict__ rnd = prm.rnd;
-  for (int i = blockIdx.x; i < prm.nroots; i += gridDim.x) {
-    const int r = prm.roots[i];
-    const int a = rp[r], b = rp[r + 1];
-    const int rr = rnd[r];
-    // P = later neighbours into LDS (ascending id); count X
-    int np = 0, nx = 0;
-    for (int base = a; base < b; base += MCE_WAVE) {
-      const int e = base + lane;
-      const bool valid = e < b;
-      const int u = valid ? ci[e] : 0;
-      const bool lat = valid && order_after(rnd[u], u, rr, r);
-      const u64 lm = ballot(lat);
-      const u64 xm = ballot(valid && !lat);
-      if (lat) {
-        const int pos = np + mbcnt(lm);
-        if (pos < MCE_MAX_P) s_pid[pos] = u;
-      }
-      np += __popcll(lm);
-      nx += __popcll(xm);
-    }
-    if (np == 0 || np > 64 * W) {   // the host only sends 1 <= |P| <= 64 W here
-      if (lane == 0) atomicOr(prm.status, MCE_E_LIMIT);
-      continue;
-    }
-    const long long nrows = mce_table_rows(np, nx, prm.micro ? MCE_MODE_IPX : prm.mode);
-    const u64 words = prm.micro ? mce_micro_table_words(np, nx) : mce_table_words(np, nx, W, prm.mode);
-    const u64 off = uni(prm.tab_off[i]) - uni(prm.tab_off[0]);
-    if (off + words > prm.heap_words) {
-      if (lane == 0) atomicOr(prm.status, MCE_E_HEAP);
-      continue;
-    }
-    u64* T = prm.heap + off;
-    u64* rows = T + 3;
-    u64* xcol = rows + (size_t)nrows * W;   // micro tables only
-    u64* hvs = prm.micro ? xcol + np : xcol;
-    int* ids = (int*)(hvs + np);
-    if (lane == 0) {
-      T[0] = (u64)(u32)np | ((u64)(u32)nx << 32);
-      T[1] = (u64)(u32)r;
-      T[2] = mce_vertex_term(r);
-    }
-    __syncthreads();   // s_pid complete
-    for (int j = lane; j < np; j += MCE_WAVE) {
-      const int g = s_pid[j];
-      ids[j] = g;
-      hvs[j] = mce_vertex_term(g);
-    }
-    int xo = 0;
-    for (int base = a; base < b; base += MCE_WAVE) {
-      const int e = base + lane;
-      const bool valid = e < b;
-      const int u = valid ? ci[e] : 0;
-      const bool ear = valid && !order_after(rnd[u], u, rr, r);
-      const u64 xm = ballot(ear);
-      if (ear) ids[np + xo + mbcnt(xm)] = u;
-      xo += __popcll(xm);
-    }
-    __syncthreads();   // X ids in the table before the rows read them back
-    for (long long ra = 0; ra < nrows; ra++) {
-      const int g = ra < np ? s_pid[ra] : ids[ra];
-      const int ga = rp[g], gb = rp[g + 1];
-      const int gdeg = gb - ga;
-      if (gdeg <= 128 * W) {
-        // stream N(g) and look every neighbour up in P
-        if (lane < W) s_row[lane] = 0;
-        __syncthreads();
-        for (int base = ga; base < gb; base += MCE_WAVE) {
-          const int e = base + lane;
-          if (e < gb) {
-            const int u = ci[e];
-            int lo = 0, len = np;
-            while (len > 0) {
-              const int half = len >> 1;
-              if (s_pid[lo + half] < u) {
-                lo += half + 1;
-                len -= half + 1;
-              } else {
-                len = half;
-              }
-            }
-            if (lo < np && s_pid[lo] == u) atomicOr(&s_row[lo >> 6], 1ull << (lo & 63));
-          }
-        }
-        __syncthreads();
-        if (lane < W) rows[(size_t)ra * W + lane] = s_row[lane];
-        __syncthreads();
-      } else {
-        // probe every P member in N(g)
-        for (int w = 0; w < W; w++) {
-          const int j = w * 64 + lane;
-          const bool bit = j < np && j != ra && csr_range_has(ci, ga, gb, s_pid[j]);
-          const u64 word = ballot(bit);
-          if (lane == 0) rows[(size_t)ra * W + w] = word;
-        }
-      }
-    }
-    if (prm.micro) {
-      // micro table: X column of every P member (the transpose of the X rows)
-      __syncthreads();   // the X rows are in the table
-      u64 col = 0;
-      if (lane < np) {
-        for (int j = 0; j < nx; j++) col |= ((rows[np + j] >> lane) & 1ull) << j;
-        xcol[lane] = col;
-      }
-    }
-    __syncthreads();
-  }
-}
-
-// ------------------------------------------------------------------ narrow tables
-// Tables of |P| <= 64 W for W <= 4 (every micro table, and the narrow width
-// classes): one wavefront per root, one lane per row. P's ids go into an LDS
-// hash table (key = vertex id, value = local index), so a lane builds its row
-// by walking its vertex's CSR row and looking every neighbour up, all rows of a
-// 64-row slab at once; rows longer than BUILD_LANE_MAX edges are built instead
-// by probing each P member in that CSR row (binary search), one lane per P
-// member, several rows per pass when |P| is small.
-#define BUILD_LANE_MAX 48
-
+// ------------------------------------------------------------------ hash of P
+// LDS open-addressing hash (key = vertex id, value = local index) over P.
 template <int HB>
 __device__ __forceinline__ u32 build_hash(int u) {
   return ((u32)u * 0x9E3779B1u) >> (32 - HB);
@@ -163,10 +45,18 @@ __device__ __forceinline__ int build_lookup(const int* hk, const short* hv, int 
   return -1;
 }
 
-template <int W>
-__global__ __launch_bounds__(64) void k_build_narrow(BuildParams prm) {
-  constexpr int PMAX = 64 * W;
-  constexpr int HB = W == 1 ? 7 : (W == 2 ? 8 : 9);   // hash slots >= 2 PMAX
+// ------------------------------------------------------------------ micro tables
+// |P| <= 64 and |X| <= 64: one wavefront per root, one lane per row. P's ids go
+// into the LDS hash, so a lane builds its row by walking its vertex's CSR row
+// and looking every neighbour up; rows longer than BUILD_LANE_MAX edges are
+// built instead by probing each P member in that CSR row (binary search), one
+// lane per P member, several rows per pass when |P| is small. The table ends
+// with the X column of every P member (the transpose of the X rows).
+#define BUILD_LANE_MAX 48
+
+__global__ __launch_bounds__(64) void k_build_micro(BuildParams prm) {
+  constexpr int PMAX = MCE_MICRO_MAX;
+  constexpr int HB = 7;   // hash slots >= 2 PMAX
   __shared__ int s_pid[PMAX];
   __shared__ int s_hk[1 << HB];
   __shared__ short s_hv[1 << HB];
@@ -176,8 +66,6 @@ __global__ __launch_bounds__(64) void k_build_narrow(BuildParams prm) {
   const int* __restrict__ rp = prm.rp;
   const int* __restrict__ ci = prm.ci;
   const int* __restrict__ rnd = prm.rnd;
-  const bool micro = prm.micro != 0;
-  const int mode = micro ? MCE_MODE_IPX : prm.mode;
   for (int i = blockIdx.x; i < prm.nroots; i += gridDim.x) {
     const int r = prm.roots[i];
     const int a = rp[r], b = rp[r + 1];
@@ -194,12 +82,12 @@ __global__ __launch_bounds__(64) void k_build_narrow(BuildParams prm) {
       np += __popcll(lm);
       nx += __popcll(xm);
     }
-    if (np == 0 || np > PMAX || (micro && nx > MCE_MICRO_MAX)) {   // the host sends only such roots here
+    if (np == 0 || np > PMAX || nx > MCE_MICRO_MAX) {   // the host sends only such roots here
       if (lane == 0) atomicOr(prm.status, MCE_E_LIMIT);
       continue;
     }
-    const int nrows = (int)mce_table_rows(np, nx, mode);
-    const u64 words = micro ? mce_micro_table_words(np, nx) : mce_table_words(np, nx, W, mode);
+    const int nrows = np + nx;
+    const u64 words = mce_micro_table_words(np, nx);
     const u64 off = uni(prm.tab_off[i]) - uni(prm.tab_off[0]);
     if (off + words > prm.heap_words) {
       if (lane == 0) atomicOr(prm.status, MCE_E_HEAP);
@@ -207,8 +95,8 @@ __global__ __launch_bounds__(64) void k_build_narrow(BuildParams prm) {
     }
     u64* T = prm.heap + off;
     u64* rows = T + 3;
-    u64* xcol = rows + (size_t)nrows * W;   // micro tables only
-    u64* hvs = micro ? xcol + np : xcol;
+    u64* xcol = rows + nrows;
+    u64* hvs = xcol + np;
     int* ids = (int*)(hvs + np);
     if (lane == 0) {
       T[0] = (u64)(u32)np | ((u64)(u32)nx << 32);
@@ -249,9 +137,7 @@ __global__ __launch_bounds__(64) void k_build_narrow(BuildParams prm) {
         if (gb - ga > BUILD_LANE_MAX) {
           s_long[atomicAdd(&s_nlong, 1)] = t;
         } else {
-          u64 w[W];
-#pragma unroll
-          for (int q = 0; q < W; q++) w[q] = 0;
+          u64 w = 0;
           for (int e = ga; e < gb; e += 4) {
             int j[4];
 #pragma unroll
@@ -260,14 +146,10 @@ __global__ __launch_bounds__(64) void k_build_narrow(BuildParams prm) {
               j[z] = u >= 0 ? build_lookup<HB>(s_hk, s_hv, u) : -1;
             }
 #pragma unroll
-            for (int z = 0; z < 4; z++) {
-#pragma unroll
-              for (int q = 0; q < W; q++)
-                if (j[z] >= 64 * q && j[z] < 64 * (q + 1)) w[q] |= 1ull << (j[z] - 64 * q);
-            }
+            for (int z = 0; z < 4; z++)
+              if (j[z] >= 0) w |= 1ull << j[z];
           }
-#pragma unroll
-          for (int q = 0; q < W; q++) rows[(size_t)t * W + q] = w[q];
+          rows[t] = w;
         }
       }
       __syncthreads();
@@ -284,39 +166,248 @@ __global__ __launch_bounds__(64) void k_build_narrow(BuildParams prm) {
           ga = rp[g];
           gb = rp[g + 1];
         }
-        for (int w0 = 0; w0 < W; w0++) {
-          const int j = w0 * 64 + jj;
-          const bool found = tq >= 0 && j < np && csr_range_has(ci, ga, gb, s_pid[j]);
-          const u64 fm = ballot(found);
-          if (jj == 0 && tq >= 0) {
-            const u64 mask = npw >= 64 ? ~0ull : ((1ull << npw) - 1ull);
-            rows[(size_t)tq * W + w0] = (fm >> (q * npw)) & mask;
-          }
+        const bool found = tq >= 0 && jj < np && csr_range_has(ci, ga, gb, s_pid[jj]);
+        const u64 fm = ballot(found);
+        if (jj == 0 && tq >= 0) {
+          const u64 mask = npw >= 64 ? ~0ull : ((1ull << npw) - 1ull);
+          rows[tq] = (fm >> (q * npw)) & mask;
         }
       }
     }
-    if (micro) {
-      // X column of every P member: the X rows' bit of that member
-      __syncthreads();   // the X rows are in the table
-      if (lane < np) {
-        u64 col = 0;
-        for (int x2 = 0; x2 < nx; x2++) col |= ((rows[np + x2] >> lane) & 1ull) << x2;
-        xcol[lane] = col;
-      }
+    // X column of every P member: the X rows' bit of that member
+    __syncthreads();   // the X rows are in the table
+    if (lane < np) {
+      u64 col = 0;
+      for (int x2 = 0; x2 < nx; x2++) col |= ((rows[np + x2] >> lane) & 1ull) << x2;
+      xcol[lane] = col;
     }
     __syncthreads();
   }
 }
 
+// ------------------------------------------------------------------ split build
+// Head: one 256-thread block per root. The four wavefronts each take a quarter
+// of the root's CSR row; a first pass counts its P (later) and X (earlier)
+// members, a second writes them at their place in the table's id array.
+__global__ __launch_bounds__(256) void k_build_head(BuildParams prm) {
+  __shared__ int s_cnt[2][4];
+  const int lane = lane_id();
+  const int wv = (int)threadIdx.x >> 6;
+  const int* __restrict__ rp = prm.rp;
+  const int* __restrict__ ci = prm.ci;
+  const int* __restrict__ rnd = prm.rnd;
+  for (int i = blockIdx.x; i < prm.nroots; i += gridDim.x) {
+    const int r = prm.roots[i];
+    const int a = rp[r], b = rp[r + 1];
+    const int rr = rnd[r];
+    const int per = ((b - a + 4 * MCE_WAVE - 1) / (4 * MCE_WAVE)) * MCE_WAVE;
+    const int wa = min(b, a + wv * per), wb = min(b, wa + per);
+    int np = 0, nx = 0;
+    for (int base = wa; base < wb; base += MCE_WAVE) {
+      const int e = base + lane;
+      const bool valid = e < wb;
+      const int u = valid ? ci[e] : 0;
+      const bool lat = valid && order_after(rnd[u], u, rr, r);
+      np += __popcll(ballot(lat));
+      nx += __popcll(ballot(valid && !lat));
+    }
+    if (lane == 0) {
+      s_cnt[0][wv] = np;
+      s_cnt[1][wv] = nx;
+    }
+    __syncthreads();
+    int NP = 0, NX = 0, pp = 0, xp = 0;
+    for (int q = 0; q < 4; q++) {
+      if (q == wv) {
+        pp = NP;
+        xp = NX;
+      }
+      NP += s_cnt[0][q];
+      NX += s_cnt[1][q];
+    }
+    __syncthreads();   // s_cnt is read before the next root writes it
+    const u64 off = uni(prm.tab_off[i]) - uni(prm.tab_off[0]);
+    const u64 words = mce_table_words(NP, NX, prm.W, prm.mode);
+    const bool fits = NP >= 1 && NP <= 64 * prm.W;   // the host sends only such roots here
+    if (!fits || off + words > prm.heap_words) {
+      // header with p = 0: the rows kernel skips the root
+      if (threadIdx.x == 0) {
+        if (off + 3 <= prm.heap_words) prm.heap[off] = 0;
+        atomicOr(prm.status, fits ? MCE_E_HEAP : MCE_E_LIMIT);
+      }
+      continue;
+    }
+    u64* T = prm.heap + off;
+    const long long nrows = mce_table_rows(NP, NX, prm.mode);
+    u64* hvs = T + 3 + (size_t)nrows * prm.W;
+    int* ids = (int*)(hvs + NP);
+    if (threadIdx.x == 0) {
+      T[0] = (u64)(u32)NP | ((u64)(u32)NX << 32);
+      T[1] = (u64)(u32)r;
+      T[2] = mce_vertex_term(r);
+    }
+    for (int base = wa; base < wb; base += MCE_WAVE) {
+      const int e = base + lane;
+      const bool valid = e < wb;
+      const int u = valid ? ci[e] : 0;
+      const bool lat = valid && order_after(rnd[u], u, rr, r);
+      const u64 lm = ballot(lat), xm = ballot(valid && !lat);
+      if (lat) {
+        const int j = pp + mbcnt(lm);
+        ids[j] = u;
+        hvs[j] = mce_vertex_term(u);
+      } else if (valid) {
+        ids[NP + xp + mbcnt(xm)] = u;
+      }
+      pp += __popcll(lm);
+      xp += __popcll(xm);
+    }
+  }
+}
+
+// Rows: block (root i, part k) builds the slabs k, k + K, k + 2K, ... of root
+// i's table. P's ids are read back from the table into an LDS hash (id -> local
+// index). A slab's 64 CSR rows are streamed as one sequence: the wavefront reads
+// 64 consecutive entries at a time (coalesced within each CSR row), finds each
+// entry's row from the rows' degree prefix sums, and ORs the P members it finds
+// into the slab's rows in LDS. The slab's work is then set by its total degree,
+// not by its longest row. A row much longer than P is built instead by probing
+// every P member in it.
+#define SPLIT_STREAM_RATIO 2
+
+template <int W>
+__global__ __launch_bounds__(64) void k_build_rows(BuildParams prm) {
+  constexpr int PMAX = 64 * W;
+  constexpr int HB = W == 1 ? 7 : W == 2 ? 8 : W == 4 ? 9 : W == 8 ? 10 : W == 16 ? 11 : 12;   // 2^HB >= 2 PMAX
+  __shared__ int s_hk[1 << HB];
+  __shared__ short s_hv[1 << HB];
+  __shared__ int s_pre[MCE_WAVE];   // exclusive prefix sum of the slab rows' streamed degrees
+  __shared__ int s_ga[MCE_WAVE];    // their CSR row starts
+  __shared__ u64 s_slab[MCE_WAVE * W];
+  const int lane = lane_id();
+  const int* __restrict__ rp = prm.rp;
+  const int* __restrict__ ci = prm.ci;
+  const int mode = prm.mode;
+  const int K = prm.parts;
+  const long long items = (long long)prm.nroots * K;
+  int cur = -1;   // the root whose P is in LDS
+  for (long long it = blockIdx.x; it < items; it += gridDim.x) {
+    const int i = (int)(it / K), k = (int)(it % K);
+    const u64 off = uni(prm.tab_off[i]) - uni(prm.tab_off[0]);
+    if (off + 3 > prm.heap_words) continue;
+    u64* T = prm.heap + off;
+    const u64 hdr = uni(T[0]);
+    const int np = (int)(u32)hdr, nx = (int)(u32)(hdr >> 32);
+    if (np < 1 || np > PMAX) continue;   // the head kernel flagged this root
+    const int nrows = (int)mce_table_rows(np, nx, mode);
+    const int nslab = (nrows + MCE_WAVE - 1) / MCE_WAVE;
+    if (k >= nslab) continue;
+    if (off + mce_table_words(np, nx, W, mode) > prm.heap_words) continue;
+    u64* rows = T + 3;
+    const u64* hvs = rows + (size_t)nrows * W;
+    const int* ids = (const int*)(hvs + np);
+    if (i != cur) {
+      __syncthreads();   // the previous root's hash is no longer read
+      for (int h = lane; h < (1 << HB); h += MCE_WAVE) s_hk[h] = -1;
+      __syncthreads();
+      for (int j = lane; j < np; j += MCE_WAVE) {
+        const int u = ids[j];
+        u32 h = build_hash<HB>(u);
+        while (atomicCAS(&s_hk[h], -1, u) != -1) h = (h + 1u) & ((1u << HB) - 1u);
+        s_hv[h] = (short)j;
+      }
+      __syncthreads();
+      cur = i;
+    }
+    for (int slab = k; slab < nslab; slab += K) {
+      const int t0 = slab * MCE_WAVE;
+      const int t = t0 + lane;
+      const bool valid = t < nrows;
+      int ga = 0, d = 0;
+      if (valid) {
+        const int g = ids[t];
+        ga = rp[g];
+        d = rp[g + 1] - ga;
+      }
+      const bool probe = valid && d > SPLIT_STREAM_RATIO * np;
+      const int dd = valid && !probe ? d : 0;
+      int inc = dd;
+#pragma unroll
+      for (int o = 1; o < MCE_WAVE; o <<= 1) {
+        const int v = __shfl_up(inc, o);
+        if (lane >= o) inc += v;
+      }
+      const int D = uni(__shfl(inc, MCE_WAVE - 1));
+      s_pre[lane] = inc - dd;
+      s_ga[lane] = ga;
+      for (int q = lane; q < MCE_WAVE * W; q += MCE_WAVE) s_slab[q] = 0;
+      __syncthreads();
+      for (int base = 0; base < D; base += 4 * MCE_WAVE) {
+        int u[4], rr[4];
+#pragma unroll
+        for (int z = 0; z < 4; z++) {
+          const int x = base + z * MCE_WAVE + lane;
+          rr[z] = -1;
+          u[z] = -1;
+          if (x < D) {
+            int r = 0;   // the last row whose prefix is <= x (it has x - prefix < its degree)
+#pragma unroll
+            for (int step = MCE_WAVE / 2; step > 0; step >>= 1)
+              if (s_pre[r + step] <= x) r += step;
+            rr[z] = r;
+            u[z] = ci[s_ga[r] + (x - s_pre[r])];
+          }
+        }
+#pragma unroll
+        for (int z = 0; z < 4; z++) {
+          if (rr[z] >= 0) {
+            const int j = build_lookup<HB>(s_hk, s_hv, u[z]);
+            if (j >= 0) atomicOr(&s_slab[rr[z] * W + (j >> 6)], 1ull << (j & 63));
+          }
+        }
+      }
+      __syncthreads();
+      const u64 pm = ballot(probe);
+      const int nr = min(MCE_WAVE, nrows - t0);
+      u64* srow = rows + (size_t)t0 * W;
+      for (int q = lane; q < nr * W; q += MCE_WAVE)
+        if (!((pm >> (q / W)) & 1ull)) srow[q] = s_slab[q];
+      // rows much longer than P: probe every P member in the CSR row
+      for (u64 m = pm; m != 0; m &= m - 1) {
+        const int l = __builtin_ctzll(m);
+        const int gal = read_lane(ga, l);
+        const int gbl = gal + read_lane(d, l);
+        for (int w0 = 0; w0 < W; w0++) {
+          const int j = w0 * 64 + lane;
+          const bool found = j < np && csr_range_has(ci, gal, gbl, ids[j]);
+          const u64 fm = ballot(found);
+          if (lane == 0) srow[(size_t)l * W + w0] = fm;
+        }
+      }
+      __syncthreads();   // s_pre, s_ga and s_slab are rewritten by the next slab
+    }
+  }
+}
+
 hipError_t mce_launch_build(const BuildParams& prm, int blocks, hipStream_t s) {
-  const int nb = std::max(1, std::min(blocks, prm.nroots));
-  if (prm.micro || prm.W == 1)
-    hipLaunchKernelGGL(k_build_narrow<1>, dim3(nb), dim3(64), 0, s, prm);
-  else if (prm.W == 2)
-    hipLaunchKernelGGL(k_build_narrow<2>, dim3(nb), dim3(64), 0, s, prm);
-  else if (prm.W == 4)
-    hipLaunchKernelGGL(k_build_narrow<4>, dim3(nb), dim3(64), 0, s, prm);
-  else
-    hipLaunchKernelGGL(k_build, dim3(nb), dim3(64), 0, s, prm);
+  if (prm.micro) {
+    const int nb = std::max(1, std::min(blocks, prm.nroots));
+    hipLaunchKernelGGL(k_build_micro, dim3(nb), dim3(64), 0, s, prm);
+    return hipGetLastError();
+  }
+  if (prm.parts < 1) return hipErrorInvalidValue;
+  const int nh = std::max(1, std::min(blocks / 4, prm.nroots));
+  hipLaunchKernelGGL(k_build_head, dim3(nh), dim3(256), 0, s, prm);
+  const long long items = (long long)prm.nroots * prm.parts;
+  const int nb = (int)std::max(1LL, std::min((long long)blocks, items));
+  switch (prm.W) {
+    case 1: hipLaunchKernelGGL(k_build_rows<1>, dim3(nb), dim3(64), 0, s, prm); break;
+    case 2: hipLaunchKernelGGL(k_build_rows<2>, dim3(nb), dim3(64), 0, s, prm); break;
+    case 4: hipLaunchKernelGGL(k_build_rows<4>, dim3(nb), dim3(64), 0, s, prm); break;
+    case 8: hipLaunchKernelGGL(k_build_rows<8>, dim3(nb), dim3(64), 0, s, prm); break;
+    case 16: hipLaunchKernelGGL(k_build_rows<16>, dim3(nb), dim3(64), 0, s, prm); break;
+    case 32: hipLaunchKernelGGL(k_build_rows<32>, dim3(nb), dim3(64), 0, s, prm); break;
+    default: return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }

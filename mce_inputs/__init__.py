@@ -193,6 +193,31 @@ def random_small(n: int, p: float, seed: int) -> Graph:
     return from_edges(n, iu[keep], ju[keep], f"gnp{n}_{p}_{seed}")
 
 
+def hub_clique(core: int, hubs: int, leaves: int, frac: float, missing: int, seed: int) -> Graph:
+    """A near-clique with hubs: `core` vertices pairwise adjacent except for
+    `missing` random pairs; each of `hubs` hubs is adjacent to a random `frac` of
+    the core and to `leaves` leaves of its own. The leaves peel first and the hubs
+    before the core, so every core root's X holds hubs whose CSR rows are far
+    longer than its P. Ids are shuffled."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    iu, ju = np.triu_indices(core, 1)
+    keep = np.ones(iu.size, bool)
+    keep[rng.choice(iu.size, size=min(missing, iu.size), replace=False)] = False
+    us, vs = [iu[keep]], [ju[keep]]
+    nxt = core + hubs
+    for h in range(hubs):
+        nb = np.flatnonzero(rng.random(core) < frac)
+        us.append(np.full(nb.size, core + h))
+        vs.append(nb)
+        us.append(np.full(leaves, core + h))
+        vs.append(np.arange(nxt, nxt + leaves))
+        nxt += leaves
+    perm = rng.permutation(nxt)
+    u = perm[np.concatenate(us).astype(np.int64)]
+    v = perm[np.concatenate(vs).astype(np.int64)]
+    return from_edges(nxt, u, v, f"hubclique{core}_{hubs}_{leaves}_{seed}")
+
+
 # ---------------------------------------------------------------- benchmark families
 def erdos_renyi(n: int, p: float, seed: int) -> Graph:
     """G(n, p): every pair i<j independently with probability p.

@@ -111,6 +111,14 @@ def test_multipartite(eng, sizes):
     assert got.count == int(np.prod(sizes))
 
 
+@pytest.mark.parametrize("core", [300, 700, 1100])
+def test_hub_rows(eng, core):
+    """Core roots of widths 8, 16 and 32 words whose X holds hubs: the hub rows
+    (degree far above 2 |P|) are built by probing P members in the CSR row, the
+    core rows by streaming, each root's slabs over many blocks."""
+    check(eng, mi.hub_clique(core, 4, 3000, 0.7, 12, core))
+
+
 def test_er_2000(eng):
     """The small configuration: G(2000, 0.01), seed 1."""
     check(eng, mi.config_graph(0))
