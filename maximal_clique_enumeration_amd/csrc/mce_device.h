@@ -91,8 +91,7 @@ struct MceCtl {
   int rounds;
   int max_p;
   int max_x;
-  int min_deg;           // peel: smallest alive degree at a level start
-  int pad0;
+  int min_deg[2];        // peel: smallest degree in each remaining list (by list parity)
   u64 isolated;          // roots of degree 0
   u64 isolated_hash;     // sum of their clique hashes
   // per classification variant (subgraph mode, micro sub-class on/off) and
@@ -104,9 +103,14 @@ struct MceCtl {
   u64 sub_words[MCE_NVAR][MCE_NSUB];
   int sub_cursor[MCE_NSUB];
   int asize[2];          // peel: alive-list sizes (ping-pong)
-  int fsize[3];          // peel: frontier sizes (rotating: read, filled, being reset)
+  int fsize[3];          // peel: frontier sizes, one slot per step (rotating: read, filled, being reset)
   int bsize[3];          // peel: big-vertex frontier sizes (same rotation)
+  int bedge[3];          // peel: the big vertices' CSR row lengths summed (same rotation)
+  int asum[2];           // peel: each remaining list's CSR row lengths summed (by list parity)
   u32 bar_count;         // grid barrier: arrivals so far in the launch
+  u32 seg_gen;           // peel: segments of tiny rounds that block 0 has handed back
+  u32 seg_arrive;        // peel: blocks that started waiting for a segment (summed over segments)
+  int seg_state[12];     // peel: the state block 0 hands back (result, list, frontier, level, round, slot, sums)
   u64 t_run;             // wall-clock tick at the start of the peel: the run's time limit counts from it
   u64 peel_ticks[4];     // block 0 of the peel: barrier waits, level passes, round work, total
 };

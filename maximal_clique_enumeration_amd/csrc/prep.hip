@@ -128,32 +128,51 @@ __device__ __forceinline__ void pmin(int* p, int v) {
 #define PEEL_THREADS 1024
 
 // Appends the lanes with `in` set to the next frontier: the regular list, or
-// the big list for vertices of degree > PEEL_BIG. Whole wave.
+// the big list for vertices of degree > PEEL_BIG, whose CSR row lengths are
+// also summed (the rows of the others are short by definition). Whole wave.
 template <int S>
 __device__ __forceinline__ void peel_append(bool in, int v, const int* __restrict__ rp, int* fr, int* fsize,
-                                            int* bfr, int* bsize) {
+                                            int* bfr, int* bsize, int* bedge) {
   const int lane = lane_id();
-  const bool big = in && rp[v + 1] - rp[v] > PEEL_BIG;
+  const int len = in ? rp[v + 1] - rp[v] : 0;
+  const bool big = len > PEEL_BIG;
   const u64 mr = ballot(in && !big);
   const u64 mb = ballot(big);
   int pr = 0, pb = 0;
   if (lane == 0 && mr) pr = padd<S>(fsize, __popcll(mr));
-  if (lane == 0 && mb) pb = padd<S>(bsize, __popcll(mb));
+  if (mb) {
+    const u32 es = wave_sum_u32(big ? (u32)len : 0u);   // distinct rows: at most nnz
+    if (lane == 0) {
+      pb = padd<S>(bsize, __popcll(mb));
+      padd<S>(bedge, (int)es);
+    }
+  }
   pr = read_lane(pr, 0);
   pb = read_lane(pb, 0);
   if (in && !big) pst<S>(&fr[pr + mbcnt(mr)], v);
   if (big) pst<S>(&bfr[pb + mbcnt(mb)], v);
 }
 
+// A neighbour's degree is taken only while it is still present. Its round is
+// read with a plain load: a stale copy can only show -1 (present), and taking a
+// degree from a removed vertex is harmless (it has degree <= k at its removal
+// and only loses more, so it never falls from k + 1 again; its degree is not
+// read any more). Skipping the removed ones saves about half of the returning
+// atomics, which bound the peel.
+#ifndef PEEL_FILTER
+#define PEEL_FILTER 1
+#endif
+__device__ __forceinline__ bool peel_present(const int* rnd, int u) {
+  return !PEEL_FILTER || rnd[u] < 0;
+}
+
 // One span of a removed vertex's row [base, min(base + PEEL_SPAN, b)): take one
-// degree from each neighbour (all four 64-edge pieces in flight together). A
-// neighbour that falls from k + 1 to k joins the next round. The decrement is
-// unconditional: a vertex already removed has degree <= k at its removal and
-// only loses more, so it never falls from k + 1 again; its degree is not read.
+// degree from each present neighbour (all four 64-edge pieces in flight
+// together). A neighbour that falls from k + 1 to k joins the next round.
 template <int S>
 __device__ __forceinline__ void peel_span(int base, int b, int k, const int* __restrict__ rp,
-                                          const int* __restrict__ ci, int* deg, int* nx, int* nxs, int* bnx,
-                                          int* bnxs) {
+                                          const int* __restrict__ ci, const int* rnd, int* deg, int* nx, int* nxs,
+                                          int* bnx, int* bnxs, int* bnxe) {
   const int lane = lane_id();
   int u[4];
   bool ok[4];
@@ -163,12 +182,14 @@ __device__ __forceinline__ void peel_span(int base, int b, int k, const int* __r
     ok[q] = e < b;
     u[q] = ok[q] ? ci[e] : 0;
   }
+#pragma unroll
+  for (int q = 0; q < 4; q++) ok[q] = ok[q] && peel_present(rnd, u[q]);
   bool joins[4];
 #pragma unroll
   for (int q = 0; q < 4; q++) joins[q] = ok[q] && padd<S>(&deg[u[q]], -1) == k + 1;
 #pragma unroll
   for (int q = 0; q < 4; q++) {
-    if (ballot(joins[q])) peel_append<S>(joins[q], u[q], rp, nx, nxs, bnx, bnxs);
+    if (ballot(joins[q])) peel_append<S>(joins[q], u[q], rp, nx, nxs, bnx, bnxs, bnxe);
   }
 }
 
@@ -187,6 +208,8 @@ struct PeelArgs {
   int* bfront1;
   MceCtl* ctl;
   u64 deadline;
+  int* sc;      // block 0's LDS counter slots while it runs a segment (12)
+  int4* sfr;   // block 0's LDS frontier lists while it runs a segment: (v, row start, row end)
   // ping-pong buffers by parity (selects, not indexed arrays: no scratch memory)
   __device__ int* alive(int i) const { return (i & 1) ? alive1 : alive0; }
   __device__ int* front(int i) const { return (i & 1) ? front1 : front0; }
@@ -195,8 +218,12 @@ struct PeelArgs {
 
 struct PeelState {
   int cur, nf, nb, k, r, na;
+  int ph;               // slot of the pending frontier's sizes
+  int fe;               // the pending frontier's CSR row lengths summed
+  int ae;               // the remaining list's CSR row lengths summed (at its level pass)
   bool level_known;     // the level's remaining list and k are known, its first round is not built
   u32 epoch;            // grid barriers passed (thread 0 of each block)
+  u32 seg;              // segments of tiny rounds handed from the grid to block 0
   u64 tb, tl, tr, tm;   // first block's thread 0: barrier, level, round ticks; last mark
 };
 
@@ -207,57 +234,130 @@ struct PeelState {
     st.tm = t;                        \
   }
 
-// Rounds of the peel at scope S (see k_peel). `wave`/`nwaves` index the waves
-// taking part. Returns 0 when every vertex is ordered, 1 when the remaining
-// list has shrunk to PEEL_SOLO vertices or fewer (grid phase only), -1 on a
-// time-out.
-template <int S, bool SOLO>
+// Who runs the rounds: the whole grid at agent scope, or block 0 alone at
+// workgroup scope once few vertices remain (the others left). Tiny rounds in
+// between are run by block 0 too (peel_seg).
+#define PEEL_GRID 0
+#define PEEL_ALONE 2
+// What peel_rounds returns.
+#define PEEL_DONE 0
+#define PEEL_TIMEOUT (-1)
+#define PEEL_TO_ALONE 1   // at most PEEL_SOLO vertices with PEEL_SOLO_EDGES edges remain
+#define PEEL_TO_SEG 2     // the next round removes at most PEEL_TINY vertices, big ones with PEEL_SEG_EDGES edges
+#define PEEL_TO_GRID 3    // block 0 hands back a larger round or a level pass
+#ifndef PEEL_TINY
+#define PEEL_TINY 32
+#endif
+static_assert(PEEL_TINY <= MCE_WAVE, "a segment round's frontier fits one wavefront's lanes");
+#ifndef PEEL_SEG_EDGES
+#define PEEL_SEG_EDGES 16384
+#endif
+#ifndef PEEL_SOLO_EDGES
+#define PEEL_SOLO_EDGES 262144
+#endif
+__device__ __forceinline__ bool peel_few_left(const PeelState& st) {
+  return st.na <= PEEL_SOLO && st.ae <= PEEL_SOLO_EDGES;
+}
+
+// Rounds of the peel (see k_peel). `wave`/`nwaves` index the waves taking part.
+//
+// Frontier sizes rotate over three slots, one step (level pass, first-round
+// scan or round: the work between two barriers) at a time. The step after slot
+// ph was filled appends the next frontier to slot ph + 1 and clears slot
+// ph + 2. A barrier lets blocks go at different times, so a slow block may
+// still be reading slot ph while a fast one works on the next step; slot ph + 2
+// was last read before the previous barrier, which every block has passed.
+// The remaining-list sizes and minima are kept per list parity for the same
+// reason: they are reset one level after they were read.
+template <int S, int MODE>
 __device__ int peel_rounds(const PeelArgs& A, PeelState& st, int wave, int nwaves, bool timer) {
   const int lane = lane_id();
-  const bool lead = SOLO ? threadIdx.x == 0 : (blockIdx.x == 0 && threadIdx.x == 0);
+  constexpr bool BLOCK = MODE != PEEL_GRID;   // block 0 alone: workgroup barriers
+  const bool lead = BLOCK ? threadIdx.x == 0 : (blockIdx.x == 0 && threadIdx.x == 0);
   MceCtl* ctl = A.ctl;
   const int* rp = A.rp;
+  int* fs = ctl->fsize;
+  int* bs = ctl->bsize;
+  int* be = ctl->bedge;
   for (;;) {
     if (st.nf == 0 && st.nb == 0) {
       if (!st.level_known) {
-      // new level: compact the remaining list and find the smallest remaining degree
-      const int* src = A.alive(st.cur);
-      int* dst = A.alive(st.cur ^ 1);
-      int mn = 0x7FFFFFFF;
-      for (int base = wave * MCE_WAVE; base < st.na; base += nwaves * MCE_WAVE) {
-        const int i = base + lane;
-        bool keep = false;
-        int v = 0;
-        if (i < st.na) {
-          v = pld<S>(&src[i]);
-          keep = pld<S>(&A.rnd[v]) < 0;
-          if (keep) mn = min(mn, pld<S>(&A.deg[v]));
+        // New level: compact the remaining list and find the smallest remaining
+        // degree. Every remaining vertex has degree > k, so the next level is
+        // k + 1 exactly when some vertex has degree k + 1: those vertices, the
+        // level's first round, are collected in the same pass.
+        const int p1 = (st.ph + 1) % 3, p2 = (st.ph + 2) % 3;
+        if (lead) {
+          pst<S>(&fs[p2], 0);
+          pst<S>(&bs[p2], 0);
+          pst<S>(&be[p2], 0);
         }
-        const u64 m = ballot(keep);
-        int pos = 0;
-        if (lane == 0 && m) pos = padd<S>(&ctl->asize[st.cur ^ 1], __popcll(m));
-        pos = read_lane(pos, 0);
-        if (keep) pst<S>(&dst[pos + mbcnt(m)], v);
-      }
-      const int wmn = wave_min_i32_nonneg(mn);
-      if (lane == 0 && wmn != 0x7FFFFFFF) pmin<S>(&ctl->min_deg, wmn);
-      PEEL_MARK(tl);
-      grid_sync(ctl, A.deadline, st.epoch, SOLO);
-      PEEL_MARK(tb);
-      st.cur ^= 1;
-      const u32 status = ld_relaxed(&ctl->status);
-      st.na = pld<S>(&ctl->asize[st.cur]);
-      const int kmin = pld<S>(&ctl->min_deg);   // no remaining vertex: k stays the degeneracy
-      if (status & MCE_E_TIMEOUT) return -1;
-      if (st.na == 0) return 0;
-      st.k = kmin;
-      if (!SOLO && gridDim.x > 1 && st.na <= PEEL_SOLO) {
-        st.level_known = true;
-        return 1;
-      }
+        const int* src = A.alive(st.cur);
+        int* dst = A.alive(st.cur ^ 1);
+        const int kn = st.k + 1;
+        // the kept rows' lengths decide whether block 0 may finish alone; they
+        // cost a gather per vertex, so they are summed only once the list is short
+        const bool sum_rows = st.na <= 8 * PEEL_SOLO;
+        int mn = 0x7FFFFFFF;
+        u32 rows = 0;   // CSR row lengths of the kept vertices (at most nnz in all)
+        for (int base = wave * MCE_WAVE; base < st.na; base += nwaves * MCE_WAVE) {
+          const int i = base + lane;
+          bool keep = false, first = false;
+          int v = 0;
+          if (i < st.na) {
+            v = pld<S>(&src[i]);
+            keep = pld<S>(&A.rnd[v]) < 0;
+            if (keep) {
+              const int dv = pld<S>(&A.deg[v]);
+              mn = min(mn, dv);
+              first = dv <= kn;
+              if (sum_rows) rows += (u32)(rp[v + 1] - rp[v]);
+            }
+          }
+          const u64 m = ballot(keep);
+          int pos = 0;
+          if (lane == 0 && m) pos = padd<S>(&ctl->asize[st.cur ^ 1], __popcll(m));
+          pos = read_lane(pos, 0);
+          if (keep) pst<S>(&dst[pos + mbcnt(m)], v);
+          if (ballot(first))
+            peel_append<S>(first, v, rp, A.front(st.r), &fs[p1], A.bfront(st.r), &bs[p1], &be[p1]);
+        }
+        const int wmn = wave_min_i32_nonneg(mn);
+        if (lane == 0 && wmn != 0x7FFFFFFF) pmin<S>(&ctl->min_deg[st.cur ^ 1], wmn);
+        if (sum_rows) {
+          const u32 wrows = wave_sum_u32(rows);
+          if (lane == 0 && wrows) padd<S>(&ctl->asum[st.cur ^ 1], (int)wrows);
+        }
+        PEEL_MARK(tl);
+        grid_sync(ctl, A.deadline, st.epoch, BLOCK);
+        PEEL_MARK(tb);
+        st.cur ^= 1;
+        st.ph = p1;
+        const u32 status = ld_relaxed(&ctl->status);
+        st.na = pld<S>(&ctl->asize[st.cur]);
+        const int kmin = pld<S>(&ctl->min_deg[st.cur]);   // no remaining vertex: k stays the degeneracy
+        st.ae = sum_rows ? pld<S>(&ctl->asum[st.cur]) : 0x7FFFFFFF;
+        st.nf = pld<S>(&fs[p1]);
+        st.nb = pld<S>(&bs[p1]);
+        st.fe = pld<S>(&be[p1]);
+        if (status & MCE_E_TIMEOUT) return PEEL_TIMEOUT;
+        if (st.na == 0) return PEEL_DONE;
+        const bool built = st.nf + st.nb > 0;   // then kmin == k + 1
+        st.k = built ? kn : kmin;
+        if (MODE == PEEL_GRID && gridDim.x > 1 && peel_few_left(st)) {
+          st.level_known = !built;
+          return PEEL_TO_ALONE;
+        }
+        if (built) continue;
       }
       st.level_known = false;
       // the level's first round: every remaining vertex of degree <= k
+      const int p1 = (st.ph + 1) % 3, p2 = (st.ph + 2) % 3;
+      if (lead) {
+        pst<S>(&fs[p2], 0);
+        pst<S>(&bs[p2], 0);
+        pst<S>(&be[p2], 0);
+      }
       const int* al = A.alive(st.cur);
       for (int base = wave * MCE_WAVE; base < st.na; base += nwaves * MCE_WAVE) {
         const int i = base + lane;
@@ -267,33 +367,39 @@ __device__ int peel_rounds(const PeelArgs& A, PeelState& st, int wave, int nwave
           v = pld<S>(&al[i]);
           in = pld<S>(&A.deg[v]) <= st.k;
         }
-        peel_append<S>(in, v, rp, A.front(st.r), &ctl->fsize[st.r % 3], A.bfront(st.r),
-                       &ctl->bsize[st.r % 3]);
+        peel_append<S>(in, v, rp, A.front(st.r), &fs[p1], A.bfront(st.r), &bs[p1], &be[p1]);
       }
       PEEL_MARK(tl);
-      grid_sync(ctl, A.deadline, st.epoch, SOLO);
+      grid_sync(ctl, A.deadline, st.epoch, BLOCK);
       PEEL_MARK(tb);
+      st.ph = p1;
       const u32 status2 = ld_relaxed(&ctl->status);
-      st.nf = pld<S>(&ctl->fsize[st.r % 3]);
-      st.nb = pld<S>(&ctl->bsize[st.r % 3]);
-      if (status2 & MCE_E_TIMEOUT) return -1;
+      st.nf = pld<S>(&fs[p1]);
+      st.nb = pld<S>(&bs[p1]);
+      st.fe = pld<S>(&be[p1]);
+      if (status2 & MCE_E_TIMEOUT) return PEEL_TIMEOUT;
     }
+    if (MODE == PEEL_GRID && gridDim.x > 1 && st.nf + st.nb <= PEEL_TINY && st.fe <= PEEL_SEG_EDGES)
+      return PEEL_TO_SEG;
     // round r: remove the frontier, take one degree from each neighbour
     const int r = st.r, k = st.k;
+    const int p1 = (st.ph + 1) % 3, p2 = (st.ph + 2) % 3;
     if (lead) {
-      // counters nobody reads any more: the frontier sizes read two rounds ago,
-      // the old remaining-list size and the level's minimum
-      pst<S>(&ctl->fsize[(r + 2) % 3], 0);
-      pst<S>(&ctl->bsize[(r + 2) % 3], 0);
+      pst<S>(&fs[p2], 0);
+      pst<S>(&bs[p2], 0);
+      pst<S>(&be[p2], 0);
+      // the other list's size, row sum and minimum were read a level ago
       pst<S>(&ctl->asize[st.cur ^ 1], 0);
-      pst<S>(&ctl->min_deg, 0x7FFFFFFF);
+      pst<S>(&ctl->asum[st.cur ^ 1], 0);
+      pst<S>(&ctl->min_deg[st.cur ^ 1], 0x7FFFFFFF);
     }
     const int* fr = A.front(r);
     const int* bfr = A.bfront(r);
     int* nx = A.front(r + 1);
-    int* nxs = &ctl->fsize[(r + 1) % 3];
+    int* nxs = &fs[p1];
     int* bnx = A.bfront(r + 1);
-    int* bnxs = &ctl->bsize[(r + 1) % 3];
+    int* bnxs = &bs[p1];
+    int* bnxe = &be[p1];
     // vertices of small degree: one wave each
     for (int i = wave; i < st.nf; i += nwaves) {
       const int v = pld<S>(&fr[i]);
@@ -302,7 +408,7 @@ __device__ int peel_rounds(const PeelArgs& A, PeelState& st, int wave, int nwave
         A.core[v] = k;
       }
       const int a = rp[v], b = rp[v + 1];
-      for (int base = a; base < b; base += PEEL_SPAN) peel_span<S>(base, b, k, rp, A.ci, A.deg, nx, nxs, bnx, bnxs);
+      for (int base = a; base < b; base += PEEL_SPAN) peel_span<S>(base, b, k, rp, A.ci, A.rnd, A.deg, nx, nxs, bnx, bnxs, bnxe);
     }
     // vertices of large degree: their spans are dealt round-robin to all waves
     for (int j0 = 0; j0 < st.nb; j0 += MCE_WAVE) {
@@ -322,18 +428,267 @@ __device__ int peel_rounds(const PeelArgs& A, PeelState& st, int wave, int nwave
         }
         const int nsp = (b - a + PEEL_SPAN - 1) / PEEL_SPAN;
         for (int c = (wave - j % nwaves + nwaves) % nwaves; c < nsp; c += nwaves)
-          peel_span<S>(a + c * PEEL_SPAN, b, k, rp, A.ci, A.deg, nx, nxs, bnx, bnxs);
+          peel_span<S>(a + c * PEEL_SPAN, b, k, rp, A.ci, A.rnd, A.deg, nx, nxs, bnx, bnxs, bnxe);
       }
     }
     PEEL_MARK(tr);
-    grid_sync(ctl, A.deadline, st.epoch, SOLO);
+    grid_sync(ctl, A.deadline, st.epoch, BLOCK);
     PEEL_MARK(tb);
+    st.ph = p1;
     const u32 status = ld_relaxed(&ctl->status);
     st.nf = pld<S>(nxs);
     st.nb = pld<S>(bnxs);
+    st.fe = pld<S>(bnxe);
     st.r++;
-    if (status & MCE_E_TIMEOUT) return -1;
+    if (status & MCE_E_TIMEOUT) return PEEL_TIMEOUT;
   }
+}
+
+// Block 0's workgroup barrier over LDS only: its global stores (rounds and core
+// numbers, spilled frontier entries) are not waited for until it hands back.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// A segment of tiny rounds, run by block 0 while the other blocks wait. The
+// frontier (vertices of any degree) is kept in LDS as (v, row start, row end),
+// its counts in LDS slots (the same three-slot rotation as the grid's); the
+// rows of a round are cut into 64-edge pieces dealt over all of block 0's
+// waves, so that a round of a few thousand edges takes about one dependent
+// chain of memory operations. The only global operations are the edge loads,
+// the degree decrements, the row bounds of the vertices that join the next
+// round, and stores nobody reads before the hand-back; joiners past the first
+// PEEL_TINY go straight to the global lists. Returns PEEL_TO_GRID (a larger
+// round, whose LDS entries it has moved to the global lists, or a level pass)
+// or PEEL_TO_ALONE.
+__device__ int peel_seg(const PeelArgs& A, PeelState& st, int wave, int nwaves, bool timer) {
+  __shared__ int s_split[2];
+  const int lane = lane_id();
+  const int* __restrict__ rp = A.rp;
+  const int* __restrict__ ci = A.ci;
+  // LDS slots: entries of the LDS list, their row lengths summed, and joiners
+  // past the list that went to the global small / big lists
+  int* c_n = A.sc;
+  int* c_e = A.sc + 3;
+  int* c_gs = A.sc + 6;
+  int* c_gb = A.sc + 9;
+  {
+    const int* fr = A.front(st.r);
+    const int* bfr = A.bfront(st.r);
+    const int tot = st.nf + st.nb;
+    if (threadIdx.x < 12) A.sc[threadIdx.x] = 0;
+    lds_barrier();
+    for (int i = threadIdx.x; i < tot; i += blockDim.x) {
+      const int v = i < st.nf ? pld<SA>(&fr[i]) : pld<SA>(&bfr[i - st.nf]);
+      const int a = rp[v], b = rp[v + 1];
+      A.sfr[i] = make_int4(v, a, b, 0);
+      if (b - a > PEEL_BIG) atomicAdd(&A.sc[3], b - a);   // big rows' lengths, in slot 0 of the edge count
+    }
+    lds_barrier();
+    st.fe = A.sc[3];
+    if (st.fe > PEEL_SEG_EDGES) return PEEL_TO_GRID;   // rows too long: the grid takes the round
+    st.nf = tot;   // in a segment nf counts the LDS entries, of any degree
+    st.nb = 0;
+  }
+  int lp = 0;
+  for (int j = 0;; j++) {
+    const int r = st.r, k = st.k;
+    const int p1 = (lp + 1) % 3, p2 = (lp + 2) % 3;
+    if (threadIdx.x == 0) {
+      c_n[p2] = 0;
+      c_e[p2] = 0;
+      c_gs[p2] = 0;
+      c_gb[p2] = 0;
+    }
+    // the two LDS lists alternate by round (selects: no indexed private array)
+    const int4* cur = (j & 1) ? A.sfr + PEEL_TINY : A.sfr;
+    int4* nxt = (j & 1) ? A.sfr : A.sfr + PEEL_TINY;
+    int* gnx = A.front(r + 1);
+    int* gbnx = A.bfront(r + 1);
+    // lane t of every wave holds entry t (nf <= PEEL_TINY <= 64); the entries'
+    // rows are cut into 64-edge pieces, dealt round-robin over the waves
+    int4 e = make_int4(0, 0, 0, 0);
+    if (lane < st.nf) e = cur[lane];
+    const int cnt = lane < st.nf ? (e.z - e.y + MCE_WAVE - 1) / MCE_WAVE : 0;
+    int incl = cnt;
+#pragma unroll
+    for (int o = 1; o < MCE_WAVE; o <<= 1) {
+      const int t = __shfl_up(incl, o);
+      if (lane >= o) incl += t;
+    }
+    const int total = read_lane(incl, MCE_WAVE - 1);
+    if (wave == 0 && lane < st.nf) {
+      pst<SA>(&A.rnd[e.x], r);
+      A.core[e.x] = k;
+    }
+    for (int p0 = wave; p0 < total; p0 += 4 * nwaves) {
+      int u[4];
+      bool ok[4], joins[4];
+#pragma unroll
+      for (int q = 0; q < 4; q++) {
+        const int pc = p0 + q * nwaves;
+        ok[q] = false;
+        u[q] = 0;
+        if (pc < total) {
+          const int t = __popcll(ballot(incl <= pc));   // the entry holding piece pc
+          const int first = read_lane(incl, t) - read_lane(cnt, t);
+          const int ed = read_lane(e.y, t) + (pc - first) * MCE_WAVE + lane;
+          ok[q] = ed < read_lane(e.z, t);
+          u[q] = ok[q] ? ci[ed] : 0;
+        }
+      }
+#pragma unroll
+      for (int q = 0; q < 4; q++) ok[q] = ok[q] && peel_present(A.rnd, u[q]);
+#pragma unroll
+      for (int q = 0; q < 4; q++) joins[q] = ok[q] && padd<SA>(&A.deg[u[q]], -1) == k + 1;
+#pragma unroll
+      for (int q = 0; q < 4; q++) {
+        if (!ballot(joins[q])) continue;
+        int a = 0, b = 0;
+        if (joins[q]) {
+          a = rp[u[q]];
+          b = rp[u[q] + 1];
+        }
+        const u64 mj = ballot(joins[q]);
+        int pos = 0;
+        if (lane == 0) pos = atomicAdd(&c_n[p1], __popcll(mj));
+        pos = read_lane(pos, 0) + mbcnt(mj);
+        const bool inl = joins[q] && pos < PEEL_TINY;
+        if (inl) nxt[pos] = make_int4(u[q], a, b, 0);
+        const u32 le = wave_sum_u32(inl && b - a > PEEL_BIG ? (u32)(b - a) : 0u);
+        if (lane == 0 && le) atomicAdd(&c_e[p1], (int)le);
+        const bool ov = joins[q] && !inl;   // past the LDS list: straight to the global lists
+        if (ballot(ov)) {
+          const bool big = ov && b - a > PEEL_BIG;
+          const u64 ms = ballot(ov && !big), mb = ballot(big);
+          int ps = 0, pb = 0;
+          if (lane == 0 && ms) ps = atomicAdd(&c_gs[p1], __popcll(ms));
+          if (lane == 0 && mb) pb = atomicAdd(&c_gb[p1], __popcll(mb));
+          ps = read_lane(ps, 0);
+          pb = read_lane(pb, 0);
+          if (ov && !big) pst<SA>(&gnx[ps + mbcnt(ms)], u[q]);
+          if (big) pst<SA>(&gbnx[pb + mbcnt(mb)], u[q]);
+        }
+      }
+    }
+    PEEL_MARK(tr);
+    lds_barrier();
+    PEEL_MARK(tb);
+    const int tot = c_n[p1];
+    const int gs = c_gs[p1], gb = c_gb[p1];
+    st.fe = c_e[p1];
+    st.r++;
+    lp = p1;
+    if (tot == 0) {
+      st.nf = 0;
+      st.nb = 0;
+      return peel_few_left(st) ? PEEL_TO_ALONE : PEEL_TO_GRID;
+    }
+    if (tot > PEEL_TINY || st.fe > PEEL_SEG_EDGES) {
+      // the grid takes this round: the LDS entries join the global lists after the spilled ones
+      if (wave == 0) {
+        const bool valid = lane < min(tot, PEEL_TINY);
+        const int4 e2 = valid ? nxt[lane] : make_int4(0, 0, 0, 0);
+        const bool big = valid && e2.z - e2.y > PEEL_BIG;
+        const u64 ms = ballot(valid && !big), mb = ballot(big);
+        if (valid && !big) pst<SA>(&gnx[gs + mbcnt(ms)], e2.x);
+        if (big) pst<SA>(&gbnx[gb + mbcnt(mb)], e2.x);
+        if (lane == 0) {
+          s_split[0] = gs + __popcll(ms);
+          s_split[1] = gb + __popcll(mb);
+        }
+      }
+      lds_barrier();
+      st.nf = s_split[0];
+      st.nb = s_split[1];
+      return PEEL_TO_GRID;
+    }
+    st.nf = tot;
+    st.nb = 0;
+  }
+}
+
+// Block 0 hands a segment back (every thread of block 0 calls this): its stores
+// complete, then, once
+// every waiting block has arrived (and so has read what the barrier before the
+// segment published), the control block's counters are set for the grid's next
+// step, then the state goes out, then the generation counter.
+__device__ int peel_hand_back(MceCtl* ctl, const PeelState& st, int res, u64 deadline) {
+  __shared__ int s_res;
+  wait_stores_complete();
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const u32 want = st.seg * (gridDim.x - 1);
+    u32 spins = 0;
+    while (__hip_atomic_load(&ctl->seg_arrive, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < want) {
+      __builtin_amdgcn_s_sleep(1);
+      if ((++spins & 1023u) == 0 && past_deadline(deadline)) {   // a block left on a time-out
+        atomicOr(&ctl->status, MCE_E_TIMEOUT);
+        res = PEEL_TIMEOUT;
+        break;
+      }
+    }
+    for (int i = 0; i < 3; i++) {
+      pst<SA>(&ctl->fsize[i], 0);
+      pst<SA>(&ctl->bsize[i], 0);
+      pst<SA>(&ctl->bedge[i], 0);
+    }
+    pst<SA>(&ctl->asize[st.cur ^ 1], 0);
+    pst<SA>(&ctl->asum[st.cur ^ 1], 0);
+    pst<SA>(&ctl->min_deg[st.cur ^ 1], 0x7FFFFFFF);
+    pst<SA>(&ctl->seg_state[0], res);
+    pst<SA>(&ctl->seg_state[1], st.cur);
+    pst<SA>(&ctl->seg_state[2], st.nf);
+    pst<SA>(&ctl->seg_state[3], st.nb);
+    pst<SA>(&ctl->seg_state[4], st.k);
+    pst<SA>(&ctl->seg_state[5], st.r);
+    pst<SA>(&ctl->seg_state[6], st.na);
+    pst<SA>(&ctl->seg_state[7], st.level_known ? 1 : 0);
+    pst<SA>(&ctl->seg_state[8], st.ph);
+    pst<SA>(&ctl->seg_state[9], st.fe);
+    pst<SA>(&ctl->seg_state[10], st.ae);
+    wait_stores_complete();
+    __hip_atomic_store(&ctl->seg_gen, st.seg, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    s_res = res;
+  }
+  __syncthreads();
+  return s_res;
+}
+
+// The other blocks while block 0 runs a segment: arrive, wait for its
+// hand-back and take over its state. Returns what block 0 handed back
+// (PEEL_TO_GRID: go on with the grid).
+__device__ int peel_wait(MceCtl* ctl, PeelState& st, u64 deadline) {
+  __shared__ int s_late;
+  if (threadIdx.x == 0) {
+    __hip_atomic_fetch_add(&ctl->seg_arrive, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    u32 spins = 0;
+    s_late = 0;
+    while (__hip_atomic_load(&ctl->seg_gen, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < st.seg) {
+      __builtin_amdgcn_s_sleep(2);
+      if ((++spins & 1023u) == 0 && past_deadline(deadline)) {
+        atomicOr(&ctl->status, MCE_E_TIMEOUT);
+        s_late = 1;
+        break;
+      }
+    }
+  }
+  __syncthreads();
+  if (s_late) return PEEL_TIMEOUT;
+  const int res = pld<SA>(&ctl->seg_state[0]);
+  st.cur = pld<SA>(&ctl->seg_state[1]);
+  st.nf = pld<SA>(&ctl->seg_state[2]);
+  st.nb = pld<SA>(&ctl->seg_state[3]);
+  st.k = pld<SA>(&ctl->seg_state[4]);
+  st.r = pld<SA>(&ctl->seg_state[5]);
+  st.na = pld<SA>(&ctl->seg_state[6]);
+  st.level_known = pld<SA>(&ctl->seg_state[7]) != 0;
+  st.ph = pld<SA>(&ctl->seg_state[8]);
+  st.fe = pld<SA>(&ctl->seg_state[9]);
+  st.ae = pld<SA>(&ctl->seg_state[10]);
+  return res;
 }
 
 // Round-synchronous peel (section 2.4 asks for a degeneracy order; this is the
@@ -344,21 +699,29 @@ __device__ int peel_rounds(const PeelArgs& A, PeelState& st, int wave, int nwave
 // becomes the smallest remaining degree. Marking the round's vertices and
 // decrementing their neighbours happen in the same phase: a vertex of the
 // current round already has degree <= k, so a decrement can never make it join
-// again (that needs a fall from k+1). One grid barrier per round. Launched
-// cooperatively; one block for small graphs. Late rounds are small (the
-// remaining graph is the dense core), so once at most PEEL_SOLO vertices remain
+// again (that needs a fall from k+1). Launched cooperatively; one block for
+// small graphs. Most rounds of a large sparse graph remove a handful of
+// vertices, and a grid barrier costs more than their work: a round of at most
+// PEEL_TINY vertices whose big rows hold at most PEEL_SEG_EDGES edges is run by
+// block 0 alone (peel_seg), with its frontier in LDS, while the other blocks
+// wait for it to hand back a larger round or a level pass. Once at most
+// PEEL_SOLO vertices with at most PEEL_SOLO_EDGES edges in their rows remain,
 // block 0 finishes alone at workgroup scope and the other blocks leave.
 __global__ __launch_bounds__(PEEL_THREADS) void k_peel(int n, const int* __restrict__ rp,
                                                         const int* __restrict__ ci, int* deg, int* rnd, int* core,
                                                         int* alive0, int* alive1, int* front0, int* front1,
                                                         int* bfront0, int* bfront1, MceCtl* ctl, u64 budget) {
+  __shared__ int s_cnt[12];
+  __shared__ int4 s_fr[2 * PEEL_TINY + 1];
   if (ld_relaxed(&ctl->status) != 0) return;   // rejected input: nothing to order
   const u64 t0 = wall_clock64();
-  PeelArgs A{n, rp, ci, deg, rnd, core, alive0, alive1, front0, front1, bfront0, bfront1, ctl, t0 + budget};
+  PeelArgs A{n,      rp,     ci,      deg,     rnd, core,       alive0, alive1, front0,
+             front1, bfront0, bfront1, ctl, t0 + budget, s_cnt, s_fr};
   const int gtid = blockIdx.x * blockDim.x + threadIdx.x;
   const int gsize = gridDim.x * blockDim.x;
   const bool timer = blockIdx.x == 0 && threadIdx.x == 0;
-  PeelState st{0, 0, 0, 0, 0, n, false, 0u, 0, 0, 0, t0};
+  // k starts below every degree: the first level is the smallest degree
+  PeelState st{0, 0, 0, -1, 0, n, 0, 0, 0, false, 0u, 0u, 0, 0, 0, t0};
 
   for (int v = gtid; v < n; v += gsize) {
     pst<SA>(&deg[v], rp[v + 1] - rp[v]);
@@ -372,28 +735,48 @@ __global__ __launch_bounds__(PEEL_THREADS) void k_peel(int n, const int* __restr
     for (int i = 0; i < 3; i++) {
       pst<SA>(&ctl->fsize[i], 0);
       pst<SA>(&ctl->bsize[i], 0);
+      pst<SA>(&ctl->bedge[i], 0);
     }
-    pst<SA>(&ctl->min_deg, 0x7FFFFFFF);
+    pst<SA>(&ctl->asum[0], 0);
+    pst<SA>(&ctl->asum[1], 0);
+    pst<SA>(&ctl->min_deg[0], 0x7FFFFFFF);
+    pst<SA>(&ctl->min_deg[1], 0x7FFFFFFF);
   }
   grid_sync(ctl, A.deadline, st.epoch);
 
+  const int bwave = threadIdx.x / MCE_WAVE, bwaves = blockDim.x / MCE_WAVE;
   int res;
   if (gridDim.x > 1) {
-    res = peel_rounds<SA, false>(A, st, gtid / MCE_WAVE, gsize / MCE_WAVE, timer);
-    if (res == 1) {
-      if (blockIdx.x != 0) return;
-      // block 0 goes on alone: drop any stale copy its XCD's caches may hold
-      // of what the other blocks wrote
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-      res = peel_rounds<SW, true>(A, st, threadIdx.x / MCE_WAVE, blockDim.x / MCE_WAVE, timer);
+    for (;;) {
+      res = peel_rounds<SA, PEEL_GRID>(A, st, gtid / MCE_WAVE, gsize / MCE_WAVE, timer);
+      if (res == PEEL_TO_SEG) {
+        st.seg++;
+        if (blockIdx.x != 0) {
+          res = peel_wait(ctl, st, A.deadline);
+          if (res == PEEL_TO_GRID) continue;
+          return;   // block 0 finishes the peel (or it timed out)
+        }
+        res = peel_seg(A, st, bwave, bwaves, timer);
+        // hand back: a larger round or a level pass for the grid, or leave
+        res = peel_hand_back(ctl, st, res, A.deadline);
+        if (res == PEEL_TO_GRID) continue;
+      }
+      if (res == PEEL_TO_ALONE) {
+        if (blockIdx.x != 0) return;
+        // block 0 goes on alone: drop any stale copy its XCD's caches may hold
+        // of what the other blocks wrote
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+        res = peel_rounds<SW, PEEL_ALONE>(A, st, bwave, bwaves, timer);
+      }
+      break;
     }
   } else {
-    res = peel_rounds<SW, true>(A, st, threadIdx.x / MCE_WAVE, blockDim.x / MCE_WAVE, timer);
+    res = peel_rounds<SW, PEEL_ALONE>(A, st, bwave, bwaves, timer);
   }
   if (res < 0) return;
   if (threadIdx.x == 0 && blockIdx.x == 0) {
     ctl->rounds = st.r;
-    ctl->degeneracy = st.k;
+    ctl->degeneracy = max(st.k, 0);
     ctl->peel_ticks[0] = st.tb;
     ctl->peel_ticks[1] = st.tl;
     ctl->peel_ticks[2] = st.tr;
