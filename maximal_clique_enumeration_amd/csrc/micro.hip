@@ -89,13 +89,14 @@ __global__ __launch_bounds__(64) void k_search_micro(MicroParams prm) {
   bool req_closed = true;   // the request word starts closed and is closed again by wl_idle
   bool abort = false;
   u32 steps = 0;
+  RootCursor rc{0u, 0u};
 
   for (;;) {
     // ---------------------------------------------------------- a table and its first frames
     u64 toff = 0;
     int nfr = 0;
     if (!phase2) {
-      const u32 idx = next_root(wl, (u32)prm.nroots);
+      const u32 idx = take_root(wl, rc, (u32)prm.nroots, (u32)prm.nworkers, 64u);
       if (idx >= (u32)prm.nroots) {
         phase2 = true;
         continue;

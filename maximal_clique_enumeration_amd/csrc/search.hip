@@ -173,13 +173,14 @@ __global__ __launch_bounds__(64) void k_search(SearchParams prm) {
   bool abort = false;
   u32 rng = 0x9E3779B9u ^ ((u32)wid * 0x85EBCA6Bu) ^ (u32)prm.nroots;
   if (rng == 0) rng = 1;
+  RootCursor rc{0u, 0u};
 
   for (;;) {
     // ---------------------------------------------------------- get a task
     int k0 = 1, lpx = 0;
     u64 toff = 0, s = 0, pj = 0, xj = 0;
     if (!phase2) {
-      const u32 idx = next_root(wl, (u32)prm.nroots);
+      const u32 idx = take_root(wl, rc, (u32)prm.nroots, (u32)prm.nworkers, 16u);
       if (idx >= (u32)prm.nroots) {
         phase2 = true;
         continue;
@@ -576,13 +577,14 @@ __global__ __launch_bounds__(64) void k_search_w1(SearchParams prm) {
   bool abort = false;
   u32 rng = 0x9E3779B9u ^ ((u32)wid * 0x85EBCA6Bu) ^ (u32)prm.nroots;
   if (rng == 0) rng = 1;
+  RootCursor rc{0u, 0u};
 
   for (;;) {
     // ---------------------------------------------------------- get a task
     int k0 = 1, lpx = 0;
     u64 toff = 0, s = 0, P = 0, XP = 0;
     if (!phase2) {
-      const u32 idx = next_root(wl, (u32)prm.nroots);
+      const u32 idx = take_root(wl, rc, (u32)prm.nroots, (u32)prm.nworkers, 16u);
       if (idx >= (u32)prm.nroots) {
         phase2 = true;
         continue;

@@ -193,12 +193,31 @@ __device__ int wl_idle(MceWl* wl, int wid, int nworkers, u64 deadline, u32* stat
 // or nroots when none is left. Every subtree goes through the counter: a wave
 // that has not started yet must never hold a subtree that other waves count as
 // taken, or they could finish and leave while it still needs the worker list.
-__device__ __forceinline__ u32 next_root(MceWl* wl, u32 nroots) {
-  u32 idx = nroots;
-  if (lane_id() == 0) {
-    if (ld_relaxed(&wl->root_ctr) < nroots) idx = atomicAdd(&wl->root_ctr, 1u);
+// Roots go out in chunks: one fetch takes about the roots left divided by
+// 2 x nworkers (at least 1, at most maxc), so that hundreds of thousands of tiny
+// subtrees do not each cost an atomic on the one shared counter (same-address
+// atomics from thousands of waves serialise), while the last roots, and the
+// few roots of a launch with more waves than roots, still go out one at a time.
+struct RootCursor {
+  u32 next, end;   // this wave's chunk [next, end)
+};
+__device__ __forceinline__ u32 take_root(MceWl* wl, RootCursor& rc, u32 nroots, u32 nworkers, u32 maxc) {
+  if (rc.next >= rc.end) {
+    u32 idx = nroots, c = 0;
+    if (lane_id() == 0) {
+      const u32 seen = ld_relaxed(&wl->root_ctr);
+      if (seen < nroots) {
+        c = min(maxc, max(1u, (nroots - seen) / (2u * nworkers)));
+        idx = atomicAdd(&wl->root_ctr, c);
+      }
+    }
+    idx = (u32)read_lane((int)idx, 0);
+    c = (u32)read_lane((int)c, 0);
+    if (idx >= nroots) return nroots;
+    rc.next = idx;
+    rc.end = min(idx + c, nroots);
   }
-  return (u32)read_lane((int)idx, 0);
+  return rc.next++;
 }
 
 // Count this wave active, and wait until the increment is performed: it must
