@@ -46,22 +46,24 @@ __device__ __forceinline__ int build_lookup(const int* hk, const short* hv, int 
 }
 
 // ------------------------------------------------------------------ micro tables
-// |P| <= 64 and |X| <= 64: one wavefront per root, one lane per row. P's ids go
-// into the LDS hash, so a lane builds its row by walking its vertex's CSR row
-// and looking every neighbour up; rows longer than BUILD_LANE_MAX edges are
-// built instead by probing each P member in that CSR row (binary search), one
-// lane per P member, several rows per pass when |P| is small. The table ends
-// with the X column of every P member (the transpose of the X rows).
-#define BUILD_LANE_MAX 48
+// |P| <= 64 and |X| <= 64: one wavefront per root, and the whole table (at most
+// 128 one-word rows) is built in LDS. One pass over the root's CSR row splits it
+// into P and X; P's ids go into the LDS hash. The members' CSR rows are then
+// streamed as one sequence, 64 consecutive entries per load (coalesced within a
+// row), each entry's row found from the rows' degree prefix sums; rows longer
+// than 4 |P| are built by probing each P member in them. The X column of
+// every P member (the transpose of the X rows) is taken in LDS, and the table is
+// written out with coalesced stores.
+#define MICRO_PROBE_RATIO 4   // rows longer than 4 |P| are probed
 
 __global__ __launch_bounds__(64) void k_build_micro(BuildParams prm) {
-  constexpr int PMAX = MCE_MICRO_MAX;
-  constexpr int HB = 7;   // hash slots >= 2 PMAX
-  __shared__ int s_pid[PMAX];
+  constexpr int HB = 7;   // hash slots >= 2 * 64
+  __shared__ int s_id[2 * MCE_MICRO_MAX];   // P ids, then X ids
   __shared__ int s_hk[1 << HB];
   __shared__ short s_hv[1 << HB];
-  __shared__ int s_long[MCE_WAVE];   // rows of the current slab that are built by probing
-  __shared__ int s_nlong;
+  __shared__ int s_pre[MCE_WAVE];
+  __shared__ int s_ga[MCE_WAVE];
+  __shared__ u64 s_row[2 * MCE_MICRO_MAX];
   const int lane = lane_id();
   const int* __restrict__ rp = prm.rp;
   const int* __restrict__ ci = prm.ci;
@@ -70,7 +72,7 @@ __global__ __launch_bounds__(64) void k_build_micro(BuildParams prm) {
     const int r = prm.roots[i];
     const int a = rp[r], b = rp[r + 1];
     const int rr = rnd[r];
-    // P (later neighbours) into LDS, in id order; count X
+    // P (later neighbours) and X (earlier ones), each in id order
     int np = 0, nx = 0;
     for (int base = a; base < b; base += MCE_WAVE) {
       const int e = base + lane;
@@ -78,18 +80,18 @@ __global__ __launch_bounds__(64) void k_build_micro(BuildParams prm) {
       const int u = valid ? ci[e] : 0;
       const bool lat = valid && order_after(rnd[u], u, rr, r);
       const u64 lm = ballot(lat), xm = ballot(valid && !lat);
-      if (lat && np + mbcnt(lm) < PMAX) s_pid[np + mbcnt(lm)] = u;
+      if (lat && np + mbcnt(lm) < MCE_MICRO_MAX) s_id[np + mbcnt(lm)] = u;
+      if (valid && !lat && nx + mbcnt(xm) < MCE_MICRO_MAX) s_id[MCE_MICRO_MAX + nx + mbcnt(xm)] = u;
       np += __popcll(lm);
       nx += __popcll(xm);
     }
-    if (np == 0 || np > PMAX || nx > MCE_MICRO_MAX) {   // the host sends only such roots here
+    if (np == 0 || np > MCE_MICRO_MAX || nx > MCE_MICRO_MAX) {   // the host sends only such roots here
       if (lane == 0) atomicOr(prm.status, MCE_E_LIMIT);
       continue;
     }
     const int nrows = np + nx;
-    const u64 words = mce_micro_table_words(np, nx);
     const u64 off = uni(prm.tab_off[i]) - uni(prm.tab_off[0]);
-    if (off + words > prm.heap_words) {
+    if (off + mce_micro_table_words(np, nx) > prm.heap_words) {
       if (lane == 0) atomicOr(prm.status, MCE_E_HEAP);
       continue;
     }
@@ -103,85 +105,98 @@ __global__ __launch_bounds__(64) void k_build_micro(BuildParams prm) {
       T[1] = (u64)(u32)r;
       T[2] = mce_vertex_term(r);
     }
-    // X ids straight into the table (rows read them back)
-    int xo = 0;
-    for (int base = a; base < b; base += MCE_WAVE) {
-      const int e = base + lane;
-      const bool valid = e < b;
-      const int u = valid ? ci[e] : 0;
-      const bool ear = valid && !order_after(rnd[u], u, rr, r);
-      const u64 xm = ballot(ear);
-      if (ear) ids[np + xo + mbcnt(xm)] = u;
-      xo += __popcll(xm);
-    }
-    // hash of P: id -> local index
     for (int h = lane; h < (1 << HB); h += MCE_WAVE) s_hk[h] = -1;
-    __syncthreads();
-    for (int j = lane; j < np; j += MCE_WAVE) {
-      const int u = s_pid[j];
-      ids[j] = u;
-      hvs[j] = mce_vertex_term(u);
+    __syncthreads();   // the ids are in LDS, the hash is clear
+    if (lane < np) {
+      const int u = s_id[lane];
+      ids[lane] = u;
+      hvs[lane] = mce_vertex_term(u);
       u32 h = build_hash<HB>(u);
       while (atomicCAS(&s_hk[h], -1, u) != -1) h = (h + 1u) & ((1u << HB) - 1u);
-      s_hv[h] = (short)j;
+      s_hv[h] = (short)lane;
     }
-    __syncthreads();   // hash complete, X ids in the table
-    // rows, a slab of 64 at a time
+    if (lane < nx) ids[np + lane] = s_id[MCE_MICRO_MAX + lane];
+    // rows, in slabs of 64 members (P members first, then X members)
     for (int t0 = 0; t0 < nrows; t0 += MCE_WAVE) {
       const int t = t0 + lane;
-      if (lane == 0) s_nlong = 0;
-      __syncthreads();
-      if (t < nrows) {
-        const int g = t < np ? s_pid[t] : ids[t];   // X member t - np sits at ids[t]
-        const int ga = rp[g], gb = rp[g + 1];
-        if (gb - ga > BUILD_LANE_MAX) {
-          s_long[atomicAdd(&s_nlong, 1)] = t;
-        } else {
-          u64 w = 0;
-          for (int e = ga; e < gb; e += 4) {
-            int j[4];
+      const bool valid = t < nrows;
+      int ga = 0, d = 0;
+      if (valid) {
+        const int g = t < np ? s_id[t] : s_id[MCE_MICRO_MAX + t - np];
+        ga = rp[g];
+        d = rp[g + 1] - ga;
+      }
+      const bool probe = valid && d > MICRO_PROBE_RATIO * np;
+      const int dd = valid && !probe ? d : 0;
+      int inc = dd;
 #pragma unroll
-            for (int z = 0; z < 4; z++) {
-              const int u = e + z < gb ? ci[e + z] : -1;
-              j[z] = u >= 0 ? build_lookup<HB>(s_hk, s_hv, u) : -1;
-            }
+      for (int o = 1; o < MCE_WAVE; o <<= 1) {
+        const int v = __shfl_up(inc, o);
+        if (lane >= o) inc += v;
+      }
+      const int D = uni(__shfl(inc, MCE_WAVE - 1));
+      s_pre[lane] = inc - dd;
+      s_ga[lane] = ga;
+      s_row[t0 + lane] = 0;
+      __syncthreads();   // the hash (first slab), the prefix sums and the cleared rows
+      for (int base = 0; base < D; base += 4 * MCE_WAVE) {
+        int u[4], rw[4];
 #pragma unroll
-            for (int z = 0; z < 4; z++)
-              if (j[z] >= 0) w |= 1ull << j[z];
+        for (int z = 0; z < 4; z++) {
+          const int x = base + z * MCE_WAVE + lane;
+          rw[z] = -1;
+          u[z] = 0;
+          if (x < D) {
+            int q = 0;   // the last row whose prefix is <= x
+#pragma unroll
+            for (int step = MCE_WAVE / 2; step > 0; step >>= 1)
+              if (s_pre[q + step] <= x) q += step;
+            rw[z] = q;
+            u[z] = ci[s_ga[q] + (x - s_pre[q])];
           }
-          rows[t] = w;
+        }
+#pragma unroll
+        for (int z = 0; z < 4; z++) {
+          if (rw[z] >= 0) {
+            const int j = build_lookup<HB>(s_hk, s_hv, u[z]);
+            if (j >= 0) atomicOr(&s_row[t0 + rw[z]], 1ull << j);
+          }
         }
       }
-      __syncthreads();
-      // long rows: lane = P member (several rows per pass when |P| is small)
-      const int nl = s_nlong;
-      const int npw = np <= 1 ? 1 : (np >= 64 ? 64 : 1 << (32 - __builtin_clz((u32)(np - 1))));
-      const int per = MCE_WAVE / npw;   // rows per pass (1 when |P| > 32)
-      for (int l0 = 0; l0 < nl; l0 += per) {
-        const int q = lane / npw, jj = lane % npw;
-        const int tq = l0 + q < nl ? s_long[l0 + q] : -1;
-        int g = 0, ga = 0, gb = 0;
-        if (tq >= 0) {
-          g = tq < np ? s_pid[tq] : ids[tq];
-          ga = rp[g];
-          gb = rp[g + 1];
-        }
-        const bool found = tq >= 0 && jj < np && csr_range_has(ci, ga, gb, s_pid[jj]);
-        const u64 fm = ballot(found);
-        if (jj == 0 && tq >= 0) {
-          const u64 mask = npw >= 64 ? ~0ull : ((1ull << npw) - 1ull);
-          rows[tq] = (fm >> (q * npw)) & mask;
+      // rows much longer than P: probe each P member, several rows per pass when |P| is small
+      const u64 pm = ballot(probe);
+      if (pm) {
+        const int npw = np <= 1 ? 1 : (np >= 64 ? 64 : 1 << (32 - __builtin_clz((u32)(np - 1))));
+        const int per = MCE_WAVE / npw;   // rows per pass
+        const int grp = lane / npw, jj = lane % npw;
+        const int cntp = __popcll(pm);
+        for (int c0 = 0; c0 < cntp; c0 += per) {
+          int l = -1;   // the lane (row) of the (c0 + grp)-th probe row
+          if (c0 + grp < cntp) {
+            u64 m = pm;
+            for (int q = 0; q < c0 + grp; q++) m &= m - 1ull;
+            l = __builtin_ctzll(m);
+          }
+          const int gal = __shfl(ga, l < 0 ? 0 : l);
+          const int gdl = __shfl(d, l < 0 ? 0 : l);
+          const bool found = l >= 0 && jj < np && csr_range_has(ci, gal, gal + gdl, s_id[jj]);
+          const u64 fm = ballot(found);
+          if (jj == 0 && l >= 0) {
+            const u64 mask = npw >= 64 ? ~0ull : ((1ull << npw) - 1ull);
+            s_row[t0 + l] = (fm >> (grp * npw)) & mask;
+          }
         }
       }
+      __syncthreads();   // the slab's rows are complete
     }
-    // X column of every P member: the X rows' bit of that member
-    __syncthreads();   // the X rows are in the table
+    // X column of every P member (the X rows' bit of that member), then the rows
     if (lane < np) {
       u64 col = 0;
-      for (int x2 = 0; x2 < nx; x2++) col |= ((rows[np + x2] >> lane) & 1ull) << x2;
+      for (int x2 = 0; x2 < nx; x2++) col |= ((s_row[np + x2] >> lane) & 1ull) << x2;
       xcol[lane] = col;
     }
-    __syncthreads();
+    for (int t = lane; t < nrows; t += MCE_WAVE) rows[t] = s_row[t];
+    __syncthreads();   // LDS is reused by the next root
   }
 }
 
