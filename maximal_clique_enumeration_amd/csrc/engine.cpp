@@ -329,10 +329,11 @@ mce_status run_impl(mce_engine* e, int32_t n, int64_t nnz, const int32_t* row_pt
     bp.tab_off = dp<u64>(e->taboff) + off.off[c];
     bp.status = &ctl->status;
     if (!micro) {
-      // enough (root, part) blocks to fill the chip, at most one part per 64-row slab
+      // enough (root, part) blocks to fill the chip, at most one part per 64-row
+      // slab, and at most about 8 slabs of the largest table per part
       const int nslab = std::max(1, (hctl->sub_maxr[var][c] + 63) / 64);
       const int want = (kSplitBlocksPerCu * e->num_cu + counts[c] - 1) / counts[c];
-      bp.parts = std::max(1, std::min(want, nslab));
+      bp.parts = std::max(1, std::min(std::max(want, (nslab + 7) / 8), nslab));
     }
     if (timing) (void)hipEventRecord(e->ev[evi], s);
     if ((h = mce_launch_build(bp, e->num_cu * 32, s)) != hipSuccess) return hip_fail(e, h, "build launch");

@@ -33,6 +33,40 @@ __device__ __forceinline__ u32 build_hash(int u) {
   return ((u32)u * 0x9E3779B1u) >> (32 - HB);
 }
 
+// Four binary searches for `key` in the sorted ranges [lo[z], hi[z]) of ci, in
+// lockstep: the four loads of a step are independent and overlap.
+__device__ __forceinline__ void csr_range_has4(const int* __restrict__ ci, const int lo_[4], const int hi_[4],
+                                               int key, bool found[4]) {
+  int lo[4], len[4];
+#pragma unroll
+  for (int z = 0; z < 4; z++) {
+    lo[z] = lo_[z];
+    len[z] = hi_[z] - lo_[z];
+  }
+  for (;;) {
+    bool any = false;
+    int v[4];
+#pragma unroll
+    for (int z = 0; z < 4; z++) v[z] = len[z] > 0 ? ci[lo[z] + (len[z] >> 1)] : 0;
+#pragma unroll
+    for (int z = 0; z < 4; z++) {
+      if (len[z] > 0) {
+        any = true;
+        const int half = len[z] >> 1;
+        if (v[z] < key) {
+          lo[z] += half + 1;
+          len[z] -= half + 1;
+        } else {
+          len[z] = half;
+        }
+      }
+    }
+    if (!any) break;
+  }
+#pragma unroll
+  for (int z = 0; z < 4; z++) found[z] = lo[z] < hi_[z] && ci[lo[z]] == key;
+}
+
 template <int HB>
 __device__ __forceinline__ int build_lookup(const int* hk, const short* hv, int u) {
   u32 h = build_hash<HB>(u);
@@ -387,16 +421,27 @@ __global__ __launch_bounds__(64) void k_build_rows(BuildParams prm) {
       u64* srow = rows + (size_t)t0 * W;
       for (int q = lane; q < nr * W; q += MCE_WAVE)
         if (!((pm >> (q / W)) & 1ull)) srow[q] = s_slab[q];
-      // rows much longer than P: probe every P member in the CSR row
-      for (u64 m = pm; m != 0; m &= m - 1) {
-        const int l = __builtin_ctzll(m);
-        const int gal = read_lane(ga, l);
-        const int gbl = gal + read_lane(d, l);
+      // rows much longer than P: probe every P member in the CSR row, four rows
+      // at a time (their binary searches run in lockstep, so the loads overlap)
+      for (u64 m = pm; m != 0;) {
+        int lr[4], lo[4], hi[4];
+#pragma unroll
+        for (int z = 0; z < 4; z++) {
+          lr[z] = m ? __builtin_ctzll(m) : -1;
+          m = m ? (m & (m - 1ull)) : 0ull;
+          lo[z] = lr[z] >= 0 ? read_lane(ga, lr[z]) : 0;
+          hi[z] = lr[z] >= 0 ? lo[z] + read_lane(d, lr[z]) : 0;
+        }
         for (int w0 = 0; w0 < W; w0++) {
           const int j = w0 * 64 + lane;
-          const bool found = j < np && csr_range_has(ci, gal, gbl, ids[j]);
-          const u64 fm = ballot(found);
-          if (lane == 0) srow[(size_t)l * W + w0] = fm;
+          const int key = j < np ? ids[j] : -1;
+          bool f[4];
+          csr_range_has4(ci, lo, hi, key, f);
+#pragma unroll
+          for (int z = 0; z < 4; z++) {
+            const u64 fm = ballot(f[z] && j < np);
+            if (lane == 0 && lr[z] >= 0) srow[(size_t)lr[z] * W + w0] = fm;
+          }
         }
       }
       __syncthreads();   // s_pre, s_ga and s_slab are rewritten by the next slab
