@@ -41,7 +41,7 @@ struct mce_engine {
   std::string err;
 
   DevBuf ctl, deg, rnd, core, alive0, alive1, front0, front1, bfront0, bfront1, pcount, xcount, lists, taboff, scan, heap, wl,
-      slots, stats, mstack, mail;
+      slots, stats, mstack, mail, vitems;
   HostPinned host;    // staging for device -> host copies
   hipEvent_t ev[4 + 4 * MCE_NSUB] = {};
   bool have_events = false;
@@ -184,7 +184,9 @@ mce_status run_impl(mce_engine* e, int32_t n, int64_t nnz, const int32_t* row_pt
   const int grid = std::max(1, e->num_cu * 8);
   if (timing) (void)hipEventRecord(e->ev[0], s);
   if (e->cfg.validate) {
-    if ((h = mce_launch_validate(n, nnz, row_ptr, col_idx, ctl, grid, s)) != hipSuccess)
+    if ((h = ensure(e->vitems, (size_t)mce_validate_items(nnz) * sizeof(u64))) != hipSuccess)
+      return hip_fail(e, h, "allocation");
+    if ((h = mce_launch_validate(n, nnz, row_ptr, col_idx, ctl, dp<u64>(e->vitems), grid, s)) != hipSuccess)
       return hip_fail(e, h, "validate launch");
   }
   if (timing) (void)hipEventRecord(e->ev[1], s);
@@ -704,7 +706,7 @@ void mce_destroy(mce_engine* e) {
   (void)hipSetDevice(e->device);
   DevBuf* bufs[] = {&e->ctl,    &e->deg,   &e->rnd,    &e->core,    &e->alive0, &e->alive1,
                     &e->front0, &e->front1, &e->bfront0, &e->bfront1, &e->pcount, &e->xcount, &e->lists,  &e->taboff, &e->scan,
-                    &e->heap,   &e->wl,    &e->slots,  &e->stats,  &e->mstack, &e->mail};
+                    &e->heap,   &e->wl,    &e->slots,  &e->stats,  &e->mstack, &e->mail, &e->vitems};
   for (DevBuf* b : bufs) release(*b);
   if (e->host.p) (void)hipHostFree(e->host.p);
   for (auto& ev : e->ev)

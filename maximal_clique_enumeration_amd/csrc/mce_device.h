@@ -108,6 +108,9 @@ struct MceCtl {
   int bedge[3];          // peel: the big vertices' CSR row lengths summed (same rotation)
   int asum[2];           // peel: each remaining list's CSR row lengths summed (by list parity)
   u32 bar_count;         // grid barrier: arrivals so far in the launch
+  u32 vitems;            // validation: pieces of long rows queued for the second pass
+  u32 vdone;             // validation: blocks of the second pass that finished
+  u64 vdown, vup;        // validation: edges from the larger (degree, id) end, and from the smaller
   u32 seg_gen;           // peel: segments of tiny rounds that block 0 has handed back
   u32 seg_arrive;        // peel: blocks that started waiting for a segment (summed over segments)
   int seg_state[12];     // peel: the state block 0 hands back (result, list, frontier, level, round, slot, sums)

@@ -34,29 +34,100 @@ __global__ __launch_bounds__(256) void k_validate_rowptr(int n, long long nnz, c
 }
 
 // Pass 2 (only if pass 1 found nothing): ids in range, no loops, rows strictly
-// ascending, and every edge present in both directions. One wavefront per row.
+// ascending, and every edge present in both directions. Symmetry is checked on
+// half of the edges, and on the cheap side: for an edge stored in the row of the
+// endpoint that comes later in (degree, id) order, the reverse edge is searched
+// in the other endpoint's row (the shorter one). Every such edge's reverse is a
+// distinct stored edge from the earlier endpoint, so if both kinds are equally
+// many, every edge of the second kind is such a reverse as well: the graph is
+// symmetric exactly when all searches succeed and the two counts are equal.
+// Rows longer than VAL_LONG go, in VAL_LONG-edge pieces, to a second pass whose
+// pieces are dealt over the whole grid (one wavefront per row would leave a hub
+// of tens of thousands of edges to a single wavefront).
+#define VAL_LONG 2048
+
+__device__ __forceinline__ u32 val_edge(const int* __restrict__ rp, const int* __restrict__ ci, int n, int v, int dv,
+                                        int e, int b, u32& down, u32& up) {
+  const int u = ci[e];
+  if (u < 0 || u >= n) return 2u;                 // MCE_GRAPH_RANGE
+  u32 bad = 0;
+  if (u == v) return 4u;                          // MCE_GRAPH_LOOP
+  if (e + 1 < b && ci[e + 1] <= u) bad |= 8u;     // MCE_GRAPH_ORDER
+  const int ua = rp[u], ub = rp[u + 1];
+  const int du = ub - ua;
+  if (dv > du || (dv == du && v > u)) {
+    down++;
+    if (!csr_range_has(ci, ua, ub, v)) bad |= 16u;   // MCE_GRAPH_ASYM
+  } else {
+    up++;
+  }
+  return bad;
+}
+
+__device__ __forceinline__ void val_flush(MceCtl* ctl, u32 bad, u32 down, u32 up) {
+  const u32 bb = wave_or_u32(bad);
+  const u32 wd = wave_sum_u32(down);   // edges of one wave: below 2^31
+  const u32 wu = wave_sum_u32(up);
+  if (lane_id() == 0) {
+    if (bb) atomicOr(&ctl->status, bb);
+    if (wd) atomicAdd(&ctl->vdown, (u64)wd);
+    if (wu) atomicAdd(&ctl->vup, (u64)wu);
+  }
+}
+
+// One wavefront per row of at most VAL_LONG edges; longer rows are queued as
+// (row, piece) items for k_validate_long.
 __global__ __launch_bounds__(256) void k_validate_cols(int n, const int* __restrict__ rp,
-                                                        const int* __restrict__ ci, MceCtl* ctl) {
+                                                        const int* __restrict__ ci, MceCtl* ctl, u64* items) {
   if (ld_relaxed(&ctl->status) != 0) return;
   const int lane = lane_id();
   const int wave = (blockIdx.x * blockDim.x + threadIdx.x) / MCE_WAVE;
   const int nwaves = gridDim.x * blockDim.x / MCE_WAVE;
-  u32 bad = 0;
+  u32 bad = 0, down = 0, up = 0;
   for (int v = wave; v < n; v += nwaves) {
-    int a = rp[v], b = rp[v + 1];
-    for (int e = a + lane; e < b; e += MCE_WAVE) {
-      int u = ci[e];
-      if (u < 0 || u >= n) {
-        bad |= 2u;                                 // MCE_GRAPH_RANGE
-        continue;
-      }
-      if (u == v) bad |= 4u;                       // MCE_GRAPH_LOOP
-      if (e + 1 < b && ci[e + 1] <= u) bad |= 8u;  // MCE_GRAPH_ORDER
-      if (!csr_range_has(ci, rp[u], rp[u + 1], v)) bad |= 16u;  // MCE_GRAPH_ASYM
+    const int a = rp[v], b = rp[v + 1];
+    const int dv = b - a;
+    if (dv > VAL_LONG) {
+      const u32 np = (u32)((dv + VAL_LONG - 1) / VAL_LONG);
+      u32 pos = 0;
+      if (lane == 0) pos = atomicAdd(&ctl->vitems, np);
+      pos = (u32)read_lane((int)pos, 0);
+      for (u32 c = (u32)lane; c < np; c += MCE_WAVE) items[pos + c] = ((u64)(u32)v << 32) | c;
+      continue;
     }
+    for (int e = a + lane; e < b; e += MCE_WAVE) bad |= val_edge(rp, ci, n, v, dv, e, b, down, up);
   }
-  u32 bb = wave_or_u32(bad);
-  if (lane == 0 && bb) atomicOr(&ctl->status, bb);
+  val_flush(ctl, bad, down, up);
+}
+
+// The queued pieces of long rows, dealt over all wavefronts. The last block to
+// finish compares the two edge counts (every block's count atomics are complete
+// before it counts itself done).
+__global__ __launch_bounds__(256) void k_validate_long(int n, const int* __restrict__ rp,
+                                                        const int* __restrict__ ci, MceCtl* ctl, const u64* items) {
+  if (ld_relaxed(&ctl->status) == 0) {
+    const int lane = lane_id();
+    const int wave = (blockIdx.x * blockDim.x + threadIdx.x) / MCE_WAVE;
+    const int nwaves = gridDim.x * blockDim.x / MCE_WAVE;
+    const u32 ni = ld_relaxed(&ctl->vitems);
+    u32 bad = 0, down = 0, up = 0;
+    for (u32 i = (u32)wave; i < ni; i += (u32)nwaves) {
+      const u64 it = items[i];
+      const int v = (int)(it >> 32);
+      const int c = (int)(u32)it;
+      const int a = rp[v], b = rp[v + 1];
+      const int e0 = a + c * VAL_LONG, e1 = min(b, e0 + VAL_LONG);
+      for (int e = e0 + lane; e < e1; e += MCE_WAVE) bad |= val_edge(rp, ci, n, v, b - a, e, b, down, up);
+    }
+    val_flush(ctl, bad, down, up);
+  }
+  wait_stores_complete();
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const u32 d = __hip_atomic_fetch_add(&ctl->vdone, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (d == gridDim.x - 1 && ld_relaxed(&ctl->status) == 0 && ld_relaxed64(&ctl->vdown) != ld_relaxed64(&ctl->vup))
+      atomicOr(&ctl->status, 16u);   // MCE_GRAPH_ASYM
+  }
 }
 
 // ------------------------------------------------------------------ k-core peel
@@ -907,14 +978,20 @@ __global__ __launch_bounds__(256) void k_bucket(const int* __restrict__ roots, i
 }
 
 // ------------------------------------------------------------------ launchers
-hipError_t mce_launch_validate(int n, long long nnz, const int* rp, const int* ci, MceCtl* ctl,
+long long mce_validate_items(long long nnz) { return 2 * nnz / VAL_LONG + 1; }
+
+hipError_t mce_launch_validate(int n, long long nnz, const int* rp, const int* ci, MceCtl* ctl, u64* items,
                                int blocks, hipStream_t s) {
   int nb = max(1, min(blocks, (n + 255) / 256));
   hipLaunchKernelGGL(k_validate_rowptr, dim3(nb), dim3(256), 0, s, n, nnz, rp, ctl);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   int nbw = (int)std::max(1LL, std::min((long long)blocks, ((long long)n + 3) / 4));
-  hipLaunchKernelGGL(k_validate_cols, dim3(nbw), dim3(256), 0, s, n, rp, ci, ctl);
+  hipLaunchKernelGGL(k_validate_cols, dim3(nbw), dim3(256), 0, s, n, rp, ci, ctl, items);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  // pieces of long rows: at most 2 nnz / VAL_LONG of them
+  const int nbl = (int)std::max(1LL, std::min((long long)blocks, nnz / (4LL * VAL_LONG)));
+  hipLaunchKernelGGL(k_validate_long, dim3(nbl), dim3(256), 0, s, n, rp, ci, ctl, (const u64*)items);
   return hipGetLastError();
 }
 

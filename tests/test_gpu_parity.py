@@ -255,6 +255,35 @@ def test_rejects_malformed(eng):
     check(eng, g)
 
 
+def _drop_edge(rp, ci, u, w):
+    """The CSR without the directed edge (u, w)."""
+    pos = rp[u] + int(np.nonzero(ci[rp[u]:rp[u + 1]] == w)[0][0])
+    keep = np.ones(ci.size, bool)
+    keep[pos] = False
+    rp2 = rp.copy()
+    rp2[u + 1:] -= 1
+    return rp2, ci[keep]
+
+
+def test_asymmetry_on_either_side(eng):
+    """Symmetry is searched only for edges stored at the endpoint later in
+    (degree, id) order, and completed by counting: a missing reverse must be
+    found whichever endpoint stores the surviving edge, also in rows longer than
+    2048 edges (checked in pieces by a second pass)."""
+    g = mi.hub_clique(300, 4, 3000, 0.7, 12, 7)
+    rp, ci = g.row_ptr, g.col_idx
+    deg = np.diff(rp)
+    hub = int(np.argmax(deg))
+    assert deg[hub] > 2048
+    leaf = int(ci[rp[hub]])                    # a neighbour of the hub of smaller degree
+    core = int(ci[rp[hub + 1] - 1]) if deg[int(ci[rp[hub + 1] - 1])] > 1 else leaf
+    a, b = map(int, g.edge_list()[len(g.edge_list()) // 2])
+    for u, w in [(hub, leaf), (leaf, hub), (hub, core), (core, hub), (a, b), (b, a)]:
+        rp2, ci2 = _drop_edge(rp, ci, u, w)
+        assert _bad(eng, g.n, rp2, ci2) == mce.MCE_GRAPH_ASYM, (u, w)
+    check(eng, g)
+
+
 def test_bad_roots_and_empty_graph(eng):
     g = mi.cycle(10)
     rp, ci = on_gpu(g)
