@@ -864,6 +864,8 @@ __global__ __launch_bounds__(PEEL_THREADS) void k_peel(int n, const int* __restr
 // micro sub-class on or off): count, largest |P|, |X| and row count, heap
 // words, so that the host can pick the variant and size every launch from one
 // read-back.
+#define ORIENT_LONG 128   // rows longer than this are counted by the whole wavefront
+
 __global__ __launch_bounds__(256) void k_orient(int n, const int* __restrict__ rp, const int* __restrict__ ci,
                                                  const int* __restrict__ rnd, const int* __restrict__ roots,
                                                  int nroots, int* pcount, int* xcount, MceCtl* ctl) {
@@ -883,13 +885,35 @@ __global__ __launch_bounds__(256) void k_orient(int n, const int* __restrict__ r
       lim |= 2u;
       pcount[i] = 0;
       xcount[i] = 0;
-    } else if (i < cnt) {
-      const int a = rp[v], b = rp[v + 1];
-      const int rv = rnd[v];
+    }
+    // later neighbours: one thread per short row; the whole wavefront takes each
+    // long row in turn (a hub row would keep one thread busy for its whole length)
+    const bool inr = i < cnt && v >= 0 && v < n;
+    int a = 0, b = 0, rv = 0;
+    if (inr) {
+      a = rp[v];
+      b = rp[v + 1];
+      rv = rnd[v];
+    }
+    const bool longrow = inr && b - a > ORIENT_LONG;
+    if (inr && !longrow) {
       for (int e = a; e < b; e++) {
         const int u = ci[e];
         p += order_after(rnd[u], u, rv, v) ? 1 : 0;
       }
+    }
+    for (u64 lm = ballot(longrow); lm; lm &= lm - 1ull) {
+      const int t = __builtin_ctzll(lm);
+      const int ta = read_lane(a, t), tb = read_lane(b, t), tv = read_lane(v, t), tr = read_lane(rv, t);
+      u32 c = 0;
+      for (int e = ta + lane; e < tb; e += MCE_WAVE) {
+        const int u = ci[e];
+        c += order_after(rnd[u], u, tr, tv) ? 1u : 0u;
+      }
+      c = wave_sum_u32(c);
+      if (lane == t) p = (int)c;
+    }
+    if (inr) {
       x = (b - a) - p;
       pcount[i] = p;
       xcount[i] = x;
