@@ -63,6 +63,10 @@ def _load():
                                    ctypes.c_int64, u64p, u64p, u64p, ctypes.c_int32,
                                    i32p, i64p]
         lib.oracle_mce.restype = ctypes.c_int
+        lib.oracle_mce_l2.argtypes = [ctypes.c_int32, i32p, i32p, i32p, i32p, ctypes.c_int32,
+                                   ctypes.c_int64, u64p, u64p, u64p, ctypes.c_int32,
+                                   i32p, i64p]
+        lib.oracle_mce_l2.restype = ctypes.c_int
         lib.oracle_list.argtypes = [ctypes.c_int32, i32p, i32p, i32p, i32p, ctypes.c_int64]
         lib.oracle_list.restype = ctypes.c_int64
         _lib = lib
@@ -116,9 +120,10 @@ class Result:
         return (self.count, self.hash, tuple(self.hist))
 
 
-def mce(n: int, row_ptr, col_idx, roots=None, node_budget: int = 0, rnd=None) -> Result:
+def mce(n: int, row_ptr, col_idx, roots=None, node_budget: int = 0, rnd=None, level: int = 1) -> Result:
     """Maximal cliques of the graph, or of the first-level subtrees of `roots`
-    (the cliques whose earliest vertex in the peel order is a listed root)."""
+    (the cliques whose earliest vertex in the peel order is a listed root).
+    level=2 finds the same cliques through second-level subtrees (Algorithm 4)."""
     rp, rpp = _i32(row_ptr)
     ci, cip = _i32(col_idx)
     if rnd is None:
@@ -136,7 +141,10 @@ def mce(n: int, row_ptr, col_idx, roots=None, node_budget: int = 0, rnd=None) ->
     hsh = ctypes.c_uint64()
     hl = ctypes.c_int32()
     nodes = ctypes.c_int64()
-    rc = _load().oracle_mce(n, rpp, cip, rnp, rop, nr, node_budget, ctypes.byref(cnt),
+    if level not in (1, 2):
+        raise ValueError("level is 1 or 2")
+    fn = _load().oracle_mce if level == 1 else _load().oracle_mce_l2
+    rc = fn(n, rpp, cip, rnp, rop, nr, node_budget, ctypes.byref(cnt),
                             ctypes.byref(hsh),
                             hist.ctypes.data_as(ctypes.POINTER(ctypes.c_uint64)), cap,
                             ctypes.byref(hl), ctypes.byref(nodes))

@@ -14,6 +14,10 @@
  *     (pivot = vertex of P u X with the most neighbours in P);
  *   - section 2.4, Algorithm 3: one independent first-level subtree per vertex
  *     v_i, P = later neighbours, X = earlier neighbours, under a degeneracy order;
+ *   - section 3.2, Algorithm 4 (oracle_mce_l2): one independent second-level
+ *     subtree per edge {v_i, v_j}, P = common neighbours after both, X = common
+ *     neighbours before the later one; vertices of degree 0 are cliques of
+ *     their own (the pages' loop over edges does not meet them);
  *   - section 2.4 "Induced Subgraphs": each subtree only needs the edges between
  *     P u X and P, so sets are bitsets over the root's neighbourhood.
  *
@@ -300,6 +304,100 @@ int oracle_mce(int32_t n, const int32_t *rp, const int32_t *ci, const int32_t *r
     if (run_root(&s, r, loc) != 0) { rc = -1; break; }
   }
   free(s.L); free(s.R); free(loc);
+  *count = s.count; *hash = s.hash; *hist_len = s.hist_len;
+  if (nodes) *nodes = s.nodes;
+  if (rc) return rc;
+  if (s.over_budget) return 1;
+  if (s.hist_overflow) return 2;
+  return 0;
+}
+
+/* Algorithm 2 from (R0, P, X) for explicit id lists: P (ascending id) and X
+   (ascending id) become L = P then X, bitsets as in run_root. R0 holds k0 ids. */
+static int run_sub(search *s, const int32_t *R0, int k0, int32_t p, int32_t x, int32_t *loc) {
+  const int32_t *rp = s->rp, *ci = s->ci;
+  int32_t nl = p + x;
+  s->p = p; s->nl = nl;
+  int wp = (p + 63) / 64; if (wp == 0) wp = 1;
+  int wl = (nl + 63) / 64; if (wl == 0) wl = 1;
+  s->wp = wp; s->wl = wl;
+  s->adjP = (uint64_t *)calloc((size_t)(nl > 0 ? nl : 1) * wp, sizeof(uint64_t));
+  s->colL = (uint64_t *)calloc((size_t)(p > 0 ? p : 1) * wl, sizeof(uint64_t));
+  s->arena = (uint64_t *)calloc((size_t)(p + k0 + 1) * (2 * wp + wl), sizeof(uint64_t));
+  if (!s->adjP || !s->colL || !s->arena) { free(s->adjP); free(s->colL); free(s->arena); return -1; }
+  for (int32_t a = 0; a < nl; a++) loc[s->L[a]] = a;
+  for (int32_t a = 0; a < nl; a++) {
+    int32_t v = s->L[a];
+    for (int64_t e = rp[v]; e < rp[v + 1]; e++) {
+      int32_t b = loc[ci[e]];
+      if (b >= 0 && b < p) s->adjP[(size_t)a * wp + (b >> 6)] |= 1ULL << (b & 63);
+    }
+  }
+  for (int32_t a = 0; a < nl; a++)
+    for (int32_t b = 0; b < p; b++)
+      if ((s->adjP[(size_t)a * wp + (b >> 6)] >> (b & 63)) & 1)
+        s->colL[(size_t)b * wl + (a >> 6)] |= 1ULL << (a & 63);
+  for (int32_t a = 0; a < nl; a++) loc[s->L[a]] = -1;
+  uint64_t *P = s->arena + (size_t)(k0 - 1) * (2 * wp + wl), *X = P + wp;
+  for (int32_t b = 0; b < p; b++) P[b >> 6] |= 1ULL << (b & 63);
+  for (int32_t a = p; a < nl; a++) X[a >> 6] |= 1ULL << (a & 63);
+  for (int i = 0; i < k0; i++) s->R[i] = R0[i];
+  bkt(s, k0 - 1);
+  free(s->adjP); free(s->colL); free(s->arena);
+  s->adjP = s->colL = s->arena = NULL;
+  return 0;
+}
+
+/* The same cliques as oracle_mce (those whose earliest vertex is a listed root,
+   or all), found through independent second-level subtrees (Algorithm 4): a root
+   of degree 0 is a clique of its own; every edge {r, w} with w after r starts
+   Algorithm 2 from R = {r, w}, P = the common neighbours after w and X = the
+   common neighbours before w. Same arguments and return codes as oracle_mce. */
+int oracle_mce_l2(int32_t n, const int32_t *rp, const int32_t *ci, const int32_t *rnd,
+                  const int32_t *roots, int32_t nroots, int64_t node_budget,
+                  uint64_t *count, uint64_t *hash, uint64_t *hist, int32_t hist_cap,
+                  int32_t *hist_len, int64_t *nodes) {
+  search s;
+  memset(&s, 0, sizeof(s));
+  s.rp = rp; s.ci = ci; s.rnd = rnd;
+  s.hist = hist; s.hist_cap = hist_cap; s.budget = node_budget;
+  for (int32_t i = 0; i < hist_cap; i++) hist[i] = 0;
+  int32_t maxdeg = 0;
+  for (int32_t v = 0; v < n; v++) if (rp[v + 1] - rp[v] > maxdeg) maxdeg = rp[v + 1] - rp[v];
+  s.L = (int32_t *)malloc(sizeof(int32_t) * (size_t)(maxdeg + 1));
+  s.R = (int32_t *)malloc(sizeof(int32_t) * (size_t)(maxdeg + 3));
+  int32_t *loc = (int32_t *)malloc(sizeof(int32_t) * (size_t)(n > 0 ? n : 1));
+  int32_t *Xtmp = (int32_t *)malloc(sizeof(int32_t) * (size_t)(maxdeg + 1));
+  if (!s.L || !s.R || !loc || !Xtmp) { free(s.L); free(s.R); free(loc); free(Xtmp); return -1; }
+  for (int32_t v = 0; v < n; v++) loc[v] = -1;
+  int rc = 0;
+  int32_t cnt = roots ? nroots : n;
+  for (int32_t i = 0; i < cnt && !s.over_budget; i++) {
+    int32_t r = roots ? roots[i] : i;
+    if (r < 0 || r >= n) { rc = -2; break; }
+    if (rp[r + 1] == rp[r]) {   /* an isolated vertex */
+      s.R[0] = r;
+      report(&s, 1);
+      continue;
+    }
+    for (int64_t e = rp[r]; e < rp[r + 1] && !s.over_budget; e++) {
+      int32_t w = ci[e];
+      if (!later(rnd, w, r)) continue;
+      /* common neighbours of r and w, split at w */
+      int32_t p = 0, x = 0;
+      for (int64_t f = rp[r]; f < rp[r + 1]; f++) {
+        int32_t c = ci[f];
+        if (c == w || !row_has(ci, rp[w], rp[w + 1], c)) continue;
+        if (later(rnd, c, w)) s.L[p++] = c;
+        else Xtmp[x++] = c;
+      }
+      for (int32_t j = 0; j < x; j++) s.L[p + j] = Xtmp[j];
+      const int32_t R0[2] = {r, w};
+      if (run_sub(&s, R0, 2, p, x, loc) != 0) { rc = -1; break; }
+    }
+    if (rc) break;
+  }
+  free(s.L); free(s.R); free(loc); free(Xtmp);
   *count = s.count; *hash = s.hash; *hist_len = s.hist_len;
   if (nodes) *nodes = s.nodes;
   if (rc) return rc;

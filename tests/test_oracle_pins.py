@@ -246,6 +246,46 @@ def test_roots_partition_adds_up():
     assert (tot_c, tot_h, tot_hist) == (whole.count, whole.hash, whole.hist)
 
 
+# ------------------------------------------------------------------ second-level subtrees
+def summary_l2(g, roots=None):
+    r = oracle.mce(g.n, g.row_ptr, g.col_idx, roots=roots, level=2)
+    assert r.complete
+    return r.count, r.hash, r.hist
+
+
+@pytest.mark.parametrize("seed", range(40))
+def test_second_level_equals_brute_force(seed):
+    """Algorithm 4 (one subtree per edge {r, w}, w after r, plus isolated
+    vertices) finds exactly the maximal cliques that subset enumeration finds."""
+    rng = np.random.default_rng(1000 + seed)
+    n = int(rng.integers(0, 16))
+    p = float(rng.choice([0.0, 0.1, 0.3, 0.5, 0.7, 0.9, 1.0]))
+    g = mi.random_small(n, p, 1000 + seed)
+    assert summary_l2(g) == expect(brute.brute_maximal_cliques(g.n, g.row_ptr, g.col_idx))
+
+
+def test_second_level_closed_forms():
+    assert summary_l2(mi.complete(40)) == expect([tuple(range(40))])
+    assert summary_l2(mi.empty(9)) == expect([(i,) for i in range(9)])
+    assert summary_l2(mi.cycle(11)) == expect([tuple(sorted((i, (i + 1) % 11))) for i in range(11)])
+    g = mi.moon_moser(24)
+    assert summary_l2(g) == _product_summary([[3 * t, 3 * t + 1, 3 * t + 2] for t in range(8)])
+    g = mi.disjoint_union(mi.complete(5), mi.empty(3), mi.star(4))
+    assert summary_l2(g) == summary_of(g)
+
+
+def test_second_level_root_sets_are_first_level_root_sets():
+    """Per root set, both decompositions give the cliques whose earliest vertex
+    is in the set: L2 subtrees of edges leaving a root carry exactly those."""
+    g = mi.chung_lu(3000, 8.0, 2.3, None, 5, planted=6, planted_min=8, planted_max=14)
+    rng = np.random.default_rng(3)
+    roots = np.sort(rng.choice(g.n, size=400, replace=False)).astype(np.int32)
+    a = oracle.mce(g.n, g.row_ptr, g.col_idx, roots=roots)
+    b = oracle.mce(g.n, g.row_ptr, g.col_idx, roots=roots, level=2)
+    assert a.key() == b.key()
+    assert summary_l2(g) == summary_of(g)
+
+
 def test_node_budget_stops():
     g = mi.moon_moser(30)
     r = oracle.mce(g.n, g.row_ptr, g.col_idx, node_budget=1000)
