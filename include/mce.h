@@ -69,6 +69,13 @@ typedef enum {
 #define MCE_FLAG_NO_MICRO 8u     /* subtrees with |P| <= 64 and |X| <= 64 go to the width-1 wavefront
                                     kernel like the rest; by default the micro kernel searches them, one
                                     search-tree node per lane (section 3.1's finer work split) */
+#define MCE_FLAG_L2 16u          /* independent second-level subtrees (section 3.2, Algorithm 4): one
+                                    subtree per edge {v, w}, w after v, with R = {v, w}, P = the common
+                                    neighbours after w and X = those before w; a vertex of degree 0 is a
+                                    clique of its own. The cliques found are the same; for mce_run_roots,
+                                    the subtrees of the edges leaving the listed roots. By default one
+                                    first-level subtree per vertex (Algorithm 3), which section 4.5
+                                    recommends */
 
 /* mce_config.subgraph: how each subtree's induced subgraph is encoded (section
    3.4). Partial: bit rows for P x P only, edges between P and X looked up in the
@@ -106,9 +113,10 @@ typedef struct {
   int32_t max_p;          /* largest |P| at a first-level subtree root (<= d) */
   int32_t max_x;          /* largest |X| at a first-level subtree root (<= Delta) */
   int64_t isolated;       /* roots with degree 0, each a maximal clique of size 1 */
-  int64_t roots;          /* first-level subtrees searched (n for mce_run) */
+  int64_t roots;          /* subtrees searched: first-level (n for mce_run) or second-level (edges) */
   uint32_t graph_errors;  /* MCE_GRAPH_* bits when the last run returned MCE_ERR_GRAPH */
   int32_t subgraph;       /* MCE_SUBGRAPH_PARTIAL or _FULL: the encoding used; 0 before the search */
+  int32_t level;          /* 1: first-level subtrees (roots = vertices); 2: second-level (roots = edges) */
 } mce_graph_facts;
 
 /* Counters of the last run, summed over wavefronts. */
@@ -151,7 +159,7 @@ typedef struct {
                                 passes, round work, total */
   int32_t launch_sub[16];    /* per search launch (up to `launches`): its sub-class (bitset width
                                 class * 2 + HBM staging, or 12 for the micro kernel) */
-  int32_t launch_roots[16];  /* first-level subtrees of the launch */
+  int32_t launch_roots[16];  /* subtrees of the launch */
   float launch_build_ms[16]; /* its induced-subgraph build, with MCE_FLAG_PHASE_TIMES */
   float launch_search_ms[16];/* its search, same flag */
 } mce_run_stats;
@@ -162,7 +170,8 @@ mce_status mce_config_init(mce_config* cfg);
 
 /* Creates an engine on cfg->device (cfg may be NULL for the defaults). The engine
    owns all device scratch memory; it grows on demand and is freed by mce_destroy.
-   On success *out receives the engine. */
+   On success *out receives the engine. MCE_ERR_ARG for a field out of range or a
+   flag outside MCE_FLAG_*. */
 mce_status mce_create(const mce_config* cfg, mce_engine** out);
 
 /* Enumerates all maximal cliques of the graph (n vertices, nnz = row_ptr[n]

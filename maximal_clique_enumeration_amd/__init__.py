@@ -20,7 +20,7 @@ LIB_PATH = os.path.join(_HERE, "libmce.so")
 MCE_OK, MCE_ERR_ARG, MCE_ERR_GRAPH, MCE_ERR_NOMEM = 0, -1, -2, -3
 MCE_ERR_DEVICE, MCE_ERR_STATE, MCE_ERR_TIMEOUT, MCE_ERR_LIMIT = -4, -5, -6, -7
 MCE_GRAPH_ROWPTR, MCE_GRAPH_RANGE, MCE_GRAPH_LOOP, MCE_GRAPH_ORDER, MCE_GRAPH_ASYM = 1, 2, 4, 8, 16
-MCE_FLAG_HBM_STAGING, MCE_FLAG_PHASE_TIMES, MCE_FLAG_COUNTERS, MCE_FLAG_NO_MICRO = 1, 2, 4, 8
+MCE_FLAG_HBM_STAGING, MCE_FLAG_PHASE_TIMES, MCE_FLAG_COUNTERS, MCE_FLAG_NO_MICRO, MCE_FLAG_L2 = 1, 2, 4, 8, 16
 MCE_SUBGRAPH_AUTO, MCE_SUBGRAPH_PARTIAL, MCE_SUBGRAPH_FULL = 0, 1, 2
 
 # every function the C header declares
@@ -53,7 +53,7 @@ class mce_graph_facts(ctypes.Structure):
                 ("degeneracy", ctypes.c_int32), ("rounds", ctypes.c_int32),
                 ("max_p", ctypes.c_int32), ("max_x", ctypes.c_int32),
                 ("isolated", ctypes.c_int64), ("roots", ctypes.c_int64),
-                ("graph_errors", ctypes.c_uint32), ("subgraph", ctypes.c_int32)]
+                ("graph_errors", ctypes.c_uint32), ("subgraph", ctypes.c_int32), ("level", ctypes.c_int32)]
 
 
 class mce_worker_record(ctypes.Structure):
@@ -208,7 +208,7 @@ class Engine:
     def __init__(self, device: int | None = None, worker_list: bool = True, donate_min_p: int = 1,
                  validate: bool = True, max_workers: int = 0, timeout_ms: int = 120000,
                  hbm_staging: bool = False, phase_times: bool = False, subgraph: str = "auto",
-                 counters: bool = False, micro: bool = True, micro_donate_min_p: int = 10):
+                 counters: bool = False, micro: bool = True, micro_donate_min_p: int = 10, level: int = 1):
         import torch
         if device is None:
             device = torch.cuda.current_device()
@@ -222,8 +222,11 @@ class Engine:
         cfg.validate = 1 if validate else 0
         cfg.max_workers = max_workers
         cfg.timeout_ms = timeout_ms
+        if level not in (1, 2):
+            raise ValueError("level is 1 (first-level subtrees) or 2 (second-level subtrees)")
         cfg.flags = ((MCE_FLAG_HBM_STAGING if hbm_staging else 0) | (MCE_FLAG_PHASE_TIMES if phase_times else 0)
-                     | (MCE_FLAG_COUNTERS if counters else 0) | (0 if micro else MCE_FLAG_NO_MICRO))
+                     | (MCE_FLAG_COUNTERS if counters else 0) | (0 if micro else MCE_FLAG_NO_MICRO)
+                     | (MCE_FLAG_L2 if level == 2 else 0))
         modes = {"auto": MCE_SUBGRAPH_AUTO, "partial": MCE_SUBGRAPH_PARTIAL, "full": MCE_SUBGRAPH_FULL}
         if subgraph not in modes:
             raise ValueError(f"subgraph must be one of {sorted(modes)}")

@@ -42,6 +42,7 @@ struct mce_engine {
 
   DevBuf ctl, deg, rnd, core, alive0, alive1, front0, front1, bfront0, bfront1, pcount, xcount, lists, taboff, scan, heap, wl,
       slots, stats, mstack, mail, vitems;
+  DevBuf src, fwd, fwdtmp, eroots, pcount2, xcount2;   // second-level subtrees
   HostPinned host;    // staging for device -> host copies
   hipEvent_t ev[4 + 4 * MCE_NSUB] = {};
   bool have_events = false;
@@ -117,7 +118,7 @@ double ms_since(std::chrono::steady_clock::time_point t0) {
   return std::chrono::duration<double, std::milli>(std::chrono::steady_clock::now() - t0).count();
 }
 
-constexpr size_t kHistWords = MCE_MAX_P + 2;   // global histogram entries
+constexpr size_t kHistWords = MCE_MAX_P + 3;   // global histogram entries (sizes up to 2 + MCE_MAX_P)
 // control block, then the result words (hash, histogram): one clear, one read-back
 constexpr size_t kIoBytes = sizeof(MceCtl) + (1 + kHistWords) * sizeof(u64);
 static_assert(sizeof(MceCtl) % sizeof(u64) == 0, "results follow the control block");
@@ -176,6 +177,17 @@ mce_status run_impl(mce_engine* e, int32_t n, int64_t nnz, const int32_t* row_pt
       (h = ensure(e->wl, sizeof(MceWl))) != hipSuccess ||
       (h = ensure_host(e->host, kIoBytes)) != hipSuccess)
     return hip_fail(e, h, "allocation");
+  // second-level subtrees (section 3.2): the roots are the vertex roots' forward edges
+  const bool l2 = (e->cfg.flags & MCE_FLAG_L2) != 0;
+  e->info.level = l2 ? 2 : 1;
+  if (l2) {
+    const size_t ne = (size_t)std::max<int64_t>(nnz, 1) * sizeof(int);
+    if ((h = ensure(e->src, ne)) != hipSuccess || (h = ensure(e->eroots, ne)) != hipSuccess ||
+        (h = ensure(e->pcount2, ne)) != hipSuccess || (h = ensure(e->xcount2, ne)) != hipSuccess ||
+        (h = ensure(e->fwd, (size_t)std::max(cnt, 1) * sizeof(u64))) != hipSuccess ||
+        (h = ensure(e->fwdtmp, (size_t)mce_scan_temp_words(std::max(cnt, 1)) * sizeof(u64))) != hipSuccess)
+      return hip_fail(e, h, "allocation");
+  }
 
   MceCtl* ctl = dp<MceCtl>(e->ctl);
   u64* results = reinterpret_cast<u64*>(dp<char>(e->ctl) + sizeof(MceCtl));   // hash, then the histogram
@@ -198,8 +210,13 @@ mce_status run_impl(mce_engine* e, int32_t n, int64_t nnz, const int32_t* row_pt
     return hip_fail(e, h, "peel launch");
   if (timing) (void)hipEventRecord(e->ev[2], s);
   if ((h = mce_launch_orient(n, row_ptr, col_idx, dp<int>(e->rnd), subset ? roots : nullptr, cnt,
-                             dp<int>(e->pcount), dp<int>(e->xcount), ctl, grid, s)) != hipSuccess)
+                             dp<int>(e->pcount), dp<int>(e->xcount), ctl, l2 ? dp<u64>(e->fwd) : nullptr, grid,
+                             s)) != hipSuccess)
     return hip_fail(e, h, "orient launch");
+  if (l2 && (h = mce_launch_l2_roots(n, nnz, row_ptr, col_idx, dp<int>(e->rnd), subset ? roots : nullptr, cnt,
+                                     dp<u64>(e->fwd), dp<u64>(e->fwdtmp), dp<int>(e->src), dp<int>(e->eroots),
+                                     dp<int>(e->pcount2), dp<int>(e->xcount2), ctl, grid, s)) != hipSuccess)
+    return hip_fail(e, h, "second-level roots launch");
   MceCtl* hctl = static_cast<MceCtl*>(e->host.p);
   if ((h = hipMemcpyAsync(hctl, ctl, sizeof(MceCtl), hipMemcpyDeviceToHost, s)) != hipSuccess)
     return hip_fail(e, h, "readback");
@@ -220,7 +237,16 @@ mce_status run_impl(mce_engine* e, int32_t n, int64_t nnz, const int32_t* row_pt
   e->info.isolated = (int64_t)hctl->isolated;
   e->have_order = true;
   if (hctl->status & MCE_E_LIMIT)
-    return fail(e, MCE_ERR_LIMIT, "a first-level subtree has more than 2048 later neighbours");
+    return fail(e, MCE_ERR_LIMIT, l2 ? "a second-level subtree has more than 2048 common later neighbours"
+                                     : "a first-level subtree has more than 2048 later neighbours");
+  // the subtree roots the search takes: vertex roots, or their forward edges
+  const int nsub = l2 ? hctl->l2_roots : cnt;
+  const int32_t* sroots = l2 ? dp<int>(e->eroots) : (subset ? roots : nullptr);
+  int* spc = l2 ? dp<int>(e->pcount2) : dp<int>(e->pcount);
+  int* sxc = l2 ? dp<int>(e->xcount2) : dp<int>(e->xcount);
+  e->info.roots = nsub;
+  if (l2 && (h = ensure(e->lists, (size_t)std::max(nsub, 1) * sizeof(int))) != hipSuccess)
+    return hip_fail(e, h, "allocation");
 
   // Induced-subgraph mode (section 3.4; section 4.5 picks partial when
   // Delta / d > 200, else full). Local row indices of the full subgraph must
@@ -301,7 +327,7 @@ mce_status run_impl(mce_engine* e, int32_t n, int64_t nnz, const int32_t* row_pt
         (mstack_bytes && (h = ensure(e->mstack, mstack_bytes)) != hipSuccess) ||
         (mail_bytes && (h = ensure(e->mail, mail_bytes)) != hipSuccess))
       return hip_fail(e, h, "search buffers");
-    if ((h = mce_launch_bucket(subset ? roots : nullptr, cnt, dp<int>(e->pcount), dp<int>(e->xcount), mode,
+    if ((h = mce_launch_bucket(sroots, nsub, spc, sxc, mode,
                                micro_on ? 1 : 0, off, dp<int>(e->lists), dp<u64>(e->taboff), ctl, grid, s)) !=
         hipSuccess)
       return hip_fail(e, h, "bucket launch");
@@ -330,6 +356,8 @@ mce_status run_impl(mce_engine* e, int32_t n, int64_t nnz, const int32_t* row_pt
     bp.heap_words = heap_words;
     bp.tab_off = dp<u64>(e->taboff) + off.off[c];
     bp.status = &ctl->status;
+    bp.l2 = l2 ? 1 : 0;
+    bp.src = dp<int>(e->src);
     if (!micro) {
       // enough (root, part) blocks to fill the chip, at most one part per 64-row
       // slab, and at most about 8 slabs of the largest table per part
@@ -421,6 +449,7 @@ mce_status run_impl(mce_engine* e, int32_t n, int64_t nnz, const int32_t* row_pt
   std::vector<uint64_t> hist(kHistWords, 0);
   for (size_t k = 0; k < kHistWords; k++) hist[k] = hres[1 + k];
   hist[1] += iso;
+  hist[2] += hctl->pairs;   // second-level roots that are maximal cliques by themselves
   u64 count = 0;
   size_t len = 0;
   for (size_t k = 0; k < kHistWords; k++) {
@@ -430,7 +459,7 @@ mce_status run_impl(mce_engine* e, int32_t n, int64_t nnz, const int32_t* row_pt
   hist.resize(len);
   e->hist = hist;
   e->count = count;
-  e->hash = hres[0] + iso_hash;
+  e->hash = hres[0] + iso_hash + hctl->pairs_hash;
   e->have_result = true;
 
   mce_run_stats& so = e->stats_out;
@@ -578,7 +607,9 @@ mce_status mce_create(const mce_config* cfg, mce_engine** out) {
   }
   if (c.donate_min_p < 1 || c.micro_donate_min_p < 0 || c.max_workers < 0 || c.timeout_ms < 0 ||
       c.subgraph < MCE_SUBGRAPH_AUTO ||
-      c.subgraph > MCE_SUBGRAPH_FULL)
+      c.subgraph > MCE_SUBGRAPH_FULL ||
+      (c.flags & ~(MCE_FLAG_HBM_STAGING | MCE_FLAG_PHASE_TIMES | MCE_FLAG_COUNTERS | MCE_FLAG_NO_MICRO |
+                   MCE_FLAG_L2)) != 0)
     return MCE_ERR_ARG;
   if (c.timeout_ms == 0) c.timeout_ms = 120000;
   mce_engine* e = new (std::nothrow) mce_engine();
@@ -706,7 +737,8 @@ void mce_destroy(mce_engine* e) {
   (void)hipSetDevice(e->device);
   DevBuf* bufs[] = {&e->ctl,    &e->deg,   &e->rnd,    &e->core,    &e->alive0, &e->alive1,
                     &e->front0, &e->front1, &e->bfront0, &e->bfront1, &e->pcount, &e->xcount, &e->lists,  &e->taboff, &e->scan,
-                    &e->heap,   &e->wl,    &e->slots,  &e->stats,  &e->mstack, &e->mail, &e->vitems};
+                    &e->heap,   &e->wl,    &e->slots,  &e->stats,  &e->mstack, &e->mail, &e->vitems,
+                    &e->src,    &e->fwd,   &e->fwdtmp, &e->eroots, &e->pcount2, &e->xcount2};
   for (DevBuf* b : bufs) release(*b);
   if (e->host.p) (void)hipHostFree(e->host.p);
   for (auto& ev : e->ev)

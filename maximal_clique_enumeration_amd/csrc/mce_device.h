@@ -50,7 +50,7 @@ __host__ __device__ inline long long mce_table_rows(int p, int x, int mode) {
 }
 
 // Words (u64) of a root's table in the heap:
-//   [0] p | x << 32    [1] root id    [2] hash term of the root
+//   [0] p | x << 32    [1] root id | |R| << 32    [2] hash terms of R summed
 //   [3 .. 3 + rows*W)  bit rows over the root's P (local index order = id order)
 //   then p hash terms of the P members, then p + x int32 ids (P ids, X ids).
 __host__ __device__ inline unsigned long long mce_table_words(int p, int x, int W, int mode) {
@@ -94,6 +94,10 @@ struct MceCtl {
   int min_deg[2];        // peel: smallest degree in each remaining list (by list parity)
   u64 isolated;          // roots of degree 0
   u64 isolated_hash;     // sum of their clique hashes
+  u64 pairs;             // second-level roots {r, w} with P and X empty: maximal cliques of size 2
+  u64 pairs_hash;        // sum of their clique hashes
+  int l2_roots;          // second-level roots (forward edges of the vertex roots)
+  int l2_pad;
   // per classification variant (subgraph mode, micro sub-class on/off) and
   // sub-class: roots, largest |P|, largest |X|, largest row count, heap words
   int sub_count[MCE_NVAR][MCE_NSUB];

@@ -107,6 +107,8 @@ struct BuildParams {
   int mode;              // MCE_MODE_IP / MCE_MODE_IPX
   int micro;             // micro table: full rows plus the X column of every P member
   int parts;             // > 0: split build, each root's 64-row slabs dealt over this many blocks
+  int l2;                // roots are CSR entries (v_i, v_j): second-level subtrees (section 3.2)
+  const int* src;        // second-level roots: the COO source of every CSR entry
   u64* heap;
   u64 heap_words;
   const u64* tab_off;    // each root's table offset, as an exclusive prefix sum of table sizes that
@@ -122,9 +124,18 @@ hipError_t mce_launch_peel(int n, const int* rp, const int* ci, int* deg, int* r
                            int* alive1, int* front0, int* front1, int* bfront0, int* bfront1, MceCtl* ctl,
                            u64 budget, int blocks, hipStream_t s);
 int mce_peel_max_blocks(int num_cu);
-// roots == NULL: the roots are 0 .. nroots-1
+// roots == NULL: the roots are 0 .. nroots-1. fwd == NULL: first-level roots,
+// tallied per sub-class; else the later-neighbour counts go to fwd (u64) and
+// the second-level roots are tallied by mce_launch_l2_roots.
 hipError_t mce_launch_orient(int n, const int* rp, const int* ci, const int* rnd, const int* roots, int nroots,
-                             int* pcount, int* xcount, MceCtl* ctl, int blocks, hipStream_t s);
+                             int* pcount, int* xcount, MceCtl* ctl, u64* fwd, int blocks, hipStream_t s);
+// Second-level roots (Algorithm 4) of the vertex roots: COO sources (src, nnz),
+// the forward edges as CSR positions (eroots, at most nnz; their number goes to
+// ctl->l2_roots), and per root |P| and |X| (pcount, xcount) and the tallies.
+// fwd holds the vertex roots' later-neighbour counts; fwd_tmp mce_scan_temp_words(nroots).
+hipError_t mce_launch_l2_roots(int n, long long nnz, const int* rp, const int* ci, const int* rnd,
+                               const int* roots, int nroots, u64* fwd, u64* fwd_tmp, int* src, int* eroots,
+                               int* pcount, int* xcount, MceCtl* ctl, int blocks, hipStream_t s);
 // Groups the roots by sub-class into `lists` and writes each one's table size
 // (u64 words) at the same position of `words`.
 hipError_t mce_launch_bucket(const int* roots, int nroots, const int* pcount, const int* xcount, int mode,

@@ -135,7 +135,7 @@ __global__ __launch_bounds__(64) void k_search_micro(MicroParams prm) {
         fP = p >= 64 ? ~0ull : ((1ull << p) - 1);
         fXX = x >= 64 ? ~0ull : ((1ull << x) - 1);
         fS = T[2];
-        fK = 1;
+        fK = (int)(T[1] >> 32);   // |R| at the root
         has = true;
         pcm = fP;
         pcx = fXX;

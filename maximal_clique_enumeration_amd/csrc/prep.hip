@@ -864,11 +864,41 @@ __global__ __launch_bounds__(PEEL_THREADS) void k_peel(int n, const int* __restr
 // micro sub-class on or off): count, largest |P|, |X| and row count, heap
 // words, so that the host can pick the variant and size every launch from one
 // read-back.
+// Tallies a wave's roots (one per lane, `valid` set) per classification variant
+// (subgraph mode, micro sub-class on or off) and sub-class: count, largest |P|,
+// |X| and row count, heap words. Whole wave.
+__device__ void tally_roots(MceCtl* ctl, bool valid, int p, int x) {
+  const int lane = lane_id();
+  for (int var = 0; var < MCE_NVAR; var++) {
+    const int mode = var & 1;
+    const int sub = valid ? mce_sub_of(p, x, mode, (var >> 1) == 0) : -1;
+    u64 pending = ballot(valid);
+    while (pending) {
+      const int s = read_lane(sub, __builtin_ctzll(pending));
+      const bool mine = sub == s;
+      const u64 m = ballot(mine);
+      pending &= ~m;
+      const u32 mp = wave_max_u32(mine ? (u32)p : 0u);
+      const u32 mx = wave_max_u32(mine ? (u32)x : 0u);
+      const u32 mr = wave_max_u32(mine ? (u32)mce_table_rows(p, x, s == MCE_SUB_MICRO ? MCE_MODE_IPX : mode) : 0u);
+      const u64 words = wave_sum_u64(mine ? mce_sub_table_words(p, x, s, mode) : 0ull);
+      if (lane == 0) {
+        atomicAdd(&ctl->sub_count[var][s], __popcll(m));
+        atomicMax(&ctl->sub_maxp[var][s], (int)mp);
+        atomicMax(&ctl->sub_maxx[var][s], (int)mx);
+        atomicMax(&ctl->sub_maxr[var][s], (int)mr);
+        atomicAdd(&ctl->sub_words[var][s], words);
+      }
+    }
+  }
+}
+
 #define ORIENT_LONG 128   // rows longer than this are counted by the whole wavefront
 
 __global__ __launch_bounds__(256) void k_orient(int n, const int* __restrict__ rp, const int* __restrict__ ci,
                                                  const int* __restrict__ rnd, const int* __restrict__ roots,
-                                                 int nroots, int* pcount, int* xcount, MceCtl* ctl) {
+                                                 int nroots, int* pcount, int* xcount, MceCtl* ctl, u64* fwd,
+                                                 int tally) {
   if (ld_relaxed(&ctl->status) != 0) return;
   const int lane = lane_id();
   const int gsize = gridDim.x * blockDim.x;
@@ -917,6 +947,7 @@ __global__ __launch_bounds__(256) void k_orient(int n, const int* __restrict__ r
       x = (b - a) - p;
       pcount[i] = p;
       xcount[i] = x;
+      if (fwd) fwd[i] = (u64)p;
       if (b == a) {
         iso++;
         iso_hash += mce_clique_term(mce_vertex_term(v), 1);
@@ -924,31 +955,12 @@ __global__ __launch_bounds__(256) void k_orient(int n, const int* __restrict__ r
       pmax = max(pmax, p);
       xmax = max(xmax, x);
       dmax = max(dmax, b - a);
-      if (p > MCE_MAX_P) lim |= 1u;
+      if (tally && p > MCE_MAX_P) lim |= 1u;
       valid = p > 0 && p <= MCE_MAX_P;
+    } else if (i < cnt && fwd) {
+      fwd[i] = 0;
     }
-    for (int var = 0; var < MCE_NVAR; var++) {
-      const int mode = var & 1;
-      const int sub = valid ? mce_sub_of(p, x, mode, (var >> 1) == 0) : -1;
-      u64 pending = ballot(valid);
-      while (pending) {
-        const int s = read_lane(sub, __builtin_ctzll(pending));
-        const bool mine = sub == s;
-        const u64 m = ballot(mine);
-        pending &= ~m;
-        const u32 mp = wave_max_u32(mine ? (u32)p : 0u);
-        const u32 mx = wave_max_u32(mine ? (u32)x : 0u);
-        const u32 mr = wave_max_u32(mine ? (u32)mce_table_rows(p, x, s == MCE_SUB_MICRO ? MCE_MODE_IPX : mode) : 0u);
-        const u64 words = wave_sum_u64(mine ? mce_sub_table_words(p, x, s, mode) : 0ull);
-        if (lane == 0) {
-          atomicAdd(&ctl->sub_count[var][s], __popcll(m));
-          atomicMax(&ctl->sub_maxp[var][s], (int)mp);
-          atomicMax(&ctl->sub_maxx[var][s], (int)mx);
-          atomicMax(&ctl->sub_maxr[var][s], (int)mr);
-          atomicAdd(&ctl->sub_words[var][s], words);
-        }
-      }
-    }
+    if (tally) tally_roots(ctl, valid, p, x);
   }
   const u64 wiso = wave_sum_u64(iso);
   const u64 whash = wave_sum_u64(iso_hash);
@@ -1039,10 +1051,137 @@ int mce_peel_max_blocks(int num_cu) {
   return num_cu;
 }
 
+// ------------------------------------------------------------------ second-level subtrees
+// Section 3.2, Algorithm 4: one subtree per edge {v_i, v_j}; v_j the later end,
+// R = {v_i, v_j}, P = the common neighbours after v_j, X = those before it. The
+// roots of a run are the forward edges (v_i, v_j), v_j after v_i, of its vertex
+// roots (a vertex of degree 0 is a clique of its own, counted by k_orient).
+
+// The COO source of every CSR entry (the page keeps CSR+COO for second-level
+// subtrees): one wavefront per row.
+__global__ __launch_bounds__(256) void k_coo_src(int n, const int* __restrict__ rp, int* src) {
+  const int lane = lane_id();
+  const int wave = (blockIdx.x * blockDim.x + threadIdx.x) / MCE_WAVE;
+  const int nwaves = gridDim.x * blockDim.x / MCE_WAVE;
+  for (int v = wave; v < n; v += nwaves)
+    for (int e = rp[v] + lane; e < rp[v + 1]; e += MCE_WAVE) src[e] = v;
+}
+
+// The forward edges of every vertex root, as CSR positions, at the root's
+// offset (an exclusive prefix sum of the later-neighbour counts). One wavefront
+// per root; the wave of the last root writes the total.
+__global__ __launch_bounds__(256) void k_l2_expand(int n, const int* __restrict__ rp, const int* __restrict__ ci,
+                                                    const int* __restrict__ rnd, const int* __restrict__ roots,
+                                                    int nroots, const u64* __restrict__ off, int* eroots,
+                                                    MceCtl* ctl) {
+  if (ld_relaxed(&ctl->status) != 0) return;
+  const int lane = lane_id();
+  const int wave = (blockIdx.x * blockDim.x + threadIdx.x) / MCE_WAVE;
+  const int nwaves = gridDim.x * blockDim.x / MCE_WAVE;
+  for (int i = wave; i < nroots; i += nwaves) {
+    const int r = roots ? roots[i] : i;
+    const int a = rp[r], b = rp[r + 1];
+    const int rr = rnd[r];
+    int pos = (int)off[i];
+    for (int base = a; base < b; base += MCE_WAVE) {
+      const int e = base + lane;
+      const bool lat = e < b && order_after(rnd[ci[e]], ci[e], rr, r);
+      const u64 m = ballot(lat);
+      if (lat) eroots[pos + mbcnt(m)] = e;
+      pos += __popcll(m);
+    }
+    if (i == nroots - 1 && lane == 0) ctl->l2_roots = pos;
+  }
+}
+
+// Per second-level root: |P| and |X| by intersecting the two rows (each entry
+// of the shorter one is searched in the longer one), then the same tallies as
+// k_orient. A wavefront takes G consecutive roots in turn, lane t keeping root
+// t's counts, so that a tally covers up to 64 roots. Roots with P and X empty
+// are maximal cliques of size 2, counted here.
+__global__ __launch_bounds__(256) void k_orient_l2(const int* __restrict__ rp, const int* __restrict__ ci,
+                                                    const int* __restrict__ rnd, const int* __restrict__ src,
+                                                    const int* __restrict__ eroots, int* pcount, int* xcount,
+                                                    MceCtl* ctl) {
+  if (ld_relaxed(&ctl->status) != 0) return;
+  const int lane = lane_id();
+  const int wave = (blockIdx.x * blockDim.x + threadIdx.x) / MCE_WAVE;
+  const int nwaves = gridDim.x * blockDim.x / MCE_WAVE;
+  const int total = ld_relaxed(&ctl->l2_roots);
+  const int G = max(8, min(MCE_WAVE, (total + nwaves - 1) / nwaves));   // 8: few tallies on small graphs
+  u64 pairs = 0, pairs_hash = 0;
+  u32 lim = 0;
+  for (int g0 = wave * G; g0 < total; g0 += nwaves * G) {
+    int p = 0, x = 0;
+    bool mine = false;
+    for (int t = 0; t < G && g0 + t < total; t++) {
+      const int e = eroots[g0 + t];
+      const int vi = src[e], vj = ci[e];
+      const int ai = rp[vi], bi = rp[vi + 1], aj = rp[vj], bj = rp[vj + 1];
+      const bool si = bi - ai <= bj - aj;   // scan the shorter row
+      const int sa = si ? ai : aj, sb = si ? bi : bj, oa = si ? aj : ai, ob = si ? bj : bi;
+      const int rj = rnd[vj];
+      u32 cp = 0, cx = 0;
+      for (int k = sa + lane; k < sb; k += MCE_WAVE) {
+        const int c = ci[k];
+        if (csr_range_has(ci, oa, ob, c)) {
+          if (order_after(rnd[c], c, rj, vj)) cp++;
+          else cx++;
+        }
+      }
+      cp = wave_sum_u32(cp);
+      cx = wave_sum_u32(cx);
+      if (lane == t) {
+        p = (int)cp;
+        x = (int)cx;
+        mine = true;
+        if (cp == 0 && cx == 0) {
+          pairs++;
+          pairs_hash += mce_clique_term(mce_vertex_term(vi) + mce_vertex_term(vj), 2);
+        }
+      }
+    }
+    if (mine) {
+      pcount[g0 + lane] = p;
+      xcount[g0 + lane] = x;
+      if (p > MCE_MAX_P) lim |= 1u;
+    }
+    tally_roots(ctl, mine && p > 0 && p <= MCE_MAX_P, p, x);
+  }
+  const u64 wp = wave_sum_u64(pairs), wh = wave_sum_u64(pairs_hash);
+  const u32 wl = wave_or_u32(lim);
+  if (lane == 0) {
+    if (wp) {
+      atomicAdd(&ctl->pairs, wp);
+      atomicAdd(&ctl->pairs_hash, wh);
+    }
+    if (wl) atomicOr(&ctl->status, MCE_E_LIMIT);
+  }
+}
+
+hipError_t mce_launch_l2_roots(int n, long long nnz, const int* rp, const int* ci, const int* rnd,
+                               const int* roots, int nroots, u64* fwd, u64* fwd_tmp, int* src, int* eroots,
+                               int* pcount, int* xcount, MceCtl* ctl, int blocks, hipStream_t s) {
+  hipError_t e;
+  const int nbr = (int)std::max(1LL, std::min((long long)blocks, ((long long)n + 3) / 4));
+  hipLaunchKernelGGL(k_coo_src, dim3(nbr), dim3(256), 0, s, n, rp, src);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if ((e = mce_launch_scan(fwd, nroots, fwd_tmp, s)) != hipSuccess) return e;
+  const int nbe = (int)std::max(1LL, std::min((long long)blocks, ((long long)nroots + 3) / 4));
+  hipLaunchKernelGGL(k_l2_expand, dim3(nbe), dim3(256), 0, s, n, rp, ci, rnd, roots, nroots, (const u64*)fwd,
+                     eroots, ctl);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  const int nbo = (int)std::max(1LL, std::min((long long)blocks, nnz / 8 + 1));
+  hipLaunchKernelGGL(k_orient_l2, dim3(nbo), dim3(256), 0, s, rp, ci, rnd, (const int*)src, (const int*)eroots,
+                     pcount, xcount, ctl);
+  return hipGetLastError();
+}
+
 hipError_t mce_launch_orient(int n, const int* rp, const int* ci, const int* rnd, const int* roots, int nroots,
-                             int* pcount, int* xcount, MceCtl* ctl, int blocks, hipStream_t s) {
+                             int* pcount, int* xcount, MceCtl* ctl, u64* fwd, int blocks, hipStream_t s) {
   const int nb = max(1, min(blocks, (nroots + 255) / 256));
-  hipLaunchKernelGGL(k_orient, dim3(nb), dim3(256), 0, s, n, rp, ci, rnd, roots, nroots, pcount, xcount, ctl);
+  hipLaunchKernelGGL(k_orient, dim3(nb), dim3(256), 0, s, n, rp, ci, rnd, roots, nroots, pcount, xcount, ctl, fwd,
+                     fwd ? 0 : 1);
   return hipGetLastError();
 }
 

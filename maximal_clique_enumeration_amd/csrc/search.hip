@@ -225,7 +225,9 @@ __global__ __launch_bounds__(64) void k_search(SearchParams prm) {
       for (int i = lane; i < p; i += MCE_WAVE) pid[i] = gids[i];
     }
     if (!phase2) {
-      // a first-level subtree: R = {root}, P = P_root, X_P = {}, X_X = X_root
+      // a subtree root: R = the root's vertices (|R| and their hash terms summed in
+      // the table), P = P_root, X_P = {}, X_X = X_root
+      k0 = (int)(T[1] >> 32);
       s = T[2];
       lpx = x;
       if (lane < W) {
@@ -635,6 +637,7 @@ __global__ __launch_bounds__(64) void k_search_w1(SearchParams prm) {
     const u64 myhv = lane < p ? ghv[lane] : 0ull;
     const int mypid = (!IPX && lane < p) ? gids[lane] : 0;
     if (!phase2) {
+      k0 = (int)uni((u32)(T[1] >> 32));
       s = uni(T[2]);
       lpx = x;
       P = p >= 64 ? ~0ull : ((1ull << p) - 1);
@@ -996,7 +999,7 @@ SearchLayout mce_search_layout(int sub, int mode, int pcap, int xcap, int rcap, 
   L.xcap = std::max(xcap, 0);
   L.rcap = std::max(rcap, 1);
   L.levels = L.pcap;
-  L.hcap = L.pcap + 2;
+  L.hcap = L.pcap + 3;   // clique sizes up to |R at the root| + |P| <= 2 + pcap
   const size_t rec = (size_t)REC_WORDS(W);
   L.srows = !force_hbm && light && L.wclass <= 2;
   const size_t stack_words = (size_t)L.levels * rec;

@@ -9,8 +9,8 @@
 //    are then looked up in the CSR during the search).
 //
 // Table layout (u64 words, see mce_table_words; micro tables add the X column of
-// every P member after the rows, see mce_micro_table_words): header (p | x << 32), root id,
-// root hash term, rows (row a = bit b set iff L[a] ~ P[b], local order = id
+// every P member after the rows, see mce_micro_table_words): header (p | x << 32), root id
+// and |R| at the root, R's hash terms summed, rows (row a = bit b set iff L[a] ~ P[b], local order = id
 // order, P first), p hash terms of the P members, p + x int32 ids.
 //
 // Two builds:
@@ -25,6 +25,50 @@
 // each P member in that CSR row.
 #include "mce_device.h"
 #include "mce_internal.h"
+
+// ------------------------------------------------------------------ a root's neighbourhood
+// First-level root r (R = {r}): N(r), split at r. Second-level root, the CSR
+// entry (v_i, v_j) with v_j the later end (R = {v_i, v_j}; section 3.2,
+// Algorithm 4): N(v_i) n N(v_j), split at v_j, found by scanning the shorter of
+// the two rows and searching the other. Either way the members come in id order.
+struct RootHood {
+  int sa, sb;      // the row scanned
+  int oa, ob;      // the row searched for membership (oa < 0: none)
+  int piv, pivr;   // P = the members after piv (round pivr), X = the others
+  int k0;          // |R|
+  u64 term;        // R's hash terms summed
+};
+
+__device__ __forceinline__ RootHood root_hood(const BuildParams& prm, int rid) {
+  const int* __restrict__ rp = prm.rp;
+  RootHood h;
+  if (!prm.l2) {
+    h.sa = rp[rid];
+    h.sb = rp[rid + 1];
+    h.oa = h.ob = -1;
+    h.piv = rid;
+    h.pivr = prm.rnd[rid];
+    h.k0 = 1;
+    h.term = mce_vertex_term(rid);
+  } else {
+    const int vi = prm.src[rid], vj = prm.ci[rid];
+    const int ai = rp[vi], bi = rp[vi + 1], aj = rp[vj], bj = rp[vj + 1];
+    const bool si = bi - ai <= bj - aj;
+    h.sa = si ? ai : aj;
+    h.sb = si ? bi : bj;
+    h.oa = si ? aj : ai;
+    h.ob = si ? bj : bi;
+    h.piv = vj;
+    h.pivr = prm.rnd[vj];
+    h.k0 = 2;
+    h.term = mce_vertex_term(vi) + mce_vertex_term(vj);
+  }
+  return h;
+}
+
+__device__ __forceinline__ bool hood_has(const int* __restrict__ ci, const RootHood& h, int u) {
+  return h.oa < 0 || csr_range_has(ci, h.oa, h.ob, u);
+}
 
 // ------------------------------------------------------------------ hash of P
 // LDS open-addressing hash (key = vertex id, value = local index) over P.
@@ -104,15 +148,15 @@ __global__ __launch_bounds__(64) void k_build_micro(BuildParams prm) {
   const int* __restrict__ rnd = prm.rnd;
   for (int i = blockIdx.x; i < prm.nroots; i += gridDim.x) {
     const int r = prm.roots[i];
-    const int a = rp[r], b = rp[r + 1];
-    const int rr = rnd[r];
-    // P (later neighbours) and X (earlier ones), each in id order
+    const RootHood hd = root_hood(prm, r);
+    const int a = hd.sa, b = hd.sb;
+    // P (members after the root) and X (the others), each in id order
     int np = 0, nx = 0;
     for (int base = a; base < b; base += MCE_WAVE) {
       const int e = base + lane;
-      const bool valid = e < b;
-      const int u = valid ? ci[e] : 0;
-      const bool lat = valid && order_after(rnd[u], u, rr, r);
+      const int u = e < b ? ci[e] : 0;
+      const bool valid = e < b && hood_has(ci, hd, u);
+      const bool lat = valid && order_after(rnd[u], u, hd.pivr, hd.piv);
       const u64 lm = ballot(lat), xm = ballot(valid && !lat);
       if (lat && np + mbcnt(lm) < MCE_MICRO_MAX) s_id[np + mbcnt(lm)] = u;
       if (valid && !lat && nx + mbcnt(xm) < MCE_MICRO_MAX) s_id[MCE_MICRO_MAX + nx + mbcnt(xm)] = u;
@@ -136,8 +180,8 @@ __global__ __launch_bounds__(64) void k_build_micro(BuildParams prm) {
     int* ids = (int*)(hvs + np);
     if (lane == 0) {
       T[0] = (u64)(u32)np | ((u64)(u32)nx << 32);
-      T[1] = (u64)(u32)r;
-      T[2] = mce_vertex_term(r);
+      T[1] = (u64)(u32)r | ((u64)(u32)hd.k0 << 32);   // root id, |R| at the root
+      T[2] = hd.term;
     }
     for (int h = lane; h < (1 << HB); h += MCE_WAVE) s_hk[h] = -1;
     __syncthreads();   // the ids are in LDS, the hash is clear
@@ -247,16 +291,16 @@ __global__ __launch_bounds__(256) void k_build_head(BuildParams prm) {
   const int* __restrict__ rnd = prm.rnd;
   for (int i = blockIdx.x; i < prm.nroots; i += gridDim.x) {
     const int r = prm.roots[i];
-    const int a = rp[r], b = rp[r + 1];
-    const int rr = rnd[r];
+    const RootHood hd = root_hood(prm, r);
+    const int a = hd.sa, b = hd.sb;
     const int per = ((b - a + 4 * MCE_WAVE - 1) / (4 * MCE_WAVE)) * MCE_WAVE;
     const int wa = min(b, a + wv * per), wb = min(b, wa + per);
     int np = 0, nx = 0;
     for (int base = wa; base < wb; base += MCE_WAVE) {
       const int e = base + lane;
-      const bool valid = e < wb;
-      const int u = valid ? ci[e] : 0;
-      const bool lat = valid && order_after(rnd[u], u, rr, r);
+      const int u = e < wb ? ci[e] : 0;
+      const bool valid = e < wb && hood_has(ci, hd, u);
+      const bool lat = valid && order_after(rnd[u], u, hd.pivr, hd.piv);
       np += __popcll(ballot(lat));
       nx += __popcll(ballot(valid && !lat));
     }
@@ -292,14 +336,14 @@ __global__ __launch_bounds__(256) void k_build_head(BuildParams prm) {
     int* ids = (int*)(hvs + NP);
     if (threadIdx.x == 0) {
       T[0] = (u64)(u32)NP | ((u64)(u32)NX << 32);
-      T[1] = (u64)(u32)r;
-      T[2] = mce_vertex_term(r);
+      T[1] = (u64)(u32)r | ((u64)(u32)hd.k0 << 32);   // root id, |R| at the root
+      T[2] = hd.term;
     }
     for (int base = wa; base < wb; base += MCE_WAVE) {
       const int e = base + lane;
-      const bool valid = e < wb;
-      const int u = valid ? ci[e] : 0;
-      const bool lat = valid && order_after(rnd[u], u, rr, r);
+      const int u = e < wb ? ci[e] : 0;
+      const bool valid = e < wb && hood_has(ci, hd, u);
+      const bool lat = valid && order_after(rnd[u], u, hd.pivr, hd.piv);
       const u64 lm = ballot(lat), xm = ballot(valid && !lat);
       if (lat) {
         const int j = pp + mbcnt(lm);

@@ -49,6 +49,23 @@ def test_status_strings_without_device(lib):
     assert cfg.struct_size == ctypes.sizeof(mce.mce_config)
 
 
+def test_flag_values_match_the_header():
+    text = open(os.path.join(ROOT, "include", "mce.h")).read()
+    flags = dict(re.findall(r"#define (MCE_FLAG_[A-Z0-9_]+) (\d+)u", text))
+    assert "MCE_FLAG_L2" in flags
+    for name, value in flags.items():
+        assert getattr(mce, name) == int(value), name
+
+
+def test_unknown_flags_are_rejected_before_any_device_work(lib):
+    cfg = mce.mce_config()
+    assert mce.mce_config_init(cfg) == 0
+    cfg.flags = 1 << 12
+    h = ctypes.c_void_p()
+    assert mce.mce_create(cfg, h) == mce.MCE_ERR_ARG
+    assert not h.value
+
+
 def test_null_arguments_are_rejected(lib):
     lib.mce_result.restype = ctypes.c_int
     assert lib.mce_result(None, None, None, None, 0, None) == mce.MCE_ERR_ARG

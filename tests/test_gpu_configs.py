@@ -53,14 +53,18 @@ def same(got, want):
     assert f"0x{got.hash:016x}" == want["hash"]
 
 
+@pytest.mark.parametrize("level", [1, 2])
 @pytest.mark.parametrize("subgraph", ["auto", "partial", "full"])
 @pytest.mark.parametrize("idx", [0, 1, 3])
-def test_whole_graph(idx, subgraph):
+def test_whole_graph(idx, subgraph, level):
+    """level 2: second-level subtrees (section 3.2), the same cliques."""
     g, rp, ci = graph(idx)
-    print(f"case cfg{idx} whole graph, subgraph {subgraph}", flush=True)
-    with mce.Engine(device=0, timeout_ms=60000, subgraph=subgraph) as e:
+    print(f"case cfg{idx} whole graph, subgraph {subgraph}, level {level}", flush=True)
+    with mce.Engine(device=0, timeout_ms=60000, subgraph=subgraph, level=level) as e:
         same(e.run(rp, ci), GOLD[str(idx)]["whole"])
-        assert e.graph_info()["degeneracy"] == GOLD[str(idx)]["degeneracy"]
+        info = e.graph_info()
+        assert info["degeneracy"] == GOLD[str(idx)]["degeneracy"]
+        assert info["level"] == level
 
 
 @pytest.mark.timeout(900)   # generating the 4M-vertex graph takes about 1.5 minutes on the host
@@ -86,3 +90,19 @@ def test_root_sample(idx, kind):
         ha = a.hist + [0] * (n - len(a.hist))
         hb = b.hist + [0] * (n - len(b.hist))
         assert [x + y for x, y in zip(ha, hb)] == got.hist
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("kind", ["uniform", "heavy"])
+@pytest.mark.parametrize("idx", [2, 4])
+def test_root_sample_second_level(idx, kind):
+    """The same root samples through second-level subtrees (section 3.2): the
+    subtrees of the edges leaving the sampled roots carry exactly the cliques
+    whose earliest vertex is a sampled root."""
+    g, rp, ci = graph(idx)
+    want = GOLD[str(idx)][kind]
+    roots = np.asarray(want["roots"], np.int32)
+    print(f"case cfg{idx} {kind} roots ({roots.size}), level 2", flush=True)
+    with mce.Engine(device=0, timeout_ms=60000, level=2) as e:
+        same(e.run(rp, ci, roots=torch.from_numpy(roots).to(DEV)), want)
+        assert e.graph_info()["level"] == 2

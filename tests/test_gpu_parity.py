@@ -20,16 +20,18 @@ import maximal_clique_enumeration_amd as mce  # noqa: E402
 DEV = torch.device("cuda", 0)
 
 
-@pytest.fixture(scope="module", params=["partial", "full", "partial-nomicro", "full-nomicro"])
+@pytest.fixture(scope="module", params=["partial", "full", "partial-nomicro", "full-nomicro", "partial-l2",
+                                        "full-l2"])
 def eng(request):
     """One engine per induced-subgraph encoding (section 3.4), with the micro
     kernel (one search-tree node per lane for subtrees with |P|, |X| <= 64) on
-    and off: every case that takes this fixture runs under all four."""
+    and off, and with second-level subtrees (section 3.2): every case that takes
+    this fixture runs under all six."""
     if not mce.lib_built():
         from maximal_clique_enumeration_amd import build
         build.build()
-    sub, _, nomicro = request.param.partition("-")
-    e = mce.Engine(device=0, timeout_ms=20000, subgraph=sub, micro=not nomicro)
+    sub, _, opt = request.param.partition("-")
+    e = mce.Engine(device=0, timeout_ms=20000, subgraph=sub, micro=opt != "nomicro", level=2 if opt == "l2" else 1)
     yield e
     e.close()
 
