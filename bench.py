@@ -43,6 +43,13 @@ def parse():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--config", type=int, default=1, help="workload index (default 1: Moon-Moser 45)")
+    ap.add_argument("--sample", choices=["uniform", "heavy"], default=None,
+                    help="run on the workload's seeded root sample (tests/golden/configs.json) instead of "
+                         "the whole graph: the maximal cliques whose earliest vertex is a sampled root")
+    ap.add_argument("--level", type=int, choices=[1, 2], default=1,
+                    help="first-level (1, default) or second-level (2) subtrees")
+    ap.add_argument("--balance", action="store_true",
+                    help="add each search launch's load balance (from the per-wavefront trace)")
     ap.add_argument("--seed", type=int, default=1)
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -90,21 +97,52 @@ def algorithmic_ops(st):
             + st["xx_tests"] * OPS_PER_XX_TEST + st["leaves"] * OPS_PER_LEAF)
 
 
-def cpu_baseline(g, budget_s):
-    """The oracle on the same graph, repeated until the budget is used (one
-    thread). Reports cliques per second over the whole sample."""
+def cpu_baseline(g, budget_s, roots=None):
+    """The oracle on this host, single-threaded, for about budget_s seconds: the
+    whole graph repeated, or (root sample) its roots in chunks of 16, in order.
+    Reports cliques per second over what it ran."""
     import oracle
     reps, cliques = 0, 0
     t0 = time.perf_counter()
-    while True:
-        r = oracle.mce(g.n, g.row_ptr, g.col_idx)
-        reps += 1
-        cliques += r.count
+    if roots is None:
+        while True:
+            r = oracle.mce(g.n, g.row_ptr, g.col_idx)
+            reps += 1
+            cliques += r.count
+            t_used = time.perf_counter() - t0
+            if t_used >= budget_s or reps >= 1000:
+                break
+        sample = f"whole graph x{reps} runs (ordering + enumeration), {t_used:.1f} s, 1 thread"
+    else:
+        import numpy as np
+        _, rnd, _ = oracle.peel(g.n, g.row_ptr, g.col_idx)
+        done = 0
+        for i in range(0, len(roots), 16):
+            chunk = np.asarray(roots[i:i + 16], np.int32)
+            cliques += oracle.mce(g.n, g.row_ptr, g.col_idx, roots=chunk, rnd=rnd).count
+            done += chunk.size
+            if time.perf_counter() - t0 >= budget_s:
+                break
         t_used = time.perf_counter() - t0
-        if t_used >= budget_s or reps >= 1000:
-            break
+        sample = f"first {done} of {len(roots)} sampled roots (ordering + enumeration), {t_used:.1f} s, 1 thread"
     return {"value": cliques / t_used, "unit": "maximal cliques/s", "cores": 1, "kind": "oracle",
-            "sample": f"whole graph x{reps} runs (ordering + enumeration), {t_used:.1f} s, 1 thread"}
+            "sample": sample}
+
+
+def balance(trace):
+    """Per search launch: the share of wavefront-time spent holding a task
+    (busy ticks over waves x the launch's span), and the largest wavefront's node
+    count over the mean (section 4.3's load measure)."""
+    out = []
+    for lid in sorted({t["launch"] for t in trace}):
+        rs = [t for t in trace if t["launch"] == lid]
+        span = max(t["end_tick"] for t in rs) - min(t["start_tick"] for t in rs)
+        nodes = [t["nodes"] for t in rs]
+        mean = sum(nodes) / len(nodes)
+        out.append({"launch": lid, "waves": len(rs),
+                    "busy_frac": sum(t["busy_ticks"] for t in rs) / (len(rs) * span) if span else None,
+                    "max_over_mean_nodes": max(nodes) / mean if mean else None})
+    return out
 
 
 def main():
@@ -123,6 +161,14 @@ def main():
     dev = torch.device("cuda", 0)
     rp = torch.from_numpy(g.row_ptr).to(dev)
     ci = torch.from_numpy(g.col_idx).to(dev)
+    roots_host, roots = None, None
+    if args.sample:
+        with open(os.path.join(ROOT, "tests", "golden", "configs.json")) as f:
+            gold = json.load(f)[str(args.config)]
+        if args.sample not in gold:
+            raise SystemExit(f"workload {args.config} has no {args.sample} root sample")
+        roots_host = gold[args.sample]["roots"]
+        roots = torch.tensor(roots_host, dtype=torch.int32, device=dev)
     if args.calib_copy_mb:
         src = torch.empty(args.calib_copy_mb << 18, dtype=torch.int32, device=dev)
         src.fill_(1)
@@ -132,14 +178,14 @@ def main():
     torch.cuda.synchronize()
 
     # counting run: exact algorithmic work of the search (deterministic tree)
-    with mce.Engine(device=0, counters=True, timeout_ms=100000) as ecnt:
-        ref = ecnt.run(rp, ci)
+    with mce.Engine(device=0, counters=True, timeout_ms=100000, level=args.level) as ecnt:
+        ref = ecnt.run(rp, ci, roots=roots)
         cst = ecnt.stats()
     ops = algorithmic_ops(cst)
 
-    eng = mce.Engine(device=0, phase_times=True, timeout_ms=100000)
+    eng = mce.Engine(device=0, phase_times=True, timeout_ms=100000, level=args.level)
     for _ in range(args.warmup):
-        r = eng.run(rp, ci)
+        r = eng.run(rp, ci, roots=roots)
         if r.key() != ref.key():
             raise SystemExit("results differ between runs")
     torch.cuda.synchronize()
@@ -149,7 +195,7 @@ def main():
     for _ in range(args.steps):
         torch.cuda.synchronize()
         t0 = time.perf_counter()
-        r = eng.run(rp, ci)
+        r = eng.run(rp, ci, roots=roots)
         torch.cuda.synchronize()
         times.append(time.perf_counter() - t0)
         st = eng.stats()
@@ -165,14 +211,15 @@ def main():
     launches = max(1, st["launches"])
     achieved = ops / avg_search_s if avg_search_s > 0 else 0.0
     kernel = "k_search_micro" if st["steps"] > 0 and launches == 1 else "k_search_w1"
-    tj = load_profile(args.traffic_json, args.config, kernel)
+    default_workload = args.sample is None and args.level == 1
+    tj = load_profile(args.traffic_json, args.config, kernel) if default_workload else None
     traffic = tj.get("bytes_per_launch") if tj else None
     roofline = {"bound": "alu", "achieved": achieved / 1e12, "peak": VALU_INT32_PEAK / 1e12,
                 "unit": "Tops/s (int32 vector lane-ops)", "frac": achieved / VALU_INT32_PEAK,
                 "traffic": traffic, "kernel": kernel,
                 "search_ms_per_step": avg_search_s * 1e3, "launches_per_step": launches,
                 "ops_per_step": ops}
-    cj = load_profile(args.counters_json, args.config, kernel)
+    cj = load_profile(args.counters_json, args.config, kernel) if default_workload else None
     if cj and avg_search_s > 0:
         # VALU issue: each wave64 VALU instruction occupies a 16-lane SIMD for 4 cycles
         simd_cycles = 256 * 4 * 2.4e9 * avg_search_s
@@ -199,7 +246,7 @@ def main():
                    "subgraph": "full" if info["subgraph"] == mce.MCE_SUBGRAPH_FULL else "partial",
                    "parallelism": "single GPU: one search-tree node per lane (micro kernel), frame stacks "
                                   "per wavefront, branch requests between wavefronts",
-                   "seed": args.seed},
+                   "seed": args.seed, "roots": args.sample or "all", "subtrees": f"level {args.level}"},
         "roofline": roofline,
         "detail": {"e2e_ms_min": min(times) * 1e3, "e2e_ms_median": sorted(times)[len(times) // 2] * 1e3,
                    "nodes": st["nodes"], "donations": st["donations"], "workers": st["workers"],
@@ -212,8 +259,10 @@ def main():
                    "pivot_rows": cst["pivot_rows"], "branches": cst["branches"],
                    "xx_tests": cst["xx_tests"], "leaves": cst["leaves"], "hash": hex(ref.hash)},
     }
+    if args.balance:
+        out["detail"]["balance"] = balance(eng.worker_trace())
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(g, args.cpu_seconds)
+        out["cpu_baseline"] = cpu_baseline(g, args.cpu_seconds, roots_host)
     else:
         out["cpu_baseline"] = None
     eng.close()
