@@ -123,6 +123,7 @@ constexpr size_t kHistWords = MCE_MAX_P + 3;   // global histogram entries (size
 constexpr size_t kIoBytes = sizeof(MceCtl) + (1 + kHistWords) * sizeof(u64);
 static_assert(sizeof(MceCtl) % sizeof(u64) == 0, "results follow the control block");
 constexpr int kMicroStack = 4096;              // frames per wavefront stack of the micro search
+constexpr int kMicroCoopRootsPerWave = 4;     // micro launches with this many roots per wave share pivot scans
 // Tables other than micro ones are built by the split build: a root's rows are
 // dealt over several blocks, about this many (root, part) blocks per CU.
 constexpr int kSplitBlocksPerCu = 16;
@@ -386,6 +387,10 @@ mce_status run_impl(mce_engine* e, int32_t n, int64_t nnz, const int32_t* row_pt
       mp.wl = dp<MceWl>(e->wl);
       mp.donate_min_p = e->cfg.micro_donate_min_p > 0 ? (int)e->cfg.micro_donate_min_p : 10;
       mp.worker_list = e->cfg.worker_list ? 1 : 0;
+      // Cooperative pivot scans pay when every wave works through its own
+      // small roots; with few large roots they spread frames thinner over the
+      // waves and cost steps (Moon-Moser n = 45: 271k -> 300k steps).
+      mp.coop = counts[c] >= kMicroCoopRootsPerWave * pl.nw ? 1 : 0;
       mp.budget = budget;
       mp.t_run = &ctl->t_run;
       mp.status = &ctl->status;

@@ -91,6 +91,7 @@ struct MicroParams {
   MceWl* wl;
   int donate_min_p;
   int worker_list;
+  int coop;              // share pivot scans out over lane groups (many more roots than waves)
   u64 budget;
   const u64* t_run;
   u32* status;

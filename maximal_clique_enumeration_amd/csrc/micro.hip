@@ -21,7 +21,9 @@
 //   2. lanes whose frame has no pivot yet score up to MICRO_K pivot candidates
 //      (Tomita: the vertex of P u X with the most neighbours in P); a frame with
 //      more candidates carries its partial maximum into the next step, so one
-//      shallow frame does not hold 63 lanes for a whole scan;
+//      shallow frame does not hold 63 lanes for a whole scan. In launches of
+//      many small roots, a step where few lanes need a pivot and one of them has
+//      many candidates left shares the scans out over lane groups (coop_pivot);
 //   3. lanes with a started frame take branches: up to MICRO_B leaf branches
 //      (R u {v} with P n N(v) empty) in a row, or one branch that descends, after
 //      which the parent goes on the stack if it has branches left;
@@ -47,9 +49,105 @@
 #define MICRO_QCAP (MCE_WAVE * (MICRO_B + 1))
 #define MICRO_DON 32   // frames per donation at most
 
-static_assert((MICRO_L & (MICRO_L - 1)) == 0 && MICRO_L >= 128, "LDS stack size");
+#ifndef MICRO_CQ
+#define MICRO_CQ 4     // pivot scans shared out over lane groups when at most this many lanes need one
+#endif
+#ifndef MICRO_CQ_MIN
+#define MICRO_CQ_MIN (2 * MICRO_K)   // ... and one of them has more candidates left than this
+#endif
 
-template <bool CNT>
+static_assert((MICRO_L & (MICRO_L - 1)) == 0 && MICRO_L >= 128, "LDS stack size");
+static_assert(MICRO_CQ == 1 || MICRO_CQ == 2 || MICRO_CQ == 4 || MICRO_CQ == 8 || MICRO_CQ == 16,
+              "cooperative scan bound");
+
+// Lane value exchange through the LDS crossbar (every lane active).
+__device__ __forceinline__ u32 lane_fetch(u32 v, int src) {
+  return (u32)__builtin_amdgcn_ds_bpermute(src << 2, (int)v);
+}
+__device__ __forceinline__ u64 lane_fetch(u64 v, int src) {
+  return ((u64)lane_fetch((u32)(v >> 32), src) << 32) | lane_fetch((u32)v, src);
+}
+
+// Cooperative pivot scan, for a step in which at most 64 / GL lanes need one:
+// group g (lanes g GL .. g GL + GL - 1) scores every remaining candidate of the
+// g-th such lane's frame, lane s of the group the candidates at bit positions
+// s, s + GL, s + 2 GL, ... of its P u X_P and X_X candidate masks, and the
+// group's maximum goes back to the frame's lane with its row. The whole scan
+// ends in this step, where one lane alone scores MICRO_K candidates per step.
+// Any maximiser of |P n N(u)| is a valid pivot (section 2.3), so the
+// tie-break (highest lane) does not change the cliques found. Every lane
+// active; pvm, xx uniform.
+template <int GL>
+__device__ __forceinline__ void coop_pivot(const u64* s_rows, int lane, u64 pvm, bool xx, bool pv, u64 fP,
+                                           u64& pcm, u64& pcx, u32& pbc, u64& pbr, u64& nrows) {
+  constexpr int NG = MCE_WAVE / GL;   // groups, and bit positions per lane
+  const int grp = lane / GL, sub = lane % GL;
+  u64 m = pvm;
+  int own = MCE_WAVE;   // none: the group has no frame to score
+#pragma unroll
+  for (int t = 0; t < NG; t++) {
+    const int o = m ? __builtin_ctzll(m) : MCE_WAVE;
+    own = t == grp ? o : own;
+    m &= m - 1ull;
+  }
+  // (the fetches run in every lane: a permute reads nothing from a lane that is
+  // switched off, and a frame's lane may sit in a group without a frame)
+  const int src = own < MCE_WAVE ? own : lane;
+  const u64 oP = lane_fetch(fP, src);
+  const u64 fM = lane_fetch(pcm, src);
+  const u64 fX = xx ? lane_fetch(pcx, src) : 0ull;
+  const u64 oM = own < MCE_WAVE ? fM : 0ull;
+  const u64 oX = own < MCE_WAVE ? fX : 0ull;
+  u64 rr[NG];
+#pragma unroll
+  for (int j = 0; j < NG; j++) rr[j] = s_rows[sub + j * GL];
+  u32 best = 0;
+  u64 brow = 0;
+#pragma unroll
+  for (int j = 0; j < NG; j++) {
+    const u32 c = (oM >> (sub + j * GL)) & 1ull ? (u32)__popcll(oP & rr[j]) + 1u : 0u;
+    if (c > best) {
+      best = c;
+      brow = rr[j];
+    }
+  }
+  if (xx) {
+#pragma unroll
+    for (int j = 0; j < NG; j++) rr[j] = s_rows[MCE_MICRO_MAX + sub + j * GL];
+#pragma unroll
+    for (int j = 0; j < NG; j++) {
+      const u32 c = (oX >> (sub + j * GL)) & 1ull ? (u32)__popcll(oP & rr[j]) + 1u : 0u;
+      if (c > best) {
+        best = c;
+        brow = rr[j];
+      }
+    }
+  }
+  // group maximum of (score, lane); then the frame's lane takes it from lane g GL
+  u32 key = (best << 8) | (u32)lane;
+#pragma unroll
+  for (int off = GL / 2; off >= 1; off >>= 1) {
+    const u32 o = lane_fetch(key, lane ^ off);
+    key = o > key ? o : key;
+  }
+  const int r = mbcnt(pvm);
+  const u32 k2 = lane_fetch(key, pv ? r * GL : lane);
+  const u64 row = lane_fetch(brow, (int)(k2 & 63u));
+  if (pv) {
+    nrows += (u64)(__popcll(pcm) + __popcll(pcx));
+    if ((k2 >> 8) > pbc) {
+      pbc = k2 >> 8;
+      pbr = row;
+    }
+    pcm = 0ull;
+    pcx = 0ull;
+  }
+}
+
+// COOP: the kernel instance with cooperative pivot scans (launches of many
+// small roots). It is a separate instance because the extra code alone makes
+// the compiler lay out the step loop of the other one worse (4-8 % slower).
+template <bool CNT, bool COOP>
 __global__ __launch_bounds__(64) void k_search_micro(MicroParams prm) {
   __shared__ u64 s_rows[2 * MCE_MICRO_MAX];
   __shared__ u64 s_xcol[MCE_MICRO_MAX];
@@ -229,7 +327,30 @@ __global__ __launch_bounds__(64) void k_search_micro(MicroParams prm) {
       if (pvm) {
         const u32 pc1 = (u32)__popcll(fP) + 1u;   // a score of pc1 means |P n N(u)| = |P|
         const bool xx = ballot(pv && pcx != 0ull) != 0ull;
-        if (pv) {
+        // few frames to score, one of them with more than MICRO_CQ_MIN
+        // candidates left: the lanes share the scans out (coop_pivot)
+        bool coop = false;
+        if constexpr (COOP) {
+          const int q = __popcll(pvm);
+          if (q <= MICRO_CQ &&
+              wave_max_u32(pv ? (u32)(__popcll(pcm) + __popcll(pcx)) : 0u) > (u32)MICRO_CQ_MIN) {
+            coop = true;
+            u64 crows = 0;
+            if (q <= 1) {
+              coop_pivot<64>(s_rows, lane, pvm, xx, pv, fP, pcm, pcx, pbc, pbr, crows);
+            } else if (MICRO_CQ >= 2 && q <= 2) {
+              coop_pivot<32>(s_rows, lane, pvm, xx, pv, fP, pcm, pcx, pbc, pbr, crows);
+            } else if (MICRO_CQ >= 4 && q <= 4) {
+              coop_pivot<16>(s_rows, lane, pvm, xx, pv, fP, pcm, pcx, pbc, pbr, crows);
+            } else if (MICRO_CQ >= 8 && q <= 8) {
+              coop_pivot<8>(s_rows, lane, pvm, xx, pv, fP, pcm, pcx, pbc, pbr, crows);
+            } else {
+              coop_pivot<4>(s_rows, lane, pvm, xx, pv, fP, pcm, pcx, pbc, pbr, crows);
+            }
+            if constexpr (CNT) st_prow += crows;
+          }
+        }
+        if (!coop && pv) {
           {
             int cu[MICRO_K];
             bool cv[MICRO_K];
@@ -511,16 +632,19 @@ __global__ __launch_bounds__(64) void k_search_micro(MicroParams prm) {
 }
 
 // ------------------------------------------------------------------ host side
-static const void* micro_kernel(bool counters) {
-  return counters ? (const void*)k_search_micro<true> : (const void*)k_search_micro<false>;
+static const void* micro_kernel(bool counters, bool coop) {
+  if (coop) return counters ? (const void*)k_search_micro<true, true> : (const void*)k_search_micro<false, true>;
+  return counters ? (const void*)k_search_micro<true, false> : (const void*)k_search_micro<false, false>;
 }
 
 int mce_micro_mail_words() { return 2 + MF * MICRO_DON; }
 
 int mce_micro_max_workers(bool counters, int num_cu) {
-  int per_cu = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, micro_kernel(counters), 64, 0) != hipSuccess) return 0;
-  long long total = (long long)per_cu * num_cu;
+  int per_cu = 0, per_cu_coop = 0;   // both instances: the launch picks one after sizing
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, micro_kernel(counters, false), 64, 0) != hipSuccess ||
+      hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu_coop, micro_kernel(counters, true), 64, 0) != hipSuccess)
+    return 0;
+  long long total = (long long)std::min(per_cu, per_cu_coop) * num_cu;
   if (total > MCE_MAX_WORKERS) total = MCE_MAX_WORKERS;
   return (int)total;
 }
@@ -528,5 +652,5 @@ int mce_micro_max_workers(bool counters, int num_cu) {
 hipError_t mce_launch_micro(bool counters, const MicroParams& prm, hipStream_t s) {
   MicroParams p = prm;
   void* args[] = {&p};
-  return hipLaunchKernel(micro_kernel(counters), dim3(prm.nworkers), dim3(64), args, 0, s);
+  return hipLaunchKernel(micro_kernel(counters, prm.coop != 0), dim3(prm.nworkers), dim3(64), args, 0, s);
 }

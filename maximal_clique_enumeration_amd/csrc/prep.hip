@@ -197,6 +197,8 @@ __device__ __forceinline__ void pmin(int* p, int v) {
 #define PEEL_SOLO 4096
 #endif
 #define PEEL_THREADS 1024
+#define PEEL_LPER 4                            // entries per thread and tile of a level pass
+#define PEEL_LTILE (PEEL_LPER * PEEL_THREADS)   // entries per tile
 
 // Appends the lanes with `in` set to the next frontier: the regular list, or
 // the big list for vertices of degree > PEEL_BIG, whose CSR row lengths are
@@ -369,35 +371,87 @@ __device__ int peel_rounds(const PeelArgs& A, PeelState& st, int wave, int nwave
         // the kept rows' lengths decide whether block 0 may finish alone; they
         // cost a gather per vertex, so they are summed only once the list is short
         const bool sum_rows = st.na <= 8 * PEEL_SOLO;
+        // Tiles of PEEL_LTILE entries per block: one atomic on the shared list
+        // size per tile, and one per block for the minimum and the row sum
+        // (same-address device-scope atomics serialise; one per wavefront and
+        // 64 entries made the early levels of a 4M-vertex graph cost 1 ms each).
+        __shared__ int s_lv[PEEL_THREADS / MCE_WAVE + 1];
+        __shared__ int s_mn;
+        __shared__ u32 s_rows;
+        const int bw = threadIdx.x / MCE_WAVE, nbw = blockDim.x / MCE_WAVE;
+        const int blk = BLOCK ? 0 : (int)blockIdx.x, nblk = BLOCK ? 1 : (int)gridDim.x;
+        if (threadIdx.x == 0) {
+          s_mn = 0x7FFFFFFF;
+          s_rows = 0u;
+        }
         int mn = 0x7FFFFFFF;
         u32 rows = 0;   // CSR row lengths of the kept vertices (at most nnz in all)
-        for (int base = wave * MCE_WAVE; base < st.na; base += nwaves * MCE_WAVE) {
-          const int i = base + lane;
-          bool keep = false, first = false;
-          int v = 0;
-          if (i < st.na) {
-            v = pld<S>(&src[i]);
-            keep = pld<S>(&A.rnd[v]) < 0;
-            if (keep) {
-              const int dv = pld<S>(&A.deg[v]);
+        for (int tb = blk * PEEL_LTILE; tb < st.na; tb += nblk * PEEL_LTILE) {   // uniform in the block
+          bool keep[PEEL_LPER], first[PEEL_LPER];
+          int v[PEEL_LPER];
+#pragma unroll
+          for (int q = 0; q < PEEL_LPER; q++) {
+            const int i = tb + q * PEEL_THREADS + (int)threadIdx.x;
+            keep[q] = first[q] = false;
+            v[q] = 0;
+            if (i < st.na) v[q] = pld<S>(&src[i]);
+          }
+#pragma unroll
+          for (int q = 0; q < PEEL_LPER; q++) {
+            const int i = tb + q * PEEL_THREADS + (int)threadIdx.x;
+            if (i < st.na) keep[q] = pld<S>(&A.rnd[v[q]]) < 0;
+          }
+#pragma unroll
+          for (int q = 0; q < PEEL_LPER; q++) {
+            if (keep[q]) {
+              const int dv = pld<S>(&A.deg[v[q]]);
               mn = min(mn, dv);
-              first = dv <= kn;
-              if (sum_rows) rows += (u32)(rp[v + 1] - rp[v]);
+              first[q] = dv <= kn;
+              if (sum_rows) rows += (u32)(rp[v[q] + 1] - rp[v[q]]);
             }
           }
-          const u64 m = ballot(keep);
-          int pos = 0;
-          if (lane == 0 && m) pos = padd<S>(&ctl->asize[st.cur ^ 1], __popcll(m));
-          pos = read_lane(pos, 0);
-          if (keep) pst<S>(&dst[pos + mbcnt(m)], v);
-          if (ballot(first))
-            peel_append<S>(first, v, rp, A.front(st.r), &fs[p1], A.bfront(st.r), &bs[p1], &be[p1]);
+          u64 m[PEEL_LPER];
+          int cnt = 0;
+#pragma unroll
+          for (int q = 0; q < PEEL_LPER; q++) {
+            m[q] = ballot(keep[q]);
+            cnt += __popcll(m[q]);
+          }
+          if (lane == 0) s_lv[bw] = cnt;
+          __syncthreads();
+          if (threadIdx.x == 0) {
+            int run = 0;
+            for (int w = 0; w < nbw; w++) {
+              const int c = s_lv[w];
+              s_lv[w] = run;
+              run += c;
+            }
+            s_lv[nbw] = run ? padd<S>(&ctl->asize[st.cur ^ 1], run) : 0;
+          }
+          __syncthreads();
+          int pos = s_lv[nbw] + s_lv[bw];
+#pragma unroll
+          for (int q = 0; q < PEEL_LPER; q++) {
+            if (keep[q]) pst<S>(&dst[pos + mbcnt(m[q])], v[q]);
+            pos += __popcll(m[q]);
+          }
+#pragma unroll
+          for (int q = 0; q < PEEL_LPER; q++) {
+            if (ballot(first[q]))
+              peel_append<S>(first[q], v[q], rp, A.front(st.r), &fs[p1], A.bfront(st.r), &bs[p1], &be[p1]);
+          }
+          __syncthreads();   // s_lv is filled again for the next tile
         }
         const int wmn = wave_min_i32_nonneg(mn);
-        if (lane == 0 && wmn != 0x7FFFFFFF) pmin<S>(&ctl->min_deg[st.cur ^ 1], wmn);
+        if (lane == 0 && wmn != 0x7FFFFFFF) atomicMin(&s_mn, wmn);
         if (sum_rows) {
           const u32 wrows = wave_sum_u32(rows);
-          if (lane == 0 && wrows) padd<S>(&ctl->asum[st.cur ^ 1], (int)wrows);
+          if (lane == 0 && wrows) atomicAdd(&s_rows, wrows);
+        }
+        __syncthreads();
+        if (threadIdx.x == 0) {
+          if (s_mn != 0x7FFFFFFF) pmin<S>(&ctl->min_deg[st.cur ^ 1], s_mn);
+          if (s_rows) padd<S>(&ctl->asum[st.cur ^ 1], (int)s_rows);
         }
         PEEL_MARK(tl);
         grid_sync(ctl, A.deadline, st.epoch, BLOCK);
