@@ -83,6 +83,9 @@ __host__ __device__ inline unsigned long long mce_sub_table_words(int p, int x, 
   return mce_table_words(p, x, 1 << (sub >> 1), mode);
 }
 
+#define MCE_BAR_GROUPS 16   // grid barrier: block groups with a counter each
+#define MCE_BAR_STRIDE 32   // u32 words from one barrier counter to the next (a 128-byte line)
+
 // Control block: one per run, zeroed by the host before the first kernel.
 struct MceCtl {
   u32 status;            // MCE_GRAPH_* | MCE_E_*
@@ -111,7 +114,6 @@ struct MceCtl {
   int bsize[3];          // peel: big-vertex frontier sizes (same rotation)
   int bedge[3];          // peel: the big vertices' CSR row lengths summed (same rotation)
   int asum[2];           // peel: each remaining list's CSR row lengths summed (by list parity)
-  u32 bar_count;         // grid barrier: arrivals so far in the launch
   u32 vitems;            // validation: pieces of long rows queued for the second pass
   u32 vdone;             // validation: blocks of the second pass that finished
   u64 vdown, vup;        // validation: edges from the larger (degree, id) end, and from the smaller
@@ -120,6 +122,10 @@ struct MceCtl {
   int seg_state[12];     // peel: the state block 0 hands back (result, list, frontier, level, round, slot, sums)
   u64 t_run;             // wall-clock tick at the start of the peel: the run's time limit counts from it
   u64 peel_ticks[4];     // block 0 of the peel: barrier waits, level passes, round work, total
+  // grid barrier of the peel, one 128-byte line each: [0] groups complete,
+  // [1] barriers released, [2 + g] arrivals of block group g (all counts since
+  // the launch began)
+  alignas(128) u32 bar[(2 + MCE_BAR_GROUPS) * MCE_BAR_STRIDE];
 };
 
 // Worker-list state of one search launch (section 3.3 of the pages). Each

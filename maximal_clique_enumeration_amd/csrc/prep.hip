@@ -136,22 +136,36 @@ __global__ __launch_bounds__(256) void k_validate_long(int n, const int* __restr
 // Everything the peel passes between blocks is read and written with
 // agent-scope relaxed atomics, which are performed at the device coherence
 // point; the barrier only has to order them: each block waits until its own
-// memory operations completed, then arrives. The arrival counter only grows
-// (it is zeroed with the control block before the launch): barrier number e of
-// the launch is complete once it reaches e * gridDim.x, so no block has to
-// reset it or open a generation, and a block needs one atomic add and its
-// polls. Bounded: past the deadline it flags MCE_E_TIMEOUT and lets the block
-// go; the caller checks the flag after every barrier.
+// memory operations completed, then arrives. Two levels, because atomics on one
+// address serialise (256 arrivals on one counter: 3.9 us a barrier; this way
+// 1.8 us): block b arrives on the counter of group b mod 16; the block that
+// completes its group counts the group complete, and the block that completes
+// the last group releases the barrier on a line that nobody adds to. Counters
+// only grow (zeroed with the control block before the launch): barrier e of the
+// launch is complete once a group counter reaches e times the group's size,
+// so no block resets anything or opens a generation. Bounded: past the
+// deadline it flags MCE_E_TIMEOUT and lets the block go; the caller checks the
+// flag after every barrier.
 __device__ void grid_sync(MceCtl* ctl, u64 deadline, u32& epoch, bool solo = false) {
   wait_stores_complete();
   __syncthreads();
   if (gridDim.x > 1 && !solo) {
     if (threadIdx.x == 0) {
       epoch++;
-      const u32 target = epoch * gridDim.x;
-      __hip_atomic_fetch_add(&ctl->bar_count, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      const u32 ng = min(gridDim.x, (u32)MCE_BAR_GROUPS);
+      const u32 g = blockIdx.x % ng;
+      const u32 gsize = (gridDim.x - g + ng - 1) / ng;   // blocks b with b mod ng == g
+      u32* done = &ctl->bar[0];
+      u32* rel = &ctl->bar[MCE_BAR_STRIDE];
+      u32* gc = &ctl->bar[(2 + g) * MCE_BAR_STRIDE];
+      bool last = false;
+      if (__hip_atomic_fetch_add(gc, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1u == epoch * gsize &&
+          __hip_atomic_fetch_add(done, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1u == epoch * ng) {
+        st_relaxed(rel, epoch);
+        last = true;
+      }
       u32 spins = 0;
-      while (ld_relaxed(&ctl->bar_count) < target) {
+      while (!last && ld_relaxed(rel) < epoch) {
         __builtin_amdgcn_s_sleep(1);
         if ((++spins & 1023u) == 0 && past_deadline(deadline)) {
           atomicOr(&ctl->status, MCE_E_TIMEOUT);
