@@ -146,7 +146,7 @@ __global__ __launch_bounds__(256) void k_validate_long(int n, const int* __restr
 // so no block resets anything or opens a generation. Bounded: past the
 // deadline it flags MCE_E_TIMEOUT and lets the block go; the caller checks the
 // flag after every barrier.
-__device__ void grid_sync(MceCtl* ctl, u64 deadline, u32& epoch, bool solo = false) {
+__device__ __forceinline__ void grid_sync(MceCtl* ctl, u64 deadline, u32& epoch, bool solo = false) {
   wait_stores_complete();
   __syncthreads();
   if (gridDim.x > 1 && !solo) {
@@ -356,8 +356,9 @@ __device__ __forceinline__ bool peel_few_left(const PeelState& st) {
 // was last read before the previous barrier, which every block has passed.
 // The remaining-list sizes and minima are kept per list parity for the same
 // reason: they are reset one level after they were read.
+// (always inlined: as a call, its state structures would live in scratch memory)
 template <int S, int MODE>
-__device__ int peel_rounds(const PeelArgs& A, PeelState& st, int wave, int nwaves, bool timer) {
+__device__ __forceinline__ int peel_rounds(const PeelArgs& A, PeelState& st, int wave, int nwaves, bool timer) {
   const int lane = lane_id();
   constexpr bool BLOCK = MODE != PEEL_GRID;   // block 0 alone: workgroup barriers
   const bool lead = BLOCK ? threadIdx.x == 0 : (blockIdx.x == 0 && threadIdx.x == 0);
@@ -602,7 +603,7 @@ __device__ __forceinline__ void lds_barrier() {
 // PEEL_TINY go straight to the global lists. Returns PEEL_TO_GRID (a larger
 // round, whose LDS entries it has moved to the global lists, or a level pass)
 // or PEEL_TO_ALONE.
-__device__ int peel_seg(const PeelArgs& A, PeelState& st, int wave, int nwaves, bool timer) {
+__device__ __forceinline__ int peel_seg(const PeelArgs& A, PeelState& st, int wave, int nwaves, bool timer) {
   __shared__ int s_split[2];
   const int lane = lane_id();
   const int* __restrict__ rp = A.rp;
@@ -754,7 +755,7 @@ __device__ int peel_seg(const PeelArgs& A, PeelState& st, int wave, int nwaves, 
 // every waiting block has arrived (and so has read what the barrier before the
 // segment published), the control block's counters are set for the grid's next
 // step, then the state goes out, then the generation counter.
-__device__ int peel_hand_back(MceCtl* ctl, const PeelState& st, int res, u64 deadline) {
+__device__ __forceinline__ int peel_hand_back(MceCtl* ctl, const PeelState& st, int res, u64 deadline) {
   __shared__ int s_res;
   wait_stores_complete();
   __syncthreads();
@@ -799,7 +800,7 @@ __device__ int peel_hand_back(MceCtl* ctl, const PeelState& st, int res, u64 dea
 // The other blocks while block 0 runs a segment: arrive, wait for its
 // hand-back and take over its state. Returns what block 0 handed back
 // (PEEL_TO_GRID: go on with the grid).
-__device__ int peel_wait(MceCtl* ctl, PeelState& st, u64 deadline) {
+__device__ __forceinline__ int peel_wait(MceCtl* ctl, PeelState& st, u64 deadline) {
   __shared__ int s_late;
   if (threadIdx.x == 0) {
     __hip_atomic_fetch_add(&ctl->seg_arrive, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);

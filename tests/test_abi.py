@@ -77,3 +77,42 @@ def test_missing_library_fails_loudly(monkeypatch, tmp_path):
     monkeypatch.setattr(mce, "_lib", None)
     with pytest.raises(mce.MceLibraryMissing):
         mce.load_library()
+
+
+LLVM_BIN = "/opt/rocm/llvm/bin"
+
+
+def test_kernels_use_no_scratch_memory(lib, tmp_path):
+    """Every kernel of the library keeps its state in registers and LDS. Scratch
+    (private segment) memory in a kernel means spilled registers, or a structure
+    handed by reference to a device function the compiler did not inline; in
+    the peel that made the 45-vertex graph's ordering three times slower. The
+    sizes come from the AMDGPU metadata of the library's own gfx950 code object."""
+    import subprocess
+    tools = [os.path.join(LLVM_BIN, t) for t in ("llvm-objcopy", "clang-offload-bundler", "llvm-readelf")]
+    if not all(os.path.exists(t) for t in tools):
+        pytest.skip("ROCm LLVM tools not installed")
+    objcopy, bundler, readelf = tools
+    fatbin, code = str(tmp_path / "fatbin"), str(tmp_path / "gfx950.co")
+    subprocess.run([objcopy, f"--dump-section=.hip_fatbin={fatbin}", mce.LIB_PATH, str(tmp_path / "lib.so")],
+                   check=True, capture_output=True)
+    # one offload bundle per source file, each starting with the bundle magic
+    blob = open(fatbin, "rb").read()
+    magic = b"__CLANG_OFFLOAD_BUNDLE__"
+    starts = [m.start() for m in re.finditer(re.escape(magic), blob)]
+    assert starts
+    names, sizes = [], []
+    for i, a in enumerate(starts):
+        piece = str(tmp_path / f"bundle{i}")
+        with open(piece, "wb") as f:
+            f.write(blob[a:starts[i + 1] if i + 1 < len(starts) else len(blob)])
+        subprocess.run([bundler, "--unbundle", "--type=o", f"--input={piece}",
+                        "--targets=hipv4-amdgcn-amd-amdhsa--gfx950", f"--output={code}"], check=True,
+                       capture_output=True)
+        notes = subprocess.run([readelf, "--notes", code], check=True, capture_output=True, text=True).stdout
+        names += re.findall(r"^\s+\.name:\s+(\S+)", notes, flags=re.M)
+        sizes += [int(x) for x in re.findall(r"\.private_segment_fixed_size:\s+(\d+)", notes)]
+    assert len(names) == len(sizes) and len(names) >= 10
+    assert any("k_peel" in n for n in names) and any("k_search_micro" in n for n in names)
+    spilled = {n: s for n, s in zip(names, sizes) if s}
+    assert not spilled, spilled
