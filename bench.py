@@ -48,6 +48,9 @@ def parse():
                          "the whole graph: the maximal cliques whose earliest vertex is a sampled root")
     ap.add_argument("--level", type=int, choices=[1, 2], default=1,
                     help="first-level (1, default) or second-level (2) subtrees")
+    ap.add_argument("--subgraph", choices=["auto", "partial", "full"], default="auto",
+                    help="induced-subgraph encoding: the engine's choice by max degree / degeneracy (default), "
+                         "P only, or P and X")
     ap.add_argument("--balance", action="store_true",
                     help="add each search launch's load balance (from the per-wavefront trace)")
     ap.add_argument("--seed", type=int, default=1)
@@ -178,12 +181,12 @@ def main():
     torch.cuda.synchronize()
 
     # counting run: exact algorithmic work of the search (deterministic tree)
-    with mce.Engine(device=0, counters=True, timeout_ms=100000, level=args.level) as ecnt:
+    with mce.Engine(device=0, counters=True, timeout_ms=100000, level=args.level, subgraph=args.subgraph) as ecnt:
         ref = ecnt.run(rp, ci, roots=roots)
         cst = ecnt.stats()
     ops = algorithmic_ops(cst)
 
-    eng = mce.Engine(device=0, phase_times=True, timeout_ms=100000, level=args.level)
+    eng = mce.Engine(device=0, phase_times=True, timeout_ms=100000, level=args.level, subgraph=args.subgraph)
     for _ in range(args.warmup):
         r = eng.run(rp, ci, roots=roots)
         if r.key() != ref.key():
@@ -211,7 +214,7 @@ def main():
     launches = max(1, st["launches"])
     achieved = ops / avg_search_s if avg_search_s > 0 else 0.0
     kernel = "k_search_micro" if st["steps"] > 0 and launches == 1 else "k_search_w1"
-    default_workload = args.sample is None and args.level == 1
+    default_workload = args.sample is None and args.level == 1 and args.subgraph == "auto"
     tj = load_profile(args.traffic_json, args.config, kernel) if default_workload else None
     traffic = tj.get("bytes_per_launch") if tj else None
     roofline = {"bound": "alu", "achieved": achieved / 1e12, "peak": VALU_INT32_PEAK / 1e12,
@@ -257,7 +260,10 @@ def main():
                    "ms_validate": st["ms_validate"], "ms_peel": st["ms_peel"],
                    "ms_orient": st["ms_orient"], "ms_build": st["ms_build"],
                    "pivot_rows": cst["pivot_rows"], "branches": cst["branches"],
-                   "xx_tests": cst["xx_tests"], "leaves": cst["leaves"], "hash": hex(ref.hash)},
+                   "xx_tests": cst["xx_tests"], "leaves": cst["leaves"], "hash": hex(ref.hash),
+                   # share of the search's wavefront cycles by activity (the counting run;
+                   # the page's section 4.5 breakdown)
+                   "activity": {k: v / max(1, sum(cst["act_cycles"].values())) for k, v in cst["act_cycles"].items()}},
     }
     if args.balance:
         out["detail"]["balance"] = balance(eng.worker_trace())

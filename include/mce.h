@@ -162,6 +162,17 @@ typedef struct {
   int32_t launch_roots[16];  /* subtrees of the launch */
   float launch_build_ms[16]; /* its induced-subgraph build, with MCE_FLAG_PHASE_TIMES */
   float launch_search_ms[16];/* its search, same flag */
+  uint64_t act_cycles[7];    /* with MCE_FLAG_COUNTERS: search-kernel shader-clock cycles summed over
+                                wavefronts, by activity (section 4.5 and Figure 5 break execution
+                                time down the same way): [0] worker-list operations (taking subtrees,
+                                answering requests, handing branches over), [1] idle (no task: asking
+                                busy wavefronts for branches until one arrives or the launch ends),
+                                [2] a task's start (its induced subgraph and mailbox read), [3] pivot
+                                selection, [4] the branches' set operations (P n N(v), X n N(v), the
+                                X_X filter, leaf tests), [5] the DFS stack (pushes, pops, spills),
+                                [6] found cliques (hash, histogram). Each wavefront's seven add up to
+                                its whole run; zero without the flag. The build kernels are timed by
+                                launch_build_ms. */
 } mce_run_stats;
 
 /* Fills cfg with the defaults: device -1, worker_list 1, donate_min_p 1, micro_donate_min_p 10,

@@ -89,7 +89,11 @@ class mce_run_stats(ctypes.Structure):
                 ("launch_sub", ctypes.c_int32 * 16),
                 ("launch_roots", ctypes.c_int32 * 16),
                 ("launch_build_ms", ctypes.c_float * 16),
-                ("launch_search_ms", ctypes.c_float * 16)]
+                ("launch_search_ms", ctypes.c_float * 16),
+                ("act_cycles", ctypes.c_uint64 * 7)]
+
+# Activities of mce_run_stats.act_cycles, in order.
+ACTIVITIES = ("worker_list", "idle", "task_start", "pivot", "set_ops", "stack", "cliques")
 
 
 _lib = None
@@ -326,4 +330,5 @@ class Engine:
         out = {name: getattr(st, name) for name, _ in mce_run_stats._fields_ if name not in ("pad_", "pad2_")}
         for key in ("peel_ticks", "launch_sub", "launch_roots", "launch_build_ms", "launch_search_ms"):
             out[key] = list(out[key])[: (4 if key == "peel_ticks" else out["launches"])]
+        out["act_cycles"] = dict(zip(ACTIVITIES, list(out["act_cycles"])))
         return out

@@ -553,6 +553,8 @@ mce_status collect_stats(mce_engine* e) {
   so.max_stack_frames = max_stack;
   so.steps = stat_sum[ST_STEPS];
   so.lane_steps = stat_sum[ST_LANE_STEPS];
+  static_assert(MCE_NACT == sizeof(so.act_cycles) / sizeof(so.act_cycles[0]), "activities");
+  for (int i = 0; i < MCE_NACT; i++) so.act_cycles[i] = stat_sum[ST_ACT0 + i];
   if (e->last_timing) {
     float a = 0, b = 0, c = 0;
     (void)hipEventElapsedTime(&a, e->ev[0], e->ev[1]);

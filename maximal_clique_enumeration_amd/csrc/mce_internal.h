@@ -13,6 +13,20 @@ struct SubOffsets {
   int off[MCE_NSUB];
 };
 
+// Activities of the per-activity cycle breakdown ("Parallelizing Maximal Clique
+// Enumeration on GPUs", section 4.5 and Figure 5, which counts cycles per block
+// and activity with clock reads). The build kernels are timed per launch.
+enum {
+  ACT_WL = 0,    // worker-list operations: taking subtrees, answering requests, handing branches over
+  ACT_IDLE,      // no task: waiting for one (asking busy waves for branches) until the launch ends
+  ACT_STAGE,     // a task's start: its induced subgraph and mailbox read into registers and LDS
+  ACT_PIVOT,     // Tomita pivot selection
+  ACT_SETOPS,    // the branches' set operations: P n N(v), X n N(v), the X_X filter, leaf tests
+  ACT_STACK,     // the DFS stack: pushes, pops, spills and refills
+  ACT_EMIT,      // found cliques: hash terms mixed, size histogram
+  MCE_NACT
+};
+
 // Per-wavefront statistics written by the search kernel (u64 each).
 enum {
   ST_NODES = 0,
@@ -37,7 +51,33 @@ enum {
   ST_LANE_STEPS,     // micro kernel: lanes holding a frame, summed over steps
   ST_FIRST_ABS,      // wall-clock tick at which the first task started (0: none)
   ST_LAST_ABS,       // wall-clock tick at which the last task ended
-  MCE_NSTAT
+  ST_ACT0,           // counting instances: shader-clock cycles per activity (MCE_NACT words)
+  MCE_NSTAT = ST_ACT0 + MCE_NACT
+};
+
+// Cycle accounting of the counting kernel instances: each mark charges the
+// cycles since the previous mark to one activity, so the activities of a wave
+// add up to its whole run. ON = false compiles to nothing.
+template <bool ON>
+struct ActClock {
+  u64 t = 0;
+  u64 c[MCE_NACT] = {};
+  __device__ __forceinline__ void start() {
+    if constexpr (ON) t = (u64)clock64();
+  }
+  __device__ __forceinline__ void mark(int a) {
+    if constexpr (ON) {
+      const u64 n = (u64)clock64();
+      c[a] += n - t;
+      t = n;
+    }
+  }
+  __device__ __forceinline__ void store(u64* st) const {
+    if constexpr (ON) {
+#pragma unroll
+      for (int i = 0; i < MCE_NACT; i++) st[ST_ACT0 + i] = c[i];
+    }
+  }
 };
 
 // Where one search launch keeps its per-wave state: LDS word offsets (dynamic

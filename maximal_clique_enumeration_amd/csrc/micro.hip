@@ -163,6 +163,8 @@ __global__ __launch_bounds__(64) void k_search_micro(MicroParams prm) {
   MceWl* wl = prm.wl;
   if (ld_relaxed(prm.status) & (MCE_E_HEAP | MCE_E_LIMIT)) return;
   const u64 t_start = wall_clock64();
+  ActClock<CNT> act;   // per-activity cycles (counting instance)
+  act.start();
   const u64 deadline = ld_relaxed64(prm.t_run) + prm.budget;
   for (int i = lane; i < MCE_MICRO_MAX + 4; i += MCE_WAVE) s_hist[i] = 0;
   wl_join(wl);
@@ -195,6 +197,7 @@ __global__ __launch_bounds__(64) void k_search_micro(MicroParams prm) {
     int nfr = 0;
     if (!phase2) {
       const u32 idx = take_root(wl, rc, (u32)prm.nroots, (u32)prm.nworkers, 64u);
+      act.mark(ACT_WL);
       if (idx >= (u32)prm.nroots) {
         phase2 = true;
         continue;
@@ -204,6 +207,7 @@ __global__ __launch_bounds__(64) void k_search_micro(MicroParams prm) {
       if (!prm.worker_list) break;
       const u64 t0 = wall_clock64();
       const int got = wl_idle(wl, wid, prm.nworkers, deadline, prm.status, rng, MCE_REQ_SLOTS);
+      act.mark(ACT_IDLE);
       req_closed = true;
       idle_ticks += wall_clock64() - t0;
       if (!got) break;
@@ -259,6 +263,7 @@ __global__ __launch_bounds__(64) void k_search_micro(MicroParams prm) {
       req_closed = false;
     }
     if (t_first == 0) t_first = wall_clock64();
+    act.mark(ACT_STAGE);
     // the stack holds virtual slots [bot, top): [bot, mid) in HBM (slot & cmask),
     // [mid, top) in LDS (slot & lmask)
     u32 bot = 0, mid = 0, top = 0;
@@ -298,6 +303,7 @@ __global__ __launch_bounds__(64) void k_search_micro(MicroParams prm) {
         top -= take;
       }
       const u64 holding = ballot(has);
+      act.mark(ACT_STACK);
       if (holding == 0) break;   // this table's frames are all done here
       st_steps++;
       st_lanes += (u64)__popcll(holding);
@@ -399,6 +405,7 @@ __global__ __launch_bounds__(64) void k_search_micro(MicroParams prm) {
         }
       }
 
+      act.mark(ACT_PIVOT);
       // 3. branches (Algorithm 2: child (P n N(v), X n N(v)), then P -= {v},
       //    X += {v}) in ascending order of v; the next MICRO_B branch vertices are
       //    known up front, so their reads overlap. Leaf branches are taken in a
@@ -484,6 +491,7 @@ __global__ __launch_bounds__(64) void k_search_micro(MicroParams prm) {
           }
         }
       }
+      act.mark(ACT_SETOPS);
       // a full round of queued cliques: mix one per lane
       while (qn >= (u32)MCE_WAVE) {
         qn -= (u32)MCE_WAVE;
@@ -498,6 +506,7 @@ __global__ __launch_bounds__(64) void k_search_micro(MicroParams prm) {
         if (lane == 0) atomicAdd(&s_hist[kf], (u64)tot);
         if (nemit != 0 && !same) atomicAdd(&s_hist[kemit], (u64)nemit);
       }
+      act.mark(ACT_EMIT);
       // parents with branches left go on the stack (LDS; its oldest frames spill to HBM)
       const u64 pm = ballot(push);
       if (pm) {
@@ -530,6 +539,7 @@ __global__ __launch_bounds__(64) void k_search_micro(MicroParams prm) {
         max_stack = max(max_stack, top - bot);
       }
 
+      act.mark(ACT_STACK);
       // 4. branch requests (up to MCE_REQ_SLOTS per step; slot k was read by
       //    lane k): each receiver gets an equal share of the stack's bottom
       //    frames (the shallowest), at most MICRO_DON, leaving this wave as much
@@ -584,6 +594,7 @@ __global__ __launch_bounds__(64) void k_search_micro(MicroParams prm) {
           }
         }
       }
+      act.mark(ACT_WL);
       // Stack slots pass between lanes of this wave from step to step: the
       // vector memory and LDS operations of one wave are performed in order,
       // and this keeps the compiler from moving them across steps.
@@ -606,6 +617,7 @@ __global__ __launch_bounds__(64) void k_search_micro(MicroParams prm) {
   }
   const u64 leaves = wave_sum_u64(mine);
   if (!abort && lane == 0 && hsum) atomicAdd(prm.g_hash, hsum);
+  act.mark(ACT_EMIT);
   const u64 prow = CNT ? wave_sum_u64(st_prow) : 0ull;
   const u64 nbr = CNT ? wave_sum_u64(st_br) : 0ull;
   if (lane == 0) {
@@ -628,6 +640,7 @@ __global__ __launch_bounds__(64) void k_search_micro(MicroParams prm) {
     st[ST_LANE_STEPS] = st_lanes;
     st[ST_FIRST_ABS] = t_first;
     st[ST_LAST_ABS] = t_last;
+    act.store(st);
   }
 }
 

@@ -134,7 +134,7 @@ __device__ int xx_filter_copy(const int* xx, int L, const T& test, int* dst) {
 }
 
 // ------------------------------------------------------------------ the kernel
-template <int W, bool IPX, bool SROWS, bool SSTACK>
+template <int W, bool IPX, bool SROWS, bool SSTACK, bool ACT>
 __global__ __launch_bounds__(64) void k_search(SearchParams prm) {
   constexpr int REC = REC_WORDS(W);
   extern __shared__ u64 lds[];
@@ -145,6 +145,8 @@ __global__ __launch_bounds__(64) void k_search(SearchParams prm) {
   const int* __restrict__ ci = prm.ci;
   MceWl* wl = prm.wl;
   const u64 t_start = wall_clock64();
+  ActClock<ACT> act;   // per-activity cycles (counting instance)
+  act.start();
   const u64 deadline = ld_relaxed64(prm.t_run) + prm.budget;
 
   char* slot = prm.slots + (size_t)wid * prm.slot_bytes;
@@ -181,6 +183,7 @@ __global__ __launch_bounds__(64) void k_search(SearchParams prm) {
     u64 toff = 0, s = 0, pj = 0, xj = 0;
     if (!phase2) {
       const u32 idx = take_root(wl, rc, (u32)prm.nroots, (u32)prm.nworkers, 16u);
+      act.mark(ACT_WL);
       if (idx >= (u32)prm.nroots) {
         phase2 = true;
         continue;
@@ -190,6 +193,7 @@ __global__ __launch_bounds__(64) void k_search(SearchParams prm) {
       if (!prm.worker_list) break;
       const u64 t0 = wall_clock64();
       const int got = wl_idle(wl, wid, prm.nworkers, deadline, prm.status, rng);
+      act.mark(ACT_IDLE);
       req_closed = true;
       idle_ticks += wall_clock64() - t0;
       if (!got) break;
@@ -252,6 +256,7 @@ __global__ __launch_bounds__(64) void k_search(SearchParams prm) {
     }
     if (t_first == 0) t_first = wall_clock64();
     u32 rq_next = 0;   // request word, read at one node and acted on at the next
+    act.mark(ACT_STAGE);
 
     // ---------------------------------------------------------- depth-first search
     // Current level in registers: P, X_P, C (lane w < W holds word w), s = sum of
@@ -336,6 +341,7 @@ __global__ __launch_bounds__(64) void k_search(SearchParams prm) {
         } else {
           if (lane < W) cj = pj & ~rows[(size_t)u * W + lane];
         }
+        act.mark(ACT_PIVOT);
 
         // Branch requests (section 3.3; the idle wave asks, see wl_idle): the
         // request word read at the previous node is acted on now. The branch
@@ -417,6 +423,7 @@ __global__ __launch_bounds__(64) void k_search(SearchParams prm) {
           }
           rq_next = wl_poll(wl, wid);
         }
+        act.mark(ACT_WL);
       }
 
       // next branch of this level: the lowest vertex of C = P - N(pivot)
@@ -438,6 +445,7 @@ __global__ __launch_bounds__(64) void k_search(SearchParams prm) {
         s = read_lane(sv, 0);
         mv = read_lane(mv, 0);
         lpx = (int)(u32)mv;
+        act.mark(ACT_STACK);
         continue;
       }
       const int j0 = __builtin_ctzll(nz);
@@ -463,17 +471,22 @@ __global__ __launch_bounds__(64) void k_search(SearchParams prm) {
         // P n N(v) is empty: R u {v} is maximal iff X n N(v) is empty too
         if (ballot(lane < W && xn != 0) == 0) {
           st_xx += (u64)lpx;
-          if (!xx_any(xx, lpx, test)) {
+          const bool maximal = !xx_any(xx, lpx, test);
+          act.mark(ACT_SETOPS);
+          if (maximal) {
             hacc += mce_clique_term(s_child, k_child);
             if (lane == 0) s_hist[k_child] += 1;
             st_leaves++;
+            act.mark(ACT_EMIT);
           }
         }
+        act.mark(ACT_SETOPS);
         continue;
       }
       // X_X n N(v): stable partition, the child's part is xx[0, lpx_child)
       st_xx += (u64)lpx;
       const int lpx_child = lpx > 0 ? xx_partition(xx, lpx, test) : 0;
+      act.mark(ACT_SETOPS);
 
       // descend: save this level, the child becomes the current level
       u64* R = stk + (size_t)l * REC;
@@ -492,6 +505,7 @@ __global__ __launch_bounds__(64) void k_search(SearchParams prm) {
       s = s_child;
       lpx = lpx_child;
       need_pivot = true;
+      act.mark(ACT_STACK);
     }
     t_last = wall_clock64();
     if (abort) break;
@@ -507,6 +521,7 @@ __global__ __launch_bounds__(64) void k_search(SearchParams prm) {
     }
     if (lane == 0 && hacc) atomicAdd(prm.g_hash, hacc);
   }
+  act.mark(ACT_EMIT);
   if (lane == 0) {
     u64* st = prm.stats + (size_t)wid * MCE_NSTAT;
     st[ST_NODES] = st_nodes;
@@ -523,6 +538,7 @@ __global__ __launch_bounds__(64) void k_search(SearchParams prm) {
     st[ST_START_ABS] = t_start;
     st[ST_FIRST_ABS] = t_first;
     st[ST_LAST_ABS] = t_last;
+    act.store(st);
   }
 }
 
@@ -553,6 +569,8 @@ __global__ __launch_bounds__(64) void k_search_w1(SearchParams prm) {
   u64* lrows = lds + prm.l_rows;
 
   if (ld_relaxed(prm.status) & (MCE_E_HEAP | MCE_E_LIMIT)) return;
+  ActClock<CNT> act;   // per-activity cycles (counting instance)
+  act.start();
   for (int i = lane; i < prm.hcap; i += MCE_WAVE) s_hist[i] = 0;
   if (lane == 0) {
     const u64 t0 = wall_clock64();
@@ -587,6 +605,7 @@ __global__ __launch_bounds__(64) void k_search_w1(SearchParams prm) {
     u64 toff = 0, s = 0, P = 0, XP = 0;
     if (!phase2) {
       const u32 idx = take_root(wl, rc, (u32)prm.nroots, (u32)prm.nworkers, 16u);
+      act.mark(ACT_WL);
       if (idx >= (u32)prm.nroots) {
         phase2 = true;
         continue;
@@ -596,6 +615,7 @@ __global__ __launch_bounds__(64) void k_search_w1(SearchParams prm) {
       if (!prm.worker_list) break;
       const u64 t0 = wall_clock64();
       const int got = wl_idle(wl, wid, prm.nworkers, uni(s_misc[1]), prm.status, rng);
+      act.mark(ACT_IDLE);
       req_closed = true;
       if (lane == 0) {
         const u64 t1 = wall_clock64();
@@ -659,6 +679,7 @@ __global__ __launch_bounds__(64) void k_search_w1(SearchParams prm) {
       req_closed = false;
     }
     u32 rq_next = 0;   // request word, read at one node and acted on at the next
+    act.mark(ACT_STAGE);
 
     // ---------------------------------------------------------- depth-first search
     u64 stP = 0, stX = 0, stC = 0, stS = 0, stL = 0;   // level stack, level l in lane l
@@ -712,6 +733,7 @@ __global__ __launch_bounds__(64) void k_search_w1(SearchParams prm) {
         const int u = MCE_MAX_LOCAL - (int)(best & (u32)MCE_MAX_LOCAL);
         const u64 ru = u < p ? read_lane(myrow, u) : uni(rows[u]);
         C = P & ~ru;
+        act.mark(ACT_PIVOT);
 
         // Branch requests (section 3.3; here the idle wave asks, see wl_idle):
         // the request word read at the previous node is acted on now, and read
@@ -796,6 +818,7 @@ __global__ __launch_bounds__(64) void k_search_w1(SearchParams prm) {
           }
           rq_next = wl_poll(wl, wid);
         }
+        act.mark(ACT_WL);
       }
 
       // next branch of this level: the lowest vertex of C = P - N(pivot)
@@ -807,6 +830,7 @@ __global__ __launch_bounds__(64) void k_search_w1(SearchParams prm) {
         C = read_lane(stC, l);
         s = read_lane(stS, l);
         lpx = (int)(u32)read_lane(stL, l);
+        act.mark(ACT_STACK);
         continue;
       }
       const int v = __builtin_ctzll(C);
@@ -836,6 +860,7 @@ __global__ __launch_bounds__(64) void k_search_w1(SearchParams prm) {
             }
             maximal = !xx_any(xx, lpx, test);
           }
+          act.mark(ACT_SETOPS);
           if (maximal) {
             const int k = k0 + l + 1;
             hacc += mce_clique_term(s + read_lane(myhv, v), k);
@@ -844,8 +869,10 @@ __global__ __launch_bounds__(64) void k_search_w1(SearchParams prm) {
             } else if (lane == 0) {
               s_hist[k] += 1;
             }
+            act.mark(ACT_EMIT);
           }
         }
+        act.mark(ACT_SETOPS);
         continue;
       }
       // X_X n N(v): stable partition, the child's part is xx[0, lpx_child)
@@ -864,6 +891,7 @@ __global__ __launch_bounds__(64) void k_search_w1(SearchParams prm) {
         }
         lpx_child = xx_partition(xx, lpx, test);
       }
+      act.mark(ACT_SETOPS);
       // descend: save this level in lane l, the child becomes the current level
       if (lane == l) {
         stP = P;
@@ -878,6 +906,7 @@ __global__ __launch_bounds__(64) void k_search_w1(SearchParams prm) {
       XP = xn;
       lpx = lpx_child;
       need_pivot = true;
+      act.mark(ACT_STACK);
     }
     t_last = wall_clock64();
     if (abort) break;
@@ -895,6 +924,7 @@ __global__ __launch_bounds__(64) void k_search_w1(SearchParams prm) {
     }
     if (lane == 0 && hacc) atomicAdd(prm.g_hash, hacc);
   }
+  act.mark(ACT_EMIT);
   for (int i = 64; i < prm.hcap; i++) leaves += s_hist[i];
   if (lane == 0) {
     u64* st = prm.stats + (size_t)wid * MCE_NSTAT;
@@ -918,6 +948,7 @@ __global__ __launch_bounds__(64) void k_search_w1(SearchParams prm) {
     st[ST_LAST_ABS] = t_last;
     st[ST_CHECKS] = st_checks;
     st[ST_DONATE_OK_TICKS] = s_misc[7];
+    act.store(st);
   }
 }
 
@@ -946,25 +977,25 @@ hipError_t mce_launch_wl_init(MceWl* wl, int nworkers, u64* stats, hipStream_t s
 }
 
 template <int W, bool IPX, bool SR, bool SS>
-static const void* fn() {
-  return (const void*)k_search<W, IPX, SR, SS>;
+static const void* fn(bool act) {
+  return act ? (const void*)k_search<W, IPX, SR, SS, true> : (const void*)k_search<W, IPX, SR, SS, false>;
 }
 
 // Variants (width 1 has its own kernel): widths 2 and 4 stage rows (light
 // sub-classes) and the stack in LDS as the layout allows; wider classes keep
 // both in HBM.
 template <bool IPX>
-static const void* pick(int wclass, bool srows, bool sstack) {
+static const void* pick(int wclass, bool srows, bool sstack, bool act) {
   switch (wclass) {
     case 1:
-      return srows ? (sstack ? fn<2, IPX, true, true>() : fn<2, IPX, true, false>())
-                   : (sstack ? fn<2, IPX, false, true>() : fn<2, IPX, false, false>());
+      return srows ? (sstack ? fn<2, IPX, true, true>(act) : fn<2, IPX, true, false>(act))
+                   : (sstack ? fn<2, IPX, false, true>(act) : fn<2, IPX, false, false>(act));
     case 2:
-      return srows ? (sstack ? fn<4, IPX, true, true>() : fn<4, IPX, true, false>())
-                   : (sstack ? fn<4, IPX, false, true>() : fn<4, IPX, false, false>());
-    case 3: return fn<8, IPX, false, false>();
-    case 4: return fn<16, IPX, false, false>();
-    case 5: return fn<32, IPX, false, false>();
+      return srows ? (sstack ? fn<4, IPX, true, true>(act) : fn<4, IPX, true, false>(act))
+                   : (sstack ? fn<4, IPX, false, true>(act) : fn<4, IPX, false, false>(act));
+    case 3: return fn<8, IPX, false, false>(act);
+    case 4: return fn<16, IPX, false, false>(act);
+    case 5: return fn<32, IPX, false, false>(act);
   }
   return nullptr;
 }
@@ -980,7 +1011,8 @@ static const void* search_kernel(const SearchLayout& L) {
                : (L.srows ? (const void*)k_search_w1<false, true, false> : (const void*)k_search_w1<false, false, false>);
   }
   if (L.wclass >= 3 && (L.srows || L.sstack)) return nullptr;
-  return L.mode == MCE_MODE_IPX ? pick<true>(L.wclass, L.srows, L.sstack) : pick<false>(L.wclass, L.srows, L.sstack);
+  return L.mode == MCE_MODE_IPX ? pick<true>(L.wclass, L.srows, L.sstack, L.counters)
+                                : pick<false>(L.wclass, L.srows, L.sstack, L.counters);
 }
 
 static size_t a256(size_t x) { return (x + 255) & ~(size_t)255; }
