@@ -1165,15 +1165,21 @@ __global__ __launch_bounds__(256) void k_l2_expand(int n, const int* __restrict_
 
 // Per second-level root: |P| and |X| by intersecting the two rows (each entry
 // of the shorter one is searched in the longer one), then the same tallies as
-// k_orient. A wavefront takes G consecutive roots in turn, lane t keeping root
-// t's counts, so that a tally covers up to 64 roots. Roots with P and X empty
-// are maximal cliques of size 2, counted here.
+// k_orient. A wavefront takes G consecutive roots, four at a time: lane group
+// q (16 lanes) intersects root t0 + q's rows, and lane t keeps root t's counts,
+// so that a tally covers up to 64 roots. (One root per wavefront left most
+// lanes idle through the search chains: the shorter row has a few dozen entries
+// on these graphs.) Roots with P and X empty are maximal cliques of size 2,
+// counted here.
+#define L2_GROUP 16   // lanes per root
 __global__ __launch_bounds__(256) void k_orient_l2(const int* __restrict__ rp, const int* __restrict__ ci,
                                                     const int* __restrict__ rnd, const int* __restrict__ src,
                                                     const int* __restrict__ eroots, int* pcount, int* xcount,
                                                     MceCtl* ctl) {
   if (ld_relaxed(&ctl->status) != 0) return;
+  constexpr int NQ = MCE_WAVE / L2_GROUP;   // roots in flight per wavefront
   const int lane = lane_id();
+  const int q = lane / L2_GROUP, sl = lane % L2_GROUP;
   const int wave = (blockIdx.x * blockDim.x + threadIdx.x) / MCE_WAVE;
   const int nwaves = gridDim.x * blockDim.x / MCE_WAVE;
   const int total = ld_relaxed(&ctl->l2_roots);
@@ -1183,30 +1189,44 @@ __global__ __launch_bounds__(256) void k_orient_l2(const int* __restrict__ rp, c
   for (int g0 = wave * G; g0 < total; g0 += nwaves * G) {
     int p = 0, x = 0;
     bool mine = false;
-    for (int t = 0; t < G && g0 + t < total; t++) {
-      const int e = eroots[g0 + t];
-      const int vi = src[e], vj = ci[e];
-      const int ai = rp[vi], bi = rp[vi + 1], aj = rp[vj], bj = rp[vj + 1];
-      const bool si = bi - ai <= bj - aj;   // scan the shorter row
-      const int sa = si ? ai : aj, sb = si ? bi : bj, oa = si ? aj : ai, ob = si ? bj : bi;
-      const int rj = rnd[vj];
+    for (int t0 = 0; t0 < G && g0 + t0 < total; t0 += NQ) {
+      const int t = t0 + q;
+      const bool live = t < G && g0 + t < total;
+      int vi = 0, vj = 0;
       u32 cp = 0, cx = 0;
-      for (int k = sa + lane; k < sb; k += MCE_WAVE) {
-        const int c = ci[k];
-        if (csr_range_has(ci, oa, ob, c)) {
-          if (order_after(rnd[c], c, rj, vj)) cp++;
-          else cx++;
+      if (live) {
+        const int e = eroots[g0 + t];
+        vi = src[e];
+        vj = ci[e];
+        const int ai = rp[vi], bi = rp[vi + 1], aj = rp[vj], bj = rp[vj + 1];
+        const bool si = bi - ai <= bj - aj;   // scan the shorter row
+        const int sa = si ? ai : aj, sb = si ? bi : bj, oa = si ? aj : ai, ob = si ? bj : bi;
+        const int rj = rnd[vj];
+        for (int k = sa + sl; k < sb; k += L2_GROUP) {
+          const int c = ci[k];
+          if (csr_range_has(ci, oa, ob, c)) {
+            if (order_after(rnd[c], c, rj, vj)) cp++;
+            else cx++;
+          }
         }
       }
-      cp = wave_sum_u32(cp);
-      cx = wave_sum_u32(cx);
-      if (lane == t) {
-        p = (int)cp;
-        x = (int)cx;
+      // group sums (every lane active again), then lane t takes root t's from its group
+#pragma unroll
+      for (int off = L2_GROUP / 2; off >= 1; off >>= 1) {
+        cp += (u32)__shfl_xor((int)cp, off);
+        cx += (u32)__shfl_xor((int)cx, off);
+      }
+      const bool take = lane >= t0 && lane < t0 + NQ;   // lane t = t0 + q' takes group q'
+      const int from = take ? (lane - t0) * L2_GROUP : lane;
+      const u32 gp = (u32)__shfl((int)cp, from), gx = (u32)__shfl((int)cx, from);
+      const int gvi = __shfl(vi, from), gvj = __shfl(vj, from);
+      if (take && lane < G && g0 + lane < total) {
+        p = (int)gp;
+        x = (int)gx;
         mine = true;
-        if (cp == 0 && cx == 0) {
+        if (gp == 0 && gx == 0) {
           pairs++;
-          pairs_hash += mce_clique_term(mce_vertex_term(vi) + mce_vertex_term(vj), 2);
+          pairs_hash += mce_clique_term(mce_vertex_term(gvi) + mce_vertex_term(gvj), 2);
         }
       }
     }
