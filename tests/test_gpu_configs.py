@@ -53,6 +53,19 @@ def same(got, want):
     assert f"0x{got.hash:016x}" == want["hash"]
 
 
+def same_order(e, g, idx):
+    """The degeneracy order (core number and peel round of every vertex) of the
+    last run equals the oracle's, read back with mce_ordering: on the large
+    configurations the peel runs on the whole grid (level passes in tiles,
+    two-level barrier, tiny rounds in block 0)."""
+    import oracle
+    core, rnd = e.ordering(g.n)
+    want_core, want_rnd, want_d = oracle.peel(g.n, g.row_ptr, g.col_idx)
+    assert e.graph_info()["degeneracy"] == want_d == GOLD[str(idx)]["degeneracy"]
+    assert np.array_equal(core.cpu().numpy(), want_core)
+    assert np.array_equal(rnd.cpu().numpy(), want_rnd)
+
+
 @pytest.mark.parametrize("level", [1, 2])
 @pytest.mark.parametrize("subgraph", ["auto", "partial", "full"])
 @pytest.mark.parametrize("idx", [0, 1, 3])
@@ -64,6 +77,8 @@ def test_whole_graph(idx, subgraph, level):
         same(e.run(rp, ci), GOLD[str(idx)]["whole"])
         info = e.graph_info()
         assert info["degeneracy"] == GOLD[str(idx)]["degeneracy"]
+        if subgraph == "auto" and level == 1:
+            same_order(e, g, idx)
         assert info["level"] == level
 
 
@@ -90,6 +105,8 @@ def test_root_sample(idx, kind):
         ha = a.hist + [0] * (n - len(a.hist))
         hb = b.hist + [0] * (n - len(b.hist))
         assert [x + y for x, y in zip(ha, hb)] == got.hist
+        if kind == "uniform":
+            same_order(e, g, idx)
 
 
 @pytest.mark.timeout(900)
@@ -106,3 +123,4 @@ def test_root_sample_second_level(idx, kind):
     with mce.Engine(device=0, timeout_ms=60000, level=2) as e:
         same(e.run(rp, ci, roots=torch.from_numpy(roots).to(DEV)), want)
         assert e.graph_info()["level"] == 2
+
