@@ -211,6 +211,9 @@ __device__ __forceinline__ void pmin(int* p, int v) {
 #define PEEL_SOLO 4096
 #endif
 #define PEEL_THREADS 1024
+#ifndef PEEL_LDS_N
+#define PEEL_LDS_N 4096   // one-block peels of at most this many vertices keep degrees and rounds in LDS
+#endif
 #define PEEL_LPER 4                            // entries per thread and tile of a level pass
 #define PEEL_LTILE (PEEL_LPER * PEEL_THREADS)   // entries per tile
 
@@ -853,10 +856,23 @@ __global__ __launch_bounds__(PEEL_THREADS) void k_peel(int n, const int* __restr
                                                         int* bfront0, int* bfront1, MceCtl* ctl, u64 budget) {
   __shared__ int s_cnt[12];
   __shared__ int4 s_fr[2 * PEEL_TINY + 1];
+  // A graph of at most PEEL_LDS_N vertices peeled by one block keeps degrees,
+  // rounds and the list and frontier counters in LDS (a copy of the control
+  // block): the peel's generic loads, stores and atomics then go to LDS instead
+  // of the L2, and a round's barrier waits on no global store. The rounds and
+  // any status bit are copied out at the end.
+  __shared__ int s_deg[PEEL_LDS_N], s_rnd[PEEL_LDS_N];
+  __shared__ MceCtl s_ctl;
   if (ld_relaxed(&ctl->status) != 0) return;   // rejected input: nothing to order
   const u64 t0 = wall_clock64();
-  PeelArgs A{n,      rp,     ci,      deg,     rnd, core,       alive0, alive1, front0,
-             front1, bfront0, bfront1, ctl, t0 + budget, s_cnt, s_fr};
+  const bool lds = gridDim.x == 1 && n <= PEEL_LDS_N;
+  MceCtl* pc = lds ? &s_ctl : ctl;   // the peel's counters
+  if (lds) {
+    for (int i = threadIdx.x; i < (int)(sizeof(MceCtl) / sizeof(u32)); i += blockDim.x) ((u32*)&s_ctl)[i] = 0u;
+    __syncthreads();
+  }
+  PeelArgs A{n,      rp,     ci,      lds ? s_deg : deg, lds ? s_rnd : rnd, core,       alive0, alive1, front0,
+             front1, bfront0, bfront1, pc, t0 + budget, s_cnt, s_fr};
   const int gtid = blockIdx.x * blockDim.x + threadIdx.x;
   const int gsize = gridDim.x * blockDim.x;
   const bool timer = blockIdx.x == 0 && threadIdx.x == 0;
@@ -864,23 +880,23 @@ __global__ __launch_bounds__(PEEL_THREADS) void k_peel(int n, const int* __restr
   PeelState st{0, 0, 0, -1, 0, n, 0, 0, 0, false, 0u, 0u, 0, 0, 0, t0};
 
   for (int v = gtid; v < n; v += gsize) {
-    pst<SA>(&deg[v], rp[v + 1] - rp[v]);
-    pst<SA>(&rnd[v], -1);
+    pst<SA>(&A.deg[v], rp[v + 1] - rp[v]);
+    pst<SA>(&A.rnd[v], -1);
     pst<SA>(&alive0[v], v);
   }
   if (gtid == 0) {
     st_relaxed64(&ctl->t_run, t0);
-    pst<SA>(&ctl->asize[0], n);
-    pst<SA>(&ctl->asize[1], 0);
+    pst<SA>(&pc->asize[0], n);
+    pst<SA>(&pc->asize[1], 0);
     for (int i = 0; i < 3; i++) {
-      pst<SA>(&ctl->fsize[i], 0);
-      pst<SA>(&ctl->bsize[i], 0);
-      pst<SA>(&ctl->bedge[i], 0);
+      pst<SA>(&pc->fsize[i], 0);
+      pst<SA>(&pc->bsize[i], 0);
+      pst<SA>(&pc->bedge[i], 0);
     }
-    pst<SA>(&ctl->asum[0], 0);
-    pst<SA>(&ctl->asum[1], 0);
-    pst<SA>(&ctl->min_deg[0], 0x7FFFFFFF);
-    pst<SA>(&ctl->min_deg[1], 0x7FFFFFFF);
+    pst<SA>(&pc->asum[0], 0);
+    pst<SA>(&pc->asum[1], 0);
+    pst<SA>(&pc->min_deg[0], 0x7FFFFFFF);
+    pst<SA>(&pc->min_deg[1], 0x7FFFFFFF);
   }
   grid_sync(ctl, A.deadline, st.epoch);
 
@@ -913,7 +929,12 @@ __global__ __launch_bounds__(PEEL_THREADS) void k_peel(int n, const int* __restr
   } else {
     res = peel_rounds<SW, PEEL_ALONE>(A, st, bwave, bwaves, timer);
   }
+  if (lds && threadIdx.x == 0 && s_ctl.status) atomicOr(&ctl->status, s_ctl.status);
   if (res < 0) return;
+  if (lds) {
+    __syncthreads();
+    for (int v = threadIdx.x; v < n; v += blockDim.x) rnd[v] = s_rnd[v];
+  }
   if (threadIdx.x == 0 && blockIdx.x == 0) {
     ctl->rounds = st.r;
     ctl->degeneracy = max(st.k, 0);
