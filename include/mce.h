@@ -77,6 +77,11 @@ typedef enum {
                                     first-level subtree per vertex (Algorithm 3), which section 4.5
                                     recommends */
 
+#define MCE_FLAG_SEARCH_TIMES 32u /* events around the search launches only (mce_run_stats.ms_search,
+                                    launch_search_ms; the other phase times stay 0): the light form of
+                                    MCE_FLAG_PHASE_TIMES for timing loops, since every recorded event
+                                    costs the stream a few microseconds */
+
 /* mce_config.subgraph: how each subtree's induced subgraph is encoded (section
    3.4). Partial: bit rows for P x P only, edges between P and X looked up in the
    CSR, pivot drawn from P u X_P (section 3.5, last paragraph). Full: bit rows for
@@ -139,7 +144,8 @@ typedef struct {
   double tick_hz;            /* rate of the tick counters */
   double ms_total;           /* mce_run wall time on the host, end to end */
   double ms_validate, ms_peel, ms_orient;   /* GPU phase times, with MCE_FLAG_PHASE_TIMES */
-  double ms_search;          /* search kernels alone (events around each launch), same flag */
+  double ms_search;          /* search kernels alone (events around each launch), same flag or
+                                MCE_FLAG_SEARCH_TIMES */
   double ms_build;           /* induced-subgraph build kernels, same flag */
   uint64_t donate_ticks;     /* sum over wavefronts of ticks spent handing branches over */
   uint64_t setup_ticks;      /* sum over wavefronts of ticks from a wake-up to the search start */
@@ -161,7 +167,7 @@ typedef struct {
                                 class * 2 + HBM staging, or 12 for the micro kernel) */
   int32_t launch_roots[16];  /* subtrees of the launch */
   float launch_build_ms[16]; /* its induced-subgraph build, with MCE_FLAG_PHASE_TIMES */
-  float launch_search_ms[16];/* its search, same flag */
+  float launch_search_ms[16];/* its search, with MCE_FLAG_PHASE_TIMES or MCE_FLAG_SEARCH_TIMES */
   uint64_t act_cycles[7];    /* with MCE_FLAG_COUNTERS: search-kernel shader-clock cycles summed over
                                 wavefronts, by activity (section 4.5 and Figure 5 break execution
                                 time down the same way): [0] worker-list operations (taking subtrees,

@@ -66,6 +66,7 @@ struct mce_engine {
   int last_stat_rows = 0;
   bool stats_pending = false;
   bool last_timing = false;
+  bool last_stimes = false;   // the search launches carry events (MCE_FLAG_SEARCH_TIMES or _PHASE_TIMES)
   // resident-wave counts per kernel variant (occupancy queries cost ~0.1 ms each)
   std::map<std::pair<int, long long>, int> occupancy;
 };
@@ -163,6 +164,8 @@ mce_status run_impl(mce_engine* e, int32_t n, int64_t nnz, const int32_t* row_pt
     return MCE_OK;
   }
   const bool timing = (e->cfg.flags & MCE_FLAG_PHASE_TIMES) && e->have_events;
+  // events around the search launches only (every recorded event costs the stream a few us)
+  const bool stimes = (timing || (e->cfg.flags & MCE_FLAG_SEARCH_TIMES)) && e->have_events;
   const bool hbm = (e->cfg.flags & MCE_FLAG_HBM_STAGING) != 0;
   const u64 budget = (u64)((double)e->cfg.timeout_ms * 1e-3 * e->tick_hz);
 
@@ -395,9 +398,9 @@ mce_status run_impl(mce_engine* e, int32_t n, int64_t nnz, const int32_t* row_pt
       mp.t_run = &ctl->t_run;
       mp.status = &ctl->status;
       mp.stats = dp<u64>(e->stats) + (size_t)stat_off * MCE_NSTAT;
-      if (timing) (void)hipEventRecord(e->ev[evi + 2], s);
+      if (stimes) (void)hipEventRecord(e->ev[evi + 2], s);
       if ((h = mce_launch_micro(counters, mp, s)) != hipSuccess) return hip_fail(e, h, "micro search launch");
-      if (timing) (void)hipEventRecord(e->ev[evi + 3], s);
+      if (stimes) (void)hipEventRecord(e->ev[evi + 3], s);
       evi += 4;
       stat_off += pl.nw;
       launches++;
@@ -433,9 +436,9 @@ mce_status run_impl(mce_engine* e, int32_t n, int64_t nnz, const int32_t* row_pt
     prm.t_run = &ctl->t_run;
     prm.status = &ctl->status;
     prm.stats = dp<u64>(e->stats) + (size_t)stat_off * MCE_NSTAT;
-    if (timing) (void)hipEventRecord(e->ev[evi + 2], s);
+    if (stimes) (void)hipEventRecord(e->ev[evi + 2], s);
     if ((h = mce_launch_search(L, prm, s)) != hipSuccess) return hip_fail(e, h, "search launch");
-    if (timing) (void)hipEventRecord(e->ev[evi + 3], s);
+    if (stimes) (void)hipEventRecord(e->ev[evi + 3], s);
     evi += 4;
     stat_off += pl.nw;
     launches++;
@@ -485,6 +488,7 @@ mce_status run_impl(mce_engine* e, int32_t n, int64_t nnz, const int32_t* row_pt
   so.micro_roots = counts[MCE_SUB_MICRO];
   e->last_stat_rows = stat_rows;
   e->last_timing = timing;
+  e->last_stimes = stimes;
   e->stats_pending = true;
   so.ms_total = ms_since(t0);
   return MCE_OK;
@@ -563,10 +567,12 @@ mce_status collect_stats(mce_engine* e) {
     so.ms_validate = a;
     so.ms_peel = b;
     so.ms_orient = c;   // orientation, host read-back and root bucketing
+  }
+  if (e->last_stimes) {
     double mb = 0, ms = 0;
     for (int i = 0; i < (int)e->last_plan.size(); i++) {
       float x = 0, y = 0;
-      (void)hipEventElapsedTime(&x, e->ev[4 + 4 * i], e->ev[5 + 4 * i]);
+      if (e->last_timing) (void)hipEventElapsedTime(&x, e->ev[4 + 4 * i], e->ev[5 + 4 * i]);
       (void)hipEventElapsedTime(&y, e->ev[6 + 4 * i], e->ev[7 + 4 * i]);
       mb += x;
       ms += y;
@@ -616,7 +622,7 @@ mce_status mce_create(const mce_config* cfg, mce_engine** out) {
       c.subgraph < MCE_SUBGRAPH_AUTO ||
       c.subgraph > MCE_SUBGRAPH_FULL ||
       (c.flags & ~(MCE_FLAG_HBM_STAGING | MCE_FLAG_PHASE_TIMES | MCE_FLAG_COUNTERS | MCE_FLAG_NO_MICRO |
-                   MCE_FLAG_L2)) != 0)
+                   MCE_FLAG_L2 | MCE_FLAG_SEARCH_TIMES)) != 0)
     return MCE_ERR_ARG;
   if (c.timeout_ms == 0) c.timeout_ms = 120000;
   mce_engine* e = new (std::nothrow) mce_engine();

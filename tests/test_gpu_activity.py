@@ -79,3 +79,19 @@ def test_plain_runs_charge_nothing():
         for g in GRAPHS[:3]:
             run(e, g)
             assert not any(e.stats()["act_cycles"].values())
+
+
+def test_search_times_record_the_search_alone():
+    """MCE_FLAG_SEARCH_TIMES: events around the search launches only, the
+    other phase times stay 0; MCE_FLAG_PHASE_TIMES gives all of them."""
+    g = GRAPHS[0]
+    with mce.Engine(device=0, timeout_ms=20000, search_times=True) as e:
+        run(e, g)
+        st = e.stats()
+        assert st["ms_search"] > 0 and len(st["launch_search_ms"]) == st["launches"] >= 1
+        assert abs(sum(st["launch_search_ms"]) - st["ms_search"]) < 1e-3
+        assert st["ms_validate"] == st["ms_peel"] == st["ms_orient"] == st["ms_build"] == 0
+    with mce.Engine(device=0, timeout_ms=20000, phase_times=True) as e:
+        run(e, g)
+        st = e.stats()
+        assert min(st["ms_validate"], st["ms_peel"], st["ms_orient"], st["ms_build"], st["ms_search"]) > 0
