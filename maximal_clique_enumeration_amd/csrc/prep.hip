@@ -130,6 +130,61 @@ __global__ __launch_bounds__(256) void k_validate_long(int n, const int* __restr
   }
 }
 
+// Small graphs: the same checks in one block, passes separated by block
+// barriers (three launches cost more than the work): row_ptr first, then the
+// rows (any length: one wavefront per row), then the two edge counts.
+#define VAL_SMALL_N 16384
+#define VAL_SMALL_NNZ 262144
+__global__ __launch_bounds__(1024) void k_validate_small(int n, long long nnz, const int* __restrict__ rp,
+                                                          const int* __restrict__ ci, MceCtl* ctl) {
+  __shared__ u32 s_bad, s_down, s_up;
+  __shared__ int s_dmax;
+  const int lane = lane_id();
+  if (threadIdx.x == 0) {
+    s_bad = 0u;
+    s_down = s_up = 0u;
+    s_dmax = 0;
+  }
+  __syncthreads();
+  u32 bad = 0;
+  int dmax = 0;
+  for (int v = threadIdx.x; v < n; v += blockDim.x) {
+    const int a = rp[v], b = rp[v + 1];
+    if (a > b || a < 0 || (long long)b > nnz) bad |= 1u;   // MCE_GRAPH_ROWPTR
+    else dmax = max(dmax, b - a);
+  }
+  if (threadIdx.x == 0 && (rp[0] != 0 || (long long)rp[n] != nnz)) bad |= 1u;
+  const u32 wb = wave_or_u32(bad);
+  const u32 wm = wave_max_u32((u32)dmax);
+  if (lane == 0) {
+    if (wb) atomicOr(&s_bad, wb);
+    if (wm) atomicMax(&s_dmax, (int)wm);
+  }
+  __syncthreads();
+  if (s_bad == 0u) {   // uniform
+    const int wave = threadIdx.x / MCE_WAVE, nwaves = blockDim.x / MCE_WAVE;
+    u32 down = 0, up = 0;
+    bad = 0;
+    for (int v = wave; v < n; v += nwaves) {
+      const int a = rp[v], b = rp[v + 1];
+      for (int e = a + lane; e < b; e += MCE_WAVE) bad |= val_edge(rp, ci, n, v, b - a, e, b, down, up);
+    }
+    const u32 bb = wave_or_u32(bad), wd = wave_sum_u32(down), wu = wave_sum_u32(up);
+    if (lane == 0) {
+      if (bb) atomicOr(&s_bad, bb);
+      if (wd) atomicAdd(&s_down, wd);
+      if (wu) atomicAdd(&s_up, wu);
+    }
+    __syncthreads();
+    if (threadIdx.x == 0 && s_bad == 0u && s_down != s_up) s_bad = 16u;   // MCE_GRAPH_ASYM
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    if (s_bad) atomicOr(&ctl->status, s_bad);
+    if (s_dmax) atomicMax(&ctl->max_degree, s_dmax);
+  }
+}
+
 // ------------------------------------------------------------------ k-core peel
 // Grid-wide barrier for a cooperative launch, without agent-scope fences (their
 // L2 write-back / invalidate serialises when hundreds of blocks issue them).
@@ -1108,6 +1163,10 @@ long long mce_validate_items(long long nnz) { return 2 * nnz / VAL_LONG + 1; }
 
 hipError_t mce_launch_validate(int n, long long nnz, const int* rp, const int* ci, MceCtl* ctl, u64* items,
                                int blocks, hipStream_t s) {
+  if (n <= VAL_SMALL_N && nnz <= VAL_SMALL_NNZ) {
+    hipLaunchKernelGGL(k_validate_small, dim3(1), dim3(1024), 0, s, n, nnz, rp, ci, ctl);
+    return hipGetLastError();
+  }
   int nb = max(1, min(blocks, (n + 255) / 256));
   hipLaunchKernelGGL(k_validate_rowptr, dim3(nb), dim3(256), 0, s, n, nnz, rp, ctl);
   hipError_t e = hipGetLastError();
