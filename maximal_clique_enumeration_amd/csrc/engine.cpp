@@ -43,6 +43,7 @@ struct mce_engine {
   DevBuf ctl, deg, rnd, core, alive0, alive1, front0, front1, bfront0, bfront1, pcount, xcount, lists, taboff, scan, heap, wl,
       slots, stats, mstack, mail, vitems;
   DevBuf src, fwd, fwdtmp, eroots, pcount2, xcount2;   // second-level subtrees
+  DevBuf hub_id, hub_v, hub_bm;                       // their hub adjacency bitmaps
   HostPinned host;    // staging for device -> host copies
   hipEvent_t ev[4 + 4 * MCE_NSUB] = {};
   bool have_events = false;
@@ -123,6 +124,8 @@ constexpr size_t kHistWords = MCE_MAX_P + 3;   // global histogram entries (size
 // control block, then the result words (hash, histogram): one clear, one read-back
 constexpr size_t kIoBytes = sizeof(MceCtl) + (1 + kHistWords) * sizeof(u64);
 static_assert(sizeof(MceCtl) % sizeof(u64) == 0, "results follow the control block");
+constexpr int kMaxHubs = 1024;                 // second-level orientation: hub adjacency bitmaps, at most
+constexpr size_t kHubBytes = 256ull << 20;     // this many, in at most this many bytes
 constexpr int kMicroStack = 4096;              // frames per wavefront stack of the micro search
 constexpr int kMicroCoopRootsPerWave = 4;     // micro launches with this many roots per wave share pivot scans
 // Tables other than micro ones are built by the split build: a root's rows are
@@ -184,12 +187,21 @@ mce_status run_impl(mce_engine* e, int32_t n, int64_t nnz, const int32_t* row_pt
   // second-level subtrees (section 3.2): the roots are the vertex roots' forward edges
   const bool l2 = (e->cfg.flags & MCE_FLAG_L2) != 0;
   e->info.level = l2 ? 2 : 1;
+  int maxhubs = 0;
   if (l2) {
     const size_t ne = (size_t)std::max<int64_t>(nnz, 1) * sizeof(int);
     if ((h = ensure(e->src, ne)) != hipSuccess || (h = ensure(e->eroots, ne)) != hipSuccess ||
         (h = ensure(e->pcount2, ne)) != hipSuccess || (h = ensure(e->xcount2, ne)) != hipSuccess ||
         (h = ensure(e->fwd, (size_t)std::max(cnt, 1) * sizeof(u64))) != hipSuccess ||
         (h = ensure(e->fwdtmp, (size_t)mce_scan_temp_words(std::max(cnt, 1)) * sizeof(u64))) != hipSuccess)
+      return hip_fail(e, h, "allocation");
+    // hub bitmaps within kHubBytes: n bits each, at most kMaxHubs
+    const size_t hub_bytes = ((size_t)n + 63) / 64 * sizeof(u64);
+    maxhubs = (int)std::min<size_t>(kMaxHubs, kHubBytes / std::max<size_t>(hub_bytes, 1));
+    if (maxhubs > 0 &&
+        ((h = ensure(e->hub_id, (size_t)n * sizeof(int))) != hipSuccess ||
+         (h = ensure(e->hub_v, (size_t)maxhubs * sizeof(int))) != hipSuccess ||
+         (h = ensure(e->hub_bm, (size_t)maxhubs * hub_bytes)) != hipSuccess))
       return hip_fail(e, h, "allocation");
   }
 
@@ -219,7 +231,8 @@ mce_status run_impl(mce_engine* e, int32_t n, int64_t nnz, const int32_t* row_pt
     return hip_fail(e, h, "orient launch");
   if (l2 && (h = mce_launch_l2_roots(n, nnz, row_ptr, col_idx, dp<int>(e->rnd), subset ? roots : nullptr, cnt,
                                      dp<u64>(e->fwd), dp<u64>(e->fwdtmp), dp<int>(e->src), dp<int>(e->eroots),
-                                     dp<int>(e->pcount2), dp<int>(e->xcount2), ctl, grid, s)) != hipSuccess)
+                                     dp<int>(e->pcount2), dp<int>(e->xcount2), dp<int>(e->hub_id),
+                                     dp<int>(e->hub_v), dp<u64>(e->hub_bm), maxhubs, ctl, grid, s)) != hipSuccess)
     return hip_fail(e, h, "second-level roots launch");
   MceCtl* hctl = static_cast<MceCtl*>(e->host.p);
   if ((h = hipMemcpyAsync(hctl, ctl, sizeof(MceCtl), hipMemcpyDeviceToHost, s)) != hipSuccess)
@@ -362,6 +375,9 @@ mce_status run_impl(mce_engine* e, int32_t n, int64_t nnz, const int32_t* row_pt
     bp.status = &ctl->status;
     bp.l2 = l2 ? 1 : 0;
     bp.src = dp<int>(e->src);
+    bp.hub_id = l2 && maxhubs > 0 ? dp<int>(e->hub_id) : nullptr;
+    bp.hub_bm = dp<u64>(e->hub_bm);
+    bp.hub_words = (n + 63) / 64;
     if (!micro) {
       // enough (root, part) blocks to fill the chip, at most one part per 64-row
       // slab, and at most about 8 slabs of the largest table per part
@@ -751,7 +767,8 @@ void mce_destroy(mce_engine* e) {
   DevBuf* bufs[] = {&e->ctl,    &e->deg,   &e->rnd,    &e->core,    &e->alive0, &e->alive1,
                     &e->front0, &e->front1, &e->bfront0, &e->bfront1, &e->pcount, &e->xcount, &e->lists,  &e->taboff, &e->scan,
                     &e->heap,   &e->wl,    &e->slots,  &e->stats,  &e->mstack, &e->mail, &e->vitems,
-                    &e->src,    &e->fwd,   &e->fwdtmp, &e->eroots, &e->pcount2, &e->xcount2};
+                    &e->src,    &e->fwd,   &e->fwdtmp, &e->eroots, &e->pcount2, &e->xcount2,
+                    &e->hub_id, &e->hub_v, &e->hub_bm};
   for (DevBuf* b : bufs) release(*b);
   if (e->host.p) (void)hipHostFree(e->host.p);
   for (auto& ev : e->ev)

@@ -155,6 +155,9 @@ struct BuildParams {
   const u64* tab_off;    // each root's table offset, as an exclusive prefix sum of table sizes that
                          // runs over all sub-classes: offsets relative to tab_off[0]
   u32* status;
+  const int* hub_id;     // second-level subtrees: hub index of each vertex (-1: none), or NULL
+  const u64* hub_bm;     // hub adjacency bitmaps, hub_words u64 each
+  int hub_words;
 };
 
 // Input checks. `items` holds mce_validate_items(nnz) words (pieces of long rows).
@@ -174,9 +177,12 @@ hipError_t mce_launch_orient(int n, const int* rp, const int* ci, const int* rnd
 // the forward edges as CSR positions (eroots, at most nnz; their number goes to
 // ctl->l2_roots), and per root |P| and |X| (pcount, xcount) and the tallies.
 // fwd holds the vertex roots' later-neighbour counts; fwd_tmp mce_scan_temp_words(nroots).
+// maxhubs > 0: hub_id (n), hub_v (maxhubs) and bm (maxhubs x ceil(n / 64) u64)
+// hold adjacency bitmaps of up to maxhubs high-degree vertices for the row tests.
 hipError_t mce_launch_l2_roots(int n, long long nnz, const int* rp, const int* ci, const int* rnd,
                                const int* roots, int nroots, u64* fwd, u64* fwd_tmp, int* src, int* eroots,
-                               int* pcount, int* xcount, MceCtl* ctl, int blocks, hipStream_t s);
+                               int* pcount, int* xcount, int* hub_id, int* hub_v, u64* bm, int maxhubs,
+                               MceCtl* ctl, int blocks, hipStream_t s);
 // Groups the roots by sub-class into `lists` and writes each one's table size
 // (u64 words) at the same position of `words`.
 hipError_t mce_launch_bucket(const int* roots, int nroots, const int* pcount, const int* xcount, int mode,

@@ -1243,6 +1243,48 @@ __global__ __launch_bounds__(256) void k_l2_expand(int n, const int* __restrict_
   }
 }
 
+// Hub adjacency bitmaps (second-level orientation). On power-law graphs most
+// forward edges point at high-degree vertices, and testing an entry of the
+// short row for membership in a hub's row took a binary search of about a
+// dozen dependent loads; with one n-bit bitmap per hub it is one load. Hubs are
+// the vertices of degree >= HUB_MIN_DEG, the first maxhubs of them by an atomic
+// counter (which ones only changes the speed).
+#define HUB_MIN_DEG 256
+__global__ __launch_bounds__(256) void k_hub_pick(int n, const int* __restrict__ rp, int* hub_id, int* hub_v,
+                                                   int maxhubs, MceCtl* ctl) {
+  if (ld_relaxed(&ctl->status) != 0) return;
+  for (int v = blockIdx.x * blockDim.x + threadIdx.x; v < n; v += gridDim.x * blockDim.x) {
+    int id = -1;
+    if (rp[v + 1] - rp[v] >= HUB_MIN_DEG) {
+      const int k = atomicAdd(&ctl->nhubs, 1);
+      if (k < maxhubs) {
+        id = k;
+        hub_v[k] = v;
+      }
+    }
+    hub_id[v] = id;
+  }
+}
+
+// One block per hub: clear its bitmap (words u64), then set the bit of every neighbour.
+__global__ __launch_bounds__(256) void k_hub_fill(const int* __restrict__ rp, const int* __restrict__ ci,
+                                                   const int* __restrict__ hub_v, int maxhubs, int words, u64* bm,
+                                                   MceCtl* ctl) {
+  if (ld_relaxed(&ctl->status) != 0) return;
+  const int nh = min(ld_relaxed(&ctl->nhubs), maxhubs);
+  for (int h = blockIdx.x; h < nh; h += gridDim.x) {
+    u64* b = bm + (size_t)h * words;
+    for (int w = threadIdx.x; w < words; w += blockDim.x) b[w] = 0ull;
+    __syncthreads();
+    const int v = hub_v[h];
+    for (int k = rp[v] + (int)threadIdx.x; k < rp[v + 1]; k += blockDim.x) {
+      const int u = ci[k];
+      atomicOr(&b[u >> 6], 1ull << (u & 63));
+    }
+    __syncthreads();
+  }
+}
+
 // Per second-level root: |P| and |X| by intersecting the two rows (each entry
 // of the shorter one is searched in the longer one), then the same tallies as
 // k_orient. A wavefront takes G consecutive roots, four at a time: lane group
@@ -1255,7 +1297,8 @@ __global__ __launch_bounds__(256) void k_l2_expand(int n, const int* __restrict_
 __global__ __launch_bounds__(256) void k_orient_l2(const int* __restrict__ rp, const int* __restrict__ ci,
                                                     const int* __restrict__ rnd, const int* __restrict__ src,
                                                     const int* __restrict__ eroots, int* pcount, int* xcount,
-                                                    MceCtl* ctl) {
+                                                    const int* __restrict__ hub_id, const u64* __restrict__ bm,
+                                                    int words, MceCtl* ctl) {
   if (ld_relaxed(&ctl->status) != 0) return;
   constexpr int NQ = MCE_WAVE / L2_GROUP;   // roots in flight per wavefront
   const int lane = lane_id();
@@ -1282,9 +1325,11 @@ __global__ __launch_bounds__(256) void k_orient_l2(const int* __restrict__ rp, c
         const bool si = bi - ai <= bj - aj;   // scan the shorter row
         const int sa = si ? ai : aj, sb = si ? bi : bj, oa = si ? aj : ai, ob = si ? bj : bi;
         const int rj = rnd[vj];
+        const int hid = hub_id ? hub_id[si ? vj : vi] : -1;   // the longer row's owner: a hub?
+        const u64* hb = bm + (size_t)(hid < 0 ? 0 : hid) * words;
         for (int k = sa + sl; k < sb; k += L2_GROUP) {
           const int c = ci[k];
-          if (csr_range_has(ci, oa, ob, c)) {
+          if (hid >= 0 ? ((hb[c >> 6] >> (c & 63)) & 1ull) != 0ull : csr_range_has(ci, oa, ob, c)) {
             if (order_after(rnd[c], c, rj, vj)) cp++;
             else cx++;
           }
@@ -1330,8 +1375,18 @@ __global__ __launch_bounds__(256) void k_orient_l2(const int* __restrict__ rp, c
 
 hipError_t mce_launch_l2_roots(int n, long long nnz, const int* rp, const int* ci, const int* rnd,
                                const int* roots, int nroots, u64* fwd, u64* fwd_tmp, int* src, int* eroots,
-                               int* pcount, int* xcount, MceCtl* ctl, int blocks, hipStream_t s) {
+                               int* pcount, int* xcount, int* hub_id, int* hub_v, u64* bm, int maxhubs,
+                               MceCtl* ctl, int blocks, hipStream_t s) {
   hipError_t e;
+  const int words = (n + 63) / 64;
+  if (maxhubs > 0) {
+    const int nbh = (int)std::max(1LL, std::min((long long)blocks, ((long long)n + 255) / 256));
+    hipLaunchKernelGGL(k_hub_pick, dim3(nbh), dim3(256), 0, s, n, rp, hub_id, hub_v, maxhubs, ctl);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipLaunchKernelGGL(k_hub_fill, dim3(std::max(1, std::min(blocks, maxhubs))), dim3(256), 0, s, rp, ci,
+                       (const int*)hub_v, maxhubs, words, bm, ctl);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
   const int nbr = (int)std::max(1LL, std::min((long long)blocks, ((long long)n + 3) / 4));
   hipLaunchKernelGGL(k_coo_src, dim3(nbr), dim3(256), 0, s, n, rp, src);
   if ((e = hipGetLastError()) != hipSuccess) return e;
@@ -1342,7 +1397,7 @@ hipError_t mce_launch_l2_roots(int n, long long nnz, const int* rp, const int* c
   if ((e = hipGetLastError()) != hipSuccess) return e;
   const int nbo = (int)std::max(1LL, std::min((long long)blocks, nnz / 8 + 1));
   hipLaunchKernelGGL(k_orient_l2, dim3(nbo), dim3(256), 0, s, rp, ci, rnd, (const int*)src, (const int*)eroots,
-                     pcount, xcount, ctl);
+                     pcount, xcount, maxhubs > 0 ? (const int*)hub_id : nullptr, (const u64*)bm, words, ctl);
   return hipGetLastError();
 }
 

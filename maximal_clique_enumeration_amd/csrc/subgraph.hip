@@ -34,10 +34,19 @@
 struct RootHood {
   int sa, sb;      // the row scanned
   int oa, ob;      // the row searched for membership (oa < 0: none)
+  const u64* hb;   // that row's owner's adjacency bitmap if it is a hub, else NULL
   int piv, pivr;   // P = the members after piv (round pivr), X = the others
   int k0;          // |R|
   u64 term;        // R's hash terms summed
 };
+
+// Adjacency bitmap of vertex v if it is a hub (second-level runs), else NULL:
+// a membership test in its row is then one load instead of a binary search.
+__device__ __forceinline__ const u64* hub_bitmap(const BuildParams& prm, int v) {
+  if (!prm.hub_id) return nullptr;
+  const int h = prm.hub_id[v];
+  return h < 0 ? nullptr : prm.hub_bm + (size_t)h * prm.hub_words;
+}
 
 __device__ __forceinline__ RootHood root_hood(const BuildParams& prm, int rid) {
   const int* __restrict__ rp = prm.rp;
@@ -46,6 +55,7 @@ __device__ __forceinline__ RootHood root_hood(const BuildParams& prm, int rid) {
     h.sa = rp[rid];
     h.sb = rp[rid + 1];
     h.oa = h.ob = -1;
+    h.hb = nullptr;
     h.piv = rid;
     h.pivr = prm.rnd[rid];
     h.k0 = 1;
@@ -58,6 +68,7 @@ __device__ __forceinline__ RootHood root_hood(const BuildParams& prm, int rid) {
     h.sb = si ? bi : bj;
     h.oa = si ? aj : ai;
     h.ob = si ? bj : bi;
+    h.hb = hub_bitmap(prm, si ? vj : vi);
     h.piv = vj;
     h.pivr = prm.rnd[vj];
     h.k0 = 2;
@@ -67,7 +78,9 @@ __device__ __forceinline__ RootHood root_hood(const BuildParams& prm, int rid) {
 }
 
 __device__ __forceinline__ bool hood_has(const int* __restrict__ ci, const RootHood& h, int u) {
-  return h.oa < 0 || csr_range_has(ci, h.oa, h.ob, u);
+  if (h.oa < 0) return true;
+  if (h.hb) return (h.hb[u >> 6] >> (u & 63)) & 1ull;
+  return csr_range_has(ci, h.oa, h.ob, u);
 }
 
 // ------------------------------------------------------------------ hash of P
@@ -198,9 +211,10 @@ __global__ __launch_bounds__(64) void k_build_micro(BuildParams prm) {
     for (int t0 = 0; t0 < nrows; t0 += MCE_WAVE) {
       const int t = t0 + lane;
       const bool valid = t < nrows;
-      int ga = 0, d = 0;
+      int ga = 0, d = 0, gv = 0;
       if (valid) {
         const int g = t < np ? s_id[t] : s_id[MCE_MICRO_MAX + t - np];
+        gv = g;
         ga = rp[g];
         d = rp[g + 1] - ga;
       }
@@ -257,7 +271,11 @@ __global__ __launch_bounds__(64) void k_build_micro(BuildParams prm) {
           }
           const int gal = __shfl(ga, l < 0 ? 0 : l);
           const int gdl = __shfl(d, l < 0 ? 0 : l);
-          const bool found = l >= 0 && jj < np && csr_range_has(ci, gal, gal + gdl, s_id[jj]);
+          const int gvl = __shfl(gv, l < 0 ? 0 : l);
+          const u64* hb = l >= 0 ? hub_bitmap(prm, gvl) : nullptr;   // a hub row: one bit per probe
+          const int key = jj < np ? s_id[jj] : 0;
+          const bool found = l >= 0 && jj < np &&
+                             (hb ? ((hb[key >> 6] >> (key & 63)) & 1ull) != 0ull : csr_range_has(ci, gal, gal + gdl, key));
           const u64 fm = ballot(found);
           if (jj == 0 && l >= 0) {
             const u64 mask = npw >= 64 ? ~0ull : ((1ull << npw) - 1ull);
