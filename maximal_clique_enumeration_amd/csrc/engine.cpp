@@ -195,7 +195,10 @@ mce_status run_impl(mce_engine* e, int32_t n, int64_t nnz, const int32_t* row_pt
         (h = ensure(e->fwd, (size_t)std::max(cnt, 1) * sizeof(u64))) != hipSuccess ||
         (h = ensure(e->fwdtmp, (size_t)mce_scan_temp_words(std::max(cnt, 1)) * sizeof(u64))) != hipSuccess)
       return hip_fail(e, h, "allocation");
-    // hub bitmaps within kHubBytes: n bits each, at most kMaxHubs
+  }
+  // hub adjacency bitmaps (second-level runs; first-level builds did not gain
+  // from them): n bits each, at most kMaxHubs within kHubBytes
+  if (l2) {
     const size_t hub_bytes = ((size_t)n + 63) / 64 * sizeof(u64);
     maxhubs = (int)std::min<size_t>(kMaxHubs, kHubBytes / std::max<size_t>(hub_bytes, 1));
     if (maxhubs > 0 &&
@@ -225,6 +228,9 @@ mce_status run_impl(mce_engine* e, int32_t n, int64_t nnz, const int32_t* row_pt
                            dp<int>(e->bfront0), dp<int>(e->bfront1), ctl, budget, pblocks, s)) != hipSuccess)
     return hip_fail(e, h, "peel launch");
   if (timing) (void)hipEventRecord(e->ev[2], s);
+  if (maxhubs > 0 && (h = mce_launch_hubs(n, row_ptr, col_idx, dp<int>(e->hub_id), dp<int>(e->hub_v),
+                                         dp<u64>(e->hub_bm), maxhubs, ctl, grid, s)) != hipSuccess)
+    return hip_fail(e, h, "hub bitmaps launch");
   if ((h = mce_launch_orient(n, row_ptr, col_idx, dp<int>(e->rnd), subset ? roots : nullptr, cnt,
                              dp<int>(e->pcount), dp<int>(e->xcount), ctl, l2 ? dp<u64>(e->fwd) : nullptr, grid,
                              s)) != hipSuccess)
@@ -375,7 +381,7 @@ mce_status run_impl(mce_engine* e, int32_t n, int64_t nnz, const int32_t* row_pt
     bp.status = &ctl->status;
     bp.l2 = l2 ? 1 : 0;
     bp.src = dp<int>(e->src);
-    bp.hub_id = l2 && maxhubs > 0 ? dp<int>(e->hub_id) : nullptr;
+    bp.hub_id = maxhubs > 0 ? dp<int>(e->hub_id) : nullptr;
     bp.hub_bm = dp<u64>(e->hub_bm);
     bp.hub_words = (n + 63) / 64;
     if (!micro) {

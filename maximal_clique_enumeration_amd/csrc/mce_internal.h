@@ -177,8 +177,13 @@ hipError_t mce_launch_orient(int n, const int* rp, const int* ci, const int* rnd
 // the forward edges as CSR positions (eroots, at most nnz; their number goes to
 // ctl->l2_roots), and per root |P| and |X| (pcount, xcount) and the tallies.
 // fwd holds the vertex roots' later-neighbour counts; fwd_tmp mce_scan_temp_words(nroots).
-// maxhubs > 0: hub_id (n), hub_v (maxhubs) and bm (maxhubs x ceil(n / 64) u64)
-// hold adjacency bitmaps of up to maxhubs high-degree vertices for the row tests.
+// maxhubs > 0: hub_id (n) and bm (maxhubs x ceil(n / 64) u64) hold the
+// adjacency bitmaps that mce_launch_hubs built, for the row tests.
+// Adjacency bitmaps of up to maxhubs vertices of degree >= HUB_MIN_DEG: hub_id
+// (n ints, -1: none), hub_v (maxhubs), bm (maxhubs x ceil(n / 64) u64); the
+// number of candidates goes to ctl->nhubs.
+hipError_t mce_launch_hubs(int n, const int* rp, const int* ci, int* hub_id, int* hub_v, u64* bm, int maxhubs,
+                           MceCtl* ctl, int blocks, hipStream_t s);
 hipError_t mce_launch_l2_roots(int n, long long nnz, const int* rp, const int* ci, const int* rnd,
                                const int* roots, int nroots, u64* fwd, u64* fwd_tmp, int* src, int* eroots,
                                int* pcount, int* xcount, int* hub_id, int* hub_v, u64* bm, int maxhubs,

@@ -1373,20 +1373,24 @@ __global__ __launch_bounds__(256) void k_orient_l2(const int* __restrict__ rp, c
   }
 }
 
+hipError_t mce_launch_hubs(int n, const int* rp, const int* ci, int* hub_id, int* hub_v, u64* bm, int maxhubs,
+                           MceCtl* ctl, int blocks, hipStream_t s) {
+  const int words = (n + 63) / 64;
+  const int nbh = (int)std::max(1LL, std::min((long long)blocks, ((long long)n + 255) / 256));
+  hipLaunchKernelGGL(k_hub_pick, dim3(nbh), dim3(256), 0, s, n, rp, hub_id, hub_v, maxhubs, ctl);
+  hipError_t e;
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipLaunchKernelGGL(k_hub_fill, dim3(std::max(1, std::min(blocks, maxhubs))), dim3(256), 0, s, rp, ci,
+                     (const int*)hub_v, maxhubs, words, bm, ctl);
+  return hipGetLastError();
+}
+
 hipError_t mce_launch_l2_roots(int n, long long nnz, const int* rp, const int* ci, const int* rnd,
                                const int* roots, int nroots, u64* fwd, u64* fwd_tmp, int* src, int* eroots,
                                int* pcount, int* xcount, int* hub_id, int* hub_v, u64* bm, int maxhubs,
                                MceCtl* ctl, int blocks, hipStream_t s) {
   hipError_t e;
   const int words = (n + 63) / 64;
-  if (maxhubs > 0) {
-    const int nbh = (int)std::max(1LL, std::min((long long)blocks, ((long long)n + 255) / 256));
-    hipLaunchKernelGGL(k_hub_pick, dim3(nbh), dim3(256), 0, s, n, rp, hub_id, hub_v, maxhubs, ctl);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-    hipLaunchKernelGGL(k_hub_fill, dim3(std::max(1, std::min(blocks, maxhubs))), dim3(256), 0, s, rp, ci,
-                       (const int*)hub_v, maxhubs, words, bm, ctl);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-  }
   const int nbr = (int)std::max(1LL, std::min((long long)blocks, ((long long)n + 3) / 4));
   hipLaunchKernelGGL(k_coo_src, dim3(nbr), dim3(256), 0, s, n, rp, src);
   if ((e = hipGetLastError()) != hipSuccess) return e;

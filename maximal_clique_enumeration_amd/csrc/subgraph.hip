@@ -434,9 +434,10 @@ __global__ __launch_bounds__(64) void k_build_rows(BuildParams prm) {
       const int t0 = slab * MCE_WAVE;
       const int t = t0 + lane;
       const bool valid = t < nrows;
-      int ga = 0, d = 0;
+      int ga = 0, d = 0, gv = 0;
       if (valid) {
         const int g = ids[t];
+        gv = g;
         ga = rp[g];
         d = rp[g + 1] - ga;
       }
@@ -487,18 +488,23 @@ __global__ __launch_bounds__(64) void k_build_rows(BuildParams prm) {
       // at a time (their binary searches run in lockstep, so the loads overlap)
       for (u64 m = pm; m != 0;) {
         int lr[4], lo[4], hi[4];
+        const u64* hbz[4];   // a hub's row: bit tests instead of the search
 #pragma unroll
         for (int z = 0; z < 4; z++) {
           lr[z] = m ? __builtin_ctzll(m) : -1;
           m = m ? (m & (m - 1ull)) : 0ull;
+          hbz[z] = lr[z] >= 0 ? hub_bitmap(prm, read_lane(gv, lr[z])) : nullptr;
           lo[z] = lr[z] >= 0 ? read_lane(ga, lr[z]) : 0;
-          hi[z] = lr[z] >= 0 ? lo[z] + read_lane(d, lr[z]) : 0;
+          hi[z] = lr[z] >= 0 && !hbz[z] ? lo[z] + read_lane(d, lr[z]) : lo[z];
         }
         for (int w0 = 0; w0 < W; w0++) {
           const int j = w0 * 64 + lane;
           const int key = j < np ? ids[j] : -1;
           bool f[4];
           csr_range_has4(ci, lo, hi, key, f);
+#pragma unroll
+          for (int z = 0; z < 4; z++)
+            if (hbz[z]) f[z] = key >= 0 && ((hbz[z][key >> 6] >> (key & 63)) & 1ull) != 0ull;
 #pragma unroll
           for (int z = 0; z < 4; z++) {
             const u64 fm = ballot(f[z] && j < np);
