@@ -113,6 +113,17 @@ def test_multipartite(eng, sizes):
     assert got.count == int(np.prod(sizes))
 
 
+def test_more_hubs_than_bitmaps():
+    """Second-level runs give vertices of degree >= 256 an adjacency bitmap, at
+    most 1024 of them. K_{600,600} has 1200 such vertices, so some rows are
+    tested with bitmaps and the others with binary searches; every edge is a
+    maximal clique (the common neighbourhoods are empty)."""
+    g = mi.complete_multipartite([600, 600])
+    with mce.Engine(device=0, timeout_ms=20000, level=2) as e:
+        got = check(e, g)
+        assert got.count == 600 * 600 and got.hist == [0, 0, 600 * 600]
+
+
 @pytest.mark.parametrize("core", [300, 700, 1100])
 def test_hub_rows(eng, core):
     """Core roots of widths 8, 16 and 32 words whose X holds hubs: the hub rows
