@@ -133,8 +133,8 @@ __global__ __launch_bounds__(256) void k_validate_long(int n, const int* __restr
 // Small graphs: the same checks in one block, passes separated by block
 // barriers (three launches cost more than the work): row_ptr first, then the
 // rows (any length: one wavefront per row), then the two edge counts.
-#define VAL_SMALL_N 16384
-#define VAL_SMALL_NNZ 262144
+#define VAL_SMALL_N 4096
+#define VAL_SMALL_NNZ 16384
 __global__ __launch_bounds__(1024) void k_validate_small(int n, long long nnz, const int* __restrict__ rp,
                                                           const int* __restrict__ ci, MceCtl* ctl) {
   __shared__ u32 s_bad, s_down, s_up;
