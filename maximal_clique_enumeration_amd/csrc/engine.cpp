@@ -41,7 +41,7 @@ struct mce_engine {
   std::string err;
 
   DevBuf ctl, deg, rnd, core, alive0, alive1, front0, front1, bfront0, bfront1, pcount, xcount, lists, taboff, scan, heap, wl,
-      slots, stats, mstack, mail, vitems;
+      slots, stats, mstack, mail;
   DevBuf src, fwd, fwdtmp, eroots, pcount2, xcount2;   // second-level subtrees
   DevBuf hub_id, hub_v, hub_bm;                       // their hub adjacency bitmaps
   HostPinned host;    // staging for device -> host copies
@@ -215,9 +215,7 @@ mce_status run_impl(mce_engine* e, int32_t n, int64_t nnz, const int32_t* row_pt
   const int grid = std::max(1, e->num_cu * 8);
   if (timing) (void)hipEventRecord(e->ev[0], s);
   if (e->cfg.validate) {
-    if ((h = ensure(e->vitems, (size_t)mce_validate_items(nnz) * sizeof(u64))) != hipSuccess)
-      return hip_fail(e, h, "allocation");
-    if ((h = mce_launch_validate(n, nnz, row_ptr, col_idx, ctl, dp<u64>(e->vitems), grid, s)) != hipSuccess)
+    if ((h = mce_launch_validate(n, nnz, row_ptr, col_idx, ctl, grid, s)) != hipSuccess)
       return hip_fail(e, h, "validate launch");
   }
   if (timing) (void)hipEventRecord(e->ev[1], s);
@@ -774,7 +772,7 @@ void mce_destroy(mce_engine* e) {
   (void)hipSetDevice(e->device);
   DevBuf* bufs[] = {&e->ctl,    &e->deg,   &e->rnd,    &e->core,    &e->alive0, &e->alive1,
                     &e->front0, &e->front1, &e->bfront0, &e->bfront1, &e->pcount, &e->xcount, &e->lists,  &e->taboff, &e->scan,
-                    &e->heap,   &e->wl,    &e->slots,  &e->stats,  &e->mstack, &e->mail, &e->vitems,
+                    &e->heap,   &e->wl,    &e->slots,  &e->stats,  &e->mstack, &e->mail,
                     &e->src,    &e->fwd,   &e->fwdtmp, &e->eroots, &e->pcount2, &e->xcount2,
                     &e->hub_id, &e->hub_v, &e->hub_bm};
   for (DevBuf* b : bufs) release(*b);

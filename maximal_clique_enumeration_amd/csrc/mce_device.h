@@ -114,8 +114,8 @@ struct MceCtl {
   int bsize[3];          // peel: big-vertex frontier sizes (same rotation)
   int bedge[3];          // peel: the big vertices' CSR row lengths summed (same rotation)
   int asum[2];           // peel: each remaining list's CSR row lengths summed (by list parity)
-  u32 vitems;            // validation: pieces of long rows queued for the second pass
-  u32 vdone;             // validation: blocks of the second pass that finished
+  u32 vpad;
+  u32 vdone;             // validation: blocks of the entry pass that finished
   u64 vdown, vup;        // validation: edges from the larger (degree, id) end, and from the smaller
   u32 seg_gen;           // peel: segments of tiny rounds that block 0 has handed back
   u32 seg_arrive;        // peel: blocks that started waiting for a segment (summed over segments)

@@ -160,10 +160,9 @@ struct BuildParams {
   int hub_words;
 };
 
-// Input checks. `items` holds mce_validate_items(nnz) words (pieces of long rows).
-long long mce_validate_items(long long nnz);
-hipError_t mce_launch_validate(int n, long long nnz, const int* rp, const int* ci, MceCtl* ctl, u64* items,
-                               int blocks, hipStream_t s);
+// Input checks.
+hipError_t mce_launch_validate(int n, long long nnz, const int* rp, const int* ci, MceCtl* ctl, int blocks,
+                               hipStream_t s);
 hipError_t mce_launch_peel(int n, const int* rp, const int* ci, int* deg, int* rnd, int* core, int* alive0,
                            int* alive1, int* front0, int* front1, int* bfront0, int* bfront1, MceCtl* ctl,
                            u64 budget, int blocks, hipStream_t s);

@@ -41,10 +41,12 @@ __global__ __launch_bounds__(256) void k_validate_rowptr(int n, long long nnz, c
 // distinct stored edge from the earlier endpoint, so if both kinds are equally
 // many, every edge of the second kind is such a reverse as well: the graph is
 // symmetric exactly when all searches succeed and the two counts are equal.
-// Rows longer than VAL_LONG go, in VAL_LONG-edge pieces, to a second pass whose
-// pieces are dealt over the whole grid (one wavefront per row would leave a hub
-// of tens of thousands of edges to a single wavefront).
-#define VAL_LONG 2048
+// The entries are dealt in equal contiguous ranges, one per wavefront: the
+// check of an entry (at most one binary search, in the shorter row) costs about
+// the same whatever the length of its row, so equal ranges are equal work on any
+// degree distribution. (Whole rows dealt to waves left single waves holding
+// twenty times the mean work on an R-MAT graph, whose degrees follow the bit
+// patterns of the ids.)
 
 __device__ __forceinline__ u32 val_edge(const int* __restrict__ rp, const int* __restrict__ ci, int n, int v, int dv,
                                         int e, int b, u32& down, u32& up) {
@@ -75,49 +77,61 @@ __device__ __forceinline__ void val_flush(MceCtl* ctl, u32 bad, u32 down, u32 up
   }
 }
 
-// One wavefront per row of at most VAL_LONG edges; longer rows are queued as
-// (row, piece) items for k_validate_long.
-__global__ __launch_bounds__(256) void k_validate_cols(int n, const int* __restrict__ rp,
-                                                        const int* __restrict__ ci, MceCtl* ctl, u64* items) {
-  if (ld_relaxed(&ctl->status) != 0) return;
+__device__ __forceinline__ int val_lane_fetch(int v, int src) { return __builtin_amdgcn_ds_bpermute(src << 2, v); }
+
+// The row holding entry e0 < nnz: the largest v with rp[v] <= e0, by a 64-way
+// search (each step probes 64 evenly spaced row starts; rp is monotone, so the
+// probes at or below e0 are a prefix of the lanes). Whole wave.
+__device__ __forceinline__ int val_row_of(const int* __restrict__ rp, int n, int e0) {
   const int lane = lane_id();
-  const int wave = (blockIdx.x * blockDim.x + threadIdx.x) / MCE_WAVE;
-  const int nwaves = gridDim.x * blockDim.x / MCE_WAVE;
-  u32 bad = 0, down = 0, up = 0;
-  for (int v = wave; v < n; v += nwaves) {
-    const int a = rp[v], b = rp[v + 1];
-    const int dv = b - a;
-    if (dv > VAL_LONG) {
-      const u32 np = (u32)((dv + VAL_LONG - 1) / VAL_LONG);
-      u32 pos = 0;
-      if (lane == 0) pos = atomicAdd(&ctl->vitems, np);
-      pos = (u32)read_lane((int)pos, 0);
-      for (u32 c = (u32)lane; c < np; c += MCE_WAVE) items[pos + c] = ((u64)(u32)v << 32) | c;
-      continue;
-    }
-    for (int e = a + lane; e < b; e += MCE_WAVE) bad |= val_edge(rp, ci, n, v, dv, e, b, down, up);
+  int lo = 0, hi = n;   // rp[lo] <= e0 < rp[hi]
+  while (hi - lo > 1) {
+    const int step = (hi - lo + MCE_WAVE - 1) / MCE_WAVE;
+    const int p = lo + lane * step;
+    const u64 m = ballot(p < hi && rp[p] <= e0);   // lane 0 (p = lo) always set
+    lo += (63 - __builtin_clzll(m)) * step;
+    hi = min(hi, lo + step);
   }
-  val_flush(ctl, bad, down, up);
+  return lo;
 }
 
-// The queued pieces of long rows, dealt over all wavefronts. The last block to
-// finish compares the two edge counts (every block's count atomics are complete
-// before it counts itself done).
-__global__ __launch_bounds__(256) void k_validate_long(int n, const int* __restrict__ rp,
-                                                        const int* __restrict__ ci, MceCtl* ctl, const u64* items) {
-  if (ld_relaxed(&ctl->status) == 0) {
+// Wave w checks entries [w * per_wave, (w + 1) * per_wave), 64 at a time. The
+// rows of a tile's entries come from one load of the next 64 row ends (lane j:
+// the end of row cur + j) and a binary search over them in registers; a tile
+// that spans more than 64 rows (empty rows) loads the next 64. The last block
+// compares the two edge counts.
+__global__ __launch_bounds__(256) void k_validate_cols(int n, long long nnz, int per_wave,
+                                                        const int* __restrict__ rp, const int* __restrict__ ci,
+                                                        MceCtl* ctl) {
+  const int wave = (blockIdx.x * blockDim.x + threadIdx.x) / MCE_WAVE;
+  const long long e0l = (long long)wave * per_wave;
+  if (ld_relaxed(&ctl->status) == 0 && e0l < nnz) {
     const int lane = lane_id();
-    const int wave = (blockIdx.x * blockDim.x + threadIdx.x) / MCE_WAVE;
-    const int nwaves = gridDim.x * blockDim.x / MCE_WAVE;
-    const u32 ni = ld_relaxed(&ctl->vitems);
+    const int e0 = (int)e0l, e1 = (int)min(nnz, e0l + per_wave);
     u32 bad = 0, down = 0, up = 0;
-    for (u32 i = (u32)wave; i < ni; i += (u32)nwaves) {
-      const u64 it = items[i];
-      const int v = (int)(it >> 32);
-      const int c = (int)(u32)it;
-      const int a = rp[v], b = rp[v + 1];
-      const int e0 = a + c * VAL_LONG, e1 = min(b, e0 + VAL_LONG);
-      for (int e = e0 + lane; e < e1; e += MCE_WAVE) bad |= val_edge(rp, ci, n, v, b - a, e, b, down, up);
+    int v = val_row_of(rp, n, e0);   // row of the tile's first entry
+    for (int t = e0; t < e1; t += MCE_WAVE) {
+      const int e = t + lane;
+      bool open = e < e1;
+      int row = 0, a = 0, b = 0;
+      for (int cur = v;; cur += MCE_WAVE) {
+        const int cend = cur + lane + 1 <= n ? rp[cur + lane + 1] : INT_MAX;
+        int k = 0;   // rows cur .. cur + k - 1 end at or before e
+        for (int st = MCE_WAVE / 2; st >= 1; st >>= 1) k += val_lane_fetch(cend, k + st - 1) <= e ? st : 0;
+        if (k == MCE_WAVE - 1 && val_lane_fetch(cend, MCE_WAVE - 1) <= e) k = MCE_WAVE;
+        const int kb = min(k, MCE_WAVE - 1);
+        const int bk = val_lane_fetch(cend, kb);
+        const int ak = val_lane_fetch(cend, kb > 0 ? kb - 1 : 0);
+        if (open && k < MCE_WAVE) {
+          row = cur + k;
+          b = bk;
+          a = k > 0 ? ak : rp[cur];
+          open = false;
+        }
+        if (!ballot(open)) break;
+      }
+      if (e < e1) bad |= val_edge(rp, ci, n, row, b - a, e, b, down, up);
+      v = read_lane(row, MCE_WAVE - 1);   // the next tile starts in or after this row
     }
     val_flush(ctl, bad, down, up);
   }
@@ -130,9 +144,6 @@ __global__ __launch_bounds__(256) void k_validate_long(int n, const int* __restr
   }
 }
 
-// Small graphs: the same checks in one block, passes separated by block
-// barriers (three launches cost more than the work): row_ptr first, then the
-// rows (any length: one wavefront per row), then the two edge counts.
 #define VAL_SMALL_N 4096
 #define VAL_SMALL_NNZ 16384
 __global__ __launch_bounds__(1024) void k_validate_small(int n, long long nnz, const int* __restrict__ rp,
@@ -1159,10 +1170,9 @@ __global__ __launch_bounds__(256) void k_bucket(const int* __restrict__ roots, i
 }
 
 // ------------------------------------------------------------------ launchers
-long long mce_validate_items(long long nnz) { return 2 * nnz / VAL_LONG + 1; }
 
-hipError_t mce_launch_validate(int n, long long nnz, const int* rp, const int* ci, MceCtl* ctl, u64* items,
-                               int blocks, hipStream_t s) {
+hipError_t mce_launch_validate(int n, long long nnz, const int* rp, const int* ci, MceCtl* ctl, int blocks,
+                               hipStream_t s) {
   if (n <= VAL_SMALL_N && nnz <= VAL_SMALL_NNZ) {
     hipLaunchKernelGGL(k_validate_small, dim3(1), dim3(1024), 0, s, n, nnz, rp, ci, ctl);
     return hipGetLastError();
@@ -1171,12 +1181,12 @@ hipError_t mce_launch_validate(int n, long long nnz, const int* rp, const int* c
   hipLaunchKernelGGL(k_validate_rowptr, dim3(nb), dim3(256), 0, s, n, nnz, rp, ctl);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  int nbw = (int)std::max(1LL, std::min((long long)blocks, ((long long)n + 3) / 4));
-  hipLaunchKernelGGL(k_validate_cols, dim3(nbw), dim3(256), 0, s, n, rp, ci, ctl, items);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
-  // pieces of long rows: at most 2 nnz / VAL_LONG of them
-  const int nbl = (int)std::max(1LL, std::min((long long)blocks, nnz / (4LL * VAL_LONG)));
-  hipLaunchKernelGGL(k_validate_long, dim3(nbl), dim3(256), 0, s, n, rp, ci, ctl, (const u64*)items);
+  // equal whole tiles of entries per wave, four waves per block
+  const long long tiles = (nnz + MCE_WAVE - 1) / MCE_WAVE;
+  const int nbw = (int)std::max(1LL, std::min((long long)blocks, (tiles + 3) / 4));
+  const long long nw = 4LL * nbw;
+  const int per_wave = (int)((tiles + nw - 1) / nw * MCE_WAVE);
+  hipLaunchKernelGGL(k_validate_cols, dim3(nbw), dim3(256), 0, s, n, nnz, per_wave, rp, ci, ctl);
   return hipGetLastError();
 }
 

@@ -247,8 +247,11 @@ def _bad(eng, n, rp, ci):
     return eng.graph_info()["graph_errors"]
 
 
-def test_rejects_malformed(eng):
-    g = mi.random_small(12, 0.5, 5)
+@pytest.mark.parametrize("make", [lambda: mi.random_small(12, 0.5, 5), lambda: mi.erdos_renyi(6000, 0.002, 3)])
+def test_rejects_malformed(eng, make):
+    """Each kind of malformed CSR is rejected: on a small graph (checked by one
+    block) and on a larger one (the grid checks: rows in 16-lane groups)."""
+    g = make()
     rp, ci = g.row_ptr.copy(), g.col_idx.copy()
     bad = ci.copy(); bad[0] = g.n
     assert _bad(eng, g.n, rp, bad) & mce.MCE_GRAPH_RANGE
