@@ -1051,10 +1051,16 @@ __device__ void tally_roots(MceCtl* ctl, bool valid, int p, int x) {
 
 #define ORIENT_LONG 128   // rows longer than this are counted by the whole wavefront
 
+// Later (|P|) and earlier (|X|) neighbours of every root. With many roots one
+// thread takes each root (a wavefront takes each long row in turn); with at most
+// one root per wavefront of the grid (per_wave), each wavefront takes one root
+// and its lanes share the row: a thread alone would walk the row one dependent
+// pair of loads (entry, then its round) at a time.
+
 __global__ __launch_bounds__(256) void k_orient(int n, const int* __restrict__ rp, const int* __restrict__ ci,
                                                  const int* __restrict__ rnd, const int* __restrict__ roots,
                                                  int nroots, int* pcount, int* xcount, MceCtl* ctl, u64* fwd,
-                                                 int tally) {
+                                                 int tally, int per_wave) {
   if (ld_relaxed(&ctl->status) != 0) return;
   const int lane = lane_id();
   const int gsize = gridDim.x * blockDim.x;
@@ -1062,61 +1068,98 @@ __global__ __launch_bounds__(256) void k_orient(int n, const int* __restrict__ r
   u64 iso = 0, iso_hash = 0;
   int pmax = 0, xmax = 0, dmax = 0;
   u32 lim = 0;
-  for (int base = blockIdx.x * blockDim.x; base < cnt; base += gsize) {
-    const int i = base + threadIdx.x;
-    int p = 0, x = 0;
-    bool valid = false;
-    const int v = i < cnt ? (roots ? roots[i] : i) : 0;
-    if (i < cnt && (v < 0 || v >= n)) {   // caller-supplied root out of range: flag it, touch nothing
-      lim |= 2u;
-      pcount[i] = 0;
-      xcount[i] = 0;
-    }
-    // later neighbours: one thread per short row; the whole wavefront takes each
-    // long row in turn (a hub row would keep one thread busy for its whole length)
-    const bool inr = i < cnt && v >= 0 && v < n;
-    int a = 0, b = 0, rv = 0;
-    if (inr) {
-      a = rp[v];
-      b = rp[v + 1];
-      rv = rnd[v];
-    }
-    const bool longrow = inr && b - a > ORIENT_LONG;
-    if (inr && !longrow) {
-      for (int e = a; e < b; e++) {
-        const int u = ci[e];
-        p += order_after(rnd[u], u, rv, v) ? 1 : 0;
+  if (per_wave) {
+    const int wave = (blockIdx.x * blockDim.x + threadIdx.x) / MCE_WAVE;
+    for (int i = wave; i < cnt; i += gsize / MCE_WAVE) {
+      const int v = roots ? roots[i] : i;
+      if (v < 0 || v >= n) {   // caller-supplied root out of range: flag it, touch nothing
+        if (lane == 0) {
+          lim |= 2u;
+          pcount[i] = 0;
+          xcount[i] = 0;
+          if (fwd) fwd[i] = 0;
+        }
+        continue;
       }
-    }
-    for (u64 lm = ballot(longrow); lm; lm &= lm - 1ull) {
-      const int t = __builtin_ctzll(lm);
-      const int ta = read_lane(a, t), tb = read_lane(b, t), tv = read_lane(v, t), tr = read_lane(rv, t);
+      const int a = rp[v], b = rp[v + 1], rv = rnd[v];
       u32 c = 0;
-      for (int e = ta + lane; e < tb; e += MCE_WAVE) {
+      for (int e = a + lane; e < b; e += MCE_WAVE) {
         const int u = ci[e];
-        c += order_after(rnd[u], u, tr, tv) ? 1u : 0u;
+        c += order_after(rnd[u], u, rv, v) ? 1u : 0u;
       }
-      c = wave_sum_u32(c);
-      if (lane == t) p = (int)c;
-    }
-    if (inr) {
-      x = (b - a) - p;
-      pcount[i] = p;
-      xcount[i] = x;
-      if (fwd) fwd[i] = (u64)p;
-      if (b == a) {
-        iso++;
-        iso_hash += mce_clique_term(mce_vertex_term(v), 1);
+      const int p = (int)wave_sum_u32(c), x = (b - a) - p;
+      if (lane == 0) {
+        pcount[i] = p;
+        xcount[i] = x;
+        if (fwd) fwd[i] = (u64)p;
+        if (b == a) {
+          iso++;
+          iso_hash += mce_clique_term(mce_vertex_term(v), 1);
+        }
+        pmax = max(pmax, p);
+        xmax = max(xmax, x);
+        dmax = max(dmax, b - a);
+        if (tally && p > MCE_MAX_P) lim |= 1u;
       }
-      pmax = max(pmax, p);
-      xmax = max(xmax, x);
-      dmax = max(dmax, b - a);
-      if (tally && p > MCE_MAX_P) lim |= 1u;
-      valid = p > 0 && p <= MCE_MAX_P;
-    } else if (i < cnt && fwd) {
-      fwd[i] = 0;
+    }   // the tallies follow in k_tally (64 roots at a time: one root each would
+        // cost a score of same-address atomics)
+  } else {
+    for (int base = blockIdx.x * blockDim.x; base < cnt; base += gsize) {
+      const int i = base + threadIdx.x;
+      int p = 0, x = 0;
+      bool valid = false;
+      const int v = i < cnt ? (roots ? roots[i] : i) : 0;
+      if (i < cnt && (v < 0 || v >= n)) {   // caller-supplied root out of range: flag it, touch nothing
+        lim |= 2u;
+        pcount[i] = 0;
+        xcount[i] = 0;
+      }
+      // later neighbours: one thread per short row; the whole wavefront takes each
+      // long row in turn (a hub row would keep one thread busy for its whole length)
+      const bool inr = i < cnt && v >= 0 && v < n;
+      int a = 0, b = 0, rv = 0;
+      if (inr) {
+        a = rp[v];
+        b = rp[v + 1];
+        rv = rnd[v];
+      }
+      const bool longrow = inr && b - a > ORIENT_LONG;
+      if (inr && !longrow) {
+        for (int e = a; e < b; e++) {
+          const int u = ci[e];
+          p += order_after(rnd[u], u, rv, v) ? 1 : 0;
+        }
+      }
+      for (u64 lm = ballot(longrow); lm; lm &= lm - 1ull) {
+        const int t = __builtin_ctzll(lm);
+        const int ta = read_lane(a, t), tb = read_lane(b, t), tv = read_lane(v, t), tr = read_lane(rv, t);
+        u32 c = 0;
+        for (int e = ta + lane; e < tb; e += MCE_WAVE) {
+          const int u = ci[e];
+          c += order_after(rnd[u], u, tr, tv) ? 1u : 0u;
+        }
+        c = wave_sum_u32(c);
+        if (lane == t) p = (int)c;
+      }
+      if (inr) {
+        x = (b - a) - p;
+        pcount[i] = p;
+        xcount[i] = x;
+        if (fwd) fwd[i] = (u64)p;
+        if (b == a) {
+          iso++;
+          iso_hash += mce_clique_term(mce_vertex_term(v), 1);
+        }
+        pmax = max(pmax, p);
+        xmax = max(xmax, x);
+        dmax = max(dmax, b - a);
+        if (tally && p > MCE_MAX_P) lim |= 1u;
+        valid = p > 0 && p <= MCE_MAX_P;
+      } else if (i < cnt && fwd) {
+        fwd[i] = 0;
+      }
+      if (tally) tally_roots(ctl, valid, p, x);
     }
-    if (tally) tally_roots(ctl, valid, p, x);
   }
   const u64 wiso = wave_sum_u64(iso);
   const u64 whash = wave_sum_u64(iso_hash);
@@ -1134,6 +1177,19 @@ __global__ __launch_bounds__(256) void k_orient(int n, const int* __restrict__ r
     atomicMax(&ctl->max_degree, (int)wdm);
     if (wl & 1u) atomicOr(&ctl->status, MCE_E_LIMIT);
     if (wl & 2u) atomicOr(&ctl->status, MCE_E_ROOTS);
+  }
+}
+
+// The sub-class tallies of the roots that k_orient counted one wavefront per
+// root: one thread per root, grouped per wavefront as in k_orient.
+__global__ __launch_bounds__(256) void k_tally(int nroots, const int* __restrict__ pcount,
+                                                const int* __restrict__ xcount, MceCtl* ctl) {
+  if (ld_relaxed(&ctl->status) != 0) return;
+  const int gsize = gridDim.x * blockDim.x;
+  for (int base = blockIdx.x * blockDim.x; base < nroots; base += gsize) {
+    const int i = base + threadIdx.x;
+    const int p = i < nroots ? pcount[i] : 0, x = i < nroots ? xcount[i] : 0;
+    tally_roots(ctl, p > 0 && p <= MCE_MAX_P, p, x);
   }
 }
 
@@ -1417,9 +1473,17 @@ hipError_t mce_launch_l2_roots(int n, long long nnz, const int* rp, const int* c
 
 hipError_t mce_launch_orient(int n, const int* rp, const int* ci, const int* rnd, const int* roots, int nroots,
                              int* pcount, int* xcount, MceCtl* ctl, u64* fwd, int blocks, hipStream_t s) {
-  const int nb = max(1, min(blocks, (nroots + 255) / 256));
+  // at most one root per wavefront of the grid: a wavefront per root, on at most
+  // 256 wavefronts (every wavefront ends with a few atomics on the same words:
+  // thousands of them cost more than walking several rows each)
+  const int per_wave = nroots <= 4 * blocks ? 1 : 0;
+  const int nb = per_wave ? max(1, min(64, (nroots + 3) / 4)) : max(1, min(blocks, (nroots + 255) / 256));
   hipLaunchKernelGGL(k_orient, dim3(nb), dim3(256), 0, s, n, rp, ci, rnd, roots, nroots, pcount, xcount, ctl, fwd,
-                     fwd ? 0 : 1);
+                     fwd ? 0 : 1, per_wave);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || !per_wave || fwd) return e;
+  hipLaunchKernelGGL(k_tally, dim3(max(1, min(blocks, (nroots + 255) / 256))), dim3(256), 0, s, nroots, pcount,
+                     xcount, ctl);
   return hipGetLastError();
 }
 

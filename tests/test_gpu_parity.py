@@ -284,8 +284,8 @@ def _drop_edge(rp, ci, u, w):
 def test_asymmetry_on_either_side(eng):
     """Symmetry is searched only for edges stored at the endpoint later in
     (degree, id) order, and completed by counting: a missing reverse must be
-    found whichever endpoint stores the surviving edge, also in rows longer than
-    2048 edges (checked in pieces by a second pass)."""
+    found whichever endpoint stores the surviving edge, also in a hub row of
+    thousands of edges (whose entries several wavefronts share)."""
     g = mi.hub_clique(300, 4, 3000, 0.7, 12, 7)
     rp, ci = g.row_ptr, g.col_idx
     deg = np.diff(rp)
@@ -298,6 +298,27 @@ def test_asymmetry_on_either_side(eng):
         rp2, ci2 = _drop_edge(rp, ci, u, w)
         assert _bad(eng, g.n, rp2, ci2) == mce.MCE_GRAPH_ASYM, (u, w)
     check(eng, g)
+
+
+@pytest.mark.parametrize("n, m, seed", [(100000, 400, 1), (70001, 2500, 2)])
+def test_long_runs_of_empty_rows(eng, n, m, seed):
+    """Entries are checked in 64-entry tiles whose rows are found among the next
+    64 row ends; between two edges lie hundreds of empty rows here, so a tile's
+    rows are found over many such loads. The graph's cliques match the oracle
+    (every isolated vertex is a maximal clique of one), and a missing reverse
+    edge anywhere is still found."""
+    rng = np.random.default_rng(seed)
+    u = rng.integers(0, n, m)
+    v = rng.integers(0, n, m)
+    g = mi.from_edges(n, u, v, f"sparse{n}")
+    check(eng, g)
+    rp, ci = g.row_ptr, g.col_idx
+    pairs = g.edge_list()
+    for k in (0, len(pairs) // 2, len(pairs) - 1):
+        x, y = map(int, pairs[k])
+        for s, t in ((x, y), (y, x)):
+            rp2, ci2 = _drop_edge(rp, ci, s, t)
+            assert _bad(eng, g.n, rp2, ci2) == mce.MCE_GRAPH_ASYM, (s, t)
 
 
 def test_bad_roots_and_empty_graph(eng):
