@@ -1050,6 +1050,7 @@ __device__ void tally_roots(MceCtl* ctl, bool valid, int p, int x) {
 }
 
 #define ORIENT_LONG 128   // rows longer than this are counted by the whole wavefront
+#define ORIENT_MUL 2654435761u   // a prime above every int32 root count
 
 // Later (|P|) and earlier (|X|) neighbours of every root. With many roots one
 // thread takes each root (a wavefront takes each long row in turn); with at most
@@ -1060,7 +1061,7 @@ __device__ void tally_roots(MceCtl* ctl, bool valid, int p, int x) {
 __global__ __launch_bounds__(256) void k_orient(int n, const int* __restrict__ rp, const int* __restrict__ ci,
                                                  const int* __restrict__ rnd, const int* __restrict__ roots,
                                                  int nroots, int* pcount, int* xcount, MceCtl* ctl, u64* fwd,
-                                                 int tally, int per_wave) {
+                                                 int tally, int per_wave, u32 mul) {
   if (ld_relaxed(&ctl->status) != 0) return;
   const int lane = lane_id();
   const int gsize = gridDim.x * blockDim.x;
@@ -1105,7 +1106,11 @@ __global__ __launch_bounds__(256) void k_orient(int n, const int* __restrict__ r
         // cost a score of same-address atomics)
   } else {
     for (int base = blockIdx.x * blockDim.x; base < cnt; base += gsize) {
-      const int i = base + threadIdx.x;
+      // thread tid takes root tid * mul mod cnt (mul a prime above cnt: a
+      // permutation), so that roots of neighbouring ids, such as the hubs of
+      // a graph whose degrees fall with the id, fall to different wavefronts
+      const int tid = base + threadIdx.x;
+      const int i = tid < cnt ? (int)((u64)tid * mul % (u64)cnt) : tid;
       int p = 0, x = 0;
       bool valid = false;
       const int v = i < cnt ? (roots ? roots[i] : i) : 0;
@@ -1479,7 +1484,7 @@ hipError_t mce_launch_orient(int n, const int* rp, const int* ci, const int* rnd
   const int per_wave = nroots <= 4 * blocks ? 1 : 0;
   const int nb = per_wave ? max(1, min(64, (nroots + 3) / 4)) : max(1, min(blocks, (nroots + 255) / 256));
   hipLaunchKernelGGL(k_orient, dim3(nb), dim3(256), 0, s, n, rp, ci, rnd, roots, nroots, pcount, xcount, ctl, fwd,
-                     fwd ? 0 : 1, per_wave);
+                     fwd ? 0 : 1, per_wave, ORIENT_MUL);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || !per_wave || fwd) return e;
   hipLaunchKernelGGL(k_tally, dim3(max(1, min(blocks, (nroots + 255) / 256))), dim3(256), 0, s, nroots, pcount,
