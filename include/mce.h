@@ -3,9 +3,10 @@
  *
  * The engine computes every maximal clique of a simple undirected graph exactly
  * ("Parallelizing Maximal Clique Enumeration on GPUs", arxiv 2212.01473v2,
- * section 2.1: a maximal clique is a clique that is not contained in a larger
- * one; section 4.1: the timed work is the clique count plus the degeneracy
- * ordering). It returns three results instead of listing cliques:
+ * section 2.1 states the problem; section 4.1 times the clique count together
+ * with the degeneracy ordering). A clique C is maximal when no vertex outside C
+ * is adjacent to every member of C. It returns three results instead of listing
+ * cliques:
  *   - count: the number of maximal cliques (64-bit; section 4, Table 1 has graphs
  *     with more than 2^32 of them);
  *   - hist[k]: the number of maximal cliques with k vertices;
@@ -48,7 +49,9 @@ typedef enum {
   MCE_ERR_NOMEM = -3,    /* device or host allocation failed */
   MCE_ERR_DEVICE = -4,   /* a HIP runtime call failed */
   MCE_ERR_STATE = -5,    /* call out of order, e.g. mce_result before any run */
-  MCE_ERR_TIMEOUT = -6,  /* the run passed mce_config.timeout_ms and was abandoned */
+  MCE_ERR_TIMEOUT = -6,  /* the run passed mce_config.timeout_ms and was abandoned; if the search
+                            had started, the cliques found before the limit are kept (see
+                            mce_result and mce_graph_facts.complete) */
   MCE_ERR_LIMIT = -7     /* the graph exceeds a limit of this build (degeneracy > 2048) */
 } mce_status;
 
@@ -122,6 +125,12 @@ typedef struct {
   uint32_t graph_errors;  /* MCE_GRAPH_* bits when the last run returned MCE_ERR_GRAPH */
   int32_t subgraph;       /* MCE_SUBGRAPH_PARTIAL or _FULL: the encoding used; 0 before the search */
   int32_t level;          /* 1: first-level subtrees (roots = vertices); 2: second-level (roots = edges) */
+  int32_t complete;       /* 1: the results cover every subtree; 0: the search stopped at the time
+                             limit (mce_run returned MCE_ERR_TIMEOUT) and they cover the cliques
+                             found before it */
+  int64_t roots_started;  /* subtree roots that were handed out: all of `roots` for a complete run;
+                             after a stop, those taken by then (each finished, or abandoned at the
+                             stop), plus the roots that need no search */
 } mce_graph_facts;
 
 /* Counters of the last run, summed over wavefronts. */
@@ -157,7 +166,8 @@ typedef struct {
                                 for the width-1 kernel */
   uint64_t max_stack_frames; /* micro kernel: most frames one wavefront's stack held */
   int32_t micro_roots;       /* first-level subtrees searched by the micro kernel */
-  int32_t pad2_;
+  int32_t micro_stack_cap;   /* frames per wavefront of the micro kernel's stack in device memory
+                                (4096) */
   uint64_t steps;            /* micro kernel: wavefront steps (each lane holding a frame takes one
                                 node or branch) */
   uint64_t lane_steps;       /* micro kernel: lanes holding a frame, summed over steps */
@@ -168,6 +178,8 @@ typedef struct {
   int32_t launch_roots[16];  /* subtrees of the launch */
   float launch_build_ms[16]; /* its induced-subgraph build, with MCE_FLAG_PHASE_TIMES */
   float launch_search_ms[16];/* its search, with MCE_FLAG_PHASE_TIMES or MCE_FLAG_SEARCH_TIMES */
+  uint64_t launch_words[16]; /* per search launch: 64-bit words of the induced-subgraph tables its
+                                build wrote */
   uint64_t act_cycles[7];    /* with MCE_FLAG_COUNTERS: search-kernel shader-clock cycles summed over
                                 wavefronts, by activity (section 4.5 and Figure 5 break execution
                                 time down the same way): [0] worker-list operations (taking subtrees,
@@ -210,10 +222,15 @@ mce_status mce_run_roots(mce_engine* e, int32_t n, int64_t nnz, const int32_t* r
                          const int32_t* col_idx, const int32_t* roots, int32_t nroots,
                          void* stream);
 
-/* Results of the last successful run, on the host. hist (nullable) receives
+/* Results of the last run, on the host. hist (nullable) receives
    hist[0..hist_len); hist_len = largest clique size + 1, or 0 if count == 0.
    If hist is non-NULL and hist_cap < hist_len the call returns MCE_ERR_ARG and
-   still sets *hist_len. count, hash and hist_len may be NULL. */
+   still sets *hist_len. count, hash and hist_len may be NULL. After a run whose
+   search stopped at the time limit the outputs are filled with the partial sums
+   (the maximal cliques found before the stop; each is a maximal clique of the
+   graph, but some are missing) and the call returns MCE_ERR_TIMEOUT.
+   MCE_ERR_STATE if the last run produced no results (an error before the
+   search, or no run yet). */
 mce_status mce_result(const mce_engine* e, uint64_t* count, uint64_t* hash, uint64_t* hist,
                       int32_t hist_cap, int32_t* hist_len);
 
@@ -246,6 +263,14 @@ typedef struct {
   uint64_t nodes;           /* search-tree nodes it expanded */
   uint64_t donations;       /* branch batches it handed over */
   uint64_t received;        /* branch batches it received */
+  uint64_t hw_location;     /* where it ran: XCC_ID << 32 | HW_ID as the hardware registers read
+                               (HW_ID bits 11:8 compute unit, bit 12 shader array, 15:13 shader
+                               engine); (XCC_ID, HW_ID bits 15:8) names one compute unit, the
+                               unit of section 4.3's per-SM load */
+  uint64_t leaves;          /* maximal cliques it found */
+  uint64_t pivot_words;     /* with MCE_FLAG_COUNTERS: 64-bit words ANDed and counted for pivots */
+  uint64_t branches;        /* with MCE_FLAG_COUNTERS: branches taken (mce_run_stats.branches) */
+  uint64_t xx_tests;        /* with MCE_FLAG_COUNTERS: X_X entries tested */
 } mce_worker_record;
 
 /* Copies up to cap records of the last run's wavefronts into out (host memory)

@@ -10,8 +10,10 @@ If the library has not been built, importing still works but every call raises
 """
 from __future__ import annotations
 
+import atexit
 import ctypes
 import os
+import weakref
 from dataclasses import dataclass, field
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -54,7 +56,8 @@ class mce_graph_facts(ctypes.Structure):
                 ("degeneracy", ctypes.c_int32), ("rounds", ctypes.c_int32),
                 ("max_p", ctypes.c_int32), ("max_x", ctypes.c_int32),
                 ("isolated", ctypes.c_int64), ("roots", ctypes.c_int64),
-                ("graph_errors", ctypes.c_uint32), ("subgraph", ctypes.c_int32), ("level", ctypes.c_int32)]
+                ("graph_errors", ctypes.c_uint32), ("subgraph", ctypes.c_int32), ("level", ctypes.c_int32),
+                ("complete", ctypes.c_int32), ("roots_started", ctypes.c_int64)]
 
 
 class mce_worker_record(ctypes.Structure):
@@ -62,7 +65,10 @@ class mce_worker_record(ctypes.Structure):
                 ("start_tick", ctypes.c_uint64), ("first_tick", ctypes.c_uint64),
                 ("last_tick", ctypes.c_uint64), ("end_tick", ctypes.c_uint64),
                 ("busy_ticks", ctypes.c_uint64), ("nodes", ctypes.c_uint64),
-                ("donations", ctypes.c_uint64), ("received", ctypes.c_uint64)]
+                ("donations", ctypes.c_uint64), ("received", ctypes.c_uint64),
+                ("hw_location", ctypes.c_uint64), ("leaves", ctypes.c_uint64),
+                ("pivot_words", ctypes.c_uint64), ("branches", ctypes.c_uint64),
+                ("xx_tests", ctypes.c_uint64)]
 
 
 class mce_run_stats(ctypes.Structure):
@@ -83,7 +89,7 @@ class mce_run_stats(ctypes.Structure):
                 ("branches", ctypes.c_uint64),
                 ("max_stack_frames", ctypes.c_uint64),
                 ("micro_roots", ctypes.c_int32),
-                ("pad2_", ctypes.c_int32),
+                ("micro_stack_cap", ctypes.c_int32),
                 ("steps", ctypes.c_uint64),
                 ("lane_steps", ctypes.c_uint64),
                 ("peel_ticks", ctypes.c_uint64 * 4),
@@ -91,6 +97,7 @@ class mce_run_stats(ctypes.Structure):
                 ("launch_roots", ctypes.c_int32 * 16),
                 ("launch_build_ms", ctypes.c_float * 16),
                 ("launch_search_ms", ctypes.c_float * 16),
+                ("launch_words", ctypes.c_uint64 * 16),
                 ("act_cycles", ctypes.c_uint64 * 7)]
 
 # Activities of mce_run_stats.act_cycles, in order.
@@ -198,9 +205,25 @@ class Result:
     count: int
     hash: int
     hist: list = field(default_factory=list)
+    complete: bool = True   # False: the search stopped at the time limit and these are partial sums
 
     def key(self):
         return (self.count, self.hash, tuple(self.hist))
+
+
+# Engines still open when the interpreter exits are destroyed here, while the
+# HIP runtime (and a profiler attached to it) is still up: device memory freed
+# from a finaliser that runs after the runtime's own teardown can crash the exit.
+_live = weakref.WeakSet()
+
+
+@atexit.register
+def _close_all():
+    for e in list(_live):
+        try:
+            e.close()
+        except Exception:
+            pass
 
 
 def _ptr(t):
@@ -241,6 +264,7 @@ class Engine:
         with torch.cuda.device(device):
             self._check(mce_create(cfg, h), "mce_create", None)
         self._h = h
+        _live.add(self)
 
     def _check(self, status, what, handle):
         if status != MCE_OK:
@@ -271,9 +295,11 @@ class Engine:
             if t.dtype != torch.int32 or not t.is_cuda or not t.is_contiguous():
                 raise ValueError(f"{name} must be a contiguous int32 CUDA tensor")
 
-    def run(self, row_ptr, col_idx, roots=None, stream=None) -> Result:
+    def run(self, row_ptr, col_idx, roots=None, stream=None, partial_ok: bool = False) -> Result:
         """Enumerate all maximal cliques (or those of the first-level subtrees of
-        `roots`). Returns (count, hash, hist)."""
+        `roots`). Returns (count, hash, hist). With partial_ok, a search stopped at
+        the time limit returns the cliques found before it (complete=False)
+        instead of raising."""
         import torch
         self._check_csr(row_ptr, col_idx)
         n = row_ptr.numel() - 1
@@ -287,19 +313,24 @@ class Engine:
             if roots.dtype != torch.int32 or not roots.is_cuda or not roots.is_contiguous():
                 raise ValueError("roots must be a contiguous int32 CUDA tensor")
             st = mce_run_roots(self._h, n, nnz, _ptr(row_ptr), _ptr(col_idx), _ptr(roots), roots.numel(), sp)
-        self._check(st, "mce_run", self._h)
+        if not (partial_ok and st == MCE_ERR_TIMEOUT and self.graph_info()["roots_started"] > 0):
+            self._check(st, "mce_run", self._h)
         return self.result()
 
     def result(self) -> Result:
+        """Results of the last run; complete=False after a search stopped at the time limit."""
         cnt = ctypes.c_uint64()
         hsh = ctypes.c_uint64()
         hl = ctypes.c_int32()
-        self._check(mce_result(self._h, ctypes.byref(cnt), ctypes.byref(hsh), None, 0, ctypes.byref(hl)),
-                    "mce_result", self._h)
+        st = mce_result(self._h, ctypes.byref(cnt), ctypes.byref(hsh), None, 0, ctypes.byref(hl))
+        if st != MCE_ERR_TIMEOUT:
+            self._check(st, "mce_result", self._h)
         cap = max(hl.value, 1)
         buf = (ctypes.c_uint64 * cap)()
-        self._check(mce_result(self._h, None, None, buf, cap, ctypes.byref(hl)), "mce_result", self._h)
-        return Result(int(cnt.value), int(hsh.value), [int(buf[i]) for i in range(hl.value)])
+        st2 = mce_result(self._h, None, None, buf, cap, ctypes.byref(hl))
+        if st2 != MCE_ERR_TIMEOUT:
+            self._check(st2, "mce_result", self._h)
+        return Result(int(cnt.value), int(hsh.value), [int(buf[i]) for i in range(hl.value)], st == MCE_OK)
 
     def graph_info(self) -> dict:
         info = mce_graph_facts()
@@ -329,8 +360,9 @@ class Engine:
         st = mce_run_stats()
         st.struct_size = ctypes.sizeof(mce_run_stats)
         self._check(mce_stats(self._h, st), "mce_stats", self._h)
-        out = {name: getattr(st, name) for name, _ in mce_run_stats._fields_ if name not in ("pad_", "pad2_")}
-        for key in ("peel_ticks", "launch_sub", "launch_roots", "launch_build_ms", "launch_search_ms"):
+        out = {name: getattr(st, name) for name, _ in mce_run_stats._fields_ if name != "pad_"}
+        for key in ("peel_ticks", "launch_sub", "launch_roots", "launch_build_ms", "launch_search_ms",
+                    "launch_words"):
             out[key] = list(out[key])[: (4 if key == "peel_ticks" else out["launches"])]
         out["act_cycles"] = dict(zip(ACTIVITIES, list(out["act_cycles"])))
         return out

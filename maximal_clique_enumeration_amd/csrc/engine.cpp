@@ -8,11 +8,11 @@
 
 #include <algorithm>
 #include <chrono>
+#include <cstdarg>
 #include <cstdio>
 #include <cstring>
-#include <map>
+#include <mutex>
 #include <new>
-#include <string>
 #include <vector>
 
 #include "../../include/mce.h"
@@ -30,6 +30,30 @@ struct HostPinned {
   size_t bytes = 0;
 };
 
+// Every device buffer of a run. An engine has two sets: its own, grown with
+// hipMalloc and kept until mce_destroy, and one carved out of the device's
+// static scratch array by mce_run_static.
+struct Bufs {
+  DevBuf ctl, deg, rnd, core, alive0, alive1, front0, front1, bfront0, bfront1, pcount, xcount, lists, taboff, scan,
+      heap, wl, slots, stats, mstack, mail;
+  DevBuf src, fwd, fwdtmp, eroots, pcount2, xcount2;   // second-level subtrees
+  DevBuf hub_id, hub_v, hub_bm;                       // their hub adjacency bitmaps
+};
+
+constexpr size_t kHistWords = MCE_MAX_P + 3;   // global histogram entries (sizes up to 2 + MCE_MAX_P)
+// control block, then the result words (hash, histogram): one clear, one read-back
+constexpr size_t kIoBytes = sizeof(MceCtl) + (1 + kHistWords) * sizeof(u64);
+static_assert(sizeof(MceCtl) % sizeof(u64) == 0, "results follow the control block");
+constexpr int kOccSlots = 64;   // cached occupancy answers per engine
+
+// Bump allocation over the static scratch (mce_run_static): buffers are laid
+// out afresh by every run, 256-byte aligned.
+struct Arena {
+  char* base = nullptr;   // nullptr: the engine's own hipMalloc'd buffers
+  size_t cap = 0, used = 0, need = 0;
+  bool short_of_space = false;
+};
+
 }  // namespace
 
 struct mce_engine {
@@ -38,50 +62,63 @@ struct mce_engine {
   int num_cu = 0;
   double tick_hz = 100e6;
   int peel_blocks_max = 1;
-  std::string err;
+  char err[512] = {0};
 
-  DevBuf ctl, deg, rnd, core, alive0, alive1, front0, front1, bfront0, bfront1, pcount, xcount, lists, taboff, scan, heap, wl,
-      slots, stats, mstack, mail;
-  DevBuf src, fwd, fwdtmp, eroots, pcount2, xcount2;   // second-level subtrees
-  DevBuf hub_id, hub_v, hub_bm;                       // their hub adjacency bitmaps
-  HostPinned host;    // staging for device -> host copies
+  Bufs own;           // grown with hipMalloc, freed by mce_destroy
+  Bufs carved;        // the static scratch, laid out by the last mce_run_static
+  Bufs* last = &own;  // the set the last run used (mce_ordering, mce_stats)
+  HostPinned host;    // staging for device -> host copies (mce_run, mce_run_roots)
+  alignas(64) unsigned char host_io[kIoBytes];   // the same for mce_run_static (pageable)
   hipEvent_t ev[4 + 4 * MCE_NSUB] = {};
   bool have_events = false;
 
   // last run
   bool have_result = false;
+  bool complete = false;      // false: the search stopped at the time limit; the results are partial
   bool have_order = false;
   int32_t last_n = 0;
   uint64_t count = 0, hash = 0;
-  std::vector<uint64_t> hist;
+  uint64_t hist[kHistWords] = {};
+  int32_t hist_len = 0;
   mce_graph_facts info{};
   mce_run_stats stats_out{};
-  std::vector<mce_worker_record> trace;
+  std::vector<mce_worker_record> trace;   // filled on demand by mce_stats / mce_worker_trace
 
   // per-wave counters of the last run stay on the device until mce_stats or
   // mce_worker_trace asks for them (they are diagnostics, not results)
   struct LaunchInfo {
     int sub, nw, roots;
   };
-  std::vector<LaunchInfo> last_plan;
+  LaunchInfo last_plan[MCE_NSUB] = {};
+  int n_last_plan = 0;
   int last_stat_rows = 0;
   bool stats_pending = false;
   bool last_timing = false;
   bool last_stimes = false;   // the search launches carry events (MCE_FLAG_SEARCH_TIMES or _PHASE_TIMES)
   // resident-wave counts per kernel variant (occupancy queries cost ~0.1 ms each)
-  std::map<std::pair<int, long long>, int> occupancy;
+  struct Occ {
+    int a;
+    long long b;
+    int v;
+  };
+  Occ occ[kOccSlots] = {};
+  int n_occ = 0;
 };
 
 namespace {
 
-mce_status fail(mce_engine* e, mce_status s, const std::string& msg) {
-  if (e) e->err = msg;
+mce_status fail(mce_engine* e, mce_status s, const char* fmt, ...) {
+  if (e) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(e->err, sizeof(e->err), fmt, ap);
+    va_end(ap);
+  }
   return s;
 }
 
 mce_status hip_fail(mce_engine* e, hipError_t h, const char* what) {
-  std::string m = std::string(what) + ": " + hipGetErrorString(h);
-  return fail(e, h == hipErrorOutOfMemory ? MCE_ERR_NOMEM : MCE_ERR_DEVICE, m);
+  return fail(e, h == hipErrorOutOfMemory ? MCE_ERR_NOMEM : MCE_ERR_DEVICE, "%s: %s", what, hipGetErrorString(h));
 }
 
 hipError_t ensure(DevBuf& b, size_t bytes) {
@@ -93,6 +130,32 @@ hipError_t ensure(DevBuf& b, size_t bytes) {
   hipError_t h = hipMalloc(&b.p, bytes);
   if (h == hipSuccess) b.bytes = bytes;
   return h;
+}
+
+// A buffer of the run: the engine's own (grown with hipMalloc) or, with an
+// arena, the next piece of the static scratch (no allocation call).
+hipError_t take(Arena& a, DevBuf& b, size_t bytes) {
+  if (!a.base) return ensure(b, bytes);
+  if (bytes == 0) bytes = 1;
+  const size_t off = (a.used + 255) & ~(size_t)255;
+  if (off + bytes > a.cap) {
+    a.short_of_space = true;
+    a.need = std::max(a.need, off + bytes);
+    return hipErrorOutOfMemory;
+  }
+  b.p = a.base + off;
+  b.bytes = bytes;
+  a.used = off + bytes;
+  return hipSuccess;
+}
+
+// An allocation failure: with the static scratch it means the run does not fit
+// (MCE_ERR_LIMIT, with the bytes it needed at least); else the device's.
+mce_status alloc_fail(mce_engine* e, const Arena& a, hipError_t h, const char* what) {
+  if (a.base && a.short_of_space)
+    return fail(e, MCE_ERR_LIMIT, "%s: the static scratch holds %zu bytes; this run needs more than %zu", what,
+                a.cap, a.need);
+  return hip_fail(e, h, what);
 }
 
 hipError_t ensure_host(HostPinned& b, size_t bytes) {
@@ -120,24 +183,38 @@ double ms_since(std::chrono::steady_clock::time_point t0) {
   return std::chrono::duration<double, std::milli>(std::chrono::steady_clock::now() - t0).count();
 }
 
-constexpr size_t kHistWords = MCE_MAX_P + 3;   // global histogram entries (sizes up to 2 + MCE_MAX_P)
-// control block, then the result words (hash, histogram): one clear, one read-back
-constexpr size_t kIoBytes = sizeof(MceCtl) + (1 + kHistWords) * sizeof(u64);
-static_assert(sizeof(MceCtl) % sizeof(u64) == 0, "results follow the control block");
+// Occupancy answer for a kernel variant, cached per engine (fixed table: the
+// run path allocates nothing on the host either).
+template <class F>
+int occupancy(mce_engine* e, int a, long long b, F query) {
+  for (int i = 0; i < e->n_occ; i++)
+    if (e->occ[i].a == a && e->occ[i].b == b) return e->occ[i].v;
+  const int v = query();
+  if (e->n_occ < kOccSlots) e->occ[e->n_occ++] = {a, b, v};
+  return v;
+}
+
 constexpr int kMaxHubs = 1024;                 // second-level orientation: hub adjacency bitmaps, at most
 constexpr size_t kHubBytes = 256ull << 20;     // this many, in at most this many bytes
 constexpr int kMicroStack = 4096;              // frames per wavefront stack of the micro search
+constexpr int kMicroStackMinStatic = 256;      // the smallest stack mce_run_static gives a micro wave
 constexpr int kMicroCoopRootsPerWave = 4;     // micro launches with this many roots per wave share pivot scans
 // Tables other than micro ones are built by the split build: a root's rows are
 // dealt over several blocks, about this many (root, part) blocks per CU.
 constexpr int kSplitBlocksPerCu = 16;
 
+// One run. `arena` empty: the engine's own buffers (grown with hipMalloc);
+// else every buffer is carved from the static scratch and nothing is allocated.
 mce_status run_impl(mce_engine* e, int32_t n, int64_t nnz, const int32_t* row_ptr, const int32_t* col_idx,
-                    const int32_t* roots, int32_t nroots, bool subset, void* stream) {
+                    const int32_t* roots, int32_t nroots, bool subset, void* stream, Arena& arena) {
   const auto t0 = std::chrono::steady_clock::now();
   if (!e) return MCE_ERR_ARG;
-  e->err.clear();
+  const bool stat = arena.base != nullptr;
+  Bufs& B = stat ? e->carved : e->own;
+  e->last = &B;
+  e->err[0] = 0;
   e->have_result = false;
+  e->complete = false;
   e->have_order = false;
   if (n < 0 || nnz < 0) return fail(e, MCE_ERR_ARG, "n and nnz must be >= 0");
   if (nnz >= 0x7FFFFFFFLL) return fail(e, MCE_ERR_ARG, "nnz must be < 2^31");
@@ -155,7 +232,7 @@ mce_status run_impl(mce_engine* e, int32_t n, int64_t nnz, const int32_t* row_pt
   std::memset(&e->stats_out, 0, sizeof(e->stats_out));
   e->stats_out.struct_size = sizeof(mce_run_stats);
   e->stats_out.tick_hz = e->tick_hz;
-  e->hist.clear();
+  e->hist_len = 0;
   e->count = e->hash = 0;
   e->last_n = n;
   const int cnt = subset ? nroots : n;
@@ -163,6 +240,8 @@ mce_status run_impl(mce_engine* e, int32_t n, int64_t nnz, const int32_t* row_pt
   if (n == 0) {
     if (subset && nroots > 0) return fail(e, MCE_ERR_ARG, "roots given for an empty graph");
     e->have_result = true;
+    e->complete = true;
+    e->info.complete = 1;
     e->stats_out.ms_total = ms_since(t0);
     return MCE_OK;
   }
@@ -173,44 +252,48 @@ mce_status run_impl(mce_engine* e, int32_t n, int64_t nnz, const int32_t* row_pt
   const u64 budget = (u64)((double)e->cfg.timeout_ms * 1e-3 * e->tick_hz);
 
   size_t nb = (size_t)n * sizeof(int);
-  if ((h = ensure(e->ctl, kIoBytes)) != hipSuccess || (h = ensure(e->deg, nb)) != hipSuccess ||
-      (h = ensure(e->rnd, nb)) != hipSuccess || (h = ensure(e->core, nb)) != hipSuccess ||
-      (h = ensure(e->alive0, nb)) != hipSuccess || (h = ensure(e->alive1, nb)) != hipSuccess ||
-      (h = ensure(e->front0, nb)) != hipSuccess || (h = ensure(e->front1, nb)) != hipSuccess ||
-      (h = ensure(e->bfront0, nb)) != hipSuccess || (h = ensure(e->bfront1, nb)) != hipSuccess ||
-      (h = ensure(e->pcount, (size_t)std::max(cnt, 1) * sizeof(int))) != hipSuccess ||
-      (h = ensure(e->xcount, (size_t)std::max(cnt, 1) * sizeof(int))) != hipSuccess ||
-      (h = ensure(e->lists, (size_t)std::max(cnt, 1) * sizeof(int))) != hipSuccess ||
-      (h = ensure(e->wl, sizeof(MceWl))) != hipSuccess ||
-      (h = ensure_host(e->host, kIoBytes)) != hipSuccess)
-    return hip_fail(e, h, "allocation");
+  if ((h = take(arena, B.ctl, kIoBytes)) != hipSuccess || (h = take(arena, B.deg, nb)) != hipSuccess ||
+      (h = take(arena, B.rnd, nb)) != hipSuccess || (h = take(arena, B.core, nb)) != hipSuccess ||
+      (h = take(arena, B.alive0, nb)) != hipSuccess || (h = take(arena, B.alive1, nb)) != hipSuccess ||
+      (h = take(arena, B.front0, nb)) != hipSuccess || (h = take(arena, B.front1, nb)) != hipSuccess ||
+      (h = take(arena, B.bfront0, nb)) != hipSuccess || (h = take(arena, B.bfront1, nb)) != hipSuccess ||
+      (h = take(arena, B.pcount, (size_t)std::max(cnt, 1) * sizeof(int))) != hipSuccess ||
+      (h = take(arena, B.xcount, (size_t)std::max(cnt, 1) * sizeof(int))) != hipSuccess ||
+      (h = take(arena, B.wl, sizeof(MceWl))) != hipSuccess)
+    return alloc_fail(e, arena, h, "allocation");
+  if (!stat && (h = ensure_host(e->host, kIoBytes)) != hipSuccess) return hip_fail(e, h, "allocation");
   // second-level subtrees (section 3.2): the roots are the vertex roots' forward edges
   const bool l2 = (e->cfg.flags & MCE_FLAG_L2) != 0;
   e->info.level = l2 ? 2 : 1;
   int maxhubs = 0;
   if (l2) {
     const size_t ne = (size_t)std::max<int64_t>(nnz, 1) * sizeof(int);
-    if ((h = ensure(e->src, ne)) != hipSuccess || (h = ensure(e->eroots, ne)) != hipSuccess ||
-        (h = ensure(e->pcount2, ne)) != hipSuccess || (h = ensure(e->xcount2, ne)) != hipSuccess ||
-        (h = ensure(e->fwd, (size_t)std::max(cnt, 1) * sizeof(u64))) != hipSuccess ||
-        (h = ensure(e->fwdtmp, (size_t)mce_scan_temp_words(std::max(cnt, 1)) * sizeof(u64))) != hipSuccess)
-      return hip_fail(e, h, "allocation");
+    if ((h = take(arena, B.src, ne)) != hipSuccess || (h = take(arena, B.eroots, ne)) != hipSuccess ||
+        (h = take(arena, B.pcount2, ne)) != hipSuccess || (h = take(arena, B.xcount2, ne)) != hipSuccess ||
+        (h = take(arena, B.fwd, (size_t)std::max(cnt, 1) * sizeof(u64))) != hipSuccess ||
+        (h = take(arena, B.fwdtmp, (size_t)mce_scan_temp_words(std::max(cnt, 1)) * sizeof(u64))) != hipSuccess)
+      return alloc_fail(e, arena, h, "allocation");
   }
   // hub adjacency bitmaps (second-level runs; first-level builds did not gain
-  // from them): n bits each, at most kMaxHubs within kHubBytes
-  if (l2) {
+  // from them): n bits each, at most kMaxHubs within kHubBytes. They only change
+  // the speed, and the static scratch has no room for them.
+  if (l2 && !stat) {
     const size_t hub_bytes = ((size_t)n + 63) / 64 * sizeof(u64);
     maxhubs = (int)std::min<size_t>(kMaxHubs, kHubBytes / std::max<size_t>(hub_bytes, 1));
     if (maxhubs > 0 &&
-        ((h = ensure(e->hub_id, (size_t)n * sizeof(int))) != hipSuccess ||
-         (h = ensure(e->hub_v, (size_t)maxhubs * sizeof(int))) != hipSuccess ||
-         (h = ensure(e->hub_bm, (size_t)maxhubs * hub_bytes)) != hipSuccess))
+        ((h = ensure(B.hub_id, (size_t)n * sizeof(int))) != hipSuccess ||
+         (h = ensure(B.hub_v, (size_t)maxhubs * sizeof(int))) != hipSuccess ||
+         (h = ensure(B.hub_bm, (size_t)maxhubs * hub_bytes)) != hipSuccess))
       return hip_fail(e, h, "allocation");
   }
+  // the root lists: one entry per vertex root, or per edge for second-level subtrees
+  const size_t lists_cap = l2 ? (size_t)std::max<int64_t>(nnz, 1) : (size_t)std::max(cnt, 1);
+  if ((h = take(arena, B.lists, lists_cap * sizeof(int))) != hipSuccess) return alloc_fail(e, arena, h, "allocation");
 
-  MceCtl* ctl = dp<MceCtl>(e->ctl);
-  u64* results = reinterpret_cast<u64*>(dp<char>(e->ctl) + sizeof(MceCtl));   // hash, then the histogram
-  if ((h = hipMemsetAsync(ctl, 0, kIoBytes, s)) != hipSuccess) return hip_fail(e, h, "memset");
+  MceCtl* ctl = dp<MceCtl>(B.ctl);
+  u64* results = reinterpret_cast<u64*>(dp<char>(B.ctl) + sizeof(MceCtl));   // hash, then the histogram
+  // cleared by a kernel (the static scratch keeps the last run's contents)
+  if ((h = mce_launch_zero(dp<u64>(B.ctl), kIoBytes / sizeof(u64), s)) != hipSuccess) return hip_fail(e, h, "clear");
 
   const int grid = std::max(1, e->num_cu * 8);
   if (timing) (void)hipEventRecord(e->ev[0], s);
@@ -223,24 +306,25 @@ mce_status run_impl(mce_engine* e, int32_t n, int64_t nnz, const int32_t* row_pt
   // block per two CUs (against one per CU: cheaper barriers and still ample
   // waves for a round; configurations 2-4 peel 3-5 % faster)
   int pblocks = n <= 16384 ? 1 : std::min(std::max(1, e->peel_blocks_max / 2), (n + 1023) / 1024);
-  if ((h = mce_launch_peel(n, row_ptr, col_idx, dp<int>(e->deg), dp<int>(e->rnd), dp<int>(e->core),
-                           dp<int>(e->alive0), dp<int>(e->alive1), dp<int>(e->front0), dp<int>(e->front1),
-                           dp<int>(e->bfront0), dp<int>(e->bfront1), ctl, budget, pblocks, s)) != hipSuccess)
+  if ((h = mce_launch_peel(n, row_ptr, col_idx, dp<int>(B.deg), dp<int>(B.rnd), dp<int>(B.core),
+                           dp<int>(B.alive0), dp<int>(B.alive1), dp<int>(B.front0), dp<int>(B.front1),
+                           dp<int>(B.bfront0), dp<int>(B.bfront1), ctl, budget, pblocks, s)) != hipSuccess)
     return hip_fail(e, h, "peel launch");
   if (timing) (void)hipEventRecord(e->ev[2], s);
-  if (maxhubs > 0 && (h = mce_launch_hubs(n, row_ptr, col_idx, dp<int>(e->hub_id), dp<int>(e->hub_v),
-                                         dp<u64>(e->hub_bm), maxhubs, ctl, grid, s)) != hipSuccess)
+  if (maxhubs > 0 && (h = mce_launch_hubs(n, row_ptr, col_idx, dp<int>(B.hub_id), dp<int>(B.hub_v),
+                                         dp<u64>(B.hub_bm), maxhubs, ctl, grid, s)) != hipSuccess)
     return hip_fail(e, h, "hub bitmaps launch");
-  if ((h = mce_launch_orient(n, row_ptr, col_idx, dp<int>(e->rnd), subset ? roots : nullptr, cnt,
-                             dp<int>(e->pcount), dp<int>(e->xcount), ctl, l2 ? dp<u64>(e->fwd) : nullptr, grid,
+  if ((h = mce_launch_orient(n, row_ptr, col_idx, dp<int>(B.rnd), subset ? roots : nullptr, cnt,
+                             dp<int>(B.pcount), dp<int>(B.xcount), ctl, l2 ? dp<u64>(B.fwd) : nullptr, grid,
                              s)) != hipSuccess)
     return hip_fail(e, h, "orient launch");
-  if (l2 && (h = mce_launch_l2_roots(n, nnz, row_ptr, col_idx, dp<int>(e->rnd), subset ? roots : nullptr, cnt,
-                                     dp<u64>(e->fwd), dp<u64>(e->fwdtmp), dp<int>(e->src), dp<int>(e->eroots),
-                                     dp<int>(e->pcount2), dp<int>(e->xcount2), dp<int>(e->hub_id),
-                                     dp<int>(e->hub_v), dp<u64>(e->hub_bm), maxhubs, ctl, grid, s)) != hipSuccess)
+  if (l2 && (h = mce_launch_l2_roots(n, nnz, row_ptr, col_idx, dp<int>(B.rnd), subset ? roots : nullptr, cnt,
+                                     dp<u64>(B.fwd), dp<u64>(B.fwdtmp), dp<int>(B.src), dp<int>(B.eroots),
+                                     dp<int>(B.pcount2), dp<int>(B.xcount2), dp<int>(B.hub_id),
+                                     dp<int>(B.hub_v), dp<u64>(B.hub_bm), maxhubs, ctl, grid, s)) != hipSuccess)
     return hip_fail(e, h, "second-level roots launch");
-  MceCtl* hctl = static_cast<MceCtl*>(e->host.p);
+  char* hio = stat ? reinterpret_cast<char*>(e->host_io) : static_cast<char*>(e->host.p);
+  MceCtl* hctl = reinterpret_cast<MceCtl*>(hio);
   if ((h = hipMemcpyAsync(hctl, ctl, sizeof(MceCtl), hipMemcpyDeviceToHost, s)) != hipSuccess)
     return hip_fail(e, h, "readback");
   if ((h = hipStreamSynchronize(s)) != hipSuccess) return hip_fail(e, h, "synchronize after orient");
@@ -264,12 +348,10 @@ mce_status run_impl(mce_engine* e, int32_t n, int64_t nnz, const int32_t* row_pt
                                      : "a first-level subtree has more than 2048 later neighbours");
   // the subtree roots the search takes: vertex roots, or their forward edges
   const int nsub = l2 ? hctl->l2_roots : cnt;
-  const int32_t* sroots = l2 ? dp<int>(e->eroots) : (subset ? roots : nullptr);
-  int* spc = l2 ? dp<int>(e->pcount2) : dp<int>(e->pcount);
-  int* sxc = l2 ? dp<int>(e->xcount2) : dp<int>(e->xcount);
+  const int32_t* sroots = l2 ? dp<int>(B.eroots) : (subset ? roots : nullptr);
+  int* spc = l2 ? dp<int>(B.pcount2) : dp<int>(B.pcount);
+  int* sxc = l2 ? dp<int>(B.xcount2) : dp<int>(B.xcount);
   e->info.roots = nsub;
-  if (l2 && (h = ensure(e->lists, (size_t)std::max(nsub, 1) * sizeof(int))) != hipSuccess)
-    return hip_fail(e, h, "allocation");
 
   // Induced-subgraph mode (section 3.4; section 4.5 picks partial when
   // Delta / d > 200, else full). Local row indices of the full subgraph must
@@ -307,8 +389,10 @@ mce_status run_impl(mce_engine* e, int32_t n, int64_t nnz, const int32_t* row_pt
     int sub, nw;
     SearchLayout L;
   };
-  std::vector<Plan> plan;
-  size_t slot_bytes = 0, mstack_bytes = 0, mail_bytes = 0;
+  Plan plan[MCE_NSUB];
+  int nplan = 0;
+  size_t slot_bytes = 0;
+  int micro_nw = 0;
   int stat_rows = 0;
   const bool counters = (e->cfg.flags & MCE_FLAG_COUNTERS) != 0;
   for (int c = MCE_NSUB - 1; c >= 0; c--) {
@@ -318,71 +402,82 @@ mce_status run_impl(mce_engine* e, int32_t n, int64_t nnz, const int32_t* row_pt
     int nw;
     if (c == MCE_SUB_MICRO) {
       // 8 wavefronts per CU: more add start-up spread and little throughput
-      const auto key = std::make_pair(-1 - (counters ? 1 : 0), 0LL);
-      auto it = e->occupancy.find(key);
-      if (it == e->occupancy.end()) it = e->occupancy.emplace(key, mce_micro_max_workers(counters, e->num_cu)).first;
-      nw = std::min(it->second, 8 * e->num_cu);
-      mstack_bytes = (size_t)std::max(nw, 1) * 6 * kMicroStack * sizeof(u64);
-      mail_bytes = (size_t)std::max(nw, 1) * mce_micro_mail_words() * sizeof(u64);
+      nw = occupancy(e, -1 - (counters ? 1 : 0), 0LL, [&] { return mce_micro_max_workers(counters, e->num_cu); });
+      nw = std::min(nw, 8 * e->num_cu);
     } else {
       pl.L = mce_search_layout(c, mode, hctl->sub_maxp[var][c], hctl->sub_maxx[var][c], hctl->sub_maxr[var][c],
                                hbm, counters);
-      const auto key = std::make_pair(((c * 2 + mode) * 2 + (counters ? 1 : 0)) * 2 + (pl.L.srows ? 1 : 0),
-                                      (long long)pl.L.lds_bytes * 2 + (pl.L.sstack ? 1 : 0));
-      auto it = e->occupancy.find(key);
-      if (it == e->occupancy.end()) it = e->occupancy.emplace(key, mce_search_max_workers(pl.L, e->num_cu)).first;
-      nw = it->second;
+      const SearchLayout& L = pl.L;
+      nw = occupancy(e, ((c * 2 + mode) * 2 + (counters ? 1 : 0)) * 2 + (L.srows ? 1 : 0),
+                     (long long)L.lds_bytes * 2 + (L.sstack ? 1 : 0),
+                     [&] { return mce_search_max_workers(L, e->num_cu); });
     }
     if (nw <= 0) return fail(e, MCE_ERR_DEVICE, "search kernel occupancy query failed");
     if (e->cfg.max_workers > 0) nw = std::min(nw, (int)e->cfg.max_workers);
     if (!e->cfg.worker_list) nw = std::min(nw, counts[c]);
     pl.nw = nw;
-    if (c != MCE_SUB_MICRO) slot_bytes = std::max(slot_bytes, pl.L.slot_bytes * (size_t)nw);
+    if (c == MCE_SUB_MICRO) micro_nw = nw;
+    else slot_bytes = std::max(slot_bytes, pl.L.slot_bytes * (size_t)nw);
     stat_rows += nw;
-    plan.push_back(pl);
+    plan[nplan++] = pl;
   }
+  // micro frame stacks: kMicroStack frames per wave; in the static scratch,
+  // the largest power of two that the space left holds, at least
+  // kMicroStackMinStatic (an overflow at run time is MCE_ERR_LIMIT)
+  int micro_cap = kMicroStack;
   if (total > 0) {
-    if ((h = ensure(e->taboff, (size_t)total * sizeof(u64))) != hipSuccess ||
-        (h = ensure(e->scan, (size_t)mce_scan_temp_words(total) * sizeof(u64))) != hipSuccess ||
-        (h = ensure(e->heap, heap_words * sizeof(u64))) != hipSuccess ||
-        (h = ensure(e->slots, slot_bytes)) != hipSuccess ||
-        (h = ensure(e->stats, (size_t)stat_rows * MCE_NSTAT * sizeof(u64))) != hipSuccess ||
-        (mstack_bytes && (h = ensure(e->mstack, mstack_bytes)) != hipSuccess) ||
-        (mail_bytes && (h = ensure(e->mail, mail_bytes)) != hipSuccess))
-      return hip_fail(e, h, "search buffers");
+    const size_t mail_bytes = (size_t)std::max(micro_nw, 1) * mce_micro_mail_words() * sizeof(u64);
+    if ((h = take(arena, B.taboff, (size_t)total * sizeof(u64))) != hipSuccess ||
+        (h = take(arena, B.scan, (size_t)mce_scan_temp_words(total) * sizeof(u64))) != hipSuccess ||
+        (h = take(arena, B.heap, heap_words * sizeof(u64))) != hipSuccess ||
+        (h = take(arena, B.slots, slot_bytes)) != hipSuccess ||
+        (h = take(arena, B.stats, (size_t)stat_rows * MCE_NSTAT * sizeof(u64))) != hipSuccess ||
+        (micro_nw && (h = take(arena, B.mail, mail_bytes)) != hipSuccess))
+      return alloc_fail(e, arena, h, "search buffers");
+    if (micro_nw) {
+      const size_t frame_bytes = 6 * sizeof(u64) * (size_t)micro_nw;
+      if (stat) {
+        const size_t used = (arena.used + 255) & ~(size_t)255;
+        const size_t room = arena.cap > used ? (arena.cap - used) / frame_bytes : 0;
+        while (micro_cap > kMicroStackMinStatic && (size_t)micro_cap > room) micro_cap >>= 1;
+      }
+      if ((h = take(arena, B.mstack, frame_bytes * (size_t)micro_cap)) != hipSuccess)
+        return alloc_fail(e, arena, h, "micro search stacks");
+    }
     if ((h = mce_launch_bucket(sroots, nsub, spc, sxc, mode,
-                               micro_on ? 1 : 0, off, dp<int>(e->lists), dp<u64>(e->taboff), ctl, grid, s)) !=
+                               micro_on ? 1 : 0, off, dp<int>(B.lists), dp<u64>(B.taboff), ctl, grid, s)) !=
         hipSuccess)
       return hip_fail(e, h, "bucket launch");
     // table sizes -> heap offsets (every sub-class's launch reuses the heap from its first root's offset)
-    if ((h = mce_launch_scan(dp<u64>(e->taboff), total, dp<u64>(e->scan), s)) != hipSuccess)
+    if ((h = mce_launch_scan(dp<u64>(B.taboff), total, dp<u64>(B.scan), s)) != hipSuccess)
       return hip_fail(e, h, "table offset scan");
   }
   if (timing) (void)hipEventRecord(e->ev[3], s);
 
   int launches = 0, max_workers_used = 0, stat_off = 0;
   int evi = 4;
-  for (const Plan& pl : plan) {
+  for (int pi = 0; pi < nplan; pi++) {
+    const Plan& pl = plan[pi];
     const int c = pl.sub;
     const SearchLayout& L = pl.L;
     BuildParams bp{};
     bp.rp = row_ptr;
     bp.ci = col_idx;
-    bp.rnd = dp<int>(e->rnd);
-    bp.roots = dp<int>(e->lists) + off.off[c];
+    bp.rnd = dp<int>(B.rnd);
+    bp.roots = dp<int>(B.lists) + off.off[c];
     bp.nroots = counts[c];
     const bool micro = c == MCE_SUB_MICRO;
     bp.W = micro ? 1 : 1 << L.wclass;
     bp.mode = micro ? MCE_MODE_IPX : mode;
     bp.micro = micro ? 1 : 0;
-    bp.heap = dp<u64>(e->heap);
+    bp.heap = dp<u64>(B.heap);
     bp.heap_words = heap_words;
-    bp.tab_off = dp<u64>(e->taboff) + off.off[c];
+    bp.tab_off = dp<u64>(B.taboff) + off.off[c];
     bp.status = &ctl->status;
     bp.l2 = l2 ? 1 : 0;
-    bp.src = dp<int>(e->src);
-    bp.hub_id = maxhubs > 0 ? dp<int>(e->hub_id) : nullptr;
-    bp.hub_bm = dp<u64>(e->hub_bm);
+    bp.src = dp<int>(B.src);
+    bp.hub_id = maxhubs > 0 ? dp<int>(B.hub_id) : nullptr;
+    bp.hub_bm = dp<u64>(B.hub_bm);
     bp.hub_words = (n + 63) / 64;
     if (!micro) {
       // enough (root, part) blocks to fill the chip, at most one part per 64-row
@@ -394,22 +489,22 @@ mce_status run_impl(mce_engine* e, int32_t n, int64_t nnz, const int32_t* row_pt
     if (timing) (void)hipEventRecord(e->ev[evi], s);
     if ((h = mce_launch_build(bp, e->num_cu * 32, s)) != hipSuccess) return hip_fail(e, h, "build launch");
     if (timing) (void)hipEventRecord(e->ev[evi + 1], s);
-    if ((h = mce_launch_wl_init(dp<MceWl>(e->wl), pl.nw, dp<u64>(e->stats) + (size_t)stat_off * MCE_NSTAT, s)) !=
+    if ((h = mce_launch_wl_init(dp<MceWl>(B.wl), pl.nw, dp<u64>(B.stats) + (size_t)stat_off * MCE_NSTAT, s)) !=
         hipSuccess)
       return hip_fail(e, h, "wl init");
     if (micro) {
       MicroParams mp{};
-      mp.heap = dp<u64>(e->heap);
-      mp.tab_off = dp<u64>(e->taboff) + off.off[c];
+      mp.heap = dp<u64>(B.heap);
+      mp.tab_off = dp<u64>(B.taboff) + off.off[c];
       mp.nroots = counts[c];
       mp.nworkers = pl.nw;
-      mp.stacks = dp<u64>(e->mstack);
-      mp.stack_cap = kMicroStack;
+      mp.stacks = dp<u64>(B.mstack);
+      mp.stack_cap = micro_cap;
       mp.mail_words = mce_micro_mail_words();
-      mp.mail = dp<u64>(e->mail);
+      mp.mail = dp<u64>(B.mail);
       mp.g_hist = results + 1;
       mp.g_hash = results;
-      mp.wl = dp<MceWl>(e->wl);
+      mp.wl = dp<MceWl>(B.wl);
       mp.donate_min_p = e->cfg.micro_donate_min_p > 0 ? (int)e->cfg.micro_donate_min_p : 10;
       mp.worker_list = e->cfg.worker_list ? 1 : 0;
       // Cooperative pivot scans pay when every wave works through its own
@@ -419,7 +514,8 @@ mce_status run_impl(mce_engine* e, int32_t n, int64_t nnz, const int32_t* row_pt
       mp.budget = budget;
       mp.t_run = &ctl->t_run;
       mp.status = &ctl->status;
-      mp.stats = dp<u64>(e->stats) + (size_t)stat_off * MCE_NSTAT;
+      mp.stats = dp<u64>(B.stats) + (size_t)stat_off * MCE_NSTAT;
+      mp.taken = &ctl->taken[launches];
       if (stimes) (void)hipEventRecord(e->ev[evi + 2], s);
       if ((h = mce_launch_micro(counters, mp, s)) != hipSuccess) return hip_fail(e, h, "micro search launch");
       if (stimes) (void)hipEventRecord(e->ev[evi + 3], s);
@@ -432,8 +528,8 @@ mce_status run_impl(mce_engine* e, int32_t n, int64_t nnz, const int32_t* row_pt
     SearchParams prm{};
     prm.rp = row_ptr;
     prm.ci = col_idx;
-    prm.heap = dp<u64>(e->heap);
-    prm.tab_off = dp<u64>(e->taboff) + off.off[c];
+    prm.heap = dp<u64>(B.heap);
+    prm.tab_off = dp<u64>(B.taboff) + off.off[c];
     prm.nroots = counts[c];
     prm.nworkers = pl.nw;
     prm.hcap = L.hcap;
@@ -450,14 +546,15 @@ mce_status run_impl(mce_engine* e, int32_t n, int64_t nnz, const int32_t* row_pt
     prm.s_mail = L.s_mail;
     prm.g_hist = results + 1;
     prm.g_hash = results;
-    prm.wl = dp<MceWl>(e->wl);
-    prm.slots = dp<char>(e->slots);
+    prm.wl = dp<MceWl>(B.wl);
+    prm.slots = dp<char>(B.slots);
     prm.donate_min_p = std::max(1, (int)e->cfg.donate_min_p);
     prm.worker_list = e->cfg.worker_list ? 1 : 0;
     prm.budget = budget;
     prm.t_run = &ctl->t_run;
     prm.status = &ctl->status;
-    prm.stats = dp<u64>(e->stats) + (size_t)stat_off * MCE_NSTAT;
+    prm.stats = dp<u64>(B.stats) + (size_t)stat_off * MCE_NSTAT;
+    prm.taken = &ctl->taken[launches];
     if (stimes) (void)hipEventRecord(e->ev[evi + 2], s);
     if ((h = mce_launch_search(L, prm, s)) != hipSuccess) return hip_fail(e, h, "search launch");
     if (stimes) (void)hipEventRecord(e->ev[evi + 3], s);
@@ -467,52 +564,67 @@ mce_status run_impl(mce_engine* e, int32_t n, int64_t nnz, const int32_t* row_pt
     max_workers_used = std::max(max_workers_used, pl.nw);
   }
   // results: one read-back of the control block and the result words
-  if ((h = hipMemcpyAsync(e->host.p, ctl, kIoBytes, hipMemcpyDeviceToHost, s)) != hipSuccess)
+  if ((h = hipMemcpyAsync(hio, ctl, kIoBytes, hipMemcpyDeviceToHost, s)) != hipSuccess)
     return hip_fail(e, h, "result readback");
   if ((h = hipStreamSynchronize(s)) != hipSuccess) return hip_fail(e, h, "synchronize at end");
-  const u64* hres = reinterpret_cast<const u64*>(static_cast<const char*>(e->host.p) + sizeof(MceCtl));
-  if (hctl->status & MCE_E_TIMEOUT) return fail(e, MCE_ERR_TIMEOUT, "search ran past the time limit");
+  const u64* hres = reinterpret_cast<const u64*>(hio + sizeof(MceCtl));
   if (hctl->status & MCE_E_PROTO) return fail(e, MCE_ERR_DEVICE, "worker-list bookkeeping error");
-  if (hctl->status & MCE_E_LIMIT) return fail(e, MCE_ERR_LIMIT, "subtree larger than its width class");
+  if (hctl->status & MCE_E_LIMIT)
+    return fail(e, MCE_ERR_LIMIT,
+                "a subtree larger than its width class, or a micro frame stack (%d frames a wave) overflowed",
+                micro_cap);
   if (hctl->status & MCE_E_HEAP) return fail(e, MCE_ERR_DEVICE, "induced-subgraph heap overflow");
 
-  std::vector<uint64_t> hist(kHistWords, 0);
+  uint64_t* hist = e->hist;
   for (size_t k = 0; k < kHistWords; k++) hist[k] = hres[1 + k];
   hist[1] += iso;
   hist[2] += hctl->pairs;   // second-level roots that are maximal cliques by themselves
   u64 count = 0;
-  size_t len = 0;
+  int32_t len = 0;
   for (size_t k = 0; k < kHistWords; k++) {
     count += hist[k];
-    if (hist[k]) len = k + 1;
+    if (hist[k]) len = (int32_t)k + 1;
   }
-  hist.resize(len);
-  e->hist = hist;
+  e->hist_len = len;
   e->count = count;
   e->hash = hres[0] + iso_hash + hctl->pairs_hash;
   e->have_result = true;
+  // a search stopped at the time limit still reports the cliques it found
+  // (every launch flushes what its waves found), marked incomplete
+  e->complete = (hctl->status & MCE_E_TIMEOUT) == 0;
+  e->info.complete = e->complete ? 1 : 0;
+  {
+    int64_t started = 0;
+    for (int i = 0; i < launches; i++) started += std::min<int64_t>(hctl->taken[i], counts[plan[i].sub]);
+    // roots that need no search: isolated vertices, and second-level roots that are cliques of size 2
+    started += (int64_t)nsub - total;
+    e->info.roots_started = started;
+  }
 
   mce_run_stats& so = e->stats_out;
   so.workers = max_workers_used;
   so.launches = launches;
   u64 words_built = 0;
-  for (const Plan& pl : plan) words_built += hctl->sub_words[var][pl.sub];
+  for (int i = 0; i < nplan; i++) words_built += hctl->sub_words[var][plan[i].sub];
   so.table_words = words_built;
-  e->last_plan.clear();
-  for (size_t i = 0; i < plan.size(); i++) {
-    e->last_plan.push_back({plan[i].sub, plan[i].nw, counts[plan[i].sub]});
+  e->n_last_plan = nplan;
+  for (int i = 0; i < nplan; i++) {
+    e->last_plan[i] = {plan[i].sub, plan[i].nw, counts[plan[i].sub]};
     if (i < 16) {
       so.launch_sub[i] = plan[i].sub;
       so.launch_roots[i] = counts[plan[i].sub];
+      so.launch_words[i] = hctl->sub_words[var][plan[i].sub];
     }
   }
   for (int i = 0; i < 4; i++) so.peel_ticks[i] = hctl->peel_ticks[i];
   so.micro_roots = counts[MCE_SUB_MICRO];
+  so.micro_stack_cap = micro_nw ? micro_cap : 0;
   e->last_stat_rows = stat_rows;
   e->last_timing = timing;
   e->last_stimes = stimes;
   e->stats_pending = true;
   so.ms_total = ms_since(t0);
+  if (!e->complete) return fail(e, MCE_ERR_TIMEOUT, "search ran past the time limit (results are partial)");
   return MCE_OK;
 }
 
@@ -522,7 +634,7 @@ mce_status collect_stats(mce_engine* e) {
   hipError_t h = hipSetDevice(e->device);
   if (h != hipSuccess) return hip_fail(e, h, "hipSetDevice");
   std::vector<u64> st((size_t)e->last_stat_rows * MCE_NSTAT);
-  if (!st.empty() && (h = hipMemcpy(st.data(), e->stats.p, st.size() * sizeof(u64), hipMemcpyDeviceToHost)) !=
+  if (!st.empty() && (h = hipMemcpy(st.data(), e->last->stats.p, st.size() * sizeof(u64), hipMemcpyDeviceToHost)) !=
                          hipSuccess)
     return hip_fail(e, h, "stats readback");
   mce_run_stats& so = e->stats_out;
@@ -530,7 +642,7 @@ mce_status collect_stats(mce_engine* e) {
   e->trace.clear();
   u64 max_busy = 0, max_nodes = 0, max_ticks = 0, start_spread = 0, max_stack = 0;
   int row = 0;
-  for (size_t li = 0; li < e->last_plan.size(); li++) {
+  for (int li = 0; li < e->n_last_plan; li++) {
     const auto& pl = e->last_plan[li];
     u64 smin = ~0ull, smax = 0;
     for (int w = 0; w < pl.nw; w++, row++) {
@@ -546,6 +658,11 @@ mce_status collect_stats(mce_engine* e) {
       rec.nodes = r[ST_NODES];
       rec.donations = r[ST_DONATIONS];
       rec.received = r[ST_RECEIVED];
+      rec.hw_location = r[ST_HWID];
+      rec.leaves = r[ST_LEAVES];
+      rec.pivot_words = r[ST_PIVOT_WORDS];
+      rec.branches = r[ST_BRANCHES];
+      rec.xx_tests = r[ST_XX_TESTS];
       e->trace.push_back(rec);
       for (int i = 0; i < MCE_NSTAT; i++) stat_sum[i] += r[i];
       max_busy = std::max(max_busy, r[ST_BUSY_TICKS]);
@@ -592,7 +709,7 @@ mce_status collect_stats(mce_engine* e) {
   }
   if (e->last_stimes) {
     double mb = 0, ms = 0;
-    for (int i = 0; i < (int)e->last_plan.size(); i++) {
+    for (int i = 0; i < e->n_last_plan; i++) {
       float x = 0, y = 0;
       if (e->last_timing) (void)hipEventElapsedTime(&x, e->ev[4 + 4 * i], e->ev[5 + 4 * i]);
       (void)hipEventElapsedTime(&y, e->ev[6 + 4 * i], e->ev[7 + 4 * i]);
@@ -685,19 +802,21 @@ mce_status mce_create(const mce_config* cfg, mce_engine** out) {
 
 mce_status mce_run(mce_engine* e, int32_t n, int64_t nnz, const int32_t* row_ptr, const int32_t* col_idx,
                    void* stream) {
-  return run_impl(e, n, nnz, row_ptr, col_idx, nullptr, 0, false, stream);
+  Arena own;
+  return run_impl(e, n, nnz, row_ptr, col_idx, nullptr, 0, false, stream, own);
 }
 
 mce_status mce_run_roots(mce_engine* e, int32_t n, int64_t nnz, const int32_t* row_ptr, const int32_t* col_idx,
                          const int32_t* roots, int32_t nroots, void* stream) {
-  return run_impl(e, n, nnz, row_ptr, col_idx, roots, nroots, true, stream);
+  Arena own;
+  return run_impl(e, n, nnz, row_ptr, col_idx, roots, nroots, true, stream, own);
 }
 
 mce_status mce_result(const mce_engine* e, uint64_t* count, uint64_t* hash, uint64_t* hist, int32_t hist_cap,
                       int32_t* hist_len) {
   if (!e) return MCE_ERR_ARG;
   if (!e->have_result) return MCE_ERR_STATE;
-  int32_t len = (int32_t)e->hist.size();
+  int32_t len = e->hist_len;
   if (hist_len) *hist_len = len;
   if (count) *count = e->count;
   if (hash) *hash = e->hash;
@@ -705,7 +824,7 @@ mce_status mce_result(const mce_engine* e, uint64_t* count, uint64_t* hash, uint
     if (hist_cap < len) return MCE_ERR_ARG;
     for (int32_t i = 0; i < len; i++) hist[i] = e->hist[i];
   }
-  return MCE_OK;
+  return e->complete ? MCE_OK : MCE_ERR_TIMEOUT;
 }
 
 mce_status mce_graph_info(const mce_engine* e, mce_graph_facts* info) {
@@ -721,8 +840,10 @@ mce_status mce_ordering(const mce_engine* e, int32_t* core, int32_t* round, void
   size_t nb = (size_t)e->last_n * sizeof(int32_t);
   if (nb == 0) return MCE_OK;
   if (hipSetDevice(e->device) != hipSuccess) return MCE_ERR_DEVICE;
-  if (core && hipMemcpyAsync(core, e->core.p, nb, hipMemcpyDeviceToDevice, s) != hipSuccess) return MCE_ERR_DEVICE;
-  if (round && hipMemcpyAsync(round, e->rnd.p, nb, hipMemcpyDeviceToDevice, s) != hipSuccess) return MCE_ERR_DEVICE;
+  if (core && hipMemcpyAsync(core, e->last->core.p, nb, hipMemcpyDeviceToDevice, s) != hipSuccess)
+    return MCE_ERR_DEVICE;
+  if (round && hipMemcpyAsync(round, e->last->rnd.p, nb, hipMemcpyDeviceToDevice, s) != hipSuccess)
+    return MCE_ERR_DEVICE;
   if (hipStreamSynchronize(s) != hipSuccess) return MCE_ERR_DEVICE;
   return MCE_OK;
 }
@@ -751,7 +872,7 @@ mce_status mce_worker_trace(const mce_engine* e, mce_worker_record* out, int32_t
   return MCE_OK;
 }
 
-const char* mce_last_error(const mce_engine* e) { return e ? e->err.c_str() : "null engine"; }
+const char* mce_last_error(const mce_engine* e) { return e ? e->err : "null engine"; }
 
 const char* mce_status_string(mce_status s) {
   switch (s) {
@@ -770,12 +891,12 @@ const char* mce_status_string(mce_status s) {
 void mce_destroy(mce_engine* e) {
   if (!e) return;
   (void)hipSetDevice(e->device);
-  DevBuf* bufs[] = {&e->ctl,    &e->deg,   &e->rnd,    &e->core,    &e->alive0, &e->alive1,
-                    &e->front0, &e->front1, &e->bfront0, &e->bfront1, &e->pcount, &e->xcount, &e->lists,  &e->taboff, &e->scan,
-                    &e->heap,   &e->wl,    &e->slots,  &e->stats,  &e->mstack, &e->mail,
-                    &e->src,    &e->fwd,   &e->fwdtmp, &e->eroots, &e->pcount2, &e->xcount2,
-                    &e->hub_id, &e->hub_v, &e->hub_bm};
-  for (DevBuf* b : bufs) release(*b);
+  Bufs& b = e->own;   // the carved set points into the static scratch: nothing to free
+  DevBuf* bufs[] = {&b.ctl,    &b.deg,    &b.rnd,     &b.core,    &b.alive0, &b.alive1,  &b.front0, &b.front1,
+                    &b.bfront0, &b.bfront1, &b.pcount, &b.xcount,  &b.lists,  &b.taboff,  &b.scan,   &b.heap,
+                    &b.wl,     &b.slots,  &b.stats,   &b.mstack,  &b.mail,   &b.src,     &b.fwd,    &b.fwdtmp,
+                    &b.eroots, &b.pcount2, &b.xcount2, &b.hub_id, &b.hub_v,  &b.hub_bm};
+  for (DevBuf* d : bufs) release(*d);
   if (e->host.p) (void)hipHostFree(e->host.p);
   for (auto& ev : e->ev)
     if (ev) (void)hipEventDestroy(ev);

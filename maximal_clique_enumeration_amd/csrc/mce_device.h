@@ -122,6 +122,7 @@ struct MceCtl {
   int seg_state[12];     // peel: the state block 0 hands back (result, list, frontier, level, round, slot, sums)
   u64 t_run;             // wall-clock tick at the start of the peel: the run's time limit counts from it
   u64 peel_ticks[4];     // block 0 of the peel: barrier waits, level passes, round work, total
+  u32 taken[2 * MCE_NCLASS + 1];   // per search launch: subtrees handed out (see record_taken)
   // grid barrier of the peel, one 128-byte line each: [0] groups complete,
   // [1] barriers released, [2 + g] arrivals of block group g (all counts since
   // the launch began)

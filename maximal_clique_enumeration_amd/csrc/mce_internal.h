@@ -51,9 +51,31 @@ enum {
   ST_LANE_STEPS,     // micro kernel: lanes holding a frame, summed over steps
   ST_FIRST_ABS,      // wall-clock tick at which the first task started (0: none)
   ST_LAST_ABS,       // wall-clock tick at which the last task ended
+  ST_HWID,           // where the wave ran: XCC_ID << 32 | HW_ID (compute unit, shader array, engine)
   ST_ACT0,           // counting instances: shader-clock cycles per activity (MCE_NACT words)
   MCE_NSTAT = ST_ACT0 + MCE_NACT
 };
+
+// Where a wave runs: XCC_ID (bits 3:0 of HW_REG_XCC_ID: the accelerator
+// complex die) in the high word, HW_REG_HW_ID in the low word (wave slot,
+// SIMD, compute unit in bits 11:8, shader array bit 12, shader engine bits
+// 15:13). The compute unit a wave ran on is (XCC_ID, bits 15:8 of HW_ID).
+__device__ __forceinline__ u64 wave_hw_location() {
+  const u32 hw = __builtin_amdgcn_s_getreg(4 | (0 << 6) | (31 << 11));    // hwreg(HW_REG_HW_ID)
+  const u32 xcc = __builtin_amdgcn_s_getreg(20 | (0 << 6) | (15 << 11));  // hwreg(HW_REG_XCC_ID, 0, 16)
+  return ((u64)(xcc & 0xFu) << 32) | hw;
+}
+
+// The end of a search launch, by wave 0 as it leaves: the subtrees handed out
+// (every one when the launch was not stopped; otherwise those taken from the
+// counter by then, each finished or abandoned at the stop).
+__device__ __forceinline__ void record_taken(u32* taken, const MceWl* wl, u32 nroots) {
+  if (!taken) return;
+  const u32 stopped = __hip_atomic_load(&wl->done, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const u32 ctr = __hip_atomic_load(&wl->root_ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __hip_atomic_store(taken, stopped ? (ctr < nroots ? ctr : nroots) : nroots, __ATOMIC_RELAXED,
+                     __HIP_MEMORY_SCOPE_AGENT);
+}
 
 // Cycle accounting of the counting kernel instances: each mark charges the
 // cycles since the previous mark to one activity, so the activities of a wave
@@ -113,6 +135,7 @@ struct SearchParams {
   const u64* t_run;      // run start tick, written by the peel
   u32* status;
   u64* stats;            // nworkers * MCE_NSTAT
+  u32* taken;            // wave 0 stores, as it leaves, the subtrees this launch handed out
 };
 
 // The micro search (|P| <= 64, |X| <= 64): one frame per lane, a frame stack
@@ -136,6 +159,7 @@ struct MicroParams {
   const u64* t_run;
   u32* status;
   u64* stats;            // nworkers * MCE_NSTAT
+  u32* taken;            // as in SearchParams
 };
 
 struct BuildParams {
@@ -160,6 +184,8 @@ struct BuildParams {
   int hub_words;
 };
 
+// Clears words u64 at p.
+hipError_t mce_launch_zero(u64* p, size_t words, hipStream_t s);
 // Input checks.
 hipError_t mce_launch_validate(int n, long long nnz, const int* rp, const int* ci, MceCtl* ctl, int blocks,
                                hipStream_t s);

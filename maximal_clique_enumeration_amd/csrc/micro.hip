@@ -161,8 +161,16 @@ __global__ __launch_bounds__(64) void k_search_micro(MicroParams prm) {
   const int lane = lane_id();
   const int wid = blockIdx.x;
   MceWl* wl = prm.wl;
-  if (ld_relaxed(prm.status) & (MCE_E_HEAP | MCE_E_LIMIT)) return;
+  // a failed build, or a run already past its time limit: search nothing
+  if (ld_relaxed(prm.status) & (MCE_E_HEAP | MCE_E_LIMIT | MCE_E_TIMEOUT)) {
+    if (wid == 0 && lane == 0 && prm.taken) {
+      const u32 ctr = ld_relaxed(&wl->root_ctr);
+      st_relaxed(prm.taken, min(ctr, (u32)prm.nroots));
+    }
+    return;
+  }
   const u64 t_start = wall_clock64();
+  const u64 hwloc = wave_hw_location();
   ActClock<CNT> act;   // per-activity cycles (counting instance)
   act.start();
   const u64 deadline = ld_relaxed64(prm.t_run) + prm.budget;
@@ -605,6 +613,8 @@ __global__ __launch_bounds__(64) void k_search_micro(MicroParams prm) {
   }
 
   // ---------------------------------------------------------- flush
+  // (also after a stop at the time limit: the cliques found so far are
+  // reported, and the run is marked incomplete)
   if ((u32)lane < qn) hacc += mce_mix64(s_q[lane]);
   const u64 t_end = wall_clock64();
   const u64 hsum = wave_sum_u64(hacc);
@@ -613,10 +623,11 @@ __global__ __launch_bounds__(64) void k_search_micro(MicroParams prm) {
   for (int i = lane; i < MCE_MICRO_MAX + 4; i += MCE_WAVE) {
     const u64 h = s_hist[i];
     mine += h;
-    if (h && !abort) atomicAdd(&prm.g_hist[i], h);
+    if (h) atomicAdd(&prm.g_hist[i], h);
   }
   const u64 leaves = wave_sum_u64(mine);
-  if (!abort && lane == 0 && hsum) atomicAdd(prm.g_hash, hsum);
+  if (lane == 0 && hsum) atomicAdd(prm.g_hash, hsum);
+  if (wid == 0 && lane == 0) record_taken(prm.taken, wl, (u32)prm.nroots);
   act.mark(ACT_EMIT);
   const u64 prow = CNT ? wave_sum_u64(st_prow) : 0ull;
   const u64 nbr = CNT ? wave_sum_u64(st_br) : 0ull;
@@ -640,6 +651,7 @@ __global__ __launch_bounds__(64) void k_search_micro(MicroParams prm) {
     st[ST_LANE_STEPS] = st_lanes;
     st[ST_FIRST_ABS] = t_first;
     st[ST_LAST_ABS] = t_last;
+    st[ST_HWID] = hwloc;
     act.store(st);
   }
 }

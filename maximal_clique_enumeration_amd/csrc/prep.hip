@@ -1230,7 +1230,22 @@ __global__ __launch_bounds__(256) void k_bucket(const int* __restrict__ roots, i
   }
 }
 
+// Clears `words` u64 (the control block before a run). A kernel rather than a
+// memset: the same stream operation, and one that a captured graph replays
+// correctly.
+__global__ __launch_bounds__(256) void k_zero(u64* p, long long words) {
+  for (long long i = blockIdx.x * (long long)blockDim.x + threadIdx.x; i < words; i += (long long)gridDim.x * blockDim.x)
+    p[i] = 0ull;
+}
+
 // ------------------------------------------------------------------ launchers
+
+hipError_t mce_launch_zero(u64* p, size_t words, hipStream_t s) {
+  if (words == 0) return hipSuccess;
+  const int nb = (int)std::min<size_t>(64, (words + 255) / 256);
+  hipLaunchKernelGGL(k_zero, dim3(nb), dim3(256), 0, s, p, (long long)words);
+  return hipGetLastError();
+}
 
 hipError_t mce_launch_validate(int n, long long nnz, const int* rp, const int* ci, MceCtl* ctl, int blocks,
                                hipStream_t s) {

@@ -158,8 +158,13 @@ __global__ __launch_bounds__(64) void k_search(SearchParams prm) {
   int* xx = SROWS ? (int*)(lds + prm.l_xx) : (int*)(slot + prm.s_xx);
   u64* lrows = lds + prm.l_rows;
 
-  // a failed build leaves some tables unwritten: search nothing
-  if (ld_relaxed(prm.status) & (MCE_E_HEAP | MCE_E_LIMIT)) return;
+  // a failed build leaves some tables unwritten, and a run past its time limit
+  // goes no further: search nothing
+  if (ld_relaxed(prm.status) & (MCE_E_HEAP | MCE_E_LIMIT | MCE_E_TIMEOUT)) {
+    if (wid == 0 && lane == 0 && prm.taken) st_relaxed(prm.taken, min(ld_relaxed(&wl->root_ctr), (u32)prm.nroots));
+    return;
+  }
+  const u64 hwloc = wave_hw_location();
   for (int i = lane; i < prm.hcap; i += MCE_WAVE) s_hist[i] = 0;
   __syncthreads();
   // this wave is active until phase 1 finds the roots exhausted (wl_idle gives
@@ -512,18 +517,19 @@ __global__ __launch_bounds__(64) void k_search(SearchParams prm) {
   }
 
   // ---------------------------------------------------------- flush
+  // (also after a stop at the time limit: the cliques found so far)
   const u64 t_end = wall_clock64();
-  if (!abort) {
-    __syncthreads();
-    for (int i = lane; i < prm.hcap; i += MCE_WAVE) {
-      const u64 h = s_hist[i];
-      if (h) atomicAdd(&prm.g_hist[i], h);
-    }
-    if (lane == 0 && hacc) atomicAdd(prm.g_hash, hacc);
+  __syncthreads();
+  for (int i = lane; i < prm.hcap; i += MCE_WAVE) {
+    const u64 h = s_hist[i];
+    if (h) atomicAdd(&prm.g_hist[i], h);
   }
+  if (lane == 0 && hacc) atomicAdd(prm.g_hash, hacc);
+  if (wid == 0 && lane == 0) record_taken(prm.taken, wl, (u32)prm.nroots);
   act.mark(ACT_EMIT);
   if (lane == 0) {
     u64* st = prm.stats + (size_t)wid * MCE_NSTAT;
+    st[ST_HWID] = hwloc;
     st[ST_NODES] = st_nodes;
     st[ST_LEAVES] = st_leaves;
     st[ST_DONATIONS] = st_don;
@@ -568,7 +574,11 @@ __global__ __launch_bounds__(64) void k_search_w1(SearchParams prm) {
   int* xx = SROWS ? (int*)(lds + prm.l_xx) : (int*)(slot + prm.s_xx);
   u64* lrows = lds + prm.l_rows;
 
-  if (ld_relaxed(prm.status) & (MCE_E_HEAP | MCE_E_LIMIT)) return;
+  if (ld_relaxed(prm.status) & (MCE_E_HEAP | MCE_E_LIMIT | MCE_E_TIMEOUT)) {
+    if (wid == 0 && lane == 0 && prm.taken) st_relaxed(prm.taken, min(ld_relaxed(&wl->root_ctr), (u32)prm.nroots));
+    return;
+  }
+  const u64 hwloc = wave_hw_location();
   ActClock<CNT> act;   // per-activity cycles (counting instance)
   act.start();
   for (int i = lane; i < prm.hcap; i += MCE_WAVE) s_hist[i] = 0;
@@ -913,17 +923,17 @@ __global__ __launch_bounds__(64) void k_search_w1(SearchParams prm) {
   }
 
   // ---------------------------------------------------------- flush
+  // (also after a stop at the time limit: the cliques found so far)
   const u64 t_end = wall_clock64();
   u64 leaves = wave_sum_u64(hist_lane);
-  if (!abort) {
-    __syncthreads();
-    if (hist_lane) atomicAdd(&prm.g_hist[lane], hist_lane);
-    for (int i = 64 + lane; i < prm.hcap; i += MCE_WAVE) {
-      const u64 h = s_hist[i];
-      if (h) atomicAdd(&prm.g_hist[i], h);
-    }
-    if (lane == 0 && hacc) atomicAdd(prm.g_hash, hacc);
+  __syncthreads();
+  if (hist_lane) atomicAdd(&prm.g_hist[lane], hist_lane);
+  for (int i = 64 + lane; i < prm.hcap; i += MCE_WAVE) {
+    const u64 h = s_hist[i];
+    if (h) atomicAdd(&prm.g_hist[i], h);
   }
+  if (lane == 0 && hacc) atomicAdd(prm.g_hash, hacc);
+  if (wid == 0 && lane == 0) record_taken(prm.taken, wl, (u32)prm.nroots);
   act.mark(ACT_EMIT);
   for (int i = 64; i < prm.hcap; i++) leaves += s_hist[i];
   if (lane == 0) {
@@ -948,6 +958,7 @@ __global__ __launch_bounds__(64) void k_search_w1(SearchParams prm) {
     st[ST_LAST_ABS] = t_last;
     st[ST_CHECKS] = st_checks;
     st[ST_DONATE_OK_TICKS] = s_misc[7];
+    st[ST_HWID] = hwloc;
     act.store(st);
   }
 }

@@ -8,8 +8,8 @@
  *
  * What it computes follows "Parallelizing Maximal Clique Enumeration on GPUs"
  * (arxiv 2212.01473v2):
- *   - section 2.1: G is simple and undirected; a maximal clique is a clique not
- *     contained in a larger clique; the answer is the set of all of them;
+ *   - section 2.1: G is simple and undirected; a clique C is maximal when no
+ *     vertex outside C is adjacent to all of C; the answer is all such cliques;
  *   - section 2.3, Algorithm 2: Bron-Kerbosch with pivoting, with Tomita's rule
  *     (pivot = vertex of P u X with the most neighbours in P);
  *   - section 2.4, Algorithm 3: one independent first-level subtree per vertex
