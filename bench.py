@@ -88,21 +88,37 @@ def parse():
 
 
 # ---------------------------------------------------------------- counters
-def sources_hash():
-    """SHA-256 prefix over every source file of the library: a counter summary
-    taken on other sources is not used."""
+# The source file that defines each kernel family; every family also compiles
+# the shared device headers.
+KERNEL_SOURCES = {"k_peel": "prep.hip", "k_validate": "prep.hip", "k_search_micro": "micro.hip",
+                  "k_search": "search.hip", "k_build": "subgraph.hip"}
+SHARED_HEADERS = ("mce_device.h", "mce_internal.h", "worklist.h")
+
+
+def family(kernel):
+    for k in sorted(KERNEL_SOURCES, key=len, reverse=True):
+        if kernel.startswith(k):
+            return k
+    return None
+
+
+def sources_hash(kernel):
+    """SHA-256 prefix over the source file that defines `kernel` and every header
+    it includes: a counter summary taken on other sources is not used."""
+    fam = family(kernel)
+    if fam is None:
+        return None
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "maximal_clique_enumeration_amd", "csrc")
-    for name in sorted(os.listdir(csrc)):
-        if name.endswith((".hip", ".h", ".cpp")):
-            with open(os.path.join(csrc, name), "rb") as f:
-                h.update(name.encode() + b"\0" + f.read())
+    for name in (KERNEL_SOURCES[fam],) + SHARED_HEADERS:
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
     return h.hexdigest()[:16]
 
 
 def load_counters(path, workload):
-    """The committed rocprofv3 counter summary for this workload, if it was taken
-    on the current sources; {kernel family: {...}} or {}."""
+    """The committed rocprofv3 counter summary for this workload: {row key: {...}}
+    for the kernels whose sources are unchanged since it was taken."""
     if not os.path.exists(path):
         return {}
     try:
@@ -110,9 +126,8 @@ def load_counters(path, workload):
             doc = json.load(f)
     except (OSError, ValueError):
         return {}
-    if doc.get("sources_sha256_16") != sources_hash():
-        return {}
-    return doc.get("workloads", {}).get(workload, {})
+    rows = doc.get("workloads", {}).get(workload, {})
+    return {k: v for k, v in rows.items() if v.get("sources_sha256_16") == sources_hash(k.split("#")[0])}
 
 
 # ---------------------------------------------------------------- work per launch
@@ -288,10 +303,14 @@ def cpu_baseline(g, budget_s, procs, roots=None):
 def measure(mce, torch, g, args, rp, ci, roots, events, steps, warmup, cap_ms=0):
     """Counting run (exact work per launch), then `steps` timed runs."""
     timeout = cap_ms if cap_ms else 100000
-    with mce.Engine(device=0, counters=True, timeout_ms=timeout, level=args.level, subgraph=args.subgraph) as ecnt:
-        ref = ecnt.run(rp, ci, roots=roots, partial_ok=bool(cap_ms))
-        cst = ecnt.stats()
-        ctrace = ecnt.worker_trace()
+    if cap_ms:
+        ref, cst, ctrace = None, None, []   # a stopped run's work is not the workload's: no counting run
+    else:
+        with mce.Engine(device=0, counters=True, timeout_ms=timeout, level=args.level,
+                        subgraph=args.subgraph) as ecnt:
+            ref = ecnt.run(rp, ci, roots=roots)
+            cst = ecnt.stats()
+            ctrace = ecnt.worker_trace()
     eng = mce.Engine(device=0, timeout_ms=timeout, level=args.level, subgraph=args.subgraph,
                      search_times=events == "search", phase_times=events == "phase")
     for _ in range(warmup):
@@ -315,6 +334,8 @@ def measure(mce, torch, g, args, rp, ci, roots, events, steps, warmup, cap_ms=0)
     trace = eng.worker_trace()
     info = eng.graph_info()
     eng.close()
+    if cap_ms:
+        ref, cst = results[-1], stats[-1]
     return ref, cst, ctrace, times, stats, results, trace, info
 
 
@@ -476,6 +497,8 @@ def main():
                    "search_steps": cst["steps"],
                    "lane_util": (cst["lane_steps"] / (64 * cst["steps"]) if cst["steps"] else None),
                    "peel_rounds": info["rounds"],
+                   # block 0 of the peel: barrier waits, level passes, round work, total (ms)
+                   "peel_ms_split": [t / st["tick_hz"] * 1e3 for t in st["peel_ticks"]],
                    "cu_load": balance,
                    "counters_profile": bool(counters),
                    # share of the search's wavefront cycles by activity (the counting run;

@@ -67,6 +67,12 @@ def _load():
                                    ctypes.c_int64, u64p, u64p, u64p, ctypes.c_int32,
                                    i32p, i64p]
         lib.oracle_mce_l2.restype = ctypes.c_int
+        lib.oracle_mce_each.argtypes = [ctypes.c_int32, i32p, i32p, i32p, i32p, ctypes.c_int32, ctypes.c_int64,
+                                        i64p, u64p, u64p, P(ctypes.c_uint8)]
+        lib.oracle_mce_each.restype = ctypes.c_int
+        lib.oracle_knuth.argtypes = [ctypes.c_int32, i32p, i32p, i32p, ctypes.c_int32, ctypes.c_int64,
+                                     ctypes.c_uint64, P(ctypes.c_double), i32p]
+        lib.oracle_knuth.restype = ctypes.c_int
         lib.oracle_list.argtypes = [ctypes.c_int32, i32p, i32p, i32p, i32p, ctypes.c_int64]
         lib.oracle_list.restype = ctypes.c_int64
         _lib = lib
@@ -178,3 +184,61 @@ def list_cliques(n: int, row_ptr, col_idx, rnd=None):
         else:
             cur.append(int(x))
     return cliques
+
+
+@dataclass
+class Estimate:
+    walks: int
+    nodes: float            # mean of the walks' node estimates
+    nodes_se: float         # its standard error
+    cliques: float          # mean of the walks' maximal-clique estimates
+    cliques_se: float
+    max_depth: int          # deepest walk (a clique of max_depth + 1 vertices ends it when maximal)
+
+
+def knuth(n: int, row_ptr, col_idx, root: int, walks: int, seed: int = 1, rnd=None) -> Estimate:
+    """Knuth's random-probe estimate of the first-level subtree of `root`
+    (nodes = calls of Algorithm 2, cliques = maximal cliques whose earliest
+    vertex is root): unbiased, with the standard error of the mean over walks."""
+    rp, rpp = _i32(row_ptr)
+    ci, cip = _i32(col_idx)
+    if rnd is None:
+        _, rnd, _ = peel(n, rp, ci)
+    rn, rnp = _i32(rnd)
+    sums = (ctypes.c_double * 4)()
+    dmax = ctypes.c_int32()
+    rc = _load().oracle_knuth(n, rpp, cip, rnp, int(root), int(walks), ctypes.c_uint64(seed & MASK64),
+                              sums, ctypes.byref(dmax))
+    if rc != 0:
+        raise RuntimeError(f"oracle_knuth failed with code {rc}")
+
+    def mean_se(s, s2):
+        m = s / walks
+        var = max(s2 / walks - m * m, 0.0)
+        return m, (var / walks) ** 0.5 if walks > 1 else float("inf")
+    nm, nse = mean_se(sums[0], sums[1])
+    cm, cse = mean_se(sums[2], sums[3])
+    return Estimate(int(walks), nm, nse, cm, cse, int(dmax.value))
+
+
+def mce_each(n: int, row_ptr, col_idx, roots, root_budget: int, rnd):
+    """Each root's first-level subtree on its own node budget: arrays (nodes,
+    count, hash, done) in the order of `roots`; count and hash of a root with
+    done == 0 are partial."""
+    rp, rpp = _i32(row_ptr)
+    ci, cip = _i32(col_idx)
+    rn, rnp = _i32(rnd)
+    ro, rop = _i32(roots if len(roots) else np.zeros(1, np.int32))
+    k = len(roots)
+    nodes = np.zeros(max(k, 1), np.int64)
+    count = np.zeros(max(k, 1), np.uint64)
+    hsh = np.zeros(max(k, 1), np.uint64)
+    done = np.zeros(max(k, 1), np.uint8)
+    rc = _load().oracle_mce_each(n, rpp, cip, rnp, rop, k, int(root_budget),
+                                 nodes.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)),
+                                 count.ctypes.data_as(ctypes.POINTER(ctypes.c_uint64)),
+                                 hsh.ctypes.data_as(ctypes.POINTER(ctypes.c_uint64)),
+                                 done.ctypes.data_as(ctypes.POINTER(ctypes.c_uint8)))
+    if rc != 0:
+        raise RuntimeError(f"oracle_mce_each failed with code {rc}")
+    return nodes[:k], count[:k], hsh[:k], done[:k]

@@ -406,6 +406,187 @@ int oracle_mce_l2(int32_t n, const int32_t *rp, const int32_t *ci, const int32_t
   return 0;
 }
 
+/* Like oracle_mce over roots[0..nroots), but each root's first-level subtree
+   gets its own budget of root_budget search-tree nodes (0: none): for root i,
+   nodes[i] = nodes searched, count[i] and hash[i] = its maximal cliques and
+   their hash sum, done[i] = 1 if the subtree was searched to the end (else its
+   count and hash are partial and must not be used). Returns 0, -1 on
+   allocation failure, -2 for a root out of range. */
+int oracle_mce_each(int32_t n, const int32_t *rp, const int32_t *ci, const int32_t *rnd,
+                    const int32_t *roots, int32_t nroots, int64_t root_budget,
+                    int64_t *nodes, uint64_t *count, uint64_t *hash, uint8_t *done) {
+  search s;
+  memset(&s, 0, sizeof(s));
+  s.rp = rp; s.ci = ci; s.rnd = rnd;
+  int32_t maxdeg = 0;
+  for (int32_t v = 0; v < n; v++) if (rp[v + 1] - rp[v] > maxdeg) maxdeg = rp[v + 1] - rp[v];
+  s.hist_cap = maxdeg + 3;
+  s.hist = (uint64_t *)calloc((size_t)s.hist_cap, sizeof(uint64_t));
+  s.L = (int32_t *)malloc(sizeof(int32_t) * (size_t)(maxdeg + 1));
+  s.R = (int32_t *)malloc(sizeof(int32_t) * (size_t)(maxdeg + 2));
+  int32_t *loc = (int32_t *)malloc(sizeof(int32_t) * (size_t)(n > 0 ? n : 1));
+  if (!s.hist || !s.L || !s.R || !loc) { free(s.hist); free(s.L); free(s.R); free(loc); return -1; }
+  for (int32_t v = 0; v < n; v++) loc[v] = -1;
+  int rc = 0;
+  for (int32_t i = 0; i < nroots; i++) {
+    int32_t r = roots[i];
+    if (r < 0 || r >= n) { rc = -2; break; }
+    s.count = 0; s.hash = 0; s.nodes = 0; s.over_budget = 0;
+    s.budget = root_budget;
+    if (run_root(&s, r, loc) != 0) { rc = -1; break; }
+    nodes[i] = s.nodes;
+    count[i] = s.count;
+    hash[i] = s.hash;
+    done[i] = s.over_budget ? 0 : 1;
+  }
+  free(s.hist); free(s.L); free(s.R); free(loc);
+  return rc;
+}
+
+/* ------------------------------------------------------------------ subtree size estimate
+   Knuth's random-probe estimate of a backtrack tree (D. E. Knuth, "Estimating
+   the efficiency of backtrack programs", Mathematics of Computation 29, 1975),
+   applied to the first-level subtree of one root (Algorithm 3 with Algorithm
+   2). A walk starts at the root node and, at every node whose P is not empty,
+   takes one of its branches uniformly at random: branch j (v_j, the j-th
+   vertex of P - N(pivot) in ascending id, pivot by Tomita's rule as in bkt) is
+   the child (P_j n N(v_j), X_j n N(v_j)), where P_j and X_j are P and X after
+   the branches before it moved v_1 .. v_{j-1} from P to X. With c_t the branch
+   count met at depth t, the walk estimates the node count (calls of bkt) as
+   1 + c_0 + c_0 c_1 + ..., and the maximal cliques as c_0 c_1 ... c_{t-1} when
+   it ends at a node with P and X empty (else 0). Both estimates are unbiased.
+   A test-side tool: it sizes workloads, it is never compared with the engine. */
+static uint64_t knuth_next(uint64_t *state) {   /* SplitMix64 sequence */
+  *state += GOLDEN;
+  return oracle_mix64(*state);
+}
+
+static void knuth_walk(search *s, uint64_t *rng, double *est_nodes, double *est_cliques, int *depth_out) {
+  int wp = s->wp, wl = s->wl;
+  double w = 1.0, nodes = 1.0;
+  int depth = 0;
+  for (;;) {
+    uint64_t *P = s->arena + (size_t)depth * (2 * wp + wl);
+    uint64_t *X = P + wp;
+    uint64_t *cand = X + wl;
+    int pe = 1, xe = 1;
+    for (int i = 0; i < wp; i++) if (P[i]) { pe = 0; break; }
+    for (int i = 0; i < wl; i++) if (X[i]) { xe = 0; break; }
+    if (pe) {
+      *est_cliques = xe ? w : 0.0;
+      break;
+    }
+    int32_t best = -1, bestc = -1;
+    for (int i = 0; i < wl; i++) {
+      uint64_t bits = X[i] | (i < wp ? P[i] : 0);
+      while (bits) {
+        int32_t u = i * 64 + __builtin_ctzll(bits);
+        bits &= bits - 1;
+        const uint64_t *row = s->adjP + (size_t)u * wp;
+        int c = 0;
+        for (int t = 0; t < wp; t++) c += popc(P[t] & row[t]);
+        if (c > bestc || (c == bestc && s->L[u] < s->L[best])) { best = u; bestc = c; }
+      }
+    }
+    const uint64_t *prow = s->adjP + (size_t)best * wp;
+    int64_t nc = 0;
+    for (int i = 0; i < wp; i++) { cand[i] = P[i] & ~prow[i]; nc += popc(cand[i]); }
+    if (nc == 0) {                 /* an X vertex adjacent to all of P: no branch */
+      *est_cliques = 0.0;
+      break;
+    }
+    const uint64_t pick = (uint64_t)(((unsigned __int128)knuth_next(rng) * (uint64_t)nc) >> 64);
+    /* the branches before the picked one move from P to X */
+    uint64_t left = pick;
+    int32_t v = -1;
+    for (int i = 0; i < wp && v < 0; i++) {
+      uint64_t bits = cand[i];
+      while (bits) {
+        const int b = __builtin_ctzll(bits);
+        bits &= bits - 1;
+        if (left == 0) { v = i * 64 + b; break; }
+        P[i] &= ~(1ULL << b);
+        X[i] |= 1ULL << b;
+        left--;
+      }
+    }
+    const uint64_t *vrow = s->adjP + (size_t)v * wp;
+    const uint64_t *vcol = s->colL + (size_t)v * wl;
+    uint64_t *Pn = s->arena + (size_t)(depth + 1) * (2 * wp + wl);
+    uint64_t *Xn = Pn + wp;
+    for (int i = 0; i < wp; i++) Pn[i] = P[i] & vrow[i];
+    for (int i = 0; i < wl; i++) Xn[i] = X[i] & vcol[i];
+    w *= (double)nc;
+    nodes += w;
+    depth++;
+  }
+  *est_nodes = nodes;
+  *depth_out = depth;
+}
+
+/* `walks` probes of root's first-level subtree (bitsets as in run_root).
+   Returns, over the walks, the sums of the node and clique estimates and of
+   their squares, and the deepest walk (its leaf is a clique of depth + 1
+   vertices when maximal). 0 on success, -1 on allocation failure, -2 for a
+   root out of range. */
+int oracle_knuth(int32_t n, const int32_t *rp, const int32_t *ci, const int32_t *rnd, int32_t root,
+                 int64_t walks, uint64_t seed, double *sums, int32_t *max_depth) {
+  if (root < 0 || root >= n) return -2;
+  search s;
+  memset(&s, 0, sizeof(s));
+  s.rp = rp; s.ci = ci; s.rnd = rnd;
+  int32_t deg = rp[root + 1] - rp[root];
+  s.L = (int32_t *)malloc(sizeof(int32_t) * (size_t)(deg + 1));
+  int32_t *loc = (int32_t *)malloc(sizeof(int32_t) * (size_t)(n > 0 ? n : 1));
+  if (!s.L || !loc) { free(s.L); free(loc); return -1; }
+  for (int32_t v = 0; v < n; v++) loc[v] = -1;
+  int32_t p = 0;
+  for (int64_t e = rp[root]; e < rp[root + 1]; e++) if (later(rnd, ci[e], root)) s.L[p++] = ci[e];
+  int32_t nx = p;
+  for (int64_t e = rp[root]; e < rp[root + 1]; e++) if (!later(rnd, ci[e], root)) s.L[nx++] = ci[e];
+  int wp = (p + 63) / 64; if (wp == 0) wp = 1;
+  int wl = (deg + 63) / 64; if (wl == 0) wl = 1;
+  s.p = p; s.nl = deg; s.wp = wp; s.wl = wl;
+  const size_t rec = (size_t)(2 * wp + wl);
+  s.adjP = (uint64_t *)calloc((size_t)(deg > 0 ? deg : 1) * wp, sizeof(uint64_t));
+  s.colL = (uint64_t *)calloc((size_t)(p > 0 ? p : 1) * wl, sizeof(uint64_t));
+  s.arena = (uint64_t *)calloc((size_t)(p + 2) * rec, sizeof(uint64_t));
+  uint64_t *root_rec = (uint64_t *)calloc(rec, sizeof(uint64_t));
+  if (!s.adjP || !s.colL || !s.arena || !root_rec) {
+    free(s.adjP); free(s.colL); free(s.arena); free(root_rec); free(s.L); free(loc);
+    return -1;
+  }
+  for (int32_t a = 0; a < deg; a++) loc[s.L[a]] = a;
+  for (int32_t a = 0; a < deg; a++) {
+    int32_t x = s.L[a];
+    for (int64_t e = rp[x]; e < rp[x + 1]; e++) {
+      int32_t b = loc[ci[e]];
+      if (b >= 0 && b < p) s.adjP[(size_t)a * wp + (b >> 6)] |= 1ULL << (b & 63);
+    }
+  }
+  for (int32_t a = 0; a < deg; a++)
+    for (int32_t b = 0; b < p; b++)
+      if ((s.adjP[(size_t)a * wp + (b >> 6)] >> (b & 63)) & 1)
+        s.colL[(size_t)b * wl + (a >> 6)] |= 1ULL << (a & 63);
+  for (int32_t b = 0; b < p; b++) root_rec[b >> 6] |= 1ULL << (b & 63);
+  for (int32_t a = p; a < deg; a++) root_rec[wp + (a >> 6)] |= 1ULL << (a & 63);
+  uint64_t rng = seed;
+  double sn = 0, sn2 = 0, sc = 0, sc2 = 0;
+  int32_t dmax = 0;
+  for (int64_t t = 0; t < walks; t++) {
+    memcpy(s.arena, root_rec, rec * sizeof(uint64_t));   /* the walk changes the root's P and X */
+    double en, ec;
+    int d;
+    knuth_walk(&s, &rng, &en, &ec, &d);
+    sn += en; sn2 += en * en; sc += ec; sc2 += ec * ec;
+    if (d > dmax) dmax = d;
+  }
+  sums[0] = sn; sums[1] = sn2; sums[2] = sc; sums[3] = sc2;
+  *max_depth = dmax;
+  free(s.adjP); free(s.colL); free(s.arena); free(root_rec); free(s.L); free(loc);
+  return 0;
+}
+
 /* Small graphs only: like oracle_mce over every root, but writes each maximal
    clique (its ids, sorted ascending) into out, cliques separated by -1.
    Returns the number of int32 written, or -1 if out_cap is too small. */

@@ -317,3 +317,72 @@ def test_validate_classes():
     rp2 = rp.copy(); rp2[u + 1:] -= 1
     assert oracle.validate(g.n, rp2, ci[keep]) == oracle.OV_ASYM
     del row
+
+
+# ---------------------------------------------------------------- subtree size estimate
+# Knuth's random probe (oracle.knuth) sizes the workloads before they are
+# enumerated. On graphs whose pivoted search tree is regular every walk is
+# exact; elsewhere the estimator is unbiased, so its mean over many walks must
+# sit within a few standard errors of the exact enumeration (the oracle,
+# pinned above by brute force and closed forms).
+@pytest.mark.parametrize("g", [mi.moon_moser(15), mi.moon_moser(18), mi.complete_multipartite([3, 3, 3, 3]),
+                               mi.complete_multipartite([2, 2, 2, 2, 2]), mi.complete(9)])
+def test_knuth_exact_on_regular_trees(g):
+    _, rnd, _ = oracle.peel(g.n, g.row_ptr, g.col_idx)
+    total = 0.0
+    for r in range(g.n):
+        e = oracle.knuth(g.n, g.row_ptr, g.col_idx, r, 40, seed=r + 1, rnd=rnd)
+        ex = oracle.mce(g.n, g.row_ptr, g.col_idx, roots=[r], rnd=rnd)
+        assert e.cliques_se == 0 and e.nodes_se == 0      # every walk gives the same product
+        assert e.cliques == ex.count and e.nodes == ex.nodes
+        total += e.cliques
+    # closed forms: 3^(n/3) for Moon-Moser, the product of part sizes for a complete multipartite graph
+    assert total == oracle.mce(g.n, g.row_ptr, g.col_idx).count
+
+
+def test_knuth_moon_moser_closed_form():
+    g = mi.moon_moser(45)
+    e = oracle.knuth(g.n, g.row_ptr, g.col_idx, 0, 8, seed=5)
+    assert e.cliques == 3 ** 14 and e.cliques_se == 0      # the cliques through vertex 0
+    assert e.max_depth == 14                               # one walk ends at a 15-vertex clique
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_knuth_unbiased_against_enumeration(seed):
+    worst, spread = 0.0, 0
+    for n, p in ((40, 0.5), (60, 0.3), (30, 0.7)):
+        g = mi.random_small(n, p, seed)
+        _, rnd, _ = oracle.peel(g.n, g.row_ptr, g.col_idx)
+        for r in range(0, n, 7):
+            e = oracle.knuth(g.n, g.row_ptr, g.col_idx, r, 4000, seed=11 + r, rnd=rnd)
+            ex = oracle.mce(g.n, g.row_ptr, g.col_idx, roots=[r], rnd=rnd)
+            for est, se, exact in ((e.cliques, e.cliques_se, ex.count), (e.nodes, e.nodes_se, ex.nodes)):
+                if se == 0:
+                    assert est == exact
+                else:
+                    spread += 1
+                    worst = max(worst, abs(est - exact) / se)
+    assert spread > 10          # the walks did vary: the test compares means, not single paths
+    assert worst < 6.0
+
+
+@pytest.mark.parametrize("seed,n,p", [(200, 14, 0.5), (201, 18, 0.7), (202, 20, 0.85), (203, 16, 0.3)])
+def test_per_root_runs_add_up_to_brute_force(seed, n, p):
+    """oracle.mce_each (one node budget per subtree) over every root gives the
+    brute-force clique count and hash; a budget below a subtree's size leaves
+    that root unfinished."""
+    g = mi.random_small(n, p, seed)
+    _, rnd, _ = oracle.peel(g.n, g.row_ptr, g.col_idx)
+    roots = np.arange(g.n, dtype=np.int32)
+    nodes, cnt, hsh, done = oracle.mce_each(g.n, g.row_ptr, g.col_idx, roots, 0, rnd)
+    want = brute.brute_maximal_cliques(g.n, g.row_ptr, g.col_idx)
+    wc, wh, _ = brute.set_summary(want)
+    assert done.all()
+    assert int(cnt.sum()) == wc
+    assert int(hsh.sum(dtype=np.uint64)) == wh
+    big = int(np.argmax(nodes))
+    if nodes[big] > 1:
+        _, _, _, d2 = oracle.mce_each(g.n, g.row_ptr, g.col_idx, roots[big:big + 1], int(nodes[big]) - 1, rnd)
+        assert d2[0] == 0
+        _, c3, _, d3 = oracle.mce_each(g.n, g.row_ptr, g.col_idx, roots[big:big + 1], int(nodes[big]), rnd)
+        assert d3[0] == 1 and c3[0] == cnt[big]
