@@ -167,7 +167,7 @@ typedef struct {
   uint64_t max_stack_frames; /* micro kernel: most frames one wavefront's stack held */
   int32_t micro_roots;       /* first-level subtrees searched by the micro kernel */
   int32_t micro_stack_cap;   /* frames per wavefront of the micro kernel's stack in device memory
-                                (4096) */
+                                (4096; mce_run_static: what its scratch had room for, >= 256) */
   uint64_t steps;            /* micro kernel: wavefront steps (each lane holding a frame takes one
                                 node or branch) */
   uint64_t lane_steps;       /* micro kernel: lanes holding a frame, summed over steps */
@@ -221,6 +221,33 @@ mce_status mce_run(mce_engine* e, int32_t n, int64_t nnz, const int32_t* row_ptr
 mce_status mce_run_roots(mce_engine* e, int32_t n, int64_t nnz, const int32_t* row_ptr,
                          const int32_t* col_idx, const int32_t* roots, int32_t nroots,
                          void* stream);
+
+/* Size of the static scratch array of mce_run_static, per device. */
+#define MCE_STATIC_SCRATCH_BYTES (64u << 20)
+
+/* mce_run for callers that cannot allocate (code under HIP graph capture, tight
+   serving loops, harnesses that forbid hipMalloc): the same work and results,
+   but every device buffer of the run (control block, peel lists, root lists,
+   induced-subgraph tables, worker list, wavefront slots and frame stacks,
+   counters) is carved out of one array of MCE_STATIC_SCRATCH_BYTES that the
+   library holds per device in static device memory until the process ends, and
+   the result read-back goes to memory inside the engine. It calls no hipMalloc,
+   hipFree, hipHostMalloc or other allocating routine. The caller still owns the
+   inputs (as for mce_run). Differences from mce_run: second-level runs build no
+   hub adjacency bitmaps (speed only), and the micro kernel's frame stacks get
+   the largest power of two up to 4096 frames per wavefront that the space left
+   holds (mce_run_stats.micro_stack_cap). A graph whose buffers do not fit
+   returns MCE_ERR_LIMIT with the bytes it needs in mce_last_error, before any
+   search; so does a micro stack overflow during the search.
+   Every call on one device shares that device's array and finds it as the
+   last call left it (the run clears what must start at zero). Calls in this
+   process are serialised by a lock; calls that overlap on one device from
+   different processes each use their own process's array. mce_ordering and the
+   per-wave counters of mce_stats / mce_worker_trace read the array, so they
+   describe the last mce_run_static call on the device. The device's array
+   address is looked up by mce_create (MCE_ERR_STATE if that did not happen). */
+mce_status mce_run_static(mce_engine* e, int32_t n, int64_t nnz, const int32_t* row_ptr,
+                          const int32_t* col_idx, void* stream);
 
 /* Results of the last run, on the host. hist (nullable) receives
    hist[0..hist_len); hist_len = largest clique size + 1, or 0 if count == 0.

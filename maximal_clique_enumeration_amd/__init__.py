@@ -27,7 +27,7 @@ MCE_FLAG_SEARCH_TIMES = 32
 MCE_SUBGRAPH_AUTO, MCE_SUBGRAPH_PARTIAL, MCE_SUBGRAPH_FULL = 0, 1, 2
 
 # every function the C header declares
-EXPORTS = ("mce_config_init", "mce_create", "mce_run", "mce_run_roots", "mce_result",
+EXPORTS = ("mce_config_init", "mce_create", "mce_run", "mce_run_roots", "mce_run_static", "mce_result",
            "mce_graph_info", "mce_ordering", "mce_stats", "mce_worker_trace", "mce_last_error",
            "mce_status_string", "mce_destroy")
 
@@ -126,6 +126,7 @@ def load_library():
     lib.mce_create.argtypes = [P(mce_config), P(vp)]
     lib.mce_run.argtypes = [vp, i32, i64, vp, vp, vp]
     lib.mce_run_roots.argtypes = [vp, i32, i64, vp, vp, vp, i32, vp]
+    lib.mce_run_static.argtypes = [vp, i32, i64, vp, vp, vp]
     lib.mce_result.argtypes = [vp, P(ctypes.c_uint64), P(ctypes.c_uint64), P(ctypes.c_uint64), i32, P(i32)]
     lib.mce_graph_info.argtypes = [vp, P(mce_graph_facts)]
     lib.mce_ordering.argtypes = [vp, vp, vp, vp]
@@ -137,7 +138,7 @@ def load_library():
     lib.mce_status_string.restype = ctypes.c_char_p
     lib.mce_destroy.argtypes = [vp]
     lib.mce_destroy.restype = None
-    for name in ("mce_config_init", "mce_create", "mce_run", "mce_run_roots", "mce_result",
+    for name in ("mce_config_init", "mce_create", "mce_run", "mce_run_roots", "mce_run_static", "mce_result",
                  "mce_graph_info", "mce_ordering", "mce_stats"):
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
@@ -159,6 +160,10 @@ def mce_run(engine, n, nnz, row_ptr, col_idx, stream) -> int:
 
 def mce_run_roots(engine, n, nnz, row_ptr, col_idx, roots, nroots, stream) -> int:
     return load_library().mce_run_roots(engine, n, nnz, row_ptr, col_idx, roots, nroots, stream)
+
+
+def mce_run_static(engine, n, nnz, row_ptr, col_idx, stream) -> int:
+    return load_library().mce_run_static(engine, n, nnz, row_ptr, col_idx, stream)
 
 
 def mce_result(engine, count, hash_, hist, hist_cap, hist_len) -> int:
@@ -294,6 +299,18 @@ class Engine:
         for name, t in (("row_ptr", row_ptr), ("col_idx", col_idx)):
             if t.dtype != torch.int32 or not t.is_cuda or not t.is_contiguous():
                 raise ValueError(f"{name} must be a contiguous int32 CUDA tensor")
+
+    def run_static(self, row_ptr, col_idx, stream=None) -> Result:
+        """mce_run_static: the whole graph, every device buffer carved from the
+        library's static scratch (no allocation)."""
+        import torch
+        self._check_csr(row_ptr, col_idx)
+        if stream is None:
+            stream = torch.cuda.current_stream(row_ptr.device)
+        st = mce_run_static(self._h, row_ptr.numel() - 1, col_idx.numel(), _ptr(row_ptr), _ptr(col_idx),
+                            ctypes.c_void_p(stream.cuda_stream))
+        self._check(st, "mce_run_static", self._h)
+        return self.result()
 
     def run(self, row_ptr, col_idx, roots=None, stream=None, partial_ok: bool = False) -> Result:
         """Enumerate all maximal cliques (or those of the first-level subtrees of

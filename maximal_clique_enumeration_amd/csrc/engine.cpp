@@ -203,6 +203,37 @@ constexpr int kMicroCoopRootsPerWave = 4;     // micro launches with this many r
 // dealt over several blocks, about this many (root, part) blocks per CU.
 constexpr int kSplitBlocksPerCu = 16;
 
+// ------------------------------------------------------------------ static scratch
+// The device memory of mce_run_static: one array per device, holding every
+// buffer of a run (partial results, counters, queues, stacks, tables), kept
+// until the process ends. In host code `scratch` names a host-side stand-in,
+// not device memory: its device address comes from hipGetSymbolAddress, once
+// per device (mce_create, with that device current), and only that address is
+// used (kernel arguments, clears).
+constexpr int kMaxDevices = 64;
+void* g_scratch_ptr[kMaxDevices] = {};
+std::mutex g_scratch_mu;      // guards g_scratch_ptr
+std::mutex g_static_run_mu;   // held by every mce_run_static call
+
+}  // namespace
+
+static __device__ __align__(256) unsigned char scratch[MCE_STATIC_SCRATCH_BYTES];
+
+namespace {
+
+hipError_t scratch_address(int dev, void** out) {
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    const hipError_t h = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (h != hipSuccess) return h;
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
+}
+
 // One run. `arena` empty: the engine's own buffers (grown with hipMalloc);
 // else every buffer is carved from the static scratch and nothing is allocated.
 mce_status run_impl(mce_engine* e, int32_t n, int64_t nnz, const int32_t* row_ptr, const int32_t* col_idx,
@@ -793,6 +824,12 @@ mce_status mce_create(const mce_config* cfg, mce_engine** out) {
     e->tick_hz = (double)khz * 1e3;
   e->num_cu = cus;
   e->peel_blocks_max = mce_peel_max_blocks(cus);
+  // the static scratch's device address, once per device, with the device current
+  void* sp = nullptr;
+  if (scratch_address(dev, &sp) != hipSuccess) {
+    delete e;
+    return MCE_ERR_DEVICE;
+  }
   e->have_events = true;
   for (auto& ev : e->ev)
     if (hipEventCreate(&ev) != hipSuccess) e->have_events = false;
@@ -810,6 +847,19 @@ mce_status mce_run_roots(mce_engine* e, int32_t n, int64_t nnz, const int32_t* r
                          const int32_t* roots, int32_t nroots, void* stream) {
   Arena own;
   return run_impl(e, n, nnz, row_ptr, col_idx, roots, nroots, true, stream, own);
+}
+
+mce_status mce_run_static(mce_engine* e, int32_t n, int64_t nnz, const int32_t* row_ptr, const int32_t* col_idx,
+                          void* stream) {
+  if (!e) return MCE_ERR_ARG;
+  if (e->device < 0 || e->device >= kMaxDevices || !g_scratch_ptr[e->device])
+    return fail(e, MCE_ERR_STATE, "the static scratch of device %d was not set up by mce_create", e->device);
+  // one run at a time per process: every run on a device shares its scratch
+  std::lock_guard<std::mutex> lk(g_static_run_mu);
+  Arena a;
+  a.base = static_cast<char*>(g_scratch_ptr[e->device]);
+  a.cap = MCE_STATIC_SCRATCH_BYTES;
+  return run_impl(e, n, nnz, row_ptr, col_idx, nullptr, 0, false, stream, a);
 }
 
 mce_status mce_result(const mce_engine* e, uint64_t* count, uint64_t* hash, uint64_t* hist, int32_t hist_cap,
