@@ -380,12 +380,16 @@ def kernel_table(g, cst, ctrace, stats, events, counters, nnz):
             traffic = c.get("fetch_bytes", 0) + c.get("write_bytes", 0)
             r["traffic"] = traffic
             r["hbm_frac"] = traffic / sec / HBM_PEAK
-            if "sq_insts_lds" in c:
-                # every LDS instruction of a wave64 moves at most 64 lanes x 8 bytes
-                r["lds_frac_upper"] = c["sq_insts_lds"] * 64 * 8 / sec / LDS_PEAK
+            if "lds_bytes" in c:
+                # LDS bytes moved (SQ_INSTS_LDS_{LOAD,STORE,ATOMIC}_BANDWIDTH, 64-byte units)
+                r["lds_bytes"] = c["lds_bytes"]
+                r["lds_frac"] = c["lds_bytes"] / sec / LDS_PEAK
             if "sq_insts_valu" in c:
                 # a wave64 VALU instruction holds a 16-lane SIMD for 4 cycles
                 r["valu_issue_frac"] = c["sq_insts_valu"] * 4 / (NUM_CU * 4 * CLOCK_HZ * sec)
+            if "sq_insts_salu" in c:
+                # one scalar instruction per CU and cycle
+                r["salu_issue_frac"] = c["sq_insts_salu"] / (NUM_CU * CLOCK_HZ * sec)
     return rows
 
 
@@ -395,7 +399,7 @@ def roofline_of(rows):
     out = {"bound": top["bound"], "achieved": top.get("achieved"), "peak": top.get("peak"), "unit": unit,
            "frac": top.get("frac"), "traffic": top.get("traffic"), "kernel": top["kernel"],
            "launch_ms": top["ms"], "algorithmic_per_launch": top["algorithmic"]}
-    for k in ("hbm_frac", "lds_frac_upper", "valu_issue_frac", "launch"):
+    for k in ("hbm_frac", "lds_frac", "valu_issue_frac", "salu_issue_frac", "launch"):
         if k in top:
             out[k] = top[k]
     return out
