@@ -68,6 +68,12 @@ def parse():
     ap.add_argument("--cap-ms", type=int, default=0,
                     help="time-capped whole-graph run: the search stops at this limit and the cliques found "
                          "by then are counted (partial: no parity)")
+    ap.add_argument("--whole-chunks", type=int, default=0,
+                    help="whole graph in this many pieces (mce_run_roots): the roots the oracle finishes within "
+                         "its budget first, then the heavy roots packed by their estimated subtree sizes; each "
+                         "piece prints its result as it ends (configurations with a light set in configs.json)")
+    ap.add_argument("--chunk-cap-ms", type=int, default=150000, help="time limit of one piece (--whole-chunks)")
+    ap.add_argument("--first-chunk", type=int, default=0, help="resume --whole-chunks at this piece")
     ap.add_argument("--level", type=int, choices=[1, 2], default=1,
                     help="first-level (1, default) or second-level (2) subtrees")
     ap.add_argument("--subgraph", choices=["auto", "partial", "full"], default="auto",
@@ -405,6 +411,62 @@ def roofline_of(rows):
     return out
 
 
+def whole_in_chunks(mce, torch, g, args, rp, ci, dev):
+    """The whole graph as a sequence of mce_run_roots calls over disjoint root
+    sets: first-level subtrees are independent (section 2.4), so the pieces'
+    counts, histograms and hashes add up to the whole graph's. Piece 0 holds the
+    roots whose subtrees the oracle finished within its budget (its sums are
+    compared with the oracle's); the heavy roots follow, packed into pieces of
+    about equal estimated size (Knuth's estimate, tests/golden/configs.json)."""
+    import numpy as np
+    with open(os.path.join(ROOT, "tests", "golden", "configs.json")) as f:
+        gold = json.load(f)[str(args.config)]
+    light = gold["light"]
+    heavy = np.asarray(light["heavy_roots"], np.int64)
+    est = np.asarray(light["heavy_est_nodes"], np.float64)
+    k = max(1, args.whole_chunks - 1)
+    order = np.argsort(-est, kind="stable")
+    pieces = [[] for _ in range(k)]
+    load = np.zeros(k)
+    for i in order:                       # largest first, into the lightest piece
+        j = int(np.argmin(load))
+        pieces[j].append(int(heavy[i]))
+        load[j] += est[i]
+    mask = np.ones(g.n, bool)
+    mask[heavy] = False
+    plan = [np.flatnonzero(mask).astype(np.int32)] + [np.asarray(sorted(pc), np.int32) for pc in pieces if pc]
+    results, times, completes = [], [], []
+    total_cnt, total_hash, hist = 0, 0, []
+    eng = mce.Engine(device=0, timeout_ms=args.chunk_cap_ms, level=args.level, subgraph=args.subgraph)
+    for i, roots in enumerate(plan):
+        if i < args.first_chunk:
+            continue
+        rt = torch.from_numpy(roots).to(dev)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        r = eng.run(rp, ci, roots=rt, partial_ok=True)
+        torch.cuda.synchronize()
+        dt = time.perf_counter() - t0
+        ok = None
+        if i == 0:
+            ok = (r.count, f"0x{r.hash:016x}", r.hist) == (light["count"], light["hash"], light["hist"])
+        rec = {"piece": i, "roots": int(roots.size), "count": r.count, "hash": f"0x{r.hash:016x}",
+               "complete": r.complete, "s": dt, "est_nodes": float(est[np.isin(heavy, roots)].sum()) if i else None,
+               "matches_oracle": ok}
+        print("bench: piece " + json.dumps(rec), file=sys.stderr, flush=True)
+        results.append(rec)
+        times.append(dt)
+        completes.append(r.complete)
+        total_cnt += r.count
+        total_hash = (total_hash + r.hash) % (1 << 64)
+        hist = [a + b for a, b in zip(hist + [0] * (len(r.hist) - len(hist)), r.hist + [0] * (len(hist) - len(r.hist)))]
+    info = eng.graph_info()
+    eng.close()
+    return {"pieces": results, "count": total_cnt, "hash": f"0x{total_hash:016x}", "hist": hist,
+            "seconds": sum(times), "complete": all(completes) and args.first_chunk == 0, "info": info,
+            "npieces": len(plan)}
+
+
 def workload_label(args):
     parts = [f"cfg{args.config}"]
     if args.sample:
@@ -450,6 +512,32 @@ def main():
         torch.cuda.synchronize()
         dst.copy_(src)
     torch.cuda.synchronize()
+    if args.whole_chunks:
+        print(f"bench: whole graph in pieces", file=sys.stderr, flush=True)
+        w = whole_in_chunks(mce, torch, g, args, rp, ci, dev)
+        feas = None
+        fpath = os.path.join(ROOT, "tests", "golden", "feasibility.json")
+        if os.path.exists(fpath):
+            with open(fpath) as f:
+                feas = json.load(f).get(str(args.config))
+        out = {"metric": "maximal cliques/sec and end-to-end MCE time per graph on 1 MI355X",
+               "value": w["count"] / w["seconds"] if w["seconds"] else None, "unit": "maximal cliques/s",
+               "n_gpus": 1, "steps": 1, "warmup": 0, "ms_per_step": w["seconds"] * 1e3,
+               "higher_is_better": True, "scaling": "strong", "vs_baseline": None,
+               "dtype": "u64 bitsets / int32 ids",
+               "data": ("synthetic (seeded generator); whole graph as independent pieces of first-level "
+                        "subtrees; parity: piece 0 against the oracle, the rest against its estimate only"),
+               "config": {"workload": g.name, "n": g.n, "edges": g.m, "maximal_cliques": w["count"],
+                          "complete": w["complete"], "pieces": w["npieces"], "hash": w["hash"],
+                          "degeneracy": w["info"]["degeneracy"], "max_degree": w["info"]["max_degree"]},
+               "detail": {"hist": w["hist"], "pieces": w["pieces"],
+                          "oracle_estimate": ({"cliques": feas["total_cliques_est"],
+                                               "cliques_se": feas["heavy_cliques_se"],
+                                               "z": (w["count"] - feas["total_cliques_est"]) / feas["heavy_cliques_se"]
+                                               if feas["heavy_cliques_se"] else None} if feas else None)},
+               "roofline": None, "cpu_baseline": None}
+        print(json.dumps(out), flush=True)
+        return
     events = args.events
     if events == "auto":
         events = "search" if args.config in (0, 1) else "phase"

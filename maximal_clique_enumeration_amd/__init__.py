@@ -119,6 +119,10 @@ def load_library():
     if not os.path.exists(LIB_PATH):
         raise MceLibraryMissing(f"{LIB_PATH} is not built; run __graft_entry__.build() or "
                                 "python -m maximal_clique_enumeration_amd.build")
+    # torch first: the library then binds to the HIP runtime torch loaded. Loaded
+    # the other way round, the process holds two HIP runtimes, and the one the
+    # library uses may find no device.
+    import torch  # noqa: F401
     lib = ctypes.CDLL(LIB_PATH)
     vp, i32, i64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
     P = ctypes.POINTER

@@ -14,7 +14,15 @@ a failing check, not as a silent mismatch) and:
     exactly the kept roots). The whole R-MAT and large Chung-Lu graphs have too
     many maximal cliques to enumerate in a test.
 
-Run from the repository root:  python tests/golden/make_configs.py
+Configurations 2 and 4 also get, with --light (multi-process oracle runs):
+  - "light": every root whose subtree the oracle finishes within LIGHT_BUDGET
+    nodes (stored as the list of the other, "heavy" roots), with the count,
+    hash and histogram of their cliques: all of the graph but its dense core;
+  - "dense": heavy roots of the largest |P| whose subtrees the oracle finishes
+    within DENSE_BUDGET nodes (Knuth's estimate picks the candidates first).
+
+Run from the repository root:  python tests/golden/make_configs.py [config ...]
+                               python tests/golden/make_configs.py --light 2 4
 """
 from __future__ import annotations
 
@@ -40,6 +48,12 @@ HEAVY_POOL = 20_000       # the roots of largest |P| ...
 N_HEAVY_TRY = 150         # ... of which this many, evenly spaced from the largest down, are tried
 N_HEAVY_KEEP = 60         # heavy roots kept
 HEAVY_BUDGET = 1_000_000  # oracle search-tree nodes allowed per heavy root
+LIGHT_BUDGET = 200_000    # nodes per root of the "light" set
+DENSE_BUDGET = 20_000_000  # nodes per root of the "dense" sample
+DENSE_KEEP = 40           # dense roots kept
+DENSE_WALKS = 16          # Knuth walks per dense candidate
+PROCS = min(8, os.cpu_count() or 1)
+_G = {}
 
 
 def later_counts(g, rnd):
@@ -53,12 +67,91 @@ def entry(res):
     return {"count": res.count, "hash": f"0x{res.hash:016x}", "hist": res.hist}
 
 
+def _each(args):
+    roots, budget = args
+    g, rnd = _G["g"], _G["rnd"]
+    nodes, _, _, done = oracle.mce_each(g.n, g.row_ptr, g.col_idx, roots, budget, rnd)
+    return roots, nodes, done
+
+
+def _sum(roots):
+    g, rnd = _G["g"], _G["rnd"]
+    r = oracle.mce(g.n, g.row_ptr, g.col_idx, roots=roots, rnd=rnd)
+    assert r.complete
+    return r.count, r.hash, r.hist
+
+
+def _probe(root):
+    g, rnd = _G["g"], _G["rnd"]
+    return root, oracle.knuth(g.n, g.row_ptr, g.col_idx, int(root), DENSE_WALKS, seed=7000 + int(root), rnd=rnd)
+
+
+def add_up(parts):
+    cnt = sum(c for c, _, _ in parts)
+    hsh = sum(h for _, h, _ in parts) % (1 << 64)
+    hl = max((len(h) for _, _, h in parts), default=0)
+    hist = [sum(h[k] for _, _, h in parts if k < len(h)) for k in range(hl)]
+    return {"count": cnt, "hash": f"0x{hsh:016x}", "hist": hist}
+
+
+def light_and_dense(idx, rec):
+    """The light set (all roots but the heavy ones) and the dense sample."""
+    import multiprocessing as mp
+    t0 = time.time()
+    g = mi.config_graph(idx)
+    assert g.sha256() == rec["sha256"]
+    _, rnd, _ = oracle.peel(g.n, g.row_ptr, g.col_idx)
+    _G["g"], _G["rnd"] = g, rnd
+    p = later_counts(g, rnd)
+    x = g.degrees() - p
+    nch = max(1, g.n // 4096)
+    order = np.argsort(-(p.astype(np.int64) * (x + p)), kind="stable").astype(np.int32)
+    with mp.get_context("fork").Pool(PROCS) as pool:   # the workers share the graph
+        done = np.zeros(g.n, bool)
+        for roots, _, dn in pool.imap_unordered(_each, [(order[i::nch], LIGHT_BUDGET) for i in range(nch)]):
+            done[roots] = dn.astype(bool)
+        heavy = np.flatnonzero(~done).astype(np.int32)
+        light = np.flatnonzero(done).astype(np.int32)
+        print(idx, "light", light.size, "heavy", heavy.size, round(time.time() - t0), flush=True)
+        parts = pool.map(_sum, [light[i::nch] for i in range(nch)])
+        rec["light"] = {"budget": LIGHT_BUDGET, "roots": int(light.size), "heavy_roots": heavy.tolist(),
+                        "max_p": int(p[light].max()), "max_x": int(x[light].max()),
+                        "roots_x_ge_10000": int((x[light] >= 10000).sum()),
+                        "roots_p_ge_300": int((p[light] >= 300).sum()), **add_up(parts)}
+        print(idx, "light done", round(time.time() - t0), flush=True)
+        # dense: the heavy roots of largest |P| that fit DENSE_BUDGET, by estimate first
+        cand = heavy[np.argsort(-p[heavy], kind="stable")]
+        est = dict(pool.map(_probe, [int(r) for r in cand]))
+        fit = [r for r in cand if est[int(r)].nodes <= DENSE_BUDGET / 4][: 3 * DENSE_KEEP]
+        kept = []
+        for roots, nodes, dn in pool.imap(_each, [(np.array([r], np.int32), DENSE_BUDGET) for r in fit]):
+            if dn[0]:
+                kept.append(int(roots[0]))
+        kept = sorted(kept, key=lambda r: -p[r])[:DENSE_KEEP]
+        dense = np.array(sorted(kept), np.int32)
+        parts = pool.map(_sum, [dense[i::PROCS] for i in range(PROCS) if dense[i::PROCS].size])
+        # every heavy root's estimated subtree size (nodes), to plan whole-graph runs in pieces
+        rec["light"]["heavy_est_nodes"] = [round(est[int(r)].nodes) for r in heavy]
+        rec["dense"] = {"budget": DENSE_BUDGET, "roots": dense.tolist(),
+                        "p_range": [int(p[dense].min()), int(p[dense].max())] if dense.size else None,
+                        "x_range": [int(x[dense].min()), int(x[dense].max())] if dense.size else None,
+                        "candidates_fitting_estimate": len(fit), **add_up(parts)}
+    print(idx, "dense", dense.size, rec["dense"]["p_range"], rec["dense"]["x_range"], round(time.time() - t0),
+          flush=True)
+
+
 def main():
     out = {}
     path = os.path.join(HERE, "configs.json")
     if os.path.exists(path):
         with open(path) as f:
             out = json.load(f)
+    if sys.argv[1:2] == ["--light"]:
+        for idx in [int(a) for a in sys.argv[2:]] or list(SAMPLED):
+            light_and_dense(idx, out[str(idx)])
+            with open(path, "w") as f:
+                json.dump(out, f, indent=1)
+        return
     which = [int(a) for a in sys.argv[1:]] or list(WHOLE + SAMPLED)
     for idx in which:
         t0 = time.time()
