@@ -82,6 +82,8 @@ def parse():
     ap.add_argument("--events", choices=["auto", "phase", "search"], default="auto",
                     help="events in the timed runs: around every phase and launch, or around the search "
                          "launches only (auto: search only for graphs whose run takes about a millisecond)")
+    ap.add_argument("--serial", action="store_true",
+                    help="sub-class launches one after another on one stream (default: overlapped)")
     ap.add_argument("--seed", type=int, default=1)
     ap.add_argument("--cpu-seconds", type=float, default=20.0, help="budget of the oracle baseline")
     ap.add_argument("--cpu-procs", type=int, default=0, help="oracle processes (0: min(16, host cores))")
@@ -313,12 +315,12 @@ def measure(mce, torch, g, args, rp, ci, roots, events, steps, warmup, cap_ms=0)
         ref, cst, ctrace = None, None, []   # a stopped run's work is not the workload's: no counting run
     else:
         with mce.Engine(device=0, counters=True, timeout_ms=timeout, level=args.level,
-                        subgraph=args.subgraph) as ecnt:
+                        subgraph=args.subgraph, overlap=not args.serial) as ecnt:
             ref = ecnt.run(rp, ci, roots=roots)
             cst = ecnt.stats()
             ctrace = ecnt.worker_trace()
     eng = mce.Engine(device=0, timeout_ms=timeout, level=args.level, subgraph=args.subgraph,
-                     search_times=events == "search", phase_times=events == "phase")
+                     search_times=events == "search", phase_times=events == "phase", overlap=not args.serial)
     for _ in range(warmup):
         r = eng.run(rp, ci, roots=roots, partial_ok=bool(cap_ms))
         if not cap_ms and r.key() != ref.key():
@@ -437,7 +439,8 @@ def whole_in_chunks(mce, torch, g, args, rp, ci, dev):
     plan = [np.flatnonzero(mask).astype(np.int32)] + [np.asarray(sorted(pc), np.int32) for pc in pieces if pc]
     results, times, completes = [], [], []
     total_cnt, total_hash, hist = 0, 0, []
-    eng = mce.Engine(device=0, timeout_ms=args.chunk_cap_ms, level=args.level, subgraph=args.subgraph)
+    eng = mce.Engine(device=0, timeout_ms=args.chunk_cap_ms, level=args.level, subgraph=args.subgraph,
+                     overlap=not args.serial)
     for i, roots in enumerate(plan):
         if i < args.first_chunk:
             continue
@@ -578,7 +581,7 @@ def main():
                    "parallelism": "single GPU: one search-tree node per lane (micro kernel) or one subtree "
                                   "per wavefront, branch requests between wavefronts",
                    "seed": args.seed, "sample": args.sample or "whole graph", "subtrees": f"level {args.level}",
-                   "cap_ms": args.cap_ms or None},
+                   "launches": "serial" if args.serial else "overlapped", "cap_ms": args.cap_ms or None},
         "roofline": roofline_of(rows),
         "detail": {"e2e_ms_min": min(times) * 1e3, "e2e_ms_median": sorted(times)[len(times) // 2] * 1e3,
                    "hash": hex(last.hash), "events": events,

@@ -84,6 +84,14 @@ typedef enum {
                                     launch_search_ms; the other phase times stay 0): the light form of
                                     MCE_FLAG_PHASE_TIMES for timing loops, since every recorded event
                                     costs the stream a few microseconds */
+#define MCE_FLAG_SERIAL 64u      /* run the sub-class launches (build, then search) one after another on
+                                    the caller's stream, reusing one table heap. By default each
+                                    sub-class has its own heap region and its build and search run on
+                                    one of the engine's own streams, forked from and joined back to the
+                                    caller's stream, so that the launches overlap (a build, which waits
+                                    on memory, beside another sub-class's search). mce_run_static always
+                                    runs them in series. The results are the same either way. */
+#define MCE_SIDE_STREAMS 4       /* the engine's own streams for the overlapped launches */
 
 /* mce_config.subgraph: how each subtree's induced subgraph is encoded (section
    3.4). Partial: bit rows for P x P only, edges between P and X looked up in the
@@ -199,6 +207,8 @@ mce_status mce_config_init(mce_config* cfg);
 
 /* Creates an engine on cfg->device (cfg may be NULL for the defaults). The engine
    owns all device scratch memory; it grows on demand and is freed by mce_destroy.
+   It also creates MCE_SIDE_STREAMS non-blocking streams of default priority
+   (the overlapped search launches), destroyed by mce_destroy.
    On success *out receives the engine. MCE_ERR_ARG for a field out of range or a
    flag outside MCE_FLAG_*. */
 mce_status mce_create(const mce_config* cfg, mce_engine** out);
@@ -208,7 +218,9 @@ mce_status mce_create(const mce_config* cfg, mce_engine** out);
    col_idx int32[nnz], every row sorted strictly ascending, both directions of
    each edge present. The caller owns both arrays; they must stay valid and
    unchanged until the call returns. Work is queued on `stream` (a hipStream_t;
-   NULL = the null stream) and the call returns after it completes. n == 0 is
+   NULL = the null stream; the search launches fork onto the engine's own
+   streams and join back, see MCE_FLAG_SERIAL) and the call returns after it
+   completes. n == 0 is
    valid (count 0). nnz must be < 2^31. Results are read with mce_result. */
 mce_status mce_run(mce_engine* e, int32_t n, int64_t nnz, const int32_t* row_ptr,
                    const int32_t* col_idx, void* stream);

@@ -24,6 +24,7 @@ MCE_ERR_DEVICE, MCE_ERR_STATE, MCE_ERR_TIMEOUT, MCE_ERR_LIMIT = -4, -5, -6, -7
 MCE_GRAPH_ROWPTR, MCE_GRAPH_RANGE, MCE_GRAPH_LOOP, MCE_GRAPH_ORDER, MCE_GRAPH_ASYM = 1, 2, 4, 8, 16
 MCE_FLAG_HBM_STAGING, MCE_FLAG_PHASE_TIMES, MCE_FLAG_COUNTERS, MCE_FLAG_NO_MICRO, MCE_FLAG_L2 = 1, 2, 4, 8, 16
 MCE_FLAG_SEARCH_TIMES = 32
+MCE_FLAG_SERIAL = 64
 MCE_SUBGRAPH_AUTO, MCE_SUBGRAPH_PARTIAL, MCE_SUBGRAPH_FULL = 0, 1, 2
 
 # every function the C header declares
@@ -246,7 +247,7 @@ class Engine:
                  validate: bool = True, max_workers: int = 0, timeout_ms: int = 120000,
                  hbm_staging: bool = False, phase_times: bool = False, subgraph: str = "auto",
                  counters: bool = False, micro: bool = True, micro_donate_min_p: int = 10, level: int = 1,
-                 search_times: bool = False):
+                 search_times: bool = False, overlap: bool = True):
         import torch
         if device is None:
             device = torch.cuda.current_device()
@@ -264,7 +265,8 @@ class Engine:
             raise ValueError("level is 1 (first-level subtrees) or 2 (second-level subtrees)")
         cfg.flags = ((MCE_FLAG_HBM_STAGING if hbm_staging else 0) | (MCE_FLAG_PHASE_TIMES if phase_times else 0)
                      | (MCE_FLAG_COUNTERS if counters else 0) | (0 if micro else MCE_FLAG_NO_MICRO)
-                     | (MCE_FLAG_L2 if level == 2 else 0) | (MCE_FLAG_SEARCH_TIMES if search_times else 0))
+                     | (MCE_FLAG_L2 if level == 2 else 0) | (MCE_FLAG_SEARCH_TIMES if search_times else 0)
+                     | (0 if overlap else MCE_FLAG_SERIAL))
         modes = {"auto": MCE_SUBGRAPH_AUTO, "partial": MCE_SUBGRAPH_PARTIAL, "full": MCE_SUBGRAPH_FULL}
         if subgraph not in modes:
             raise ValueError(f"subgraph must be one of {sorted(modes)}")

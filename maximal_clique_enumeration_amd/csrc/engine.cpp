@@ -71,6 +71,11 @@ struct mce_engine {
   alignas(64) unsigned char host_io[kIoBytes];   // the same for mce_run_static (pageable)
   hipEvent_t ev[4 + 4 * MCE_NSUB] = {};
   bool have_events = false;
+  // the overlapped search launches: streams forked from the caller's stream
+  // (fork_ev) and joined back to it (join_ev)
+  hipStream_t side[MCE_SIDE_STREAMS] = {};
+  hipEvent_t fork_ev = nullptr;
+  hipEvent_t join_ev[MCE_SIDE_STREAMS] = {};
 
   // last run
   bool have_result = false;
@@ -281,6 +286,9 @@ mce_status run_impl(mce_engine* e, int32_t n, int64_t nnz, const int32_t* row_pt
   const bool stimes = (timing || (e->cfg.flags & MCE_FLAG_SEARCH_TIMES)) && e->have_events;
   const bool hbm = (e->cfg.flags & MCE_FLAG_HBM_STAGING) != 0;
   const u64 budget = (u64)((double)e->cfg.timeout_ms * 1e-3 * e->tick_hz);
+  // sub-class launches overlapped on the engine's streams, each with its own
+  // heap region, worker list and slots; else one after another, sharing them
+  const bool overlap = !stat && (e->cfg.flags & MCE_FLAG_SERIAL) == 0;
 
   size_t nb = (size_t)n * sizeof(int);
   if ((h = take(arena, B.ctl, kIoBytes)) != hipSuccess || (h = take(arena, B.deg, nb)) != hipSuccess ||
@@ -290,7 +298,7 @@ mce_status run_impl(mce_engine* e, int32_t n, int64_t nnz, const int32_t* row_pt
       (h = take(arena, B.bfront0, nb)) != hipSuccess || (h = take(arena, B.bfront1, nb)) != hipSuccess ||
       (h = take(arena, B.pcount, (size_t)std::max(cnt, 1) * sizeof(int))) != hipSuccess ||
       (h = take(arena, B.xcount, (size_t)std::max(cnt, 1) * sizeof(int))) != hipSuccess ||
-      (h = take(arena, B.wl, sizeof(MceWl))) != hipSuccess)
+      (h = take(arena, B.wl, sizeof(MceWl) * (overlap ? MCE_NSUB : 1))) != hipSuccess)
     return alloc_fail(e, arena, h, "allocation");
   if (!stat && (h = ensure_host(e->host, kIoBytes)) != hipSuccess) return hip_fail(e, h, "allocation");
   // second-level subtrees (section 3.2): the roots are the vertex roots' forward edges
@@ -406,18 +414,25 @@ mce_status run_impl(mce_engine* e, int32_t n, int64_t nnz, const int32_t* row_pt
   SubOffsets off{};
   int counts[MCE_NSUB];
   int total = 0;
-  size_t heap_words = 0;
+  size_t heap_words = 0;            // in series: the largest sub-class's tables; overlapped: all of them
+  size_t heap_base[MCE_NSUB] = {};  // a sub-class's region (overlapped)
   for (int c = 0; c < MCE_NSUB; c++) {
     counts[c] = hctl->sub_count[var][c];
     off.off[c] = total;
     total += counts[c];
-    heap_words = std::max(heap_words, (size_t)hctl->sub_words[var][c]);
+    if (overlap) {
+      heap_base[c] = heap_words;
+      heap_words += (size_t)hctl->sub_words[var][c];
+    } else {
+      heap_words = std::max(heap_words, (size_t)hctl->sub_words[var][c]);
+    }
   }
   const u64 iso = hctl->isolated, iso_hash = hctl->isolated_hash;
 
   // launch plan, heaviest width first; every buffer sized before any launch
   struct Plan {
     int sub, nw;
+    size_t slot_off;   // its wavefront slots in B.slots (bytes)
     SearchLayout L;
   };
   Plan plan[MCE_NSUB];
@@ -447,8 +462,14 @@ mce_status run_impl(mce_engine* e, int32_t n, int64_t nnz, const int32_t* row_pt
     if (e->cfg.max_workers > 0) nw = std::min(nw, (int)e->cfg.max_workers);
     if (!e->cfg.worker_list) nw = std::min(nw, counts[c]);
     pl.nw = nw;
-    if (c == MCE_SUB_MICRO) micro_nw = nw;
-    else slot_bytes = std::max(slot_bytes, pl.L.slot_bytes * (size_t)nw);
+    if (c == MCE_SUB_MICRO) {
+      micro_nw = nw;
+    } else if (overlap) {
+      pl.slot_off = slot_bytes;
+      slot_bytes += (pl.L.slot_bytes * (size_t)nw + 255) & ~(size_t)255;
+    } else {
+      slot_bytes = std::max(slot_bytes, pl.L.slot_bytes * (size_t)nw);
+    }
     stat_rows += nw;
     plan[nplan++] = pl;
   }
@@ -485,12 +506,36 @@ mce_status run_impl(mce_engine* e, int32_t n, int64_t nnz, const int32_t* row_pt
   }
   if (timing) (void)hipEventRecord(e->ev[3], s);
 
+  // Overlapped: launch pi (its build, worker-list init and search) runs on side
+  // stream pi mod MCE_SIDE_STREAMS, after everything queued on s so far, and s
+  // waits for every side stream used before the read-back.
+  bool side_used[MCE_SIDE_STREAMS] = {};
+  auto launch_fail = [&](hipError_t herr, const char* what) {
+    if (overlap)   // leave no launch of this run behind on a side stream
+      for (int k = 0; k < MCE_SIDE_STREAMS; k++)
+        if (side_used[k]) (void)hipStreamSynchronize(e->side[k]);
+    return hip_fail(e, herr, what);
+  };
+  if (overlap && nplan > 0 && (h = hipEventRecord(e->fork_ev, s)) != hipSuccess) return hip_fail(e, h, "fork");
+
   int launches = 0, max_workers_used = 0, stat_off = 0;
   int evi = 4;
   for (int pi = 0; pi < nplan; pi++) {
     const Plan& pl = plan[pi];
     const int c = pl.sub;
     const SearchLayout& L = pl.L;
+    hipStream_t ls = s;
+    if (overlap) {
+      const int k = pi % MCE_SIDE_STREAMS;
+      ls = e->side[k];
+      if (!side_used[k]) {
+        if ((h = hipStreamWaitEvent(ls, e->fork_ev, 0)) != hipSuccess) return launch_fail(h, "fork");
+        side_used[k] = true;
+      }
+    }
+    u64* heap = dp<u64>(B.heap) + heap_base[c];
+    const size_t hwords = overlap ? (size_t)hctl->sub_words[var][c] : heap_words;
+    MceWl* wl = dp<MceWl>(B.wl) + (overlap ? pi : 0);
     BuildParams bp{};
     bp.rp = row_ptr;
     bp.ci = col_idx;
@@ -501,8 +546,8 @@ mce_status run_impl(mce_engine* e, int32_t n, int64_t nnz, const int32_t* row_pt
     bp.W = micro ? 1 : 1 << L.wclass;
     bp.mode = micro ? MCE_MODE_IPX : mode;
     bp.micro = micro ? 1 : 0;
-    bp.heap = dp<u64>(B.heap);
-    bp.heap_words = heap_words;
+    bp.heap = heap;
+    bp.heap_words = hwords;
     bp.tab_off = dp<u64>(B.taboff) + off.off[c];
     bp.status = &ctl->status;
     bp.l2 = l2 ? 1 : 0;
@@ -517,15 +562,14 @@ mce_status run_impl(mce_engine* e, int32_t n, int64_t nnz, const int32_t* row_pt
       const int want = (kSplitBlocksPerCu * e->num_cu + counts[c] - 1) / counts[c];
       bp.parts = std::max(1, std::min(std::max(want, (nslab + 7) / 8), nslab));
     }
-    if (timing) (void)hipEventRecord(e->ev[evi], s);
-    if ((h = mce_launch_build(bp, e->num_cu * 32, s)) != hipSuccess) return hip_fail(e, h, "build launch");
-    if (timing) (void)hipEventRecord(e->ev[evi + 1], s);
-    if ((h = mce_launch_wl_init(dp<MceWl>(B.wl), pl.nw, dp<u64>(B.stats) + (size_t)stat_off * MCE_NSTAT, s)) !=
-        hipSuccess)
-      return hip_fail(e, h, "wl init");
+    if (timing) (void)hipEventRecord(e->ev[evi], ls);
+    if ((h = mce_launch_build(bp, e->num_cu * 32, ls)) != hipSuccess) return launch_fail(h, "build launch");
+    if (timing) (void)hipEventRecord(e->ev[evi + 1], ls);
+    if ((h = mce_launch_wl_init(wl, pl.nw, dp<u64>(B.stats) + (size_t)stat_off * MCE_NSTAT, ls)) != hipSuccess)
+      return launch_fail(h, "wl init");
     if (micro) {
       MicroParams mp{};
-      mp.heap = dp<u64>(B.heap);
+      mp.heap = heap;
       mp.tab_off = dp<u64>(B.taboff) + off.off[c];
       mp.nroots = counts[c];
       mp.nworkers = pl.nw;
@@ -535,7 +579,7 @@ mce_status run_impl(mce_engine* e, int32_t n, int64_t nnz, const int32_t* row_pt
       mp.mail = dp<u64>(B.mail);
       mp.g_hist = results + 1;
       mp.g_hash = results;
-      mp.wl = dp<MceWl>(B.wl);
+      mp.wl = wl;
       mp.donate_min_p = e->cfg.micro_donate_min_p > 0 ? (int)e->cfg.micro_donate_min_p : 10;
       mp.worker_list = e->cfg.worker_list ? 1 : 0;
       // Cooperative pivot scans pay when every wave works through its own
@@ -547,9 +591,9 @@ mce_status run_impl(mce_engine* e, int32_t n, int64_t nnz, const int32_t* row_pt
       mp.status = &ctl->status;
       mp.stats = dp<u64>(B.stats) + (size_t)stat_off * MCE_NSTAT;
       mp.taken = &ctl->taken[launches];
-      if (stimes) (void)hipEventRecord(e->ev[evi + 2], s);
-      if ((h = mce_launch_micro(counters, mp, s)) != hipSuccess) return hip_fail(e, h, "micro search launch");
-      if (stimes) (void)hipEventRecord(e->ev[evi + 3], s);
+      if (stimes) (void)hipEventRecord(e->ev[evi + 2], ls);
+      if ((h = mce_launch_micro(counters, mp, ls)) != hipSuccess) return launch_fail(h, "micro search launch");
+      if (stimes) (void)hipEventRecord(e->ev[evi + 3], ls);
       evi += 4;
       stat_off += pl.nw;
       launches++;
@@ -559,7 +603,7 @@ mce_status run_impl(mce_engine* e, int32_t n, int64_t nnz, const int32_t* row_pt
     SearchParams prm{};
     prm.rp = row_ptr;
     prm.ci = col_idx;
-    prm.heap = dp<u64>(B.heap);
+    prm.heap = heap;
     prm.tab_off = dp<u64>(B.taboff) + off.off[c];
     prm.nroots = counts[c];
     prm.nworkers = pl.nw;
@@ -577,8 +621,8 @@ mce_status run_impl(mce_engine* e, int32_t n, int64_t nnz, const int32_t* row_pt
     prm.s_mail = L.s_mail;
     prm.g_hist = results + 1;
     prm.g_hash = results;
-    prm.wl = dp<MceWl>(B.wl);
-    prm.slots = dp<char>(B.slots);
+    prm.wl = wl;
+    prm.slots = dp<char>(B.slots) + pl.slot_off;
     prm.donate_min_p = std::max(1, (int)e->cfg.donate_min_p);
     prm.worker_list = e->cfg.worker_list ? 1 : 0;
     prm.budget = budget;
@@ -586,13 +630,21 @@ mce_status run_impl(mce_engine* e, int32_t n, int64_t nnz, const int32_t* row_pt
     prm.status = &ctl->status;
     prm.stats = dp<u64>(B.stats) + (size_t)stat_off * MCE_NSTAT;
     prm.taken = &ctl->taken[launches];
-    if (stimes) (void)hipEventRecord(e->ev[evi + 2], s);
-    if ((h = mce_launch_search(L, prm, s)) != hipSuccess) return hip_fail(e, h, "search launch");
-    if (stimes) (void)hipEventRecord(e->ev[evi + 3], s);
+    if (stimes) (void)hipEventRecord(e->ev[evi + 2], ls);
+    if ((h = mce_launch_search(L, prm, ls)) != hipSuccess) return launch_fail(h, "search launch");
+    if (stimes) (void)hipEventRecord(e->ev[evi + 3], ls);
     evi += 4;
     stat_off += pl.nw;
     launches++;
     max_workers_used = std::max(max_workers_used, pl.nw);
+  }
+  if (overlap) {
+    for (int k = 0; k < MCE_SIDE_STREAMS; k++) {
+      if (!side_used[k]) continue;
+      if ((h = hipEventRecord(e->join_ev[k], e->side[k])) != hipSuccess ||
+          (h = hipStreamWaitEvent(s, e->join_ev[k], 0)) != hipSuccess)
+        return launch_fail(h, "join");
+    }
   }
   // results: one read-back of the control block and the result words
   if ((h = hipMemcpyAsync(hio, ctl, kIoBytes, hipMemcpyDeviceToHost, s)) != hipSuccess)
@@ -792,7 +844,7 @@ mce_status mce_create(const mce_config* cfg, mce_engine** out) {
       c.subgraph < MCE_SUBGRAPH_AUTO ||
       c.subgraph > MCE_SUBGRAPH_FULL ||
       (c.flags & ~(MCE_FLAG_HBM_STAGING | MCE_FLAG_PHASE_TIMES | MCE_FLAG_COUNTERS | MCE_FLAG_NO_MICRO |
-                   MCE_FLAG_L2 | MCE_FLAG_SEARCH_TIMES)) != 0)
+                   MCE_FLAG_L2 | MCE_FLAG_SEARCH_TIMES | MCE_FLAG_SERIAL)) != 0)
     return MCE_ERR_ARG;
   if (c.timeout_ms == 0) c.timeout_ms = 120000;
   mce_engine* e = new (std::nothrow) mce_engine();
@@ -833,6 +885,15 @@ mce_status mce_create(const mce_config* cfg, mce_engine** out) {
   e->have_events = true;
   for (auto& ev : e->ev)
     if (hipEventCreate(&ev) != hipSuccess) e->have_events = false;
+  bool side_ok = hipEventCreateWithFlags(&e->fork_ev, hipEventDisableTiming) == hipSuccess;
+  for (int k = 0; k < MCE_SIDE_STREAMS; k++) {
+    side_ok = side_ok && hipStreamCreateWithFlags(&e->side[k], hipStreamNonBlocking) == hipSuccess;
+    side_ok = side_ok && hipEventCreateWithFlags(&e->join_ev[k], hipEventDisableTiming) == hipSuccess;
+  }
+  if (!side_ok) {
+    mce_destroy(e);
+    return MCE_ERR_DEVICE;
+  }
   *out = e;
   return MCE_OK;
 }
@@ -950,6 +1011,11 @@ void mce_destroy(mce_engine* e) {
   if (e->host.p) (void)hipHostFree(e->host.p);
   for (auto& ev : e->ev)
     if (ev) (void)hipEventDestroy(ev);
+  for (auto& ev : e->join_ev)
+    if (ev) (void)hipEventDestroy(ev);
+  if (e->fork_ev) (void)hipEventDestroy(e->fork_ev);
+  for (auto& st : e->side)
+    if (st) (void)hipStreamDestroy(st);
   delete e;
 }
 

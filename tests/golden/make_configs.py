@@ -18,11 +18,16 @@ Configurations 2 and 4 also get, with --light (multi-process oracle runs):
   - "light": every root whose subtree the oracle finishes within LIGHT_BUDGET
     nodes (stored as the list of the other, "heavy" roots), with the count,
     hash and histogram of their cliques: all of the graph but its dense core;
-  - "dense": heavy roots of the largest |P| whose subtrees the oracle finishes
-    within DENSE_BUDGET nodes (Knuth's estimate picks the candidates first).
+  - "dense" (with --dense, after --light): heavy roots whose subtrees the
+    oracle finishes within DENSE_BUDGET nodes, the largest |P| first. The
+    candidates are the DENSE_TRY heavy roots of smallest estimated size: a
+    single root's Knuth estimate from a few walks is far too low more often than
+    not (the bulk of a heavy subtree sits on rare paths), so it only orders
+    the candidates, and the oracle decides.
 
 Run from the repository root:  python tests/golden/make_configs.py [config ...]
                                python tests/golden/make_configs.py --light 2 4
+                               python tests/golden/make_configs.py --dense 2 4
 """
 from __future__ import annotations
 
@@ -49,7 +54,8 @@ N_HEAVY_TRY = 150         # ... of which this many, evenly spaced from the large
 N_HEAVY_KEEP = 60         # heavy roots kept
 HEAVY_BUDGET = 1_000_000  # oracle search-tree nodes allowed per heavy root
 LIGHT_BUDGET = 200_000    # nodes per root of the "light" set
-DENSE_BUDGET = 20_000_000  # nodes per root of the "dense" sample
+DENSE_BUDGET = 2_000_000  # nodes per root of the "dense" sample
+DENSE_TRY = 800           # heavy roots tried for it
 DENSE_KEEP = 40           # dense roots kept
 DENSE_WALKS = 16          # Knuth walks per dense candidate
 PROCS = min(8, os.cpu_count() or 1)
@@ -94,8 +100,8 @@ def add_up(parts):
     return {"count": cnt, "hash": f"0x{hsh:016x}", "hist": hist}
 
 
-def light_and_dense(idx, rec):
-    """The light set (all roots but the heavy ones) and the dense sample."""
+def light_set(idx, rec):
+    """The light set (all roots but the heavy ones) and every heavy root's estimated size."""
     import multiprocessing as mp
     t0 = time.time()
     g = mi.config_graph(idx)
@@ -119,23 +125,36 @@ def light_and_dense(idx, rec):
                         "roots_x_ge_10000": int((x[light] >= 10000).sum()),
                         "roots_p_ge_300": int((p[light] >= 300).sum()), **add_up(parts)}
         print(idx, "light done", round(time.time() - t0), flush=True)
-        # dense: the heavy roots of largest |P| that fit DENSE_BUDGET, by estimate first
-        cand = heavy[np.argsort(-p[heavy], kind="stable")]
-        est = dict(pool.map(_probe, [int(r) for r in cand]))
-        fit = [r for r in cand if est[int(r)].nodes <= DENSE_BUDGET / 4][: 3 * DENSE_KEEP]
+        # every heavy root's estimated subtree size (nodes), to plan whole-graph runs in pieces
+        est = dict(pool.map(_probe, [int(r) for r in heavy]))
+        rec["light"]["heavy_est_nodes"] = [round(est[int(r)].nodes) for r in heavy]
+
+
+def dense_sample(idx, rec):
+    """Heavy roots that the oracle finishes within DENSE_BUDGET nodes, the largest |P| first."""
+    import multiprocessing as mp
+    t0 = time.time()
+    g = mi.config_graph(idx)
+    assert g.sha256() == rec["sha256"]
+    _, rnd, _ = oracle.peel(g.n, g.row_ptr, g.col_idx)
+    _G["g"], _G["rnd"] = g, rnd
+    p = later_counts(g, rnd)
+    x = g.degrees() - p
+    heavy = np.asarray(rec["light"]["heavy_roots"], np.int32)
+    est = np.asarray(rec["light"]["heavy_est_nodes"], np.float64)
+    cand = heavy[np.argsort(est, kind="stable")][:DENSE_TRY]
+    with mp.get_context("fork").Pool(PROCS) as pool:
         kept = []
-        for roots, nodes, dn in pool.imap(_each, [(np.array([r], np.int32), DENSE_BUDGET) for r in fit]):
+        for roots, nodes, dn in pool.imap_unordered(_each, [(np.array([r], np.int32), DENSE_BUDGET) for r in cand]):
             if dn[0]:
                 kept.append(int(roots[0]))
         kept = sorted(kept, key=lambda r: -p[r])[:DENSE_KEEP]
         dense = np.array(sorted(kept), np.int32)
         parts = pool.map(_sum, [dense[i::PROCS] for i in range(PROCS) if dense[i::PROCS].size])
-        # every heavy root's estimated subtree size (nodes), to plan whole-graph runs in pieces
-        rec["light"]["heavy_est_nodes"] = [round(est[int(r)].nodes) for r in heavy]
-        rec["dense"] = {"budget": DENSE_BUDGET, "roots": dense.tolist(),
-                        "p_range": [int(p[dense].min()), int(p[dense].max())] if dense.size else None,
-                        "x_range": [int(x[dense].min()), int(x[dense].max())] if dense.size else None,
-                        "candidates_fitting_estimate": len(fit), **add_up(parts)}
+    rec["dense"] = {"budget": DENSE_BUDGET, "roots": dense.tolist(), "tried": int(cand.size),
+                    "p_range": [int(p[dense].min()), int(p[dense].max())] if dense.size else None,
+                    "x_range": [int(x[dense].min()), int(x[dense].max())] if dense.size else None,
+                    **add_up(parts)}
     print(idx, "dense", dense.size, rec["dense"]["p_range"], rec["dense"]["x_range"], round(time.time() - t0),
           flush=True)
 
@@ -146,9 +165,9 @@ def main():
     if os.path.exists(path):
         with open(path) as f:
             out = json.load(f)
-    if sys.argv[1:2] == ["--light"]:
+    if sys.argv[1:2] in (["--light"], ["--dense"]):
         for idx in [int(a) for a in sys.argv[2:]] or list(SAMPLED):
-            light_and_dense(idx, out[str(idx)])
+            (light_set if sys.argv[1] == "--light" else dense_sample)(idx, out[str(idx)])
             with open(path, "w") as f:
                 json.dump(out, f, indent=1)
         return

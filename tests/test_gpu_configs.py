@@ -82,6 +82,24 @@ def test_whole_graph(idx, subgraph, level):
         assert info["level"] == level
 
 
+@pytest.mark.parametrize("level", [1, 2])
+@pytest.mark.parametrize("idx", [0, 3])
+def test_serial_launches(idx, level):
+    """MCE_FLAG_SERIAL: the sub-class launches one after another on the
+    caller's stream, sharing one table heap, give the same results as the
+    default overlapped launches (side streams, one heap region per sub-class),
+    run after run on one engine."""
+    g, rp, ci = graph(idx)
+    print(f"case cfg{idx} whole graph, serial and overlapped launches, level {level}", flush=True)
+    want = GOLD[str(idx)]["whole"]
+    with mce.Engine(device=0, timeout_ms=60000, level=level, overlap=False) as es, \
+            mce.Engine(device=0, timeout_ms=60000, level=level) as eo:
+        for _ in range(2):
+            same(es.run(rp, ci), want)
+            same(eo.run(rp, ci), want)
+        assert es.stats()["launches"] == eo.stats()["launches"] >= 1
+
+
 @pytest.mark.timeout(900)   # generating the 4M-vertex graph takes about 1.5 minutes on the host
 @pytest.mark.parametrize("kind", ["uniform", "heavy"])
 @pytest.mark.parametrize("idx", [2, 4])
@@ -124,3 +142,39 @@ def test_root_sample_second_level(idx, kind):
         same(e.run(rp, ci, roots=torch.from_numpy(roots).to(DEV)), want)
         assert e.graph_info()["level"] == 2
 
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("idx", [2, 4])
+def test_light_set(idx):
+    """Every root whose first-level subtree the oracle finishes within its
+    budget (all roots but the dense core's heavy ones: on R-MAT 1,042,681 of
+    1,048,576, among them the hub roots with |X| >= 10,000), compared whole."""
+    if "light" not in GOLD.get(str(idx), {}):
+        pytest.skip(f"no light set for configuration {idx} in tests/golden/configs.json")
+    g, rp, ci = graph(idx)
+    want = GOLD[str(idx)]["light"]
+    mask = np.ones(g.n, bool)
+    mask[np.asarray(want["heavy_roots"], np.int64)] = False
+    roots = np.flatnonzero(mask).astype(np.int32)
+    assert roots.size == want["roots"]
+    print(f"case cfg{idx} light set ({roots.size} roots, |X| up to {want['max_x']})", flush=True)
+    with mce.Engine(device=0, timeout_ms=120000) as e:
+        same(e.run(rp, ci, roots=torch.from_numpy(roots).to(DEV)), want)
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("level", [1, 2])
+@pytest.mark.parametrize("idx", [2, 4])
+def test_dense_sample(idx, level):
+    """Heavy roots of the largest |P| (the dense core) that the oracle finishes
+    within its larger budget; first- and second-level subtrees."""
+    if "dense" not in GOLD.get(str(idx), {}):
+        pytest.skip(f"no dense sample for configuration {idx} in tests/golden/configs.json")
+    g, rp, ci = graph(idx)
+    want = GOLD[str(idx)]["dense"]
+    roots = np.asarray(want["roots"], np.int32)
+    assert roots.size > 0
+    print(f"case cfg{idx} dense sample ({roots.size} roots, |P| {want['p_range']}, |X| {want['x_range']}), "
+          f"level {level}", flush=True)
+    with mce.Engine(device=0, timeout_ms=120000, level=level) as e:
+        same(e.run(rp, ci, roots=torch.from_numpy(roots).to(DEV)), want)
