@@ -99,7 +99,7 @@ def parse():
 # The source file that defines each kernel family; every family also compiles
 # the shared device headers.
 KERNEL_SOURCES = {"k_peel": "prep.hip", "k_validate": "prep.hip", "k_search_micro": "micro.hip",
-                  "k_search": "search.hip", "k_build": "subgraph.hip"}
+                  "k_search": "search.hip", "k_build": "subgraph.hip", "k_forward_adj": "prep.hip"}
 SHARED_HEADERS = ("mce_device.h", "mce_internal.h", "worklist.h")
 
 
@@ -111,14 +111,19 @@ def family(kernel):
 
 
 def sources_hash(kernel):
-    """SHA-256 prefix over the source file that defines `kernel` and every header
-    it includes: a counter summary taken on other sources is not used."""
-    fam = family(kernel)
-    if fam is None:
-        return None
+    """SHA-256 prefix over the source files that define `kernel` (a row such as
+    "k_build_micro+k_forward_adj" names several kernels) and every header they
+    include: a counter summary taken on other sources is not used."""
+    files = []
+    for part in kernel.split("+"):
+        fam = family(part)
+        if fam is None:
+            return None
+        if KERNEL_SOURCES[fam] not in files:
+            files.append(KERNEL_SOURCES[fam])
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "maximal_clique_enumeration_amd", "csrc")
-    for name in (KERNEL_SOURCES[fam],) + SHARED_HEADERS:
+    for name in tuple(files) + SHARED_HEADERS:
         with open(os.path.join(csrc, name), "rb") as f:
             h.update(name.encode() + b"\0" + f.read())
     return h.hexdigest()[:16]

@@ -38,6 +38,7 @@ struct Bufs {
       heap, wl, slots, stats, mstack, mail;
   DevBuf src, fwd, fwdtmp, eroots, pcount2, xcount2;   // second-level subtrees
   DevBuf hub_id, hub_v, hub_bm;                       // their hub adjacency bitmaps
+  DevBuf fadj, fdeg;                                  // forward adjacency (micro-table builds)
 };
 
 constexpr size_t kHistWords = MCE_MAX_P + 3;   // global histogram entries (sizes up to 2 + MCE_MAX_P)
@@ -473,6 +474,11 @@ mce_status run_impl(mce_engine* e, int32_t n, int64_t nnz, const int32_t* row_pt
     stat_rows += nw;
     plan[nplan++] = pl;
   }
+  // the forward adjacency pays where a build reads rows of X members: micro
+  // tables, and full-subgraph tables
+  bool use_fadj = false;
+  for (int i = 0; i < nplan; i++) use_fadj |= plan[i].sub == MCE_SUB_MICRO || mode == MCE_MODE_IPX;
+  use_fadj = use_fadj && !stat;
   // micro frame stacks: kMicroStack frames per wave; in the static scratch,
   // the largest power of two that the space left holds, at least
   // kMicroStackMinStatic (an overflow at run time is MCE_ERR_LIMIT)
@@ -486,6 +492,13 @@ mce_status run_impl(mce_engine* e, int32_t n, int64_t nnz, const int32_t* row_pt
         (h = take(arena, B.stats, (size_t)stat_rows * MCE_NSTAT * sizeof(u64))) != hipSuccess ||
         (micro_nw && (h = take(arena, B.mail, mail_bytes)) != hipSuccess))
       return alloc_fail(e, arena, h, "search buffers");
+    // the forward adjacency, for micro tables and the X rows of full-subgraph
+    // tables (the builds read CSR rows otherwise: the static scratch has no
+    // room for nnz more entries)
+    if (use_fadj &&
+        ((h = take(arena, B.fadj, (size_t)std::max<int64_t>(nnz, 1) * sizeof(int))) != hipSuccess ||
+         (h = take(arena, B.fdeg, (size_t)n * sizeof(int))) != hipSuccess))
+      return alloc_fail(e, arena, h, "forward adjacency");
     if (micro_nw) {
       const size_t frame_bytes = 6 * sizeof(u64) * (size_t)micro_nw;
       if (stat) {
@@ -503,6 +516,9 @@ mce_status run_impl(mce_engine* e, int32_t n, int64_t nnz, const int32_t* row_pt
     // table sizes -> heap offsets (every sub-class's launch reuses the heap from its first root's offset)
     if ((h = mce_launch_scan(dp<u64>(B.taboff), total, dp<u64>(B.scan), s)) != hipSuccess)
       return hip_fail(e, h, "table offset scan");
+    if (use_fadj && (h = mce_launch_forward_adj(n, row_ptr, col_idx, dp<int>(B.rnd), dp<int>(B.fadj),
+                                                dp<int>(B.fdeg), e->num_cu * 16, s)) != hipSuccess)
+      return hip_fail(e, h, "forward adjacency launch");
   }
   if (timing) (void)hipEventRecord(e->ev[3], s);
 
@@ -561,6 +577,10 @@ mce_status run_impl(mce_engine* e, int32_t n, int64_t nnz, const int32_t* row_pt
       const int nslab = std::max(1, (hctl->sub_maxr[var][c] + 63) / 64);
       const int want = (kSplitBlocksPerCu * e->num_cu + counts[c] - 1) / counts[c];
       bp.parts = std::max(1, std::min(std::max(want, (nslab + 7) / 8), nslab));
+    }
+    if (use_fadj) {
+      bp.fadj = dp<int>(B.fadj);
+      bp.fdeg = dp<int>(B.fdeg);
     }
     if (timing) (void)hipEventRecord(e->ev[evi], ls);
     if ((h = mce_launch_build(bp, e->num_cu * 32, ls)) != hipSuccess) return launch_fail(h, "build launch");
@@ -1006,7 +1026,7 @@ void mce_destroy(mce_engine* e) {
   DevBuf* bufs[] = {&b.ctl,    &b.deg,    &b.rnd,     &b.core,    &b.alive0, &b.alive1,  &b.front0, &b.front1,
                     &b.bfront0, &b.bfront1, &b.pcount, &b.xcount,  &b.lists,  &b.taboff,  &b.scan,   &b.heap,
                     &b.wl,     &b.slots,  &b.stats,   &b.mstack,  &b.mail,   &b.src,     &b.fwd,    &b.fwdtmp,
-                    &b.eroots, &b.pcount2, &b.xcount2, &b.hub_id, &b.hub_v,  &b.hub_bm};
+                    &b.eroots, &b.pcount2, &b.xcount2, &b.hub_id, &b.hub_v,  &b.hub_bm, &b.fadj, &b.fdeg};
   for (DevBuf* d : bufs) release(*d);
   if (e->host.p) (void)hipHostFree(e->host.p);
   for (auto& ev : e->ev)

@@ -1185,6 +1185,34 @@ __global__ __launch_bounds__(256) void k_orient(int n, const int* __restrict__ r
   }
 }
 
+// Forward adjacency of every vertex (the oriented graph of section 2.4): the
+// neighbours after v in the peel order, kept in id order at the start of v's
+// own CSR span (so no offsets need computing), and their number. Micro-table
+// builds read these rows instead of whole CSR rows: every edge between two
+// members of a subtree's P u X sits in the forward row of its earlier end, and
+// a forward row is no longer than that end's core number, where a CSR row can
+// be as long as the maximum degree. One wavefront per vertex, its lanes over
+// the row; a ballot keeps the entries in order.
+__global__ __launch_bounds__(256) void k_forward_adj(int n, const int* __restrict__ rp, const int* __restrict__ ci,
+                                                      const int* __restrict__ rnd, int* __restrict__ fadj,
+                                                      int* __restrict__ fdeg) {
+  const int lane = lane_id();
+  const int nwaves = gridDim.x * (blockDim.x / MCE_WAVE);
+  for (int v = blockIdx.x * (blockDim.x / MCE_WAVE) + threadIdx.x / MCE_WAVE; v < n; v += nwaves) {
+    const int a = rp[v], b = rp[v + 1], rv = rnd[v];
+    int k = 0;
+    for (int base = a; base < b; base += MCE_WAVE) {
+      const int e = base + lane;
+      const int u = e < b ? ci[e] : 0;
+      const bool later = e < b && order_after(rnd[u], u, rv, v);
+      const u64 m = ballot(later);
+      if (later) fadj[a + k + mbcnt(m)] = u;
+      k += __popcll(m);
+    }
+    if (lane == 0) fdeg[v] = k;
+  }
+}
+
 // The sub-class tallies of the roots that k_orient counted one wavefront per
 // root: one thread per root, grouped per wavefront as in k_orient.
 __global__ __launch_bounds__(256) void k_tally(int nroots, const int* __restrict__ pcount,
@@ -1504,6 +1532,13 @@ hipError_t mce_launch_orient(int n, const int* rp, const int* ci, const int* rnd
   if (e != hipSuccess || !per_wave || fwd) return e;
   hipLaunchKernelGGL(k_tally, dim3(max(1, min(blocks, (nroots + 255) / 256))), dim3(256), 0, s, nroots, pcount,
                      xcount, ctl);
+  return hipGetLastError();
+}
+
+hipError_t mce_launch_forward_adj(int n, const int* rp, const int* ci, const int* rnd, int* fadj, int* fdeg,
+                                  int blocks, hipStream_t s) {
+  const int nb = max(1, min(blocks, (n + 3) / 4));   // four wavefronts a block, one vertex each at a time
+  hipLaunchKernelGGL(k_forward_adj, dim3(nb), dim3(256), 0, s, n, rp, ci, rnd, fadj, fdeg);
   return hipGetLastError();
 }
 

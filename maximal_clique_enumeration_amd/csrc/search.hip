@@ -104,6 +104,53 @@ __device__ int xx_partition(int* xx, int L, const T& test) {
   return wk;
 }
 
+// The X_X part of Tomita's pivot with the full subgraph: the key of every
+// entry a of xx[0, L) (|N(a) n P| << 20, ties to the smallest local index) goes
+// into `best`, and, in the same pass over 64-entry chunks, the entries with no
+// neighbour in P move behind the others in a stable in-place partition
+// (xx_partition's steps). Such an entry can hold no clique of this subtree back
+// from being maximal: R is reported only where P is empty, and the X of every
+// node below is X n N(v) for branch vertices v taken from this P, which it
+// misses; and it cannot be the pivot of a node below (its key there is that of
+// a neighbour count of 0 and a local index after every P member's). So the node
+// and its subtree keep only the others: the return value is their number. The
+// scan ends early when an X vertex adjacent to all of P turns up (pc = |P|: the
+// node has no branch, and L is returned unchanged). Only the order of xx[0, L)
+// changes, so every enclosing level's X_X, a prefix xx[0, L') with L' >= L,
+// still holds the same set.
+template <class Score>
+__device__ int xx_pivot_prune(int* xx, int L, u32 pc, u32& best, const Score& score) {
+  const int lane = lane_id();
+  int wk = 0;
+  for (int c = 0; c < L; c += MCE_WAVE) {
+    const int i = c + lane;
+    const bool valid = i < L;
+    const int x = valid ? xx[i] : 0;
+    const int kc_bound = min(MCE_WAVE, c - wk);
+    const int dval = lane < kc_bound ? xx[wk + lane] : 0;
+    u32 nb = 0;
+    if (valid) {
+      nb = score(x);
+      const u32 key = (nb << 20) | (u32)(MCE_MAX_LOCAL - x);
+      best = best > key ? best : key;
+    }
+    const bool keep = valid && nb != 0u;
+    const u64 km = ballot(keep);
+    const u64 vm = ballot(valid);
+    const int kc = __popcll(km);
+    const int D = min(kc, c - wk);
+    const int base = max(c, wk + kc);
+    __syncthreads();   // every lane holds its values before anything is written
+    if (keep) xx[wk + mbcnt(km)] = x;
+    if (lane < D) xx[base + lane] = dval;
+    if (valid && !keep) xx[base + D + mbcnt(vm & ~km)] = x;
+    wk += kc;
+    __syncthreads();
+    if (c + MCE_WAVE < L && (wave_max_u32(best) >> 20) == pc) return L;
+  }
+  return wk;
+}
+
 // Is any entry of xx[0, L) adjacent to v? (X_X n N(v) emptiness at a leaf.)
 template <class T>
 __device__ bool xx_any(const int* xx, int L, const T& test) {
@@ -321,20 +368,17 @@ __global__ __launch_bounds__(64) void k_search(SearchParams prm) {
             if constexpr (W == 1) pc = (u32)__popcll(read_lane(pj, 0));
             else pc = wave_sum_u32(lane < W ? (u32)__popcll(pj) : 0u);
             st_prow += (u64)lpx;
-            for (int c0 = 0; c0 < lpx; c0 += MCE_WAVE) {
-              const int i = c0 + lane;
-              if (i < lpx) {
-                const int a = xx[i];
-                const u64* row = rows + (size_t)a * W;
-                u32 c = 0;
+            u64 pw[W];
 #pragma unroll
-                for (int w = 0; w < W; w++) c += (u32)__popcll(read_lane(pj, w) & row[w]);
-                const u32 key = (c << 20) | (u32)(MCE_MAX_LOCAL - a);
-                best = best > key ? best : key;
-              }
-              // an X vertex adjacent to all of P: every branch is fruitless
-              if (c0 + MCE_WAVE < lpx && (wave_max_u32(best) >> 20) == pc) break;
-            }
+            for (int w = 0; w < W; w++) pw[w] = read_lane(pj, w);
+            // (an X vertex adjacent to all of P makes every branch fruitless)
+            lpx = xx_pivot_prune(xx, lpx, pc, best, [&](int a) {
+              const u64* row = rows + (size_t)a * W;
+              u32 c = 0;
+#pragma unroll
+              for (int w = 0; w < W; w++) c += (u32)__popcll(pw[w] & row[w]);
+              return c;
+            });
           }
         }
         best = wave_max_u32(best);
@@ -728,15 +772,7 @@ __global__ __launch_bounds__(64) void k_search_w1(SearchParams prm) {
           if (lpx > 0) {
             const u32 pc = (u32)__popcll(P);
             if constexpr (CNT) st_prow += (u64)lpx;
-            for (int c0 = 0; c0 < lpx; c0 += MCE_WAVE) {
-              const int i = c0 + lane;
-              if (i < lpx) {
-                const int a = xx[i];
-                const u32 key = ((u32)__popcll(P & rows[a]) << 20) | (u32)(MCE_MAX_LOCAL - a);
-                best = best > key ? best : key;
-              }
-              if (c0 + MCE_WAVE < lpx && (wave_max_u32(best) >> 20) == pc) break;
-            }
+            lpx = xx_pivot_prune(xx, lpx, pc, best, [&](int a) { return (u32)__popcll(P & rows[a]); });
           }
         }
         best = wave_max_u32(best);

@@ -139,16 +139,21 @@ __device__ __forceinline__ int build_lookup(const int* hk, const short* hv, int 
 // ------------------------------------------------------------------ micro tables
 // |P| <= 64 and |X| <= 64: one wavefront per root, and the whole table (at most
 // 128 one-word rows) is built in LDS. One pass over the root's CSR row splits it
-// into P and X; P's ids go into the LDS hash. The members' CSR rows are then
-// streamed as one sequence, 64 consecutive entries per load (coalesced within a
-// row), each entry's row found from the rows' degree prefix sums; rows longer
-// than 4 |P| are built by probing each P member in them. The X column of
-// every P member (the transpose of the X rows) is taken in LDS, and the table is
+// into P and X. Then, with the forward adjacency (prm.fadj): the ids of P u X go
+// into an LDS hash, and the members' forward rows are streamed as one sequence,
+// 64 consecutive entries per load (coalesced within a row), each entry's row
+// found from the rows' length prefix sums; an edge between two members, found
+// in the forward row of its earlier end, sets its bit in the row of each end
+// that has a row over P (every row is over P, so: the X end's row if the other
+// end is in P, and both rows if both are). Without it: P's ids go into the
+// hash, the members' whole CSR rows are streamed the same way, and rows longer
+// than 4 |P| are built by probing each P member in them. The X column of every
+// P member (the transpose of the X rows) is taken in LDS, and the table is
 // written out with coalesced stores.
 #define MICRO_PROBE_RATIO 4   // rows longer than 4 |P| are probed
 
 __global__ __launch_bounds__(64) void k_build_micro(BuildParams prm) {
-  constexpr int HB = 7;   // hash slots >= 2 * 64
+  constexpr int HB = 8;   // hash slots >= 2 * 128
   __shared__ int s_id[2 * MCE_MICRO_MAX];   // P ids, then X ids
   __shared__ int s_hk[1 << HB];
   __shared__ short s_hv[1 << HB];
@@ -198,6 +203,7 @@ __global__ __launch_bounds__(64) void k_build_micro(BuildParams prm) {
     }
     for (int h = lane; h < (1 << HB); h += MCE_WAVE) s_hk[h] = -1;
     __syncthreads();   // the ids are in LDS, the hash is clear
+    const bool fwd = prm.fadj != nullptr;
     if (lane < np) {
       const int u = s_id[lane];
       ids[lane] = u;
@@ -206,9 +212,67 @@ __global__ __launch_bounds__(64) void k_build_micro(BuildParams prm) {
       while (atomicCAS(&s_hk[h], -1, u) != -1) h = (h + 1u) & ((1u << HB) - 1u);
       s_hv[h] = (short)lane;
     }
-    if (lane < nx) ids[np + lane] = s_id[MCE_MICRO_MAX + lane];
+    if (lane < nx) {
+      const int u = s_id[MCE_MICRO_MAX + lane];
+      ids[np + lane] = u;
+      if (fwd) {
+        u32 h = build_hash<HB>(u);
+        while (atomicCAS(&s_hk[h], -1, u) != -1) h = (h + 1u) & ((1u << HB) - 1u);
+        s_hv[h] = (short)(np + lane);
+      }
+    }
+    if (fwd) {
+      for (int t = lane; t < nrows; t += MCE_WAVE) s_row[t] = 0;
+      // forward rows, in slabs of 64 members (P members first, then X members)
+      for (int t0 = 0; t0 < nrows; t0 += MCE_WAVE) {
+        const int t = t0 + lane;
+        int ga = 0, d = 0;
+        if (t < nrows) {
+          const int g = t < np ? s_id[t] : s_id[MCE_MICRO_MAX + t - np];
+          ga = rp[g];
+          d = prm.fdeg[g];
+        }
+        int inc = d;
+#pragma unroll
+        for (int o = 1; o < MCE_WAVE; o <<= 1) {
+          const int v = __shfl_up(inc, o);
+          if (lane >= o) inc += v;
+        }
+        const int D = uni(__shfl(inc, MCE_WAVE - 1));
+        s_pre[lane] = inc - d;
+        s_ga[lane] = ga;
+        __syncthreads();   // the hash and cleared rows (first slab), the prefix sums
+        for (int base = 0; base < D; base += 4 * MCE_WAVE) {
+          int u[4], rw[4];
+#pragma unroll
+          for (int z = 0; z < 4; z++) {
+            const int x = base + z * MCE_WAVE + lane;
+            rw[z] = -1;
+            u[z] = 0;
+            if (x < D) {
+              int q = 0;   // the last row whose prefix is <= x
+#pragma unroll
+              for (int step = MCE_WAVE / 2; step > 0; step >>= 1)
+                if (s_pre[q + step] <= x) q += step;
+              rw[z] = q;
+              u[z] = prm.fadj[s_ga[q] + (x - s_pre[q])];
+            }
+          }
+#pragma unroll
+          for (int z = 0; z < 4; z++) {
+            if (rw[z] >= 0) {
+              const int j = build_lookup<HB>(s_hk, s_hv, u[z]);
+              const int ta = t0 + rw[z];
+              if (j >= 0 && j < np) atomicOr(&s_row[ta], 1ull << j);
+              if (j >= 0 && ta < np) atomicOr(&s_row[j], 1ull << ta);
+            }
+          }
+        }
+        __syncthreads();   // the prefix sums are rewritten by the next slab
+      }
+    }
     // rows, in slabs of 64 members (P members first, then X members)
-    for (int t0 = 0; t0 < nrows; t0 += MCE_WAVE) {
+    for (int t0 = 0; !fwd && t0 < nrows; t0 += MCE_WAVE) {
       const int t = t0 + lane;
       const bool valid = t < nrows;
       int ga = 0, d = 0, gv = 0;
@@ -383,7 +447,10 @@ __global__ __launch_bounds__(256) void k_build_head(BuildParams prm) {
 // entry's row from the rows' degree prefix sums, and ORs the P members it finds
 // into the slab's rows in LDS. The slab's work is then set by its total degree,
 // not by its longest row. A row much longer than P is built instead by probing
-// every P member in it.
+// every P member in it. With the forward adjacency (prm.fadj), an X member's row
+// is its forward row: every P member comes after every X member in the peel
+// order (P after the pivot vertex, X before it), so the P members adjacent to
+// it are all in that row, which is no longer than the member's core number.
 #define SPLIT_STREAM_RATIO 2
 
 template <int W>
@@ -394,6 +461,7 @@ __global__ __launch_bounds__(64) void k_build_rows(BuildParams prm) {
   __shared__ short s_hv[1 << HB];
   __shared__ int s_pre[MCE_WAVE];   // exclusive prefix sum of the slab rows' streamed degrees
   __shared__ int s_ga[MCE_WAVE];    // their CSR row starts
+  __shared__ int s_fw[MCE_WAVE];    // 1: the row streamed is the forward row
   __shared__ u64 s_slab[MCE_WAVE * W];
   const int lane = lane_id();
   const int* __restrict__ rp = prm.rp;
@@ -435,13 +503,14 @@ __global__ __launch_bounds__(64) void k_build_rows(BuildParams prm) {
       const int t = t0 + lane;
       const bool valid = t < nrows;
       int ga = 0, d = 0, gv = 0;
+      const bool fw = valid && prm.fadj && t >= np;   // an X member's row, from its forward row
       if (valid) {
         const int g = ids[t];
         gv = g;
         ga = rp[g];
-        d = rp[g + 1] - ga;
+        d = fw ? prm.fdeg[g] : rp[g + 1] - ga;
       }
-      const bool probe = valid && d > SPLIT_STREAM_RATIO * np;
+      const bool probe = valid && !fw && d > SPLIT_STREAM_RATIO * np;
       const int dd = valid && !probe ? d : 0;
       int inc = dd;
 #pragma unroll
@@ -452,6 +521,7 @@ __global__ __launch_bounds__(64) void k_build_rows(BuildParams prm) {
       const int D = uni(__shfl(inc, MCE_WAVE - 1));
       s_pre[lane] = inc - dd;
       s_ga[lane] = ga;
+      s_fw[lane] = fw ? 1 : 0;
       for (int q = lane; q < MCE_WAVE * W; q += MCE_WAVE) s_slab[q] = 0;
       __syncthreads();
       for (int base = 0; base < D; base += 4 * MCE_WAVE) {
@@ -467,7 +537,7 @@ __global__ __launch_bounds__(64) void k_build_rows(BuildParams prm) {
             for (int step = MCE_WAVE / 2; step > 0; step >>= 1)
               if (s_pre[r + step] <= x) r += step;
             rr[z] = r;
-            u[z] = ci[s_ga[r] + (x - s_pre[r])];
+            u[z] = (s_fw[r] ? prm.fadj : ci)[s_ga[r] + (x - s_pre[r])];
           }
         }
 #pragma unroll
