@@ -354,9 +354,21 @@ mce_status run_impl(mce_engine* e, int32_t n, int64_t nnz, const int32_t* row_pt
   if (maxhubs > 0 && (h = mce_launch_hubs(n, row_ptr, col_idx, dp<int>(B.hub_id), dp<int>(B.hub_v),
                                          dp<u64>(B.hub_bm), maxhubs, ctl, grid, s)) != hipSuccess)
     return hip_fail(e, h, "hub bitmaps launch");
+  // A first-level run over every vertex builds the forward adjacency before
+  // the orientation, which then reads |P| from it; other runs build it after
+  // the root bucketing when a build needs it (not mce_run_static: its scratch
+  // has no room for nnz more entries).
+  const bool early_fadj = !stat && !l2 && !subset;
+  if (early_fadj &&
+      ((h = take(arena, B.fadj, (size_t)std::max<int64_t>(nnz, 1) * sizeof(int))) != hipSuccess ||
+       (h = take(arena, B.fdeg, (size_t)n * sizeof(int))) != hipSuccess))
+    return alloc_fail(e, arena, h, "forward adjacency");
+  if (early_fadj && (h = mce_launch_forward_adj(n, row_ptr, col_idx, dp<int>(B.rnd), dp<int>(B.fadj),
+                                                dp<int>(B.fdeg), e->num_cu * 16, s)) != hipSuccess)
+    return hip_fail(e, h, "forward adjacency launch");
   if ((h = mce_launch_orient(n, row_ptr, col_idx, dp<int>(B.rnd), subset ? roots : nullptr, cnt,
-                             dp<int>(B.pcount), dp<int>(B.xcount), ctl, l2 ? dp<u64>(B.fwd) : nullptr, grid,
-                             s)) != hipSuccess)
+                             dp<int>(B.pcount), dp<int>(B.xcount), ctl, l2 ? dp<u64>(B.fwd) : nullptr,
+                             early_fadj ? dp<int>(B.fdeg) : nullptr, grid, s)) != hipSuccess)
     return hip_fail(e, h, "orient launch");
   if (l2 && (h = mce_launch_l2_roots(n, nnz, row_ptr, col_idx, dp<int>(B.rnd), subset ? roots : nullptr, cnt,
                                      dp<u64>(B.fwd), dp<u64>(B.fwdtmp), dp<int>(B.src), dp<int>(B.eroots),
@@ -478,7 +490,7 @@ mce_status run_impl(mce_engine* e, int32_t n, int64_t nnz, const int32_t* row_pt
   // tables, and full-subgraph tables
   bool use_fadj = false;
   for (int i = 0; i < nplan; i++) use_fadj |= plan[i].sub == MCE_SUB_MICRO || mode == MCE_MODE_IPX;
-  use_fadj = use_fadj && !stat;
+  use_fadj = early_fadj || (use_fadj && !stat);
   // micro frame stacks: kMicroStack frames per wave; in the static scratch,
   // the largest power of two that the space left holds, at least
   // kMicroStackMinStatic (an overflow at run time is MCE_ERR_LIMIT)
@@ -495,7 +507,7 @@ mce_status run_impl(mce_engine* e, int32_t n, int64_t nnz, const int32_t* row_pt
     // the forward adjacency, for micro tables and the X rows of full-subgraph
     // tables (the builds read CSR rows otherwise: the static scratch has no
     // room for nnz more entries)
-    if (use_fadj &&
+    if (use_fadj && !early_fadj &&
         ((h = take(arena, B.fadj, (size_t)std::max<int64_t>(nnz, 1) * sizeof(int))) != hipSuccess ||
          (h = take(arena, B.fdeg, (size_t)n * sizeof(int))) != hipSuccess))
       return alloc_fail(e, arena, h, "forward adjacency");
@@ -516,7 +528,7 @@ mce_status run_impl(mce_engine* e, int32_t n, int64_t nnz, const int32_t* row_pt
     // table sizes -> heap offsets (every sub-class's launch reuses the heap from its first root's offset)
     if ((h = mce_launch_scan(dp<u64>(B.taboff), total, dp<u64>(B.scan), s)) != hipSuccess)
       return hip_fail(e, h, "table offset scan");
-    if (use_fadj && (h = mce_launch_forward_adj(n, row_ptr, col_idx, dp<int>(B.rnd), dp<int>(B.fadj),
+    if (use_fadj && !early_fadj && (h = mce_launch_forward_adj(n, row_ptr, col_idx, dp<int>(B.rnd), dp<int>(B.fadj),
                                                 dp<int>(B.fdeg), e->num_cu * 16, s)) != hipSuccess)
       return hip_fail(e, h, "forward adjacency launch");
   }
@@ -532,6 +544,17 @@ mce_status run_impl(mce_engine* e, int32_t n, int64_t nnz, const int32_t* row_pt
         if (side_used[k]) (void)hipStreamSynchronize(e->side[k]);
     return hip_fail(e, herr, what);
   };
+  // overlapped: every launch's worker list is set up here, before the fork (a
+  // small kernel queued behind a build on a busy side stream waits for free
+  // compute units, and the search behind it waits too)
+  if (overlap) {
+    for (int pi = 0, so = 0; pi < nplan; pi++) {
+      if ((h = mce_launch_wl_init(dp<MceWl>(B.wl) + pi, plan[pi].nw, dp<u64>(B.stats) + (size_t)so * MCE_NSTAT, s)) !=
+          hipSuccess)
+        return hip_fail(e, h, "wl init");
+      so += plan[pi].nw;
+    }
+  }
   if (overlap && nplan > 0 && (h = hipEventRecord(e->fork_ev, s)) != hipSuccess) return hip_fail(e, h, "fork");
 
   int launches = 0, max_workers_used = 0, stat_off = 0;
@@ -585,7 +608,8 @@ mce_status run_impl(mce_engine* e, int32_t n, int64_t nnz, const int32_t* row_pt
     if (timing) (void)hipEventRecord(e->ev[evi], ls);
     if ((h = mce_launch_build(bp, e->num_cu * 32, ls)) != hipSuccess) return launch_fail(h, "build launch");
     if (timing) (void)hipEventRecord(e->ev[evi + 1], ls);
-    if ((h = mce_launch_wl_init(wl, pl.nw, dp<u64>(B.stats) + (size_t)stat_off * MCE_NSTAT, ls)) != hipSuccess)
+    if (!overlap &&
+        (h = mce_launch_wl_init(wl, pl.nw, dp<u64>(B.stats) + (size_t)stat_off * MCE_NSTAT, ls)) != hipSuccess)
       return launch_fail(h, "wl init");
     if (micro) {
       MicroParams mp{};

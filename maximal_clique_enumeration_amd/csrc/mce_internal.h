@@ -204,8 +204,11 @@ int mce_peel_max_blocks(int num_cu);
 // peel order (id order), fdeg[v] = how many there are.
 hipError_t mce_launch_forward_adj(int n, const int* rp, const int* ci, const int* rnd, int* fadj, int* fdeg,
                                   int blocks, hipStream_t s);
+// fdeg: the forward adjacency's row lengths, when every vertex is a root of a
+// first-level run (roots == NULL, fwd == NULL): |P| is read from it.
 hipError_t mce_launch_orient(int n, const int* rp, const int* ci, const int* rnd, const int* roots, int nroots,
-                             int* pcount, int* xcount, MceCtl* ctl, u64* fwd, int blocks, hipStream_t s);
+                             int* pcount, int* xcount, MceCtl* ctl, u64* fwd, const int* fdeg, int blocks,
+                             hipStream_t s);
 // Second-level roots (Algorithm 4) of the vertex roots: COO sources (src, nnz),
 // the forward edges as CSR positions (eroots, at most nnz; their number goes to
 // ctl->l2_roots), and per root |P| and |X| (pcount, xcount) and the tallies.

@@ -1020,10 +1020,52 @@ __global__ __launch_bounds__(PEEL_THREADS) void k_peel(int n, const int* __restr
 // micro sub-class on or off): count, largest |P|, |X| and row count, heap
 // words, so that the host can pick the variant and size every launch from one
 // read-back.
+// A block's sub-class tallies, in LDS: the waves add to them with LDS atomics
+// and the block adds them to the control block once, at its end (same-address
+// atomics in device memory serialise: one set per wave cost the orientation of
+// a 500k-vertex graph about 0.5 ms).
+struct TallyAcc {
+  int count[MCE_NVAR][MCE_NSUB];
+  int maxp[MCE_NVAR][MCE_NSUB];
+  int maxx[MCE_NVAR][MCE_NSUB];
+  int maxr[MCE_NVAR][MCE_NSUB];
+  u64 words[MCE_NVAR][MCE_NSUB];
+};
+
+// Clears the block's tallies and reads whether the run still goes on (status
+// clear), one read for the whole block so that every thread takes the same way
+// (the kernels that tally end with a block barrier). Whole block.
+__device__ __forceinline__ bool tally_begin(TallyAcc& t, int* s_ok, MceCtl* ctl) {
+  for (int i = threadIdx.x; i < MCE_NVAR * MCE_NSUB; i += blockDim.x) {
+    (&t.count[0][0])[i] = 0;
+    (&t.maxp[0][0])[i] = 0;
+    (&t.maxx[0][0])[i] = 0;
+    (&t.maxr[0][0])[i] = 0;
+    (&t.words[0][0])[i] = 0ull;
+  }
+  if (threadIdx.x == 0) *s_ok = ld_relaxed(&ctl->status) == 0 ? 1 : 0;
+  __syncthreads();
+  return *s_ok != 0;
+}
+
+// Adds the block's tallies to the control block. Whole block.
+__device__ __forceinline__ void tally_end(TallyAcc& t, MceCtl* ctl) {
+  __syncthreads();
+  for (int i = threadIdx.x; i < MCE_NVAR * MCE_NSUB; i += blockDim.x) {
+    const int var = i / MCE_NSUB, sub = i % MCE_NSUB;
+    if (t.count[var][sub] == 0) continue;
+    atomicAdd(&ctl->sub_count[var][sub], t.count[var][sub]);
+    atomicMax(&ctl->sub_maxp[var][sub], t.maxp[var][sub]);
+    atomicMax(&ctl->sub_maxx[var][sub], t.maxx[var][sub]);
+    atomicMax(&ctl->sub_maxr[var][sub], t.maxr[var][sub]);
+    atomicAdd(&ctl->sub_words[var][sub], t.words[var][sub]);
+  }
+}
+
 // Tallies a wave's roots (one per lane, `valid` set) per classification variant
 // (subgraph mode, micro sub-class on or off) and sub-class: count, largest |P|,
-// |X| and row count, heap words. Whole wave.
-__device__ void tally_roots(MceCtl* ctl, bool valid, int p, int x) {
+// |X| and row count, heap words, into the block's tallies. Whole wave.
+__device__ __forceinline__ void tally_roots(TallyAcc& acc, bool valid, int p, int x) {
   const int lane = lane_id();
   for (int var = 0; var < MCE_NVAR; var++) {
     const int mode = var & 1;
@@ -1039,11 +1081,11 @@ __device__ void tally_roots(MceCtl* ctl, bool valid, int p, int x) {
       const u32 mr = wave_max_u32(mine ? (u32)mce_table_rows(p, x, s == MCE_SUB_MICRO ? MCE_MODE_IPX : mode) : 0u);
       const u64 words = wave_sum_u64(mine ? mce_sub_table_words(p, x, s, mode) : 0ull);
       if (lane == 0) {
-        atomicAdd(&ctl->sub_count[var][s], __popcll(m));
-        atomicMax(&ctl->sub_maxp[var][s], (int)mp);
-        atomicMax(&ctl->sub_maxx[var][s], (int)mx);
-        atomicMax(&ctl->sub_maxr[var][s], (int)mr);
-        atomicAdd(&ctl->sub_words[var][s], words);
+        atomicAdd(&acc.count[var][s], __popcll(m));
+        atomicMax(&acc.maxp[var][s], (int)mp);
+        atomicMax(&acc.maxx[var][s], (int)mx);
+        atomicMax(&acc.maxr[var][s], (int)mr);
+        atomicAdd(&acc.words[var][s], words);
       }
     }
   }
@@ -1056,13 +1098,16 @@ __device__ void tally_roots(MceCtl* ctl, bool valid, int p, int x) {
 // thread takes each root (a wavefront takes each long row in turn); with at most
 // one root per wavefront of the grid (per_wave), each wavefront takes one root
 // and its lanes share the row: a thread alone would walk the row one dependent
-// pair of loads (entry, then its round) at a time.
+// pair of loads (entry, then its round) at a time. With the forward adjacency
+// already counted (fdeg, every vertex a root) |P| is read, not counted.
 
 __global__ __launch_bounds__(256) void k_orient(int n, const int* __restrict__ rp, const int* __restrict__ ci,
                                                  const int* __restrict__ rnd, const int* __restrict__ roots,
                                                  int nroots, int* pcount, int* xcount, MceCtl* ctl, u64* fwd,
-                                                 int tally, int per_wave, u32 mul) {
-  if (ld_relaxed(&ctl->status) != 0) return;
+                                                 const int* __restrict__ fdeg, int tally, int per_wave, u32 mul) {
+  __shared__ TallyAcc s_tally;
+  __shared__ int s_ok;
+  if (!tally_begin(s_tally, &s_ok, ctl)) return;
   const int lane = lane_id();
   const int gsize = gridDim.x * blockDim.x;
   const int cnt = nroots;   // roots == NULL: the identity list 0..nroots-1
@@ -1128,9 +1173,22 @@ __global__ __launch_bounds__(256) void k_orient(int n, const int* __restrict__ r
         b = rp[v + 1];
         rv = rnd[v];
       }
-      const bool longrow = inr && b - a > ORIENT_LONG;
-      if (inr && !longrow) {
-        for (int e = a; e < b; e++) {
+      const bool longrow = inr && !fdeg && b - a > ORIENT_LONG;
+      if (inr && fdeg) {
+        p = fdeg[v];
+      } else if (inr && !longrow) {
+        // four entries at a time: their loads, then their rounds' loads, overlap
+        int e = a;
+        for (; e + 4 <= b; e += 4) {
+          int u[4], r[4];
+#pragma unroll
+          for (int z = 0; z < 4; z++) u[z] = ci[e + z];
+#pragma unroll
+          for (int z = 0; z < 4; z++) r[z] = rnd[u[z]];
+#pragma unroll
+          for (int z = 0; z < 4; z++) p += order_after(r[z], u[z], rv, v) ? 1 : 0;
+        }
+        for (; e < b; e++) {
           const int u = ci[e];
           p += order_after(rnd[u], u, rv, v) ? 1 : 0;
         }
@@ -1163,7 +1221,7 @@ __global__ __launch_bounds__(256) void k_orient(int n, const int* __restrict__ r
       } else if (i < cnt && fwd) {
         fwd[i] = 0;
       }
-      if (tally) tally_roots(ctl, valid, p, x);
+      if (tally) tally_roots(s_tally, valid, p, x);
     }
   }
   const u64 wiso = wave_sum_u64(iso);
@@ -1183,6 +1241,7 @@ __global__ __launch_bounds__(256) void k_orient(int n, const int* __restrict__ r
     if (wl & 1u) atomicOr(&ctl->status, MCE_E_LIMIT);
     if (wl & 2u) atomicOr(&ctl->status, MCE_E_ROOTS);
   }
+  if (tally) tally_end(s_tally, ctl);
 }
 
 // Forward adjacency of every vertex (the oriented graph of section 2.4): the
@@ -1217,43 +1276,69 @@ __global__ __launch_bounds__(256) void k_forward_adj(int n, const int* __restric
 // root: one thread per root, grouped per wavefront as in k_orient.
 __global__ __launch_bounds__(256) void k_tally(int nroots, const int* __restrict__ pcount,
                                                 const int* __restrict__ xcount, MceCtl* ctl) {
-  if (ld_relaxed(&ctl->status) != 0) return;
+  __shared__ TallyAcc s_tally;
+  __shared__ int s_ok;
+  if (!tally_begin(s_tally, &s_ok, ctl)) return;
   const int gsize = gridDim.x * blockDim.x;
   for (int base = blockIdx.x * blockDim.x; base < nroots; base += gsize) {
     const int i = base + threadIdx.x;
     const int p = i < nroots ? pcount[i] : 0, x = i < nroots ? xcount[i] : 0;
-    tally_roots(ctl, p > 0 && p <= MCE_MAX_P, p, x);
+    tally_roots(s_tally, p > 0 && p <= MCE_MAX_P, p, x);
   }
+  tally_end(s_tally, ctl);
 }
 
 // Scatter the roots with 1 <= |P| <= MCE_MAX_P into one list per sub-class of
-// the chosen mode, starting at off[sub].
+// the chosen mode, starting at off[sub]. Each block takes a contiguous range of
+// roots in two passes: it counts them per sub-class (LDS atomics, one per wave
+// and sub-class), reserves its places with one device atomic per sub-class,
+// then places them from LDS cursors. (One device atomic per wave and sub-class
+// on the shared cursors cost a 500k-root run about 0.13 ms.)
 __global__ __launch_bounds__(256) void k_bucket(const int* __restrict__ roots, int nroots,
                                                  const int* __restrict__ pcount, const int* __restrict__ xcount,
                                                  int mode, int micro, SubOffsets off, int* lists, u64* words,
                                                  MceCtl* ctl) {
-  if (ld_relaxed(&ctl->status) != 0) return;
+  __shared__ int s_cnt[MCE_NSUB];
+  __shared__ int s_cur[MCE_NSUB];
+  __shared__ int s_ok;
+  if (threadIdx.x == 0) s_ok = ld_relaxed(&ctl->status) == 0 ? 1 : 0;
+  for (int i = threadIdx.x; i < MCE_NSUB; i += blockDim.x) s_cnt[i] = 0;
+  __syncthreads();
+  if (!s_ok) return;
   const int lane = lane_id();
-  const int gsize = gridDim.x * blockDim.x;
-  for (int base = blockIdx.x * blockDim.x; base < nroots; base += gsize) {
-    const int i = base + threadIdx.x;
-    const int p = i < nroots ? pcount[i] : 0;
-    const int x = i < nroots ? xcount[i] : 0;
-    const bool valid = p > 0 && p <= MCE_MAX_P;
-    const int sub = valid ? mce_sub_of(p, x, mode, micro != 0) : -1;
-    u64 pending = ballot(valid);
-    while (pending) {
-      const int s = read_lane(sub, __builtin_ctzll(pending));
-      const bool mine = sub == s;
-      const u64 m = ballot(mine);
-      pending &= ~m;
-      int pos = 0;
-      if (lane == 0) pos = atomicAdd(&ctl->sub_cursor[s], __popcll(m));
-      pos = read_lane(pos, 0);
-      if (mine) {
-        lists[off.off[s] + pos + mbcnt(m)] = roots ? roots[i] : i;
-        words[off.off[s] + pos + mbcnt(m)] = mce_sub_table_words(p, x, s, mode);
+  const int per = (nroots + gridDim.x - 1) / gridDim.x;
+  const int r0 = min(nroots, blockIdx.x * per), r1 = min(nroots, r0 + per);
+  for (int pass = 0; pass < 2; pass++) {
+    for (int base = r0; base < r1; base += blockDim.x) {
+      const int i = base + threadIdx.x;
+      const int p = i < r1 ? pcount[i] : 0;
+      const int x = i < r1 ? xcount[i] : 0;
+      const bool valid = p > 0 && p <= MCE_MAX_P;
+      const int sub = valid ? mce_sub_of(p, x, mode, micro != 0) : -1;
+      u64 pending = ballot(valid);
+      while (pending) {
+        const int sc = read_lane(sub, __builtin_ctzll(pending));
+        const bool mine = sub == sc;
+        const u64 m = ballot(mine);
+        pending &= ~m;
+        if (pass == 0) {
+          if (lane == 0) atomicAdd(&s_cnt[sc], __popcll(m));
+        } else {
+          int pos = 0;
+          if (lane == 0) pos = atomicAdd(&s_cur[sc], __popcll(m));
+          pos = read_lane(pos, 0);
+          if (mine) {
+            lists[off.off[sc] + pos + mbcnt(m)] = roots ? roots[i] : i;
+            words[off.off[sc] + pos + mbcnt(m)] = mce_sub_table_words(p, x, sc, mode);
+          }
+        }
       }
+    }
+    if (pass == 0) {
+      __syncthreads();
+      for (int c = threadIdx.x; c < MCE_NSUB; c += blockDim.x)
+        s_cur[c] = s_cnt[c] ? atomicAdd(&ctl->sub_cursor[c], s_cnt[c]) : 0;
+      __syncthreads();
     }
   }
 }
@@ -1413,7 +1498,9 @@ __global__ __launch_bounds__(256) void k_orient_l2(const int* __restrict__ rp, c
                                                     const int* __restrict__ eroots, int* pcount, int* xcount,
                                                     const int* __restrict__ hub_id, const u64* __restrict__ bm,
                                                     int words, MceCtl* ctl) {
-  if (ld_relaxed(&ctl->status) != 0) return;
+  __shared__ TallyAcc s_tally;
+  __shared__ int s_ok;
+  if (!tally_begin(s_tally, &s_ok, ctl)) return;
   constexpr int NQ = MCE_WAVE / L2_GROUP;   // roots in flight per wavefront
   const int lane = lane_id();
   const int q = lane / L2_GROUP, sl = lane % L2_GROUP;
@@ -1474,7 +1561,7 @@ __global__ __launch_bounds__(256) void k_orient_l2(const int* __restrict__ rp, c
       xcount[g0 + lane] = x;
       if (p > MCE_MAX_P) lim |= 1u;
     }
-    tally_roots(ctl, mine && p > 0 && p <= MCE_MAX_P, p, x);
+    tally_roots(s_tally, mine && p > 0 && p <= MCE_MAX_P, p, x);
   }
   const u64 wp = wave_sum_u64(pairs), wh = wave_sum_u64(pairs_hash);
   const u32 wl = wave_or_u32(lim);
@@ -1485,6 +1572,7 @@ __global__ __launch_bounds__(256) void k_orient_l2(const int* __restrict__ rp, c
     }
     if (wl) atomicOr(&ctl->status, MCE_E_LIMIT);
   }
+  tally_end(s_tally, ctl);
 }
 
 hipError_t mce_launch_hubs(int n, const int* rp, const int* ci, int* hub_id, int* hub_v, u64* bm, int maxhubs,
@@ -1520,14 +1608,20 @@ hipError_t mce_launch_l2_roots(int n, long long nnz, const int* rp, const int* c
 }
 
 hipError_t mce_launch_orient(int n, const int* rp, const int* ci, const int* rnd, const int* roots, int nroots,
-                             int* pcount, int* xcount, MceCtl* ctl, u64* fwd, int blocks, hipStream_t s) {
+                             int* pcount, int* xcount, MceCtl* ctl, u64* fwd, const int* fdeg, int blocks,
+                             hipStream_t s) {
+  if (fdeg && (roots || fwd || nroots != n)) return hipErrorInvalidValue;   // every vertex a root, first level
   // at most one root per wavefront of the grid: a wavefront per root, on at most
   // 256 wavefronts (every wavefront ends with a few atomics on the same words:
   // thousands of them cost more than walking several rows each)
-  const int per_wave = nroots <= 4 * blocks ? 1 : 0;
-  const int nb = per_wave ? max(1, min(64, (nroots + 3) / 4)) : max(1, min(blocks, (nroots + 255) / 256));
+  const int per_wave = !fdeg && nroots <= 4 * blocks ? 1 : 0;
+  // (a thread per root otherwise; each block adds its tallies to the control
+  // block once, so with |P| read from fdeg, where a thread does little else,
+  // fewer blocks take more roots each)
+  const int tb = fdeg ? max(1, blocks / 8) : blocks;
+  const int nb = per_wave ? max(1, min(64, (nroots + 3) / 4)) : max(1, min(tb, (nroots + 255) / 256));
   hipLaunchKernelGGL(k_orient, dim3(nb), dim3(256), 0, s, n, rp, ci, rnd, roots, nroots, pcount, xcount, ctl, fwd,
-                     fwd ? 0 : 1, per_wave, ORIENT_MUL);
+                     fdeg, fwd ? 0 : 1, per_wave, ORIENT_MUL);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || !per_wave || fwd) return e;
   hipLaunchKernelGGL(k_tally, dim3(max(1, min(blocks, (nroots + 255) / 256))), dim3(256), 0, s, nroots, pcount,
@@ -1545,7 +1639,8 @@ hipError_t mce_launch_forward_adj(int n, const int* rp, const int* ci, const int
 hipError_t mce_launch_bucket(const int* roots, int nroots, const int* pcount, const int* xcount, int mode,
                              int micro, SubOffsets off, int* lists, u64* words, MceCtl* ctl, int blocks,
                              hipStream_t s) {
-  const int nb = max(1, min(blocks, (nroots + 255) / 256));
+  // (at most blocks / 8 blocks, each over a contiguous range of roots)
+  const int nb = max(1, min(max(1, blocks / 8), (nroots + 255) / 256));
   hipLaunchKernelGGL(k_bucket, dim3(nb), dim3(256), 0, s, roots, nroots, pcount, xcount, mode, micro, off, lists,
                      words, ctl);
   return hipGetLastError();
