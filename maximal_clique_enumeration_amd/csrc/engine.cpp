@@ -38,7 +38,7 @@ struct Bufs {
       heap, wl, slots, stats, mstack, mail;
   DevBuf src, fwd, fwdtmp, eroots, pcount2, xcount2;   // second-level subtrees
   DevBuf hub_id, hub_v, hub_bm;                       // their hub adjacency bitmaps
-  DevBuf fadj, fdeg;                                  // forward adjacency (micro-table builds)
+  DevBuf fadj, fdeg, flong;                           // forward adjacency (table builds)
 };
 
 constexpr size_t kHistWords = MCE_MAX_P + 3;   // global histogram entries (sizes up to 2 + MCE_MAX_P)
@@ -361,10 +361,11 @@ mce_status run_impl(mce_engine* e, int32_t n, int64_t nnz, const int32_t* row_pt
   const bool early_fadj = !stat && !l2 && !subset;
   if (early_fadj &&
       ((h = take(arena, B.fadj, (size_t)std::max<int64_t>(nnz, 1) * sizeof(int))) != hipSuccess ||
-       (h = take(arena, B.fdeg, (size_t)n * sizeof(int))) != hipSuccess))
+       (h = take(arena, B.fdeg, (size_t)n * sizeof(int))) != hipSuccess ||
+       (h = take(arena, B.flong, (size_t)n * sizeof(int))) != hipSuccess))
     return alloc_fail(e, arena, h, "forward adjacency");
   if (early_fadj && (h = mce_launch_forward_adj(n, row_ptr, col_idx, dp<int>(B.rnd), dp<int>(B.fadj),
-                                                dp<int>(B.fdeg), e->num_cu * 16, s)) != hipSuccess)
+                                                dp<int>(B.fdeg), dp<int>(B.flong), ctl, e->num_cu * 16, s)) != hipSuccess)
     return hip_fail(e, h, "forward adjacency launch");
   if ((h = mce_launch_orient(n, row_ptr, col_idx, dp<int>(B.rnd), subset ? roots : nullptr, cnt,
                              dp<int>(B.pcount), dp<int>(B.xcount), ctl, l2 ? dp<u64>(B.fwd) : nullptr,
@@ -509,7 +510,8 @@ mce_status run_impl(mce_engine* e, int32_t n, int64_t nnz, const int32_t* row_pt
     // room for nnz more entries)
     if (use_fadj && !early_fadj &&
         ((h = take(arena, B.fadj, (size_t)std::max<int64_t>(nnz, 1) * sizeof(int))) != hipSuccess ||
-         (h = take(arena, B.fdeg, (size_t)n * sizeof(int))) != hipSuccess))
+         (h = take(arena, B.fdeg, (size_t)n * sizeof(int))) != hipSuccess ||
+         (h = take(arena, B.flong, (size_t)n * sizeof(int))) != hipSuccess))
       return alloc_fail(e, arena, h, "forward adjacency");
     if (micro_nw) {
       const size_t frame_bytes = 6 * sizeof(u64) * (size_t)micro_nw;
@@ -529,7 +531,7 @@ mce_status run_impl(mce_engine* e, int32_t n, int64_t nnz, const int32_t* row_pt
     if ((h = mce_launch_scan(dp<u64>(B.taboff), total, dp<u64>(B.scan), s)) != hipSuccess)
       return hip_fail(e, h, "table offset scan");
     if (use_fadj && !early_fadj && (h = mce_launch_forward_adj(n, row_ptr, col_idx, dp<int>(B.rnd), dp<int>(B.fadj),
-                                                dp<int>(B.fdeg), e->num_cu * 16, s)) != hipSuccess)
+                                                dp<int>(B.fdeg), dp<int>(B.flong), ctl, e->num_cu * 16, s)) != hipSuccess)
       return hip_fail(e, h, "forward adjacency launch");
   }
   if (timing) (void)hipEventRecord(e->ev[3], s);
@@ -1050,7 +1052,7 @@ void mce_destroy(mce_engine* e) {
   DevBuf* bufs[] = {&b.ctl,    &b.deg,    &b.rnd,     &b.core,    &b.alive0, &b.alive1,  &b.front0, &b.front1,
                     &b.bfront0, &b.bfront1, &b.pcount, &b.xcount,  &b.lists,  &b.taboff,  &b.scan,   &b.heap,
                     &b.wl,     &b.slots,  &b.stats,   &b.mstack,  &b.mail,   &b.src,     &b.fwd,    &b.fwdtmp,
-                    &b.eroots, &b.pcount2, &b.xcount2, &b.hub_id, &b.hub_v,  &b.hub_bm, &b.fadj, &b.fdeg};
+                    &b.eroots, &b.pcount2, &b.xcount2, &b.hub_id, &b.hub_v,  &b.hub_bm, &b.fadj, &b.fdeg, &b.flong};
   for (DevBuf* d : bufs) release(*d);
   if (e->host.p) (void)hipHostFree(e->host.p);
   for (auto& ev : e->ev)

@@ -101,6 +101,7 @@ struct MceCtl {
   u64 pairs_hash;        // sum of their clique hashes
   int l2_roots;          // second-level roots (forward edges of the vertex roots)
   int nhubs;             // vertices of degree >= HUB_MIN_DEG seen (the first ones get an adjacency bitmap)
+  int nlong;             // forward adjacency: rows too long for one wavefront, listed for the second pass
   // per classification variant (subgraph mode, micro sub-class on/off) and
   // sub-class: roots, largest |P|, largest |X|, largest row count, heap words
   int sub_count[MCE_NVAR][MCE_NSUB];

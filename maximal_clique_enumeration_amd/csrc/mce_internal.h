@@ -182,8 +182,8 @@ struct BuildParams {
   const int* hub_id;     // second-level subtrees: hub index of each vertex (-1: none), or NULL
   const u64* hub_bm;     // hub adjacency bitmaps, hub_words u64 each
   int hub_words;
-  // forward adjacency (micro tables), or NULL: vertex v's neighbours after v in
-  // the peel order at fadj[rp[v] .. rp[v] + fdeg[v]), in id order
+  // forward adjacency (micro tables, X rows), or NULL: vertex v's neighbours
+  // after v in the peel order at fadj[rp[v] .. rp[v] + fdeg[v]), in id order
   const int* fadj;
   const int* fdeg;
 };
@@ -200,10 +200,10 @@ int mce_peel_max_blocks(int num_cu);
 // roots == NULL: the roots are 0 .. nroots-1. fwd == NULL: first-level roots,
 // tallied per sub-class; else the later-neighbour counts go to fwd (u64) and
 // the second-level roots are tallied by mce_launch_l2_roots.
-// Forward adjacency: fadj[rp[v] + k] = the k-th neighbour of v after v in the
-// peel order (id order), fdeg[v] = how many there are.
+// Forward adjacency: fadj[rp[v] .. rp[v] + fdeg[v]) = the neighbours of v after
+// v in the peel order, in id order. flong: n ints of scratch (the long rows' list).
 hipError_t mce_launch_forward_adj(int n, const int* rp, const int* ci, const int* rnd, int* fadj, int* fdeg,
-                                  int blocks, hipStream_t s);
+                                  int* flong, MceCtl* ctl, int blocks, hipStream_t s);
 // fdeg: the forward adjacency's row lengths, when every vertex is a root of a
 // first-level run (roots == NULL, fwd == NULL): |P| is read from it.
 hipError_t mce_launch_orient(int n, const int* rp, const int* ci, const int* rnd, const int* roots, int nroots,

@@ -1245,20 +1245,43 @@ __global__ __launch_bounds__(256) void k_orient(int n, const int* __restrict__ r
 }
 
 // Forward adjacency of every vertex (the oriented graph of section 2.4): the
-// neighbours after v in the peel order, kept in id order at the start of v's
-// own CSR span (so no offsets need computing), and their number. Micro-table
-// builds read these rows instead of whole CSR rows: every edge between two
-// members of a subtree's P u X sits in the forward row of its earlier end, and
-// a forward row is no longer than that end's core number, where a CSR row can
-// be as long as the maximum degree. One wavefront per vertex, its lanes over
-// the row; a ballot keeps the entries in order.
+// neighbours after v in the peel order, kept at the start of v's own CSR span
+// (so no offsets need computing), and their number. Micro-table builds read
+// these rows instead of whole CSR rows: every edge between two members of a
+// subtree's P u X sits in the forward row of its earlier end, and a forward row
+// is no longer than that end's core number, where a CSR row can be as long as
+// the maximum degree. The readers look every entry up in a hash, so the order
+// of a forward row is free, but both passes keep it in id order: rows of up
+// to FWD_LONG entries are taken by one wavefront (a ballot keeps them in order);
+// a longer row is only listed here, and k_forward_adj_long gives each one a
+// whole block that takes 1,024 entries at a time (a hub's row, tens of
+// thousands of entries on power-law graphs, kept one wavefront busy for
+// milliseconds).
+#define FWD_LONG 1024
 __global__ __launch_bounds__(256) void k_forward_adj(int n, const int* __restrict__ rp, const int* __restrict__ ci,
                                                       const int* __restrict__ rnd, int* __restrict__ fadj,
-                                                      int* __restrict__ fdeg) {
+                                                      int* __restrict__ fdeg, int* __restrict__ flong, MceCtl* ctl) {
+  // the block's long rows, listed in LDS and added to the list with one atomic
+  // (one per row on the shared count took a 4M-vertex graph's ~20k hub rows
+  // about 0.3 ms); a block with more than FWD_LCAP of them lists the rest
+  // directly
+  constexpr int FWD_LCAP = 256;
+  __shared__ int s_long[FWD_LCAP];
+  __shared__ int s_nl, s_base;
+  if (threadIdx.x == 0) s_nl = 0;
+  __syncthreads();
   const int lane = lane_id();
   const int nwaves = gridDim.x * (blockDim.x / MCE_WAVE);
   for (int v = blockIdx.x * (blockDim.x / MCE_WAVE) + threadIdx.x / MCE_WAVE; v < n; v += nwaves) {
     const int a = rp[v], b = rp[v + 1], rv = rnd[v];
+    if (b - a > FWD_LONG) {
+      if (lane == 0) {
+        const int q = atomicAdd(&s_nl, 1);
+        if (q < FWD_LCAP) s_long[q] = v;
+        else flong[atomicAdd(&ctl->nlong, 1)] = v;
+      }
+      continue;
+    }
     int k = 0;
     for (int base = a; base < b; base += MCE_WAVE) {
       const int e = base + lane;
@@ -1269,6 +1292,65 @@ __global__ __launch_bounds__(256) void k_forward_adj(int n, const int* __restric
       k += __popcll(m);
     }
     if (lane == 0) fdeg[v] = k;
+  }
+  __syncthreads();
+  const int nl = min(s_nl, FWD_LCAP);
+  if (threadIdx.x == 0) s_base = nl ? atomicAdd(&ctl->nlong, nl) : 0;
+  __syncthreads();
+  for (int i = threadIdx.x; i < nl; i += blockDim.x) flong[s_base + i] = s_long[i];
+}
+
+// The long rows listed by k_forward_adj, one block per row: each thread loads
+// four entries (then their rounds) per step, and the block places the step's
+// later entries in order (entry groups z, then wavefronts) behind the ones
+// already placed.
+__global__ __launch_bounds__(256) void k_forward_adj_long(const int* __restrict__ rp, const int* __restrict__ ci,
+                                                           const int* __restrict__ rnd, int* __restrict__ fadj,
+                                                           int* __restrict__ fdeg, const int* __restrict__ flong,
+                                                           MceCtl* ctl) {
+  constexpr int NW = 256 / MCE_WAVE;
+  __shared__ int s_cnt[4][NW];
+  const int lane = lane_id(), wv = threadIdx.x / MCE_WAVE;
+  const int nl = ld_relaxed(&ctl->nlong);
+  for (int j = blockIdx.x; j < nl; j += gridDim.x) {
+    const int v = flong[j];
+    const int a = rp[v], b = rp[v + 1], rv = rnd[v];
+    int k = 0;   // entries placed so far (the same in every thread)
+    for (int base = a; base < b; base += 4 * 256) {
+      int u[4];
+      bool lat[4];
+      u64 m[4];
+#pragma unroll
+      for (int z = 0; z < 4; z++) {
+        const int e = base + z * 256 + (int)threadIdx.x;
+        u[z] = e < b ? ci[e] : 0;
+      }
+#pragma unroll
+      for (int z = 0; z < 4; z++) {
+        const int e = base + z * 256 + (int)threadIdx.x;
+        lat[z] = e < b && order_after(rnd[u[z]], u[z], rv, v);
+      }
+#pragma unroll
+      for (int z = 0; z < 4; z++) {
+        m[z] = ballot(lat[z]);
+        if (lane == 0) s_cnt[z][wv] = __popcll(m[z]);
+      }
+      __syncthreads();
+      int before = k, total = 0;
+#pragma unroll
+      for (int z = 0; z < 4; z++) {
+        int off = before;
+        for (int w = 0; w < NW; w++) {
+          if (w < wv) off += s_cnt[z][w];
+          total += s_cnt[z][w];
+        }
+        if (lat[z]) fadj[a + off + mbcnt(m[z])] = u[z];
+        for (int w = 0; w < NW; w++) before += s_cnt[z][w];
+      }
+      k += total;
+      __syncthreads();   // s_cnt is rewritten by the next step
+    }
+    if (threadIdx.x == 0) fdeg[v] = k;
   }
 }
 
@@ -1630,9 +1712,12 @@ hipError_t mce_launch_orient(int n, const int* rp, const int* ci, const int* rnd
 }
 
 hipError_t mce_launch_forward_adj(int n, const int* rp, const int* ci, const int* rnd, int* fadj, int* fdeg,
-                                  int blocks, hipStream_t s) {
+                                  int* flong, MceCtl* ctl, int blocks, hipStream_t s) {
   const int nb = max(1, min(blocks, (n + 3) / 4));   // four wavefronts a block, one vertex each at a time
-  hipLaunchKernelGGL(k_forward_adj, dim3(nb), dim3(256), 0, s, n, rp, ci, rnd, fadj, fdeg);
+  hipLaunchKernelGGL(k_forward_adj, dim3(nb), dim3(256), 0, s, n, rp, ci, rnd, fadj, fdeg, flong, ctl);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k_forward_adj_long, dim3(max(1, blocks)), dim3(256), 0, s, rp, ci, rnd, fadj, fdeg, flong, ctl);
   return hipGetLastError();
 }
 
