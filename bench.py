@@ -198,7 +198,12 @@ def cu_load(trace, num_cu):
     most tree nodes any of its blocks visited)."""
     out = []
     for lid in sorted({t["launch"] for t in trace}):
-        rs = [t for t in trace if t["launch"] == lid]
+        # (a wave that found the run already stopped returns before it records anything)
+        rs = [t for t in trace if t["launch"] == lid and t["start_tick"]]
+        if not rs:
+            out.append({"launch": lid, "waves": 0, "cus_seen": 0, "cu_busy_frac": None, "wave_busy_frac": None,
+                        "cu_mean_wave_busy_frac": None, "cu_load_max_over_mean": None, "span_ms": None})
+            continue
         span = max(t["end_tick"] for t in rs) - min(t["start_tick"] for t in rs)
         per_cu = {}
         for t in rs:
