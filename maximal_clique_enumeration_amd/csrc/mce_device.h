@@ -27,7 +27,9 @@ typedef unsigned int u32;
 #define MCE_SUB_MICRO (2 * MCE_NCLASS)
 #define MCE_NSUB (2 * MCE_NCLASS + 1)
 #define MCE_MICRO_MAX 64
-#define MCE_LIGHT_BYTES 4096
+#ifndef MCE_LIGHT_BYTES
+#define MCE_LIGHT_BYTES 4096   // largest staged rows + X_X array of a "light" root
+#endif
 // classification variants tallied by the orientation: mode | (micro off << 1)
 #define MCE_NVAR 4
 // pivot keys pack (count << 20 | ~local index): local indices stay below 2^20

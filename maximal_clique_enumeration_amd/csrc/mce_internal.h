@@ -237,7 +237,10 @@ hipError_t mce_launch_scan(u64* a, int n, u64* tsum, hipStream_t s);
 // the ids and hash terms, then a rows kernel over nroots * parts blocks.
 hipError_t mce_launch_build(const BuildParams& prm, int blocks, hipStream_t s);
 
-SearchLayout mce_search_layout(int sub, int mode, int pcap, int xcap, int rcap, bool force_hbm, bool counters);
+// nroots, num_cu: the launch's roots and the device's CUs (a heavy sub-class of
+// few roots stages its tables in LDS when they fit)
+SearchLayout mce_search_layout(int sub, int mode, int pcap, int xcap, int rcap, int nroots, int num_cu,
+                               bool force_hbm, bool counters);
 // Resident wavefronts of a search layout over the whole chip (0 on error).
 int mce_search_max_workers(const SearchLayout& L, int num_cu);
 hipError_t mce_launch_search(const SearchLayout& L, const SearchParams& prm, hipStream_t s);

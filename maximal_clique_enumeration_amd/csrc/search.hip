@@ -1066,7 +1066,17 @@ static size_t a256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 // LDS words: histogram, hash terms, P ids (partial only), then the stack and the
 // staged rows and X_X array when they are placed in LDS.
-SearchLayout mce_search_layout(int sub, int mode, int pcap, int xcap, int rcap, bool force_hbm, bool counters) {
+// Heavy sub-classes (tables over MCE_LIGHT_BYTES) stage their rows in LDS too
+// when the launch has few roots (at most two per CU) and its largest table and
+// X_X array fit in this many bytes: a node's row reads then cost an LDS round
+// trip, not an L2 one, and a launch of few roots needs no more waves than the
+// LDS leaves (R-MAT's heaviest width-4 sample: 6.3 -> 3.6 ms). A launch of
+// thousands of heavy roots keeps them in HBM and its wavefronts (the 500k
+// Chung-Lu graph's width-2 launch ran slower with its rows in LDS).
+#define HEAVY_STAGE_BYTES (24 * 1024)
+
+SearchLayout mce_search_layout(int sub, int mode, int pcap, int xcap, int rcap, int nroots, int num_cu,
+                               bool force_hbm, bool counters) {
   SearchLayout L{};
   L.counters = counters;
   L.sub = sub;
@@ -1080,7 +1090,9 @@ SearchLayout mce_search_layout(int sub, int mode, int pcap, int xcap, int rcap, 
   L.levels = L.pcap;
   L.hcap = L.pcap + 3;   // clique sizes up to |R at the root| + |P| <= 2 + pcap
   const size_t rec = (size_t)REC_WORDS(W);
-  L.srows = !force_hbm && light && L.wclass <= 2;
+  const size_t stage = (size_t)L.rcap * W * 8 + (size_t)L.xcap * 4;
+  L.srows = !force_hbm && L.wclass <= 2 &&
+            (light || (nroots <= 2 * num_cu && stage <= (size_t)HEAVY_STAGE_BYTES));
   const size_t stack_words = (size_t)L.levels * rec;
   // width 1 keeps its level stack in VGPRs
   L.sstack = L.wclass > 0 && !force_hbm && L.wclass <= 2 && stack_words * 8 <= 12288;
