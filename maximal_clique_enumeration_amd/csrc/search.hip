@@ -339,27 +339,58 @@ __global__ __launch_bounds__(64) void k_search(SearchParams prm) {
         // Tomita pivot: most neighbours in P among P u X_P (and X_X with the full
         // subgraph); ties go to the largest key, i.e. the smallest local index.
         u32 best = 0;
+        if constexpr (W >= 2 && W <= 4) {
+          // every word's candidate rows are loaded before any is scored, so
+          // their reads overlap (one round trip where the words took W); a lane
+          // without a candidate reads row 0, which every table has
+          u64 pw[W], cwv[W], rw[W][W];
 #pragma unroll
-        for (int wb = 0; wb < W; wb++) {
-          const u64 cw = read_lane(pj | xj, wb);
-          if (cw == 0) continue;
-          st_prow += (u64)__popcll(cw);
-          const int i = wb * 64 + lane;
-          if ((cw >> lane) & 1ull) {
-            u32 c = 0;
-            if constexpr (W == 1) {
-              if (lane < p) {
-                c = (u32)__popcll(read_lane(pj, 0) & myrow);
-              } else {
-                c = (u32)__popcll(read_lane(pj, 0) & rows[i]);
-              }
-            } else {
-              const u64* row = rows + (size_t)i * W;
+          for (int w = 0; w < W; w++) {
+            pw[w] = read_lane(pj, w);
+            cwv[w] = read_lane(pj | xj, w);
+          }
 #pragma unroll
-              for (int w = 0; w < W; w++) c += (u32)__popcll(read_lane(pj, w) & row[w]);
+          for (int wb = 0; wb < W; wb++) {
+            const bool on = (cwv[wb] >> lane) & 1ull;
+            const u64* row = rows + (size_t)(on ? wb * 64 + lane : 0) * W;
+#pragma unroll
+            for (int w = 0; w < W; w++) rw[wb][w] = row[w];
+          }
+#pragma unroll
+          for (int wb = 0; wb < W; wb++) {
+            if (cwv[wb] == 0) continue;
+            st_prow += (u64)__popcll(cwv[wb]);
+            if ((cwv[wb] >> lane) & 1ull) {
+              u32 c = 0;
+#pragma unroll
+              for (int w = 0; w < W; w++) c += (u32)__popcll(pw[w] & rw[wb][w]);
+              const u32 key = (c << 20) | (u32)(MCE_MAX_LOCAL - (wb * 64 + lane));
+              best = best > key ? best : key;
             }
-            const u32 key = (c << 20) | (u32)(MCE_MAX_LOCAL - i);
-            best = best > key ? best : key;
+          }
+        } else {
+#pragma unroll
+          for (int wb = 0; wb < W; wb++) {
+            const u64 cw = read_lane(pj | xj, wb);
+            if (cw == 0) continue;
+            st_prow += (u64)__popcll(cw);
+            const int i = wb * 64 + lane;
+            if ((cw >> lane) & 1ull) {
+              u32 c = 0;
+              if constexpr (W == 1) {
+                if (lane < p) {
+                  c = (u32)__popcll(read_lane(pj, 0) & myrow);
+                } else {
+                  c = (u32)__popcll(read_lane(pj, 0) & rows[i]);
+                }
+              } else {
+                const u64* row = rows + (size_t)i * W;
+#pragma unroll
+                for (int w = 0; w < W; w++) c += (u32)__popcll(read_lane(pj, w) & row[w]);
+              }
+              const u32 key = (c << 20) | (u32)(MCE_MAX_LOCAL - i);
+              best = best > key ? best : key;
+            }
           }
         }
         if constexpr (IPX) {
