@@ -52,7 +52,9 @@ typedef enum {
   MCE_ERR_TIMEOUT = -6,  /* the run passed mce_config.timeout_ms and was abandoned; if the search
                             had started, the cliques found before the limit are kept (see
                             mce_result and mce_graph_facts.complete) */
-  MCE_ERR_LIMIT = -7     /* the graph exceeds a limit of this build (degeneracy > 2048) */
+  MCE_ERR_LIMIT = -7     /* the graph exceeds a limit of this build (degeneracy > 2048), or a micro
+                            frame stack overflowed at 2^20 frames (mce_run_static: at what its
+                            scratch holds) */
 } mce_status;
 
 /* Classes of malformed input, reported in mce_graph_info.graph_errors when
@@ -117,6 +119,12 @@ typedef struct {
   int32_t subgraph;       /* MCE_SUBGRAPH_* (0 = auto) */
   int32_t micro_donate_min_p; /* micro kernel: donate a batch of frames only if their |P| add up to
                              at least this; 0 = 10, else >= 1 */
+  int32_t micro_stack_frames; /* micro kernel: frames per wavefront stack in device memory to start
+                             with; 0 = 4096, else a power of two in [64, 2^20]. A run of mce_run or
+                             mce_run_roots whose stacks overflow is run again, whole, with four
+                             times as many (up to 2^20, then MCE_ERR_LIMIT); mce_stats reports the
+                             size the last run used. The engine keeps the grown size for its later
+                             runs. mce_run_static takes what its scratch holds instead. */
 } mce_config;
 
 /* Facts about the last graph run. */
@@ -175,7 +183,8 @@ typedef struct {
   uint64_t max_stack_frames; /* micro kernel: most frames one wavefront's stack held */
   int32_t micro_roots;       /* first-level subtrees searched by the micro kernel */
   int32_t micro_stack_cap;   /* frames per wavefront of the micro kernel's stack in device memory
-                                (4096; mce_run_static: what its scratch had room for, >= 256) */
+                                (mce_config.micro_stack_frames, grown after an overflow;
+                                mce_run_static: what its scratch had room for, >= 256) */
   uint64_t steps;            /* micro kernel: wavefront steps (each lane holding a frame takes one
                                 node or branch) */
   uint64_t lane_steps;       /* micro kernel: lanes holding a frame, summed over steps */

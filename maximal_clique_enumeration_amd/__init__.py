@@ -49,7 +49,8 @@ class mce_config(ctypes.Structure):
                 ("worker_list", ctypes.c_int32), ("donate_min_p", ctypes.c_int32),
                 ("validate", ctypes.c_int32), ("max_workers", ctypes.c_int32),
                 ("timeout_ms", ctypes.c_int64), ("flags", ctypes.c_uint32),
-                ("subgraph", ctypes.c_int32), ("micro_donate_min_p", ctypes.c_int32)]
+                ("subgraph", ctypes.c_int32), ("micro_donate_min_p", ctypes.c_int32),
+                ("micro_stack_frames", ctypes.c_int32)]
 
 
 class mce_graph_facts(ctypes.Structure):
@@ -247,7 +248,7 @@ class Engine:
                  validate: bool = True, max_workers: int = 0, timeout_ms: int = 120000,
                  hbm_staging: bool = False, phase_times: bool = False, subgraph: str = "auto",
                  counters: bool = False, micro: bool = True, micro_donate_min_p: int = 10, level: int = 1,
-                 search_times: bool = False, overlap: bool = True):
+                 search_times: bool = False, overlap: bool = True, micro_stack_frames: int = 0):
         import torch
         if device is None:
             device = torch.cuda.current_device()
@@ -258,6 +259,7 @@ class Engine:
         cfg.worker_list = 1 if worker_list else 0
         cfg.donate_min_p = donate_min_p
         cfg.micro_donate_min_p = micro_donate_min_p
+        cfg.micro_stack_frames = micro_stack_frames
         cfg.validate = 1 if validate else 0
         cfg.max_workers = max_workers
         cfg.timeout_ms = timeout_ms

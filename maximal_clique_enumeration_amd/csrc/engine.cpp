@@ -109,6 +109,7 @@ struct mce_engine {
   };
   Occ occ[kOccSlots] = {};
   int n_occ = 0;
+  int micro_stack = 4096;   // micro frame stack of mce_run / mce_run_roots, frames per wave (grows)
 };
 
 namespace {
@@ -202,9 +203,14 @@ int occupancy(mce_engine* e, int a, long long b, F query) {
 
 constexpr int kMaxHubs = 1024;                 // second-level orientation: hub adjacency bitmaps, at most
 constexpr size_t kHubBytes = 256ull << 20;     // this many, in at most this many bytes
-constexpr int kMicroStack = 4096;              // frames per wavefront stack of the micro search
+constexpr int kMicroStack = 4096;              // frames per wavefront stack of the micro search, to start with
+constexpr int kMicroStackMax = 1 << 20;        // ... grown 4x after an overflow, up to this many
 constexpr int kMicroStackMinStatic = 256;      // the smallest stack mce_run_static gives a micro wave
-constexpr int kMicroCoopRootsPerWave = 4;     // micro launches with this many roots per wave share pivot scans
+#ifndef MCE_MICRO_COOP_ROOTS_PER_WAVE
+#define MCE_MICRO_COOP_ROOTS_PER_WAVE 4
+#endif
+// micro launches with this many roots per wave share pivot scans
+constexpr int kMicroCoopRootsPerWave = MCE_MICRO_COOP_ROOTS_PER_WAVE;
 // Tables other than micro ones are built by the split build: a root's rows are
 // dealt over several blocks, about this many (root, part) blocks per CU.
 constexpr int kSplitBlocksPerCu = 16;
@@ -242,8 +248,10 @@ hipError_t scratch_address(int dev, void** out) {
 
 // One run. `arena` empty: the engine's own buffers (grown with hipMalloc);
 // else every buffer is carved from the static scratch and nothing is allocated.
-mce_status run_impl(mce_engine* e, int32_t n, int64_t nnz, const int32_t* row_ptr, const int32_t* col_idx,
-                    const int32_t* roots, int32_t nroots, bool subset, void* stream, Arena& arena) {
+// One attempt of a run. *grow: the micro kernel's frame stacks overflowed, and
+// the run should be made again with larger ones.
+mce_status run_once(mce_engine* e, int32_t n, int64_t nnz, const int32_t* row_ptr, const int32_t* col_idx,
+                    const int32_t* roots, int32_t nroots, bool subset, void* stream, Arena& arena, bool* grow) {
   const auto t0 = std::chrono::steady_clock::now();
   if (!e) return MCE_ERR_ARG;
   const bool stat = arena.base != nullptr;
@@ -495,7 +503,7 @@ mce_status run_impl(mce_engine* e, int32_t n, int64_t nnz, const int32_t* row_pt
   // micro frame stacks: kMicroStack frames per wave; in the static scratch,
   // the largest power of two that the space left holds, at least
   // kMicroStackMinStatic (an overflow at run time is MCE_ERR_LIMIT)
-  int micro_cap = kMicroStack;
+  int micro_cap = stat ? kMicroStack : e->micro_stack;
   if (total > 0) {
     const size_t mail_bytes = (size_t)std::max(micro_nw, 1) * mce_micro_mail_words() * sizeof(u64);
     if ((h = take(arena, B.taboff, (size_t)total * sizeof(u64))) != hipSuccess ||
@@ -698,10 +706,12 @@ mce_status run_impl(mce_engine* e, int32_t n, int64_t nnz, const int32_t* row_pt
   if ((h = hipStreamSynchronize(s)) != hipSuccess) return hip_fail(e, h, "synchronize at end");
   const u64* hres = reinterpret_cast<const u64*>(hio + sizeof(MceCtl));
   if (hctl->status & MCE_E_PROTO) return fail(e, MCE_ERR_DEVICE, "worker-list bookkeeping error");
-  if (hctl->status & MCE_E_LIMIT)
-    return fail(e, MCE_ERR_LIMIT,
-                "a subtree larger than its width class, or a micro frame stack (%d frames a wave) overflowed",
-                micro_cap);
+  if (hctl->status & MCE_E_LIMIT) return fail(e, MCE_ERR_LIMIT, "a subtree larger than its width class");
+  if (hctl->status & MCE_E_MSTACK) {
+    // the sums are of an aborted search: the caller runs again with larger stacks
+    *grow = !stat && micro_cap < kMicroStackMax;
+    return fail(e, MCE_ERR_LIMIT, "a micro frame stack (%d frames a wave) overflowed", micro_cap);
+  }
   if (hctl->status & MCE_E_HEAP) return fail(e, MCE_ERR_DEVICE, "induced-subgraph heap overflow");
 
   uint64_t* hist = e->hist;
@@ -755,6 +765,21 @@ mce_status run_impl(mce_engine* e, int32_t n, int64_t nnz, const int32_t* row_pt
   so.ms_total = ms_since(t0);
   if (!e->complete) return fail(e, MCE_ERR_TIMEOUT, "search ran past the time limit (results are partial)");
   return MCE_OK;
+}
+
+// A run: attempts until the micro kernel's frame stacks hold the search. No
+// bound short of the whole tree caps a wavefront's stack (its 64 lanes share
+// one LIFO stack, and a frame buried under newer ones stays there), so an
+// overflow aborts the attempt, and the next one gets four times the frames.
+// The engine keeps the grown size.
+mce_status run_impl(mce_engine* e, int32_t n, int64_t nnz, const int32_t* row_ptr, const int32_t* col_idx,
+                    const int32_t* roots, int32_t nroots, bool subset, void* stream, Arena& arena) {
+  for (;;) {
+    bool grow = false;
+    const mce_status st = run_once(e, n, nnz, row_ptr, col_idx, roots, nroots, subset, stream, arena, &grow);
+    if (!grow) return st;
+    e->micro_stack = std::min(kMicroStackMax, e->micro_stack * 4);
+  }
 }
 
 // Per-wave counters and phase times of the last run, read on demand.
@@ -886,7 +911,10 @@ mce_status mce_create(const mce_config* cfg, mce_engine** out) {
     std::memcpy(&c, cfg, sz);
     c.struct_size = sizeof(mce_config);
   }
-  if (c.donate_min_p < 1 || c.micro_donate_min_p < 0 || c.max_workers < 0 || c.timeout_ms < 0 ||
+  const bool stack_ok = c.micro_stack_frames == 0 ||
+                        (c.micro_stack_frames >= 64 && c.micro_stack_frames <= (1 << 20) &&
+                         (c.micro_stack_frames & (c.micro_stack_frames - 1)) == 0);
+  if (!stack_ok || c.donate_min_p < 1 || c.micro_donate_min_p < 0 || c.max_workers < 0 || c.timeout_ms < 0 ||
       c.subgraph < MCE_SUBGRAPH_AUTO ||
       c.subgraph > MCE_SUBGRAPH_FULL ||
       (c.flags & ~(MCE_FLAG_HBM_STAGING | MCE_FLAG_PHASE_TIMES | MCE_FLAG_COUNTERS | MCE_FLAG_NO_MICRO |
@@ -896,6 +924,7 @@ mce_status mce_create(const mce_config* cfg, mce_engine** out) {
   mce_engine* e = new (std::nothrow) mce_engine();
   if (!e) return MCE_ERR_NOMEM;
   e->cfg = c;
+  e->micro_stack = c.micro_stack_frames ? c.micro_stack_frames : kMicroStack;
   int dev = c.device;
   if (dev < 0) {
     if (hipGetDevice(&dev) != hipSuccess) {

@@ -16,6 +16,9 @@ typedef unsigned int u32;
 #define MCE_E_PROTO (1u << 18)     // worker-list bookkeeping went wrong
 #define MCE_E_ROOTS (1u << 19)     // a root id outside [0, n)
 #define MCE_E_HEAP (1u << 20)      // the induced-subgraph heap was too small
+#define MCE_E_MSTACK (1u << 21)    // a micro frame stack overflowed (the engine runs again with larger ones)
+// a search kernel that finds any of these set searches nothing more
+#define MCE_E_STOP (MCE_E_HEAP | MCE_E_LIMIT | MCE_E_TIMEOUT | MCE_E_MSTACK)
 
 // Bitset-width classes: widths 1, 2, 4, 8, 16, 32 words of 64 bits (P up to 2048).
 #define MCE_NCLASS 6

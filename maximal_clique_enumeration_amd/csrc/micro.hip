@@ -162,7 +162,7 @@ __global__ __launch_bounds__(64) void k_search_micro(MicroParams prm) {
   const int wid = blockIdx.x;
   MceWl* wl = prm.wl;
   // a failed build, or a run already past its time limit: search nothing
-  if (ld_relaxed(prm.status) & (MCE_E_HEAP | MCE_E_LIMIT | MCE_E_TIMEOUT)) {
+  if (ld_relaxed(prm.status) & MCE_E_STOP) {
     if (wid == 0 && lane == 0 && prm.taken) {
       const u32 ctr = ld_relaxed(&wl->root_ctr);
       st_relaxed(prm.taken, min(ctr, (u32)prm.nroots));
@@ -523,7 +523,7 @@ __global__ __launch_bounds__(64) void k_search_micro(MicroParams prm) {
           // move the oldest MCE_WAVE LDS frames to HBM (top - mid > MICRO_L - 64 here)
           if (mid - bot + (u32)MCE_WAVE > cap) {
             if (lane == 0) {
-              atomicOr(prm.status, MCE_E_LIMIT);
+              atomicOr(prm.status, MCE_E_MSTACK);
               st_relaxed(&wl->done, 1u);
             }
             abort = true;

@@ -207,7 +207,7 @@ __global__ __launch_bounds__(64) void k_search(SearchParams prm) {
 
   // a failed build leaves some tables unwritten, and a run past its time limit
   // goes no further: search nothing
-  if (ld_relaxed(prm.status) & (MCE_E_HEAP | MCE_E_LIMIT | MCE_E_TIMEOUT)) {
+  if (ld_relaxed(prm.status) & MCE_E_STOP) {
     if (wid == 0 && lane == 0 && prm.taken) st_relaxed(prm.taken, min(ld_relaxed(&wl->root_ctr), (u32)prm.nroots));
     return;
   }
@@ -649,7 +649,7 @@ __global__ __launch_bounds__(64) void k_search_w1(SearchParams prm) {
   int* xx = SROWS ? (int*)(lds + prm.l_xx) : (int*)(slot + prm.s_xx);
   u64* lrows = lds + prm.l_rows;
 
-  if (ld_relaxed(prm.status) & (MCE_E_HEAP | MCE_E_LIMIT | MCE_E_TIMEOUT)) {
+  if (ld_relaxed(prm.status) & MCE_E_STOP) {
     if (wid == 0 && lane == 0 && prm.taken) st_relaxed(prm.taken, min(ld_relaxed(&wl->root_ctr), (u32)prm.nroots));
     return;
   }

@@ -66,6 +66,17 @@ def test_unknown_flags_are_rejected_before_any_device_work(lib):
     assert not h.value
 
 
+@pytest.mark.parametrize("frames", [1, 63, 100, 3000, 1 << 21, -64])
+def test_bad_micro_stack_sizes_are_rejected_before_any_device_work(lib, frames):
+    cfg = mce.mce_config()
+    assert mce.mce_config_init(cfg) == 0
+    assert cfg.micro_stack_frames == 0          # 0: the default size
+    cfg.micro_stack_frames = frames             # not a power of two in [64, 2^20]
+    h = ctypes.c_void_p()
+    assert mce.mce_create(cfg, h) == mce.MCE_ERR_ARG
+    assert not h.value
+
+
 def test_null_arguments_are_rejected(lib):
     lib.mce_result.restype = ctypes.c_int
     assert lib.mce_result(None, None, None, None, 0, None) == mce.MCE_ERR_ARG

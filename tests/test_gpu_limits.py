@@ -78,3 +78,26 @@ def test_full_run_after_a_stopped_one():
         assert got.count == MM45["count"] and got.hist == MM45["hist"]
         assert f"0x{got.hash:016x}" == MM45["hash"]
         assert e.graph_info()["roots_started"] == g.n
+
+
+def test_micro_stack_grows_after_an_overflow():
+    """A micro frame stack too small for the search aborts the attempt; the
+    engine runs the whole graph again with four times the frames, keeps that
+    size for later runs, and the result is exact."""
+    g = mi.moon_moser(45)
+    rp, ci = on_gpu(g)
+    print("case moon_moser45 micro_stack_frames=64, one wave", flush=True)
+    with mce.Engine(device=0, timeout_ms=60000, max_workers=1, worker_list=False,
+                    micro_stack_frames=64) as e:
+        for _ in range(2):
+            got = e.run(rp, ci)
+            st = e.stats()
+            assert got.complete
+            assert got.count == MM45["count"] and got.hist == MM45["hist"]
+            assert f"0x{got.hash:016x}" == MM45["hash"]
+            assert 64 < st["micro_stack_cap"] <= 1 << 20
+            assert st["micro_stack_cap"] & (st["micro_stack_cap"] - 1) == 0
+        grown = st["micro_stack_cap"]
+        # the grown size stays: a third run starts with it
+        e.run(rp, ci)
+        assert e.stats()["micro_stack_cap"] == grown
