@@ -39,6 +39,7 @@ struct Bufs {
   DevBuf src, fwd, fwdtmp, eroots, pcount2, xcount2;   // second-level subtrees
   DevBuf hub_id, hub_v, hub_bm;                       // their hub adjacency bitmaps
   DevBuf fadj, fdeg, flong;                           // forward adjacency (table builds)
+  DevBuf tcol, tcrow;                                 // the peel's compacted residual graph
 };
 
 constexpr size_t kHistWords = MCE_MAX_P + 3;   // global histogram entries (sizes up to 2 + MCE_MAX_P)
@@ -206,6 +207,12 @@ constexpr size_t kHubBytes = 256ull << 20;     // this many, in at most this man
 constexpr int kMicroStack = 4096;              // frames per wavefront stack of the micro search, to start with
 constexpr int kMicroStackMax = 1 << 20;        // ... grown 4x after an overflow, up to this many
 constexpr int kMicroStackMinStatic = 256;      // the smallest stack mce_run_static gives a micro wave
+// The peel finishes in block 0 on the residual graph compacted to 16-bit local
+// ids once at most this many entries remain (96 MB): one compute unit reads
+// them all, and past this it would take longer than the grid's rounds.
+#ifndef MCE_PEEL_TAIL_ENTRIES
+#define MCE_PEEL_TAIL_ENTRIES (48ll << 20)
+#endif
 #ifndef MCE_MICRO_COOP_ROOTS_PER_WAVE
 #define MCE_MICRO_COOP_ROOTS_PER_WAVE 4
 #endif
@@ -354,9 +361,20 @@ mce_status run_once(mce_engine* e, int32_t n, int64_t nnz, const int32_t* row_pt
   // block per two CUs (against one per CU: cheaper barriers and still ample
   // waves for a round; configurations 2-4 peel 3-5 % faster)
   int pblocks = n <= 16384 ? 1 : std::min(std::max(1, e->peel_blocks_max / 2), (n + 1023) / 1024);
+  // the grid peel's tail: the residual graph compacted for block 0 (not
+  // mce_run_static: its scratch is kept for the search; the grid peels to the end)
+  long long tcap = 0;
+  if (pblocks > 1 && !stat) {
+    tcap = std::min<long long>(nnz + nnz / 64 + (1ll << 20), MCE_PEEL_TAIL_ENTRIES);
+    if ((h = ensure(B.tcol, (size_t)tcap * sizeof(unsigned short))) != hipSuccess ||
+        (h = ensure(B.tcrow, (size_t)mce_peel_tail_rows() * sizeof(int))) != hipSuccess)
+      return hip_fail(e, h, "allocation");
+  }
   if ((h = mce_launch_peel(n, row_ptr, col_idx, dp<int>(B.deg), dp<int>(B.rnd), dp<int>(B.core),
                            dp<int>(B.alive0), dp<int>(B.alive1), dp<int>(B.front0), dp<int>(B.front1),
-                           dp<int>(B.bfront0), dp<int>(B.bfront1), ctl, budget, pblocks, s)) != hipSuccess)
+                           dp<int>(B.bfront0), dp<int>(B.bfront1), ctl, budget,
+                           tcap ? dp<unsigned short>(B.tcol) : nullptr, tcap, tcap ? dp<int>(B.tcrow) : nullptr,
+                           pblocks, s)) != hipSuccess)
     return hip_fail(e, h, "peel launch");
   if (timing) (void)hipEventRecord(e->ev[2], s);
   if (maxhubs > 0 && (h = mce_launch_hubs(n, row_ptr, col_idx, dp<int>(B.hub_id), dp<int>(B.hub_v),
@@ -1081,7 +1099,8 @@ void mce_destroy(mce_engine* e) {
   DevBuf* bufs[] = {&b.ctl,    &b.deg,    &b.rnd,     &b.core,    &b.alive0, &b.alive1,  &b.front0, &b.front1,
                     &b.bfront0, &b.bfront1, &b.pcount, &b.xcount,  &b.lists,  &b.taboff,  &b.scan,   &b.heap,
                     &b.wl,     &b.slots,  &b.stats,   &b.mstack,  &b.mail,   &b.src,     &b.fwd,    &b.fwdtmp,
-                    &b.eroots, &b.pcount2, &b.xcount2, &b.hub_id, &b.hub_v,  &b.hub_bm, &b.fadj, &b.fdeg, &b.flong};
+                    &b.eroots, &b.pcount2, &b.xcount2, &b.hub_id, &b.hub_v,  &b.hub_bm, &b.fadj, &b.fdeg, &b.flong,
+                    &b.tcol,   &b.tcrow};
   for (DevBuf* d : bufs) release(*d);
   if (e->host.p) (void)hipHostFree(e->host.p);
   for (auto& ev : e->ev)

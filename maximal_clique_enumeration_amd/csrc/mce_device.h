@@ -120,6 +120,10 @@ struct MceCtl {
   int bsize[3];          // peel: big-vertex frontier sizes (same rotation)
   int bedge[3];          // peel: the big vertices' CSR row lengths summed (same rotation)
   int asum[2];           // peel: each remaining list's CSR row lengths summed (by list parity)
+  int tmax[2];           // peel: each remaining list's largest degree (by list parity; short lists only)
+  u64 tsum[2];           // peel: the compacted residual graph's size in 16-bit entries (same)
+  int tlong;             // peel compaction: remaining vertices whose rows are written in spans
+  int tpad;
   u32 vpad;
   u32 vdone;             // validation: blocks of the entry pass that finished
   u64 vdown, vup;        // validation: edges from the larger (degree, id) end, and from the smaller

@@ -193,9 +193,13 @@ hipError_t mce_launch_zero(u64* p, size_t words, hipStream_t s);
 // Input checks.
 hipError_t mce_launch_validate(int n, long long nnz, const int* rp, const int* ci, MceCtl* ctl, int blocks,
                                hipStream_t s);
+// tcol (tcap 16-bit entries) and tcrow (mce_peel_tail_rows() ints): the residual
+// graph that block 0 of a grid peel finishes on once few vertices remain; tcap 0
+// keeps the grid to the end.
 hipError_t mce_launch_peel(int n, const int* rp, const int* ci, int* deg, int* rnd, int* core, int* alive0,
                            int* alive1, int* front0, int* front1, int* bfront0, int* bfront1, MceCtl* ctl,
-                           u64 budget, int blocks, hipStream_t s);
+                           u64 budget, unsigned short* tcol, long long tcap, int* tcrow, int blocks, hipStream_t s);
+int mce_peel_tail_rows();
 int mce_peel_max_blocks(int num_cu);
 // roots == NULL: the roots are 0 .. nroots-1. fwd == NULL: first-level roots,
 // tallied per sub-class; else the later-neighbour counts go to fwd (u64) and

@@ -281,6 +281,29 @@ __device__ __forceinline__ void pmin(int* p, int v) {
 #define PEEL_LDS_N 4096   // one-block peels of at most this many vertices keep degrees and rounds in LDS
 #endif
 #define PEEL_LPER 4                            // entries per thread and tile of a level pass
+// The tail: once at most PEEL_TT vertices remain, each with at most
+// PEEL_TMAXDEG live neighbours, and their live entries fill at most tcap
+// 16-bit words, block 0 finishes on the residual graph compacted to local ids
+// (0xFFFF pads rows and is no local id), with the degrees in its LDS.
+#define PEEL_TT 65535
+#define PEEL_TMAXDEG 32767
+#define PEEL_TLONG 8192     // rows longer than this (CSR entries) are compacted in spans by every wavefront
+#define PEEL_TSPAN 1024     // CSR entries of a span, and of a step of a shorter row (16 per lane)
+#define PEEL_TPER (PEEL_TSPAN / MCE_WAVE)
+#ifndef PEEL_TQ
+#define PEEL_TQ 2           // tail rounds: 16-byte loads per lane in flight
+#endif
+#ifndef PEEL_TFCAP
+#define PEEL_TFCAP 2048     // frontier entries of a tail round kept in LDS; more go to a global list
+#endif
+#define PEEL_TPOOL ((PEEL_TT + 1) / 2 + PEEL_TFCAP)   // LDS words of the tail: packed degrees, two lists
+// Entries a remaining vertex of degree d and CSR row length len takes in the
+// compacted graph: its live neighbours, padded to a multiple of 8 (one 16-byte
+// load per lane reads 8); a row compacted in spans pads every span.
+__device__ __forceinline__ long long tail_budget(int d, int len) {
+  const int extra = len > PEEL_TLONG ? 7 * ((len + PEEL_TSPAN - 1) / PEEL_TSPAN) : 0;
+  return (long long)((d + extra + 7) & ~7);
+}
 #define PEEL_LTILE (PEEL_LPER * PEEL_THREADS)   // entries per tile
 
 // Appends the lanes with `in` set to the next frontier: the regular list, or
@@ -366,6 +389,11 @@ struct PeelArgs {
   u64 deadline;
   int* sc;      // block 0's LDS counter slots while it runs a segment (12)
   int4* sfr;   // block 0's LDS frontier lists while it runs a segment: (v, row start, row end)
+  // the residual graph compacted for block 0 (peel_tail_build, peel_tail_rounds)
+  unsigned short* tcol;   // rows of 16-bit local ids, each padded to a multiple of 8 entries
+  long long tcap;         // entries tcol holds; 0: no compaction, the grid peels to the end
+  int* tcrow;             // row starts, PEEL_TT + 1
+  u32* pool;              // block 0's LDS in the tail: packed degrees and frontier lists
   // ping-pong buffers by parity (selects, not indexed arrays: no scratch memory)
   __device__ int* alive(int i) const { return (i & 1) ? alive1 : alive0; }
   __device__ int* front(int i) const { return (i & 1) ? front1 : front0; }
@@ -377,6 +405,8 @@ struct PeelState {
   int ph;               // slot of the pending frontier's sizes
   int fe;               // the pending frontier's CSR row lengths summed
   int ae;               // the remaining list's CSR row lengths summed (at its level pass)
+  int tdmax;            // its largest degree, and
+  long long tsize;      // its compacted size in entries (both when it is short enough to compact)
   bool level_known;     // the level's remaining list and k are known, its first round is not built
   u32 epoch;            // grid barriers passed (thread 0 of each block)
   u32 seg;              // segments of tiny rounds handed from the grid to block 0
@@ -401,6 +431,7 @@ struct PeelState {
 #define PEEL_TO_ALONE 1   // at most PEEL_SOLO vertices with PEEL_SOLO_EDGES edges remain
 #define PEEL_TO_SEG 2     // the next round removes at most PEEL_TINY vertices, big ones with PEEL_SEG_EDGES edges
 #define PEEL_TO_GRID 3    // block 0 hands back a larger round or a level pass
+#define PEEL_TO_TAIL 4    // few enough vertices remain to compact the residual graph for block 0
 #ifndef PEEL_TINY
 #define PEEL_TINY 32
 #endif
@@ -455,6 +486,9 @@ __device__ __forceinline__ int peel_rounds(const PeelArgs& A, PeelState& st, int
         // the kept rows' lengths decide whether block 0 may finish alone; they
         // cost a gather per vertex, so they are summed only once the list is short
         const bool sum_rows = st.na <= 8 * PEEL_SOLO;
+        // the kept vertices' largest degree and compacted size decide whether
+        // block 0 can finish on the compacted residual graph
+        const bool sum_tail = MODE == PEEL_GRID && A.tcap > 0 && st.na <= 2 * PEEL_TT;
         // Tiles of PEEL_LTILE entries per block: one atomic on the shared list
         // size per tile, and one per block for the minimum and the row sum
         // (same-address device-scope atomics serialise; one per wavefront and
@@ -462,14 +496,20 @@ __device__ __forceinline__ int peel_rounds(const PeelArgs& A, PeelState& st, int
         __shared__ int s_lv[PEEL_THREADS / MCE_WAVE + 1];
         __shared__ int s_mn;
         __shared__ u32 s_rows;
+        __shared__ int s_tmax;
+        __shared__ unsigned long long s_tsum;
         const int bw = threadIdx.x / MCE_WAVE, nbw = blockDim.x / MCE_WAVE;
         const int blk = BLOCK ? 0 : (int)blockIdx.x, nblk = BLOCK ? 1 : (int)gridDim.x;
         if (threadIdx.x == 0) {
           s_mn = 0x7FFFFFFF;
           s_rows = 0u;
+          s_tmax = 0;
+          s_tsum = 0ull;
         }
         int mn = 0x7FFFFFFF;
         u32 rows = 0;   // CSR row lengths of the kept vertices (at most nnz in all)
+        long long tsum = 0;
+        int tmax = 0;
         for (int tb = blk * PEEL_LTILE; tb < st.na; tb += nblk * PEEL_LTILE) {   // uniform in the block
           bool keep[PEEL_LPER], first[PEEL_LPER];
           int v[PEEL_LPER];
@@ -491,7 +531,14 @@ __device__ __forceinline__ int peel_rounds(const PeelArgs& A, PeelState& st, int
               const int dv = pld<S>(&A.deg[v[q]]);
               mn = min(mn, dv);
               first[q] = dv <= kn;
-              if (sum_rows) rows += (u32)(rp[v[q] + 1] - rp[v[q]]);
+              if (sum_rows || sum_tail) {
+                const int len = rp[v[q] + 1] - rp[v[q]];
+                if (sum_rows) rows += (u32)len;
+                if (sum_tail) {
+                  tsum += tail_budget(dv, len);
+                  tmax = max(tmax, dv);
+                }
+              }
             }
           }
           u64 m[PEEL_LPER];
@@ -532,10 +579,20 @@ __device__ __forceinline__ int peel_rounds(const PeelArgs& A, PeelState& st, int
           const u32 wrows = wave_sum_u32(rows);
           if (lane == 0 && wrows) atomicAdd(&s_rows, wrows);
         }
+        if (sum_tail) {
+          const u64 wts = wave_sum_u64((u64)tsum);
+          const u32 wtm = wave_max_u32((u32)tmax);
+          if (lane == 0) {
+            if (wts) atomicAdd(&s_tsum, (unsigned long long)wts);
+            if (wtm) atomicMax(&s_tmax, (int)wtm);
+          }
+        }
         __syncthreads();
         if (threadIdx.x == 0) {
           if (s_mn != 0x7FFFFFFF) pmin<S>(&ctl->min_deg[st.cur ^ 1], s_mn);
           if (s_rows) padd<S>(&ctl->asum[st.cur ^ 1], (int)s_rows);
+          if (s_tsum) __hip_atomic_fetch_add(&ctl->tsum[st.cur ^ 1], (u64)s_tsum, __ATOMIC_RELAXED, S);
+          if (s_tmax) __hip_atomic_fetch_max(&ctl->tmax[st.cur ^ 1], s_tmax, __ATOMIC_RELAXED, S);
         }
         PEEL_MARK(tl);
         grid_sync(ctl, A.deadline, st.epoch, BLOCK);
@@ -546,6 +603,8 @@ __device__ __forceinline__ int peel_rounds(const PeelArgs& A, PeelState& st, int
         st.na = pld<S>(&ctl->asize[st.cur]);
         const int kmin = pld<S>(&ctl->min_deg[st.cur]);   // no remaining vertex: k stays the degeneracy
         st.ae = sum_rows ? pld<S>(&ctl->asum[st.cur]) : 0x7FFFFFFF;
+        st.tsize = sum_tail ? (long long)__hip_atomic_load(&ctl->tsum[st.cur], __ATOMIC_RELAXED, S) : 0x7FFFFFFFFFFFFFFFll;
+        st.tdmax = sum_tail ? pld<S>(&ctl->tmax[st.cur]) : 0x7FFFFFFF;
         st.nf = pld<S>(&fs[p1]);
         st.nb = pld<S>(&bs[p1]);
         st.fe = pld<S>(&be[p1]);
@@ -553,6 +612,12 @@ __device__ __forceinline__ int peel_rounds(const PeelArgs& A, PeelState& st, int
         if (st.na == 0) return PEEL_DONE;
         const bool built = st.nf + st.nb > 0;   // then kmin == k + 1
         st.k = built ? kn : kmin;
+        // few enough vertices with few enough live entries: compact the
+        // residual graph, and block 0 finishes on it (the level's first round
+        // is found again there from the degrees)
+        if (MODE == PEEL_GRID && gridDim.x > 1 && sum_tail && st.na <= PEEL_TT && st.tdmax <= PEEL_TMAXDEG &&
+            st.tsize <= A.tcap)
+          return PEEL_TO_TAIL;
         if (MODE == PEEL_GRID && gridDim.x > 1 && peel_few_left(st)) {
           st.level_known = !built;
           return PEEL_TO_ALONE;
@@ -601,6 +666,8 @@ __device__ __forceinline__ int peel_rounds(const PeelArgs& A, PeelState& st, int
       pst<S>(&ctl->asize[st.cur ^ 1], 0);
       pst<S>(&ctl->asum[st.cur ^ 1], 0);
       pst<S>(&ctl->min_deg[st.cur ^ 1], 0x7FFFFFFF);
+      pst<S>(&ctl->tmax[st.cur ^ 1], 0);
+      __hip_atomic_store(&ctl->tsum[st.cur ^ 1], 0ull, __ATOMIC_RELAXED, S);
     }
     const int* fr = A.front(r);
     const int* bfr = A.bfront(r);
@@ -847,6 +914,8 @@ __device__ __forceinline__ int peel_hand_back(MceCtl* ctl, const PeelState& st, 
     pst<SA>(&ctl->asize[st.cur ^ 1], 0);
     pst<SA>(&ctl->asum[st.cur ^ 1], 0);
     pst<SA>(&ctl->min_deg[st.cur ^ 1], 0x7FFFFFFF);
+    pst<SA>(&ctl->tmax[st.cur ^ 1], 0);
+    __hip_atomic_store(&ctl->tsum[st.cur ^ 1], 0ull, __ATOMIC_RELAXED, SA);
     pst<SA>(&ctl->seg_state[0], res);
     pst<SA>(&ctl->seg_state[1], st.cur);
     pst<SA>(&ctl->seg_state[2], st.nf);
@@ -900,6 +969,535 @@ __device__ __forceinline__ int peel_wait(MceCtl* ctl, PeelState& st, u64 deadlin
   return res;
 }
 
+// ------------------------------------------------------------------ the peel's tail
+// Late in the peel few vertices remain, their rows still hold every removed
+// neighbour, and the rounds left are many and small: each costs the grid a
+// barrier and a few device-scope round trips. Once a level pass finds at most
+// PEEL_TT vertices left (peel_rounds returns PEEL_TO_TAIL), every block writes
+// the residual graph once, in local ids (a vertex's position in the remaining
+// list), keeping only live entries, and block 0 finishes alone with the
+// degrees in its LDS: a round is then one load of the frontier's rows and LDS
+// atomics, with no grid barrier.
+//
+// peel_tail_build, every block. L = the remaining list (na entries).
+//   a. block b takes L[bC, (b+1)C): rnd[v] = -2 - i marks v present with local
+//      id i (any negative rnd still reads as present, and rnd is written again
+//      when v leaves), the block-local prefix of the rows' sizes (tail_budget)
+//      into tcrow[], the block's total into front1[b], the rows longer than
+//      PEEL_TLONG into bfront0;
+//   b. tcrow[] += the totals of the blocks before; tcrow[na] = all of them; the
+//      long rows' write cursors (bfront1[i]) start at their row starts;
+//   c. rows of at most PEEL_TLONG entries: one wavefront each, live entries in
+//      CSR order, then 0xFFFF up to the row end; longer rows: PEEL_TSPAN-entry
+//      spans dealt to every wavefront, each reserving its live entries rounded
+//      up to 8 with an atomic on the row's cursor (the order of a row's
+//      entries does not matter) and padding them;
+//   d. the long rows' unreserved ends are padded.
+// A vertex's degree is exactly its live entries (every removed neighbour took
+// one). A row that would take more than its size sets MCE_E_PROTO instead of
+// writing past it; so does a short row that ends with another count.
+__device__ __forceinline__ int peel_tail_build(const PeelArgs& A, PeelState& st) {
+  __shared__ long long s_bc[PEEL_THREADS / MCE_WAVE + 1];
+  __shared__ long long s_off;
+  const int lane = lane_id();
+  const int na = st.na;
+  const int* L = A.alive(st.cur);
+  const int* __restrict__ rp = A.rp;
+  const int* __restrict__ ci = A.ci;
+  int* bsum = A.front1;      // per-block totals (int: at most tcap <= INT_MAX in all)
+  int* longl = A.bfront0;    // local ids of the long rows
+  int* cursor = A.bfront1;   // their write cursors, by local id
+  int* livec = A.alive(st.cur ^ 1);   // and their live entries (the other remaining list is free)
+  int* crow = A.tcrow;
+  unsigned short* tcol = A.tcol;
+  MceCtl* ctl = A.ctl;
+  const int nblk = gridDim.x;
+  const int C = (na + nblk - 1) / nblk;
+  const int lo = min(na, (int)blockIdx.x * C), hi = min(na, lo + C);
+  const int bw = threadIdx.x / MCE_WAVE, nbw = blockDim.x / MCE_WAVE;
+  // a. local ids, block-local prefix of the row sizes, long rows
+  long long run = 0;
+  for (int base = lo; base < hi; base += PEEL_THREADS) {   // uniform in the block
+    const int i = base + (int)threadIdx.x;
+    long long sz = 0;
+    bool lg = false;
+    if (i < hi) {
+      const int v = pld<SA>(&L[i]);
+      const int d = pld<SA>(&A.deg[v]);
+      const int len = rp[v + 1] - rp[v];
+      sz = tail_budget(d, len);
+      lg = len > PEEL_TLONG;
+      pst<SA>(&A.rnd[v], -2 - i);
+    }
+    long long incl = sz;
+#pragma unroll
+    for (int o = 1; o < MCE_WAVE; o <<= 1) {
+      const long long t = __shfl_up(incl, o);
+      if (lane >= o) incl += t;
+    }
+    if (lane == MCE_WAVE - 1) s_bc[bw] = incl;
+    const u64 lm = ballot(lg);
+    int lpos = 0;
+    if (lm && lane == 0) lpos = padd<SA>(&ctl->tlong, __popcll(lm));
+    lpos = read_lane(lpos, 0);
+    if (lg) pst<SA>(&longl[lpos + mbcnt(lm)], i);
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      long long r2 = 0;
+      for (int w = 0; w < nbw; w++) {
+        const long long c = s_bc[w];
+        s_bc[w] = r2;
+        r2 += c;
+      }
+      s_bc[nbw] = r2;
+    }
+    __syncthreads();
+    if (i < hi) pst<SA>(&crow[i], (int)(run + s_bc[bw] + incl - sz));
+    run += s_bc[nbw];
+    __syncthreads();   // s_bc is filled again for the next piece
+  }
+  if (threadIdx.x == 0) pst<SA>(&bsum[blockIdx.x], (int)run);
+  grid_sync(ctl, A.deadline, st.epoch);
+  if (ld_relaxed(&ctl->status) & MCE_E_TIMEOUT) return PEEL_TIMEOUT;
+  // b. the blocks' offsets
+  if (bw == 0) {
+    long long acc = 0, all = 0;
+    for (int j = lane; j < nblk; j += MCE_WAVE) {
+      const long long t = pld<SA>(&bsum[j]);
+      all += t;
+      if (j < (int)blockIdx.x) acc += t;
+    }
+    acc = (long long)wave_sum_u64((u64)acc);
+    all = (long long)wave_sum_u64((u64)all);
+    if (lane == 0) {
+      s_off = acc;
+      if (blockIdx.x == 0) pst<SA>(&crow[na], (int)all);
+    }
+  }
+  __syncthreads();
+  for (int i = lo + (int)threadIdx.x; i < hi; i += PEEL_THREADS) {
+    const int c = pld<SA>(&crow[i]) + (int)s_off;
+    pst<SA>(&crow[i], c);
+    pst<SA>(&cursor[i], c);
+    pst<SA>(&livec[i], 0);
+  }
+  grid_sync(ctl, A.deadline, st.epoch);
+  if (ld_relaxed(&ctl->status) & MCE_E_TIMEOUT) return PEEL_TIMEOUT;
+  // c. the live entries. Every rnd written so far went to memory with
+  // agent-scope stores, and the barrier above orders them: with this XCD's L2
+  // invalidated once, plain loads read them (-2 - local id: present).
+  if (threadIdx.x == 0) fence_acquire_agent();
+  __syncthreads();
+  const int gw = (int)blockIdx.x * nbw + bw, ngw = nblk * nbw;
+  u32 bad = 0;
+  for (int i = gw; i < na; i += ngw) {
+    const int v = pld<SA>(&L[i]);
+    const int a = rp[v], b = rp[v + 1];
+    if (b - a > PEEL_TLONG) continue;
+    const int start = pld<SA>(&crow[i]);
+    const int end = pld<SA>(&crow[i + 1]);
+    const int d = pld<SA>(&A.deg[v]);
+    int out = start;
+    for (int e0 = a; e0 < b; e0 += PEEL_TSPAN) {
+      int x[PEEL_TPER];
+#pragma unroll
+      for (int q = 0; q < PEEL_TPER; q++) {
+        const int e = e0 + q * MCE_WAVE + lane;
+        x[q] = e < b ? ci[e] : -1;
+      }
+#pragma unroll
+      for (int q = 0; q < PEEL_TPER; q++) x[q] = x[q] >= 0 ? A.rnd[x[q]] : 0;
+#pragma unroll
+      for (int q = 0; q < PEEL_TPER; q++) {
+        const bool live = x[q] <= -2;
+        const u64 m = ballot(live);
+        const int pos = out + mbcnt(m);
+        if (live) {
+          if (pos < end) tcol[pos] = (unsigned short)(-2 - x[q]);
+          else bad = 1;
+        }
+        out += __popcll(m);
+      }
+    }
+    if (out - start != d) bad = 1;
+    for (int p = out + lane; p < end; p += MCE_WAVE) tcol[p] = (unsigned short)0xFFFFu;
+  }
+  const int nlong = pld<SA>(&ctl->tlong);
+  for (int j0 = 0; j0 < nlong; j0 += MCE_WAVE) {
+    const int jl = j0 + lane;
+    const int il = jl < nlong ? pld<SA>(&longl[jl]) : 0;
+    const int vl = jl < nlong ? pld<SA>(&L[il]) : 0;
+    const int al = jl < nlong ? rp[vl] : 0, bl = jl < nlong ? rp[vl + 1] : 0;
+    const int endl = jl < nlong ? pld<SA>(&crow[il + 1]) : 0;
+    const int cnt = min(MCE_WAVE, nlong - j0);
+    for (int t = 0; t < cnt; t++) {
+      const int j = j0 + t;
+      const int i = read_lane(il, t), a = read_lane(al, t), b = read_lane(bl, t), end = read_lane(endl, t);
+      const int nsp = (b - a + PEEL_TSPAN - 1) / PEEL_TSPAN;
+      for (int c = (gw - j % ngw + ngw) % ngw; c < nsp; c += ngw) {
+        const int e0 = a + c * PEEL_TSPAN;
+        int x[PEEL_TPER];
+#pragma unroll
+        for (int q = 0; q < PEEL_TPER; q++) {
+          const int e = e0 + q * MCE_WAVE + lane;
+          x[q] = e < b ? ci[e] : -1;
+        }
+#pragma unroll
+        for (int q = 0; q < PEEL_TPER; q++) x[q] = x[q] >= 0 ? A.rnd[x[q]] : 0;
+        int tot = 0;
+#pragma unroll
+        for (int q = 0; q < PEEL_TPER; q++) tot += __popcll(ballot(x[q] <= -2));
+        const int sz = (tot + 7) & ~7;
+        int base = 0;
+        if (lane == 0 && sz) {
+          base = padd<SA>(&cursor[i], sz);
+          padd<SA>(&livec[i], tot);
+        }
+        base = read_lane(base, 0);
+        if (sz && base + sz > end) {
+          bad = 1;
+          continue;
+        }
+        int out = base;
+#pragma unroll
+        for (int q = 0; q < PEEL_TPER; q++) {
+          const bool live = x[q] <= -2;
+          const u64 m = ballot(live);
+          if (live) tcol[out + mbcnt(m)] = (unsigned short)(-2 - x[q]);
+          out += __popcll(m);
+        }
+        if (lane < sz - tot) tcol[out + lane] = (unsigned short)0xFFFFu;
+      }
+    }
+  }
+  if (wave_or_u32(bad) && lane == 0) atomicOr(&ctl->status, MCE_E_PROTO);
+  grid_sync(ctl, A.deadline, st.epoch);
+  if (ld_relaxed(&ctl->status) & (MCE_E_TIMEOUT | MCE_E_PROTO)) return PEEL_TIMEOUT;
+  // d. the long rows' ends past their last span; their live entries counted
+  for (int j = gw; j < nlong; j += ngw) {
+    const int i = pld<SA>(&longl[j]);
+    const int c = pld<SA>(&cursor[i]);
+    const int end = pld<SA>(&crow[i + 1]);
+    for (int p = c + lane; p < end; p += MCE_WAVE) tcol[p] = (unsigned short)0xFFFFu;
+    if (pld<SA>(&livec[i]) != pld<SA>(&A.deg[pld<SA>(&L[i])])) bad = 1;
+  }
+  if (wave_or_u32(bad) && lane == 0) atomicOr(&ctl->status, MCE_E_PROTO);
+  // the rows were written with plain stores: out of this XCD's L2 before the
+  // barrier (one write-back per block, after all of its waves' stores)
+  wait_stores_complete();
+  __syncthreads();
+  if (threadIdx.x == 0) fence_release_agent();
+  grid_sync(ctl, A.deadline, st.epoch);
+  if (ld_relaxed(&ctl->status) & (MCE_E_TIMEOUT | MCE_E_PROTO)) return PEEL_TIMEOUT;
+  return PEEL_TO_TAIL;
+}
+
+// Appends local id u of the lanes with `in` set to a tail frontier list: the
+// LDS list holds PEEL_TFCAP entries, more go to the global list `ov`. Whole wave.
+__device__ __forceinline__ void tail_push(bool in, int u, int* cnt, unsigned short* lst, int* ov) {
+  const u64 m = ballot(in);
+  if (!m) return;
+  int pos = 0;
+  if (lane_id() == 0) pos = atomicAdd(cnt, __popcll(m));
+  pos = read_lane(pos, 0) + mbcnt(m);
+  if (in) {
+    if (pos < PEEL_TFCAP) lst[pos] = (unsigned short)u;
+    else ov[pos - PEEL_TFCAP] = u;
+  }
+}
+
+// One group of up to 64 frontier entries (lane t holds entry t: its row
+// [a, b) in tcol, a multiple of 8 entries long; incl = the lanes' inclusive
+// prefix of their rows' 8-entry chunks, C = all of them). The group's chunks
+// are taken 64 at a time (a step: lane l takes chunk 64 s + l, whichever row
+// it falls in, found by a binary search over the lanes' prefix); this wave
+// takes steps sfirst, sfirst + sstep, ..., PEEL_TQ at a time (that many
+// 16-byte loads per lane in flight), and takes one degree from every neighbour
+// in them. A
+// load's 8 decrements are issued before any returned value is read, and the
+// joiners are appended only when the wave has any. Whole wave.
+__device__ __forceinline__ void tail_chunks(int a, int incl, int C, int sfirst, int sstep, int na, int k, u32* deg,
+                                            const unsigned short* __restrict__ tcol, int* cnt, unsigned short* nl,
+                                            int* nov) {
+  const int lane = lane_id();
+  const int nsteps = (C + MCE_WAVE - 1) / MCE_WAVE;
+  for (int s0 = sfirst; s0 < nsteps; s0 += PEEL_TQ * sstep) {
+    uint4 w[PEEL_TQ];
+#pragma unroll
+    for (int q = 0; q < PEEL_TQ; q++) {
+      const int c = (s0 + q * sstep) * MCE_WAVE + lane;
+      w[q] = make_uint4(0xFFFFFFFFu, 0xFFFFFFFFu, 0xFFFFFFFFu, 0xFFFFFFFFu);   // padding: no vertex
+      if (s0 + q * sstep < nsteps) {
+        // t = the lanes whose prefix is <= c: chunk c lies in lane t's row
+        int t = 0;
+#pragma unroll
+        for (int step = 32; step > 0; step >>= 1) {
+          const int v = __shfl(incl, t + step - 1);
+          if (v <= c) t += step;
+        }
+        // (every lane takes part in each shuffle: a lane that sits one out
+        // would read 0 from the lanes that do)
+        const int tt = min(t, MCE_WAVE - 1);
+        const int at = __shfl(a, tt);
+        const int pre = __shfl(incl, max(tt - 1, 0));
+        const int before = tt > 0 ? pre : 0;   // chunks of the rows before lane tt's
+        if (c < C) w[q] = *reinterpret_cast<const uint4*>(tcol + at + (c - before) * 8);
+      }
+    }
+    u32 jm = 0;
+#pragma unroll
+    for (int q = 0; q < PEEL_TQ; q++) {
+      u32 old[8];
+#pragma unroll
+      for (int h = 0; h < 8; h++) {
+        const u32 word = (h >> 1) == 0 ? w[q].x : (h >> 1) == 1 ? w[q].y : (h >> 1) == 2 ? w[q].z : w[q].w;
+        const u32 u = (word >> ((h & 1) * 16)) & 0xFFFFu;
+        old[h] = 0u;
+        if ((int)u < na) old[h] = atomicSub(&deg[u >> 1], 1u << ((u & 1u) * 16u));
+      }
+#pragma unroll
+      for (int h = 0; h < 8; h++) {
+        const u32 word = (h >> 1) == 0 ? w[q].x : (h >> 1) == 1 ? w[q].y : (h >> 1) == 2 ? w[q].z : w[q].w;
+        const u32 u = (word >> ((h & 1) * 16)) & 0xFFFFu;
+        const u32 sh = (u & 1u) * 16u;
+        if ((int)u < na && ((old[h] >> sh) & 0xFFFFu) == (u32)(k + 1)) {
+          atomicOr(&deg[u >> 1], 0x8000u << sh);
+          jm |= 1u << (q * 8 + h);
+        }
+      }
+    }
+    if (ballot(jm != 0u)) {
+#pragma unroll
+      for (int q = 0; q < PEEL_TQ; q++) {
+#pragma unroll
+        for (int h = 0; h < 8; h++) {
+          const u32 word = (h >> 1) == 0 ? w[q].x : (h >> 1) == 1 ? w[q].y : (h >> 1) == 2 ? w[q].z : w[q].w;
+          tail_push(((jm >> (q * 8 + h)) & 1u) != 0u, (int)((word >> ((h & 1) * 16)) & 0xFFFFu), cnt, nl, nov);
+        }
+      }
+    }
+  }
+}
+
+// Block 0 alone on the compacted residual graph, from the level peel_rounds
+// ended at: the same rule (a level's first round is every remaining vertex of
+// degree <= k; a round removes its frontier and a neighbour whose degree falls
+// from k + 1 to k joins the next; when a round removes nothing, k rises to the
+// smallest remaining degree). Degrees are packed 16-bit fields in LDS, two a
+// word. A vertex's field gets bit 15 when it joins a frontier; it then takes
+// exactly as many more decrements as neighbours of its that had not left when
+// it was counted, so no field ever borrows from its neighbour in the word, and
+// a field with bit 15 never reads k + 1 again. A round's rows are read in
+// steps of 64 chunks of 8 entries (one 16-byte load per lane, see tail_chunks).
+// A frontier of at most 64 entries has its steps dealt over all of the block's
+// waves; a larger one is cut into one slice per wave, each taken 64 entries at
+// a time (the next 64 entries' rows are loaded while a group's steps are
+// taken). Rounds and core numbers are written through the remaining list.
+__device__ __forceinline__ int peel_tail_rounds(const PeelArgs& A, PeelState& st, bool timer) {
+  // [0..2] frontier sizes (rotating), [3] remaining, [4] smallest degree, [5] vertices of the
+  // tentative level, [6] stop; s_wt: the waves' shares of a level's first round
+  __shared__ int s_t[8];
+  __shared__ int s_wt[PEEL_THREADS / MCE_WAVE + 1];
+  const int lane = lane_id();
+  const int bw = threadIdx.x / MCE_WAVE, nbw = blockDim.x / MCE_WAVE;
+  const int na = st.na;
+  const int nw = (na + 1) / 2;
+  const int* L = A.alive(st.cur);
+  const int* __restrict__ crow = A.tcrow;
+  const unsigned short* __restrict__ tcol = A.tcol;
+  u32* deg = A.pool;
+  unsigned short* fl0 = (unsigned short*)(A.pool + (PEEL_TT + 1) / 2);
+  unsigned short* fl1 = fl0 + PEEL_TFCAP;
+  for (int w = threadIdx.x; w < nw; w += blockDim.x) {
+    const u32 d0 = (u32)A.deg[L[2 * w]];
+    const u32 d1 = 2 * w + 1 < na ? (u32)A.deg[L[2 * w + 1]] : 0x8000u;   // padding: gone already
+    deg[w] = d0 | (d1 << 16);
+  }
+  if (threadIdx.x < 8) s_t[threadIdx.x] = 0;
+  int k = st.k, r = st.r, cur = 0, nf = 0, slot = 0, rot = 0;
+  bool entry = true;   // the level peel_rounds found: k is already that level
+  __syncthreads();
+  for (;;) {
+    if (nf == 0) {
+      // ---- a new level. Every remaining vertex has degree > k (>= k on
+      // entry): the level is kt = k + 1 (k on entry) when some vertex has
+      // that degree, else the smallest degree. Pass 1 counts the remaining
+      // vertices, their smallest degree, those of degree <= kt, and per
+      // thread its smallest degree and how many have it; pass 2 collects the
+      // level's first round, each thread's share placed by a block-wide scan.
+      const int kdone = k;
+      const int kt = entry ? k : k + 1;
+      entry = false;
+      if (threadIdx.x == 0) {
+        s_t[(slot + 2) % 3] = 0;
+        s_t[3] = 0;
+        s_t[4] = 0x7FFFFFFF;
+        s_t[5] = 0;
+      }
+      __syncthreads();
+      int rem = 0, mn = 0x7FFFFFFF, nmn = 0, le = 0;
+      for (int w0 = threadIdx.x; w0 < nw; w0 += 4 * PEEL_THREADS) {
+        u32 x[4];
+#pragma unroll
+        for (int q = 0; q < 4; q++) {
+          const int w = w0 + q * PEEL_THREADS;
+          x[q] = w < nw ? deg[w] : 0x80008000u;
+        }
+#pragma unroll
+        for (int q = 0; q < 4; q++) {
+#pragma unroll
+          for (int h = 0; h < 2; h++) {
+            const u32 f = h ? x[q] >> 16 : x[q] & 0xFFFFu;
+            if (f < 0x8000u) {
+              rem++;
+              le += (int)f <= kt;
+              if ((int)f < mn) {
+                mn = (int)f;
+                nmn = 0;
+              }
+              nmn += (int)f == mn;
+            }
+          }
+        }
+      }
+      const int wrem = (int)wave_sum_u32((u32)rem);
+      const int wle = (int)wave_sum_u32((u32)le);
+      const int wmn = wave_min_i32_nonneg(mn);
+      if (lane == 0) {
+        if (wrem) atomicAdd(&s_t[3], wrem);
+        if (wle) atomicAdd(&s_t[5], wle);
+        atomicMin(&s_t[4], wmn);
+      }
+      __syncthreads();
+      if (s_t[3] == 0) {
+        PEEL_MARK(tl);
+        st.k = kdone;
+        st.r = r;
+        st.na = 0;
+        return PEEL_DONE;
+      }
+      k = s_t[5] > 0 ? kt : s_t[4];
+      // pass 2: this thread's vertices of degree <= k, marked, at its place in the list
+      int c = s_t[5] > 0 ? le : (mn == k ? nmn : 0);
+      int incl = c;
+#pragma unroll
+      for (int o = 1; o < MCE_WAVE; o <<= 1) {
+        const int t = __shfl_up(incl, o);
+        if (lane >= o) incl += t;
+      }
+      if (lane == MCE_WAVE - 1) s_wt[bw] = incl;
+      __syncthreads();
+      if (threadIdx.x == 0) {
+        int run = 0;
+        for (int i = 0; i < nbw; i++) {
+          const int t = s_wt[i];
+          s_wt[i] = run;
+          run += t;
+        }
+        s_wt[nbw] = run;
+      }
+      __syncthreads();
+      {
+        unsigned short* fl = cur ? fl1 : fl0;
+        int* ov = cur ? A.front1 : A.front0;
+        int pos = s_wt[bw] + incl - c;
+        for (int w = threadIdx.x; w < nw && c > 0; w += PEEL_THREADS) {
+          u32 x = deg[w];
+          const u32 f0 = x & 0xFFFFu, f1 = x >> 16;
+          const bool in0 = f0 < 0x8000u && (int)f0 <= k, in1 = f1 < 0x8000u && (int)f1 <= k;
+          if (in0) {
+            x |= 0x8000u;
+            if (pos < PEEL_TFCAP) fl[pos] = (unsigned short)(2 * w);
+            else ov[pos - PEEL_TFCAP] = 2 * w;
+            pos++;
+            c--;
+          }
+          if (in1) {
+            x |= 0x80000000u;
+            if (pos < PEEL_TFCAP) fl[pos] = (unsigned short)(2 * w + 1);
+            else ov[pos - PEEL_TFCAP] = 2 * w + 1;
+            pos++;
+            c--;
+          }
+          if (in0 || in1) deg[w] = x;
+        }
+      }
+      nf = s_wt[nbw];
+      slot = (slot + 1) % 3;
+      __syncthreads();
+      PEEL_MARK(tl);
+    }
+    // ---- round r: remove the frontier (list cur), take one degree from each neighbour
+    if ((r & 63) == 0) {
+      if (threadIdx.x == 0) s_t[6] = past_deadline(A.deadline) ? 1 : 0;
+      __syncthreads();
+      if (s_t[6]) {
+        if (threadIdx.x == 0) atomicOr(&A.ctl->status, MCE_E_TIMEOUT);
+        return PEEL_TIMEOUT;
+      }
+    }
+    const int p1 = (slot + 1) % 3;
+    if (threadIdx.x == 0) s_t[(slot + 2) % 3] = 0;
+    const unsigned short* fl = cur ? fl1 : fl0;
+    const int* ov = cur ? A.front1 : A.front0;
+    unsigned short* nl = cur ? fl0 : fl1;
+    int* nov = cur ? A.front0 : A.front1;
+    // this wave's entries: all of a frontier of at most 64 (pieces shared by
+    // all waves), else a slice of about nf / nbw
+    const bool shared = nf <= MCE_WAVE;
+    const int lo = shared ? 0 : (int)(((long long)nf * bw) / nbw);
+    const int hi = shared ? nf : (int)(((long long)nf * (bw + 1)) / nbw);
+    int li = -1, a = 0, b = 0;
+    if (lo + lane < hi) {
+      const int j = lo + lane;
+      li = j < PEEL_TFCAP ? (int)fl[j] : ov[j - PEEL_TFCAP];
+      a = crow[li];
+      b = crow[li + 1];
+    }
+    for (int g0 = lo; g0 < hi; g0 += MCE_WAVE) {
+      // the next group's rows are in flight while this group's pieces are taken
+      int lin = -1, an = 0, bn = 0;
+      if (g0 + MCE_WAVE + lane < hi) {
+        const int j = g0 + MCE_WAVE + lane;
+        lin = j < PEEL_TFCAP ? (int)fl[j] : ov[j - PEEL_TFCAP];
+        an = crow[lin];
+        bn = crow[lin + 1];
+      }
+      // the group's vertices leave in round r (one wave writes them)
+      if (li >= 0 && (!shared || bw == r % nbw)) {
+        const int v = L[li];
+        A.rnd[v] = r;
+        A.core[v] = k;
+      }
+      int incl = (b - a) >> 3;   // the row's 8-entry chunks
+#pragma unroll
+      for (int o = 1; o < MCE_WAVE; o <<= 1) {
+        const int t = __shfl_up(incl, o);
+        if (lane >= o) incl += t;
+      }
+      const int C = read_lane(incl, MCE_WAVE - 1);
+      if (shared) {
+        // step s goes to wave (s + rot) mod nbw; rot moves on, so that rounds
+        // of few steps do not all start on the same waves
+        const int S = (C + MCE_WAVE - 1) / MCE_WAVE;
+        tail_chunks(a, incl, C, ((bw - rot) % nbw + nbw) % nbw, nbw, na, k, deg, tcol, &s_t[p1], nl, nov);
+        rot = (rot + S) % nbw;
+      } else {
+        tail_chunks(a, incl, C, 0, 1, na, k, deg, tcol, &s_t[p1], nl, nov);
+      }
+      li = lin;
+      a = an;
+      b = bn;
+    }
+    PEEL_MARK(tr);
+    __syncthreads();
+    nf = s_t[p1];
+    slot = p1;
+    cur ^= 1;
+    r++;
+  }
+}
+
 // Round-synchronous peel (section 2.4 asks for a degeneracy order; this is the
 // one the engine uses). Level k: every remaining vertex of current degree <= k
 // leaves in one round (rnd = round, core = k). The removed vertices'
@@ -919,31 +1517,40 @@ __device__ __forceinline__ int peel_wait(MceCtl* ctl, PeelState& st, u64 deadlin
 __global__ __launch_bounds__(PEEL_THREADS) void k_peel(int n, const int* __restrict__ rp,
                                                         const int* __restrict__ ci, int* deg, int* rnd, int* core,
                                                         int* alive0, int* alive1, int* front0, int* front1,
-                                                        int* bfront0, int* bfront1, MceCtl* ctl, u64 budget) {
+                                                        int* bfront0, int* bfront1, MceCtl* ctl, u64 budget,
+                                                        unsigned short* tcol, long long tcap, int* tcrow) {
   __shared__ int s_cnt[12];
   __shared__ int4 s_fr[2 * PEEL_TINY + 1];
-  // A graph of at most PEEL_LDS_N vertices peeled by one block keeps degrees,
-  // rounds and the list and frontier counters in LDS (a copy of the control
-  // block): the peel's generic loads, stores and atomics then go to LDS instead
-  // of the L2, and a round's barrier waits on no global store. The rounds and
-  // any status bit are copied out at the end.
-  __shared__ int s_deg[PEEL_LDS_N], s_rnd[PEEL_LDS_N];
-  __shared__ MceCtl s_ctl;
+  // One LDS pool, used one of two ways in a launch:
+  //  - a graph of at most PEEL_LDS_N vertices peeled by one block keeps
+  //    degrees, rounds and the list and frontier counters in LDS (a copy of the
+  //    control block): the peel's generic loads, stores and atomics then go to
+  //    LDS instead of the L2, and a round's barrier waits on no global store
+  //    (the rounds and any status bit are copied out at the end);
+  //  - block 0 of a grid peel, in its tail: packed degrees and frontier lists.
+  __shared__ __align__(128) u32 s_pool[PEEL_TPOOL];
+  static_assert(2 * PEEL_LDS_N + (sizeof(MceCtl) + 3) / 4 <= PEEL_TPOOL, "the small-graph state fits the pool");
+  static_assert(alignof(MceCtl) <= 128 && (2 * PEEL_LDS_N * 4) % alignof(MceCtl) == 0,
+                "the control block's copy is aligned in the pool");
+  int* s_deg = (int*)s_pool;
+  int* s_rnd = s_deg + PEEL_LDS_N;
+  MceCtl* s_ctl = (MceCtl*)(s_pool + 2 * PEEL_LDS_N);
   if (ld_relaxed(&ctl->status) != 0) return;   // rejected input: nothing to order
   const u64 t0 = wall_clock64();
   const bool lds = gridDim.x == 1 && n <= PEEL_LDS_N;
-  MceCtl* pc = lds ? &s_ctl : ctl;   // the peel's counters
+  MceCtl* pc = lds ? s_ctl : ctl;   // the peel's counters
   if (lds) {
-    for (int i = threadIdx.x; i < (int)(sizeof(MceCtl) / sizeof(u32)); i += blockDim.x) ((u32*)&s_ctl)[i] = 0u;
+    for (int i = threadIdx.x; i < (int)(sizeof(MceCtl) / sizeof(u32)); i += blockDim.x) ((u32*)s_ctl)[i] = 0u;
     __syncthreads();
   }
-  PeelArgs A{n,      rp,     ci,      lds ? s_deg : deg, lds ? s_rnd : rnd, core,       alive0, alive1, front0,
-             front1, bfront0, bfront1, pc, t0 + budget, s_cnt, s_fr};
+  PeelArgs A{n,      rp,     ci,      lds ? s_deg : deg, lds ? s_rnd : rnd, core,        alive0,
+             alive1, front0, front1,  bfront0,           bfront1,           pc,          t0 + budget,
+             s_cnt,  s_fr,   tcol,    gridDim.x > 1 ? tcap : 0LL,           tcrow,       s_pool};
   const int gtid = blockIdx.x * blockDim.x + threadIdx.x;
   const int gsize = gridDim.x * blockDim.x;
   const bool timer = blockIdx.x == 0 && threadIdx.x == 0;
   // k starts below every degree: the first level is the smallest degree
-  PeelState st{0, 0, 0, -1, 0, n, 0, 0, 0, false, 0u, 0u, 0, 0, 0, t0};
+  PeelState st{0, 0, 0, -1, 0, n, 0, 0, 0, 0, 0, false, 0u, 0u, 0, 0, 0, t0};
 
   for (int v = gtid; v < n; v += gsize) {
     pst<SA>(&A.deg[v], rp[v + 1] - rp[v]);
@@ -963,6 +1570,11 @@ __global__ __launch_bounds__(PEEL_THREADS) void k_peel(int n, const int* __restr
     pst<SA>(&pc->asum[1], 0);
     pst<SA>(&pc->min_deg[0], 0x7FFFFFFF);
     pst<SA>(&pc->min_deg[1], 0x7FFFFFFF);
+    for (int i = 0; i < 2; i++) {
+      pst<SA>(&pc->tmax[i], 0);
+      __hip_atomic_store(&pc->tsum[i], 0ull, __ATOMIC_RELAXED, SA);
+    }
+    pst<SA>(&pc->tlong, 0);
   }
   grid_sync(ctl, A.deadline, st.epoch);
 
@@ -983,6 +1595,16 @@ __global__ __launch_bounds__(PEEL_THREADS) void k_peel(int n, const int* __restr
         res = peel_hand_back(ctl, st, res, A.deadline);
         if (res == PEEL_TO_GRID) continue;
       }
+      if (res == PEEL_TO_TAIL) {
+        // every block writes the compacted residual graph; block 0 finishes on it
+        res = peel_tail_build(A, st);
+        if (blockIdx.x != 0) return;
+        if (res == PEEL_TO_TAIL) {
+          fence_acquire_agent();
+          res = peel_tail_rounds(A, st, timer);
+        }
+        break;
+      }
       if (res == PEEL_TO_ALONE) {
         if (blockIdx.x != 0) return;
         // block 0 goes on alone: drop any stale copy its XCD's caches may hold
@@ -995,7 +1617,7 @@ __global__ __launch_bounds__(PEEL_THREADS) void k_peel(int n, const int* __restr
   } else {
     res = peel_rounds<SW, PEEL_ALONE>(A, st, bwave, bwaves, timer);
   }
-  if (lds && threadIdx.x == 0 && s_ctl.status) atomicOr(&ctl->status, s_ctl.status);
+  if (lds && threadIdx.x == 0 && s_ctl->status) atomicOr(&ctl->status, s_ctl->status);
   if (res < 0) return;
   if (lds) {
     __syncthreads();
@@ -1463,9 +2085,11 @@ hipError_t mce_launch_validate(int n, long long nnz, const int* rp, const int* c
 
 hipError_t mce_launch_peel(int n, const int* rp, const int* ci, int* deg, int* rnd, int* core, int* alive0,
                            int* alive1, int* front0, int* front1, int* bfront0, int* bfront1, MceCtl* ctl,
-                           u64 budget, int blocks, hipStream_t s) {
-  void* args[] = {&n, (void*)&rp, (void*)&ci, &deg, &rnd, &core, &alive0, &alive1,
-                  &front0, &front1, &bfront0, &bfront1, &ctl, &budget};
+                           u64 budget, unsigned short* tcol, long long tcap, int* tcrow, int blocks, hipStream_t s) {
+  if (!tcol || !tcrow) tcap = 0;
+  tcap = tcap < 0 ? 0 : (tcap > 0x7FFFFFFFll ? 0x7FFFFFFFll : tcap);   // row offsets are int
+  void* args[] = {&n,      (void*)&rp, (void*)&ci, &deg, &rnd,    &core, &alive0, &alive1, &front0,
+                  &front1, &bfront0,   &bfront1,   &ctl, &budget, &tcol, &tcap,   &tcrow};
   // one block needs no grid barrier, hence no cooperative launch
   if (blocks == 1) return hipLaunchKernel((const void*)k_peel, dim3(1), dim3(PEEL_THREADS), args, 0, s);
   return hipLaunchCooperativeKernel((const void*)k_peel, dim3(blocks), dim3(PEEL_THREADS), args, 0, s);
@@ -1473,6 +2097,8 @@ hipError_t mce_launch_peel(int n, const int* rp, const int* ci, int* deg, int* r
 
 // The peel's grid barrier needs every block resident: one block per CU, well
 // inside the occupancy limit.
+int mce_peel_tail_rows() { return PEEL_TT + 1; }
+
 int mce_peel_max_blocks(int num_cu) {
   int per_cu = 0;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, (const void*)k_peel, PEEL_THREADS, 0) != hipSuccess ||
