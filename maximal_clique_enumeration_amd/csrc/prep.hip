@@ -280,7 +280,7 @@ __device__ __forceinline__ void pmin(int* p, int v) {
 #ifndef PEEL_LDS_N
 #define PEEL_LDS_N 4096   // one-block peels of at most this many vertices keep degrees and rounds in LDS
 #endif
-#define PEEL_LPER 4                            // entries per thread and tile of a level pass
+#define PEEL_LPER 8                            // entries per thread and tile of a level pass
 // The tail: once at most PEEL_TT vertices remain, each with at most
 // PEEL_TMAXDEG live neighbours, and their live entries fill at most tcap
 // 16-bit words, block 0 finishes on the residual graph compacted to local ids
@@ -520,15 +520,22 @@ __device__ __forceinline__ int peel_rounds(const PeelArgs& A, PeelState& st, int
             v[q] = 0;
             if (i < st.na) v[q] = pld<S>(&src[i]);
           }
+          // a vertex's round and degree are loaded together (the degree of a
+          // removed one is not used)
+          int dvq[PEEL_LPER];
 #pragma unroll
           for (int q = 0; q < PEEL_LPER; q++) {
             const int i = tb + q * PEEL_THREADS + (int)threadIdx.x;
-            if (i < st.na) keep[q] = pld<S>(&A.rnd[v[q]]) < 0;
+            dvq[q] = 0;
+            if (i < st.na) {
+              keep[q] = pld<S>(&A.rnd[v[q]]) < 0;
+              dvq[q] = pld<S>(&A.deg[v[q]]);
+            }
           }
 #pragma unroll
           for (int q = 0; q < PEEL_LPER; q++) {
             if (keep[q]) {
-              const int dv = pld<S>(&A.deg[v[q]]);
+              const int dv = dvq[q];
               mn = min(mn, dv);
               first[q] = dv <= kn;
               if (sum_rows || sum_tail) {
@@ -566,10 +573,44 @@ __device__ __forceinline__ int peel_rounds(const PeelArgs& A, PeelState& st, int
             if (keep[q]) pst<S>(&dst[pos + mbcnt(m[q])], v[q]);
             pos += __popcll(m[q]);
           }
+          // the tile's first-round vertices: one append per list and wave for
+          // all of the tile's entries (each is a device-scope round trip)
+          {
+            u64 mr[PEEL_LPER], mbg[PEEL_LPER];
+            int nr = 0, nbg = 0;
+            u32 eb = 0;
 #pragma unroll
-          for (int q = 0; q < PEEL_LPER; q++) {
-            if (ballot(first[q]))
-              peel_append<S>(first[q], v[q], rp, A.front(st.r), &fs[p1], A.bfront(st.r), &bs[p1], &be[p1]);
+            for (int q = 0; q < PEEL_LPER; q++) {
+              const int len = first[q] ? rp[v[q] + 1] - rp[v[q]] : 0;
+              const bool big = len > PEEL_BIG;
+              mr[q] = ballot(first[q] && !big);
+              mbg[q] = ballot(big);
+              nr += __popcll(mr[q]);
+              nbg += __popcll(mbg[q]);
+              eb += big ? (u32)len : 0u;
+            }
+            if (nr + nbg > 0) {
+              const u32 es = nbg ? wave_sum_u32(eb) : 0u;
+              int pr = 0, pb = 0;
+              if (lane == 0) {
+                if (nr) pr = padd<S>(&fs[p1], nr);
+                if (nbg) {
+                  pb = padd<S>(&bs[p1], nbg);
+                  padd<S>(&be[p1], (int)es);
+                }
+              }
+              pr = read_lane(pr, 0);
+              pb = read_lane(pb, 0);
+              int* fr = A.front(st.r);
+              int* bfr = A.bfront(st.r);
+#pragma unroll
+              for (int q = 0; q < PEEL_LPER; q++) {
+                if ((mr[q] >> lane) & 1ull) pst<S>(&fr[pr + mbcnt(mr[q])], v[q]);
+                if ((mbg[q] >> lane) & 1ull) pst<S>(&bfr[pb + mbcnt(mbg[q])], v[q]);
+                pr += __popcll(mr[q]);
+                pb += __popcll(mbg[q]);
+              }
+            }
           }
           __syncthreads();   // s_lv is filled again for the next tile
         }
@@ -1294,8 +1335,8 @@ __device__ __forceinline__ void tail_chunks(int a, int incl, int C, int sfirst, 
 // a time (the next 64 entries' rows are loaded while a group's steps are
 // taken). Rounds and core numbers are written through the remaining list.
 __device__ __forceinline__ int peel_tail_rounds(const PeelArgs& A, PeelState& st, bool timer) {
-  // [0..2] frontier sizes (rotating), [3] remaining, [4] smallest degree, [5] vertices of the
-  // tentative level, [6] stop; s_wt: the waves' shares of a level's first round
+  // [0..2] frontier sizes (rotating), [4] smallest field, [5] vertices of the tentative
+  // level, [6] stop; s_wt: the waves' shares of a level's first round
   __shared__ int s_t[8];
   __shared__ int s_wt[PEEL_THREADS / MCE_WAVE + 1];
   const int lane = lane_id();
@@ -1321,55 +1362,48 @@ __device__ __forceinline__ int peel_tail_rounds(const PeelArgs& A, PeelState& st
     if (nf == 0) {
       // ---- a new level. Every remaining vertex has degree > k (>= k on
       // entry): the level is kt = k + 1 (k on entry) when some vertex has
-      // that degree, else the smallest degree. Pass 1 counts the remaining
-      // vertices, their smallest degree, those of degree <= kt, and per
-      // thread its smallest degree and how many have it; pass 2 collects the
-      // level's first round, each thread's share placed by a block-wide scan.
+      // that degree, else the smallest degree. Pass 1 finds the smallest field
+      // (a removed vertex's is at least 0x8000, so it is the smallest degree
+      // while any vertex remains) and counts the fields <= kt (all of them
+      // remaining vertices' degrees); pass 2 collects the level's first round,
+      // each thread's share placed by a block-wide scan. Both passes are
+      // issue-bound (two fields a word): a few instructions a word.
       const int kdone = k;
       const int kt = entry ? k : k + 1;
       entry = false;
       if (threadIdx.x == 0) {
         s_t[(slot + 2) % 3] = 0;
-        s_t[3] = 0;
         s_t[4] = 0x7FFFFFFF;
         s_t[5] = 0;
       }
       __syncthreads();
-      int rem = 0, mn = 0x7FFFFFFF, nmn = 0, le = 0;
-      for (int w0 = threadIdx.x; w0 < nw; w0 += 4 * PEEL_THREADS) {
+      u32 mn = 0xFFFFu;
+      int le = 0;
+      u32 wm = 0;   // bit j: word threadIdx.x + j * PEEL_THREADS holds some of them (nw <= 32 * PEEL_THREADS)
+      for (int j0 = 0; j0 * PEEL_THREADS < nw; j0 += 4) {
         u32 x[4];
 #pragma unroll
         for (int q = 0; q < 4; q++) {
-          const int w = w0 + q * PEEL_THREADS;
-          x[q] = w < nw ? deg[w] : 0x80008000u;
+          const int w = (j0 + q) * PEEL_THREADS + (int)threadIdx.x;
+          x[q] = w < nw ? deg[w] : 0xFFFFFFFFu;
         }
 #pragma unroll
         for (int q = 0; q < 4; q++) {
-#pragma unroll
-          for (int h = 0; h < 2; h++) {
-            const u32 f = h ? x[q] >> 16 : x[q] & 0xFFFFu;
-            if (f < 0x8000u) {
-              rem++;
-              le += (int)f <= kt;
-              if ((int)f < mn) {
-                mn = (int)f;
-                nmn = 0;
-              }
-              nmn += (int)f == mn;
-            }
-          }
+          const u32 f0 = x[q] & 0xFFFFu, f1 = x[q] >> 16;
+          mn = min(mn, min(f0, f1));
+          const int c2 = ((int)f0 <= kt) + ((int)f1 <= kt);
+          le += c2;
+          wm |= c2 ? 1u << (j0 + q) : 0u;
         }
       }
-      const int wrem = (int)wave_sum_u32((u32)rem);
       const int wle = (int)wave_sum_u32((u32)le);
-      const int wmn = wave_min_i32_nonneg(mn);
+      const int wmn = wave_min_i32_nonneg((int)mn);
       if (lane == 0) {
-        if (wrem) atomicAdd(&s_t[3], wrem);
         if (wle) atomicAdd(&s_t[5], wle);
         atomicMin(&s_t[4], wmn);
       }
       __syncthreads();
-      if (s_t[3] == 0) {
+      if (s_t[4] >= 0x8000) {   // every field marked: no vertex remains
         PEEL_MARK(tl);
         st.k = kdone;
         st.r = r;
@@ -1377,8 +1411,19 @@ __device__ __forceinline__ int peel_tail_rounds(const PeelArgs& A, PeelState& st
         return PEEL_DONE;
       }
       k = s_t[5] > 0 ? kt : s_t[4];
+      int c = le;
+      if (s_t[5] == 0) {   // a jump: this thread's vertices of the smallest degree
+        c = 0;
+        wm = 0;
+        for (int j = 0; j * PEEL_THREADS < nw; j++) {
+          const int w = j * PEEL_THREADS + (int)threadIdx.x;
+          const u32 x = w < nw ? deg[w] : 0xFFFFFFFFu;
+          const int c2 = ((int)(x & 0xFFFFu) == k) + ((int)(x >> 16) == k);
+          c += c2;
+          wm |= c2 ? 1u << j : 0u;
+        }
+      }
       // pass 2: this thread's vertices of degree <= k, marked, at its place in the list
-      int c = s_t[5] > 0 ? le : (mn == k ? nmn : 0);
       int incl = c;
 #pragma unroll
       for (int o = 1; o < MCE_WAVE; o <<= 1) {
@@ -1401,23 +1446,23 @@ __device__ __forceinline__ int peel_tail_rounds(const PeelArgs& A, PeelState& st
         unsigned short* fl = cur ? fl1 : fl0;
         int* ov = cur ? A.front1 : A.front0;
         int pos = s_wt[bw] + incl - c;
-        for (int w = threadIdx.x; w < nw && c > 0; w += PEEL_THREADS) {
+        while (wm) {
+          const int w = __builtin_ctz(wm) * PEEL_THREADS + (int)threadIdx.x;
+          wm &= wm - 1u;
           u32 x = deg[w];
           const u32 f0 = x & 0xFFFFu, f1 = x >> 16;
-          const bool in0 = f0 < 0x8000u && (int)f0 <= k, in1 = f1 < 0x8000u && (int)f1 <= k;
+          const bool in0 = (int)f0 <= k, in1 = (int)f1 <= k;   // k < 0x8000: remaining vertices only
           if (in0) {
             x |= 0x8000u;
             if (pos < PEEL_TFCAP) fl[pos] = (unsigned short)(2 * w);
             else ov[pos - PEEL_TFCAP] = 2 * w;
             pos++;
-            c--;
           }
           if (in1) {
             x |= 0x80000000u;
             if (pos < PEEL_TFCAP) fl[pos] = (unsigned short)(2 * w + 1);
             else ov[pos - PEEL_TFCAP] = 2 * w + 1;
             pos++;
-            c--;
           }
           if (in0 || in1) deg[w] = x;
         }
