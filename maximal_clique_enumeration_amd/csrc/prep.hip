@@ -372,6 +372,95 @@ __device__ __forceinline__ void peel_span(int base, int b, int k, const int* __r
   }
 }
 
+// Appends the joiners of up to four loads at once (lane l of load q joins when
+// bit l of jm[q] is set; its vertex is u[q]): one device-scope atomic per list
+// (regular, big) for all of them. Whole wave.
+template <int S>
+__device__ __forceinline__ void peel_append4(const u64 (&jm)[4], const int (&u)[4], const int* __restrict__ rp,
+                                             int* fr, int* fsize, int* bfr, int* bsize, int* bedge) {
+  const int lane = lane_id();
+  if (!(jm[0] | jm[1] | jm[2] | jm[3])) return;
+  u64 mr[4], mb[4];
+  int nr = 0, nbg = 0;
+  u32 eb = 0;
+#pragma unroll
+  for (int q = 0; q < 4; q++) {
+    const bool in = (jm[q] >> lane) & 1ull;
+    const int len = in ? rp[u[q] + 1] - rp[u[q]] : 0;
+    const bool big = len > PEEL_BIG;
+    mr[q] = ballot(in && !big);
+    mb[q] = ballot(big);
+    nr += __popcll(mr[q]);
+    nbg += __popcll(mb[q]);
+    eb += big ? (u32)len : 0u;
+  }
+  const u32 es = nbg ? wave_sum_u32(eb) : 0u;
+  int pr = 0, pb = 0;
+  if (lane == 0) {
+    if (nr) pr = padd<S>(fsize, nr);
+    if (nbg) {
+      pb = padd<S>(bsize, nbg);
+      padd<S>(bedge, (int)es);
+    }
+  }
+  pr = read_lane(pr, 0);
+  pb = read_lane(pb, 0);
+#pragma unroll
+  for (int q = 0; q < 4; q++) {
+    if ((mr[q] >> lane) & 1ull) pst<S>(&fr[pr + mbcnt(mr[q])], u[q]);
+    if ((mb[q] >> lane) & 1ull) pst<S>(&bfr[pb + mbcnt(mb[q])], u[q]);
+    pr += __popcll(mr[q]);
+    pb += __popcll(mb[q]);
+  }
+}
+
+// The rows of a group of up to 64 frontier vertices (lane t: vertex t's CSR
+// row [a, a + len), incl = the lanes' inclusive prefix of the lengths, E =
+// all of them), their entries taken 64 at a time whichever rows they fall in
+// (lane l of step s takes entry 64 s + l, its row found by a binary search
+// over the lanes' prefix), four steps in flight: each present neighbour loses
+// one degree, and one that falls from k + 1 to k joins the next round. Whole
+// wave.
+// ONE: the group is one vertex (lane 0's row), found without a search.
+template <int S, bool ONE>
+__device__ __forceinline__ void peel_group(int a, int incl, int E, int k, const int* __restrict__ rp,
+                                           const int* __restrict__ ci, const int* rnd, int* deg, int* nx, int* nxs,
+                                           int* bnx, int* bnxs, int* bnxe) {
+  const int lane = lane_id();
+  const int a0 = read_lane(a, 0);
+  for (int e0 = 0; e0 < E; e0 += 4 * MCE_WAVE) {
+    int u[4];
+    bool ok[4];
+#pragma unroll
+    for (int q = 0; q < 4; q++) {
+      const int e = e0 + q * MCE_WAVE + lane;
+      int pos = a0 + e;
+      if (!ONE) {
+        // (every lane takes part in each shuffle: one that sat out would read
+        // 0 from the lanes that do)
+        int t = 0;
+#pragma unroll
+        for (int step = 32; step > 0; step >>= 1) {
+          const int v = __shfl(incl, t + step - 1);
+          if (v <= e) t += step;
+        }
+        const int tt = min(t, MCE_WAVE - 1);
+        const int at = __shfl(a, tt);
+        const int pre = __shfl(incl, max(tt - 1, 0));
+        pos = at + e - (tt > 0 ? pre : 0);
+      }
+      ok[q] = e < E;
+      u[q] = ok[q] ? ci[pos] : 0;
+    }
+#pragma unroll
+    for (int q = 0; q < 4; q++) ok[q] = ok[q] && peel_present(rnd, u[q]);
+    u64 jm[4];
+#pragma unroll
+    for (int q = 0; q < 4; q++) jm[q] = ballot(ok[q] && padd<S>(&deg[u[q]], -1) == k + 1);
+    peel_append4<S>(jm, u, rp, nx, nxs, bnx, bnxs, bnxe);
+  }
+}
+
 struct PeelArgs {
   int n;
   const int* rp;
@@ -717,15 +806,33 @@ __device__ __forceinline__ int peel_rounds(const PeelArgs& A, PeelState& st, int
     int* bnx = A.bfront(r + 1);
     int* bnxs = &bs[p1];
     int* bnxe = &be[p1];
-    // vertices of small degree: one wave each
-    for (int i = wave; i < st.nf; i += nwaves) {
-      const int v = pld<S>(&fr[i]);
-      if (lane == 0) {
-        pst<S>(&A.rnd[v], r);
-        A.core[v] = k;
+    // vertices of small degree (rows of at most PEEL_BIG entries): groups of
+    // G per wave, G = 1 while there are at most as many as waves (a vertex's
+    // row gets all 64 lanes), up to 64 on the large rounds at the start of a
+    // level (one lane per vertex would leave most lanes idle on short rows,
+    // and one vertex per wave at a time made such rounds a chain of hundreds
+    // of dependent round trips)
+    {
+      const int G = min(MCE_WAVE, (st.nf + nwaves - 1) / nwaves);
+      for (int g0 = wave * G; g0 < st.nf; g0 += nwaves * G) {
+        int a = 0, len = 0;
+        if (lane < G && g0 + lane < st.nf) {
+          const int v = pld<S>(&fr[g0 + lane]);
+          pst<S>(&A.rnd[v], r);
+          A.core[v] = k;
+          a = rp[v];
+          len = rp[v + 1] - a;
+        }
+        int incl = len;
+#pragma unroll
+        for (int o = 1; o < MCE_WAVE; o <<= 1) {
+          const int t = __shfl_up(incl, o);
+          if (lane >= o) incl += t;
+        }
+        const int E = read_lane(incl, MCE_WAVE - 1);
+        if (G == 1) peel_group<S, true>(a, incl, E, k, rp, A.ci, A.rnd, A.deg, nx, nxs, bnx, bnxs, bnxe);
+        else peel_group<S, false>(a, incl, E, k, rp, A.ci, A.rnd, A.deg, nx, nxs, bnx, bnxs, bnxe);
       }
-      const int a = rp[v], b = rp[v + 1];
-      for (int base = a; base < b; base += PEEL_SPAN) peel_span<S>(base, b, k, rp, A.ci, A.rnd, A.deg, nx, nxs, bnx, bnxs, bnxe);
     }
     // vertices of large degree: their spans are dealt round-robin to all waves
     for (int j0 = 0; j0 < st.nb; j0 += MCE_WAVE) {
