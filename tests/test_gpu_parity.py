@@ -153,10 +153,12 @@ def test_disjoint_union_and_isolated(eng):
                                   lambda: mi.chung_lu(200000, 20.0, 2.3, None, 11, planted=50),
                                   lambda: mi.path(40), lambda: mi.random_small(500, 0.3, 4),
                                   # grid peels that hand the residual graph to block 0 at once: one
-                                  # round of 30,000 vertices, 20,000 rounds of two, rows over 2,048
-                                  # entries compacted in spans
+                                  # round of 30,000 vertices, 20,000 rounds of two, a 10,000-entry
+                                  # row compacted in spans
                                   lambda: mi.cycle(30000), lambda: mi.path(40000),
                                   lambda: mi.chung_lu(40000, 20.0, 2.1, 8000.0, 5),
+                                  lambda: mi.disjoint_union(mi.complete_multipartite([1, 10000]), mi.cycle(20000),
+                                                            mi.chung_lu(20000, 12.0, 2.0, 9000.0, 7)),
                                   # a hub of degree 40,000 keeps the grid until it is gone
                                   lambda: mi.complete_multipartite([1, 40000])])
 def test_ordering_matches_oracle(eng, make):
