@@ -294,6 +294,27 @@ mce_status mce_graph_info(const mce_engine* e, mce_graph_facts* info);
    Either pointer may be NULL. Synchronous on `stream`. */
 mce_status mce_ordering(const mce_engine* e, int32_t* core, int32_t* round, void* stream);
 
+/* The bit-encoded induced subgraph (section 3.4) that the last run built for
+   first-level root `root`, copied into `words` (HOST memory, cap u64 words);
+   *len = its size in words, *form = its encoding: bits 0-7 the row width W in
+   64-bit words, bit 8 set for a micro table (|P|, |X| <= 64: X columns follow
+   the rows), bit 9 set when it holds rows for X members too (full subgraph).
+   Layout, in u64 words: [0] |P| | |X| << 32; [1] root | |R| << 32 (|R| = 1);
+   [2] the root's hash term (mix64(root + 0x9E3779B97F4A7C15)); then one row of
+   W words per member of P, then (full) of X, members in id order within each:
+   bit b of a row set iff that member is adjacent to the b-th member of P; then
+   (micro) for each P member the bitset of its X neighbours (bit a: the a-th X
+   member); then the P members' hash terms; then the ids of P, then of X, as
+   int32, two a word (the high half of the last word is padding when
+   |P| + |X| is odd). For checking the build against an independent encoding.
+   MCE_ERR_STATE: no such table, because the root has no later neighbour, or
+   the last run was not a complete first-level run of mce_run / mce_run_roots
+   with overlapped launches (launches in series, and mce_run_static, share one
+   table area that later launches overwrite). MCE_ERR_ARG: cap < *len (*len and
+   *form still set). Synchronous on `stream`. */
+mce_status mce_root_table(const mce_engine* e, int32_t root, uint64_t* words, int64_t cap, int64_t* len,
+                          int32_t* form, void* stream);
+
 /* Counters of the last run. stats->struct_size must be set by the caller. */
 mce_status mce_stats(const mce_engine* e, mce_run_stats* stats);
 

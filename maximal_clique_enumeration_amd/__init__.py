@@ -29,8 +29,8 @@ MCE_SUBGRAPH_AUTO, MCE_SUBGRAPH_PARTIAL, MCE_SUBGRAPH_FULL = 0, 1, 2
 
 # every function the C header declares
 EXPORTS = ("mce_config_init", "mce_create", "mce_run", "mce_run_roots", "mce_run_static", "mce_result",
-           "mce_graph_info", "mce_ordering", "mce_stats", "mce_worker_trace", "mce_last_error",
-           "mce_status_string", "mce_destroy")
+           "mce_graph_info", "mce_ordering", "mce_root_table", "mce_stats", "mce_worker_trace",
+           "mce_last_error", "mce_status_string", "mce_destroy")
 
 
 class MceLibraryMissing(RuntimeError):
@@ -136,6 +136,7 @@ def load_library():
     lib.mce_result.argtypes = [vp, P(ctypes.c_uint64), P(ctypes.c_uint64), P(ctypes.c_uint64), i32, P(i32)]
     lib.mce_graph_info.argtypes = [vp, P(mce_graph_facts)]
     lib.mce_ordering.argtypes = [vp, vp, vp, vp]
+    lib.mce_root_table.argtypes = [vp, i32, P(ctypes.c_uint64), i64, P(i64), P(i32), vp]
     lib.mce_stats.argtypes = [vp, P(mce_run_stats)]
     lib.mce_worker_trace.argtypes = [vp, P(mce_worker_record), i32, P(i32)]
     lib.mce_last_error.argtypes = [vp]
@@ -145,7 +146,7 @@ def load_library():
     lib.mce_destroy.argtypes = [vp]
     lib.mce_destroy.restype = None
     for name in ("mce_config_init", "mce_create", "mce_run", "mce_run_roots", "mce_run_static", "mce_result",
-                 "mce_graph_info", "mce_ordering", "mce_stats"):
+                 "mce_graph_info", "mce_ordering", "mce_root_table", "mce_stats"):
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -182,6 +183,10 @@ def mce_graph_info(engine, info: mce_graph_facts) -> int:
 
 def mce_ordering(engine, core, round_, stream) -> int:
     return load_library().mce_ordering(engine, core, round_, stream)
+
+
+def mce_root_table(engine, root, words, cap, length, form, stream) -> int:
+    return load_library().mce_root_table(engine, root, words, cap, length, form, stream)
 
 
 def mce_stats(engine, stats: mce_run_stats) -> int:
@@ -372,6 +377,25 @@ class Engine:
         self._check(mce_ordering(self._h, _ptr(core), _ptr(rnd), ctypes.c_void_p(stream.cuda_stream)),
                     "mce_ordering", self._h)
         return core, rnd
+
+    def root_table(self, root: int):
+        """(words as a uint64 numpy array, form) of the table the last run built
+        for first-level root `root`, or None when it built none (see mce.h)."""
+        import numpy as np
+        import torch
+        stream = ctypes.c_void_p(torch.cuda.current_stream(torch.device("cuda", self.device)).cuda_stream)
+        length = ctypes.c_int64()
+        form = ctypes.c_int32()
+        st = mce_root_table(self._h, int(root), None, 0, ctypes.byref(length), ctypes.byref(form), stream)
+        if st == MCE_ERR_STATE:
+            return None
+        if st not in (MCE_OK, MCE_ERR_ARG):
+            self._check(st, "mce_root_table", self._h)
+        words = np.zeros(max(1, length.value), np.uint64)
+        self._check(mce_root_table(self._h, int(root), words.ctypes.data_as(ctypes.POINTER(ctypes.c_uint64)),
+                                   length.value, ctypes.byref(length), ctypes.byref(form), stream),
+                    "mce_root_table", self._h)
+        return words[:length.value], form.value
 
     def worker_trace(self) -> list[dict]:
         """One record per wavefront of the last run's search launches."""

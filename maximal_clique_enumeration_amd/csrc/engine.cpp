@@ -97,6 +97,16 @@ struct mce_engine {
     int sub, nw, roots;
   };
   LaunchInfo last_plan[MCE_NSUB] = {};
+  // where the last run's induced-subgraph tables sit (mce_root_table): valid
+  // after a complete first-level run with overlapped launches, each sub-class
+  // in its own heap region
+  struct TableMap {
+    bool valid = false;
+    int mode = 0;
+    int total = 0;                      // root-list entries
+    int off[MCE_NSUB] = {}, count[MCE_NSUB] = {};
+    size_t heap_base[MCE_NSUB] = {};    // u64 words
+  } tabs;
   int n_last_plan = 0;
   int last_stat_rows = 0;
   bool stats_pending = false;
@@ -268,6 +278,7 @@ mce_status run_once(mce_engine* e, int32_t n, int64_t nnz, const int32_t* row_pt
   e->have_result = false;
   e->complete = false;
   e->have_order = false;
+  e->tabs.valid = false;
   if (n < 0 || nnz < 0) return fail(e, MCE_ERR_ARG, "n and nnz must be >= 0");
   if (nnz >= 0x7FFFFFFFLL) return fail(e, MCE_ERR_ARG, "nnz must be < 2^31");
   if (n > 0 && !row_ptr) return fail(e, MCE_ERR_ARG, "row_ptr is NULL");
@@ -780,6 +791,17 @@ mce_status run_once(mce_engine* e, int32_t n, int64_t nnz, const int32_t* row_pt
   e->last_timing = timing;
   e->last_stimes = stimes;
   e->stats_pending = true;
+  if (e->complete && overlap && !l2 && !stat) {
+    mce_engine::TableMap& tm = e->tabs;
+    tm.mode = mode;
+    tm.total = total;
+    for (int c = 0; c < MCE_NSUB; c++) {
+      tm.off[c] = off.off[c];
+      tm.count[c] = counts[c];
+      tm.heap_base[c] = heap_base[c];
+    }
+    tm.valid = true;
+  }
   so.ms_total = ms_since(t0);
   if (!e->complete) return fail(e, MCE_ERR_TIMEOUT, "search ran past the time limit (results are partial)");
   return MCE_OK;
@@ -1034,6 +1056,53 @@ mce_status mce_result(const mce_engine* e, uint64_t* count, uint64_t* hash, uint
 mce_status mce_graph_info(const mce_engine* e, mce_graph_facts* info) {
   if (!e || !info) return MCE_ERR_ARG;
   *info = e->info;
+  return MCE_OK;
+}
+
+mce_status mce_root_table(const mce_engine* e, int32_t root, uint64_t* words, int64_t cap, int64_t* len,
+                          int32_t* form, void* stream) {
+  if (!e || !len || !form || cap < 0 || (cap > 0 && !words)) return MCE_ERR_ARG;
+  const mce_engine::TableMap& tm = e->tabs;
+  if (!tm.valid || root < 0 || root >= e->last_n) return MCE_ERR_STATE;
+  if (hipSetDevice(e->device) != hipSuccess) return MCE_ERR_DEVICE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  // the root's place in the bucketed root lists, hence its sub-class
+  std::vector<int32_t> lists((size_t)std::max(tm.total, 1));
+  if (tm.total > 0 && (hipMemcpyAsync(lists.data(), e->own.lists.p, (size_t)tm.total * sizeof(int32_t),
+                                      hipMemcpyDeviceToHost, s) != hipSuccess ||
+                       hipStreamSynchronize(s) != hipSuccess))
+    return MCE_ERR_DEVICE;
+  int i = -1;
+  for (int j = 0; j < tm.total; j++)
+    if (lists[j] == root) {
+      i = j;
+      break;
+    }
+  if (i < 0) return MCE_ERR_STATE;   // no table: the root has no later neighbour
+  int c = 0;
+  while (c < MCE_NSUB && !(i >= tm.off[c] && i < tm.off[c] + tm.count[c])) c++;
+  if (c == MCE_NSUB) return MCE_ERR_STATE;
+  u64 to[2] = {0, 0};
+  const u64* taboff = static_cast<const u64*>(e->own.taboff.p);
+  if (hipMemcpyAsync(&to[0], taboff + i, sizeof(u64), hipMemcpyDeviceToHost, s) != hipSuccess ||
+      hipMemcpyAsync(&to[1], taboff + tm.off[c], sizeof(u64), hipMemcpyDeviceToHost, s) != hipSuccess ||
+      hipStreamSynchronize(s) != hipSuccess)
+    return MCE_ERR_DEVICE;
+  const u64* T = static_cast<const u64*>(e->own.heap.p) + tm.heap_base[c] + (to[0] - to[1]);
+  u64 hdr = 0;
+  if (hipMemcpyAsync(&hdr, T, sizeof(u64), hipMemcpyDeviceToHost, s) != hipSuccess ||
+      hipStreamSynchronize(s) != hipSuccess)
+    return MCE_ERR_DEVICE;
+  const int p = (int)(u32)hdr, x = (int)(hdr >> 32);
+  const bool micro = c == MCE_SUB_MICRO;
+  const int W = micro ? 1 : 1 << (c >> 1);
+  const u64 nw = micro ? mce_micro_table_words(p, x) : mce_table_words(p, x, W, tm.mode);
+  *len = (int64_t)nw;
+  *form = W | (micro ? 1 << 8 : 0) | ((micro || tm.mode == MCE_MODE_IPX) ? 1 << 9 : 0);
+  if ((u64)cap < nw) return MCE_ERR_ARG;
+  if (hipMemcpyAsync(words, T, nw * sizeof(u64), hipMemcpyDeviceToHost, s) != hipSuccess ||
+      hipStreamSynchronize(s) != hipSuccess)
+    return MCE_ERR_DEVICE;
   return MCE_OK;
 }
 

@@ -75,6 +75,9 @@ def _load():
         lib.oracle_knuth.restype = ctypes.c_int
         lib.oracle_list.argtypes = [ctypes.c_int32, i32p, i32p, i32p, i32p, ctypes.c_int64]
         lib.oracle_list.restype = ctypes.c_int64
+        lib.oracle_root_table.argtypes = [ctypes.c_int32, i32p, i32p, i32p, ctypes.c_int32, ctypes.c_int32,
+                                          ctypes.c_int32, ctypes.c_int32, u64p, ctypes.c_int64]
+        lib.oracle_root_table.restype = ctypes.c_int64
         _lib = lib
     return _lib
 
@@ -242,3 +245,24 @@ def mce_each(n: int, row_ptr, col_idx, roots, root_budget: int, rnd):
     if rc != 0:
         raise RuntimeError(f"oracle_mce_each failed with code {rc}")
     return nodes[:k], count[:k], hsh[:k], done[:k]
+
+
+def root_table(n: int, row_ptr, col_idx, rnd, root: int, W: int, micro: bool, full: bool) -> np.ndarray:
+    """One first-level root's bit-encoded induced subgraph (section 2.4 "Induced
+    Subgraphs", section 3.4) in the word layout of the engine's table
+    inspection: header (|P|, |X|; root, |R| = 1; h(root)), one row of W words
+    per member of P (then of X when `full`): bit b set iff the member is
+    adjacent to P's b-th member; with `micro`, each P member's neighbours in X
+    as a bitset; P's hash terms; the ids of P and X as int32 pairs. P and X in
+    ascending id order; adjacency looked up pair by pair in the CSR."""
+    rp, rpp = _i32(row_ptr)
+    ci, cip = _i32(col_idx)
+    rn, rnp = _i32(rnd)
+    deg = int(rp[root + 1] - rp[root])
+    cap = 3 + (deg * W) + 2 * deg + (deg + 1) // 2 + 4
+    out = np.zeros(cap, np.uint64)
+    k = _load().oracle_root_table(n, rpp, cip, rnp, int(root), int(W), 1 if micro else 0, 1 if full else 0,
+                                  out.ctypes.data_as(ctypes.POINTER(ctypes.c_uint64)), cap)
+    if k < 0:
+        raise ValueError("oracle_root_table: width too small for P, or a bad root")
+    return out[:k]

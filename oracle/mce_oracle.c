@@ -668,3 +668,53 @@ int64_t oracle_list(int32_t n, const int32_t *rp, const int32_t *ci, const int32
   g_list = NULL;
   return l.overflow ? -1 : l.len;
 }
+
+/* ------------------------------------------------------------------------
+ * One root's bit-encoded induced subgraph (section 2.4 "Induced Subgraphs",
+ * section 3.4), written in the word layout the GPU engine's inspection call
+ * documents, so that the engine's build can be compared with it word by word:
+ *   [0] |P| | |X| << 32   [1] root | 1 << 32   [2] h(root)
+ *   rows: for each member of P, then (full) of X, in id order within each,
+ *         W words; bit b set iff the member is adjacent to the b-th member of P
+ *   (micro) for each member of P, the bitset of its neighbours in X
+ *   the hash terms h(u) of P's members, then the ids of P and of X as int32,
+ *   two a word (the last word's high half is left 0 when |P| + |X| is odd).
+ * P = the root's later neighbours, X = its earlier ones (Algorithm 3), each
+ * in ascending id order as the CSR row holds them. Adjacency is looked up
+ * pair by pair in the CSR (a binary search per pair). Returns the number of
+ * words, or -1 if cap is too small or W cannot hold P. */
+int64_t oracle_root_table(int32_t n, const int32_t *rp, const int32_t *ci, const int32_t *rnd, int32_t root,
+                          int32_t W, int32_t micro, int32_t full, uint64_t *out, int64_t cap) {
+  if (root < 0 || root >= n || W < 1) return -1;
+  int32_t deg = rp[root + 1] - rp[root];
+  int32_t *L = (int32_t *)malloc(sizeof(int32_t) * (size_t)(deg > 0 ? deg : 1));
+  if (!L) return -1;
+  int32_t p = 0, x = 0;
+  for (int64_t e = rp[root]; e < rp[root + 1]; e++)
+    if (later(rnd, ci[e], root)) L[p++] = ci[e];
+  for (int64_t e = rp[root]; e < rp[root + 1]; e++)
+    if (!later(rnd, ci[e], root)) L[p + x++] = ci[e];
+  const int64_t rows = full ? (int64_t)p + x : p;
+  const int64_t need = 3 + rows * W + (micro ? p : 0) + p + ((int64_t)p + x + 1) / 2;
+  if (p > 64 * W || need > cap) {
+    free(L);
+    return -1;
+  }
+  memset(out, 0, sizeof(uint64_t) * (size_t)need);
+  out[0] = (uint64_t)(uint32_t)p | ((uint64_t)(uint32_t)x << 32);
+  out[1] = (uint64_t)(uint32_t)root | (1ULL << 32);
+  out[2] = oracle_mix64((uint64_t)(int64_t)root + GOLDEN);
+  int64_t w = 3;
+  for (int64_t a = 0; a < rows; a++, w += W)
+    for (int32_t b = 0; b < p; b++)
+      if (adjacent(rp, ci, L[a], L[b])) out[w + b / 64] |= 1ULL << (b % 64);
+  if (micro) {
+    for (int32_t j = 0; j < p; j++, w++)
+      for (int32_t a = 0; a < x; a++)
+        if (adjacent(rp, ci, L[j], L[p + a])) out[w] |= 1ULL << a;
+  }
+  for (int32_t j = 0; j < p; j++) out[w++] = oracle_mix64((uint64_t)(int64_t)L[j] + GOLDEN);
+  for (int32_t j = 0; j < p + x; j++) out[w + j / 2] |= (uint64_t)(uint32_t)L[j] << (32 * (j % 2));
+  free(L);
+  return need;
+}

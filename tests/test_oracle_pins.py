@@ -386,3 +386,39 @@ def test_per_root_runs_add_up_to_brute_force(seed, n, p):
         assert d2[0] == 0
         _, c3, _, d3 = oracle.mce_each(g.n, g.row_ptr, g.col_idx, roots[big:big + 1], int(nodes[big]), rnd)
         assert d3[0] == 1 and c3[0] == cnt[big]
+
+
+# ------------------------------------------------------------------ a root's bit-encoded subgraph
+def _dense_table(g, rnd, root, W, micro, full):
+    """The same words from a dense adjacency matrix and Python integers."""
+    n = g.n
+    A = np.zeros((n, n), bool)
+    src = np.repeat(np.arange(n), np.diff(g.row_ptr))
+    A[src, g.col_idx] = True
+    nb = sorted(int(u) for u in np.nonzero(A[root])[0])
+    lat = lambda u: (int(rnd[u]), u) > (int(rnd[root]), root)
+    P = [u for u in nb if lat(u)]
+    X = [u for u in nb if not lat(u)]
+    G = 0x9E3779B97F4A7C15
+    words = [len(P) | (len(X) << 32), root | (1 << 32), brute.mix64(root + G)]
+    for m in P + (X if full else []):
+        row = sum(1 << b for b, u in enumerate(P) if A[m, u])
+        words += [(row >> (64 * i)) & (2 ** 64 - 1) for i in range(W)]
+    if micro:
+        words += [sum(1 << a for a, u in enumerate(X) if A[v, u]) for v in P]
+    words += [brute.mix64(u + G) for u in P]
+    ids = P + X
+    words += [ids[j] | ((ids[j + 1] if j + 1 < len(ids) else 0) << 32) for j in range(0, len(ids), 2)]
+    return np.array(words, dtype=np.uint64)
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_root_table_matches_dense_adjacency(seed):
+    g = mi.random_small(70, 0.35 if seed % 2 else 0.15, seed)
+    _, rnd, _ = oracle.peel(g.n, g.row_ptr, g.col_idx)
+    for root in range(g.n):
+        for W, micro, full in [(1, True, True), (1, False, True), (1, False, False), (2, False, True)]:
+            deg = int(g.row_ptr[root + 1] - g.row_ptr[root])
+            got = oracle.root_table(g.n, g.row_ptr, g.col_idx, rnd, root, W, micro, full)
+            want = _dense_table(g, rnd, root, W, micro, full)
+            assert np.array_equal(got, want), (seed, root, W, micro, full, deg)
