@@ -451,12 +451,20 @@ __global__ __launch_bounds__(256) void k_build_head(BuildParams prm) {
 // is its forward row: every P member comes after every X member in the peel
 // order (P after the pivot vertex, X before it), so the P members adjacent to
 // it are all in that row, which is no longer than the member's core number.
+// With the forward adjacency and W <= PROWS_MAX_W, the P rows are built by
+// k_build_prows instead, and this kernel's slabs cover the X rows only.
 #define SPLIT_STREAM_RATIO 2
+#define PROWS_MAX_W 8
+
+template <int W>
+__host__ __device__ constexpr int build_hash_bits() {   // 2^HB >= 2 PMAX
+  return W == 1 ? 7 : W == 2 ? 8 : W == 4 ? 9 : W == 8 ? 10 : W == 16 ? 11 : 12;
+}
 
 template <int W>
 __global__ __launch_bounds__(64) void k_build_rows(BuildParams prm) {
   constexpr int PMAX = 64 * W;
-  constexpr int HB = W == 1 ? 7 : W == 2 ? 8 : W == 4 ? 9 : W == 8 ? 10 : W == 16 ? 11 : 12;   // 2^HB >= 2 PMAX
+  constexpr int HB = build_hash_bits<W>();
   __shared__ int s_hk[1 << HB];
   __shared__ short s_hv[1 << HB];
   __shared__ int s_pre[MCE_WAVE];   // exclusive prefix sum of the slab rows' streamed degrees
@@ -479,7 +487,8 @@ __global__ __launch_bounds__(64) void k_build_rows(BuildParams prm) {
     const int np = (int)(u32)hdr, nx = (int)(u32)(hdr >> 32);
     if (np < 1 || np > PMAX) continue;   // the head kernel flagged this root
     const int nrows = (int)mce_table_rows(np, nx, mode);
-    const int nslab = (nrows + MCE_WAVE - 1) / MCE_WAVE;
+    const int rfirst = prm.fadj && W <= PROWS_MAX_W ? np : 0;   // the first row built here
+    const int nslab = (nrows - rfirst + MCE_WAVE - 1) / MCE_WAVE;
     if (k >= nslab) continue;
     if (off + mce_table_words(np, nx, W, mode) > prm.heap_words) continue;
     u64* rows = T + 3;
@@ -499,7 +508,7 @@ __global__ __launch_bounds__(64) void k_build_rows(BuildParams prm) {
       cur = i;
     }
     for (int slab = k; slab < nslab; slab += K) {
-      const int t0 = slab * MCE_WAVE;
+      const int t0 = rfirst + slab * MCE_WAVE;
       const int t = t0 + lane;
       const bool valid = t < nrows;
       int ga = 0, d = 0, gv = 0;
@@ -587,6 +596,110 @@ __global__ __launch_bounds__(64) void k_build_rows(BuildParams prm) {
   }
 }
 
+// P rows from the forward adjacency: block i builds every P row of root i in
+// LDS. The forward rows of the P members are streamed, 64 members (a slab) at a
+// time as one sequence, its entries dealt over the block's four wavefronts 64 at
+// a time with four loads in flight per lane, each entry's member found from the
+// slab's prefix sums of forward degrees. An entry that is a P member is an edge
+// between two P members, seen from its earlier end in the peel order, and it
+// sets its bit in the rows of both ends; every such edge lies in exactly one of
+// the forward rows streamed, so each row is complete once all are. A forward
+// row is no longer than the member's core number, where the CSR rows of P's hub
+// members run to thousands of entries (each P member was looked up in them by
+// binary search).
+template <int W>
+__global__ __launch_bounds__(256) void k_build_prows(BuildParams prm) {
+  constexpr int PMAX = 64 * W;
+  constexpr int HB = build_hash_bits<W>();
+  constexpr int NWV = 4;   // wavefronts per block
+  __shared__ int s_hk[1 << HB];
+  __shared__ short s_hv[1 << HB];
+  __shared__ int s_pre[MCE_WAVE];   // exclusive prefix sum of the slab members' forward degrees
+  __shared__ int s_ga[MCE_WAVE];    // their row starts
+  __shared__ int s_D;               // the slab's total
+  __shared__ u64 s_rows[PMAX * W];
+  const int lane = lane_id();
+  const int wv = (int)threadIdx.x / MCE_WAVE;
+  const int* __restrict__ rp = prm.rp;
+  const int* __restrict__ fadj = prm.fadj;
+  const int* __restrict__ fdeg = prm.fdeg;
+  for (int i = blockIdx.x; i < prm.nroots; i += gridDim.x) {
+    const u64 off = uni(prm.tab_off[i]) - uni(prm.tab_off[0]);
+    if (off + 3 > prm.heap_words) continue;
+    u64* T = prm.heap + off;
+    const u64 hdr = uni(T[0]);
+    const int np = (int)(u32)hdr, nx = (int)(u32)(hdr >> 32);
+    if (np < 1 || np > PMAX) continue;   // the head kernel flagged this root
+    const int nrows = (int)mce_table_rows(np, nx, prm.mode);
+    if (off + mce_table_words(np, nx, W, prm.mode) > prm.heap_words) continue;
+    u64* rows = T + 3;
+    const u64* hvs = rows + (size_t)nrows * W;
+    const int* ids = (const int*)(hvs + np);
+    __syncthreads();   // the previous root's rows are written out, its hash no longer read
+    for (int h = threadIdx.x; h < (1 << HB); h += blockDim.x) s_hk[h] = -1;
+    for (int q = threadIdx.x; q < np * W; q += blockDim.x) s_rows[q] = 0;
+    __syncthreads();
+    for (int j = threadIdx.x; j < np; j += blockDim.x) {
+      const int u = ids[j];
+      u32 h = build_hash<HB>(u);
+      while (atomicCAS(&s_hk[h], -1, u) != -1) h = (h + 1u) & ((1u << HB) - 1u);
+      s_hv[h] = (short)j;
+    }
+    for (int t0 = 0; t0 < np; t0 += MCE_WAVE) {
+      if (wv == 0) {
+        const int t = t0 + lane;
+        int ga = 0, d = 0;
+        if (t < np) {
+          const int g = ids[t];
+          ga = rp[g];
+          d = fdeg[g];
+        }
+        int inc = d;
+#pragma unroll
+        for (int o = 1; o < MCE_WAVE; o <<= 1) {
+          const int v = __shfl_up(inc, o);
+          if (lane >= o) inc += v;
+        }
+        s_pre[lane] = inc - d;
+        s_ga[lane] = ga;
+        if (lane == MCE_WAVE - 1) s_D = inc;
+      }
+      __syncthreads();   // the hash (first slab) and the slab's prefix sums
+      const int D = s_D;
+      for (int base = wv * MCE_WAVE; base < D; base += 4 * NWV * MCE_WAVE) {
+        int u[4], rr[4];
+#pragma unroll
+        for (int z = 0; z < 4; z++) {
+          const int x = base + z * NWV * MCE_WAVE + lane;
+          rr[z] = -1;
+          u[z] = -1;
+          if (x < D) {
+            int r = 0;   // the last member whose prefix is <= x (it has x - prefix < its degree)
+#pragma unroll
+            for (int step = MCE_WAVE / 2; step > 0; step >>= 1)
+              if (s_pre[r + step] <= x) r += step;
+            rr[z] = r;
+            u[z] = fadj[s_ga[r] + (x - s_pre[r])];
+          }
+        }
+#pragma unroll
+        for (int z = 0; z < 4; z++) {
+          if (rr[z] >= 0) {
+            const int j = build_lookup<HB>(s_hk, s_hv, u[z]);
+            if (j >= 0) {
+              const int a = t0 + rr[z];
+              atomicOr(&s_rows[a * W + (j >> 6)], 1ull << (j & 63));
+              atomicOr(&s_rows[j * W + (a >> 6)], 1ull << (a & 63));
+            }
+          }
+        }
+      }
+      __syncthreads();   // the slab's prefix sums are rewritten by the next slab; the rows are complete
+    }
+    for (int q = threadIdx.x; q < np * W; q += blockDim.x) rows[q] = s_rows[q];
+  }
+}
+
 hipError_t mce_launch_build(const BuildParams& prm, int blocks, hipStream_t s) {
   if (prm.micro) {
     const int nb = std::max(1, std::min(blocks, prm.nroots));
@@ -596,6 +709,16 @@ hipError_t mce_launch_build(const BuildParams& prm, int blocks, hipStream_t s) {
   if (prm.parts < 1) return hipErrorInvalidValue;
   const int nh = std::max(1, std::min(blocks / 4, prm.nroots));
   hipLaunchKernelGGL(k_build_head, dim3(nh), dim3(256), 0, s, prm);
+  if (prm.fadj && prm.W <= PROWS_MAX_W) {
+    const int np = std::max(1, std::min(blocks / 4, prm.nroots));
+    switch (prm.W) {
+      case 1: hipLaunchKernelGGL(k_build_prows<1>, dim3(np), dim3(256), 0, s, prm); break;
+      case 2: hipLaunchKernelGGL(k_build_prows<2>, dim3(np), dim3(256), 0, s, prm); break;
+      case 4: hipLaunchKernelGGL(k_build_prows<4>, dim3(np), dim3(256), 0, s, prm); break;
+      case 8: hipLaunchKernelGGL(k_build_prows<8>, dim3(np), dim3(256), 0, s, prm); break;
+      default: return hipErrorInvalidValue;
+    }
+  }
   const long long items = (long long)prm.nroots * prm.parts;
   const int nb = (int)std::max(1LL, std::min((long long)blocks, items));
   switch (prm.W) {
