@@ -505,7 +505,7 @@ mce_status run_once(mce_engine* e, int32_t n, int64_t nnz, const int32_t* row_pt
       pl.L = mce_search_layout(c, mode, hctl->sub_maxp[var][c], hctl->sub_maxx[var][c], hctl->sub_maxr[var][c],
                                counts[c], e->num_cu, hbm, counters);
       const SearchLayout& L = pl.L;
-      nw = occupancy(e, ((c * 2 + mode) * 2 + (counters ? 1 : 0)) * 2 + (L.srows ? 1 : 0),
+      nw = occupancy(e, (((c * 2 + mode) * 2 + (counters ? 1 : 0)) * 2 + (L.srows ? 1 : 0)) * 2 + (L.sprows ? 1 : 0),
                      (long long)L.lds_bytes * 2 + (L.sstack ? 1 : 0),
                      [&] { return mce_search_max_workers(L, e->num_cu); });
     }

@@ -109,6 +109,7 @@ struct SearchLayout {
   int pcap, xcap, rcap;   // largest |P|, |X|, row count over the launch's roots
   int levels, hcap;       // stack records, histogram entries
   bool srows, sstack;     // rows + X_X staged in LDS; level stack in LDS
+  bool sprows;            // (without srows) the P rows staged in LDS
   bool counters;          // count pivot rows and X_X tests (width 1 keeps them out of the timed kernel)
   int l_misc, l_hist, l_hv, l_pid, l_stack, l_rows, l_xx;
   size_t lds_bytes;

@@ -73,33 +73,52 @@ struct XxTest {
   }
 };
 
+// The X_X passes below read XX_GROUP chunks of 64 entries, and issue their row
+// loads, before acting on the first: with the rows in HBM, each chunk's loads
+// were one dependent round trip. A chunk's writes stay below its own end, so
+// reading the later chunks of the group early sees the values they would have.
+#define XX_GROUP 4
+
 // Stable in-place partition of xx[0, L): entries adjacent to v move to the front
 // in their order, the others after them (section 3.5, Figure 2). Returns the
 // number kept. Each 64-entry chunk is read whole before any of it is written:
 // kept entries go to [wk, wk+kc); removed entries that sat there move, with the
-// chunk's removed entries, behind the kept ones.
+// chunk's removed entries, behind the kept ones (all below the chunk's end).
 template <class T>
 __device__ int xx_partition(int* xx, int L, const T& test) {
   const int lane = lane_id();
   int wk = 0;
-  for (int c = 0; c < L; c += MCE_WAVE) {
-    const int i = c + lane;
-    const bool valid = i < L;
-    const int x = valid ? xx[i] : 0;
-    const int kc_bound = min(MCE_WAVE, c - wk);
-    const int dval = lane < kc_bound ? xx[wk + lane] : 0;
-    const bool keep = valid && test.adj(x);
-    const u64 km = ballot(keep);
-    const u64 vm = ballot(valid);
-    const int kc = __popcll(km);
-    const int D = min(kc, c - wk);
-    const int base = max(c, wk + kc);
-    __syncthreads();   // every lane holds its values before anything is written
-    if (keep) xx[wk + mbcnt(km)] = x;
-    if (lane < D) xx[base + lane] = dval;
-    if (valid && !keep) xx[base + D + mbcnt(vm & ~km)] = x;
-    wk += kc;
-    __syncthreads();
+  for (int c0 = 0; c0 < L; c0 += XX_GROUP * MCE_WAVE) {
+    int xg[XX_GROUP];
+    bool kg[XX_GROUP];
+#pragma unroll
+    for (int z = 0; z < XX_GROUP; z++) {
+      const int i = c0 + z * MCE_WAVE + lane;
+      xg[z] = i < L ? xx[i] : 0;
+    }
+#pragma unroll
+    for (int z = 0; z < XX_GROUP; z++) kg[z] = c0 + z * MCE_WAVE + lane < L && test.adj(xg[z]);
+#pragma unroll
+    for (int z = 0; z < XX_GROUP; z++) {
+      const int c = c0 + z * MCE_WAVE;
+      if (c >= L) break;
+      const int x = xg[z];
+      const bool valid = c + lane < L;
+      const int kc_bound = min(MCE_WAVE, c - wk);
+      const int dval = lane < kc_bound ? xx[wk + lane] : 0;
+      const bool keep = kg[z];
+      const u64 km = ballot(keep);
+      const u64 vm = ballot(valid);
+      const int kc = __popcll(km);
+      const int D = min(kc, c - wk);
+      const int base = max(c, wk + kc);
+      __syncthreads();   // every lane holds its values before anything is written
+      if (keep) xx[wk + mbcnt(km)] = x;
+      if (lane < D) xx[base + lane] = dval;
+      if (valid && !keep) xx[base + D + mbcnt(vm & ~km)] = x;
+      wk += kc;
+      __syncthreads();
+    }
   }
   return wk;
 }
@@ -122,31 +141,43 @@ template <class Score>
 __device__ int xx_pivot_prune(int* xx, int L, u32 pc, u32& best, const Score& score) {
   const int lane = lane_id();
   int wk = 0;
-  for (int c = 0; c < L; c += MCE_WAVE) {
-    const int i = c + lane;
-    const bool valid = i < L;
-    const int x = valid ? xx[i] : 0;
-    const int kc_bound = min(MCE_WAVE, c - wk);
-    const int dval = lane < kc_bound ? xx[wk + lane] : 0;
-    u32 nb = 0;
-    if (valid) {
-      nb = score(x);
-      const u32 key = (nb << 20) | (u32)(MCE_MAX_LOCAL - x);
-      best = best > key ? best : key;
+  for (int c0 = 0; c0 < L; c0 += XX_GROUP * MCE_WAVE) {
+    int xg[XX_GROUP];
+    u32 ng[XX_GROUP];
+#pragma unroll
+    for (int z = 0; z < XX_GROUP; z++) {
+      const int i = c0 + z * MCE_WAVE + lane;
+      xg[z] = i < L ? xx[i] : 0;
     }
-    const bool keep = valid && nb != 0u;
-    const u64 km = ballot(keep);
-    const u64 vm = ballot(valid);
-    const int kc = __popcll(km);
-    const int D = min(kc, c - wk);
-    const int base = max(c, wk + kc);
-    __syncthreads();   // every lane holds its values before anything is written
-    if (keep) xx[wk + mbcnt(km)] = x;
-    if (lane < D) xx[base + lane] = dval;
-    if (valid && !keep) xx[base + D + mbcnt(vm & ~km)] = x;
-    wk += kc;
-    __syncthreads();
-    if (c + MCE_WAVE < L && (wave_max_u32(best) >> 20) == pc) return L;
+#pragma unroll
+    for (int z = 0; z < XX_GROUP; z++) ng[z] = c0 + z * MCE_WAVE + lane < L ? score(xg[z]) : 0u;
+#pragma unroll
+    for (int z = 0; z < XX_GROUP; z++) {
+      const int c = c0 + z * MCE_WAVE;
+      if (c >= L) break;
+      const int x = xg[z];
+      const bool valid = c + lane < L;
+      const int kc_bound = min(MCE_WAVE, c - wk);
+      const int dval = lane < kc_bound ? xx[wk + lane] : 0;
+      const u32 nb = ng[z];
+      if (valid) {
+        const u32 key = (nb << 20) | (u32)(MCE_MAX_LOCAL - x);
+        best = best > key ? best : key;
+      }
+      const bool keep = valid && nb != 0u;
+      const u64 km = ballot(keep);
+      const u64 vm = ballot(valid);
+      const int kc = __popcll(km);
+      const int D = min(kc, c - wk);
+      const int base = max(c, wk + kc);
+      __syncthreads();   // every lane holds its values before anything is written
+      if (keep) xx[wk + mbcnt(km)] = x;
+      if (lane < D) xx[base + lane] = dval;
+      if (valid && !keep) xx[base + D + mbcnt(vm & ~km)] = x;
+      wk += kc;
+      __syncthreads();
+      if (c + MCE_WAVE < L && (wave_max_u32(best) >> 20) == pc) return L;
+    }
   }
   return wk;
 }
@@ -155,9 +186,13 @@ __device__ int xx_pivot_prune(int* xx, int L, u32 pc, u32& best, const Score& sc
 template <class T>
 __device__ bool xx_any(const int* xx, int L, const T& test) {
   const int lane = lane_id();
-  for (int c = 0; c < L; c += MCE_WAVE) {
-    const int i = c + lane;
-    const bool hit = i < L && test.adj(xx[i]);
+  for (int c0 = 0; c0 < L; c0 += XX_GROUP * MCE_WAVE) {
+    bool hit = false;
+#pragma unroll
+    for (int z = 0; z < XX_GROUP; z++) {
+      const int i = c0 + z * MCE_WAVE + lane;
+      hit |= i < L && test.adj(xx[i]);
+    }
     if (ballot(hit)) return true;
   }
   return false;
@@ -169,19 +204,32 @@ template <class T>
 __device__ int xx_filter_copy(const int* xx, int L, const T& test, int* dst) {
   const int lane = lane_id();
   int n = 0;
-  for (int c = 0; c < L; c += MCE_WAVE) {
-    const int i = c + lane;
-    const int a = i < L ? xx[i] : 0;
-    const bool keep = i < L && test.adj(a);
-    const u64 m = ballot(keep);
-    if (keep) st_relaxed_i(&dst[n + mbcnt(m)], a);
-    n += __popcll(m);
+  for (int c0 = 0; c0 < L; c0 += XX_GROUP * MCE_WAVE) {
+    int ag[XX_GROUP];
+    bool kg[XX_GROUP];
+#pragma unroll
+    for (int z = 0; z < XX_GROUP; z++) {
+      const int i = c0 + z * MCE_WAVE + lane;
+      ag[z] = i < L ? xx[i] : 0;
+    }
+#pragma unroll
+    for (int z = 0; z < XX_GROUP; z++) kg[z] = c0 + z * MCE_WAVE + lane < L && test.adj(ag[z]);
+#pragma unroll
+    for (int z = 0; z < XX_GROUP; z++) {
+      const u64 m = ballot(kg[z]);
+      if (kg[z]) st_relaxed_i(&dst[n + mbcnt(m)], ag[z]);
+      n += __popcll(m);
+    }
   }
   return n;
 }
 
 // ------------------------------------------------------------------ the kernel
-template <int W, bool IPX, bool SROWS, bool SSTACK, bool ACT>
+// STG: where the root's table is read from. 0: HBM; 1: the P rows staged in
+// LDS (the rows every node reads: pivot candidates of P u X_P, the branch
+// vertex's row), the X rows read from HBM by the X_X passes; 2: every row and
+// the X_X array in LDS.
+template <int W, bool IPX, int STG, bool SSTACK, bool ACT>
 __global__ __launch_bounds__(64) void k_search(SearchParams prm) {
   constexpr int REC = REC_WORDS(W);
   extern __shared__ u64 lds[];
@@ -202,7 +250,7 @@ __global__ __launch_bounds__(64) void k_search(SearchParams prm) {
   u64* hv = lds + prm.l_hv;
   int* pid = (int*)(lds + prm.l_pid);   // partial subgraph: ids of the P members
   u64* stk = SSTACK ? lds + prm.l_stack : (u64*)(slot + prm.s_stack);
-  int* xx = SROWS ? (int*)(lds + prm.l_xx) : (int*)(slot + prm.s_xx);
+  int* xx = STG == 2 ? (int*)(lds + prm.l_xx) : (int*)(slot + prm.s_xx);
   u64* lrows = lds + prm.l_rows;
 
   // a failed build leaves some tables unwritten, and a run past its time limit
@@ -269,12 +317,17 @@ __global__ __launch_bounds__(64) void k_search(SearchParams prm) {
     const u64* grow = T + 3;
     const u64* ghv = grow + (size_t)nrows * W;
     const int* gids = (const int*)(ghv + p);
-    const u64* rows;
-    if constexpr (SROWS) {
+    const u64* rows;   // every row
+    const u64* prow;   // the P rows (local index < p)
+    if constexpr (STG == 2) {
       for (int i = lane; i < nrows * W; i += MCE_WAVE) lrows[i] = grow[i];
-      rows = lrows;
-    } else {
+      rows = prow = lrows;
+    } else if constexpr (STG == 1) {
+      for (int i = lane; i < p * W; i += MCE_WAVE) lrows[i] = grow[i];
       rows = grow;
+      prow = lrows;
+    } else {
+      rows = prow = grow;
     }
     for (int i = lane; i < p; i += MCE_WAVE) hv[i] = ghv[i];
     if constexpr (!IPX) {
@@ -352,7 +405,7 @@ __global__ __launch_bounds__(64) void k_search(SearchParams prm) {
 #pragma unroll
           for (int wb = 0; wb < W; wb++) {
             const bool on = (cwv[wb] >> lane) & 1ull;
-            const u64* row = rows + (size_t)(on ? wb * 64 + lane : 0) * W;
+            const u64* row = prow + (size_t)(on ? wb * 64 + lane : 0) * W;
 #pragma unroll
             for (int w = 0; w < W; w++) rw[wb][w] = row[w];
           }
@@ -384,7 +437,7 @@ __global__ __launch_bounds__(64) void k_search(SearchParams prm) {
                   c = (u32)__popcll(read_lane(pj, 0) & rows[i]);
                 }
               } else {
-                const u64* row = rows + (size_t)i * W;
+                const u64* row = prow + (size_t)i * W;
 #pragma unroll
                 for (int w = 0; w < W; w++) c += (u32)__popcll(read_lane(pj, w) & row[w]);
               }
@@ -419,7 +472,7 @@ __global__ __launch_bounds__(64) void k_search(SearchParams prm) {
           const u64 ru = (u < p) ? read_lane(myrow, u) : rows[u];
           if (lane == 0) cj = pj & ~ru;
         } else {
-          if (lane < W) cj = pj & ~rows[(size_t)u * W + lane];
+          if (lane < W) cj = pj & ~(u < p ? prow : rows)[(size_t)u * W + lane];
         }
         act.mark(ACT_PIVOT);
 
@@ -459,7 +512,7 @@ __global__ __launch_bounds__(64) void k_search(SearchParams prm) {
               const u64 cw = read_lane(dC, j0);
               const int v = j0 * 64 + __builtin_ctzll(cw);
               const u64 vbit = cw & (~cw + 1);
-              const u64 rv = lane < W ? rows[(size_t)v * W + lane] : 0ull;
+              const u64 rv = lane < W ? prow[(size_t)v * W + lane] : 0ull;
               const u64 pn = dP & rv;
               const u64 xn = dX & rv;
               if ((int)wave_sum_u32(lane < W ? (u32)__popcll(pn) : 0u) >= prm.donate_min_p) {
@@ -535,7 +588,7 @@ __global__ __launch_bounds__(64) void k_search(SearchParams prm) {
       st_br++;
       u64 rv;
       if constexpr (W == 1) rv = read_lane(myrow, v);
-      else rv = lane < W ? rows[(size_t)v * W + lane] : 0;
+      else rv = lane < W ? prow[(size_t)v * W + lane] : 0;
       const u64 pn = pj & rv;   // P n N(v)
       const u64 xn = xj & rv;   // X_P n N(v)
       if (lane == j0) {         // C -= {v}; P -= {v}; X_P += {v} (Algorithm 2)
@@ -1054,26 +1107,32 @@ hipError_t mce_launch_wl_init(MceWl* wl, int nworkers, u64* stats, hipStream_t s
   return hipGetLastError();
 }
 
-template <int W, bool IPX, bool SR, bool SS>
+template <int W, bool IPX, int STG, bool SS>
 static const void* fn(bool act) {
-  return act ? (const void*)k_search<W, IPX, SR, SS, true> : (const void*)k_search<W, IPX, SR, SS, false>;
+  return act ? (const void*)k_search<W, IPX, STG, SS, true> : (const void*)k_search<W, IPX, STG, SS, false>;
 }
 
-// Variants (width 1 has its own kernel): widths 2 and 4 stage rows (light
-// sub-classes) and the stack in LDS as the layout allows; wider classes keep
-// both in HBM.
+template <int W, bool IPX>
+static const void* pick_w(int stg, bool sstack, bool act) {
+  switch (stg) {
+    case 0: return sstack ? fn<W, IPX, 0, true>(act) : fn<W, IPX, 0, false>(act);
+    case 1: return sstack ? fn<W, IPX, 1, true>(act) : fn<W, IPX, 1, false>(act);
+    case 2: return sstack ? fn<W, IPX, 2, true>(act) : fn<W, IPX, 2, false>(act);
+  }
+  return nullptr;
+}
+
+// Variants (width 1 has its own kernel): widths 2 and 4 stage rows (all of a
+// light sub-class's, or the P rows) and the stack in LDS as the layout allows;
+// wider classes keep both in HBM.
 template <bool IPX>
-static const void* pick(int wclass, bool srows, bool sstack, bool act) {
+static const void* pick(int wclass, int stg, bool sstack, bool act) {
   switch (wclass) {
-    case 1:
-      return srows ? (sstack ? fn<2, IPX, true, true>(act) : fn<2, IPX, true, false>(act))
-                   : (sstack ? fn<2, IPX, false, true>(act) : fn<2, IPX, false, false>(act));
-    case 2:
-      return srows ? (sstack ? fn<4, IPX, true, true>(act) : fn<4, IPX, true, false>(act))
-                   : (sstack ? fn<4, IPX, false, true>(act) : fn<4, IPX, false, false>(act));
-    case 3: return fn<8, IPX, false, false>(act);
-    case 4: return fn<16, IPX, false, false>(act);
-    case 5: return fn<32, IPX, false, false>(act);
+    case 1: return pick_w<2, IPX>(stg, sstack, act);
+    case 2: return pick_w<4, IPX>(stg, sstack, act);
+    case 3: return fn<8, IPX, 0, false>(act);
+    case 4: return fn<16, IPX, 0, false>(act);
+    case 5: return fn<32, IPX, 0, false>(act);
   }
   return nullptr;
 }
@@ -1088,9 +1147,10 @@ static const void* search_kernel(const SearchLayout& L) {
     return ipx ? (L.srows ? (const void*)k_search_w1<true, true, false> : (const void*)k_search_w1<true, false, false>)
                : (L.srows ? (const void*)k_search_w1<false, true, false> : (const void*)k_search_w1<false, false, false>);
   }
-  if (L.wclass >= 3 && (L.srows || L.sstack)) return nullptr;
-  return L.mode == MCE_MODE_IPX ? pick<true>(L.wclass, L.srows, L.sstack, L.counters)
-                                : pick<false>(L.wclass, L.srows, L.sstack, L.counters);
+  if (L.wclass >= 3 && (L.srows || L.sprows || L.sstack)) return nullptr;
+  const int stg = L.srows ? 2 : L.sprows ? 1 : 0;
+  return L.mode == MCE_MODE_IPX ? pick<true>(L.wclass, stg, L.sstack, L.counters)
+                                : pick<false>(L.wclass, stg, L.sstack, L.counters);
 }
 
 static size_t a256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -1105,6 +1165,11 @@ static size_t a256(size_t x) { return (x + 255) & ~(size_t)255; }
 // thousands of heavy roots keeps them in HBM and its wavefronts (the 500k
 // Chung-Lu graph's width-2 launch ran slower with its rows in LDS).
 #define HEAVY_STAGE_BYTES (24 * 1024)
+// Otherwise a width-2 or width-4 launch stages the P rows alone when they take
+// at most this many bytes: the rows that every node reads (pivot candidates of
+// P u X_P, the branch vertex's row) then cost an LDS round trip, while the X
+// rows, read only by the X_X passes, stay in HBM.
+#define PROWS_STAGE_BYTES 2048
 
 SearchLayout mce_search_layout(int sub, int mode, int pcap, int xcap, int rcap, int nroots, int num_cu,
                                bool force_hbm, bool counters) {
@@ -1124,6 +1189,8 @@ SearchLayout mce_search_layout(int sub, int mode, int pcap, int xcap, int rcap, 
   const size_t stage = (size_t)L.rcap * W * 8 + (size_t)L.xcap * 4;
   L.srows = !force_hbm && L.wclass <= 2 &&
             (light || (nroots <= 2 * num_cu && stage <= (size_t)HEAVY_STAGE_BYTES));
+  L.sprows = !force_hbm && !L.srows && L.wclass >= 1 && L.wclass <= 2 &&
+             (size_t)L.pcap * W * 8 <= (size_t)PROWS_STAGE_BYTES;
   const size_t stack_words = (size_t)L.levels * rec;
   // width 1 keeps its level stack in VGPRs
   L.sstack = L.wclass > 0 && !force_hbm && L.wclass <= 2 && stack_words * 8 <= 12288;
@@ -1140,6 +1207,7 @@ SearchLayout mce_search_layout(int sub, int mode, int pcap, int xcap, int rcap, 
   if (L.sstack) o += stack_words;
   L.l_rows = (int)o;
   if (L.srows) o += (size_t)L.rcap * W;
+  else if (L.sprows) o += (size_t)L.pcap * W;
   L.l_xx = (int)o;
   if (L.srows) o += ((size_t)L.xcap + 1) / 2;
   L.lds_bytes = o * 8;
