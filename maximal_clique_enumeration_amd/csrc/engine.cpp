@@ -228,6 +228,15 @@ constexpr int kMicroStackMinStatic = 256;      // the smallest stack mce_run_sta
 #endif
 // micro launches with this many roots per wave share pivot scans
 constexpr int kMicroCoopRootsPerWave = MCE_MICRO_COOP_ROOTS_PER_WAVE;
+#ifndef MCE_W1_WAVES_PER_CU
+#define MCE_W1_WAVES_PER_CU 8
+#endif
+// Width-1 launches keep at most this many wavefronts per CU. Their waves are
+// fast and soon idle, and every idle wave asks the busy ones for branches, so
+// more of them cost the waves that hold the work more than they add (the 500k
+// Chung-Lu graph's 143 and 20,491 width-1 roots: 2.3 and 2.2 ms with 28 waves
+// per CU, 1.1 and 0.9 ms with 8).
+constexpr int kW1WavesPerCu = MCE_W1_WAVES_PER_CU;
 // Tables other than micro ones are built by the split build: a root's rows are
 // dealt over several blocks, about this many (root, part) blocks per CU.
 constexpr int kSplitBlocksPerCu = 16;
@@ -510,6 +519,7 @@ mce_status run_once(mce_engine* e, int32_t n, int64_t nnz, const int32_t* row_pt
                      [&] { return mce_search_max_workers(L, e->num_cu); });
     }
     if (nw <= 0) return fail(e, MCE_ERR_DEVICE, "search kernel occupancy query failed");
+    if (c != MCE_SUB_MICRO && (c >> 1) == 0) nw = std::min(nw, kW1WavesPerCu * e->num_cu);
     if (e->cfg.max_workers > 0) nw = std::min(nw, (int)e->cfg.max_workers);
     if (!e->cfg.worker_list) nw = std::min(nw, counts[c]);
     pl.nw = nw;
