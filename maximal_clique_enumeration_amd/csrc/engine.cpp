@@ -40,6 +40,8 @@ struct Bufs {
   DevBuf hub_id, hub_v, hub_bm;                       // their hub adjacency bitmaps
   DevBuf fadj, fdeg, flong;                           // forward adjacency (table builds)
   DevBuf tcol, tcrow;                                 // the peel's compacted residual graph
+  // the early launch of a split peel (the roots that left before the tail)
+  DevBuf ctl1, snap, fadj1, fdeg1, flong1, pcount1, xcount1, lists1, taboff1, scan1, heap1, mstack1, mail1, stats1;
 };
 
 constexpr size_t kHistWords = MCE_MAX_P + 3;   // global histogram entries (sizes up to 2 + MCE_MAX_P)
@@ -71,13 +73,19 @@ struct mce_engine {
   Bufs* last = &own;  // the set the last run used (mce_ordering, mce_stats)
   HostPinned host;    // staging for device -> host copies (mce_run, mce_run_roots)
   alignas(64) unsigned char host_io[kIoBytes];   // the same for mce_run_static (pageable)
-  hipEvent_t ev[4 + 4 * MCE_NSUB] = {};
+  hipEvent_t ev[4 + 4 * (MCE_NSUB + 1)] = {};
   bool have_events = false;
   // the overlapped search launches: streams forked from the caller's stream
   // (fork_ev) and joined back to it (join_ev)
   hipStream_t side[MCE_SIDE_STREAMS] = {};
   hipEvent_t fork_ev = nullptr;
   hipEvent_t join_ev[MCE_SIDE_STREAMS] = {};
+  // the early launch of a split peel: its own stream, which starts at the
+  // grid's hand-over (handed_ev) and is joined back (early_join_ev); its
+  // control block is read back through host1
+  hipStream_t early = nullptr;
+  hipEvent_t handed_ev = nullptr, early_join_ev = nullptr;
+  HostPinned host1;
 
   // last run
   bool have_result = false;
@@ -95,8 +103,9 @@ struct mce_engine {
   // mce_worker_trace asks for them (they are diagnostics, not results)
   struct LaunchInfo {
     int sub, nw, roots;
+    bool early;   // the split peel's early launch: its counters are in stats1
   };
-  LaunchInfo last_plan[MCE_NSUB] = {};
+  LaunchInfo last_plan[MCE_NSUB + 1] = {};
   // where the last run's induced-subgraph tables sit (mce_root_table): valid
   // after a complete first-level run with overlapped launches, each sub-class
   // in its own heap region
@@ -106,6 +115,7 @@ struct mce_engine {
     int total = 0;                      // root-list entries
     int off[MCE_NSUB] = {}, count[MCE_NSUB] = {};
     size_t heap_base[MCE_NSUB] = {};    // u64 words
+    int early = 0;                      // the early launch's roots (micro tables in heap1)
   } tabs;
   int n_last_plan = 0;
   int last_stat_rows = 0;
@@ -240,6 +250,8 @@ constexpr int kW1WavesPerCu = MCE_W1_WAVES_PER_CU;
 // Tables other than micro ones are built by the split build: a root's rows are
 // dealt over several blocks, about this many (root, part) blocks per CU.
 constexpr int kSplitBlocksPerCu = 16;
+// the split peel's early launch records its subtrees taken here (MceCtl::taken)
+constexpr int kTakenEarly = 2 * MCE_NCLASS + 1;
 
 // ------------------------------------------------------------------ static scratch
 // The device memory of mce_run_static: one array per device, holding every
@@ -321,6 +333,7 @@ mce_status run_once(mce_engine* e, int32_t n, int64_t nnz, const int32_t* row_pt
   // events around the search launches only (every recorded event costs the stream a few us)
   const bool stimes = (timing || (e->cfg.flags & MCE_FLAG_SEARCH_TIMES)) && e->have_events;
   const bool hbm = (e->cfg.flags & MCE_FLAG_HBM_STAGING) != 0;
+  const bool counters_on = (e->cfg.flags & MCE_FLAG_COUNTERS) != 0;
   const u64 budget = (u64)((double)e->cfg.timeout_ms * 1e-3 * e->tick_hz);
   // sub-class launches overlapped on the engine's streams, each with its own
   // heap region, worker list and slots; else one after another, sharing them
@@ -334,7 +347,7 @@ mce_status run_once(mce_engine* e, int32_t n, int64_t nnz, const int32_t* row_pt
       (h = take(arena, B.bfront0, nb)) != hipSuccess || (h = take(arena, B.bfront1, nb)) != hipSuccess ||
       (h = take(arena, B.pcount, (size_t)std::max(cnt, 1) * sizeof(int))) != hipSuccess ||
       (h = take(arena, B.xcount, (size_t)std::max(cnt, 1) * sizeof(int))) != hipSuccess ||
-      (h = take(arena, B.wl, sizeof(MceWl) * (overlap ? MCE_NSUB : 1))) != hipSuccess)
+      (h = take(arena, B.wl, sizeof(MceWl) * (overlap ? MCE_NSUB + 1 : 1))) != hipSuccess)
     return alloc_fail(e, arena, h, "allocation");
   if (!stat && (h = ensure_host(e->host, kIoBytes)) != hipSuccess) return hip_fail(e, h, "allocation");
   // second-level subtrees (section 3.2): the roots are the vertex roots' forward edges
@@ -390,11 +403,32 @@ mce_status run_once(mce_engine* e, int32_t n, int64_t nnz, const int32_t* row_pt
         (h = ensure(B.tcrow, (size_t)mce_peel_tail_rows() * sizeof(int))) != hipSuccess)
       return hip_fail(e, h, "allocation");
   }
+  // Split peel: the grid stops where block 0 would finish alone on the
+  // compacted residual graph, and the tail runs as a one-block launch of its
+  // own. Every vertex gone by then has its final round, and every vertex still
+  // in the tail comes after it, so those roots' subtrees are fixed already: the
+  // micro-sized ones are built and searched on the early stream, on the compute
+  // units the tail leaves idle (whole-graph first-level runs with overlapped
+  // launches and the micro kernel).
+  const bool micro_on = (e->cfg.flags & MCE_FLAG_NO_MICRO) == 0;
+  const bool split = overlap && !l2 && !subset && micro_on && tcap > 0;
+  MceCtl* ctl1 = nullptr;
+  if (split) {
+    const size_t snap_words = ((size_t)n + 7) / 8;
+    if ((h = ensure(B.ctl1, sizeof(MceCtl))) != hipSuccess ||
+        (h = ensure(B.snap, snap_words * sizeof(u64))) != hipSuccess)
+      return hip_fail(e, h, "allocation");
+    ctl1 = dp<MceCtl>(B.ctl1);
+    if ((h = mce_launch_zero(dp<u64>(B.ctl1), sizeof(MceCtl) / sizeof(u64), s)) != hipSuccess ||
+        (h = mce_launch_zero(dp<u64>(B.snap), snap_words, s)) != hipSuccess)
+      return hip_fail(e, h, "clear");
+  }
   if ((h = mce_launch_peel(n, row_ptr, col_idx, dp<int>(B.deg), dp<int>(B.rnd), dp<int>(B.core),
                            dp<int>(B.alive0), dp<int>(B.alive1), dp<int>(B.front0), dp<int>(B.front1),
                            dp<int>(B.bfront0), dp<int>(B.bfront1), ctl, budget,
                            tcap ? dp<unsigned short>(B.tcol) : nullptr, tcap, tcap ? dp<int>(B.tcrow) : nullptr,
-                           pblocks, s)) != hipSuccess)
+                           pblocks, split ? 1 : 0, split ? dp<unsigned char>(B.snap) : nullptr,
+                           split ? e->handed_ev : nullptr, s)) != hipSuccess)
     return hip_fail(e, h, "peel launch");
   if (timing) (void)hipEventRecord(e->ev[2], s);
   if (maxhubs > 0 && (h = mce_launch_hubs(n, row_ptr, col_idx, dp<int>(B.hub_id), dp<int>(B.hub_v),
@@ -415,7 +449,7 @@ mce_status run_once(mce_engine* e, int32_t n, int64_t nnz, const int32_t* row_pt
     return hip_fail(e, h, "forward adjacency launch");
   if ((h = mce_launch_orient(n, row_ptr, col_idx, dp<int>(B.rnd), subset ? roots : nullptr, cnt,
                              dp<int>(B.pcount), dp<int>(B.xcount), ctl, l2 ? dp<u64>(B.fwd) : nullptr,
-                             early_fadj ? dp<int>(B.fdeg) : nullptr, grid, s)) != hipSuccess)
+                             early_fadj ? dp<int>(B.fdeg) : nullptr, grid, s, split ? 1 : 0)) != hipSuccess)
     return hip_fail(e, h, "orient launch");
   if (l2 && (h = mce_launch_l2_roots(n, nnz, row_ptr, col_idx, dp<int>(B.rnd), subset ? roots : nullptr, cnt,
                                      dp<u64>(B.fwd), dp<u64>(B.fwdtmp), dp<int>(B.src), dp<int>(B.eroots),
@@ -426,6 +460,112 @@ mce_status run_once(mce_engine* e, int32_t n, int64_t nnz, const int32_t* row_pt
   MceCtl* hctl = reinterpret_cast<MceCtl*>(hio);
   if ((h = hipMemcpyAsync(hctl, ctl, sizeof(MceCtl), hipMemcpyDeviceToHost, s)) != hipSuccess)
     return hip_fail(e, h, "readback");
+
+  // The early launch, on its own stream from the grid's hand-over (while the
+  // tail and the steps above run on s): the early forward adjacency, the early
+  // roots' tallies (read back), then their micro tables and search. A return
+  // on any path after this waits for that stream first.
+  struct StreamGuard {
+    hipStream_t st = nullptr;
+    ~StreamGuard() {
+      if (st) (void)hipStreamSynchronize(st);
+    }
+  } early_guard;
+  int n1 = 0, early_nw = 0;
+  u64 words1 = 0;
+  if (split) {
+    if ((h = ensure(B.fadj1, (size_t)std::max<int64_t>(nnz, 1) * sizeof(int))) != hipSuccess ||
+        (h = ensure(B.fdeg1, (size_t)n * sizeof(int))) != hipSuccess ||
+        (h = ensure(B.flong1, (size_t)n * sizeof(int))) != hipSuccess ||
+        (h = ensure(B.pcount1, (size_t)n * sizeof(int))) != hipSuccess ||
+        (h = ensure(B.xcount1, (size_t)n * sizeof(int))) != hipSuccess ||
+        (h = ensure_host(e->host1, sizeof(MceCtl))) != hipSuccess)
+      return hip_fail(e, h, "allocation");
+    early_guard.st = e->early;
+    MceCtl* h1 = static_cast<MceCtl*>(e->host1.p);
+    if ((h = hipStreamWaitEvent(e->early, e->handed_ev, 0)) != hipSuccess ||
+        (h = mce_launch_forward_adj(n, row_ptr, col_idx, dp<int>(B.rnd), dp<int>(B.fadj1), dp<int>(B.fdeg1),
+                                    dp<int>(B.flong1), ctl1, e->num_cu * 16, e->early, ctl,
+                                    dp<unsigned char>(B.snap), dp<int>(B.deg))) != hipSuccess ||
+        (h = mce_launch_orient_early(n, row_ptr, dp<unsigned char>(B.snap), dp<int>(B.fdeg1), ctl,
+                                     dp<int>(B.pcount1), dp<int>(B.xcount1), ctl1, grid, e->early)) != hipSuccess ||
+        (h = hipMemcpyAsync(h1, ctl1, sizeof(MceCtl), hipMemcpyDeviceToHost, e->early)) != hipSuccess ||
+        (h = hipStreamSynchronize(e->early)) != hipSuccess)
+      return hip_fail(e, h, "early orientation");
+    if (h1->status) return fail(e, MCE_ERR_DEVICE, "early orientation failed");
+    if (h1->tail_go) {
+      n1 = h1->sub_count[0][MCE_SUB_MICRO];
+      words1 = h1->sub_words[0][MCE_SUB_MICRO];
+    }
+    if (n1 > 0) {
+      // as the micro launch below: at most 8 wavefronts per CU
+      early_nw = occupancy(e, -1 - (counters_on ? 1 : 0), 0LL,
+                           [&] { return mce_micro_max_workers(counters_on, e->num_cu); });
+      early_nw = std::min(early_nw, 8 * e->num_cu);
+      if (early_nw <= 0) return fail(e, MCE_ERR_DEVICE, "micro kernel occupancy query failed");
+      if (e->cfg.max_workers > 0) early_nw = std::min(early_nw, (int)e->cfg.max_workers);
+      if (!e->cfg.worker_list) early_nw = std::min(early_nw, n1);
+      const int cap1 = e->micro_stack;
+      if ((h = ensure(B.lists1, (size_t)n1 * sizeof(int))) != hipSuccess ||
+          (h = ensure(B.taboff1, (size_t)n1 * sizeof(u64))) != hipSuccess ||
+          (h = ensure(B.scan1, (size_t)mce_scan_temp_words(n1) * sizeof(u64))) != hipSuccess ||
+          (h = ensure(B.heap1, (size_t)words1 * sizeof(u64))) != hipSuccess ||
+          (h = ensure(B.mstack1, 6 * sizeof(u64) * (size_t)early_nw * (size_t)cap1)) != hipSuccess ||
+          (h = ensure(B.mail1, (size_t)early_nw * mce_micro_mail_words() * sizeof(u64))) != hipSuccess ||
+          (h = ensure(B.stats1, (size_t)early_nw * MCE_NSTAT * sizeof(u64))) != hipSuccess)
+        return hip_fail(e, h, "early search buffers");
+      SubOffsets off1{};
+      MceWl* wl1 = dp<MceWl>(B.wl) + MCE_NSUB;
+      if ((h = mce_launch_bucket(nullptr, n, dp<int>(B.pcount1), dp<int>(B.xcount1), MCE_MODE_IPX, 1, off1,
+                                 dp<int>(B.lists1), dp<u64>(B.taboff1), ctl1, grid, e->early)) != hipSuccess ||
+          (h = mce_launch_scan(dp<u64>(B.taboff1), n1, dp<u64>(B.scan1), e->early)) != hipSuccess ||
+          (h = mce_launch_wl_init(wl1, early_nw, dp<u64>(B.stats1), e->early)) != hipSuccess)
+        return hip_fail(e, h, "early launch");
+      BuildParams bp{};
+      bp.rp = row_ptr;
+      bp.ci = col_idx;
+      bp.rnd = dp<int>(B.rnd);
+      bp.roots = dp<int>(B.lists1);
+      bp.nroots = n1;
+      bp.W = 1;
+      bp.mode = MCE_MODE_IPX;
+      bp.micro = 1;
+      bp.heap = dp<u64>(B.heap1);
+      bp.heap_words = (size_t)words1;
+      bp.tab_off = dp<u64>(B.taboff1);
+      bp.status = &ctl->status;
+      bp.fadj = dp<int>(B.fadj1);
+      bp.fdeg = dp<int>(B.fdeg1);
+      bp.snap = dp<unsigned char>(B.snap);
+      if (timing) (void)hipEventRecord(e->ev[4], e->early);
+      if ((h = mce_launch_build(bp, e->num_cu * 32, e->early)) != hipSuccess) return hip_fail(e, h, "early build");
+      if (timing) (void)hipEventRecord(e->ev[5], e->early);
+      MicroParams mp{};
+      mp.heap = dp<u64>(B.heap1);
+      mp.tab_off = dp<u64>(B.taboff1);
+      mp.nroots = n1;
+      mp.nworkers = early_nw;
+      mp.stacks = dp<u64>(B.mstack1);
+      mp.stack_cap = cap1;
+      mp.mail_words = mce_micro_mail_words();
+      mp.mail = dp<u64>(B.mail1);
+      mp.g_hist = results + 1;
+      mp.g_hash = results;
+      mp.wl = wl1;
+      mp.donate_min_p = e->cfg.micro_donate_min_p > 0 ? (int)e->cfg.micro_donate_min_p : 10;
+      mp.worker_list = e->cfg.worker_list ? 1 : 0;
+      mp.coop = n1 >= kMicroCoopRootsPerWave * early_nw ? 1 : 0;
+      mp.budget = budget;
+      mp.t_run = &ctl->t_run;
+      mp.status = &ctl->status;
+      mp.stats = dp<u64>(B.stats1);
+      mp.taken = &ctl->taken[kTakenEarly];
+      if (stimes) (void)hipEventRecord(e->ev[6], e->early);
+      if ((h = mce_launch_micro(counters_on, mp, e->early)) != hipSuccess) return hip_fail(e, h, "early search");
+      if (stimes) (void)hipEventRecord(e->ev[7], e->early);
+      if ((h = hipEventRecord(e->early_join_ev, e->early)) != hipSuccess) return hip_fail(e, h, "early join");
+    }
+  }
   if ((h = hipStreamSynchronize(s)) != hipSuccess) return hip_fail(e, h, "synchronize after orient");
 
   const u32 gbits = hctl->status & 0x1Fu;
@@ -469,7 +609,6 @@ mce_status run_once(mce_engine* e, int32_t n, int64_t nnz, const int32_t* row_pt
   e->info.subgraph = mode == MCE_MODE_IPX ? MCE_SUBGRAPH_FULL : MCE_SUBGRAPH_PARTIAL;
 
   // roots per sub-class of that mode (and with the micro sub-class on or off)
-  const bool micro_on = (e->cfg.flags & MCE_FLAG_NO_MICRO) == 0;
   const int var = mode | (micro_on ? 0 : 2);
   SubOffsets off{};
   int counts[MCE_NSUB];
@@ -607,7 +746,7 @@ mce_status run_once(mce_engine* e, int32_t n, int64_t nnz, const int32_t* row_pt
   if (overlap && nplan > 0 && (h = hipEventRecord(e->fork_ev, s)) != hipSuccess) return hip_fail(e, h, "fork");
 
   int launches = 0, max_workers_used = 0, stat_off = 0;
-  int evi = 4;
+  int evi = n1 > 0 ? 8 : 4;   // the early launch has events 4..7
   for (int pi = 0; pi < nplan; pi++) {
     const Plan& pl = plan[pi];
     const int c = pl.sub;
@@ -739,6 +878,7 @@ mce_status run_once(mce_engine* e, int32_t n, int64_t nnz, const int32_t* row_pt
         return launch_fail(h, "join");
     }
   }
+  if (n1 > 0 && (h = hipStreamWaitEvent(s, e->early_join_ev, 0)) != hipSuccess) return launch_fail(h, "early join");
   // results: one read-back of the control block and the result words
   if ((h = hipMemcpyAsync(hio, ctl, kIoBytes, hipMemcpyDeviceToHost, s)) != hipSuccess)
     return hip_fail(e, h, "result readback");
@@ -774,29 +914,37 @@ mce_status run_once(mce_engine* e, int32_t n, int64_t nnz, const int32_t* row_pt
   {
     int64_t started = 0;
     for (int i = 0; i < launches; i++) started += std::min<int64_t>(hctl->taken[i], counts[plan[i].sub]);
+    if (n1 > 0) started += std::min<int64_t>(hctl->taken[kTakenEarly], n1);
     // roots that need no search: isolated vertices, and second-level roots that are cliques of size 2
-    started += (int64_t)nsub - total;
+    started += (int64_t)nsub - total - n1;
     e->info.roots_started = started;
   }
 
   mce_run_stats& so = e->stats_out;
-  so.workers = max_workers_used;
-  so.launches = launches;
-  u64 words_built = 0;
+  so.workers = std::max(max_workers_used, early_nw);
+  const int e0 = n1 > 0 ? 1 : 0;   // the early launch comes first in the launch lists
+  so.launches = launches + e0;
+  u64 words_built = words1;
   for (int i = 0; i < nplan; i++) words_built += hctl->sub_words[var][plan[i].sub];
   so.table_words = words_built;
-  e->n_last_plan = nplan;
+  e->n_last_plan = nplan + e0;
+  if (e0) {
+    e->last_plan[0] = {MCE_SUB_MICRO, early_nw, n1, true};
+    so.launch_sub[0] = MCE_SUB_MICRO;
+    so.launch_roots[0] = n1;
+    so.launch_words[0] = words1;
+  }
   for (int i = 0; i < nplan; i++) {
-    e->last_plan[i] = {plan[i].sub, plan[i].nw, counts[plan[i].sub]};
-    if (i < 16) {
-      so.launch_sub[i] = plan[i].sub;
-      so.launch_roots[i] = counts[plan[i].sub];
-      so.launch_words[i] = hctl->sub_words[var][plan[i].sub];
+    e->last_plan[e0 + i] = {plan[i].sub, plan[i].nw, counts[plan[i].sub], false};
+    if (e0 + i < 16) {
+      so.launch_sub[e0 + i] = plan[i].sub;
+      so.launch_roots[e0 + i] = counts[plan[i].sub];
+      so.launch_words[e0 + i] = hctl->sub_words[var][plan[i].sub];
     }
   }
   for (int i = 0; i < 4; i++) so.peel_ticks[i] = hctl->peel_ticks[i];
-  so.micro_roots = counts[MCE_SUB_MICRO];
-  so.micro_stack_cap = micro_nw ? micro_cap : 0;
+  so.micro_roots = counts[MCE_SUB_MICRO] + n1;
+  so.micro_stack_cap = micro_nw || early_nw ? micro_cap : 0;
   e->last_stat_rows = stat_rows;
   e->last_timing = timing;
   e->last_stimes = stimes;
@@ -805,6 +953,7 @@ mce_status run_once(mce_engine* e, int32_t n, int64_t nnz, const int32_t* row_pt
     mce_engine::TableMap& tm = e->tabs;
     tm.mode = mode;
     tm.total = total;
+    tm.early = n1;
     for (int c = 0; c < MCE_NSUB; c++) {
       tm.off[c] = off.off[c];
       tm.count[c] = counts[c];
@@ -841,6 +990,14 @@ mce_status collect_stats(mce_engine* e) {
   if (!st.empty() && (h = hipMemcpy(st.data(), e->last->stats.p, st.size() * sizeof(u64), hipMemcpyDeviceToHost)) !=
                          hipSuccess)
     return hip_fail(e, h, "stats readback");
+  // the split peel's early launch keeps its rows apart
+  std::vector<u64> st1;
+  if (e->n_last_plan > 0 && e->last_plan[0].early) {
+    st1.resize((size_t)e->last_plan[0].nw * MCE_NSTAT);
+    if ((h = hipMemcpy(st1.data(), e->last->stats1.p, st1.size() * sizeof(u64), hipMemcpyDeviceToHost)) !=
+        hipSuccess)
+      return hip_fail(e, h, "stats readback");
+  }
   mce_run_stats& so = e->stats_out;
   std::vector<u64> stat_sum(MCE_NSTAT, 0);
   e->trace.clear();
@@ -849,8 +1006,8 @@ mce_status collect_stats(mce_engine* e) {
   for (int li = 0; li < e->n_last_plan; li++) {
     const auto& pl = e->last_plan[li];
     u64 smin = ~0ull, smax = 0;
-    for (int w = 0; w < pl.nw; w++, row++) {
-      const u64* r = &st[(size_t)row * MCE_NSTAT];
+    for (int w = 0; w < pl.nw; w++) {
+      const u64* r = pl.early ? &st1[(size_t)w * MCE_NSTAT] : &st[(size_t)(row++) * MCE_NSTAT];
       mce_worker_record rec{};
       rec.launch = (int32_t)li;
       rec.worker = w;
@@ -1015,6 +1172,9 @@ mce_status mce_create(const mce_config* cfg, mce_engine** out) {
     side_ok = side_ok && hipStreamCreateWithFlags(&e->side[k], hipStreamNonBlocking) == hipSuccess;
     side_ok = side_ok && hipEventCreateWithFlags(&e->join_ev[k], hipEventDisableTiming) == hipSuccess;
   }
+  side_ok = side_ok && hipStreamCreateWithFlags(&e->early, hipStreamNonBlocking) == hipSuccess &&
+            hipEventCreateWithFlags(&e->handed_ev, hipEventDisableTiming) == hipSuccess &&
+            hipEventCreateWithFlags(&e->early_join_ev, hipEventDisableTiming) == hipSuccess;
   if (!side_ok) {
     mce_destroy(e);
     return MCE_ERR_DEVICE;
@@ -1076,6 +1236,41 @@ mce_status mce_root_table(const mce_engine* e, int32_t root, uint64_t* words, in
   if (!tm.valid || root < 0 || root >= e->last_n) return MCE_ERR_STATE;
   if (hipSetDevice(e->device) != hipSuccess) return MCE_ERR_DEVICE;
   hipStream_t s = static_cast<hipStream_t>(stream);
+  // a split peel's early root: a micro table in the early launch's heap
+  if (tm.early > 0) {
+    std::vector<int32_t> l1((size_t)tm.early);
+    if (hipMemcpyAsync(l1.data(), e->own.lists1.p, (size_t)tm.early * sizeof(int32_t), hipMemcpyDeviceToHost, s) !=
+            hipSuccess ||
+        hipStreamSynchronize(s) != hipSuccess)
+      return MCE_ERR_DEVICE;
+    int i1 = -1;
+    for (int j = 0; j < tm.early; j++)
+      if (l1[j] == root) {
+        i1 = j;
+        break;
+      }
+    if (i1 >= 0) {
+      u64 to[2] = {0, 0};
+      const u64* taboff1 = static_cast<const u64*>(e->own.taboff1.p);
+      if (hipMemcpyAsync(&to[0], taboff1 + i1, sizeof(u64), hipMemcpyDeviceToHost, s) != hipSuccess ||
+          hipMemcpyAsync(&to[1], taboff1, sizeof(u64), hipMemcpyDeviceToHost, s) != hipSuccess ||
+          hipStreamSynchronize(s) != hipSuccess)
+        return MCE_ERR_DEVICE;
+      const u64* T = static_cast<const u64*>(e->own.heap1.p) + (to[0] - to[1]);
+      u64 hdr = 0;
+      if (hipMemcpyAsync(&hdr, T, sizeof(u64), hipMemcpyDeviceToHost, s) != hipSuccess ||
+          hipStreamSynchronize(s) != hipSuccess)
+        return MCE_ERR_DEVICE;
+      const u64 nw = mce_micro_table_words((int)(u32)hdr, (int)(hdr >> 32));
+      *len = (int64_t)nw;
+      *form = 1 | (1 << 8) | (1 << 9);
+      if ((u64)cap < nw) return MCE_ERR_ARG;
+      if (hipMemcpyAsync(words, T, nw * sizeof(u64), hipMemcpyDeviceToHost, s) != hipSuccess ||
+          hipStreamSynchronize(s) != hipSuccess)
+        return MCE_ERR_DEVICE;
+      return MCE_OK;
+    }
+  }
   // the root's place in the bucketed root lists, hence its sub-class
   std::vector<int32_t> lists((size_t)std::max(tm.total, 1));
   if (tm.total > 0 && (hipMemcpyAsync(lists.data(), e->own.lists.p, (size_t)tm.total * sizeof(int32_t),
@@ -1179,16 +1374,21 @@ void mce_destroy(mce_engine* e) {
                     &b.bfront0, &b.bfront1, &b.pcount, &b.xcount,  &b.lists,  &b.taboff,  &b.scan,   &b.heap,
                     &b.wl,     &b.slots,  &b.stats,   &b.mstack,  &b.mail,   &b.src,     &b.fwd,    &b.fwdtmp,
                     &b.eroots, &b.pcount2, &b.xcount2, &b.hub_id, &b.hub_v,  &b.hub_bm, &b.fadj, &b.fdeg, &b.flong,
-                    &b.tcol,   &b.tcrow};
+                    &b.tcol,   &b.tcrow,  &b.ctl1,    &b.snap,    &b.fadj1,   &b.fdeg1,  &b.flong1,  &b.pcount1, &b.xcount1,
+                    &b.lists1, &b.taboff1, &b.scan1,  &b.heap1,   &b.mstack1, &b.mail1,  &b.stats1};
   for (DevBuf* d : bufs) release(*d);
   if (e->host.p) (void)hipHostFree(e->host.p);
+  if (e->host1.p) (void)hipHostFree(e->host1.p);
   for (auto& ev : e->ev)
     if (ev) (void)hipEventDestroy(ev);
   for (auto& ev : e->join_ev)
     if (ev) (void)hipEventDestroy(ev);
   if (e->fork_ev) (void)hipEventDestroy(e->fork_ev);
+  if (e->handed_ev) (void)hipEventDestroy(e->handed_ev);
+  if (e->early_join_ev) (void)hipEventDestroy(e->early_join_ev);
   for (auto& st : e->side)
     if (st) (void)hipStreamDestroy(st);
+  if (e->early) (void)hipStreamDestroy(e->early);
   delete e;
 }
 

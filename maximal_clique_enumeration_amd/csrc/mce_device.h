@@ -132,7 +132,14 @@ struct MceCtl {
   int seg_state[12];     // peel: the state block 0 hands back (result, list, frontier, level, round, slot, sums)
   u64 t_run;             // wall-clock tick at the start of the peel: the run's time limit counts from it
   u64 peel_ticks[4];     // block 0 of the peel: barrier waits, level passes, round work, total
-  u32 taken[2 * MCE_NCLASS + 1];   // per search launch: subtrees handed out (see record_taken)
+  // split peel (the grid stops where block 0 would go on alone on the compacted
+  // residual graph, and k_peel_tail goes on from here in a launch of its own)
+  int tail_go;           // 1: the grid handed over, with the state below
+  int tail_r0;           // the tail's first round: every vertex with a smaller round has left
+  int tail_st[4];        // level, round, vertices left, which remaining list
+  u64 tail_ticks[3];     // block 0's barrier, level and round ticks up to the hand-over
+  u32 taken[2 * MCE_NCLASS + 2];   // per search launch: subtrees handed out (see record_taken); the
+                                   // last one is the split peel's early launch's
   // grid barrier of the peel, one 128-byte line each: [0] groups complete,
   // [1] barriers released, [2 + g] arrivals of block group g (all counts since
   // the launch began)

@@ -187,6 +187,9 @@ struct BuildParams {
   // after v in the peel order at fadj[rp[v] .. rp[v] + fdeg[v]), in id order
   const int* fadj;
   const int* fdeg;
+  // a split peel's early roots (micro build only), the tail still running:
+  // its hand-over snapshot (1: still in the tail, hence later than the root)
+  const unsigned char* snap;
 };
 
 // Clears words u64 at p.
@@ -196,10 +199,14 @@ hipError_t mce_launch_validate(int n, long long nnz, const int* rp, const int* c
                                hipStream_t s);
 // tcol (tcap 16-bit entries) and tcrow (mce_peel_tail_rows() ints): the residual
 // graph that block 0 of a grid peel finishes on once few vertices remain; tcap 0
-// keeps the grid to the end.
+// keeps the grid to the end. split (grid peel with a tail): the tail runs as a
+// second, one-block launch, and `handed` (if not NULL) is recorded between the
+// two; ctl->tail_go then says whether the grid handed anything over, and snap
+// (n bytes, cleared by the caller) holds 1 for every vertex still present then.
 hipError_t mce_launch_peel(int n, const int* rp, const int* ci, int* deg, int* rnd, int* core, int* alive0,
                            int* alive1, int* front0, int* front1, int* bfront0, int* bfront1, MceCtl* ctl,
-                           u64 budget, unsigned short* tcol, long long tcap, int* tcrow, int blocks, hipStream_t s);
+                           u64 budget, unsigned short* tcol, long long tcap, int* tcrow, int blocks, int split,
+                           unsigned char* snap, hipEvent_t handed, hipStream_t s);
 int mce_peel_tail_rows();
 int mce_peel_max_blocks(int num_cu);
 // roots == NULL: the roots are 0 .. nroots-1. fwd == NULL: first-level roots,
@@ -207,13 +214,30 @@ int mce_peel_max_blocks(int num_cu);
 // the second-level roots are tallied by mce_launch_l2_roots.
 // Forward adjacency: fadj[rp[v] .. rp[v] + fdeg[v]) = the neighbours of v after
 // v in the peel order, in id order. flong: n ints of scratch (the long rows' list).
+// tctl, snap, hdeg (a split peel's control block, hand-over snapshot and the
+// degrees it handed over, its tail still running): the same for the vertices
+// that left before the tail, a vertex still in it ranking after all of them and
+// getting its neighbours in the tail that come after it by (degree, id)
+// (nothing if the grid handed no tail over); ctl then only holds the long rows'
+// count.
 hipError_t mce_launch_forward_adj(int n, const int* rp, const int* ci, const int* rnd, int* fadj, int* fdeg,
-                                  int* flong, MceCtl* ctl, int blocks, hipStream_t s);
+                                  int* flong, MceCtl* ctl, int blocks, hipStream_t s, const MceCtl* tctl = nullptr,
+                                  const unsigned char* snap = nullptr, const int* hdeg = nullptr);
 // fdeg: the forward adjacency's row lengths, when every vertex is a root of a
 // first-level run (roots == NULL, fwd == NULL): |P| is read from it.
+// skip_early (whole-graph first-level runs with fdeg): a split peel's early
+// roots (see mce_launch_orient_early) get pcount = xcount = 0 here.
 hipError_t mce_launch_orient(int n, const int* rp, const int* ci, const int* rnd, const int* roots, int nroots,
                              int* pcount, int* xcount, MceCtl* ctl, u64* fwd, const int* fdeg, int blocks,
-                             hipStream_t s);
+                             hipStream_t s, int skip_early = 0);
+// A split peel's early roots: the vertices gone before the tail (not in the
+// hand-over snapshot snap; tctl, the run's control block) with micro-sized subtrees, |P| from the early forward
+// adjacency's fdeg; |P| and |X| into pcount / xcount (n each, 0 for the other
+// vertices), tallied into ctl (a control block of their own, which also gets
+// tctl's tail_go and tail_r0).
+hipError_t mce_launch_orient_early(int n, const int* rp, const unsigned char* snap, const int* fdeg,
+                                   const MceCtl* tctl, int* pcount, int* xcount, MceCtl* ctl, int blocks,
+                                   hipStream_t s);
 // Second-level roots (Algorithm 4) of the vertex roots: COO sources (src, nnz),
 // the forward edges as CSR positions (eroots, at most nnz; their number goes to
 // ctl->l2_roots), and per root |P| and |X| (pcount, xcount) and the tallies.

@@ -483,6 +483,7 @@ struct PeelArgs {
   long long tcap;         // entries tcol holds; 0: no compaction, the grid peels to the end
   int* tcrow;             // row starts, PEEL_TT + 1
   u32* pool;              // block 0's LDS in the tail: packed degrees and frontier lists
+  unsigned char* snap;    // split peel (or NULL): 1 for every vertex still present at the hand-over
   // ping-pong buffers by parity (selects, not indexed arrays: no scratch memory)
   __device__ int* alive(int i) const { return (i & 1) ? alive1 : alive0; }
   __device__ int* front(int i) const { return (i & 1) ? front1 : front0; }
@@ -1176,6 +1177,7 @@ __device__ __forceinline__ int peel_tail_build(const PeelArgs& A, PeelState& st)
       sz = tail_budget(d, len);
       lg = len > PEEL_TLONG;
       pst<SA>(&A.rnd[v], -2 - i);
+      if (A.snap) A.snap[v] = 1;
     }
     long long incl = sz;
 #pragma unroll
@@ -1670,7 +1672,8 @@ __global__ __launch_bounds__(PEEL_THREADS) void k_peel(int n, const int* __restr
                                                         const int* __restrict__ ci, int* deg, int* rnd, int* core,
                                                         int* alive0, int* alive1, int* front0, int* front1,
                                                         int* bfront0, int* bfront1, MceCtl* ctl, u64 budget,
-                                                        unsigned short* tcol, long long tcap, int* tcrow) {
+                                                        unsigned short* tcol, long long tcap, int* tcrow,
+                                                        int split, unsigned char* snap) {
   __shared__ int s_cnt[12];
   __shared__ int4 s_fr[2 * PEEL_TINY + 1];
   // One LDS pool, used one of two ways in a launch:
@@ -1697,7 +1700,8 @@ __global__ __launch_bounds__(PEEL_THREADS) void k_peel(int n, const int* __restr
   }
   PeelArgs A{n,      rp,     ci,      lds ? s_deg : deg, lds ? s_rnd : rnd, core,        alive0,
              alive1, front0, front1,  bfront0,           bfront1,           pc,          t0 + budget,
-             s_cnt,  s_fr,   tcol,    gridDim.x > 1 ? tcap : 0LL,           tcrow,       s_pool};
+             s_cnt,  s_fr,   tcol,    gridDim.x > 1 ? tcap : 0LL,           tcrow,       s_pool,
+             split ? snap : nullptr};
   const int gtid = blockIdx.x * blockDim.x + threadIdx.x;
   const int gsize = gridDim.x * blockDim.x;
   const bool timer = blockIdx.x == 0 && threadIdx.x == 0;
@@ -1752,6 +1756,23 @@ __global__ __launch_bounds__(PEEL_THREADS) void k_peel(int n, const int* __restr
         res = peel_tail_build(A, st);
         if (blockIdx.x != 0) return;
         if (res == PEEL_TO_TAIL) {
+          if (split) {
+            // the tail is k_peel_tail's, a launch of its own: hand over the
+            // state (this launch's end makes all of its writes visible to the
+            // launches that follow it)
+            if (threadIdx.x == 0) {
+              ctl->tail_st[0] = st.k;
+              ctl->tail_st[1] = st.r;
+              ctl->tail_st[2] = st.na;
+              ctl->tail_st[3] = st.cur;
+              ctl->tail_ticks[0] = st.tb;
+              ctl->tail_ticks[1] = st.tl;
+              ctl->tail_ticks[2] = st.tr;
+              ctl->tail_r0 = st.r;
+              ctl->tail_go = 1;
+            }
+            return;
+          }
           fence_acquire_agent();
           res = peel_tail_rounds(A, st, timer);
         }
@@ -1776,6 +1797,46 @@ __global__ __launch_bounds__(PEEL_THREADS) void k_peel(int n, const int* __restr
     for (int v = threadIdx.x; v < n; v += blockDim.x) rnd[v] = s_rnd[v];
   }
   if (threadIdx.x == 0 && blockIdx.x == 0) {
+    ctl->rounds = st.r;
+    ctl->degeneracy = max(st.k, 0);
+    ctl->peel_ticks[0] = st.tb;
+    ctl->peel_ticks[1] = st.tl;
+    ctl->peel_ticks[2] = st.tr;
+    ctl->peel_ticks[3] = wall_clock64() - t0;
+  }
+}
+
+// The split peel's second launch: block 0's tail on the compacted residual
+// graph (peel_tail_rounds), from the state the grid handed over. It runs as an
+// ordinary one-block launch, so kernels on other streams can use the rest of
+// the chip meanwhile (the subtrees of the vertices that have left already).
+// Nothing to do when the grid peeled to the end or stopped.
+__global__ __launch_bounds__(PEEL_THREADS) void k_peel_tail(int n, const int* __restrict__ rp,
+                                                             const int* __restrict__ ci, int* deg, int* rnd,
+                                                             int* core, int* alive0, int* alive1, int* front0,
+                                                             int* front1, int* bfront0, int* bfront1, MceCtl* ctl,
+                                                             u64 budget, unsigned short* tcol, long long tcap,
+                                                             int* tcrow) {
+  __shared__ int s_cnt[12];
+  __shared__ int4 s_fr[2 * PEEL_TINY + 1];
+  __shared__ __align__(128) u32 s_pool[PEEL_TPOOL];
+  if (ctl->tail_go == 0) return;
+  const u64 t0 = ctl->t_run;
+  PeelArgs A{n,      rp,     ci,     deg,    rnd,   core, alive0, alive1, front0, front1,
+             bfront0, bfront1, ctl,  t0 + budget, s_cnt, s_fr, tcol,   tcap,   tcrow,  s_pool, nullptr};
+  const bool timer = threadIdx.x == 0;
+  PeelState st{0, 0, 0, -1, 0, 0, 0, 0, 0, 0, 0, false, 0u, 0u, 0, 0, 0, 0};
+  st.k = ctl->tail_st[0];
+  st.r = ctl->tail_st[1];
+  st.na = ctl->tail_st[2];
+  st.cur = ctl->tail_st[3];
+  st.tb = ctl->tail_ticks[0];
+  st.tl = ctl->tail_ticks[1];
+  st.tr = ctl->tail_ticks[2];
+  st.tm = wall_clock64();
+  const int res = peel_tail_rounds(A, st, timer);
+  if (res < 0) return;
+  if (threadIdx.x == 0) {
     ctl->rounds = st.r;
     ctl->degeneracy = max(st.k, 0);
     ctl->peel_ticks[0] = st.tb;
@@ -1878,10 +1939,14 @@ __device__ __forceinline__ void tally_roots(TallyAcc& acc, bool valid, int p, in
 __global__ __launch_bounds__(256) void k_orient(int n, const int* __restrict__ rp, const int* __restrict__ ci,
                                                  const int* __restrict__ rnd, const int* __restrict__ roots,
                                                  int nroots, int* pcount, int* xcount, MceCtl* ctl, u64* fwd,
-                                                 const int* __restrict__ fdeg, int tally, int per_wave, u32 mul) {
+                                                 const int* __restrict__ fdeg, int tally, int per_wave, u32 mul,
+                                                 int skip_early) {
   __shared__ TallyAcc s_tally;
   __shared__ int s_ok;
   if (!tally_begin(s_tally, &s_ok, ctl)) return;
+  // a split peel's early roots (left before the tail, micro-sized) are searched
+  // by their own launch: neither bucketed nor tallied here
+  const int r0 = skip_early && ctl->tail_go ? ctl->tail_r0 : -1;
   const int lane = lane_id();
   const int gsize = gridDim.x * blockDim.x;
   const int cnt = nroots;   // roots == NULL: the identity list 0..nroots-1
@@ -1980,8 +2045,9 @@ __global__ __launch_bounds__(256) void k_orient(int n, const int* __restrict__ r
       }
       if (inr) {
         x = (b - a) - p;
-        pcount[i] = p;
-        xcount[i] = x;
+        const bool early = rv < r0 && p >= 1 && mce_is_micro(p, x);
+        pcount[i] = early ? 0 : p;
+        xcount[i] = early ? 0 : x;
         if (fwd) fwd[i] = (u64)p;
         if (b == a) {
           iso++;
@@ -1991,7 +2057,7 @@ __global__ __launch_bounds__(256) void k_orient(int n, const int* __restrict__ r
         xmax = max(xmax, x);
         dmax = max(dmax, b - a);
         if (tally && p > MCE_MAX_P) lim |= 1u;
-        valid = p > 0 && p <= MCE_MAX_P;
+        valid = !early && p > 0 && p <= MCE_MAX_P;
       } else if (i < cnt && fwd) {
         fwd[i] = 0;
       }
@@ -2031,10 +2097,40 @@ __global__ __launch_bounds__(256) void k_orient(int n, const int* __restrict__ r
 // whole block that takes 1,024 entries at a time (a hub's row, tens of
 // thousands of entries on power-law graphs, kept one wavefront busy for
 // milliseconds).
+//
+// With tctl and snap (a split peel's control block and hand-over snapshot,
+// its tail still running): the forward rows of the vertices that left before
+// the tail, where every vertex still in the tail (snap 1; its round is not
+// read, as the tail writes it meanwhile) ranks after them, and, for a vertex
+// still in the tail, its neighbours in the tail that come after it by (degree
+// at the hand-over, id): every edge of the residual graph once, in the row of
+// its end of smaller degree, so that a hub's row stays short (the tail keeps
+// its degrees in LDS and leaves deg as it was handed over). Nothing is done
+// when the grid peeled to the end.
 #define FWD_LONG 1024
+#define FWD_TAIL 0x7FFFFFFF   // the rank of a vertex still in the tail
+
+__device__ __forceinline__ int fwd_rank(const int* rnd, const unsigned char* snap, int u) {
+  return snap && snap[u] ? FWD_TAIL : rnd[u];
+}
+
+// Is u after v? rv = fwd_rank(v), dv = v's degree at the hand-over if rv is FWD_TAIL.
+__device__ __forceinline__ bool fwd_later(const int* rnd, const unsigned char* snap, const int* deg, int u, int rv,
+                                          int dv, int v) {
+  const int ru = fwd_rank(rnd, snap, u);
+  if (ru == FWD_TAIL && rv == FWD_TAIL) {
+    const int du = deg[u];
+    return du > dv || (du == dv && u > v);
+  }
+  return order_after(ru, u, rv, v);
+}
+
 __global__ __launch_bounds__(256) void k_forward_adj(int n, const int* __restrict__ rp, const int* __restrict__ ci,
                                                       const int* __restrict__ rnd, int* __restrict__ fadj,
-                                                      int* __restrict__ fdeg, int* __restrict__ flong, MceCtl* ctl) {
+                                                      int* __restrict__ fdeg, int* __restrict__ flong, MceCtl* ctl,
+                                                      const MceCtl* tctl, const unsigned char* __restrict__ snap,
+                                                      const int* __restrict__ hdeg) {
+  if (tctl && !tctl->tail_go) return;
   // the block's long rows, listed in LDS and added to the list with one atomic
   // (one per row on the shared count took a 4M-vertex graph's ~20k hub rows
   // about 0.3 ms); a block with more than FWD_LCAP of them lists the rest
@@ -2047,7 +2143,8 @@ __global__ __launch_bounds__(256) void k_forward_adj(int n, const int* __restric
   const int lane = lane_id();
   const int nwaves = gridDim.x * (blockDim.x / MCE_WAVE);
   for (int v = blockIdx.x * (blockDim.x / MCE_WAVE) + threadIdx.x / MCE_WAVE; v < n; v += nwaves) {
-    const int a = rp[v], b = rp[v + 1], rv = rnd[v];
+    const int a = rp[v], b = rp[v + 1], rv = fwd_rank(rnd, snap, v);
+    const int dv = rv == FWD_TAIL ? hdeg[v] : 0;
     if (b - a > FWD_LONG) {
       if (lane == 0) {
         const int q = atomicAdd(&s_nl, 1);
@@ -2060,7 +2157,7 @@ __global__ __launch_bounds__(256) void k_forward_adj(int n, const int* __restric
     for (int base = a; base < b; base += MCE_WAVE) {
       const int e = base + lane;
       const int u = e < b ? ci[e] : 0;
-      const bool later = e < b && order_after(rnd[u], u, rv, v);
+      const bool later = e < b && fwd_later(rnd, snap, hdeg, u, rv, dv, v);
       const u64 m = ballot(later);
       if (later) fadj[a + k + mbcnt(m)] = u;
       k += __popcll(m);
@@ -2081,14 +2178,18 @@ __global__ __launch_bounds__(256) void k_forward_adj(int n, const int* __restric
 __global__ __launch_bounds__(256) void k_forward_adj_long(const int* __restrict__ rp, const int* __restrict__ ci,
                                                            const int* __restrict__ rnd, int* __restrict__ fadj,
                                                            int* __restrict__ fdeg, const int* __restrict__ flong,
-                                                           MceCtl* ctl) {
+                                                           MceCtl* ctl, const MceCtl* tctl,
+                                                           const unsigned char* __restrict__ snap,
+                                                           const int* __restrict__ hdeg) {
   constexpr int NW = 256 / MCE_WAVE;
   __shared__ int s_cnt[4][NW];
+  if (tctl && !tctl->tail_go) return;
   const int lane = lane_id(), wv = threadIdx.x / MCE_WAVE;
   const int nl = ld_relaxed(&ctl->nlong);
   for (int j = blockIdx.x; j < nl; j += gridDim.x) {
     const int v = flong[j];
-    const int a = rp[v], b = rp[v + 1], rv = rnd[v];
+    const int a = rp[v], b = rp[v + 1], rv = fwd_rank(rnd, snap, v);
+    const int dv = rv == FWD_TAIL ? hdeg[v] : 0;
     int k = 0;   // entries placed so far (the same in every thread)
     for (int base = a; base < b; base += 4 * 256) {
       int u[4];
@@ -2102,7 +2203,7 @@ __global__ __launch_bounds__(256) void k_forward_adj_long(const int* __restrict_
 #pragma unroll
       for (int z = 0; z < 4; z++) {
         const int e = base + z * 256 + (int)threadIdx.x;
-        lat[z] = e < b && order_after(rnd[u[z]], u[z], rv, v);
+        lat[z] = e < b && fwd_later(rnd, snap, hdeg, u[z], rv, dv, v);
       }
 #pragma unroll
       for (int z = 0; z < 4; z++) {
@@ -2140,6 +2241,46 @@ __global__ __launch_bounds__(256) void k_tally(int nroots, const int* __restrict
     const int i = base + threadIdx.x;
     const int p = i < nroots ? pcount[i] : 0, x = i < nroots ? xcount[i] : 0;
     tally_roots(s_tally, p > 0 && p <= MCE_MAX_P, p, x);
+  }
+  tally_end(s_tally, ctl);
+}
+
+// A split peel's early roots: the vertices that left before the tail, whose
+// later neighbours are already known (every vertex still in the tail is later),
+// with micro-sized subtrees (|P| = fdeg from the early forward adjacency). Their
+// |P| and |X| go to pcount / xcount (0 for every other vertex) and they are
+// tallied into `ctl` (a control block of their own); the grid's hand-over
+// fields are copied there for the host. A vertex is early when the hand-over
+// snapshot does not hold it (no round is read: the tail writes its vertices'
+// meanwhile).
+__global__ __launch_bounds__(256) void k_orient_early(int n, const int* __restrict__ rp,
+                                                      const unsigned char* __restrict__ snap,
+                                                      const int* __restrict__ fdeg, const MceCtl* tctl,
+                                                      int* pcount, int* xcount, MceCtl* ctl) {
+  __shared__ TallyAcc s_tally;
+  __shared__ int s_ok;
+  if (!tally_begin(s_tally, &s_ok, ctl)) return;
+  const int go = tctl->tail_go;
+  const int r0 = go ? tctl->tail_r0 : -1;
+  if (blockIdx.x == 0 && threadIdx.x == 0) {
+    ctl->tail_go = go;
+    ctl->tail_r0 = r0;
+  }
+  const int gsize = gridDim.x * blockDim.x;
+  for (int base = blockIdx.x * blockDim.x; base < n; base += gsize) {
+    const int v = base + threadIdx.x;
+    int p = 0, x = 0;
+    bool take = false;
+    if (v < n && r0 >= 0 && !snap[v]) {
+      p = fdeg[v];
+      x = (rp[v + 1] - rp[v]) - p;
+      take = p >= 1 && mce_is_micro(p, x);
+    }
+    if (v < n) {
+      pcount[v] = take ? p : 0;
+      xcount[v] = take ? x : 0;
+    }
+    tally_roots(s_tally, take, p, x);
   }
   tally_end(s_tally, ctl);
 }
@@ -2237,14 +2378,21 @@ hipError_t mce_launch_validate(int n, long long nnz, const int* rp, const int* c
 
 hipError_t mce_launch_peel(int n, const int* rp, const int* ci, int* deg, int* rnd, int* core, int* alive0,
                            int* alive1, int* front0, int* front1, int* bfront0, int* bfront1, MceCtl* ctl,
-                           u64 budget, unsigned short* tcol, long long tcap, int* tcrow, int blocks, hipStream_t s) {
+                           u64 budget, unsigned short* tcol, long long tcap, int* tcrow, int blocks, int split,
+                           unsigned char* snap, hipEvent_t handed, hipStream_t s) {
   if (!tcol || !tcrow) tcap = 0;
   tcap = tcap < 0 ? 0 : (tcap > 0x7FFFFFFFll ? 0x7FFFFFFFll : tcap);   // row offsets are int
-  void* args[] = {&n,      (void*)&rp, (void*)&ci, &deg, &rnd,    &core, &alive0, &alive1, &front0,
-                  &front1, &bfront0,   &bfront1,   &ctl, &budget, &tcol, &tcap,   &tcrow};
+  if (blocks == 1 || tcap == 0 || !snap) split = 0;
+  void* args[] = {&n,      (void*)&rp, (void*)&ci, &deg,    &rnd,  &core, &alive0, &alive1, &front0, &front1,
+                  &bfront0, &bfront1,  &ctl,       &budget, &tcol, &tcap, &tcrow,  &split,  &snap};
   // one block needs no grid barrier, hence no cooperative launch
   if (blocks == 1) return hipLaunchKernel((const void*)k_peel, dim3(1), dim3(PEEL_THREADS), args, 0, s);
-  return hipLaunchCooperativeKernel((const void*)k_peel, dim3(blocks), dim3(PEEL_THREADS), args, 0, s);
+  hipError_t e = hipLaunchCooperativeKernel((const void*)k_peel, dim3(blocks), dim3(PEEL_THREADS), args, 0, s);
+  if (e != hipSuccess || !split) return e;
+  if (handed && (e = hipEventRecord(handed, s)) != hipSuccess) return e;
+  hipLaunchKernelGGL(k_peel_tail, dim3(1), dim3(PEEL_THREADS), 0, s, n, rp, ci, deg, rnd, core, alive0, alive1,
+                     front0, front1, bfront0, bfront1, ctl, budget, tcol, tcap, tcrow);
+  return hipGetLastError();
 }
 
 // The peel's grid barrier needs every block resident: one block per CU, well
@@ -2467,9 +2615,18 @@ hipError_t mce_launch_l2_roots(int n, long long nnz, const int* rp, const int* c
   return hipGetLastError();
 }
 
+hipError_t mce_launch_orient_early(int n, const int* rp, const unsigned char* snap, const int* fdeg,
+                                   const MceCtl* tctl, int* pcount, int* xcount, MceCtl* ctl, int blocks,
+                                   hipStream_t s) {
+  const int nb = max(1, min(max(1, blocks / 8), (n + 255) / 256));
+  hipLaunchKernelGGL(k_orient_early, dim3(nb), dim3(256), 0, s, n, rp, snap, fdeg, tctl, pcount, xcount, ctl);
+  return hipGetLastError();
+}
+
 hipError_t mce_launch_orient(int n, const int* rp, const int* ci, const int* rnd, const int* roots, int nroots,
                              int* pcount, int* xcount, MceCtl* ctl, u64* fwd, const int* fdeg, int blocks,
-                             hipStream_t s) {
+                             hipStream_t s, int skip_early) {
+  if (skip_early && !fdeg) return hipErrorInvalidValue;
   if (fdeg && (roots || fwd || nroots != n)) return hipErrorInvalidValue;   // every vertex a root, first level
   // at most one root per wavefront of the grid: a wavefront per root, on at most
   // 256 wavefronts (every wavefront ends with a few atomics on the same words:
@@ -2481,7 +2638,7 @@ hipError_t mce_launch_orient(int n, const int* rp, const int* ci, const int* rnd
   const int tb = fdeg ? max(1, blocks / 8) : blocks;
   const int nb = per_wave ? max(1, min(64, (nroots + 3) / 4)) : max(1, min(tb, (nroots + 255) / 256));
   hipLaunchKernelGGL(k_orient, dim3(nb), dim3(256), 0, s, n, rp, ci, rnd, roots, nroots, pcount, xcount, ctl, fwd,
-                     fdeg, fwd ? 0 : 1, per_wave, ORIENT_MUL);
+                     fdeg, fwd ? 0 : 1, per_wave, ORIENT_MUL, skip_early);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || !per_wave || fwd) return e;
   hipLaunchKernelGGL(k_tally, dim3(max(1, min(blocks, (nroots + 255) / 256))), dim3(256), 0, s, nroots, pcount,
@@ -2490,12 +2647,16 @@ hipError_t mce_launch_orient(int n, const int* rp, const int* ci, const int* rnd
 }
 
 hipError_t mce_launch_forward_adj(int n, const int* rp, const int* ci, const int* rnd, int* fadj, int* fdeg,
-                                  int* flong, MceCtl* ctl, int blocks, hipStream_t s) {
+                                  int* flong, MceCtl* ctl, int blocks, hipStream_t s, const MceCtl* tctl,
+                                  const unsigned char* snap, const int* hdeg) {
+  if (!tctl != !snap || !tctl != !hdeg) return hipErrorInvalidValue;
   const int nb = max(1, min(blocks, (n + 3) / 4));   // four wavefronts a block, one vertex each at a time
-  hipLaunchKernelGGL(k_forward_adj, dim3(nb), dim3(256), 0, s, n, rp, ci, rnd, fadj, fdeg, flong, ctl);
+  hipLaunchKernelGGL(k_forward_adj, dim3(nb), dim3(256), 0, s, n, rp, ci, rnd, fadj, fdeg, flong, ctl, tctl, snap,
+                     hdeg);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_forward_adj_long, dim3(max(1, blocks)), dim3(256), 0, s, rp, ci, rnd, fadj, fdeg, flong, ctl);
+  hipLaunchKernelGGL(k_forward_adj_long, dim3(max(1, blocks)), dim3(256), 0, s, rp, ci, rnd, fadj, fdeg, flong, ctl,
+                     tctl, snap, hdeg);
   return hipGetLastError();
 }
 

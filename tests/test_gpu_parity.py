@@ -174,6 +174,31 @@ def test_ordering_matches_oracle(eng, make):
     assert info["max_degree"] == int(g.degrees().max())
 
 
+# ------------------------------------------------------------------ split peel
+def test_split_peel_early_launch():
+    """More vertices than the peel's tail takes: the grid hands the tail to a
+    one-block launch, and the micro-sized roots gone before it are built and
+    searched meanwhile on the early stream. The cliques, the order and the
+    micro roots match the oracle and a serial run (no split), run after run."""
+    g = mi.chung_lu(200000, 20.0, 2.3, None, 11, planted=50)
+    rp, ci = on_gpu(g)
+    print(f"case {g.name} n={g.n} m={g.m}, split peel", flush=True)
+    want = oracle.mce(g.n, g.row_ptr, g.col_idx)
+    ocore, ornd, d = oracle.peel(g.n, g.row_ptr, g.col_idx)
+    with mce.Engine(device=0, timeout_ms=60000) as eo, \
+            mce.Engine(device=0, timeout_ms=60000, overlap=False) as es:
+        for _ in range(2):
+            for e in (eo, es):
+                got = e.run(rp, ci)
+                assert (got.count, got.hist, got.hash) == (want.count, want.hist, want.hash)
+                core, rnd = e.ordering(g.n)
+                assert np.array_equal(core.cpu().numpy(), ocore) and np.array_equal(rnd.cpu().numpy(), ornd)
+                assert e.graph_info()["roots_started"] == g.n
+        so, ss = eo.stats(), es.stats()
+        assert so["launches"] == ss["launches"] + 1 and so["launch_sub"][0] == 12
+        assert 0 < so["launch_roots"][0] < so["micro_roots"] == ss["micro_roots"]
+
+
 # ------------------------------------------------------------------ root subsets
 def test_root_subsets(eng):
     g = mi.chung_lu(20000, 12.0, 2.3, None, 5, planted=20, planted_min=8, planted_max=25)

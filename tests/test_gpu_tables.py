@@ -29,6 +29,9 @@ GRAPHS = {
     "hub_clique": lambda: mi.hub_clique(700, 4, 3000, 0.7, 12, 700),
     "hub_clique_110": lambda: mi.hub_clique(110, 4, 3000, 0.7, 12, 110),
     "hub_clique_1100": lambda: mi.hub_clique(1100, 4, 3000, 0.7, 12, 1100),
+    # more vertices than the peel's tail takes: the roots gone before the tail
+    # get their micro tables from the early launch (built while the tail runs)
+    "chung_lu_100k": lambda: mi.chung_lu(100000, 12.0, 2.3, None, 3, planted=40, planted_min=10, planted_max=30),
 }
 
 
