@@ -250,6 +250,17 @@ constexpr int kW1WavesPerCu = MCE_W1_WAVES_PER_CU;
 // Tables other than micro ones are built by the split build: a root's rows are
 // dealt over several blocks, about this many (root, part) blocks per CU.
 constexpr int kSplitBlocksPerCu = 16;
+#ifndef MCE_WIDE_WAVES_PER_CU
+#define MCE_WIDE_WAVES_PER_CU 14
+#endif
+// Wider launches beside other launches keep at most this many wavefronts per
+// CU. A search launch is persistent: its waves hold their compute units until
+// the launch's work is done, so a launch queued on another side stream that
+// finds no room waits for it. The 500k Chung-Lu graph's width-2 launch filled
+// 17 waves per CU (its LDS limit) and the width-1 chains ran after it (19.7 ms a
+// step); capped at 10 / 12 / 13 / 14 / 15 / 16 waves: 19.2 / 18.6 / 18.4 /
+// 18.2 / 18.7 / 19.5 ms.
+constexpr int kWideWavesPerCu = MCE_WIDE_WAVES_PER_CU;
 // the split peel's early launch records its subtrees taken here (MceCtl::taken)
 constexpr int kTakenEarly = 2 * MCE_NCLASS + 1;
 
@@ -640,6 +651,8 @@ mce_status run_once(mce_engine* e, int32_t n, int64_t nnz, const int32_t* row_pt
   int micro_nw = 0;
   int stat_rows = 0;
   const bool counters = (e->cfg.flags & MCE_FLAG_COUNTERS) != 0;
+  int busy_subs = 0;   // sub-classes with roots: their launches
+  for (int c = 0; c < MCE_NSUB; c++) busy_subs += counts[c] > 0 ? 1 : 0;
   for (int c = MCE_NSUB - 1; c >= 0; c--) {
     if (counts[c] == 0) continue;
     Plan pl{};
@@ -659,6 +672,8 @@ mce_status run_once(mce_engine* e, int32_t n, int64_t nnz, const int32_t* row_pt
     }
     if (nw <= 0) return fail(e, MCE_ERR_DEVICE, "search kernel occupancy query failed");
     if (c != MCE_SUB_MICRO && (c >> 1) == 0) nw = std::min(nw, kW1WavesPerCu * e->num_cu);
+    if (kWideWavesPerCu > 0 && overlap && busy_subs + (n1 > 0 ? 1 : 0) > 1 && c != MCE_SUB_MICRO && (c >> 1) > 0)
+      nw = std::min(nw, kWideWavesPerCu * e->num_cu);
     if (e->cfg.max_workers > 0) nw = std::min(nw, (int)e->cfg.max_workers);
     if (!e->cfg.worker_list) nw = std::min(nw, counts[c]);
     pl.nw = nw;
