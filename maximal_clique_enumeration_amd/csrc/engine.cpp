@@ -80,11 +80,9 @@ struct mce_engine {
   hipStream_t side[MCE_SIDE_STREAMS] = {};
   hipEvent_t fork_ev = nullptr;
   hipEvent_t join_ev[MCE_SIDE_STREAMS] = {};
-  // the early launch of a split peel: its own stream, which starts at the
-  // grid's hand-over (handed_ev) and is joined back (early_join_ev); its
-  // control block is read back through host1
-  hipStream_t early = nullptr;
-  hipEvent_t handed_ev = nullptr, early_join_ev = nullptr;
+  // the early launch of a split peel runs on side stream 0 from the grid's
+  // hand-over (handed_ev); its control block is read back through host1
+  hipEvent_t handed_ev = nullptr;
   HostPinned host1;
 
   // last run
@@ -261,6 +259,7 @@ constexpr int kSplitBlocksPerCu = 16;
 // step); capped at 10 / 12 / 13 / 14 / 15 / 16 waves: 19.2 / 18.6 / 18.4 /
 // 18.2 / 18.7 / 19.5 ms.
 constexpr int kWideWavesPerCu = MCE_WIDE_WAVES_PER_CU;
+
 // the split peel's early launch records its subtrees taken here (MceCtl::taken)
 constexpr int kTakenEarly = 2 * MCE_NCLASS + 1;
 
@@ -484,6 +483,10 @@ mce_status run_once(mce_engine* e, int32_t n, int64_t nnz, const int32_t* row_pt
   } early_guard;
   int n1 = 0, early_nw = 0;
   u64 words1 = 0;
+  // the early stream: side stream 0, whose later launches come after it (with
+  // a stream of its own, it shared a hardware queue with the stream of the
+  // longest chain, which then waited for it: 18.0 against 18.3 ms a step)
+  hipStream_t es = e->side[0];
   if (split) {
     if ((h = ensure(B.fadj1, (size_t)std::max<int64_t>(nnz, 1) * sizeof(int))) != hipSuccess ||
         (h = ensure(B.fdeg1, (size_t)n * sizeof(int))) != hipSuccess ||
@@ -492,16 +495,16 @@ mce_status run_once(mce_engine* e, int32_t n, int64_t nnz, const int32_t* row_pt
         (h = ensure(B.xcount1, (size_t)n * sizeof(int))) != hipSuccess ||
         (h = ensure_host(e->host1, sizeof(MceCtl))) != hipSuccess)
       return hip_fail(e, h, "allocation");
-    early_guard.st = e->early;
+    early_guard.st = es;
     MceCtl* h1 = static_cast<MceCtl*>(e->host1.p);
-    if ((h = hipStreamWaitEvent(e->early, e->handed_ev, 0)) != hipSuccess ||
+    if ((h = hipStreamWaitEvent(es, e->handed_ev, 0)) != hipSuccess ||
         (h = mce_launch_forward_adj(n, row_ptr, col_idx, dp<int>(B.rnd), dp<int>(B.fadj1), dp<int>(B.fdeg1),
-                                    dp<int>(B.flong1), ctl1, e->num_cu * 16, e->early, ctl,
+                                    dp<int>(B.flong1), ctl1, e->num_cu * 16, es, ctl,
                                     dp<unsigned char>(B.snap), dp<int>(B.deg))) != hipSuccess ||
         (h = mce_launch_orient_early(n, row_ptr, dp<unsigned char>(B.snap), dp<int>(B.fdeg1), ctl,
-                                     dp<int>(B.pcount1), dp<int>(B.xcount1), ctl1, grid, e->early)) != hipSuccess ||
-        (h = hipMemcpyAsync(h1, ctl1, sizeof(MceCtl), hipMemcpyDeviceToHost, e->early)) != hipSuccess ||
-        (h = hipStreamSynchronize(e->early)) != hipSuccess)
+                                     dp<int>(B.pcount1), dp<int>(B.xcount1), ctl1, grid, es)) != hipSuccess ||
+        (h = hipMemcpyAsync(h1, ctl1, sizeof(MceCtl), hipMemcpyDeviceToHost, es)) != hipSuccess ||
+        (h = hipStreamSynchronize(es)) != hipSuccess)
       return hip_fail(e, h, "early orientation");
     if (h1->status) return fail(e, MCE_ERR_DEVICE, "early orientation failed");
     if (h1->tail_go) {
@@ -528,9 +531,9 @@ mce_status run_once(mce_engine* e, int32_t n, int64_t nnz, const int32_t* row_pt
       SubOffsets off1{};
       MceWl* wl1 = dp<MceWl>(B.wl) + MCE_NSUB;
       if ((h = mce_launch_bucket(nullptr, n, dp<int>(B.pcount1), dp<int>(B.xcount1), MCE_MODE_IPX, 1, off1,
-                                 dp<int>(B.lists1), dp<u64>(B.taboff1), ctl1, grid, e->early)) != hipSuccess ||
-          (h = mce_launch_scan(dp<u64>(B.taboff1), n1, dp<u64>(B.scan1), e->early)) != hipSuccess ||
-          (h = mce_launch_wl_init(wl1, early_nw, dp<u64>(B.stats1), e->early)) != hipSuccess)
+                                 dp<int>(B.lists1), dp<u64>(B.taboff1), ctl1, grid, es)) != hipSuccess ||
+          (h = mce_launch_scan(dp<u64>(B.taboff1), n1, dp<u64>(B.scan1), es)) != hipSuccess ||
+          (h = mce_launch_wl_init(wl1, early_nw, dp<u64>(B.stats1), es)) != hipSuccess)
         return hip_fail(e, h, "early launch");
       BuildParams bp{};
       bp.rp = row_ptr;
@@ -548,9 +551,9 @@ mce_status run_once(mce_engine* e, int32_t n, int64_t nnz, const int32_t* row_pt
       bp.fadj = dp<int>(B.fadj1);
       bp.fdeg = dp<int>(B.fdeg1);
       bp.snap = dp<unsigned char>(B.snap);
-      if (timing) (void)hipEventRecord(e->ev[4], e->early);
-      if ((h = mce_launch_build(bp, e->num_cu * 32, e->early)) != hipSuccess) return hip_fail(e, h, "early build");
-      if (timing) (void)hipEventRecord(e->ev[5], e->early);
+      if (timing) (void)hipEventRecord(e->ev[4], es);
+      if ((h = mce_launch_build(bp, e->num_cu * 32, es)) != hipSuccess) return hip_fail(e, h, "early build");
+      if (timing) (void)hipEventRecord(e->ev[5], es);
       MicroParams mp{};
       mp.heap = dp<u64>(B.heap1);
       mp.tab_off = dp<u64>(B.taboff1);
@@ -571,10 +574,9 @@ mce_status run_once(mce_engine* e, int32_t n, int64_t nnz, const int32_t* row_pt
       mp.status = &ctl->status;
       mp.stats = dp<u64>(B.stats1);
       mp.taken = &ctl->taken[kTakenEarly];
-      if (stimes) (void)hipEventRecord(e->ev[6], e->early);
-      if ((h = mce_launch_micro(counters_on, mp, e->early)) != hipSuccess) return hip_fail(e, h, "early search");
-      if (stimes) (void)hipEventRecord(e->ev[7], e->early);
-      if ((h = hipEventRecord(e->early_join_ev, e->early)) != hipSuccess) return hip_fail(e, h, "early join");
+      if (stimes) (void)hipEventRecord(e->ev[6], es);
+      if ((h = mce_launch_micro(counters_on, mp, es)) != hipSuccess) return hip_fail(e, h, "early search");
+      if (stimes) (void)hipEventRecord(e->ev[7], es);
     }
   }
   if ((h = hipStreamSynchronize(s)) != hipSuccess) return hip_fail(e, h, "synchronize after orient");
@@ -741,6 +743,25 @@ mce_status run_once(mce_engine* e, int32_t n, int64_t nnz, const int32_t* row_pt
   // stream pi mod MCE_SIDE_STREAMS, after everything queued on s so far, and s
   // waits for every side stream used before the read-back.
   bool side_used[MCE_SIDE_STREAMS] = {};
+  bool side_forked[MCE_SIDE_STREAMS] = {};
+  // with the early launch on side stream 0: the launch with the most table
+  // words (the longest chain) gets side stream 1 to itself, and the others
+  // take streams 2 and 0 in turn (three side streams, so that with the
+  // caller's stream no two share a hardware queue)
+  const bool early_side = n1 > 0;
+  if (early_side) side_used[0] = true;
+  int heavy = -1;
+  if (early_side) {
+    u64 best = 0;
+    for (int i = 0; i < nplan; i++) {
+      const u64 w = hctl->sub_words[var][plan[i].sub];
+      if (plan[i].sub != MCE_SUB_MICRO && w >= best) {
+        best = w;
+        heavy = i;
+      }
+    }
+  }
+  int next_other = 0;
   auto launch_fail = [&](hipError_t herr, const char* what) {
     if (overlap)   // leave no launch of this run behind on a side stream
       for (int k = 0; k < MCE_SIDE_STREAMS; k++)
@@ -768,10 +789,12 @@ mce_status run_once(mce_engine* e, int32_t n, int64_t nnz, const int32_t* row_pt
     const SearchLayout& L = pl.L;
     hipStream_t ls = s;
     if (overlap) {
-      const int k = pi % MCE_SIDE_STREAMS;
+      int k = pi % MCE_SIDE_STREAMS;
+      if (early_side) k = pi == heavy ? 1 : ((next_other++ & 1) == 0 ? 2 : 0);
       ls = e->side[k];
-      if (!side_used[k]) {
+      if (!side_forked[k]) {
         if ((h = hipStreamWaitEvent(ls, e->fork_ev, 0)) != hipSuccess) return launch_fail(h, "fork");
+        side_forked[k] = true;
         side_used[k] = true;
       }
     }
@@ -893,7 +916,6 @@ mce_status run_once(mce_engine* e, int32_t n, int64_t nnz, const int32_t* row_pt
         return launch_fail(h, "join");
     }
   }
-  if (n1 > 0 && (h = hipStreamWaitEvent(s, e->early_join_ev, 0)) != hipSuccess) return launch_fail(h, "early join");
   // results: one read-back of the control block and the result words
   if ((h = hipMemcpyAsync(hio, ctl, kIoBytes, hipMemcpyDeviceToHost, s)) != hipSuccess)
     return hip_fail(e, h, "result readback");
@@ -1187,9 +1209,7 @@ mce_status mce_create(const mce_config* cfg, mce_engine** out) {
     side_ok = side_ok && hipStreamCreateWithFlags(&e->side[k], hipStreamNonBlocking) == hipSuccess;
     side_ok = side_ok && hipEventCreateWithFlags(&e->join_ev[k], hipEventDisableTiming) == hipSuccess;
   }
-  side_ok = side_ok && hipStreamCreateWithFlags(&e->early, hipStreamNonBlocking) == hipSuccess &&
-            hipEventCreateWithFlags(&e->handed_ev, hipEventDisableTiming) == hipSuccess &&
-            hipEventCreateWithFlags(&e->early_join_ev, hipEventDisableTiming) == hipSuccess;
+  side_ok = side_ok && hipEventCreateWithFlags(&e->handed_ev, hipEventDisableTiming) == hipSuccess;
   if (!side_ok) {
     mce_destroy(e);
     return MCE_ERR_DEVICE;
@@ -1400,10 +1420,8 @@ void mce_destroy(mce_engine* e) {
     if (ev) (void)hipEventDestroy(ev);
   if (e->fork_ev) (void)hipEventDestroy(e->fork_ev);
   if (e->handed_ev) (void)hipEventDestroy(e->handed_ev);
-  if (e->early_join_ev) (void)hipEventDestroy(e->early_join_ev);
   for (auto& st : e->side)
     if (st) (void)hipStreamDestroy(st);
-  if (e->early) (void)hipStreamDestroy(e->early);
   delete e;
 }
 
