@@ -83,6 +83,7 @@ struct mce_engine {
   // the early launch of a split peel runs on side stream 0 from the grid's
   // hand-over (handed_ev); its control block is read back through host1
   hipEvent_t handed_ev = nullptr;
+  hipEvent_t early_built_ev = nullptr;   // the early build has read the early forward rows
   HostPinned host1;
 
   // last run
@@ -454,22 +455,45 @@ mce_status run_once(mce_engine* e, int32_t n, int64_t nnz, const int32_t* row_pt
        (h = take(arena, B.fdeg, (size_t)n * sizeof(int))) != hipSuccess ||
        (h = take(arena, B.flong, (size_t)n * sizeof(int))) != hipSuccess))
     return alloc_fail(e, arena, h, "forward adjacency");
-  if (early_fadj && (h = mce_launch_forward_adj(n, row_ptr, col_idx, dp<int>(B.rnd), dp<int>(B.fadj),
-                                                dp<int>(B.fdeg), dp<int>(B.flong), ctl, e->num_cu * 16, s)) != hipSuccess)
-    return hip_fail(e, h, "forward adjacency launch");
-  if ((h = mce_launch_orient(n, row_ptr, col_idx, dp<int>(B.rnd), subset ? roots : nullptr, cnt,
-                             dp<int>(B.pcount), dp<int>(B.xcount), ctl, l2 ? dp<u64>(B.fwd) : nullptr,
-                             early_fadj ? dp<int>(B.fdeg) : nullptr, grid, s, split ? 1 : 0)) != hipSuccess)
-    return hip_fail(e, h, "orient launch");
-  if (l2 && (h = mce_launch_l2_roots(n, nnz, row_ptr, col_idx, dp<int>(B.rnd), subset ? roots : nullptr, cnt,
-                                     dp<u64>(B.fwd), dp<u64>(B.fwdtmp), dp<int>(B.src), dp<int>(B.eroots),
-                                     dp<int>(B.pcount2), dp<int>(B.xcount2), dp<int>(B.hub_id),
-                                     dp<int>(B.hub_v), dp<u64>(B.hub_bm), maxhubs, ctl, grid, s)) != hipSuccess)
-    return hip_fail(e, h, "second-level roots launch");
+  // The steps after the peel on s (forward adjacency, orientation, read-back).
+  // With a split peel they are queued after the early launch (below): the final
+  // rows of the tail's vertices go over their early rows, once the early build
+  // has read them; every other vertex's early row is its final one.
+  bool fadj_in1 = false;   // the run's forward adjacency is the early one, its tail rows made final
   char* hio = stat ? reinterpret_cast<char*>(e->host_io) : static_cast<char*>(e->host.p);
   MceCtl* hctl = reinterpret_cast<MceCtl*>(hio);
-  if ((h = hipMemcpyAsync(hctl, ctl, sizeof(MceCtl), hipMemcpyDeviceToHost, s)) != hipSuccess)
-    return hip_fail(e, h, "readback");
+  auto post_peel = [&](bool tail_rows) -> mce_status {
+    if (early_fadj) {
+      if (tail_rows) {
+        fadj_in1 = true;
+        if ((h = hipStreamWaitEvent(s, e->early_built_ev, 0)) != hipSuccess) return hip_fail(e, h, "early build wait");
+        h = mce_launch_forward_adj(n, row_ptr, col_idx, dp<int>(B.rnd), dp<int>(B.fadj1), dp<int>(B.fdeg1),
+                                   dp<int>(B.flong), ctl, e->num_cu * 16, s, nullptr, dp<unsigned char>(B.snap),
+                                   nullptr, 1);
+      } else {
+        h = mce_launch_forward_adj(n, row_ptr, col_idx, dp<int>(B.rnd), dp<int>(B.fadj), dp<int>(B.fdeg),
+                                   dp<int>(B.flong), ctl, e->num_cu * 16, s);
+      }
+      if (h != hipSuccess) return hip_fail(e, h, "forward adjacency launch");
+    }
+    if ((h = mce_launch_orient(n, row_ptr, col_idx, dp<int>(B.rnd), subset ? roots : nullptr, cnt,
+                               dp<int>(B.pcount), dp<int>(B.xcount), ctl, l2 ? dp<u64>(B.fwd) : nullptr,
+                               early_fadj ? dp<int>(fadj_in1 ? B.fdeg1 : B.fdeg) : nullptr, grid, s,
+                               split ? 1 : 0)) != hipSuccess)
+      return hip_fail(e, h, "orient launch");
+    if (l2 && (h = mce_launch_l2_roots(n, nnz, row_ptr, col_idx, dp<int>(B.rnd), subset ? roots : nullptr, cnt,
+                                       dp<u64>(B.fwd), dp<u64>(B.fwdtmp), dp<int>(B.src), dp<int>(B.eroots),
+                                       dp<int>(B.pcount2), dp<int>(B.xcount2), dp<int>(B.hub_id),
+                                       dp<int>(B.hub_v), dp<u64>(B.hub_bm), maxhubs, ctl, grid, s)) != hipSuccess)
+      return hip_fail(e, h, "second-level roots launch");
+    if ((h = hipMemcpyAsync(hctl, ctl, sizeof(MceCtl), hipMemcpyDeviceToHost, s)) != hipSuccess)
+      return hip_fail(e, h, "readback");
+    return MCE_OK;
+  };
+  if (!split) {
+    const mce_status ps = post_peel(false);
+    if (ps != MCE_OK) return ps;
+  }
 
   // The early launch, on its own stream from the grid's hand-over (while the
   // tail and the steps above run on s): the early forward adjacency, the early
@@ -507,6 +531,11 @@ mce_status run_once(mce_engine* e, int32_t n, int64_t nnz, const int32_t* row_pt
         (h = hipStreamSynchronize(es)) != hipSuccess)
       return hip_fail(e, h, "early orientation");
     if (h1->status) return fail(e, MCE_ERR_DEVICE, "early orientation failed");
+    // (nothing of the early launch reads the early rows after this point unless
+    // its build is queued below; the event then follows the build)
+    if (!h1->tail_go || h1->sub_count[0][MCE_SUB_MICRO] == 0) {
+      if ((h = hipEventRecord(e->early_built_ev, es)) != hipSuccess) return hip_fail(e, h, "early build event");
+    }
     if (h1->tail_go) {
       n1 = h1->sub_count[0][MCE_SUB_MICRO];
       words1 = h1->sub_words[0][MCE_SUB_MICRO];
@@ -553,6 +582,7 @@ mce_status run_once(mce_engine* e, int32_t n, int64_t nnz, const int32_t* row_pt
       bp.snap = dp<unsigned char>(B.snap);
       if (timing) (void)hipEventRecord(e->ev[4], es);
       if ((h = mce_launch_build(bp, e->num_cu * 32, es)) != hipSuccess) return hip_fail(e, h, "early build");
+      if ((h = hipEventRecord(e->early_built_ev, es)) != hipSuccess) return hip_fail(e, h, "early build event");
       if (timing) (void)hipEventRecord(e->ev[5], es);
       MicroParams mp{};
       mp.heap = dp<u64>(B.heap1);
@@ -578,6 +608,10 @@ mce_status run_once(mce_engine* e, int32_t n, int64_t nnz, const int32_t* row_pt
       if ((h = mce_launch_micro(counters_on, mp, es)) != hipSuccess) return hip_fail(e, h, "early search");
       if (stimes) (void)hipEventRecord(e->ev[7], es);
     }
+  }
+  if (split) {
+    const mce_status ps = post_peel(static_cast<MceCtl*>(e->host1.p)->tail_go != 0);
+    if (ps != MCE_OK) return ps;
   }
   if ((h = hipStreamSynchronize(s)) != hipSuccess) return hip_fail(e, h, "synchronize after orient");
 
@@ -827,9 +861,9 @@ mce_status run_once(mce_engine* e, int32_t n, int64_t nnz, const int32_t* row_pt
       const int want = (kSplitBlocksPerCu * e->num_cu + counts[c] - 1) / counts[c];
       bp.parts = std::max(1, std::min(std::max(want, (nslab + 7) / 8), nslab));
     }
-    if (use_fadj) {
-      bp.fadj = dp<int>(B.fadj);
-      bp.fdeg = dp<int>(B.fdeg);
+    if (use_fadj) {   // (B.fadj may have been allocated after the peel: read the pointers here)
+      bp.fadj = dp<int>(fadj_in1 ? B.fadj1 : B.fadj);
+      bp.fdeg = dp<int>(fadj_in1 ? B.fdeg1 : B.fdeg);
     }
     if (timing) (void)hipEventRecord(e->ev[evi], ls);
     if ((h = mce_launch_build(bp, e->num_cu * 32, ls)) != hipSuccess) return launch_fail(h, "build launch");
@@ -1209,7 +1243,8 @@ mce_status mce_create(const mce_config* cfg, mce_engine** out) {
     side_ok = side_ok && hipStreamCreateWithFlags(&e->side[k], hipStreamNonBlocking) == hipSuccess;
     side_ok = side_ok && hipEventCreateWithFlags(&e->join_ev[k], hipEventDisableTiming) == hipSuccess;
   }
-  side_ok = side_ok && hipEventCreateWithFlags(&e->handed_ev, hipEventDisableTiming) == hipSuccess;
+  side_ok = side_ok && hipEventCreateWithFlags(&e->handed_ev, hipEventDisableTiming) == hipSuccess &&
+            hipEventCreateWithFlags(&e->early_built_ev, hipEventDisableTiming) == hipSuccess;
   if (!side_ok) {
     mce_destroy(e);
     return MCE_ERR_DEVICE;
@@ -1420,6 +1455,7 @@ void mce_destroy(mce_engine* e) {
     if (ev) (void)hipEventDestroy(ev);
   if (e->fork_ev) (void)hipEventDestroy(e->fork_ev);
   if (e->handed_ev) (void)hipEventDestroy(e->handed_ev);
+  if (e->early_built_ev) (void)hipEventDestroy(e->early_built_ev);
   for (auto& st : e->side)
     if (st) (void)hipStreamDestroy(st);
   delete e;

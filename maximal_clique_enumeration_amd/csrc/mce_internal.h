@@ -219,10 +219,11 @@ int mce_peel_max_blocks(int num_cu);
 // that left before the tail, a vertex still in it ranking after all of them and
 // getting its neighbours in the tail that come after it by (degree, id)
 // (nothing if the grid handed no tail over); ctl then only holds the long rows'
-// count.
+// count. only_tail (with snap alone): after the tail, the final rows of the
+// vertices it held, written over their early rows (the others' are final).
 hipError_t mce_launch_forward_adj(int n, const int* rp, const int* ci, const int* rnd, int* fadj, int* fdeg,
                                   int* flong, MceCtl* ctl, int blocks, hipStream_t s, const MceCtl* tctl = nullptr,
-                                  const unsigned char* snap = nullptr, const int* hdeg = nullptr);
+                                  const unsigned char* snap = nullptr, const int* hdeg = nullptr, int only_tail = 0);
 // fdeg: the forward adjacency's row lengths, when every vertex is a root of a
 // first-level run (roots == NULL, fwd == NULL): |P| is read from it.
 // skip_early (whole-graph first-level runs with fdeg): a split peel's early

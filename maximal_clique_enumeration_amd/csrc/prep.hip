@@ -2129,8 +2129,9 @@ __global__ __launch_bounds__(256) void k_forward_adj(int n, const int* __restric
                                                       const int* __restrict__ rnd, int* __restrict__ fadj,
                                                       int* __restrict__ fdeg, int* __restrict__ flong, MceCtl* ctl,
                                                       const MceCtl* tctl, const unsigned char* __restrict__ snap,
-                                                      const int* __restrict__ hdeg) {
+                                                      const int* __restrict__ hdeg, int only_tail) {
   if (tctl && !tctl->tail_go) return;
+  const unsigned char* rs = only_tail ? nullptr : snap;   // ranks from the snapshot: the early rows
   // the block's long rows, listed in LDS and added to the list with one atomic
   // (one per row on the shared count took a 4M-vertex graph's ~20k hub rows
   // about 0.3 ms); a block with more than FWD_LCAP of them lists the rest
@@ -2143,7 +2144,8 @@ __global__ __launch_bounds__(256) void k_forward_adj(int n, const int* __restric
   const int lane = lane_id();
   const int nwaves = gridDim.x * (blockDim.x / MCE_WAVE);
   for (int v = blockIdx.x * (blockDim.x / MCE_WAVE) + threadIdx.x / MCE_WAVE; v < n; v += nwaves) {
-    const int a = rp[v], b = rp[v + 1], rv = fwd_rank(rnd, snap, v);
+    if (only_tail && !snap[v]) continue;
+    const int a = rp[v], b = rp[v + 1], rv = fwd_rank(rnd, rs, v);
     const int dv = rv == FWD_TAIL ? hdeg[v] : 0;
     if (b - a > FWD_LONG) {
       if (lane == 0) {
@@ -2157,7 +2159,7 @@ __global__ __launch_bounds__(256) void k_forward_adj(int n, const int* __restric
     for (int base = a; base < b; base += MCE_WAVE) {
       const int e = base + lane;
       const int u = e < b ? ci[e] : 0;
-      const bool later = e < b && fwd_later(rnd, snap, hdeg, u, rv, dv, v);
+      const bool later = e < b && fwd_later(rnd, rs, hdeg, u, rv, dv, v);
       const u64 m = ballot(later);
       if (later) fadj[a + k + mbcnt(m)] = u;
       k += __popcll(m);
@@ -2180,15 +2182,16 @@ __global__ __launch_bounds__(256) void k_forward_adj_long(const int* __restrict_
                                                            int* __restrict__ fdeg, const int* __restrict__ flong,
                                                            MceCtl* ctl, const MceCtl* tctl,
                                                            const unsigned char* __restrict__ snap,
-                                                           const int* __restrict__ hdeg) {
+                                                           const int* __restrict__ hdeg, int only_tail) {
   constexpr int NW = 256 / MCE_WAVE;
   __shared__ int s_cnt[4][NW];
   if (tctl && !tctl->tail_go) return;
+  const unsigned char* rs = only_tail ? nullptr : snap;
   const int lane = lane_id(), wv = threadIdx.x / MCE_WAVE;
   const int nl = ld_relaxed(&ctl->nlong);
   for (int j = blockIdx.x; j < nl; j += gridDim.x) {
     const int v = flong[j];
-    const int a = rp[v], b = rp[v + 1], rv = fwd_rank(rnd, snap, v);
+    const int a = rp[v], b = rp[v + 1], rv = fwd_rank(rnd, rs, v);
     const int dv = rv == FWD_TAIL ? hdeg[v] : 0;
     int k = 0;   // entries placed so far (the same in every thread)
     for (int base = a; base < b; base += 4 * 256) {
@@ -2203,7 +2206,7 @@ __global__ __launch_bounds__(256) void k_forward_adj_long(const int* __restrict_
 #pragma unroll
       for (int z = 0; z < 4; z++) {
         const int e = base + z * 256 + (int)threadIdx.x;
-        lat[z] = e < b && fwd_later(rnd, snap, hdeg, u[z], rv, dv, v);
+        lat[z] = e < b && fwd_later(rnd, rs, hdeg, u[z], rv, dv, v);
       }
 #pragma unroll
       for (int z = 0; z < 4; z++) {
@@ -2648,15 +2651,15 @@ hipError_t mce_launch_orient(int n, const int* rp, const int* ci, const int* rnd
 
 hipError_t mce_launch_forward_adj(int n, const int* rp, const int* ci, const int* rnd, int* fadj, int* fdeg,
                                   int* flong, MceCtl* ctl, int blocks, hipStream_t s, const MceCtl* tctl,
-                                  const unsigned char* snap, const int* hdeg) {
-  if (!tctl != !snap || !tctl != !hdeg) return hipErrorInvalidValue;
+                                  const unsigned char* snap, const int* hdeg, int only_tail) {
+  if (only_tail ? (tctl || hdeg || !snap) : (!tctl != !snap || !tctl != !hdeg)) return hipErrorInvalidValue;
   const int nb = max(1, min(blocks, (n + 3) / 4));   // four wavefronts a block, one vertex each at a time
   hipLaunchKernelGGL(k_forward_adj, dim3(nb), dim3(256), 0, s, n, rp, ci, rnd, fadj, fdeg, flong, ctl, tctl, snap,
-                     hdeg);
+                     hdeg, only_tail);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(k_forward_adj_long, dim3(max(1, blocks)), dim3(256), 0, s, rp, ci, rnd, fadj, fdeg, flong, ctl,
-                     tctl, snap, hdeg);
+                     tctl, snap, hdeg, only_tail);
   return hipGetLastError();
 }
 
