@@ -154,7 +154,9 @@ def kernel_name(sub):
 def build_name(sub):
     if sub == MICRO_SUB:
         return "k_build_micro"
-    return f"k_build_head+k_build_rows<{1 << (sub >> 1)}>"
+    w = 1 << (sub >> 1)
+    # widths up to 8 build their P rows in a kernel of their own (with the forward adjacency)
+    return f"k_build_head+k_build_prows+k_build_rows<{w}>" if w <= 8 else f"k_build_head+k_build_rows<{w}>"
 
 
 def launch_ops(trace, launch):
@@ -363,8 +365,9 @@ def kernel_table(g, cst, ctrace, stats, events, counters, nnz):
     mean = lambda key: sum(s[key] for s in stats) / n_st   # noqa: E731
     rows = []
     if events == "phase":
-        rows.append({"kernel": "k_peel", "ms": mean("ms_peel"), "bound": "hbm",
-                     "algorithmic": peel_bytes(g.n, nnz), "unit": "B"})
+        # a split peel is two launches (the grid's, then the tail's): the events span both
+        rows.append({"kernel": "k_peel+k_peel_tail" if stats[0].get("early_launch") else "k_peel",
+                     "ms": mean("ms_peel"), "bound": "hbm", "algorithmic": peel_bytes(g.n, nnz), "unit": "B"})
         rows.append({"kernel": "k_validate_*", "ms": mean("ms_validate"), "bound": "hbm",
                      "algorithmic": 4 * (g.n + 1) + 4 * nnz, "unit": "B"})
     launches = stats[0]["launches"]
@@ -393,7 +396,16 @@ def kernel_table(g, cst, ctrace, stats, events, counters, nnz):
             r["achieved"] = r["algorithmic"] / sec / 1e9
             r["peak"] = HBM_PEAK / 1e9
             r["frac"] = r["algorithmic"] / sec / HBM_PEAK
-        c = counters.get(r["kernel"] if "launch" not in r else f'{r["kernel"]}#{r["launch"]}')
+        # the counter passes run the launches in series (no split peel: one peel
+        # launch, no early launch, one micro launch for all micro roots)
+        early = stats[0].get("early_launch", 0)
+        if "launch" not in r:
+            ckey = "k_peel" if r["kernel"].startswith("k_peel") else r["kernel"]
+        elif early and "micro" in r["kernel"]:
+            ckey = None
+        else:
+            ckey = f'{r["kernel"]}#{r["launch"] - early}'
+        c = counters.get(ckey) if ckey else None
         if c:
             traffic = c.get("fetch_bytes", 0) + c.get("write_bytes", 0)
             r["traffic"] = traffic

@@ -75,7 +75,7 @@ class mce_worker_record(ctypes.Structure):
 
 class mce_run_stats(ctypes.Structure):
     _fields_ = [("struct_size", ctypes.c_uint32), ("workers", ctypes.c_int32),
-                ("launches", ctypes.c_int32), ("pad_", ctypes.c_int32),
+                ("launches", ctypes.c_int32), ("early_launch", ctypes.c_int32),
                 ("nodes", ctypes.c_uint64), ("leaves", ctypes.c_uint64),
                 ("donations", ctypes.c_uint64), ("pivot_rows", ctypes.c_uint64),
                 ("pivot_words", ctypes.c_uint64), ("xx_tests", ctypes.c_uint64),
@@ -409,7 +409,7 @@ class Engine:
         st = mce_run_stats()
         st.struct_size = ctypes.sizeof(mce_run_stats)
         self._check(mce_stats(self._h, st), "mce_stats", self._h)
-        out = {name: getattr(st, name) for name, _ in mce_run_stats._fields_ if name != "pad_"}
+        out = {name: getattr(st, name) for name, _ in mce_run_stats._fields_}
         for key in ("peel_ticks", "launch_sub", "launch_roots", "launch_build_ms", "launch_search_ms",
                     "launch_words"):
             out[key] = list(out[key])[: (4 if key == "peel_ticks" else out["launches"])]

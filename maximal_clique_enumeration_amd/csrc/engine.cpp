@@ -995,6 +995,7 @@ mce_status run_once(mce_engine* e, int32_t n, int64_t nnz, const int32_t* row_pt
   so.workers = std::max(max_workers_used, early_nw);
   const int e0 = n1 > 0 ? 1 : 0;   // the early launch comes first in the launch lists
   so.launches = launches + e0;
+  so.early_launch = e0;
   u64 words_built = words1;
   for (int i = 0; i < nplan; i++) words_built += hctl->sub_words[var][plan[i].sub];
   so.table_words = words_built;

@@ -195,6 +195,7 @@ def test_split_peel_early_launch():
                 assert np.array_equal(core.cpu().numpy(), ocore) and np.array_equal(rnd.cpu().numpy(), ornd)
                 assert e.graph_info()["roots_started"] == g.n
         so, ss = eo.stats(), es.stats()
+        assert so["early_launch"] == 1 and ss["early_launch"] == 0
         assert so["launches"] == ss["launches"] + 1 and so["launch_sub"][0] == 12
         assert 0 < so["launch_roots"][0] < so["micro_roots"] == ss["micro_roots"]
 
