@@ -366,7 +366,7 @@ def kernel_table(g, cst, ctrace, stats, events, counters, nnz):
     rows = []
     if events == "phase":
         # a split peel is two launches (the grid's, then the tail's): the events span both
-        rows.append({"kernel": "k_peel+k_peel_tail" if stats[0].get("early_launch") else "k_peel",
+        rows.append({"kernel": "k_peel+k_peel_tail" if stats[0].get("handover_round", -1) >= 0 else "k_peel",
                      "ms": mean("ms_peel"), "bound": "hbm", "algorithmic": peel_bytes(g.n, nnz), "unit": "B"})
         rows.append({"kernel": "k_validate_*", "ms": mean("ms_validate"), "bound": "hbm",
                      "algorithmic": 4 * (g.n + 1) + 4 * nnz, "unit": "B"})
@@ -397,15 +397,12 @@ def kernel_table(g, cst, ctrace, stats, events, counters, nnz):
             r["peak"] = HBM_PEAK / 1e9
             r["frac"] = r["algorithmic"] / sec / HBM_PEAK
         # the counter passes run the launches in series (no split peel: one peel
-        # launch, no early launch, one micro launch for all micro roots)
-        early = stats[0].get("early_launch", 0)
+        # launch, and the peel's order, whose sub-classes come in the same order)
         if "launch" not in r:
             ckey = "k_peel" if r["kernel"].startswith("k_peel") else r["kernel"]
-        elif early and "micro" in r["kernel"]:
-            ckey = None
         else:
-            ckey = f'{r["kernel"]}#{r["launch"] - early}'
-        c = counters.get(ckey) if ckey else None
+            ckey = f'{r["kernel"]}#{r["launch"]}'
+        c = counters.get(ckey)
         if c:
             traffic = c.get("fetch_bytes", 0) + c.get("write_bytes", 0)
             r["traffic"] = traffic

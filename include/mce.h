@@ -153,11 +153,13 @@ typedef struct {
 typedef struct {
   uint32_t struct_size;      /* sizeof(mce_run_stats) */
   int32_t workers;           /* wavefronts in the largest search launch */
-  int32_t launches;          /* search launches (one per bitset width and staging sub-class, and
-                                the early launch) */
-  int32_t early_launch;      /* 1: the peel was split (its tail ran as a launch of its own, beside
-                                the early launch, which is launch 0: the micro-sized first-level
-                                subtrees of the vertices gone before the tail); 0 otherwise */
+  int32_t launches;          /* search launches (one per bitset width and staging sub-class) */
+  int32_t handover_round;    /* -1: the search took the peel's order. Else the peel was split at
+                                this round (its tail ran as a launch of its own, beside the
+                                search), and the search took the hand-over order: the vertices
+                                gone before the round by their rounds, then the vertices still
+                                present by their degree among themselves, then id (every maximal
+                                clique is reported once under any vertex order) */
   uint64_t nodes;            /* search-tree nodes whose pivot was evaluated */
   uint64_t leaves;           /* maximal cliques reported (== count minus isolated) */
   uint64_t donations;        /* branches handed to idle wavefronts (section 3.3, Table 2) */

@@ -75,7 +75,7 @@ class mce_worker_record(ctypes.Structure):
 
 class mce_run_stats(ctypes.Structure):
     _fields_ = [("struct_size", ctypes.c_uint32), ("workers", ctypes.c_int32),
-                ("launches", ctypes.c_int32), ("early_launch", ctypes.c_int32),
+                ("launches", ctypes.c_int32), ("handover_round", ctypes.c_int32),
                 ("nodes", ctypes.c_uint64), ("leaves", ctypes.c_uint64),
                 ("donations", ctypes.c_uint64), ("pivot_rows", ctypes.c_uint64),
                 ("pivot_words", ctypes.c_uint64), ("xx_tests", ctypes.c_uint64),

@@ -41,7 +41,7 @@ struct Bufs {
   DevBuf fadj, fdeg, flong;                           // forward adjacency (table builds)
   DevBuf tcol, tcrow;                                 // the peel's compacted residual graph
   // the early launch of a split peel (the roots that left before the tail)
-  DevBuf ctl1, snap, fadj1, fdeg1, flong1, pcount1, xcount1, lists1, taboff1, scan1, heap1, mstack1, mail1, stats1;
+  DevBuf ctl1, snap, srank, fadj1, fdeg1, flong1, pcount1, xcount1;
 };
 
 constexpr size_t kHistWords = MCE_MAX_P + 3;   // global histogram entries (sizes up to 2 + MCE_MAX_P)
@@ -73,17 +73,16 @@ struct mce_engine {
   Bufs* last = &own;  // the set the last run used (mce_ordering, mce_stats)
   HostPinned host;    // staging for device -> host copies (mce_run, mce_run_roots)
   alignas(64) unsigned char host_io[kIoBytes];   // the same for mce_run_static (pageable)
-  hipEvent_t ev[4 + 4 * (MCE_NSUB + 1)] = {};
+  hipEvent_t ev[4 + 4 * MCE_NSUB] = {};
   bool have_events = false;
   // the overlapped search launches: streams forked from the caller's stream
   // (fork_ev) and joined back to it (join_ev)
   hipStream_t side[MCE_SIDE_STREAMS] = {};
   hipEvent_t fork_ev = nullptr;
   hipEvent_t join_ev[MCE_SIDE_STREAMS] = {};
-  // the early launch of a split peel runs on side stream 0 from the grid's
+  // a split peel's hand-over order is set up on side stream 0 from the grid's
   // hand-over (handed_ev); its control block is read back through host1
   hipEvent_t handed_ev = nullptr;
-  hipEvent_t early_built_ev = nullptr;   // the early build has read the early forward rows
   HostPinned host1;
 
   // last run
@@ -102,9 +101,8 @@ struct mce_engine {
   // mce_worker_trace asks for them (they are diagnostics, not results)
   struct LaunchInfo {
     int sub, nw, roots;
-    bool early;   // the split peel's early launch: its counters are in stats1
   };
-  LaunchInfo last_plan[MCE_NSUB + 1] = {};
+  LaunchInfo last_plan[MCE_NSUB] = {};
   // where the last run's induced-subgraph tables sit (mce_root_table): valid
   // after a complete first-level run with overlapped launches, each sub-class
   // in its own heap region
@@ -114,7 +112,6 @@ struct mce_engine {
     int total = 0;                      // root-list entries
     int off[MCE_NSUB] = {}, count[MCE_NSUB] = {};
     size_t heap_base[MCE_NSUB] = {};    // u64 words
-    int early = 0;                      // the early launch's roots (micro tables in heap1)
   } tabs;
   int n_last_plan = 0;
   int last_stat_rows = 0;
@@ -261,8 +258,7 @@ constexpr int kSplitBlocksPerCu = 16;
 // 18.2 / 18.7 / 19.5 ms.
 constexpr int kWideWavesPerCu = MCE_WIDE_WAVES_PER_CU;
 
-// the split peel's early launch records its subtrees taken here (MceCtl::taken)
-constexpr int kTakenEarly = 2 * MCE_NCLASS + 1;
+
 
 // ------------------------------------------------------------------ static scratch
 // The device memory of mce_run_static: one array per device, holding every
@@ -417,12 +413,15 @@ mce_status run_once(mce_engine* e, int32_t n, int64_t nnz, const int32_t* row_pt
   // Split peel: the grid stops where block 0 would finish alone on the
   // compacted residual graph, and the tail runs as a one-block launch of its
   // own. Every vertex gone by then has its final round, and every vertex still
-  // in the tail comes after it, so those roots' subtrees are fixed already: the
-  // micro-sized ones are built and searched on the early stream, on the compute
-  // units the tail leaves idle (whole-graph first-level runs with overlapped
-  // launches and the micro kernel).
+  // in the tail comes after it; the search takes the vertices of the tail
+  // among themselves by their degree in the remaining graph (then id) instead
+  // of their rounds, so that every subtree is fixed at the hand-over and the
+  // whole search runs on the compute units the tail leaves idle (whole-graph
+  // first-level runs with overlapped launches). Any vertex order reports each
+  // maximal clique once; the degeneracy order is what keeps |P| small, and the
+  // tail's vertices are the last ones of it either way.
   const bool micro_on = (e->cfg.flags & MCE_FLAG_NO_MICRO) == 0;
-  const bool split = overlap && !l2 && !subset && micro_on && tcap > 0;
+  const bool split = overlap && !l2 && !subset && tcap > 0;
   MceCtl* ctl1 = nullptr;
   if (split) {
     const size_t snap_words = ((size_t)n + 7) / 8;
@@ -450,36 +449,61 @@ mce_status run_once(mce_engine* e, int32_t n, int64_t nnz, const int32_t* row_pt
   // the root bucketing when a build needs it (not mce_run_static: its scratch
   // has no room for nnz more entries).
   const bool early_fadj = !stat && !l2 && !subset;
-  if (early_fadj &&
-      ((h = take(arena, B.fadj, (size_t)std::max<int64_t>(nnz, 1) * sizeof(int))) != hipSuccess ||
-       (h = take(arena, B.fdeg, (size_t)n * sizeof(int))) != hipSuccess ||
-       (h = take(arena, B.flong, (size_t)n * sizeof(int))) != hipSuccess))
-    return alloc_fail(e, arena, h, "forward adjacency");
-  // The steps after the peel on s (forward adjacency, orientation, read-back).
-  // With a split peel they are queued after the early launch (below): the final
-  // rows of the tail's vertices go over their early rows, once the early build
-  // has read them; every other vertex's early row is its final one.
-  bool fadj_in1 = false;   // the run's forward adjacency is the early one, its tail rows made final
   char* hio = stat ? reinterpret_cast<char*>(e->host_io) : static_cast<char*>(e->host.p);
   MceCtl* hctl = reinterpret_cast<MceCtl*>(hio);
-  auto post_peel = [&](bool tail_rows) -> mce_status {
-    if (early_fadj) {
-      if (tail_rows) {
-        fadj_in1 = true;
-        if ((h = hipStreamWaitEvent(s, e->early_built_ev, 0)) != hipSuccess) return hip_fail(e, h, "early build wait");
-        h = mce_launch_forward_adj(n, row_ptr, col_idx, dp<int>(B.rnd), dp<int>(B.fadj1), dp<int>(B.fdeg1),
-                                   dp<int>(B.flong), ctl, e->num_cu * 16, s, nullptr, dp<unsigned char>(B.snap),
-                                   nullptr, 1);
-      } else {
-        h = mce_launch_forward_adj(n, row_ptr, col_idx, dp<int>(B.rnd), dp<int>(B.fadj), dp<int>(B.fdeg),
-                                   dp<int>(B.flong), ctl, e->num_cu * 16, s);
-      }
-      if (h != hipSuccess) return hip_fail(e, h, "forward adjacency launch");
+
+  // Split peel: the search takes the hand-over order, set up on side stream 0
+  // from the grid's hand-over event while the tail runs on s: its ranks, its
+  // forward adjacency and the orientation of every root, read back; the whole
+  // search is then planned from them. A return on any path after this waits
+  // for that stream first.
+  struct StreamGuard {
+    hipStream_t st = nullptr;
+    ~StreamGuard() {
+      if (st) (void)hipStreamSynchronize(st);
     }
+  } early_guard;
+  hipStream_t es = e->side[0];
+  bool handover = false;
+  MceCtl* h1 = static_cast<MceCtl*>(e->host1.p);
+  if (split) {
+    if ((h = ensure(B.srank, (size_t)n * sizeof(int))) != hipSuccess ||
+        (h = ensure(B.fadj1, (size_t)std::max<int64_t>(nnz, 1) * sizeof(int))) != hipSuccess ||
+        (h = ensure(B.fdeg1, (size_t)n * sizeof(int))) != hipSuccess ||
+        (h = ensure(B.flong1, (size_t)n * sizeof(int))) != hipSuccess ||
+        (h = ensure(B.pcount1, (size_t)n * sizeof(int))) != hipSuccess ||
+        (h = ensure(B.xcount1, (size_t)n * sizeof(int))) != hipSuccess ||
+        (h = ensure_host(e->host1, sizeof(MceCtl))) != hipSuccess)
+      return hip_fail(e, h, "allocation");
+    h1 = static_cast<MceCtl*>(e->host1.p);
+    early_guard.st = es;
+    if ((h = hipStreamWaitEvent(es, e->handed_ev, 0)) != hipSuccess ||
+        (h = mce_launch_search_rank(n, dp<int>(B.rnd), dp<int>(B.deg), dp<unsigned char>(B.snap), ctl,
+                                    dp<int>(B.srank), grid, es)) != hipSuccess ||
+        (h = mce_launch_forward_adj(n, row_ptr, col_idx, dp<int>(B.srank), dp<int>(B.fadj1), dp<int>(B.fdeg1),
+                                    dp<int>(B.flong1), ctl1, e->num_cu * 16, es, ctl)) != hipSuccess ||
+        (h = mce_launch_orient_handover(n, row_ptr, dp<int>(B.fdeg1), ctl, dp<int>(B.pcount1),
+                                        dp<int>(B.xcount1), ctl1, grid, es)) != hipSuccess ||
+        (h = hipMemcpyAsync(h1, ctl1, sizeof(MceCtl), hipMemcpyDeviceToHost, es)) != hipSuccess ||
+        (h = hipStreamSynchronize(es)) != hipSuccess)
+      return hip_fail(e, h, "hand-over orientation");
+    // (a root of more than MCE_MAX_P later neighbours in the hand-over order:
+    // the search waits for the peel's order instead, which may have none)
+    handover = h1->tail_go != 0 && (h1->status & MCE_E_LIMIT) == 0;
+  }
+  if (!handover) {
+    if (early_fadj &&
+        ((h = take(arena, B.fadj, (size_t)std::max<int64_t>(nnz, 1) * sizeof(int))) != hipSuccess ||
+         (h = take(arena, B.fdeg, (size_t)n * sizeof(int))) != hipSuccess ||
+         (h = take(arena, B.flong, (size_t)n * sizeof(int))) != hipSuccess))
+      return alloc_fail(e, arena, h, "forward adjacency");
+    if (early_fadj && (h = mce_launch_forward_adj(n, row_ptr, col_idx, dp<int>(B.rnd), dp<int>(B.fadj),
+                                                  dp<int>(B.fdeg), dp<int>(B.flong), ctl, e->num_cu * 16, s)) !=
+                          hipSuccess)
+      return hip_fail(e, h, "forward adjacency launch");
     if ((h = mce_launch_orient(n, row_ptr, col_idx, dp<int>(B.rnd), subset ? roots : nullptr, cnt,
                                dp<int>(B.pcount), dp<int>(B.xcount), ctl, l2 ? dp<u64>(B.fwd) : nullptr,
-                               early_fadj ? dp<int>(fadj_in1 ? B.fdeg1 : B.fdeg) : nullptr, grid, s,
-                               split ? 1 : 0)) != hipSuccess)
+                               early_fadj ? dp<int>(B.fdeg) : nullptr, grid, s)) != hipSuccess)
       return hip_fail(e, h, "orient launch");
     if (l2 && (h = mce_launch_l2_roots(n, nnz, row_ptr, col_idx, dp<int>(B.rnd), subset ? roots : nullptr, cnt,
                                        dp<u64>(B.fwd), dp<u64>(B.fwdtmp), dp<int>(B.src), dp<int>(B.eroots),
@@ -488,170 +512,60 @@ mce_status run_once(mce_engine* e, int32_t n, int64_t nnz, const int32_t* row_pt
       return hip_fail(e, h, "second-level roots launch");
     if ((h = hipMemcpyAsync(hctl, ctl, sizeof(MceCtl), hipMemcpyDeviceToHost, s)) != hipSuccess)
       return hip_fail(e, h, "readback");
-    return MCE_OK;
-  };
-  if (!split) {
-    const mce_status ps = post_peel(false);
-    if (ps != MCE_OK) return ps;
-  }
-
-  // The early launch, on its own stream from the grid's hand-over (while the
-  // tail and the steps above run on s): the early forward adjacency, the early
-  // roots' tallies (read back), then their micro tables and search. A return
-  // on any path after this waits for that stream first.
-  struct StreamGuard {
-    hipStream_t st = nullptr;
-    ~StreamGuard() {
-      if (st) (void)hipStreamSynchronize(st);
+    if ((h = hipStreamSynchronize(s)) != hipSuccess) return hip_fail(e, h, "synchronize after orient");
+    const u32 gbits = hctl->status & 0x1Fu;
+    e->info.max_degree = hctl->max_degree;
+    if (gbits) {
+      e->info.graph_errors = gbits;
+      return fail(e, MCE_ERR_GRAPH, "input is not a simple undirected graph in CSR form");
     }
-  } early_guard;
-  int n1 = 0, early_nw = 0;
-  u64 words1 = 0;
-  // the early stream: side stream 0, whose later launches come after it (with
-  // a stream of its own, it shared a hardware queue with the stream of the
-  // longest chain, which then waited for it: 18.0 against 18.3 ms a step)
-  hipStream_t es = e->side[0];
-  if (split) {
-    if ((h = ensure(B.fadj1, (size_t)std::max<int64_t>(nnz, 1) * sizeof(int))) != hipSuccess ||
-        (h = ensure(B.fdeg1, (size_t)n * sizeof(int))) != hipSuccess ||
-        (h = ensure(B.flong1, (size_t)n * sizeof(int))) != hipSuccess ||
-        (h = ensure(B.pcount1, (size_t)n * sizeof(int))) != hipSuccess ||
-        (h = ensure(B.xcount1, (size_t)n * sizeof(int))) != hipSuccess ||
-        (h = ensure_host(e->host1, sizeof(MceCtl))) != hipSuccess)
-      return hip_fail(e, h, "allocation");
-    early_guard.st = es;
-    MceCtl* h1 = static_cast<MceCtl*>(e->host1.p);
-    if ((h = hipStreamWaitEvent(es, e->handed_ev, 0)) != hipSuccess ||
-        (h = mce_launch_forward_adj(n, row_ptr, col_idx, dp<int>(B.rnd), dp<int>(B.fadj1), dp<int>(B.fdeg1),
-                                    dp<int>(B.flong1), ctl1, e->num_cu * 16, es, ctl,
-                                    dp<unsigned char>(B.snap), dp<int>(B.deg))) != hipSuccess ||
-        (h = mce_launch_orient_early(n, row_ptr, dp<unsigned char>(B.snap), dp<int>(B.fdeg1), ctl,
-                                     dp<int>(B.pcount1), dp<int>(B.xcount1), ctl1, grid, es)) != hipSuccess ||
-        (h = hipMemcpyAsync(h1, ctl1, sizeof(MceCtl), hipMemcpyDeviceToHost, es)) != hipSuccess ||
-        (h = hipStreamSynchronize(es)) != hipSuccess)
-      return hip_fail(e, h, "early orientation");
-    if (h1->status) return fail(e, MCE_ERR_DEVICE, "early orientation failed");
-    // (nothing of the early launch reads the early rows after this point unless
-    // its build is queued below; the event then follows the build)
-    if (!h1->tail_go || h1->sub_count[0][MCE_SUB_MICRO] == 0) {
-      if ((h = hipEventRecord(e->early_built_ev, es)) != hipSuccess) return hip_fail(e, h, "early build event");
-    }
-    if (h1->tail_go) {
-      n1 = h1->sub_count[0][MCE_SUB_MICRO];
-      words1 = h1->sub_words[0][MCE_SUB_MICRO];
-    }
-    if (n1 > 0) {
-      // as the micro launch below: at most 8 wavefronts per CU
-      early_nw = occupancy(e, -1 - (counters_on ? 1 : 0), 0LL,
-                           [&] { return mce_micro_max_workers(counters_on, e->num_cu); });
-      early_nw = std::min(early_nw, 8 * e->num_cu);
-      if (early_nw <= 0) return fail(e, MCE_ERR_DEVICE, "micro kernel occupancy query failed");
-      if (e->cfg.max_workers > 0) early_nw = std::min(early_nw, (int)e->cfg.max_workers);
-      if (!e->cfg.worker_list) early_nw = std::min(early_nw, n1);
-      const int cap1 = e->micro_stack;
-      if ((h = ensure(B.lists1, (size_t)n1 * sizeof(int))) != hipSuccess ||
-          (h = ensure(B.taboff1, (size_t)n1 * sizeof(u64))) != hipSuccess ||
-          (h = ensure(B.scan1, (size_t)mce_scan_temp_words(n1) * sizeof(u64))) != hipSuccess ||
-          (h = ensure(B.heap1, (size_t)words1 * sizeof(u64))) != hipSuccess ||
-          (h = ensure(B.mstack1, 6 * sizeof(u64) * (size_t)early_nw * (size_t)cap1)) != hipSuccess ||
-          (h = ensure(B.mail1, (size_t)early_nw * mce_micro_mail_words() * sizeof(u64))) != hipSuccess ||
-          (h = ensure(B.stats1, (size_t)early_nw * MCE_NSTAT * sizeof(u64))) != hipSuccess)
-        return hip_fail(e, h, "early search buffers");
-      SubOffsets off1{};
-      MceWl* wl1 = dp<MceWl>(B.wl) + MCE_NSUB;
-      if ((h = mce_launch_bucket(nullptr, n, dp<int>(B.pcount1), dp<int>(B.xcount1), MCE_MODE_IPX, 1, off1,
-                                 dp<int>(B.lists1), dp<u64>(B.taboff1), ctl1, grid, es)) != hipSuccess ||
-          (h = mce_launch_scan(dp<u64>(B.taboff1), n1, dp<u64>(B.scan1), es)) != hipSuccess ||
-          (h = mce_launch_wl_init(wl1, early_nw, dp<u64>(B.stats1), es)) != hipSuccess)
-        return hip_fail(e, h, "early launch");
-      BuildParams bp{};
-      bp.rp = row_ptr;
-      bp.ci = col_idx;
-      bp.rnd = dp<int>(B.rnd);
-      bp.roots = dp<int>(B.lists1);
-      bp.nroots = n1;
-      bp.W = 1;
-      bp.mode = MCE_MODE_IPX;
-      bp.micro = 1;
-      bp.heap = dp<u64>(B.heap1);
-      bp.heap_words = (size_t)words1;
-      bp.tab_off = dp<u64>(B.taboff1);
-      bp.status = &ctl->status;
-      bp.fadj = dp<int>(B.fadj1);
-      bp.fdeg = dp<int>(B.fdeg1);
-      bp.snap = dp<unsigned char>(B.snap);
-      if (timing) (void)hipEventRecord(e->ev[4], es);
-      if ((h = mce_launch_build(bp, e->num_cu * 32, es)) != hipSuccess) return hip_fail(e, h, "early build");
-      if ((h = hipEventRecord(e->early_built_ev, es)) != hipSuccess) return hip_fail(e, h, "early build event");
-      if (timing) (void)hipEventRecord(e->ev[5], es);
-      MicroParams mp{};
-      mp.heap = dp<u64>(B.heap1);
-      mp.tab_off = dp<u64>(B.taboff1);
-      mp.nroots = n1;
-      mp.nworkers = early_nw;
-      mp.stacks = dp<u64>(B.mstack1);
-      mp.stack_cap = cap1;
-      mp.mail_words = mce_micro_mail_words();
-      mp.mail = dp<u64>(B.mail1);
-      mp.g_hist = results + 1;
-      mp.g_hash = results;
-      mp.wl = wl1;
-      mp.donate_min_p = e->cfg.micro_donate_min_p > 0 ? (int)e->cfg.micro_donate_min_p : 10;
-      mp.worker_list = e->cfg.worker_list ? 1 : 0;
-      mp.coop = n1 >= kMicroCoopRootsPerWave * early_nw ? 1 : 0;
-      mp.budget = budget;
-      mp.t_run = &ctl->t_run;
-      mp.status = &ctl->status;
-      mp.stats = dp<u64>(B.stats1);
-      mp.taken = &ctl->taken[kTakenEarly];
-      if (stimes) (void)hipEventRecord(e->ev[6], es);
-      if ((h = mce_launch_micro(counters_on, mp, es)) != hipSuccess) return hip_fail(e, h, "early search");
-      if (stimes) (void)hipEventRecord(e->ev[7], es);
-    }
+    if (hctl->status & MCE_E_TIMEOUT) return fail(e, MCE_ERR_TIMEOUT, "k-core peel ran past the time limit");
+    if (hctl->status & MCE_E_ROOTS) return fail(e, MCE_ERR_ARG, "a root id is outside [0, n)");
+    e->info.degeneracy = hctl->degeneracy;
+    e->info.rounds = hctl->rounds;
+    e->have_order = true;
+  } else {
+    // (the grid ran, so the input passed validation; the peel's order is known
+    // once the tail ends, at the final read-back)
+    e->info.max_degree = h1->max_degree;
   }
-  if (split) {
-    const mce_status ps = post_peel(static_cast<MceCtl*>(e->host1.p)->tail_go != 0);
-    if (ps != MCE_OK) return ps;
-  }
-  if ((h = hipStreamSynchronize(s)) != hipSuccess) return hip_fail(e, h, "synchronize after orient");
-
-  const u32 gbits = hctl->status & 0x1Fu;
-  e->info.max_degree = hctl->max_degree;
-  if (gbits) {
-    e->info.graph_errors = gbits;
-    return fail(e, MCE_ERR_GRAPH, "input is not a simple undirected graph in CSR form");
-  }
-  if (hctl->status & MCE_E_TIMEOUT) return fail(e, MCE_ERR_TIMEOUT, "k-core peel ran past the time limit");
-  if (hctl->status & MCE_E_ROOTS) return fail(e, MCE_ERR_ARG, "a root id is outside [0, n)");
-  e->info.degeneracy = hctl->degeneracy;
-  e->info.rounds = hctl->rounds;
-  e->info.max_p = hctl->max_p;
-  e->info.max_x = hctl->max_x;
-  e->info.isolated = (int64_t)hctl->isolated;
-  e->have_order = true;
-  if (hctl->status & MCE_E_LIMIT)
+  // The facts the plan reads, the device control block whose cursors the
+  // bucketing takes, the stream the plan's set-up runs on (it forks from it),
+  // the order the builds split each root's neighbours by, the forward adjacency
+  // and the roots' |P| and |X|: the hand-over order's or the peel's.
+  const MceCtl* tc = handover ? h1 : hctl;
+  MceCtl* tdev = handover ? ctl1 : ctl;
+  hipStream_t fs = handover ? es : s;
+  int* srnd = handover ? dp<int>(B.srank) : dp<int>(B.rnd);
+  int* fadj_p = handover ? dp<int>(B.fadj1) : nullptr;
+  int* fdeg_p = handover ? dp<int>(B.fdeg1) : nullptr;
+  e->info.max_p = tc->max_p;
+  e->info.max_x = tc->max_x;
+  e->info.isolated = (int64_t)tc->isolated;
+  if (tc->status & MCE_E_LIMIT)
     return fail(e, MCE_ERR_LIMIT, l2 ? "a second-level subtree has more than 2048 common later neighbours"
                                      : "a first-level subtree has more than 2048 later neighbours");
   // the subtree roots the search takes: vertex roots, or their forward edges
   const int nsub = l2 ? hctl->l2_roots : cnt;
   const int32_t* sroots = l2 ? dp<int>(B.eroots) : (subset ? roots : nullptr);
-  int* spc = l2 ? dp<int>(B.pcount2) : dp<int>(B.pcount);
-  int* sxc = l2 ? dp<int>(B.xcount2) : dp<int>(B.xcount);
+  int* spc = handover ? dp<int>(B.pcount1) : l2 ? dp<int>(B.pcount2) : dp<int>(B.pcount);
+  int* sxc = handover ? dp<int>(B.xcount1) : l2 ? dp<int>(B.xcount2) : dp<int>(B.xcount);
   e->info.roots = nsub;
 
   // Induced-subgraph mode (section 3.4; section 4.5 picks partial when
-  // Delta / d > 200, else full). Local row indices of the full subgraph must
-  // stay below 2^20 for the pivot keys.
+  // Delta / d > 200, else full; with the hand-over order, d is the level the
+  // peel had reached, a lower bound). Local row indices of the full subgraph
+  // must stay below 2^20 for the pivot keys.
   int mode;
-  const int dd = std::max(1, hctl->degeneracy);
-  const bool full_fits = (long long)hctl->max_p + hctl->max_x < (long long)MCE_MAX_LOCAL;
+  const int dd = std::max(1, tc->degeneracy);
+  const bool full_fits = (long long)tc->max_p + tc->max_x < (long long)MCE_MAX_LOCAL;
   if (e->cfg.subgraph == MCE_SUBGRAPH_PARTIAL) {
     mode = MCE_MODE_IP;
   } else if (e->cfg.subgraph == MCE_SUBGRAPH_FULL) {
     if (!full_fits) return fail(e, MCE_ERR_LIMIT, "full induced subgraph: |P| + |X| of a root exceeds 2^20");
     mode = MCE_MODE_IPX;
   } else {
-    mode = (hctl->max_degree > 200LL * dd || !full_fits) ? MCE_MODE_IP : MCE_MODE_IPX;
+    mode = (tc->max_degree > 200LL * dd || !full_fits) ? MCE_MODE_IP : MCE_MODE_IPX;
   }
   e->info.subgraph = mode == MCE_MODE_IPX ? MCE_SUBGRAPH_FULL : MCE_SUBGRAPH_PARTIAL;
 
@@ -663,17 +577,17 @@ mce_status run_once(mce_engine* e, int32_t n, int64_t nnz, const int32_t* row_pt
   size_t heap_words = 0;            // in series: the largest sub-class's tables; overlapped: all of them
   size_t heap_base[MCE_NSUB] = {};  // a sub-class's region (overlapped)
   for (int c = 0; c < MCE_NSUB; c++) {
-    counts[c] = hctl->sub_count[var][c];
+    counts[c] = tc->sub_count[var][c];
     off.off[c] = total;
     total += counts[c];
     if (overlap) {
       heap_base[c] = heap_words;
-      heap_words += (size_t)hctl->sub_words[var][c];
+      heap_words += (size_t)tc->sub_words[var][c];
     } else {
-      heap_words = std::max(heap_words, (size_t)hctl->sub_words[var][c]);
+      heap_words = std::max(heap_words, (size_t)tc->sub_words[var][c]);
     }
   }
-  const u64 iso = hctl->isolated, iso_hash = hctl->isolated_hash;
+  const u64 iso = tc->isolated, iso_hash = tc->isolated_hash;
 
   // launch plan, heaviest width first; every buffer sized before any launch
   struct Plan {
@@ -699,7 +613,7 @@ mce_status run_once(mce_engine* e, int32_t n, int64_t nnz, const int32_t* row_pt
       nw = occupancy(e, -1 - (counters ? 1 : 0), 0LL, [&] { return mce_micro_max_workers(counters, e->num_cu); });
       nw = std::min(nw, 8 * e->num_cu);
     } else {
-      pl.L = mce_search_layout(c, mode, hctl->sub_maxp[var][c], hctl->sub_maxx[var][c], hctl->sub_maxr[var][c],
+      pl.L = mce_search_layout(c, mode, tc->sub_maxp[var][c], tc->sub_maxx[var][c], tc->sub_maxr[var][c],
                                counts[c], e->num_cu, hbm, counters);
       const SearchLayout& L = pl.L;
       nw = occupancy(e, (((c * 2 + mode) * 2 + (counters ? 1 : 0)) * 2 + (L.srows ? 1 : 0)) * 2 + (L.sprows ? 1 : 0),
@@ -708,7 +622,7 @@ mce_status run_once(mce_engine* e, int32_t n, int64_t nnz, const int32_t* row_pt
     }
     if (nw <= 0) return fail(e, MCE_ERR_DEVICE, "search kernel occupancy query failed");
     if (c != MCE_SUB_MICRO && (c >> 1) == 0) nw = std::min(nw, kW1WavesPerCu * e->num_cu);
-    if (kWideWavesPerCu > 0 && overlap && busy_subs + (n1 > 0 ? 1 : 0) > 1 && c != MCE_SUB_MICRO && (c >> 1) > 0)
+    if (kWideWavesPerCu > 0 && overlap && busy_subs > 1 && c != MCE_SUB_MICRO && (c >> 1) > 0)
       nw = std::min(nw, kWideWavesPerCu * e->num_cu);
     if (e->cfg.max_workers > 0) nw = std::min(nw, (int)e->cfg.max_workers);
     if (!e->cfg.worker_list) nw = std::min(nw, counts[c]);
@@ -761,34 +675,38 @@ mce_status run_once(mce_engine* e, int32_t n, int64_t nnz, const int32_t* row_pt
         return alloc_fail(e, arena, h, "micro search stacks");
     }
     if ((h = mce_launch_bucket(sroots, nsub, spc, sxc, mode,
-                               micro_on ? 1 : 0, off, dp<int>(B.lists), dp<u64>(B.taboff), ctl, grid, s)) !=
+                               micro_on ? 1 : 0, off, dp<int>(B.lists), dp<u64>(B.taboff), tdev, grid, fs)) !=
         hipSuccess)
       return hip_fail(e, h, "bucket launch");
     // table sizes -> heap offsets (every sub-class's launch reuses the heap from its first root's offset)
-    if ((h = mce_launch_scan(dp<u64>(B.taboff), total, dp<u64>(B.scan), s)) != hipSuccess)
+    if ((h = mce_launch_scan(dp<u64>(B.taboff), total, dp<u64>(B.scan), fs)) != hipSuccess)
       return hip_fail(e, h, "table offset scan");
     if (use_fadj && !early_fadj && (h = mce_launch_forward_adj(n, row_ptr, col_idx, dp<int>(B.rnd), dp<int>(B.fadj),
                                                 dp<int>(B.fdeg), dp<int>(B.flong), ctl, e->num_cu * 16, s)) != hipSuccess)
       return hip_fail(e, h, "forward adjacency launch");
   }
-  if (timing) (void)hipEventRecord(e->ev[3], s);
+  if (!handover) {
+    fadj_p = dp<int>(B.fadj);
+    fdeg_p = dp<int>(B.fdeg);
+  }
+  if (timing) (void)hipEventRecord(e->ev[3], fs);
 
   // Overlapped: launch pi (its build, worker-list init and search) runs on side
-  // stream pi mod MCE_SIDE_STREAMS, after everything queued on s so far, and s
-  // waits for every side stream used before the read-back.
+  // stream pi mod MCE_SIDE_STREAMS, after everything queued so far on the
+  // stream the set-up ran on, and s waits for every side stream used before the
+  // read-back.
   bool side_used[MCE_SIDE_STREAMS] = {};
   bool side_forked[MCE_SIDE_STREAMS] = {};
-  // with the early launch on side stream 0: the launch with the most table
-  // words (the longest chain) gets side stream 1 to itself, and the others
-  // take streams 2 and 0 in turn (three side streams, so that with the
+  // with the hand-over order (set up on side stream 0): the launch with the
+  // most table words (the longest chain) gets side stream 1 to itself, and the
+  // others take streams 2 and 0 in turn (three side streams, so that with the
   // caller's stream no two share a hardware queue)
-  const bool early_side = n1 > 0;
-  if (early_side) side_used[0] = true;
+  if (handover) side_used[0] = true;
   int heavy = -1;
-  if (early_side) {
+  if (handover) {
     u64 best = 0;
     for (int i = 0; i < nplan; i++) {
-      const u64 w = hctl->sub_words[var][plan[i].sub];
+      const u64 w = tc->sub_words[var][plan[i].sub];
       if (plan[i].sub != MCE_SUB_MICRO && w >= best) {
         best = w;
         heavy = i;
@@ -807,16 +725,16 @@ mce_status run_once(mce_engine* e, int32_t n, int64_t nnz, const int32_t* row_pt
   // compute units, and the search behind it waits too)
   if (overlap) {
     for (int pi = 0, so = 0; pi < nplan; pi++) {
-      if ((h = mce_launch_wl_init(dp<MceWl>(B.wl) + pi, plan[pi].nw, dp<u64>(B.stats) + (size_t)so * MCE_NSTAT, s)) !=
-          hipSuccess)
+      if ((h = mce_launch_wl_init(dp<MceWl>(B.wl) + pi, plan[pi].nw, dp<u64>(B.stats) + (size_t)so * MCE_NSTAT,
+                                  fs)) != hipSuccess)
         return hip_fail(e, h, "wl init");
       so += plan[pi].nw;
     }
   }
-  if (overlap && nplan > 0 && (h = hipEventRecord(e->fork_ev, s)) != hipSuccess) return hip_fail(e, h, "fork");
+  if (overlap && nplan > 0 && (h = hipEventRecord(e->fork_ev, fs)) != hipSuccess) return hip_fail(e, h, "fork");
 
   int launches = 0, max_workers_used = 0, stat_off = 0;
-  int evi = n1 > 0 ? 8 : 4;   // the early launch has events 4..7
+  int evi = 4;
   for (int pi = 0; pi < nplan; pi++) {
     const Plan& pl = plan[pi];
     const int c = pl.sub;
@@ -824,7 +742,7 @@ mce_status run_once(mce_engine* e, int32_t n, int64_t nnz, const int32_t* row_pt
     hipStream_t ls = s;
     if (overlap) {
       int k = pi % MCE_SIDE_STREAMS;
-      if (early_side) k = pi == heavy ? 1 : ((next_other++ & 1) == 0 ? 2 : 0);
+      if (handover) k = pi == heavy ? 1 : ((next_other++ & 1) == 0 ? 2 : 0);
       ls = e->side[k];
       if (!side_forked[k]) {
         if ((h = hipStreamWaitEvent(ls, e->fork_ev, 0)) != hipSuccess) return launch_fail(h, "fork");
@@ -833,12 +751,12 @@ mce_status run_once(mce_engine* e, int32_t n, int64_t nnz, const int32_t* row_pt
       }
     }
     u64* heap = dp<u64>(B.heap) + heap_base[c];
-    const size_t hwords = overlap ? (size_t)hctl->sub_words[var][c] : heap_words;
+    const size_t hwords = overlap ? (size_t)tc->sub_words[var][c] : heap_words;
     MceWl* wl = dp<MceWl>(B.wl) + (overlap ? pi : 0);
     BuildParams bp{};
     bp.rp = row_ptr;
     bp.ci = col_idx;
-    bp.rnd = dp<int>(B.rnd);
+    bp.rnd = srnd;
     bp.roots = dp<int>(B.lists) + off.off[c];
     bp.nroots = counts[c];
     const bool micro = c == MCE_SUB_MICRO;
@@ -862,8 +780,8 @@ mce_status run_once(mce_engine* e, int32_t n, int64_t nnz, const int32_t* row_pt
       bp.parts = std::max(1, std::min(std::max(want, (nslab + 7) / 8), nslab));
     }
     if (use_fadj) {   // (B.fadj may have been allocated after the peel: read the pointers here)
-      bp.fadj = dp<int>(fadj_in1 ? B.fadj1 : B.fadj);
-      bp.fdeg = dp<int>(fadj_in1 ? B.fdeg1 : B.fdeg);
+      bp.fadj = fadj_p;
+      bp.fdeg = fdeg_p;
     }
     if (timing) (void)hipEventRecord(e->ev[evi], ls);
     if ((h = mce_launch_build(bp, e->num_cu * 32, ls)) != hipSuccess) return launch_fail(h, "build launch");
@@ -955,6 +873,11 @@ mce_status run_once(mce_engine* e, int32_t n, int64_t nnz, const int32_t* row_pt
     return hip_fail(e, h, "result readback");
   if ((h = hipStreamSynchronize(s)) != hipSuccess) return hip_fail(e, h, "synchronize at end");
   const u64* hres = reinterpret_cast<const u64*>(hio + sizeof(MceCtl));
+  if (handover) {   // the tail has ended: the peel's order is complete
+    e->info.degeneracy = hctl->degeneracy;
+    e->info.rounds = hctl->rounds;
+    e->have_order = true;
+  }
   if (hctl->status & MCE_E_PROTO) return fail(e, MCE_ERR_DEVICE, "worker-list bookkeeping error");
   if (hctl->status & MCE_E_LIMIT) return fail(e, MCE_ERR_LIMIT, "a subtree larger than its width class");
   if (hctl->status & MCE_E_MSTACK) {
@@ -985,38 +908,30 @@ mce_status run_once(mce_engine* e, int32_t n, int64_t nnz, const int32_t* row_pt
   {
     int64_t started = 0;
     for (int i = 0; i < launches; i++) started += std::min<int64_t>(hctl->taken[i], counts[plan[i].sub]);
-    if (n1 > 0) started += std::min<int64_t>(hctl->taken[kTakenEarly], n1);
     // roots that need no search: isolated vertices, and second-level roots that are cliques of size 2
-    started += (int64_t)nsub - total - n1;
+    started += (int64_t)nsub - total;
     e->info.roots_started = started;
   }
 
   mce_run_stats& so = e->stats_out;
-  so.workers = std::max(max_workers_used, early_nw);
-  const int e0 = n1 > 0 ? 1 : 0;   // the early launch comes first in the launch lists
-  so.launches = launches + e0;
-  so.early_launch = e0;
-  u64 words_built = words1;
-  for (int i = 0; i < nplan; i++) words_built += hctl->sub_words[var][plan[i].sub];
+  so.workers = max_workers_used;
+  so.launches = launches;
+  so.handover_round = handover ? tc->tail_r0 : -1;
+  u64 words_built = 0;
+  for (int i = 0; i < nplan; i++) words_built += tc->sub_words[var][plan[i].sub];
   so.table_words = words_built;
-  e->n_last_plan = nplan + e0;
-  if (e0) {
-    e->last_plan[0] = {MCE_SUB_MICRO, early_nw, n1, true};
-    so.launch_sub[0] = MCE_SUB_MICRO;
-    so.launch_roots[0] = n1;
-    so.launch_words[0] = words1;
-  }
+  e->n_last_plan = nplan;
   for (int i = 0; i < nplan; i++) {
-    e->last_plan[e0 + i] = {plan[i].sub, plan[i].nw, counts[plan[i].sub], false};
-    if (e0 + i < 16) {
-      so.launch_sub[e0 + i] = plan[i].sub;
-      so.launch_roots[e0 + i] = counts[plan[i].sub];
-      so.launch_words[e0 + i] = hctl->sub_words[var][plan[i].sub];
+    e->last_plan[i] = {plan[i].sub, plan[i].nw, counts[plan[i].sub]};
+    if (i < 16) {
+      so.launch_sub[i] = plan[i].sub;
+      so.launch_roots[i] = counts[plan[i].sub];
+      so.launch_words[i] = tc->sub_words[var][plan[i].sub];
     }
   }
   for (int i = 0; i < 4; i++) so.peel_ticks[i] = hctl->peel_ticks[i];
-  so.micro_roots = counts[MCE_SUB_MICRO] + n1;
-  so.micro_stack_cap = micro_nw || early_nw ? micro_cap : 0;
+  so.micro_roots = counts[MCE_SUB_MICRO];
+  so.micro_stack_cap = micro_nw ? micro_cap : 0;
   e->last_stat_rows = stat_rows;
   e->last_timing = timing;
   e->last_stimes = stimes;
@@ -1025,7 +940,6 @@ mce_status run_once(mce_engine* e, int32_t n, int64_t nnz, const int32_t* row_pt
     mce_engine::TableMap& tm = e->tabs;
     tm.mode = mode;
     tm.total = total;
-    tm.early = n1;
     for (int c = 0; c < MCE_NSUB; c++) {
       tm.off[c] = off.off[c];
       tm.count[c] = counts[c];
@@ -1062,14 +976,6 @@ mce_status collect_stats(mce_engine* e) {
   if (!st.empty() && (h = hipMemcpy(st.data(), e->last->stats.p, st.size() * sizeof(u64), hipMemcpyDeviceToHost)) !=
                          hipSuccess)
     return hip_fail(e, h, "stats readback");
-  // the split peel's early launch keeps its rows apart
-  std::vector<u64> st1;
-  if (e->n_last_plan > 0 && e->last_plan[0].early) {
-    st1.resize((size_t)e->last_plan[0].nw * MCE_NSTAT);
-    if ((h = hipMemcpy(st1.data(), e->last->stats1.p, st1.size() * sizeof(u64), hipMemcpyDeviceToHost)) !=
-        hipSuccess)
-      return hip_fail(e, h, "stats readback");
-  }
   mce_run_stats& so = e->stats_out;
   std::vector<u64> stat_sum(MCE_NSTAT, 0);
   e->trace.clear();
@@ -1079,7 +985,7 @@ mce_status collect_stats(mce_engine* e) {
     const auto& pl = e->last_plan[li];
     u64 smin = ~0ull, smax = 0;
     for (int w = 0; w < pl.nw; w++) {
-      const u64* r = pl.early ? &st1[(size_t)w * MCE_NSTAT] : &st[(size_t)(row++) * MCE_NSTAT];
+      const u64* r = &st[(size_t)(row++) * MCE_NSTAT];
       mce_worker_record rec{};
       rec.launch = (int32_t)li;
       rec.worker = w;
@@ -1244,8 +1150,7 @@ mce_status mce_create(const mce_config* cfg, mce_engine** out) {
     side_ok = side_ok && hipStreamCreateWithFlags(&e->side[k], hipStreamNonBlocking) == hipSuccess;
     side_ok = side_ok && hipEventCreateWithFlags(&e->join_ev[k], hipEventDisableTiming) == hipSuccess;
   }
-  side_ok = side_ok && hipEventCreateWithFlags(&e->handed_ev, hipEventDisableTiming) == hipSuccess &&
-            hipEventCreateWithFlags(&e->early_built_ev, hipEventDisableTiming) == hipSuccess;
+  side_ok = side_ok && hipEventCreateWithFlags(&e->handed_ev, hipEventDisableTiming) == hipSuccess;
   if (!side_ok) {
     mce_destroy(e);
     return MCE_ERR_DEVICE;
@@ -1307,41 +1212,6 @@ mce_status mce_root_table(const mce_engine* e, int32_t root, uint64_t* words, in
   if (!tm.valid || root < 0 || root >= e->last_n) return MCE_ERR_STATE;
   if (hipSetDevice(e->device) != hipSuccess) return MCE_ERR_DEVICE;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  // a split peel's early root: a micro table in the early launch's heap
-  if (tm.early > 0) {
-    std::vector<int32_t> l1((size_t)tm.early);
-    if (hipMemcpyAsync(l1.data(), e->own.lists1.p, (size_t)tm.early * sizeof(int32_t), hipMemcpyDeviceToHost, s) !=
-            hipSuccess ||
-        hipStreamSynchronize(s) != hipSuccess)
-      return MCE_ERR_DEVICE;
-    int i1 = -1;
-    for (int j = 0; j < tm.early; j++)
-      if (l1[j] == root) {
-        i1 = j;
-        break;
-      }
-    if (i1 >= 0) {
-      u64 to[2] = {0, 0};
-      const u64* taboff1 = static_cast<const u64*>(e->own.taboff1.p);
-      if (hipMemcpyAsync(&to[0], taboff1 + i1, sizeof(u64), hipMemcpyDeviceToHost, s) != hipSuccess ||
-          hipMemcpyAsync(&to[1], taboff1, sizeof(u64), hipMemcpyDeviceToHost, s) != hipSuccess ||
-          hipStreamSynchronize(s) != hipSuccess)
-        return MCE_ERR_DEVICE;
-      const u64* T = static_cast<const u64*>(e->own.heap1.p) + (to[0] - to[1]);
-      u64 hdr = 0;
-      if (hipMemcpyAsync(&hdr, T, sizeof(u64), hipMemcpyDeviceToHost, s) != hipSuccess ||
-          hipStreamSynchronize(s) != hipSuccess)
-        return MCE_ERR_DEVICE;
-      const u64 nw = mce_micro_table_words((int)(u32)hdr, (int)(hdr >> 32));
-      *len = (int64_t)nw;
-      *form = 1 | (1 << 8) | (1 << 9);
-      if ((u64)cap < nw) return MCE_ERR_ARG;
-      if (hipMemcpyAsync(words, T, nw * sizeof(u64), hipMemcpyDeviceToHost, s) != hipSuccess ||
-          hipStreamSynchronize(s) != hipSuccess)
-        return MCE_ERR_DEVICE;
-      return MCE_OK;
-    }
-  }
   // the root's place in the bucketed root lists, hence its sub-class
   std::vector<int32_t> lists((size_t)std::max(tm.total, 1));
   if (tm.total > 0 && (hipMemcpyAsync(lists.data(), e->own.lists.p, (size_t)tm.total * sizeof(int32_t),
@@ -1446,7 +1316,7 @@ void mce_destroy(mce_engine* e) {
                     &b.wl,     &b.slots,  &b.stats,   &b.mstack,  &b.mail,   &b.src,     &b.fwd,    &b.fwdtmp,
                     &b.eroots, &b.pcount2, &b.xcount2, &b.hub_id, &b.hub_v,  &b.hub_bm, &b.fadj, &b.fdeg, &b.flong,
                     &b.tcol,   &b.tcrow,  &b.ctl1,    &b.snap,    &b.fadj1,   &b.fdeg1,  &b.flong1,  &b.pcount1, &b.xcount1,
-                    &b.lists1, &b.taboff1, &b.scan1,  &b.heap1,   &b.mstack1, &b.mail1,  &b.stats1};
+                    &b.srank};
   for (DevBuf* d : bufs) release(*d);
   if (e->host.p) (void)hipHostFree(e->host.p);
   if (e->host1.p) (void)hipHostFree(e->host1.p);
@@ -1456,7 +1326,6 @@ void mce_destroy(mce_engine* e) {
     if (ev) (void)hipEventDestroy(ev);
   if (e->fork_ev) (void)hipEventDestroy(e->fork_ev);
   if (e->handed_ev) (void)hipEventDestroy(e->handed_ev);
-  if (e->early_built_ev) (void)hipEventDestroy(e->early_built_ev);
   for (auto& st : e->side)
     if (st) (void)hipStreamDestroy(st);
   delete e;

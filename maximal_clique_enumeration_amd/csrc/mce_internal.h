@@ -187,9 +187,6 @@ struct BuildParams {
   // after v in the peel order at fadj[rp[v] .. rp[v] + fdeg[v]), in id order
   const int* fadj;
   const int* fdeg;
-  // a split peel's early roots (micro build only), the tail still running:
-  // its hand-over snapshot (1: still in the tail, hence later than the root)
-  const unsigned char* snap;
 };
 
 // Clears words u64 at p.
@@ -214,31 +211,27 @@ int mce_peel_max_blocks(int num_cu);
 // the second-level roots are tallied by mce_launch_l2_roots.
 // Forward adjacency: fadj[rp[v] .. rp[v] + fdeg[v]) = the neighbours of v after
 // v in the peel order, in id order. flong: n ints of scratch (the long rows' list).
-// tctl, snap, hdeg (a split peel's control block, hand-over snapshot and the
-// degrees it handed over, its tail still running): the same for the vertices
-// that left before the tail, a vertex still in it ranking after all of them and
-// getting its neighbours in the tail that come after it by (degree, id)
-// (nothing if the grid handed no tail over); ctl then only holds the long rows'
-// count. only_tail (with snap alone): after the tail, the final rows of the
-// vertices it held, written over their early rows (the others' are final).
+// tctl (a split peel's control block): nothing is done unless its grid handed
+// a tail over (rnd is then the hand-over order's ranks, mce_launch_search_rank).
 hipError_t mce_launch_forward_adj(int n, const int* rp, const int* ci, const int* rnd, int* fadj, int* fdeg,
-                                  int* flong, MceCtl* ctl, int blocks, hipStream_t s, const MceCtl* tctl = nullptr,
-                                  const unsigned char* snap = nullptr, const int* hdeg = nullptr, int only_tail = 0);
+                                  int* flong, MceCtl* ctl, int blocks, hipStream_t s, const MceCtl* tctl = nullptr);
+// A split peel's hand-over order as ranks compared like rounds (srank, n ints):
+// the round of a vertex gone before the tail; r0 + the degree handed over for a
+// vertex still in it (snap 1). Nothing if the grid handed no tail over.
+hipError_t mce_launch_search_rank(int n, const int* rnd, const int* deg, const unsigned char* snap,
+                                  const MceCtl* tctl, int* srank, int blocks, hipStream_t s);
 // fdeg: the forward adjacency's row lengths, when every vertex is a root of a
 // first-level run (roots == NULL, fwd == NULL): |P| is read from it.
-// skip_early (whole-graph first-level runs with fdeg): a split peel's early
-// roots (see mce_launch_orient_early) get pcount = xcount = 0 here.
 hipError_t mce_launch_orient(int n, const int* rp, const int* ci, const int* rnd, const int* roots, int nroots,
                              int* pcount, int* xcount, MceCtl* ctl, u64* fwd, const int* fdeg, int blocks,
-                             hipStream_t s, int skip_early = 0);
-// A split peel's early roots: the vertices gone before the tail (not in the
-// hand-over snapshot snap; tctl, the run's control block) with micro-sized subtrees, |P| from the early forward
-// adjacency's fdeg; |P| and |X| into pcount / xcount (n each, 0 for the other
-// vertices), tallied into ctl (a control block of their own, which also gets
-// tctl's tail_go and tail_r0).
-hipError_t mce_launch_orient_early(int n, const int* rp, const unsigned char* snap, const int* fdeg,
-                                   const MceCtl* tctl, int* pcount, int* xcount, MceCtl* ctl, int blocks,
-                                   hipStream_t s);
+                             hipStream_t s);
+// The roots of a split peel's hand-over order (fdeg: its forward degrees), all
+// of them: |P| and |X| into pcount / xcount (n each), the sub-class tallies,
+// largest |P| / |X|, isolated vertices into ctl (a control block of its own),
+// with tctl's tail_go, tail_r0, max_degree and the level reached (as
+// `degeneracy`) copied there.
+hipError_t mce_launch_orient_handover(int n, const int* rp, const int* fdeg, const MceCtl* tctl, int* pcount,
+                                      int* xcount, MceCtl* ctl, int blocks, hipStream_t s);
 // Second-level roots (Algorithm 4) of the vertex roots: COO sources (src, nnz),
 // the forward edges as CSR positions (eroots, at most nnz; their number goes to
 // ctl->l2_roots), and per root |P| and |X| (pcount, xcount) and the tallies.

@@ -1939,14 +1939,11 @@ __device__ __forceinline__ void tally_roots(TallyAcc& acc, bool valid, int p, in
 __global__ __launch_bounds__(256) void k_orient(int n, const int* __restrict__ rp, const int* __restrict__ ci,
                                                  const int* __restrict__ rnd, const int* __restrict__ roots,
                                                  int nroots, int* pcount, int* xcount, MceCtl* ctl, u64* fwd,
-                                                 const int* __restrict__ fdeg, int tally, int per_wave, u32 mul,
-                                                 int skip_early) {
+                                                 const int* __restrict__ fdeg, int tally, int per_wave, u32 mul) {
   __shared__ TallyAcc s_tally;
   __shared__ int s_ok;
   if (!tally_begin(s_tally, &s_ok, ctl)) return;
-  // a split peel's early roots (left before the tail, micro-sized) are searched
-  // by their own launch: neither bucketed nor tallied here
-  const int r0 = skip_early && ctl->tail_go ? ctl->tail_r0 : -1;
+
   const int lane = lane_id();
   const int gsize = gridDim.x * blockDim.x;
   const int cnt = nroots;   // roots == NULL: the identity list 0..nroots-1
@@ -2045,9 +2042,8 @@ __global__ __launch_bounds__(256) void k_orient(int n, const int* __restrict__ r
       }
       if (inr) {
         x = (b - a) - p;
-        const bool early = rv < r0 && p >= 1 && mce_is_micro(p, x);
-        pcount[i] = early ? 0 : p;
-        xcount[i] = early ? 0 : x;
+        pcount[i] = p;
+        xcount[i] = x;
         if (fwd) fwd[i] = (u64)p;
         if (b == a) {
           iso++;
@@ -2057,7 +2053,7 @@ __global__ __launch_bounds__(256) void k_orient(int n, const int* __restrict__ r
         xmax = max(xmax, x);
         dmax = max(dmax, b - a);
         if (tally && p > MCE_MAX_P) lim |= 1u;
-        valid = !early && p > 0 && p <= MCE_MAX_P;
+        valid = p > 0 && p <= MCE_MAX_P;
       } else if (i < cnt && fwd) {
         fwd[i] = 0;
       }
@@ -2098,40 +2094,16 @@ __global__ __launch_bounds__(256) void k_orient(int n, const int* __restrict__ r
 // thousands of entries on power-law graphs, kept one wavefront busy for
 // milliseconds).
 //
-// With tctl and snap (a split peel's control block and hand-over snapshot,
-// its tail still running): the forward rows of the vertices that left before
-// the tail, where every vertex still in the tail (snap 1; its round is not
-// read, as the tail writes it meanwhile) ranks after them, and, for a vertex
-// still in the tail, its neighbours in the tail that come after it by (degree
-// at the hand-over, id): every edge of the residual graph once, in the row of
-// its end of smaller degree, so that a hub's row stays short (the tail keeps
-// its degrees in LDS and leaves deg as it was handed over). Nothing is done
-// when the grid peeled to the end.
+// With tctl (a split peel's control block): nothing is done unless the grid
+// handed a tail over (the rows are then those of the hand-over order, rnd being
+// its ranks, see k_search_rank).
 #define FWD_LONG 1024
-#define FWD_TAIL 0x7FFFFFFF   // the rank of a vertex still in the tail
-
-__device__ __forceinline__ int fwd_rank(const int* rnd, const unsigned char* snap, int u) {
-  return snap && snap[u] ? FWD_TAIL : rnd[u];
-}
-
-// Is u after v? rv = fwd_rank(v), dv = v's degree at the hand-over if rv is FWD_TAIL.
-__device__ __forceinline__ bool fwd_later(const int* rnd, const unsigned char* snap, const int* deg, int u, int rv,
-                                          int dv, int v) {
-  const int ru = fwd_rank(rnd, snap, u);
-  if (ru == FWD_TAIL && rv == FWD_TAIL) {
-    const int du = deg[u];
-    return du > dv || (du == dv && u > v);
-  }
-  return order_after(ru, u, rv, v);
-}
 
 __global__ __launch_bounds__(256) void k_forward_adj(int n, const int* __restrict__ rp, const int* __restrict__ ci,
                                                       const int* __restrict__ rnd, int* __restrict__ fadj,
                                                       int* __restrict__ fdeg, int* __restrict__ flong, MceCtl* ctl,
-                                                      const MceCtl* tctl, const unsigned char* __restrict__ snap,
-                                                      const int* __restrict__ hdeg, int only_tail) {
+                                                      const MceCtl* tctl) {
   if (tctl && !tctl->tail_go) return;
-  const unsigned char* rs = only_tail ? nullptr : snap;   // ranks from the snapshot: the early rows
   // the block's long rows, listed in LDS and added to the list with one atomic
   // (one per row on the shared count took a 4M-vertex graph's ~20k hub rows
   // about 0.3 ms); a block with more than FWD_LCAP of them lists the rest
@@ -2144,9 +2116,7 @@ __global__ __launch_bounds__(256) void k_forward_adj(int n, const int* __restric
   const int lane = lane_id();
   const int nwaves = gridDim.x * (blockDim.x / MCE_WAVE);
   for (int v = blockIdx.x * (blockDim.x / MCE_WAVE) + threadIdx.x / MCE_WAVE; v < n; v += nwaves) {
-    if (only_tail && !snap[v]) continue;
-    const int a = rp[v], b = rp[v + 1], rv = fwd_rank(rnd, rs, v);
-    const int dv = rv == FWD_TAIL ? hdeg[v] : 0;
+    const int a = rp[v], b = rp[v + 1], rv = rnd[v];
     if (b - a > FWD_LONG) {
       if (lane == 0) {
         const int q = atomicAdd(&s_nl, 1);
@@ -2159,7 +2129,7 @@ __global__ __launch_bounds__(256) void k_forward_adj(int n, const int* __restric
     for (int base = a; base < b; base += MCE_WAVE) {
       const int e = base + lane;
       const int u = e < b ? ci[e] : 0;
-      const bool later = e < b && fwd_later(rnd, rs, hdeg, u, rv, dv, v);
+      const bool later = e < b && order_after(rnd[u], u, rv, v);
       const u64 m = ballot(later);
       if (later) fadj[a + k + mbcnt(m)] = u;
       k += __popcll(m);
@@ -2180,19 +2150,15 @@ __global__ __launch_bounds__(256) void k_forward_adj(int n, const int* __restric
 __global__ __launch_bounds__(256) void k_forward_adj_long(const int* __restrict__ rp, const int* __restrict__ ci,
                                                            const int* __restrict__ rnd, int* __restrict__ fadj,
                                                            int* __restrict__ fdeg, const int* __restrict__ flong,
-                                                           MceCtl* ctl, const MceCtl* tctl,
-                                                           const unsigned char* __restrict__ snap,
-                                                           const int* __restrict__ hdeg, int only_tail) {
+                                                           MceCtl* ctl, const MceCtl* tctl) {
   constexpr int NW = 256 / MCE_WAVE;
   __shared__ int s_cnt[4][NW];
   if (tctl && !tctl->tail_go) return;
-  const unsigned char* rs = only_tail ? nullptr : snap;
   const int lane = lane_id(), wv = threadIdx.x / MCE_WAVE;
   const int nl = ld_relaxed(&ctl->nlong);
   for (int j = blockIdx.x; j < nl; j += gridDim.x) {
     const int v = flong[j];
-    const int a = rp[v], b = rp[v + 1], rv = fwd_rank(rnd, rs, v);
-    const int dv = rv == FWD_TAIL ? hdeg[v] : 0;
+    const int a = rp[v], b = rp[v + 1], rv = rnd[v];
     int k = 0;   // entries placed so far (the same in every thread)
     for (int base = a; base < b; base += 4 * 256) {
       int u[4];
@@ -2206,7 +2172,7 @@ __global__ __launch_bounds__(256) void k_forward_adj_long(const int* __restrict_
 #pragma unroll
       for (int z = 0; z < 4; z++) {
         const int e = base + z * 256 + (int)threadIdx.x;
-        lat[z] = e < b && fwd_later(rnd, rs, hdeg, u[z], rv, dv, v);
+        lat[z] = e < b && order_after(rnd[u[z]], u[z], rv, v);
       }
 #pragma unroll
       for (int z = 0; z < 4; z++) {
@@ -2248,42 +2214,82 @@ __global__ __launch_bounds__(256) void k_tally(int nroots, const int* __restrict
   tally_end(s_tally, ctl);
 }
 
-// A split peel's early roots: the vertices that left before the tail, whose
-// later neighbours are already known (every vertex still in the tail is later),
-// with micro-sized subtrees (|P| = fdeg from the early forward adjacency). Their
-// |P| and |X| go to pcount / xcount (0 for every other vertex) and they are
-// tallied into `ctl` (a control block of their own); the grid's hand-over
-// fields are copied there for the host. A vertex is early when the hand-over
-// snapshot does not hold it (no round is read: the tail writes its vertices'
-// meanwhile).
-__global__ __launch_bounds__(256) void k_orient_early(int n, const int* __restrict__ rp,
-                                                      const unsigned char* __restrict__ snap,
-                                                      const int* __restrict__ fdeg, const MceCtl* tctl,
-                                                      int* pcount, int* xcount, MceCtl* ctl) {
+// A split peel's hand-over order, as ranks compared like rounds (rank, then
+// id): a vertex gone before the tail keeps its round; a vertex still in the
+// tail (snap 1) gets r0 + its degree in the remaining graph (deg, which the
+// tail leaves as it was handed over), so it comes after every vertex gone and,
+// among the tail's, by that degree, then id. Every maximal clique is reported
+// once under any vertex order (the subtree of its first vertex, section 2.4);
+// the degeneracy order is what bounds |P|, and the hand-over order keeps it
+// where the peel left off. The round of a tail vertex is not read: the tail
+// writes it meanwhile.
+__global__ __launch_bounds__(256) void k_search_rank(int n, const int* __restrict__ rnd, const int* __restrict__ deg,
+                                                     const unsigned char* __restrict__ snap, const MceCtl* tctl,
+                                                     int* srank) {
+  if (!tctl->tail_go) return;
+  const int r0 = tctl->tail_r0;
+  for (int v = blockIdx.x * blockDim.x + threadIdx.x; v < n; v += gridDim.x * blockDim.x)
+    srank[v] = snap[v] ? r0 + deg[v] : rnd[v];
+}
+
+// The roots of a split peel's hand-over order (every vertex gone before the
+// tail by its round, then the tail's vertices by their degree in the remaining
+// graph, then id: the order of the early forward adjacency, whose fdeg is |P|).
+// Like k_orient's thread-per-root pass: |P| and |X| of every vertex into pcount /
+// xcount, the sub-class tallies, the largest |P|, |X| and degree, the isolated
+// vertices (maximal cliques of one) into `ctl` (a control block of its own),
+// with the grid's hand-over facts copied there for the host: tail_go, tail_r0,
+// and the level reached (a lower bound of the degeneracy) in `degeneracy`.
+__global__ __launch_bounds__(256) void k_orient_handover(int n, const int* __restrict__ rp,
+                                                         const int* __restrict__ fdeg, const MceCtl* tctl,
+                                                         int* pcount, int* xcount, MceCtl* ctl) {
   __shared__ TallyAcc s_tally;
   __shared__ int s_ok;
   if (!tally_begin(s_tally, &s_ok, ctl)) return;
   const int go = tctl->tail_go;
-  const int r0 = go ? tctl->tail_r0 : -1;
   if (blockIdx.x == 0 && threadIdx.x == 0) {
     ctl->tail_go = go;
-    ctl->tail_r0 = r0;
+    ctl->tail_r0 = go ? tctl->tail_r0 : -1;
+    ctl->degeneracy = go ? tctl->tail_st[0] : 0;
+    ctl->max_degree = tctl->max_degree;
   }
+  if (!go) return;   // (a block-uniform exit: every thread read the same word)
+  const int lane = lane_id();
+  u64 iso = 0, iso_hash = 0;
+  int pmax = 0, xmax = 0;
+  u32 lim = 0;
   const int gsize = gridDim.x * blockDim.x;
   for (int base = blockIdx.x * blockDim.x; base < n; base += gsize) {
     const int v = base + threadIdx.x;
     int p = 0, x = 0;
-    bool take = false;
-    if (v < n && r0 >= 0 && !snap[v]) {
+    if (v < n) {
       p = fdeg[v];
       x = (rp[v + 1] - rp[v]) - p;
-      take = p >= 1 && mce_is_micro(p, x);
+      pcount[v] = p;
+      xcount[v] = x;
+      if (p == 0 && x == 0) {
+        iso++;
+        iso_hash += mce_clique_term(mce_vertex_term(v), 1);
+      }
+      pmax = max(pmax, p);
+      xmax = max(xmax, x);
+      if (p > MCE_MAX_P) lim |= 1u;
     }
-    if (v < n) {
-      pcount[v] = take ? p : 0;
-      xcount[v] = take ? x : 0;
+    tally_roots(s_tally, p > 0 && p <= MCE_MAX_P, p, x);
+  }
+  const u64 wiso = wave_sum_u64(iso);
+  const u64 whash = wave_sum_u64(iso_hash);
+  const u32 wpm = wave_max_u32((u32)pmax);
+  const u32 wxm = wave_max_u32((u32)xmax);
+  const u32 wl = wave_or_u32(lim);
+  if (lane == 0) {
+    if (wiso) {
+      atomicAdd(&ctl->isolated, wiso);
+      atomicAdd(&ctl->isolated_hash, whash);
     }
-    tally_roots(s_tally, take, p, x);
+    atomicMax(&ctl->max_p, (int)wpm);
+    atomicMax(&ctl->max_x, (int)wxm);
+    if (wl & 1u) atomicOr(&ctl->status, MCE_E_LIMIT);
   }
   tally_end(s_tally, ctl);
 }
@@ -2618,18 +2624,23 @@ hipError_t mce_launch_l2_roots(int n, long long nnz, const int* rp, const int* c
   return hipGetLastError();
 }
 
-hipError_t mce_launch_orient_early(int n, const int* rp, const unsigned char* snap, const int* fdeg,
-                                   const MceCtl* tctl, int* pcount, int* xcount, MceCtl* ctl, int blocks,
-                                   hipStream_t s) {
+hipError_t mce_launch_search_rank(int n, const int* rnd, const int* deg, const unsigned char* snap,
+                                  const MceCtl* tctl, int* srank, int blocks, hipStream_t s) {
+  const int nb = max(1, min(blocks, (n + 255) / 256));
+  hipLaunchKernelGGL(k_search_rank, dim3(nb), dim3(256), 0, s, n, rnd, deg, snap, tctl, srank);
+  return hipGetLastError();
+}
+
+hipError_t mce_launch_orient_handover(int n, const int* rp, const int* fdeg, const MceCtl* tctl, int* pcount,
+                                      int* xcount, MceCtl* ctl, int blocks, hipStream_t s) {
   const int nb = max(1, min(max(1, blocks / 8), (n + 255) / 256));
-  hipLaunchKernelGGL(k_orient_early, dim3(nb), dim3(256), 0, s, n, rp, snap, fdeg, tctl, pcount, xcount, ctl);
+  hipLaunchKernelGGL(k_orient_handover, dim3(nb), dim3(256), 0, s, n, rp, fdeg, tctl, pcount, xcount, ctl);
   return hipGetLastError();
 }
 
 hipError_t mce_launch_orient(int n, const int* rp, const int* ci, const int* rnd, const int* roots, int nroots,
                              int* pcount, int* xcount, MceCtl* ctl, u64* fwd, const int* fdeg, int blocks,
-                             hipStream_t s, int skip_early) {
-  if (skip_early && !fdeg) return hipErrorInvalidValue;
+                             hipStream_t s) {
   if (fdeg && (roots || fwd || nroots != n)) return hipErrorInvalidValue;   // every vertex a root, first level
   // at most one root per wavefront of the grid: a wavefront per root, on at most
   // 256 wavefronts (every wavefront ends with a few atomics on the same words:
@@ -2641,7 +2652,7 @@ hipError_t mce_launch_orient(int n, const int* rp, const int* ci, const int* rnd
   const int tb = fdeg ? max(1, blocks / 8) : blocks;
   const int nb = per_wave ? max(1, min(64, (nroots + 3) / 4)) : max(1, min(tb, (nroots + 255) / 256));
   hipLaunchKernelGGL(k_orient, dim3(nb), dim3(256), 0, s, n, rp, ci, rnd, roots, nroots, pcount, xcount, ctl, fwd,
-                     fdeg, fwd ? 0 : 1, per_wave, ORIENT_MUL, skip_early);
+                     fdeg, fwd ? 0 : 1, per_wave, ORIENT_MUL);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || !per_wave || fwd) return e;
   hipLaunchKernelGGL(k_tally, dim3(max(1, min(blocks, (nroots + 255) / 256))), dim3(256), 0, s, nroots, pcount,
@@ -2650,16 +2661,13 @@ hipError_t mce_launch_orient(int n, const int* rp, const int* ci, const int* rnd
 }
 
 hipError_t mce_launch_forward_adj(int n, const int* rp, const int* ci, const int* rnd, int* fadj, int* fdeg,
-                                  int* flong, MceCtl* ctl, int blocks, hipStream_t s, const MceCtl* tctl,
-                                  const unsigned char* snap, const int* hdeg, int only_tail) {
-  if (only_tail ? (tctl || hdeg || !snap) : (!tctl != !snap || !tctl != !hdeg)) return hipErrorInvalidValue;
+                                  int* flong, MceCtl* ctl, int blocks, hipStream_t s, const MceCtl* tctl) {
   const int nb = max(1, min(blocks, (n + 3) / 4));   // four wavefronts a block, one vertex each at a time
-  hipLaunchKernelGGL(k_forward_adj, dim3(nb), dim3(256), 0, s, n, rp, ci, rnd, fadj, fdeg, flong, ctl, tctl, snap,
-                     hdeg, only_tail);
+  hipLaunchKernelGGL(k_forward_adj, dim3(nb), dim3(256), 0, s, n, rp, ci, rnd, fadj, fdeg, flong, ctl, tctl);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(k_forward_adj_long, dim3(max(1, blocks)), dim3(256), 0, s, rp, ci, rnd, fadj, fdeg, flong, ctl,
-                     tctl, snap, hdeg, only_tail);
+                     tctl);
   return hipGetLastError();
 }
 

@@ -174,10 +174,7 @@ __global__ __launch_bounds__(64) void k_build_micro(BuildParams prm) {
       const int e = base + lane;
       const int u = e < b ? ci[e] : 0;
       const bool valid = e < b && hood_has(ci, hd, u);
-      // (a split peel's early root: a neighbour still in the tail is later, and
-      // its round, which the tail may be writing, is not read)
-      const int ru = prm.snap && prm.snap[u] ? 0x7FFFFFFF : rnd[u];
-      const bool lat = valid && order_after(ru, u, hd.pivr, hd.piv);
+      const bool lat = valid && order_after(rnd[u], u, hd.pivr, hd.piv);
       const u64 lm = ballot(lat), xm = ballot(valid && !lat);
       if (lat && np + mbcnt(lm) < MCE_MICRO_MAX) s_id[np + mbcnt(lm)] = u;
       if (valid && !lat && nx + mbcnt(xm) < MCE_MICRO_MAX) s_id[MCE_MICRO_MAX + nx + mbcnt(xm)] = u;

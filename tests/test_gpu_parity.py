@@ -175,11 +175,13 @@ def test_ordering_matches_oracle(eng, make):
 
 
 # ------------------------------------------------------------------ split peel
-def test_split_peel_early_launch():
+def test_split_peel_handover_order():
     """More vertices than the peel's tail takes: the grid hands the tail to a
-    one-block launch, and the micro-sized roots gone before it are built and
-    searched meanwhile on the early stream. The cliques, the order and the
-    micro roots match the oracle and a serial run (no split), run after run."""
+    one-block launch, and the whole search runs beside it in the hand-over
+    order (the vertices gone before the tail by round, then the tail's by their
+    degree among themselves, then id). The cliques match the oracle and a serial
+    run (the peel's order), and the peel's order itself matches the oracle's,
+    run after run."""
     g = mi.chung_lu(200000, 20.0, 2.3, None, 11, planted=50)
     rp, ci = on_gpu(g)
     print(f"case {g.name} n={g.n} m={g.m}, split peel", flush=True)
@@ -193,11 +195,14 @@ def test_split_peel_early_launch():
                 assert (got.count, got.hist, got.hash) == (want.count, want.hist, want.hash)
                 core, rnd = e.ordering(g.n)
                 assert np.array_equal(core.cpu().numpy(), ocore) and np.array_equal(rnd.cpu().numpy(), ornd)
-                assert e.graph_info()["roots_started"] == g.n
+                info = e.graph_info()
+                assert info["roots_started"] == g.n and info["degeneracy"] == d
+                assert info["rounds"] == int(ornd.max()) + 1
         so, ss = eo.stats(), es.stats()
-        assert so["early_launch"] == 1 and ss["early_launch"] == 0
-        assert so["launches"] == ss["launches"] + 1 and so["launch_sub"][0] == 12
-        assert 0 < so["launch_roots"][0] < so["micro_roots"] == ss["micro_roots"]
+        r0 = so["handover_round"]
+        assert ss["handover_round"] == -1 and 0 < r0 <= int(ornd.max())
+        # the vertices still present at the hand-over: at most the tail's capacity
+        assert 0 < int((ornd >= r0).sum()) <= 65535
 
 
 # ------------------------------------------------------------------ root subsets

@@ -29,10 +29,20 @@ GRAPHS = {
     "hub_clique": lambda: mi.hub_clique(700, 4, 3000, 0.7, 12, 700),
     "hub_clique_110": lambda: mi.hub_clique(110, 4, 3000, 0.7, 12, 110),
     "hub_clique_1100": lambda: mi.hub_clique(1100, 4, 3000, 0.7, 12, 1100),
-    # more vertices than the peel's tail takes: the roots gone before the tail
-    # get their micro tables from the early launch (built while the tail runs)
+    # more vertices than the peel's tail takes: the search (and these tables)
+    # take the hand-over order, built while the tail runs
     "chung_lu_100k": lambda: mi.chung_lu(100000, 12.0, 2.3, None, 3, planted=40, planted_min=10, planted_max=30),
 }
+
+
+def handover_order(g, rnd, r0):
+    """The search's vertex ranks after a split peel at round r0 (compared like
+    rounds, then id): a vertex gone before r0 keeps its round; a vertex still
+    present gets r0 + its number of neighbours still present."""
+    src = np.repeat(np.arange(g.n), np.diff(g.row_ptr))
+    tail = rnd >= r0
+    live = np.bincount(src, weights=tail[g.col_idx] & tail[src], minlength=g.n).astype(np.int64)
+    return np.where(tail, r0 + live, rnd).astype(np.int32)
 
 
 def roots_to_check(g, rnd, k=250, seed=5):
@@ -55,12 +65,16 @@ def test_tables_equal_the_oracle_encoding(name, subgraph):
     rp = torch.from_numpy(g.row_ptr).to(DEV)
     ci = torch.from_numpy(g.col_idx).to(DEV)
     _, rnd, _ = oracle.peel(g.n, g.row_ptr, g.col_idx)
-    roots, P, X = roots_to_check(g, rnd)
     seen = set()
     with mce.Engine(device=0, timeout_ms=60000, subgraph=subgraph) as e:
         got_all = e.run(rp, ci)
         want_all = oracle.mce(g.n, g.row_ptr, g.col_idx)
         assert got_all.key() == want_all.key()
+        r0 = e.stats()["handover_round"]
+        if r0 >= 0:   # the search took the hand-over order
+            print(f"  hand-over at round {r0}: {int((rnd >= r0).sum())} vertices left", flush=True)
+            rnd = handover_order(g, rnd, r0)
+        roots, P, X = roots_to_check(g, rnd)
         for root in roots:
             t = e.root_table(root)
             if P[root] == 0:
