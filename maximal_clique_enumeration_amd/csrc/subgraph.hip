@@ -151,6 +151,7 @@ __device__ __forceinline__ int build_lookup(const int* hk, const short* hv, int 
 // P member (the transpose of the X rows) is taken in LDS, and the table is
 // written out with coalesced stores.
 #define MICRO_PROBE_RATIO 4   // rows longer than 4 |P| are probed
+#define MICRO_MASK_CHUNKS 128 // forward-row slabs of up to 128 x 64 entries find rows by masks
 
 __global__ __launch_bounds__(64) void k_build_micro(BuildParams prm) {
   constexpr int HB = 8;   // hash slots >= 2 * 128
@@ -160,6 +161,8 @@ __global__ __launch_bounds__(64) void k_build_micro(BuildParams prm) {
   __shared__ int s_pre[MCE_WAVE];
   __shared__ int s_ga[MCE_WAVE];
   __shared__ u64 s_row[2 * MCE_MICRO_MAX];
+  __shared__ u64 s_mask[MICRO_MASK_CHUNKS];   // per chunk of 64 streamed entries: bit j, a row starts at entry j
+  __shared__ int s_nzr[MCE_WAVE];             // the slab's non-empty rows, in order
   const int lane = lane_id();
   const int* __restrict__ rp = prm.rp;
   const int* __restrict__ ci = prm.ci;
@@ -241,7 +244,23 @@ __global__ __launch_bounds__(64) void k_build_micro(BuildParams prm) {
         const int D = uni(__shfl(inc, MCE_WAVE - 1));
         s_pre[lane] = inc - d;
         s_ga[lane] = ga;
-        __syncthreads();   // the hash and cleared rows (first slab), the prefix sums
+        // Up to MICRO_MASK_CHUNKS chunks of 64 entries, an entry's row is found
+        // from the chunk's mask of row starts: the non-empty rows in order, the
+        // rows started at or before the entry in its chunk counted with one
+        // popcount, plus those started before the chunk; else by a binary search
+        // over the rows' prefix sums.
+        const bool masks = D <= MICRO_MASK_CHUNKS * MCE_WAVE;
+        if (masks) {
+          for (int c = lane; c < (D + MCE_WAVE - 1) / MCE_WAVE; c += MCE_WAVE) s_mask[c] = 0;
+          const u64 nz = ballot(d > 0);
+          if (d > 0) s_nzr[mbcnt(nz)] = lane;
+        }
+        __syncthreads();   // the hash and cleared rows (first slab), the prefix sums, the cleared masks
+        if (masks) {
+          if (d > 0) atomicOr(&s_mask[(inc - d) >> 6], 1ull << ((inc - d) & 63));
+          __syncthreads();
+        }
+        int started = 0;   // non-empty rows started before the current chunk
         for (int base = 0; base < D; base += 4 * MCE_WAVE) {
           int u[4], rw[4];
 #pragma unroll
@@ -249,11 +268,19 @@ __global__ __launch_bounds__(64) void k_build_micro(BuildParams prm) {
             const int x = base + z * MCE_WAVE + lane;
             rw[z] = -1;
             u[z] = 0;
-            if (x < D) {
-              int q = 0;   // the last row whose prefix is <= x
+            int q = 0;   // the last row whose prefix is <= x
+            if (masks) {
+              const u64 m = base + z * MCE_WAVE < D ? s_mask[(base >> 6) + z] : 0ull;
+              const u64 upto = lane == MCE_WAVE - 1 ? ~0ull : (2ull << lane) - 1ull;
+              const int k = started + (int)__popcll(m & upto) - 1;   // >= 0 for every x < D
+              q = s_nzr[k < 0 ? 0 : k];
+              started += (int)__popcll(m);
+            } else if (x < D) {
 #pragma unroll
               for (int step = MCE_WAVE / 2; step > 0; step >>= 1)
                 if (s_pre[q + step] <= x) q += step;
+            }
+            if (x < D) {
               rw[z] = q;
               u[z] = prm.fadj[s_ga[q] + (x - s_pre[q])];
             }
