@@ -243,6 +243,15 @@ constexpr int kMicroCoopRootsPerWave = MCE_MICRO_COOP_ROOTS_PER_WAVE;
 // Chung-Lu graph's 143 and 20,491 width-1 roots: 2.3 and 2.2 ms with 28 waves
 // per CU, 1.1 and 0.9 ms with 8).
 constexpr int kW1WavesPerCu = MCE_W1_WAVES_PER_CU;
+#ifndef MCE_W1_WAVES_PER_CU_BESIDE
+#define MCE_W1_WAVES_PER_CU_BESIDE 4
+#endif
+// ... and this many beside other launches, where the waves they leave free go
+// to the width-2 launch that sets the step's length (the 500k Chung-Lu graph:
+// 17.24 / 17.11 / 17.11 / 17.08 ms a step at 8 / 6 / 5 / 4 waves per CU; alone,
+// 4 waves per CU made the width-1 launches slower, 23.56 -> 23.8 ms a step with
+// the launches in series).
+constexpr int kW1WavesPerCuBeside = MCE_W1_WAVES_PER_CU_BESIDE;
 // Tables other than micro ones are built by the split build: a root's rows are
 // dealt over several blocks, about this many (root, part) blocks per CU.
 constexpr int kSplitBlocksPerCu = 16;
@@ -622,7 +631,8 @@ mce_status run_once(mce_engine* e, int32_t n, int64_t nnz, const int32_t* row_pt
                      [&] { return mce_search_max_workers(L, e->num_cu); });
     }
     if (nw <= 0) return fail(e, MCE_ERR_DEVICE, "search kernel occupancy query failed");
-    if (c != MCE_SUB_MICRO && (c >> 1) == 0) nw = std::min(nw, kW1WavesPerCu * e->num_cu);
+    if (c != MCE_SUB_MICRO && (c >> 1) == 0)
+      nw = std::min(nw, (overlap && busy_subs > 1 ? kW1WavesPerCuBeside : kW1WavesPerCu) * e->num_cu);
     if (kWideWavesPerCu > 0 && overlap && busy_subs > 1 && c != MCE_SUB_MICRO && (c >> 1) > 0)
       nw = std::min(nw, kWideWavesPerCu * e->num_cu);
     if (e->cfg.max_workers > 0) nw = std::min(nw, (int)e->cfg.max_workers);
