@@ -232,6 +232,17 @@ constexpr int kMicroStackMinStatic = 256;      // the smallest stack mce_run_sta
 #ifndef MCE_MICRO_COOP_ROOTS_PER_WAVE
 #define MCE_MICRO_COOP_ROOTS_PER_WAVE 4
 #endif
+#ifndef MCE_MICRO_WAVES_PER_CU
+#define MCE_MICRO_WAVES_PER_CU 8
+#endif
+#ifndef MCE_MICRO_WAVES_PER_CU_BESIDE
+#define MCE_MICRO_WAVES_PER_CU_BESIDE 4
+#endif
+// Micro launches keep at most 8 wavefronts per CU alone (more add start-up
+// spread and little throughput), 4 beside other launches, which then get the
+// compute units: the 500k Chung-Lu graph at 8 / 5 / 4 / 3 / 2 waves per CU
+// beside the others, 17.14 / 16.90 / 16.88 / 16.85 / 17.70 ms a step; in series,
+// 23.65 ms at 8 and 25.57 ms at 4.
 // micro launches with this many roots per wave share pivot scans
 constexpr int kMicroCoopRootsPerWave = MCE_MICRO_COOP_ROOTS_PER_WAVE;
 #ifndef MCE_W1_WAVES_PER_CU
@@ -619,9 +630,9 @@ mce_status run_once(mce_engine* e, int32_t n, int64_t nnz, const int32_t* row_pt
     pl.sub = c;
     int nw;
     if (c == MCE_SUB_MICRO) {
-      // 8 wavefronts per CU: more add start-up spread and little throughput
       nw = occupancy(e, -1 - (counters ? 1 : 0), 0LL, [&] { return mce_micro_max_workers(counters, e->num_cu); });
-      nw = std::min(nw, 8 * e->num_cu);
+      nw = std::min(nw, (overlap && busy_subs > 1 ? MCE_MICRO_WAVES_PER_CU_BESIDE : MCE_MICRO_WAVES_PER_CU) *
+                            e->num_cu);
     } else {
       pl.L = mce_search_layout(c, mode, tc->sub_maxp[var][c], tc->sub_maxx[var][c], tc->sub_maxr[var][c],
                                counts[c], e->num_cu, hbm, counters);
