@@ -265,7 +265,10 @@ constexpr int kW1WavesPerCu = MCE_W1_WAVES_PER_CU;
 constexpr int kW1WavesPerCuBeside = MCE_W1_WAVES_PER_CU_BESIDE;
 // Tables other than micro ones are built by the split build: a root's rows are
 // dealt over several blocks, about this many (root, part) blocks per CU.
-constexpr int kSplitBlocksPerCu = 16;
+#ifndef MCE_SPLIT_BLOCKS_PER_CU
+#define MCE_SPLIT_BLOCKS_PER_CU 16
+#endif
+constexpr int kSplitBlocksPerCu = MCE_SPLIT_BLOCKS_PER_CU;
 #ifndef MCE_WIDE_WAVES_PER_CU
 #define MCE_WIDE_WAVES_PER_CU 14
 #endif
