@@ -232,6 +232,9 @@ constexpr int kMicroStackMinStatic = 256;      // the smallest stack mce_run_sta
 #ifndef MCE_MICRO_COOP_ROOTS_PER_WAVE
 #define MCE_MICRO_COOP_ROOTS_PER_WAVE 4
 #endif
+#ifndef MCE_BUILD_BLOCKS_PER_CU
+#define MCE_BUILD_BLOCKS_PER_CU 32   // micro build: one-wave blocks per CU; the split build's kernels a quarter of it
+#endif
 #ifndef MCE_MICRO_WAVES_PER_CU
 #define MCE_MICRO_WAVES_PER_CU 8
 #endif
@@ -812,7 +815,8 @@ mce_status run_once(mce_engine* e, int32_t n, int64_t nnz, const int32_t* row_pt
       bp.fdeg = fdeg_p;
     }
     if (timing) (void)hipEventRecord(e->ev[evi], ls);
-    if ((h = mce_launch_build(bp, e->num_cu * 32, ls)) != hipSuccess) return launch_fail(h, "build launch");
+    if ((h = mce_launch_build(bp, e->num_cu * MCE_BUILD_BLOCKS_PER_CU, ls)) != hipSuccess)
+      return launch_fail(h, "build launch");
     if (timing) (void)hipEventRecord(e->ev[evi + 1], ls);
     if (!overlap &&
         (h = mce_launch_wl_init(wl, pl.nw, dp<u64>(B.stats) + (size_t)stat_off * MCE_NSTAT, ls)) != hipSuccess)
