@@ -239,13 +239,14 @@ constexpr int kMicroStackMinStatic = 256;      // the smallest stack mce_run_sta
 #define MCE_MICRO_WAVES_PER_CU 8
 #endif
 #ifndef MCE_MICRO_WAVES_PER_CU_BESIDE
-#define MCE_MICRO_WAVES_PER_CU_BESIDE 4
+#define MCE_MICRO_WAVES_PER_CU_BESIDE 3
 #endif
 // Micro launches keep at most 8 wavefronts per CU alone (more add start-up
-// spread and little throughput), 4 beside other launches, which then get the
+// spread and little throughput), 3 beside other launches, which then get the
 // compute units: the 500k Chung-Lu graph at 8 / 5 / 4 / 3 / 2 waves per CU
-// beside the others, 17.14 / 16.90 / 16.88 / 16.85 / 17.70 ms a step; in series,
-// 23.65 ms at 8 and 25.57 ms at 4.
+// beside the others, 17.14 / 16.90 / 16.88 / 16.85 / 17.70 ms a step (3 against
+// 4 in three more comparisons: 0.07-0.08 ms faster; the 4M-vertex uniform
+// sample 62.61 -> 62.37 ms); in series, 23.65 ms at 8 and 25.57 ms at 4.
 // micro launches with this many roots per wave share pivot scans
 constexpr int kMicroCoopRootsPerWave = MCE_MICRO_COOP_ROOTS_PER_WAVE;
 #ifndef MCE_W1_WAVES_PER_CU
